@@ -1,0 +1,164 @@
+"""CPU oracle for INT8 conv_fprop (INT32 output) — test infrastructure only.
+
+Only ``tests/``, the smoke check and the benchmark's CPU-baseline leg use this
+package.  The product path never imports it.  It wraps the plain nested-loop C
+implementation in ``conv_fprop_oracle.c`` (64-bit sums over the definition on
+the cuDNN "Convolutions" page, section "Convolution Fprop"; loop order and
+strided addressing from "Building a From-Scratch INT8 Strided Convolution
+Kernel", steps 1 and 2) through ctypes, marshalling torch CPU tensors (any
+strides) into pointers, dims and element strides.
+
+Parity status: every entry point here is pinned by ``tests/test_oracle_pins.py``
+(brute force, a float64 library convolution, closed forms, invariants and
+mutation checks), none is "parity unpinned".
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Sequence
+
+import numpy as np
+import torch
+
+from . import build as _build
+
+__all__ = ["OracleError", "Oracle", "load", "out_dims", "conv_fprop", "conv_fprop_points",
+           "max_threads"]
+
+_ERRORS = {
+    1: "bad argument (null pointer, negative size, stride/dilation < 1, negative padding)",
+    2: "channel mismatch or empty output window",
+    3: "output dims are not [N, K, P, Q]",
+    4: "a sum does not fit in int32",
+}
+
+_I64x4 = ctypes.c_int64 * 4
+_I64x2 = ctypes.c_int64 * 2
+
+
+class OracleError(RuntimeError):
+    def __init__(self, code: int):
+        super().__init__(f"oracle error {code}: {_ERRORS.get(code, 'unknown')}")
+        self.code = code
+
+
+def _v4(v) -> ctypes.Array:
+    v = [int(a) for a in v]
+    assert len(v) == 4
+    return _I64x4(*v)
+
+
+def _v2(v) -> ctypes.Array:
+    if isinstance(v, int):
+        v = (v, v)
+    v = [int(a) for a in v]
+    assert len(v) == 2
+    return _I64x2(*v)
+
+
+class Oracle:
+    """One loaded copy of the oracle library (tests may load mutated builds)."""
+
+    def __init__(self, path: str):
+        self.path = path
+        lib = ctypes.CDLL(path)
+        P = ctypes.c_void_p
+        lib.oracle_out_dims.argtypes = [P] * 7
+        lib.oracle_out_dims.restype = ctypes.c_int
+        lib.oracle_conv_fprop.argtypes = [P] * 13 + [ctypes.c_int]
+        lib.oracle_conv_fprop.restype = ctypes.c_int
+        lib.oracle_conv_fprop_points.argtypes = [P] * 10 + [P, ctypes.c_int64, P]
+        lib.oracle_conv_fprop_points.restype = ctypes.c_int
+        lib.oracle_max_threads.argtypes = []
+        lib.oracle_max_threads.restype = ctypes.c_int
+        self.lib = lib
+
+    def max_threads(self) -> int:
+        return int(self.lib.oracle_max_threads())
+
+    def out_dims(self, xdims, wdims, pre, post, stride, dil):
+        out = _I64x4()
+        rc = self.lib.oracle_out_dims(_v4(xdims), _v4(wdims), _v2(pre), _v2(post),
+                                      _v2(stride), _v2(dil), out)
+        if rc:
+            raise OracleError(rc)
+        return tuple(int(a) for a in out)
+
+    def conv_fprop(self, x: torch.Tensor, w: torch.Tensor, pre=0, post=0, stride=1, dil=1,
+                   out: Optional[torch.Tensor] = None, threads: int = 0,
+                   allow_overflow: bool = False) -> torch.Tensor:
+        """Y = conv(x, w) as int32.  x, w: int8 CPU tensors with any strides.
+
+        ``out`` (int32, CPU, any non-overlapping strides) receives the result
+        if given; otherwise a contiguous N,K,P,Q tensor is returned.
+        """
+        _check_cpu(x, torch.int8, "x")
+        _check_cpu(w, torch.int8, "w")
+        yd = self.out_dims(x.shape, w.shape, pre, post, stride, dil)
+        if out is None:
+            out = torch.empty(yd, dtype=torch.int32)
+        _check_cpu(out, torch.int32, "out")
+        if tuple(out.shape) != yd:
+            raise OracleError(3)
+        rc = self.lib.oracle_conv_fprop(
+            ctypes.c_void_p(x.data_ptr()), _v4(x.shape), _v4(x.stride()),
+            ctypes.c_void_p(w.data_ptr()), _v4(w.shape), _v4(w.stride()),
+            ctypes.c_void_p(out.data_ptr()), _v4(out.shape), _v4(out.stride()),
+            _v2(pre), _v2(post), _v2(stride), _v2(dil), int(threads))
+        if rc and not (rc == 4 and allow_overflow):
+            raise OracleError(rc)
+        return out
+
+    def conv_fprop_points(self, x: torch.Tensor, w: torch.Tensor, idx, pre=0, post=0,
+                          stride=1, dil=1) -> np.ndarray:
+        """Exact int64 sums at the (n, k, p, q) rows of ``idx``."""
+        _check_cpu(x, torch.int8, "x")
+        _check_cpu(w, torch.int8, "w")
+        idx = np.ascontiguousarray(np.asarray(idx, dtype=np.int64).reshape(-1, 4))
+        res = np.empty(idx.shape[0], dtype=np.int64)
+        rc = self.lib.oracle_conv_fprop_points(
+            ctypes.c_void_p(x.data_ptr()), _v4(x.shape), _v4(x.stride()),
+            ctypes.c_void_p(w.data_ptr()), _v4(w.shape), _v4(w.stride()),
+            _v2(pre), _v2(post), _v2(stride), _v2(dil),
+            idx.ctypes.data_as(ctypes.c_void_p), ctypes.c_int64(idx.shape[0]),
+            res.ctypes.data_as(ctypes.c_void_p))
+        if rc:
+            raise OracleError(rc)
+        return res
+
+
+def _check_cpu(t: torch.Tensor, dtype, name: str):
+    if not isinstance(t, torch.Tensor) or t.device.type != "cpu" or t.dtype != dtype or t.dim() != 4:
+        raise TypeError(f"{name}: expected a 4-D CPU tensor of {dtype}")
+
+
+_DEFAULT: Optional[Oracle] = None
+
+
+def load(path: Optional[str] = None) -> Oracle:
+    """Load the oracle library, compiling it first if it is not built."""
+    global _DEFAULT
+    if path is not None:
+        return Oracle(path)
+    if _DEFAULT is None:
+        if not os.path.exists(_build.LIB):
+            _build.compile_oracle()
+        _DEFAULT = Oracle(_build.LIB)
+    return _DEFAULT
+
+
+def out_dims(*a, **k):
+    return load().out_dims(*a, **k)
+
+
+def conv_fprop(*a, **k):
+    return load().conv_fprop(*a, **k)
+
+
+def conv_fprop_points(*a, **k):
+    return load().conv_fprop_points(*a, **k)
+
+
+def max_threads() -> int:
+    return load().max_threads()

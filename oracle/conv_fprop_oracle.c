@@ -1,0 +1,206 @@
+/*
+ * Plain CPU oracle for INT8 convolution forward with INT32 output.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Only the tests, the smoke check and the
+ * benchmark's CPU-baseline leg load this library.  It shares no source,
+ * header, table or helper with the HIP library, and it is deliberately slow:
+ * a direct nested loop over the definition, 64-bit accumulation, no blocking.
+ *
+ * What it computes (cuDNN docs page "Convolutions", section "Convolution
+ * Fprop": the response is the image convolved with the filter; its Python API
+ * list names pre_padding, post_padding, stride and dilation):
+ *
+ *   Y[n,k,p,q] = sum_{r<R} sum_{s<S} sum_{c<C}
+ *                  Xpad[n, c, p*sh - ph + r*dh, q*sw - pw + s*dw] * W[k,c,r,s]
+ *
+ * with Xpad equal to X inside the image and 0 outside it (zero padding).
+ * Readings taken where the pages leave a step open:
+ *   - "convolved" is read as cross-correlation (no flip of the filter): the
+ *     naive loop of "Building a From-Scratch INT8 Strided Convolution Kernel",
+ *     "Step 2: Implement the Naive Strided Loop", reads input[ih+kh] against
+ *     kernel[kh], and the forum page takes torch's conv2d as the truth;
+ *   - the filter is indexed [k, c, r, s]; the same loop on that page adds the
+ *     channel stride twice for the filter, which is read as a slip for the
+ *     output-channel stride plus the input-channel stride;
+ *   - no clamp: the result is INT32, not the clamped INT8 of that loop;
+ *   - padding is zero; pre_padding is added before row/column 0, post_padding
+ *     after the last one; spatial pairs are [h, w].
+ *
+ * Tensors are addressed as in "Step 1: Define the Strided Tensor Layout" of
+ * the same page: logical dims plus strides counted in elements, so element
+ * (a,b,c,d) of a tensor lives at ptr + a*s0 + b*s1 + c*s2 + d*s3.
+ *
+ * Output size per spatial dim: out = floor((in + pre + post - dil*(k-1) - 1) / stride) + 1,
+ * rejected when the numerator is negative (checked before dividing).
+ *
+ * The loop nest follows the naive loop's order: batch, output channel, output
+ * row, output column, then filter row, filter column, input channel.  OpenMP
+ * splits only the (batch, output channel) pairs; each output element is
+ * summed by one thread in that fixed order.
+ */
+#include <stdint.h>
+#include <stddef.h>
+
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+enum {
+    ORACLE_OK = 0,
+    ORACLE_ERR_ARG = 1,      /* null pointer or negative size / parameter */
+    ORACLE_ERR_SHAPE = 2,    /* channel mismatch or empty output window */
+    ORACLE_ERR_OUT_DIMS = 3, /* output dims are not [N, K, P, Q] */
+    ORACLE_ERR_OVERFLOW = 4  /* some sum does not fit in int32 */
+};
+
+/* Output size of one spatial dimension; -1 if the window never fits. */
+static int64_t oracle_out_len(int64_t in, int64_t pre, int64_t post,
+                              int64_t filt, int64_t stride, int64_t dil)
+{
+    int64_t span = in + pre + post - dil * (filt - 1) - 1;
+    if (span < 0)
+        return -1;
+    return span / stride + 1;
+}
+
+int oracle_out_dims(const int64_t xdims[4], const int64_t wdims[4],
+                    const int64_t pre[2], const int64_t post[2],
+                    const int64_t stride[2], const int64_t dil[2],
+                    int64_t ydims[4])
+{
+    if (!xdims || !wdims || !pre || !post || !stride || !dil || !ydims)
+        return ORACLE_ERR_ARG;
+    for (int i = 0; i < 4; ++i)
+        if (xdims[i] < 0 || wdims[i] < 0)
+            return ORACLE_ERR_ARG;
+    for (int i = 0; i < 2; ++i)
+        if (pre[i] < 0 || post[i] < 0 || stride[i] < 1 || dil[i] < 1)
+            return ORACLE_ERR_ARG;
+    if (xdims[1] != wdims[1])
+        return ORACLE_ERR_SHAPE;
+    int64_t p = oracle_out_len(xdims[2], pre[0], post[0], wdims[2], stride[0], dil[0]);
+    int64_t q = oracle_out_len(xdims[3], pre[1], post[1], wdims[3], stride[1], dil[1]);
+    if (p < 1 || q < 1)
+        return ORACLE_ERR_SHAPE;
+    ydims[0] = xdims[0];
+    ydims[1] = wdims[0];
+    ydims[2] = p;
+    ydims[3] = q;
+    return ORACLE_OK;
+}
+
+/* One output element, summed over the filter window in the naive loop's order. */
+static int64_t oracle_point(const int8_t *x, const int64_t xd[4], const int64_t xs[4],
+                            const int8_t *w, const int64_t wd[4], const int64_t ws[4],
+                            int64_t n, int64_t k, int64_t p, int64_t q,
+                            const int64_t pre[2], const int64_t stride[2],
+                            const int64_t dil[2])
+{
+    const int64_t C = xd[1], H = xd[2], Wd = xd[3];
+    const int64_t R = wd[2], S = wd[3];
+    int64_t acc = 0;
+    for (int64_t r = 0; r < R; ++r) {
+        const int64_t h = p * stride[0] - pre[0] + r * dil[0];
+        for (int64_t s = 0; s < S; ++s) {
+            const int64_t wc = q * stride[1] - pre[1] + s * dil[1];
+            if (h < 0 || h >= H || wc < 0 || wc >= Wd)
+                continue; /* zero padding: the term is 0 */
+            for (int64_t c = 0; c < C; ++c) {
+                const int64_t xv = x[n * xs[0] + c * xs[1] + h * xs[2] + wc * xs[3]];
+                const int64_t wv = w[k * ws[0] + c * ws[1] + r * ws[2] + s * ws[3]];
+                acc += xv * wv;
+            }
+        }
+    }
+    return acc;
+}
+
+/*
+ * Full convolution.  x, w, y point at element (0,0,0,0) of each tensor.
+ * ydims must equal oracle_out_dims(...).  Returns ORACLE_ERR_OVERFLOW (after
+ * writing the wrapped values) if any sum leaves the int32 range.
+ * nthreads <= 0 uses the OpenMP default.
+ */
+int oracle_conv_fprop(const int8_t *x, const int64_t xdims[4], const int64_t xstr[4],
+                      const int8_t *w, const int64_t wdims[4], const int64_t wstr[4],
+                      int32_t *y, const int64_t ydims[4], const int64_t ystr[4],
+                      const int64_t pre[2], const int64_t post[2],
+                      const int64_t stride[2], const int64_t dil[2], int nthreads)
+{
+    int64_t want[4];
+    if (!x || !w || !y || !xstr || !wstr || !ystr)
+        return ORACLE_ERR_ARG;
+    int rc = oracle_out_dims(xdims, wdims, pre, post, stride, dil, want);
+    if (rc != ORACLE_OK)
+        return rc;
+    for (int i = 0; i < 4; ++i)
+        if (ydims[i] != want[i])
+            return ORACLE_ERR_OUT_DIMS;
+
+    const int64_t N = ydims[0], K = ydims[1], P = ydims[2], Q = ydims[3];
+    int overflow = 0;
+#ifdef _OPENMP
+    if (nthreads > 0)
+        omp_set_num_threads(nthreads);
+#else
+    (void)nthreads;
+#endif
+#pragma omp parallel for collapse(2) schedule(dynamic, 1) reduction(| : overflow)
+    for (int64_t n = 0; n < N; ++n) {
+        for (int64_t k = 0; k < K; ++k) {
+            for (int64_t p = 0; p < P; ++p) {
+                for (int64_t q = 0; q < Q; ++q) {
+                    int64_t acc = oracle_point(x, xdims, xstr, w, wdims, wstr,
+                                               n, k, p, q, pre, stride, dil);
+                    if (acc < INT32_MIN || acc > INT32_MAX)
+                        overflow = 1;
+                    y[n * ystr[0] + k * ystr[1] + p * ystr[2] + q * ystr[3]] =
+                        (int32_t)(uint32_t)(uint64_t)acc;
+                }
+            }
+        }
+    }
+    return overflow ? ORACLE_ERR_OVERFLOW : ORACLE_OK;
+}
+
+/*
+ * Selected output elements only: idx holds npts rows of (n, k, p, q); the
+ * exact 64-bit sums go to out[i].  Used to check outputs of workloads too
+ * large to recompute whole.
+ */
+int oracle_conv_fprop_points(const int8_t *x, const int64_t xdims[4], const int64_t xstr[4],
+                             const int8_t *w, const int64_t wdims[4], const int64_t wstr[4],
+                             const int64_t pre[2], const int64_t post[2],
+                             const int64_t stride[2], const int64_t dil[2],
+                             const int64_t *idx, int64_t npts, int64_t *out)
+{
+    int64_t yd[4];
+    if (!x || !w || !xstr || !wstr || (npts > 0 && (!idx || !out)) || npts < 0)
+        return ORACLE_ERR_ARG;
+    int rc = oracle_out_dims(xdims, wdims, pre, post, stride, dil, yd);
+    if (rc != ORACLE_OK)
+        return rc;
+    for (int64_t i = 0; i < npts; ++i) {
+        const int64_t *t = idx + 4 * i;
+        for (int d = 0; d < 4; ++d)
+            if (t[d] < 0 || t[d] >= yd[d])
+                return ORACLE_ERR_ARG;
+    }
+#pragma omp parallel for schedule(static)
+    for (int64_t i = 0; i < npts; ++i) {
+        const int64_t *t = idx + 4 * i;
+        out[i] = oracle_point(x, xdims, xstr, w, wdims, wstr, t[0], t[1], t[2], t[3],
+                              pre, stride, dil);
+    }
+    return ORACLE_OK;
+}
+
+/* Threads an OpenMP parallel region gets by default (1 without OpenMP). */
+int oracle_max_threads(void)
+{
+#ifdef _OPENMP
+    return omp_get_max_threads();
+#else
+    return 1;
+#endif
+}

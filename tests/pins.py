@@ -1,0 +1,273 @@
+"""Independent references that pin the oracle (CPU only).
+
+Nothing here imports the HIP library.  Each check takes an ``oracle.Oracle``
+object so that the mutation test can run the same checks against deliberately
+broken builds of the oracle.
+
+* ``brute_force`` computes the convolution a second, unrelated way: explicit
+  zero padding of the image (``numpy.pad``), zero insertion between filter taps
+  for dilation, then a dot product of every stride-spaced window with the
+  dilated filter.  Where the oracle evaluates bounds per tap, this one never
+  tests a bound.
+* ``f64_library_conv`` is torch's CPU conv2d in float64 after an explicit
+  asymmetric ``F.pad`` — exact here, since every partial sum is an integer far
+  below 2**53 (the forum page checks its INT8 result against torch's conv2d).
+* the closed forms (delta filters, ones-by-ones counts, constant operands) come
+  from the definition on the cuDNN "Convolutions" page, section
+  "Convolution Fprop", worked out by hand.
+"""
+from __future__ import annotations
+
+import numpy as np
+import torch
+import torch.nn.functional as F
+
+
+def brute_force(x: np.ndarray, w: np.ndarray, pre, post, stride, dil) -> np.ndarray:
+    """int64 conv by explicit padding, zero-inserted dilation and windows."""
+    x = np.asarray(x, dtype=np.int64)
+    w = np.asarray(w, dtype=np.int64)
+    N, C, H, W = x.shape
+    K, C2, R, S = w.shape
+    assert C == C2
+    xp = np.pad(x, ((0, 0), (0, 0), (pre[0], post[0]), (pre[1], post[1])))
+    Rd, Sd = dil[0] * (R - 1) + 1, dil[1] * (S - 1) + 1
+    wd = np.zeros((K, C, Rd, Sd), dtype=np.int64)
+    wd[:, :, ::dil[0], ::dil[1]] = w
+    Hp, Wp = xp.shape[2], xp.shape[3]
+    if Hp < Rd or Wp < Sd:
+        return np.zeros((N, K, 0, 0), dtype=np.int64)
+    P = len(range(0, Hp - Rd + 1, stride[0]))
+    Q = len(range(0, Wp - Sd + 1, stride[1]))
+    y = np.zeros((N, K, P, Q), dtype=np.int64)
+    wflat = wd.reshape(K, -1)
+    for p in range(P):
+        for q in range(Q):
+            win = xp[:, :, p * stride[0]:p * stride[0] + Rd, q * stride[1]:q * stride[1] + Sd]
+            y[:, :, p, q] = win.reshape(N, -1) @ wflat.T
+    return y
+
+
+def f64_library_conv(x: torch.Tensor, w: torch.Tensor, pre, post, stride, dil) -> torch.Tensor:
+    xp = F.pad(x.to(torch.float64), (pre[1], post[1], pre[0], post[0]))
+    y = F.conv2d(xp, w.to(torch.float64), stride=tuple(stride), dilation=tuple(dil))
+    return y.round().to(torch.int64)
+
+
+def in_bounds_taps(H, W, R, S, pre, stride, dil, P, Q) -> np.ndarray:
+    """T[p, q] = number of filter taps (r, s) that land inside the image."""
+    rows = np.array([sum(1 for r in range(R) if 0 <= p * stride[0] - pre[0] + r * dil[0] < H)
+                     for p in range(P)], dtype=np.int64)
+    cols = np.array([sum(1 for s in range(S) if 0 <= q * stride[1] - pre[1] + s * dil[1] < W)
+                     for q in range(Q)], dtype=np.int64)
+    return rows[:, None] * cols[None, :]
+
+
+def rand_i8(rng: np.random.Generator, shape) -> torch.Tensor:
+    return torch.from_numpy(rng.integers(-128, 128, size=shape, dtype=np.int64).astype(np.int8))
+
+
+# --------------------------------------------------------------------------
+# Check routines (raise AssertionError on the first disagreement).
+# --------------------------------------------------------------------------
+
+def check_random_vs_brute_force(orc, n_cases: int = 300, seed: int = 7) -> None:
+    """Random small problems over the full parameter grid vs brute force."""
+    rng = np.random.default_rng(seed)
+    done = 0
+    while done < n_cases:
+        N, C, K = (int(v) for v in rng.integers(1, 4, size=3))
+        H, W = (int(v) for v in rng.integers(1, 8, size=2))
+        R, S = (int(v) for v in rng.integers(1, 4, size=2))
+        st = tuple(int(v) for v in rng.integers(1, 4, size=2))
+        dl = tuple(int(v) for v in rng.integers(1, 4, size=2))
+        pre = tuple(int(v) for v in rng.integers(0, 3, size=2))
+        post = tuple(int(v) for v in rng.integers(0, 3, size=2))
+        if H + pre[0] + post[0] - dl[0] * (R - 1) - 1 < 0 or W + pre[1] + post[1] - dl[1] * (S - 1) - 1 < 0:
+            continue
+        x = rand_i8(rng, (N, C, H, W))
+        w = rand_i8(rng, (K, C, R, S))
+        y = orc.conv_fprop(x, w, pre, post, st, dl)
+        ref = brute_force(x.numpy(), w.numpy(), pre, post, st, dl)
+        assert tuple(y.shape) == ref.shape, (y.shape, ref.shape, (N, C, H, W, K, R, S, st, dl, pre, post))
+        assert np.array_equal(y.numpy().astype(np.int64), ref), (N, C, H, W, K, R, S, st, dl, pre, post)
+        done += 1
+
+
+def check_one_dim_sweep(orc, seed: int = 11) -> None:
+    """Every (H, R, stride, dilation, pre, post) with H<=7, R<=3, the rest <=2/3,
+    in the row direction and, transposed, in the column direction."""
+    rng = np.random.default_rng(seed)
+    for H in range(1, 8):
+        for R in range(1, 4):
+            for st in range(1, 4):
+                for dl in range(1, 4):
+                    for pre in range(0, 3):
+                        for post in range(0, 3):
+                            if H + pre + post - dl * (R - 1) - 1 < 0:
+                                continue
+                            for axis in (0, 1):
+                                if axis == 0:
+                                    xs, ws = (1, 2, H, 2), (2, 2, R, 2)
+                                    a = dict(pre=(pre, 1), post=(post, 0), stride=(st, 1), dil=(dl, 1))
+                                else:
+                                    xs, ws = (1, 2, 2, H), (2, 2, 2, R)
+                                    a = dict(pre=(1, pre), post=(0, post), stride=(1, st), dil=(1, dl))
+                                x = rand_i8(rng, xs)
+                                w = rand_i8(rng, ws)
+                                y = orc.conv_fprop(x, w, **a)
+                                ref = brute_force(x.numpy(), w.numpy(), a["pre"], a["post"],
+                                                  a["stride"], a["dil"])
+                                assert np.array_equal(y.numpy().astype(np.int64), ref), (H, R, st, dl, pre, post, axis)
+
+
+def check_offcentre_delta(orc) -> None:
+    """Filter = 1 at one off-centre tap (r0, s0) on the diagonal k == c:
+    Y[n,k,p,q] = X[n,k, p*sh - ph + r0*dh, q*sw - pw + s0*dw] (0 outside)."""
+    rng = np.random.default_rng(3)
+    for (R, S, r0, s0, st, dl, pre, post) in [
+            (3, 5, 0, 3, (1, 1), (1, 1), (1, 2), (2, 1)),
+            (3, 5, 2, 1, (2, 1), (2, 2), (2, 1), (1, 3)),
+            (2, 3, 1, 0, (1, 2), (3, 1), (0, 2), (1, 0))]:
+        C = 3
+        x = rand_i8(rng, (2, C, 9, 8))
+        w = torch.zeros((C, C, R, S), dtype=torch.int8)
+        for k in range(C):
+            w[k, k, r0, s0] = 1
+        y = orc.conv_fprop(x, w, pre, post, st, dl).numpy()
+        N, K, P, Q = y.shape
+        xn = x.numpy().astype(np.int64)
+        for p in range(P):
+            for q in range(Q):
+                h = p * st[0] - pre[0] + r0 * dl[0]
+                ww = q * st[1] - pre[1] + s0 * dl[1]
+                want = xn[:, :, h, ww] if (0 <= h < 9 and 0 <= ww < 8) else np.zeros((N, K), np.int64)
+                assert np.array_equal(y[:, :, p, q], want), (R, S, r0, s0, p, q)
+
+
+def check_identity_1x1(orc) -> None:
+    """1x1 delta filter (W[k,c] = [k == c]) reproduces X, subsamples it under
+    a stride, and embeds it in zeros under padding."""
+    rng = np.random.default_rng(5)
+    x = rand_i8(rng, (2, 4, 7, 6))
+    w = torch.eye(4, dtype=torch.int8).reshape(4, 4, 1, 1)
+    y = orc.conv_fprop(x, w)
+    assert torch.equal(y, x.to(torch.int32))
+    y = orc.conv_fprop(x, w, stride=(2, 3))
+    assert torch.equal(y, x[:, :, ::2, ::3].to(torch.int32))
+    y = orc.conv_fprop(x, w, pre=(1, 2), post=(2, 0))
+    z = torch.zeros((2, 4, 10, 8), dtype=torch.int32)
+    z[:, :, 1:8, 2:8] = x.to(torch.int32)
+    assert torch.equal(y, z)
+
+
+def check_ones_count(orc) -> None:
+    """All-ones image and filter: every output equals C * (in-bounds taps);
+    C*R*S wherever the whole window is inside."""
+    for (C, H, W, R, S, pre, post, st, dl) in [
+            (5, 6, 7, 3, 3, (0, 0), (0, 0), (1, 1), (1, 1)),
+            (3, 9, 8, 3, 5, (2, 1), (1, 3), (2, 1), (2, 2)),
+            (2, 5, 5, 2, 3, (1, 1), (1, 1), (1, 2), (1, 1))]:
+        x = torch.ones((2, C, H, W), dtype=torch.int8)
+        w = torch.ones((3, C, R, S), dtype=torch.int8)
+        y = orc.conv_fprop(x, w, pre, post, st, dl).numpy()
+        _, _, P, Q = y.shape
+        T = in_bounds_taps(H, W, R, S, pre, st, dl, P, Q)
+        assert np.array_equal(y, np.broadcast_to(C * T, y.shape)), (C, H, W, R, S)
+        if pre == (0, 0) and post == (0, 0):
+            assert (y == C * R * S).all()
+
+
+def check_constant_min(orc) -> None:
+    """Image and filter constant -128: each in-bounds tap adds 16384 per channel."""
+    C, H, W, R, S = 4, 9, 8, 3, 5
+    pre, post, st, dl = (2, 1), (1, 3), (2, 1), (2, 2)
+    x = torch.full((1, C, H, W), -128, dtype=torch.int8)
+    w = torch.full((2, C, R, S), -128, dtype=torch.int8)
+    y = orc.conv_fprop(x, w, pre, post, st, dl).numpy()
+    T = in_bounds_taps(H, W, R, S, pre, st, dl, y.shape[2], y.shape[3])
+    assert np.array_equal(y[0, 0], 16384 * C * T)
+
+
+def check_layouts(orc) -> None:
+    """Same logical values as NCHW, NHWC, a 2x-wide strided view, a permuted
+    filter and a zero-stride broadcast image give identical outputs."""
+    rng = np.random.default_rng(9)
+    x = rand_i8(rng, (2, 5, 7, 6))
+    w = rand_i8(rng, (3, 5, 3, 2))
+    a = dict(pre=(1, 0), post=(0, 2), stride=(2, 1), dil=(1, 2))
+    ref = orc.conv_fprop(x, w, **a)
+    nhwc = x.contiguous(memory_format=torch.channels_last)
+    assert torch.equal(orc.conv_fprop(nhwc, w.contiguous(memory_format=torch.channels_last), **a), ref)
+    wide = torch.zeros((2, 5, 7, 12), dtype=torch.int8)
+    wide[..., ::2] = x
+    wide[..., 1::2] = rand_i8(rng, (2, 5, 7, 6))
+    assert torch.equal(orc.conv_fprop(wide[..., ::2], w, **a), ref)
+    krsc_view = w.permute(0, 2, 3, 1).contiguous().permute(0, 3, 1, 2)
+    assert torch.equal(orc.conv_fprop(x, krsc_view, **a), ref)
+    row = rand_i8(rng, (1, 5, 7, 6))
+    bcast = row.expand(4, 5, 7, 6)
+    y = orc.conv_fprop(bcast, w, **a)
+    y1 = orc.conv_fprop(row, w, **a)
+    assert all(torch.equal(y[i], y1[0]) for i in range(4))
+    # output written through strides lands in the right places
+    out_cl = torch.full(ref.shape, -1, dtype=torch.int32).contiguous(memory_format=torch.channels_last)
+    orc.conv_fprop(x, w, out=out_cl, **a)
+    assert torch.equal(out_cl, ref)
+
+
+def check_metamorphic(orc) -> None:
+    """Stride = subsampled stride-1 output; dilation = zero-inserted filter;
+    padding = explicit zero pad; linearity in X and W; slicing N and K."""
+    rng = np.random.default_rng(13)
+    x = rand_i8(rng, (3, 4, 11, 10))
+    w = rand_i8(rng, (5, 4, 3, 2))
+    base = orc.conv_fprop(x, w, pre=(1, 2), post=(1, 0))
+    strided = orc.conv_fprop(x, w, pre=(1, 2), post=(1, 0), stride=(3, 2))
+    assert torch.equal(strided, base[:, :, ::3, ::2])
+    # dilation (2, 3) == dilation 1 with a zero-inserted filter
+    wz = torch.zeros((5, 4, 5, 4), dtype=torch.int8)
+    wz[:, :, ::2, ::3] = w
+    assert torch.equal(orc.conv_fprop(x, w, dil=(2, 3)), orc.conv_fprop(x, wz))
+    # padding == explicit zero pad, then no padding
+    xp = F.pad(x, (2, 1, 1, 3))
+    assert torch.equal(orc.conv_fprop(x, w, pre=(1, 2), post=(3, 1)), orc.conv_fprop(xp, w))
+    # linearity (values kept small so sums stay int8)
+    xa = torch.from_numpy(rng.integers(-64, 64, size=(3, 4, 11, 10)).astype(np.int8))
+    xb = torch.from_numpy(rng.integers(-64, 64, size=(3, 4, 11, 10)).astype(np.int8))
+    ya, yb, yab = (orc.conv_fprop(v, w) for v in (xa, xb, xa + xb))
+    assert torch.equal(yab, ya + yb)
+    wa = torch.from_numpy(rng.integers(-64, 64, size=(5, 4, 3, 2)).astype(np.int8))
+    wb = torch.from_numpy(rng.integers(-64, 64, size=(5, 4, 3, 2)).astype(np.int8))
+    assert torch.equal(orc.conv_fprop(x, wa + wb), orc.conv_fprop(x, wa) + orc.conv_fprop(x, wb))
+    # negation of X negates Y (catches an unsigned widening of int8)
+    xn = torch.from_numpy(rng.integers(-127, 128, size=(3, 4, 11, 10)).astype(np.int8))
+    assert torch.equal(orc.conv_fprop(-xn, w), -orc.conv_fprop(xn, w))
+    # slicing the batch or the filters slices the output
+    assert torch.equal(orc.conv_fprop(x[1:], w), orc.conv_fprop(x, w)[1:])
+    assert torch.equal(orc.conv_fprop(x, w[2:4]), orc.conv_fprop(x, w)[:, 2:4])
+
+
+def check_printed_shapes(orc, cases) -> None:
+    for c in cases:
+        got = orc.out_dims(c["image"], c["filter"], c["pre"], c["post"], c["stride"], c["dilation"])
+        assert list(got) == c["out"], (c, got)
+
+
+def check_points(orc) -> None:
+    """The per-element entry agrees with the full one."""
+    rng = np.random.default_rng(17)
+    x = rand_i8(rng, (2, 3, 9, 8))
+    w = rand_i8(rng, (4, 3, 3, 5))
+    a = dict(pre=(2, 1), post=(1, 3), stride=(2, 1), dil=(2, 2))
+    y = orc.conv_fprop(x, w, **a).numpy()
+    idx = np.array([[n, k, p, q] for n in range(2) for k in range(4)
+                    for p in range(y.shape[2]) for q in range(y.shape[3])], dtype=np.int64)
+    v = orc.conv_fprop_points(x, w, idx, **a)
+    assert np.array_equal(v, y[idx[:, 0], idx[:, 1], idx[:, 2], idx[:, 3]].astype(np.int64))
+
+
+QUICK_CHECKS = [
+    check_random_vs_brute_force, check_offcentre_delta, check_identity_1x1, check_ones_count,
+    check_constant_min, check_layouts, check_metamorphic, check_points,
+]
