@@ -1,0 +1,243 @@
+"""Benchmark: INT8 conv_fprop throughput on one MI355X.
+
+One step = one conv_fprop_i8 call (the whole path: layout normalisation if
+the operands need it, implicit-GEMM kernel with its epilogue) over one batch
+of seeded synthetic input that is already resident in HBM.  Inputs and
+outputs rotate over enough buffer sets (> 512 MB) that the 256 MB Infinity
+Cache cannot serve a step from a previous one.
+
+Prints one JSON line: the metric (TOPS = 2*N*K*P*Q*C*R*S / s), ms per step,
+the roofline of the implicit-GEMM kernel timed alone with HIP events on the
+launch stream, and the CPU oracle timed on the host as a baseline.
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "INT8 conv_fprop TOPS (2·NKPQ·CRS/s) and % of MI355X INT8 MFMA peak"
+INT8_PEAK_TOPS = 5000.0     # MI355X dense int8 MFMA, published
+HBM_PEAK_GBS = 8000.0       # MI355X HBM3E, published
+DEFAULT_WORKLOAD = "large_channel_n64_c512_14"
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
+    ap.add_argument("--rotate-mb", type=float, default=600.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0,
+                    help="target CPU time of the oracle baseline sample")
+    return ap.parse_args()
+
+
+def kernel_source_digest() -> str:
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "int8_convolution_forward_amd", "csrc")
+    for f in sorted(os.listdir(csrc)):
+        with open(os.path.join(csrc, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def traffic_from_profiles(workload: str, launch_bytes_alg: float):
+    """HBM bytes per launch from committed rocprofv3 counter summaries, if
+    they were taken on the current kernel source."""
+    path = os.path.join(ROOT, "profiles", f"traffic_{workload}.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        t = json.load(f)
+    if t.get("kernel_source_digest") != kernel_source_digest():
+        return None
+    return t.get("hbm_bytes_per_launch")
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py: this build runs on one GPU only; the convolution shards over the "
+              "batch with no exchange, but no multi-GPU run is provided (--gpus 1).",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import int8_convolution_forward_amd as ci8
+    import workloads as wl
+
+    c = wl.case(args.workload)
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    d = wl.make_inputs(c, c.seed_base)
+    N, K, P, Q = c.out.dims
+    _, C, R, S = c.filter.dims
+    ops = c.ops
+
+    # ---- resident, rotating buffer sets --------------------------------
+    x0_storage, _ = wl.to_device(d["x_storage"], c.image, dev)
+    w0_storage, _ = wl.to_device(d["w_storage"], c.filter, dev)
+    set_bytes = (x0_storage.numel() + w0_storage.numel() + 4 * c.out.storage_size)
+    nsets = max(2, min(128, int(args.rotate_mb * 2**20 // set_bytes) + 1))
+    sets = []
+    for i in range(nsets):
+        xs = x0_storage.clone()
+        ws_ = w0_storage.clone()
+        ys = torch.empty(c.out.storage_size, dtype=torch.int32, device=dev)
+        x = torch.as_strided(xs, c.image.dims, c.image.strides, c.image.offset)
+        w = torch.as_strided(ws_, c.filter.dims, c.filter.strides, c.filter.offset)
+        y = torch.as_strided(ys, c.out.dims, c.out.strides, c.out.offset)
+        sets.append((xs, ws_, ys, x, w, y))
+    ws_bytes = ci8.conv_fprop_i8_workspace_size(sets[0][3], sets[0][4], sets[0][5], c.pre, c.post,
+                                                c.stride, c.dilation)
+    workspace = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
+    plan = ci8.conv_fprop_i8_plan(sets[0][3], sets[0][4], sets[0][5], c.pre, c.post, c.stride,
+                                  c.dilation)
+
+    stream = torch.cuda.current_stream()
+    sh = ctypes.c_void_p(stream.cuda_stream)
+    params = ci8._params(c.pre, c.post, c.stride, c.dilation, None)
+
+    def prebuilt(x, w, y):
+        return (ctypes.byref(ci8.desc(x)), ctypes.c_void_p(x.data_ptr()),
+                ctypes.byref(ci8.desc(w)), ctypes.c_void_p(w.data_ptr()),
+                ctypes.byref(ci8.desc(y)), ctypes.c_void_p(y.data_ptr()), *params,
+                ctypes.c_void_p(workspace.data_ptr()) if ws_bytes else None,
+                ctypes.c_size_t(ws_bytes), sh)
+
+    calls = [prebuilt(s[3], s[4], s[5]) for s in sets]
+    fn = ci8.lib.conv_fprop_i8_ws
+
+    def step(i):
+        rc = fn(*calls[i % nsets])
+        if rc != 0:
+            raise RuntimeError(ci8.status_string(rc))
+
+    print(f"bench: {c.name} plan: {plan}; {nsets} buffer sets of {set_bytes / 2**20:.1f} MiB",
+          file=sys.stderr, flush=True)
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+
+    # ---- timed region: exactly `steps` steps ---------------------------
+    t_start = torch.cuda.Event(enable_timing=True)
+    t_end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t_start.record(stream)
+    for i in range(args.steps):
+        step(i)
+    t_end.record(stream)
+    torch.cuda.synchronize()
+    ms_per_step = t_start.elapsed_time(t_end) / args.steps
+    tops = ops / (ms_per_step * 1e-3) / 1e12
+    print(f"bench: {ms_per_step * 1e3:.2f} us/step, {tops:.1f} TOPS", file=sys.stderr, flush=True)
+
+    # ---- implicit-GEMM kernel alone, one event pair per launch ---------
+    # Operands that the whole path would repack are given to it already
+    # channel-innermost, so each call is exactly one implicit-GEMM launch.
+    kcalls = []
+    for s in sets:
+        x, w, y = s[3], s[4], s[5]
+        f = ci8.plan_fields(ci8.conv_fprop_i8_plan(x, w, y, c.pre, c.post, c.stride, c.dilation))
+        if f["repack_image"] == "1":
+            x = x.contiguous(memory_format=torch.channels_last)
+        if f["repack_filter"] == "1":
+            w = w.contiguous(memory_format=torch.channels_last)
+        kcalls.append((x, w, y))
+    kf = ci8.plan_fields(ci8.conv_fprop_i8_plan(*kcalls[0], c.pre, c.post, c.stride, c.dilation))
+    kernel_only = kf["repack_image"] == "0" and kf["repack_filter"] == "0" and \
+        ci8.conv_fprop_i8_workspace_size(*kcalls[0], c.pre, c.post, c.stride, c.dilation) == 0
+    kpre = [prebuilt(*t) for t in kcalls]
+    nk = max(args.steps, 50)
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(nk)]
+    for i in range(min(10, nk)):
+        fn(*kpre[i % nsets])
+    torch.cuda.synchronize()
+    for i in range(nk):
+        evs[i][0].record(stream)
+        rc = fn(*kpre[i % nsets])
+        evs[i][1].record(stream)
+        if rc:
+            raise RuntimeError(ci8.status_string(rc))
+    torch.cuda.synchronize()
+    k_ms = sorted(a.elapsed_time(b) for a, b in evs)
+    k_avg_ms = sum(k_ms) / len(k_ms)
+    k_med_ms = k_ms[len(k_ms) // 2]
+
+    # algorithmic bytes: image, filter read once, int32 output written once
+    alg_bytes = N * C * c.image.dims[2] * c.image.dims[3] + K * C * R * S + 4 * N * K * P * Q
+    ai = ops / alg_bytes
+    ridge = INT8_PEAK_TOPS * 1e12 / (HBM_PEAK_GBS * 1e9)
+    if ai >= ridge:
+        roof = {"bound": "mfma", "achieved": ops / (k_avg_ms * 1e-3) / 1e12, "peak": INT8_PEAK_TOPS,
+                "unit": "TOP/s"}
+    else:
+        roof = {"bound": "hbm", "achieved": alg_bytes / (k_avg_ms * 1e-3) / 1e9, "peak": HBM_PEAK_GBS,
+                "unit": "GB/s"}
+    roof["frac"] = roof["achieved"] / roof["peak"]
+    roof["traffic"] = traffic_from_profiles(c.name, alg_bytes)
+    roof["kernel"] = "conv_igemm_kernel"
+    roof["kernel_avg_us"] = k_avg_ms * 1e3
+    roof["kernel_median_us"] = k_med_ms * 1e3
+    roof["kernel_only_launch"] = kernel_only
+    roof["algorithmic_bytes"] = alg_bytes
+    roof["algorithmic_ops"] = ops
+
+    # ---- CPU oracle baseline (rank 0, one GPU) -------------------------
+    cpu = None
+    if not args.no_cpu_baseline:
+        import oracle
+        orc = oracle.load()
+        threads = orc.max_threads()
+        t0 = time.perf_counter()
+        reps = 0
+        while True:
+            orc.conv_fprop(d["x"], d["w"], c.pre, c.post, c.stride, c.dilation, threads=threads)
+            reps += 1
+            el = time.perf_counter() - t0
+            if el >= args.cpu_seconds or reps >= 20:
+                break
+        cpu = {"value": ops * reps / el / 1e12, "unit": "TOPS", "cores": threads, "kind": "oracle",
+               "sample": f"the whole {c.name} workload, {reps} run(s), {el:.1f} s wall, "
+                         f"{threads} OpenMP threads, plain -O2 C with int64 sums"}
+
+    out = {
+        "metric": METRIC,
+        "value": tops,
+        "unit": "TOPS",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "int8",
+        "data": "synthetic",
+        "config": {"workload": c.name, "image": list(c.image.dims), "image_strides": list(c.image.strides),
+                   "filter": list(c.filter.dims), "filter_strides": list(c.filter.strides),
+                   "out": list(c.out.dims), "out_strides": list(c.out.strides),
+                   "pre_padding": list(c.pre), "post_padding": list(c.post),
+                   "stride": list(c.stride), "dilation": list(c.dilation),
+                   "accumulate": "int32", "output": "int32", "plan": plan,
+                   "buffer_sets": nsets},
+        "frac_of_int8_peak": tops / INT8_PEAK_TOPS,
+        "roofline": roof,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,174 @@
+/*
+ * conv_i8.h — INT8 2-D convolution forward (conv_fprop) with INT32
+ * accumulation and INT32 output, for AMD Instinct MI355X (gfx950).
+ *
+ * The operation (cuDNN docs page "Convolutions", section "Convolution Fprop",
+ * and its "Python API" list: image, weight, pre_padding, post_padding, stride,
+ * dilation):
+ *
+ *   Y[n,k,p,q] = sum_{c<C} sum_{r<R} sum_{s<S}
+ *                  X[n, c, p*stride_h - pre_h + r*dil_h, q*stride_w - pre_w + s*dil_w]
+ *                * W[k, c, r, s]
+ *
+ * where X reads as 0 outside 0 <= h < H, 0 <= w < W (zero padding).  It is a
+ * cross-correlation: the filter is not flipped (the naive loop of "Building a
+ * From-Scratch INT8 Strided Convolution Kernel", "Step 2", reads the input at
+ * oh*stride + kh against kernel tap kh).  The result is exact: every product
+ * of two int8 values is summed in 32-bit integers, which cannot overflow while
+ * C*R*S <= 131071 (|product| <= 16384); larger reductions are refused.  There
+ * is no saturation and no int8 output (the forum thread "INT8 convolution
+ * using cuDNN Python Frontend" shows what an int8 output descriptor produces:
+ * the true sums clamped to int8 and packed into the int32 buffer).
+ *
+ * Output size: P = floor((H + pre_h + post_h - dil_h*(R-1) - 1) / stride_h) + 1,
+ * and Q likewise; a negative numerator is an error.
+ *
+ * Tensors are described as in the forum thread's graph.tensor(dim, stride)
+ * and the blog's "Step 1: Define the Strided Tensor Layout": four logical dims
+ * plus four strides counted in ELEMENTS (not bytes).  Logical orders are
+ *   image  [N, C, H, W]   int8
+ *   filter [K, C, R, S]   int8
+ *   output [N, K, P, Q]   int32
+ * so NCHW, NHWC (channels_last), KCRS, KRSC and strided views are all just
+ * stride choices.  Element (a,b,c,d) lives at ptr + a*s0 + b*s1 + c*s2 + d*s3,
+ * where ptr points at element (0,0,0,0).  The stride of a dim of size 1 is
+ * ignored.  Strides must be >= 0; input strides may be 0 (broadcast); the
+ * output must not overlap itself.  Spatial pairs are [h, w].
+ *
+ * Ownership: the caller owns every buffer.  Pointers are device pointers
+ * (HIP memory of the current device); the library never frees them and keeps
+ * no state between calls.  All device work is enqueued on `stream` (a
+ * hipStream_t; NULL means the default stream); calls return without waiting
+ * for it.
+ *
+ * Errors: argument errors are detected on the host before any device work is
+ * enqueued, and then nothing is written.  CONV_I8_ERR_HIP means a HIP call
+ * failed while enqueueing; faults inside kernels surface at the caller's next
+ * synchronisation of the stream.  Only the output elements the descriptor
+ * addresses are written; gaps of a strided output are left untouched.
+ */
+#ifndef CONV_I8_H
+#define CONV_I8_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    CONV_I8_DT_INT8 = 1,
+    CONV_I8_DT_INT32 = 2
+} conv_i8_dtype_t;
+
+/* A 4-D tensor: dtype (conv_i8_dtype_t), ndim (must be 4), logical dims and
+ * element strides in the logical order given above. */
+typedef struct {
+    int32_t dtype;
+    int32_t ndim;
+    int64_t dims[4];
+    int64_t strides[4];
+} conv_i8_desc_t;
+
+typedef enum {
+    CONV_I8_OK = 0,
+    CONV_I8_ERR_NULL = 1,        /* a required pointer is NULL */
+    CONV_I8_ERR_DTYPE = 2,       /* image/filter not INT8, or output not INT32 */
+    CONV_I8_ERR_RANK = 3,        /* ndim != 4 */
+    CONV_I8_ERR_DIMS = 4,        /* negative dim, or a filter dim R or S < 1 */
+    CONV_I8_ERR_PARAM = 5,       /* stride < 1, dilation < 1 or padding < 0 */
+    CONV_I8_ERR_CHANNELS = 6,    /* image C != filter C */
+    CONV_I8_ERR_OUT_DIMS = 7,    /* output dims != [N, K, P, Q], or P or Q < 1 */
+    CONV_I8_ERR_STRIDES = 8,     /* negative stride, or an output that overlaps itself */
+    CONV_I8_ERR_RANGE = 9,       /* C*R*S > 131071: int32 sums no longer exact */
+    CONV_I8_ERR_WORKSPACE = 10,  /* workspace smaller than conv_fprop_i8_workspace_size */
+    CONV_I8_ERR_UNSUPPORTED = 11,/* one image or the filter spans >= 2 GiB */
+    CONV_I8_ERR_HIP = 12         /* a HIP runtime call failed */
+} conv_i8_status_t;
+
+/* Largest C*R*S for which the int32 sum is exact for all int8 inputs. */
+#define CONV_I8_MAX_REDUCTION 131071
+
+/*
+ * Output dims [N, K, P, Q] for an image and filter descriptor and the conv
+ * parameters.  Validates the same fields conv_fprop_i8 does except the output.
+ * Host-only: touches no device.
+ */
+conv_i8_status_t conv_fprop_i8_out_dims(const conv_i8_desc_t *image,
+                                        const conv_i8_desc_t *filter,
+                                        const int64_t pre_padding[2],
+                                        const int64_t post_padding[2],
+                                        const int64_t stride[2],
+                                        const int64_t dilation[2],
+                                        int64_t out_dims[4]);
+
+/*
+ * Bytes of device workspace conv_fprop_i8_ws needs for this problem (0 when
+ * both the image and the filter are already channel-innermost with C a
+ * multiple of 16 and 16-byte aligned rows; otherwise room for their packed
+ * N,H,W,C / K,R,S,C copies).  image_ptr and filter_ptr are only inspected for
+ * their 16-byte alignment and may be NULL (then they count as aligned).
+ * Host-only.
+ */
+conv_i8_status_t conv_fprop_i8_workspace_size(const conv_i8_desc_t *image, const void *image_ptr,
+                                              const conv_i8_desc_t *filter, const void *filter_ptr,
+                                              const conv_i8_desc_t *out,
+                                              const int64_t pre_padding[2],
+                                              const int64_t post_padding[2],
+                                              const int64_t stride[2],
+                                              const int64_t dilation[2],
+                                              size_t *workspace_bytes);
+
+/*
+ * Y = conv_fprop(image, filter) into `out_ptr`, with caller-provided device
+ * workspace of `workspace_bytes` bytes, 256-byte aligned (may be NULL when the
+ * size needed is 0; CONV_I8_ERR_WORKSPACE if too small or misaligned).  Never
+ * allocates, never synchronises: safe to record into a HIP graph.  The
+ * workspace must stay untouched until the stream has run the call.
+ */
+conv_i8_status_t conv_fprop_i8_ws(const conv_i8_desc_t *image, const void *image_ptr,
+                                  const conv_i8_desc_t *filter, const void *filter_ptr,
+                                  const conv_i8_desc_t *out, void *out_ptr,
+                                  const int64_t pre_padding[2],
+                                  const int64_t post_padding[2],
+                                  const int64_t stride[2],
+                                  const int64_t dilation[2],
+                                  void *workspace, size_t workspace_bytes,
+                                  void *stream);
+
+/*
+ * Same as conv_fprop_i8_ws, but any workspace needed is taken with
+ * hipMallocAsync on `stream` and released with hipFreeAsync after the work.
+ */
+conv_i8_status_t conv_fprop_i8(const conv_i8_desc_t *image, const void *image_ptr,
+                               const conv_i8_desc_t *filter, const void *filter_ptr,
+                               const conv_i8_desc_t *out, void *out_ptr,
+                               const int64_t pre_padding[2],
+                               const int64_t post_padding[2],
+                               const int64_t stride[2],
+                               const int64_t dilation[2],
+                               void *stream);
+
+/*
+ * A one-line, human-readable description of how conv_fprop_i8_ws would run
+ * this problem (which operands are repacked, the tile shape, the grid).
+ * Writes at most `len` bytes including the terminating NUL.  Host-only.
+ */
+conv_i8_status_t conv_fprop_i8_plan(const conv_i8_desc_t *image, const void *image_ptr,
+                                    const conv_i8_desc_t *filter, const void *filter_ptr,
+                                    const conv_i8_desc_t *out,
+                                    const int64_t pre_padding[2],
+                                    const int64_t post_padding[2],
+                                    const int64_t stride[2],
+                                    const int64_t dilation[2],
+                                    char *buf, size_t len);
+
+/* Static string naming a status code. */
+const char *conv_i8_status_string(conv_i8_status_t status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* CONV_I8_H */

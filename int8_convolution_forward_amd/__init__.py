@@ -1,0 +1,236 @@
+"""INT8 conv_fprop for MI355X (gfx950): thin ctypes binding of libconv_i8.so.
+
+Argument marshalling only: torch tensors are turned into the C descriptors
+(logical dims + element strides, dtype), device pointers and the current HIP
+stream, and every step of the convolution runs in the library's HIP kernels.
+PyTorch provides the device memory (outputs, workspace) and the stream.
+
+The operation is the one of the cuDNN "Convolutions" page ("Convolution
+Fprop"): image [N,C,H,W] int8, weight [K,C,R,S] int8 -> [N,K,P,Q] int32, with
+pre/post padding, stride and dilation as in its Python API list; the
+symmetric ``padding`` overload sets pre = post.  If the compiled library is
+missing this module raises on import: there is no fallback implementation.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+from typing import Optional, Sequence, Tuple, Union
+
+import torch
+
+from . import build as _build
+
+__all__ = [
+    "ConvI8Error", "conv_fprop_i8", "conv_fprop_i8_ws", "conv_fprop_i8_plain",
+    "conv_fprop_i8_out_dims", "conv_fprop_i8_workspace_size", "conv_fprop_i8_plan",
+    "status_string", "LIB_PATH", "DT_INT8", "DT_INT32", "MAX_REDUCTION", "lib",
+]
+
+LIB_PATH = _build.LIB
+DT_INT8 = 1
+DT_INT32 = 2
+MAX_REDUCTION = 131071
+
+STATUS = {
+    0: "CONV_I8_OK", 1: "CONV_I8_ERR_NULL", 2: "CONV_I8_ERR_DTYPE", 3: "CONV_I8_ERR_RANK",
+    4: "CONV_I8_ERR_DIMS", 5: "CONV_I8_ERR_PARAM", 6: "CONV_I8_ERR_CHANNELS",
+    7: "CONV_I8_ERR_OUT_DIMS", 8: "CONV_I8_ERR_STRIDES", 9: "CONV_I8_ERR_RANGE",
+    10: "CONV_I8_ERR_WORKSPACE", 11: "CONV_I8_ERR_UNSUPPORTED", 12: "CONV_I8_ERR_HIP",
+}
+
+
+class Desc(ctypes.Structure):
+    _fields_ = [("dtype", ctypes.c_int32), ("ndim", ctypes.c_int32),
+                ("dims", ctypes.c_int64 * 4), ("strides", ctypes.c_int64 * 4)]
+
+
+class ConvI8Error(RuntimeError):
+    def __init__(self, code: int, msg: str):
+        super().__init__(msg)
+        self.code = code
+        self.name = STATUS.get(code, str(code))
+
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError(
+        f"{LIB_PATH} is not built; run int8_convolution_forward_amd/build.py "
+        "(or __graft_entry__.build()) first. There is no fallback implementation.")
+
+lib = ctypes.CDLL(LIB_PATH)
+_P = ctypes.c_void_p
+_DP = ctypes.POINTER(Desc)
+_V2 = ctypes.POINTER(ctypes.c_int64)
+
+lib.conv_fprop_i8_out_dims.argtypes = [_DP, _DP, _V2, _V2, _V2, _V2, _V2]
+lib.conv_fprop_i8_workspace_size.argtypes = [_DP, _P, _DP, _P, _DP, _V2, _V2, _V2, _V2,
+                                             ctypes.POINTER(ctypes.c_size_t)]
+lib.conv_fprop_i8_ws.argtypes = [_DP, _P, _DP, _P, _DP, _P, _V2, _V2, _V2, _V2, _P,
+                                 ctypes.c_size_t, _P]
+lib.conv_fprop_i8.argtypes = [_DP, _P, _DP, _P, _DP, _P, _V2, _V2, _V2, _V2, _P]
+lib.conv_fprop_i8_plan.argtypes = [_DP, _P, _DP, _P, _DP, _V2, _V2, _V2, _V2,
+                                   ctypes.c_char_p, ctypes.c_size_t]
+lib.conv_i8_status_string.argtypes = [ctypes.c_int]
+lib.conv_i8_status_string.restype = ctypes.c_char_p
+for _f in ("conv_fprop_i8_out_dims", "conv_fprop_i8_workspace_size", "conv_fprop_i8_ws",
+           "conv_fprop_i8", "conv_fprop_i8_plan"):
+    getattr(lib, _f).restype = ctypes.c_int
+
+
+def status_string(code: int) -> str:
+    return lib.conv_i8_status_string(int(code)).decode()
+
+
+def _check(code: int):
+    if code != 0:
+        raise ConvI8Error(code, status_string(code))
+
+
+_DTYPES = {torch.int8: DT_INT8, torch.int32: DT_INT32}
+
+
+def desc(t_or_dims, strides=None, dtype: Union[int, torch.dtype, None] = None, ndim: int = 4) -> Desc:
+    """C descriptor from a tensor (its shape, element strides and dtype) or
+    from explicit dims / strides / dtype code."""
+    d = Desc()
+    if isinstance(t_or_dims, torch.Tensor):
+        t = t_or_dims
+        dims, strides = tuple(t.shape), tuple(t.stride())
+        dtype = _DTYPES.get(t.dtype, 0) if dtype is None else dtype
+        ndim = t.dim()
+    else:
+        dims = tuple(t_or_dims)
+    if isinstance(dtype, torch.dtype):
+        dtype = _DTYPES.get(dtype, 0)
+    d.dtype = int(dtype or 0)
+    d.ndim = int(ndim)
+    for i in range(min(4, len(dims))):
+        d.dims[i] = int(dims[i])
+        d.strides[i] = int(strides[i])
+    return d
+
+
+def _pair(v) -> ctypes.Array:
+    if isinstance(v, int):
+        v = (v, v)
+    v = tuple(int(a) for a in v)
+    if len(v) != 2:
+        raise ValueError("spatial parameters are [h, w] pairs")
+    return (ctypes.c_int64 * 2)(*v)
+
+
+def _params(pre_padding, post_padding, stride, dilation, padding):
+    if padding is not None:
+        pre_padding = post_padding = padding
+    return _pair(pre_padding), _pair(post_padding), _pair(stride), _pair(dilation)
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def conv_fprop_i8_out_dims(x, w, pre_padding=0, post_padding=0, stride=1, dilation=1,
+                           padding=None) -> Tuple[int, int, int, int]:
+    pre, post, st, dl = _params(pre_padding, post_padding, stride, dilation, padding)
+    out = (ctypes.c_int64 * 4)()
+    _check(lib.conv_fprop_i8_out_dims(ctypes.byref(_as_desc(x)), ctypes.byref(_as_desc(w)),
+                                      pre, post, st, dl, out))
+    return tuple(int(v) for v in out)
+
+
+def _as_desc(t) -> Desc:
+    return t if isinstance(t, Desc) else desc(t)
+
+
+def _out_like(x: torch.Tensor, dims) -> torch.Tensor:
+    fmt = torch.contiguous_format
+    if x.dim() == 4 and x.is_contiguous(memory_format=torch.channels_last) and not x.is_contiguous():
+        fmt = torch.channels_last
+    return torch.empty(dims, dtype=torch.int32, device=x.device, memory_format=fmt)
+
+
+def conv_fprop_i8_workspace_size(x, w, out, pre_padding=0, post_padding=0, stride=1,
+                                 dilation=1, padding=None) -> int:
+    pre, post, st, dl = _params(pre_padding, post_padding, stride, dilation, padding)
+    n = ctypes.c_size_t()
+    xp = _ptr(x) if isinstance(x, torch.Tensor) else None
+    wp = _ptr(w) if isinstance(w, torch.Tensor) else None
+    _check(lib.conv_fprop_i8_workspace_size(ctypes.byref(_as_desc(x)), xp, ctypes.byref(_as_desc(w)),
+                                            wp, ctypes.byref(_as_desc(out)), pre, post, st, dl,
+                                            ctypes.byref(n)))
+    return int(n.value)
+
+
+def conv_fprop_i8_plan(x, w, out=None, pre_padding=0, post_padding=0, stride=1, dilation=1,
+                       padding=None) -> str:
+    pre, post, st, dl = _params(pre_padding, post_padding, stride, dilation, padding)
+    if out is None:
+        dims = conv_fprop_i8_out_dims(x, w, pre_padding, post_padding, stride, dilation, padding)
+        out = desc(dims, _contig(dims), DT_INT32)
+    buf = ctypes.create_string_buffer(512)
+    xp = _ptr(x) if isinstance(x, torch.Tensor) else None
+    wp = _ptr(w) if isinstance(w, torch.Tensor) else None
+    _check(lib.conv_fprop_i8_plan(ctypes.byref(_as_desc(x)), xp, ctypes.byref(_as_desc(w)), wp,
+                                  ctypes.byref(_as_desc(out)), pre, post, st, dl, buf, 512))
+    return buf.value.decode()
+
+
+def plan_fields(plan: str) -> dict:
+    return dict(re.findall(r"(\w+)=(\S+)", plan))
+
+
+def _contig(dims):
+    s, acc = [], 1
+    for d in reversed(dims):
+        s.append(acc)
+        acc *= d
+    return tuple(reversed(s))
+
+
+def _stream_handle(stream) -> Optional[ctypes.c_void_p]:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def conv_fprop_i8_ws(x: torch.Tensor, w: torch.Tensor, out: torch.Tensor, workspace: Optional[torch.Tensor],
+                     pre_padding=0, post_padding=0, stride=1, dilation=1, padding=None,
+                     stream=None) -> torch.Tensor:
+    """Direct call of the C entry with an explicit workspace tensor."""
+    pre, post, st, dl = _params(pre_padding, post_padding, stride, dilation, padding)
+    ws_ptr = _ptr(workspace)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(lib.conv_fprop_i8_ws(ctypes.byref(desc(x)), _ptr(x), ctypes.byref(desc(w)), _ptr(w),
+                                ctypes.byref(desc(out)), _ptr(out), pre, post, st, dl,
+                                ws_ptr, ctypes.c_size_t(ws_bytes), _stream_handle(stream)))
+    return out
+
+
+def conv_fprop_i8_plain(x: torch.Tensor, w: torch.Tensor, out: torch.Tensor, pre_padding=0,
+                        post_padding=0, stride=1, dilation=1, padding=None, stream=None) -> torch.Tensor:
+    """The C entry that takes its own workspace with hipMallocAsync."""
+    pre, post, st, dl = _params(pre_padding, post_padding, stride, dilation, padding)
+    _check(lib.conv_fprop_i8(ctypes.byref(desc(x)), _ptr(x), ctypes.byref(desc(w)), _ptr(w),
+                             ctypes.byref(desc(out)), _ptr(out), pre, post, st, dl,
+                             _stream_handle(stream)))
+    return out
+
+
+def conv_fprop_i8(x: torch.Tensor, w: torch.Tensor, out: Optional[torch.Tensor] = None,
+                  pre_padding=0, post_padding=0, stride=1, dilation=1, padding=None,
+                  stream=None) -> torch.Tensor:
+    """Y = conv_fprop(x, w) as int32 on x's device.
+
+    x: int8 [N,C,H,W], w: int8 [K,C,R,S], any strides.  ``out`` (int32
+    [N,K,P,Q], any non-overlapping strides) is written if given; otherwise a
+    new tensor in x's memory format is returned.  The workspace, if needed, is
+    a torch allocation on the same stream.
+    """
+    if out is None:
+        dims = conv_fprop_i8_out_dims(x, w, pre_padding, post_padding, stride, dilation, padding)
+        out = _out_like(x, dims)
+    n = conv_fprop_i8_workspace_size(x, w, out, pre_padding, post_padding, stride, dilation, padding)
+    ws = torch.empty(n, dtype=torch.uint8, device=out.device) if n else None
+    return conv_fprop_i8_ws(x, w, out, ws, pre_padding, post_padding, stride, dilation, padding,
+                            stream)

@@ -1,0 +1,674 @@
+// conv_i8: host side of the INT8 conv_fprop library (gfx950).
+//
+// Validates the descriptors and conv parameters (all on the host, before any
+// device work), decides whether the image and/or filter must first be
+// repacked to a channel-innermost layout, picks a tile shape, and enqueues
+// the kernels on the caller's stream.  See include/conv_i8.h for the
+// contract; the operation is the one of the cuDNN "Convolutions" page,
+// section "Convolution Fprop", with the parameters of its Python API list.
+#include "conv_i8.h"
+
+#include <hip/hip_runtime.h>
+
+#include <stdint.h>
+#include <stdio.h>
+#include <stdlib.h>
+#include <string.h>
+
+#include <algorithm>
+#include <string>
+
+#include "igemm_kernel.hpp"
+#include "repack_kernel.hpp"
+
+namespace convi8 {
+namespace {
+
+constexpr int64_t kI32Max = 0x7fffffffLL;
+constexpr int kCUs = 256;  // MI355X compute units (8 XCDs x 32)
+
+struct T4 {
+    int64_t d[4];
+    int64_t s[4];  // element strides; 0 for dims of size <= 1
+    int64_t elems() const { return d[0] * d[1] * d[2] * d[3]; }
+};
+
+bool mul_ok(int64_t a, int64_t b, int64_t *r) { return !__builtin_mul_overflow(a, b, r); }
+bool add_ok(int64_t a, int64_t b, int64_t *r) { return !__builtin_add_overflow(a, b, r); }
+
+// Largest element offset addressed by a tensor, +1 (0 if it has no elements).
+bool span_of(const T4 &t, int64_t *span)
+{
+    for (int i = 0; i < 4; ++i)
+        if (t.d[i] == 0) {
+            *span = 0;
+            return true;
+        }
+    int64_t acc = 1;
+    for (int i = 0; i < 4; ++i) {
+        int64_t term;
+        if (!mul_ok(t.d[i] - 1, t.s[i], &term) || !add_ok(acc, term, &acc))
+            return false;
+    }
+    *span = acc;
+    return true;
+}
+
+conv_i8_status_t read_desc(const conv_i8_desc_t *desc, int32_t dtype, T4 *t)
+{
+    if (!desc)
+        return CONV_I8_ERR_NULL;
+    if (desc->ndim != 4)
+        return CONV_I8_ERR_RANK;
+    if (desc->dtype != dtype)
+        return CONV_I8_ERR_DTYPE;
+    for (int i = 0; i < 4; ++i) {
+        if (desc->dims[i] < 0)
+            return CONV_I8_ERR_DIMS;
+        t->d[i] = desc->dims[i];
+        // The stride of a dim of size 1 never multiplies a nonzero index.
+        t->s[i] = desc->dims[i] > 1 ? desc->strides[i] : 0;
+        if (t->s[i] < 0)
+            return CONV_I8_ERR_STRIDES;
+    }
+    return CONV_I8_OK;
+}
+
+// True when no two logical indices of t address the same element.
+bool non_overlapping(const T4 &t)
+{
+    for (int i = 0; i < 4; ++i)
+        if (t.d[i] == 0)
+            return true;  // no elements, nothing can overlap
+    int idx[4] = {0, 1, 2, 3};
+    std::sort(idx, idx + 4, [&](int a, int b) { return t.s[a] < t.s[b]; });
+    int64_t reach = 0;  // largest offset reachable by the dims sorted so far
+    for (int k = 0; k < 4; ++k) {
+        const int i = idx[k];
+        if (t.d[i] <= 1)
+            continue;
+        if (t.s[i] <= reach)
+            return false;
+        int64_t term;
+        if (!mul_ok(t.d[i] - 1, t.s[i], &term) || !add_ok(reach, term, &reach))
+            return false;
+    }
+    return true;
+}
+
+struct Problem {
+    T4 x, w, y;
+    int64_t N, C, H, W, K, R, S, P, Q;
+    int64_t pre[2], post[2], str[2], dil[2];
+};
+
+conv_i8_status_t read_params(const int64_t *pre, const int64_t *post, const int64_t *stride,
+                             const int64_t *dil, Problem *pb)
+{
+    if (!pre || !post || !stride || !dil)
+        return CONV_I8_ERR_NULL;
+    for (int i = 0; i < 2; ++i) {
+        if (pre[i] < 0 || post[i] < 0 || stride[i] < 1 || dil[i] < 1)
+            return CONV_I8_ERR_PARAM;
+        if (pre[i] > kI32Max / 4 || post[i] > kI32Max / 4 || stride[i] > kI32Max / 4 ||
+            dil[i] > kI32Max / 4)
+            return CONV_I8_ERR_UNSUPPORTED;
+        pb->pre[i] = pre[i];
+        pb->post[i] = post[i];
+        pb->str[i] = stride[i];
+        pb->dil[i] = dil[i];
+    }
+    return CONV_I8_OK;
+}
+
+// Output length of one spatial dim; -1 when the dilated window never fits.
+int64_t out_len(int64_t in, int64_t pre, int64_t post, int64_t f, int64_t stride, int64_t dil)
+{
+    const int64_t span = in + pre + post - dil * (f - 1) - 1;
+    if (span < 0)
+        return -1;
+    return span / stride + 1;
+}
+
+conv_i8_status_t analyze_inputs(const conv_i8_desc_t *image, const conv_i8_desc_t *filter,
+                                const int64_t *pre, const int64_t *post, const int64_t *stride,
+                                const int64_t *dil, Problem *pb)
+{
+    conv_i8_status_t st;
+    if ((st = read_desc(image, CONV_I8_DT_INT8, &pb->x)) != CONV_I8_OK)
+        return st;
+    if ((st = read_desc(filter, CONV_I8_DT_INT8, &pb->w)) != CONV_I8_OK)
+        return st;
+    if ((st = read_params(pre, post, stride, dil, pb)) != CONV_I8_OK)
+        return st;
+    pb->N = pb->x.d[0];
+    pb->C = pb->x.d[1];
+    pb->H = pb->x.d[2];
+    pb->W = pb->x.d[3];
+    pb->K = pb->w.d[0];
+    pb->R = pb->w.d[2];
+    pb->S = pb->w.d[3];
+    if (pb->R < 1 || pb->S < 1)
+        return CONV_I8_ERR_DIMS;
+    if (pb->w.d[1] != pb->C)
+        return CONV_I8_ERR_CHANNELS;
+    for (int i = 0; i < 4; ++i)
+        if (pb->x.d[i] > kI32Max / 4 || pb->w.d[i] > kI32Max / 4)
+            return CONV_I8_ERR_UNSUPPORTED;
+    int64_t crs;
+    if (!mul_ok(pb->C, pb->R * pb->S, &crs) || crs > CONV_I8_MAX_REDUCTION)
+        return CONV_I8_ERR_RANGE;
+    pb->P = out_len(pb->H, pb->pre[0], pb->post[0], pb->R, pb->str[0], pb->dil[0]);
+    pb->Q = out_len(pb->W, pb->pre[1], pb->post[1], pb->S, pb->str[1], pb->dil[1]);
+    if (pb->P < 1 || pb->Q < 1)
+        return CONV_I8_ERR_OUT_DIMS;
+    int64_t sp;
+    if (!span_of(pb->x, &sp) || !span_of(pb->w, &sp))
+        return CONV_I8_ERR_UNSUPPORTED;
+    return CONV_I8_OK;
+}
+
+conv_i8_status_t analyze(const conv_i8_desc_t *image, const conv_i8_desc_t *filter,
+                         const conv_i8_desc_t *out, const int64_t *pre, const int64_t *post,
+                         const int64_t *stride, const int64_t *dil, Problem *pb)
+{
+    conv_i8_status_t st = analyze_inputs(image, filter, pre, post, stride, dil, pb);
+    if (st != CONV_I8_OK)
+        return st;
+    // The output dtype is checked like every other field: an INT8 output
+    // descriptor is refused rather than written as saturated bytes.
+    if ((st = read_desc(out, CONV_I8_DT_INT32, &pb->y)) != CONV_I8_OK)
+        return st;
+    const int64_t want[4] = {pb->N, pb->K, pb->P, pb->Q};
+    for (int i = 0; i < 4; ++i)
+        if (pb->y.d[i] != want[i])
+            return CONV_I8_ERR_OUT_DIMS;
+    int64_t sp;
+    if (!span_of(pb->y, &sp))
+        return CONV_I8_ERR_UNSUPPORTED;
+    if (!non_overlapping(pb->y))
+        return CONV_I8_ERR_STRIDES;
+    return CONV_I8_OK;
+}
+
+// ---------------------------------------------------------------------------
+// Tile configurations instantiated for the implicit-GEMM kernel.
+// ---------------------------------------------------------------------------
+struct TileCfg {
+    int tm, tn, bk;
+    double eff;  // relative per-CU throughput of this tile shape (cost model)
+};
+
+const TileCfg kTiles[] = {
+    {64, 64, 64, 0.55},   {128, 64, 64, 0.75},  {64, 128, 64, 0.75}, {128, 128, 64, 0.9},
+    {128, 128, 128, 0.95}, {256, 128, 64, 1.0}, {128, 256, 64, 1.0},
+};
+constexpr int kNumTiles = sizeof(kTiles) / sizeof(kTiles[0]);
+
+template <int TM, int TN, int BK>
+void launch_cfg(bool pix_j, dim3 grid, hipStream_t stream, const IgemmArgs &a)
+{
+    if (pix_j)
+        hipLaunchKernelGGL((conv_igemm_kernel<TM, TN, BK, true>), grid, dim3(256), 0, stream, a);
+    else
+        hipLaunchKernelGGL((conv_igemm_kernel<TM, TN, BK, false>), grid, dim3(256), 0, stream, a);
+}
+
+void launch_igemm(int cfg, bool pix_j, dim3 grid, hipStream_t stream, const IgemmArgs &a)
+{
+    switch (cfg) {
+    case 0: launch_cfg<64, 64, 64>(pix_j, grid, stream, a); break;
+    case 1: launch_cfg<128, 64, 64>(pix_j, grid, stream, a); break;
+    case 2: launch_cfg<64, 128, 64>(pix_j, grid, stream, a); break;
+    case 3: launch_cfg<128, 128, 64>(pix_j, grid, stream, a); break;
+    case 4: launch_cfg<128, 128, 128>(pix_j, grid, stream, a); break;
+    case 5: launch_cfg<256, 128, 64>(pix_j, grid, stream, a); break;
+    case 6: launch_cfg<128, 256, 64>(pix_j, grid, stream, a); break;
+    default: break;
+    }
+}
+
+struct Plan {
+    bool repack_x = false, repack_w = false;
+    int64_t Cp = 0;                    // channels as the kernel reads them
+    size_t ws_x_off = 0, ws_w_off = 0, ws_bytes = 0;
+    // kernel view of the image and filter (byte strides; channel stride 1)
+    int64_t xsN = 0, xsH = 0, xsW = 0, x_img_span = 0;
+    int64_t wsK = 0, wsR = 0, wsS = 0, w_span = 0;
+    int cfg = 0;
+    bool pix_j = false;
+    bool blocked = true;
+    int64_t nstages = 0;
+    int64_t batch_chunk = 1;           // images per igemm launch
+};
+
+size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
+
+bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
+
+// Can the kernel read this tensor directly: channels innermost, C a multiple
+// of 16, and every 16-channel run 16-byte aligned?
+bool direct_ok(const T4 &t, const void *ptr)
+{
+    const int64_t C = t.d[1];
+    if (C % 16 != 0)
+        return false;
+    if (C > 1 && t.s[1] != 1)
+        return false;
+    for (int i : {0, 2, 3})
+        if (t.s[i] % 16 != 0)
+            return false;
+    return ptr == nullptr || aligned16(ptr);
+}
+
+const char *env_tile() { return getenv("CONV_I8_TILE"); }
+
+conv_i8_status_t make_plan(const Problem &pb, const void *x_ptr, const void *w_ptr, Plan *pl)
+{
+    pl->repack_x = !direct_ok(pb.x, x_ptr);
+    pl->repack_w = !direct_ok(pb.w, w_ptr);
+    pl->Cp = (pb.C + 15) / 16 * 16;
+
+    size_t off = 0;
+    if (pl->repack_x) {
+        int64_t b;
+        if (!mul_ok(pb.N * pb.H, pb.W * pl->Cp, &b))
+            return CONV_I8_ERR_UNSUPPORTED;
+        pl->ws_x_off = off;
+        off = align_up(off + (size_t)b, 256);
+        pl->xsW = pl->Cp;
+        pl->xsH = pb.W * pl->Cp;
+        pl->xsN = pb.H * pb.W * pl->Cp;
+        if (pb.N * pb.H > kI32Max || pb.W > 65535 * 64LL || pl->Cp > 65535 * 64LL)
+            return CONV_I8_ERR_UNSUPPORTED;
+    } else {
+        pl->xsN = pb.x.s[0];
+        pl->xsH = pb.x.s[2];
+        pl->xsW = pb.x.s[3];
+    }
+    if (pl->repack_w) {
+        int64_t b;
+        if (!mul_ok(pb.K * pb.R, pb.S * pl->Cp, &b))
+            return CONV_I8_ERR_UNSUPPORTED;
+        pl->ws_w_off = off;
+        off = align_up(off + (size_t)b, 256);
+        pl->wsS = pl->Cp;
+        pl->wsR = pb.S * pl->Cp;
+        pl->wsK = pb.R * pb.S * pl->Cp;
+        if (pb.K * pb.R > kI32Max || pb.S > 65535 * 64LL || pl->Cp > 65535 * 64LL)
+            return CONV_I8_ERR_UNSUPPORTED;
+    } else {
+        pl->wsK = pb.w.s[0];
+        pl->wsR = pb.w.s[2];
+        pl->wsS = pb.w.s[3];
+    }
+    pl->ws_bytes = off;
+
+    // Span of one image in the kernel's view, including every tap offset the
+    // kernel forms (padding and dilation may reach past the image before the
+    // bounds test rejects the tap): all must fit in 31 bits.
+    {
+        T4 v{};
+        v.d[0] = 1; v.d[1] = pl->Cp; v.d[2] = pb.H; v.d[3] = pb.W;
+        v.s[0] = 0; v.s[1] = 1; v.s[2] = pb.H > 1 ? pl->xsH : 0; v.s[3] = pb.W > 1 ? pl->xsW : 0;
+        int64_t sp;
+        if (!span_of(v, &sp) || sp > kI32Max)
+            return CONV_I8_ERR_UNSUPPORTED;
+        pl->x_img_span = sp;
+        int64_t reach_h, reach_w;
+        if (!mul_ok(pb.H + pb.pre[0] + pb.post[0] + 1, pl->xsH, &reach_h) ||
+            !mul_ok(pb.W + pb.pre[1] + pb.post[1] + 1, pl->xsW, &reach_w) ||
+            reach_h + reach_w + pl->Cp > kI32Max)
+            return CONV_I8_ERR_UNSUPPORTED;
+        T4 f{};
+        f.d[0] = pb.K; f.d[1] = pl->Cp; f.d[2] = pb.R; f.d[3] = pb.S;
+        f.s[0] = pb.K > 1 ? pl->wsK : 0; f.s[1] = 1;
+        f.s[2] = pb.R > 1 ? pl->wsR : 0; f.s[3] = pb.S > 1 ? pl->wsS : 0;
+        if (!span_of(f, &sp) || sp > kI32Max)
+            return CONV_I8_ERR_UNSUPPORTED;
+        pl->w_span = sp;
+    }
+
+    // Images per launch: the image bytes one launch addresses, and its
+    // N*P*Q rows, must stay below 2^31.
+    {
+        const int64_t pq = pb.P * pb.Q;
+        int64_t nb = std::max<int64_t>(1, pb.N);
+        if (pl->xsN > 0)
+            nb = std::min<int64_t>(nb, (kI32Max - pl->x_img_span) / pl->xsN + 1);
+        nb = std::min<int64_t>(nb, kI32Max / pq);
+        if (nb < 1)
+            return CONV_I8_ERR_UNSUPPORTED;
+        int64_t t;
+        if (!mul_ok(nb, pl->xsN, &t) || nb * pq > kI32Max)
+            return CONV_I8_ERR_UNSUPPORTED;
+        pl->batch_chunk = nb;
+    }
+
+    // Output layout: make the MFMA column (lanes) walk the contiguous dim.
+    const int64_t oK = pb.y.s[1], oQ = pb.y.s[3];
+    if (oK == 1)
+        pl->pix_j = false;
+    else if (oQ == 1)
+        pl->pix_j = true;
+    else
+        pl->pix_j = oQ != 0 && (oK == 0 || oQ < oK);
+
+    // Tile choice: rounds of 256 tiles times tile work over relative efficiency.
+    const int64_t cc = pl->Cp / 16;
+    const int64_t M = std::min(pb.N, pl->batch_chunk) * pb.P * pb.Q;
+    int best = -1;
+    double best_cost = 0;
+    const char *forced = env_tile();
+    for (int i = 0; i < kNumTiles; ++i) {
+        const TileCfg &c = kTiles[i];
+        if (forced) {
+            char name[32];
+            snprintf(name, sizeof name, "%dx%dx%d", c.tm, c.tn, c.bk);
+            if (strcmp(forced, name) != 0)
+                continue;
+        }
+        const int cps = c.bk / 16;
+        double eff = c.eff;
+        if (cc % cps != 0) {
+            // flat order: the tail stage is partly empty
+            const int64_t chunks = pb.R * pb.S * cc;
+            const int64_t stages = (chunks + cps - 1) / cps;
+            eff *= chunks > 0 ? (double)chunks / (double)(stages * cps) : 1.0;
+        }
+        const int64_t tiles = ((M + c.tm - 1) / c.tm) * ((pb.K + c.tn - 1) / c.tn);
+        const int64_t rounds = (tiles + kCUs - 1) / kCUs;
+        const double cost = (double)rounds * c.tm * c.tn / eff;
+        if (best < 0 || cost < best_cost - 1e-9) {
+            best = i;
+            best_cost = cost;
+        }
+    }
+    if (best < 0)
+        best = 3;  // unknown CONV_I8_TILE value: default shape
+    pl->cfg = best;
+    const int cps = kTiles[best].bk / 16;
+    pl->blocked = cc % cps == 0;
+    pl->nstages = pl->blocked ? pb.R * pb.S * (cc / cps) : (pb.R * pb.S * cc + cps - 1) / cps;
+    return CONV_I8_OK;
+}
+
+std::string describe(const Problem &pb, const Plan &pl)
+{
+    const TileCfg &c = kTiles[pl.cfg];
+    const int64_t M = pb.N * pb.P * pb.Q;
+    const int64_t tiles = ((M + c.tm - 1) / c.tm) * ((pb.K + c.tn - 1) / c.tn);
+    char buf[512];
+    snprintf(buf, sizeof buf,
+             "repack_image=%d repack_filter=%d Cp=%lld tile=%dx%dx%d order=%s stages=%lld "
+             "lanes=%s tiles=%lld batch_chunk=%lld workspace=%zu",
+             (int)pl.repack_x, (int)pl.repack_w, (long long)pl.Cp, c.tm, c.tn, c.bk,
+             pl.blocked ? "blocked" : "flat", (long long)pl.nstages,
+             pl.pix_j ? "pixels" : "channels", (long long)tiles, (long long)pl.batch_chunk,
+             pl.ws_bytes);
+    return buf;
+}
+
+bool log_enabled()
+{
+    const char *e = getenv("CONV_I8_LOG");
+    return e && *e && strcmp(e, "0") != 0;
+}
+
+conv_i8_status_t launch_repack(const T4 &t, const int8_t *src, int8_t *dst, int64_t Cp,
+                               hipStream_t stream)
+{
+    RepackArgs r{};
+    r.src = src;
+    r.s0 = t.s[0];
+    r.s1 = t.s[1];
+    r.s2 = t.s[2];
+    r.s3 = t.s[3];
+    r.A = (int)t.d[0];
+    r.C = (int)t.d[1];
+    r.Y = (int)t.d[2];
+    r.X = (int)t.d[3];
+    r.Cp = (int)Cp;
+    // Walk x with the lanes when it is the cheaper (smaller) stride.
+    r.x_fast = (t.d[1] <= 1) || (t.d[3] > 1 && t.s[3] <= t.s[1]);
+    r.dst = dst;
+    const int64_t ay = t.d[0] * t.d[2];
+    if (ay == 0 || t.d[3] == 0 || Cp == 0)
+        return CONV_I8_OK;
+    dim3 grid((unsigned)ay, (unsigned)((t.d[3] + 63) / 64), (unsigned)((Cp + 63) / 64));
+    hipLaunchKernelGGL(repack_to_channels_last_kernel, grid, dim3(256), 0, stream, r);
+    return hipGetLastError() == hipSuccess ? CONV_I8_OK : CONV_I8_ERR_HIP;
+}
+
+conv_i8_status_t run(const Problem &pb, const Plan &pl, const void *x_ptr, const void *w_ptr,
+                     void *y_ptr, void *ws, hipStream_t stream)
+{
+    const int8_t *x = (const int8_t *)x_ptr;
+    const int8_t *w = (const int8_t *)w_ptr;
+    int8_t *wsb = (int8_t *)ws;
+    conv_i8_status_t st;
+    if (pl.repack_x && pb.C > 0) {
+        if ((st = launch_repack(pb.x, x, wsb + pl.ws_x_off, pl.Cp, stream)) != CONV_I8_OK)
+            return st;
+        x = wsb + pl.ws_x_off;
+    }
+    if (pl.repack_w && pb.C > 0) {
+        if ((st = launch_repack(pb.w, w, wsb + pl.ws_w_off, pl.Cp, stream)) != CONV_I8_OK)
+            return st;
+        w = wsb + pl.ws_w_off;
+    }
+    const TileCfg &c = kTiles[pl.cfg];
+    IgemmArgs a{};
+    a.flt = w;
+    a.flt_range = (int)pl.w_span;
+    a.H = (int)pb.H;
+    a.W = (int)pb.W;
+    a.C = (int)pl.Cp;
+    a.sH = (int)pl.xsH;
+    a.sW = (int)pl.xsW;
+    a.K = (int)pb.K;
+    a.R = (int)pb.R;
+    a.S = (int)pb.S;
+    a.fK = (int)pl.wsK;
+    a.fR = (int)pl.wsR;
+    a.fS = (int)pl.wsS;
+    a.P = (int)pb.P;
+    a.Q = (int)pb.Q;
+    a.PQ = (int)(pb.P * pb.Q);
+    a.strH = (int)pb.str[0];
+    a.strW = (int)pb.str[1];
+    a.dilH = (int)pb.dil[0];
+    a.dilW = (int)pb.dil[1];
+    a.padH = (int)pb.pre[0];
+    a.padW = (int)pb.pre[1];
+    a.oN = pb.y.s[0];
+    a.oK = pb.y.s[1];
+    a.oP = pb.y.s[2];
+    a.oQ = pb.y.s[3];
+    a.nstages = pb.C > 0 ? (int)pl.nstages : 0;
+    a.cc = (int)(pl.Cp / 16);
+    a.blocked = pl.blocked ? 1 : 0;
+    a.tiles_n = (int)((pb.K + c.tn - 1) / c.tn);
+    for (int64_t n0 = 0; n0 < pb.N; n0 += pl.batch_chunk) {
+        const int64_t nb = std::min(pl.batch_chunk, pb.N - n0);
+        a.img = x + n0 * pl.xsN;
+        a.img_range = (int)((nb - 1) * pl.xsN + pl.x_img_span);
+        a.out = (int32_t *)y_ptr + n0 * pb.y.s[0];
+        a.N = (int)nb;
+        a.sN = (int)pl.xsN;
+        a.M = (int)(nb * pb.P * pb.Q);
+        const int64_t tiles = ((a.M + c.tm - 1) / c.tm) * (int64_t)a.tiles_n;
+        if (tiles == 0)
+            continue;
+        a.tiles = (int)tiles;
+        launch_igemm(pl.cfg, pl.pix_j, dim3((unsigned)tiles), stream, a);
+        if (hipGetLastError() != hipSuccess)
+            return CONV_I8_ERR_HIP;
+    }
+    return CONV_I8_OK;
+}
+
+conv_i8_status_t prepare(const conv_i8_desc_t *image, const void *image_ptr,
+                         const conv_i8_desc_t *filter, const void *filter_ptr,
+                         const conv_i8_desc_t *out, const int64_t *pre, const int64_t *post,
+                         const int64_t *stride, const int64_t *dil, Problem *pb, Plan *pl)
+{
+    conv_i8_status_t st = analyze(image, filter, out, pre, post, stride, dil, pb);
+    if (st != CONV_I8_OK)
+        return st;
+    return make_plan(*pb, image_ptr, filter_ptr, pl);
+}
+
+conv_i8_status_t check_ptrs(const Problem &pb, const void *x, const void *w, const void *y)
+{
+    if (pb.y.elems() == 0)
+        return CONV_I8_OK;
+    if (!y)
+        return CONV_I8_ERR_NULL;
+    if (pb.C > 0 && ((pb.x.elems() > 0 && !x) || (pb.w.elems() > 0 && !w)))
+        return CONV_I8_ERR_NULL;
+    return CONV_I8_OK;
+}
+
+}  // namespace
+}  // namespace convi8
+
+using namespace convi8;
+
+extern "C" {
+
+conv_i8_status_t conv_fprop_i8_out_dims(const conv_i8_desc_t *image, const conv_i8_desc_t *filter,
+                                        const int64_t pre_padding[2], const int64_t post_padding[2],
+                                        const int64_t stride[2], const int64_t dilation[2],
+                                        int64_t out_dims[4])
+{
+    if (!out_dims)
+        return CONV_I8_ERR_NULL;
+    Problem pb;
+    conv_i8_status_t st = analyze_inputs(image, filter, pre_padding, post_padding, stride, dilation, &pb);
+    if (st != CONV_I8_OK)
+        return st;
+    out_dims[0] = pb.N;
+    out_dims[1] = pb.K;
+    out_dims[2] = pb.P;
+    out_dims[3] = pb.Q;
+    return CONV_I8_OK;
+}
+
+conv_i8_status_t conv_fprop_i8_workspace_size(const conv_i8_desc_t *image, const void *image_ptr,
+                                              const conv_i8_desc_t *filter, const void *filter_ptr,
+                                              const conv_i8_desc_t *out,
+                                              const int64_t pre_padding[2],
+                                              const int64_t post_padding[2],
+                                              const int64_t stride[2], const int64_t dilation[2],
+                                              size_t *workspace_bytes)
+{
+    if (!workspace_bytes)
+        return CONV_I8_ERR_NULL;
+    Problem pb;
+    Plan pl;
+    conv_i8_status_t st = prepare(image, image_ptr, filter, filter_ptr, out, pre_padding,
+                                  post_padding, stride, dilation, &pb, &pl);
+    if (st != CONV_I8_OK)
+        return st;
+    *workspace_bytes = pb.y.elems() == 0 || pb.C == 0 ? 0 : pl.ws_bytes;
+    return CONV_I8_OK;
+}
+
+conv_i8_status_t conv_fprop_i8_plan(const conv_i8_desc_t *image, const void *image_ptr,
+                                    const conv_i8_desc_t *filter, const void *filter_ptr,
+                                    const conv_i8_desc_t *out, const int64_t pre_padding[2],
+                                    const int64_t post_padding[2], const int64_t stride[2],
+                                    const int64_t dilation[2], char *buf, size_t len)
+{
+    if (!buf || len == 0)
+        return CONV_I8_ERR_NULL;
+    Problem pb;
+    Plan pl;
+    conv_i8_status_t st = prepare(image, image_ptr, filter, filter_ptr, out, pre_padding,
+                                  post_padding, stride, dilation, &pb, &pl);
+    if (st != CONV_I8_OK)
+        return st;
+    snprintf(buf, len, "%s", describe(pb, pl).c_str());
+    return CONV_I8_OK;
+}
+
+conv_i8_status_t conv_fprop_i8_ws(const conv_i8_desc_t *image, const void *image_ptr,
+                                  const conv_i8_desc_t *filter, const void *filter_ptr,
+                                  const conv_i8_desc_t *out, void *out_ptr,
+                                  const int64_t pre_padding[2], const int64_t post_padding[2],
+                                  const int64_t stride[2], const int64_t dilation[2],
+                                  void *workspace, size_t workspace_bytes, void *stream)
+{
+    Problem pb;
+    Plan pl;
+    conv_i8_status_t st = prepare(image, image_ptr, filter, filter_ptr, out, pre_padding,
+                                  post_padding, stride, dilation, &pb, &pl);
+    if (st != CONV_I8_OK)
+        return st;
+    if ((st = check_ptrs(pb, image_ptr, filter_ptr, out_ptr)) != CONV_I8_OK)
+        return st;
+    if (pb.y.elems() == 0)
+        return CONV_I8_OK;
+    const size_t need = pb.C == 0 ? 0 : pl.ws_bytes;
+    if (workspace_bytes < need)
+        return CONV_I8_ERR_WORKSPACE;
+    if (need > 0 && !workspace)
+        return CONV_I8_ERR_NULL;
+    if (need > 0 && ((uintptr_t)workspace & 255u) != 0)
+        return CONV_I8_ERR_WORKSPACE;
+    if (log_enabled())
+        fprintf(stderr, "conv_i8: %s\n", describe(pb, pl).c_str());
+    return run(pb, pl, image_ptr, filter_ptr, out_ptr, workspace, (hipStream_t)stream);
+}
+
+conv_i8_status_t conv_fprop_i8(const conv_i8_desc_t *image, const void *image_ptr,
+                               const conv_i8_desc_t *filter, const void *filter_ptr,
+                               const conv_i8_desc_t *out, void *out_ptr,
+                               const int64_t pre_padding[2], const int64_t post_padding[2],
+                               const int64_t stride[2], const int64_t dilation[2], void *stream)
+{
+    Problem pb;
+    Plan pl;
+    conv_i8_status_t st = prepare(image, image_ptr, filter, filter_ptr, out, pre_padding,
+                                  post_padding, stride, dilation, &pb, &pl);
+    if (st != CONV_I8_OK)
+        return st;
+    if ((st = check_ptrs(pb, image_ptr, filter_ptr, out_ptr)) != CONV_I8_OK)
+        return st;
+    if (pb.y.elems() == 0)
+        return CONV_I8_OK;
+    const size_t need = pb.C == 0 ? 0 : pl.ws_bytes;
+    hipStream_t s = (hipStream_t)stream;
+    void *ws = nullptr;
+    if (need > 0 && hipMallocAsync(&ws, need, s) != hipSuccess)
+        return CONV_I8_ERR_HIP;
+    if (log_enabled())
+        fprintf(stderr, "conv_i8: %s\n", describe(pb, pl).c_str());
+    st = run(pb, pl, image_ptr, filter_ptr, out_ptr, ws, s);
+    if (ws && hipFreeAsync(ws, s) != hipSuccess && st == CONV_I8_OK)
+        st = CONV_I8_ERR_HIP;
+    return st;
+}
+
+const char *conv_i8_status_string(conv_i8_status_t status)
+{
+    switch (status) {
+    case CONV_I8_OK: return "CONV_I8_OK";
+    case CONV_I8_ERR_NULL: return "CONV_I8_ERR_NULL: a required pointer is NULL";
+    case CONV_I8_ERR_DTYPE: return "CONV_I8_ERR_DTYPE: image/filter must be INT8 and the output INT32";
+    case CONV_I8_ERR_RANK: return "CONV_I8_ERR_RANK: descriptors must have ndim == 4";
+    case CONV_I8_ERR_DIMS: return "CONV_I8_ERR_DIMS: negative dim, or filter R or S < 1";
+    case CONV_I8_ERR_PARAM: return "CONV_I8_ERR_PARAM: stride and dilation must be >= 1, padding >= 0";
+    case CONV_I8_ERR_CHANNELS: return "CONV_I8_ERR_CHANNELS: image C != filter C";
+    case CONV_I8_ERR_OUT_DIMS: return "CONV_I8_ERR_OUT_DIMS: output dims must be [N, K, P, Q] with P, Q >= 1";
+    case CONV_I8_ERR_STRIDES: return "CONV_I8_ERR_STRIDES: negative stride or self-overlapping output";
+    case CONV_I8_ERR_RANGE: return "CONV_I8_ERR_RANGE: C*R*S > 131071, int32 sums would not be exact";
+    case CONV_I8_ERR_WORKSPACE: return "CONV_I8_ERR_WORKSPACE: workspace too small or not 256-byte aligned";
+    case CONV_I8_ERR_UNSUPPORTED: return "CONV_I8_ERR_UNSUPPORTED: a single image or the filter spans >= 2 GiB";
+    case CONV_I8_ERR_HIP: return "CONV_I8_ERR_HIP: a HIP runtime call failed";
+    }
+    return "unknown conv_i8 status";
+}
+
+}  // extern "C"

@@ -89,6 +89,11 @@ int oracle_out_dims(const int64_t xdims[4], const int64_t wdims[4],
     return ORACLE_OK;
 }
 
+static int64_t oracle_elems(const int64_t d[4])
+{
+    return d[0] * d[1] * d[2] * d[3];
+}
+
 /* One output element, summed over the filter window in the naive loop's order. */
 static int64_t oracle_point(const int8_t *x, const int64_t xd[4], const int64_t xs[4],
                             const int8_t *w, const int64_t wd[4], const int64_t ws[4],
@@ -128,11 +133,15 @@ int oracle_conv_fprop(const int8_t *x, const int64_t xdims[4], const int64_t xst
                       const int64_t stride[2], const int64_t dil[2], int nthreads)
 {
     int64_t want[4];
-    if (!x || !w || !y || !xstr || !wstr || !ystr)
+    if (!xstr || !wstr || !ystr)
         return ORACLE_ERR_ARG;
     int rc = oracle_out_dims(xdims, wdims, pre, post, stride, dil, want);
     if (rc != ORACLE_OK)
         return rc;
+    /* a tensor with no elements is never read, so it may have no storage */
+    if ((!x && oracle_elems(xdims) > 0) || (!w && oracle_elems(wdims) > 0) ||
+        (!y && oracle_elems(ydims) > 0))
+        return ORACLE_ERR_ARG;
     for (int i = 0; i < 4; ++i)
         if (ydims[i] != want[i])
             return ORACLE_ERR_OUT_DIMS;
@@ -175,11 +184,13 @@ int oracle_conv_fprop_points(const int8_t *x, const int64_t xdims[4], const int6
                              const int64_t *idx, int64_t npts, int64_t *out)
 {
     int64_t yd[4];
-    if (!x || !w || !xstr || !wstr || (npts > 0 && (!idx || !out)) || npts < 0)
+    if (!xstr || !wstr || (npts > 0 && (!idx || !out)) || npts < 0)
         return ORACLE_ERR_ARG;
     int rc = oracle_out_dims(xdims, wdims, pre, post, stride, dil, yd);
     if (rc != ORACLE_OK)
         return rc;
+    if ((!x && oracle_elems(xdims) > 0) || (!w && oracle_elems(wdims) > 0))
+        return ORACLE_ERR_ARG;
     for (int64_t i = 0; i < npts; ++i) {
         const int64_t *t = idx + 4 * i;
         for (int d = 0; d < 4; ++d)

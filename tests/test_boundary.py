@@ -1,0 +1,192 @@
+"""The C-ABI boundary on the CPU: the library loads, exports every declared
+symbol, and refuses bad arguments on the host before touching a device."""
+import ctypes
+import os
+import re
+
+import pytest
+import torch
+
+import int8_convolution_forward_amd as ci8
+import workloads as wl
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "conv_i8.h")
+
+# A non-null, 256-byte aligned address that is never dereferenced: every call
+# below fails validation before any HIP call is made.
+FAKE = ctypes.c_void_p(0x1000000)
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(conv_\w+)\s*\(", text, flags=re.M)))
+
+
+def test_every_declared_symbol_is_exported():
+    names = declared_functions()
+    assert {"conv_fprop_i8", "conv_fprop_i8_ws", "conv_fprop_i8_out_dims",
+            "conv_fprop_i8_workspace_size", "conv_fprop_i8_plan", "conv_i8_status_string"} <= set(names)
+    lib = ctypes.CDLL(ci8.LIB_PATH)
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_status_strings():
+    for code, name in ci8.STATUS.items():
+        assert ci8.status_string(code).startswith(name)
+    assert "unknown" in ci8.status_string(99)
+
+
+def _args(c: wl.ConvCase, **over):
+    a = dict(x=ci8.desc(c.image.dims, c.image.strides, ci8.DT_INT8),
+             w=ci8.desc(c.filter.dims, c.filter.strides, ci8.DT_INT8),
+             y=ci8.desc(c.out.dims, c.out.strides, ci8.DT_INT32),
+             pre=c.pre, post=c.post, stride=c.stride, dil=c.dilation)
+    a.update(over)
+    return a
+
+
+def _call_ws(a, ws_bytes=0, ws=None, xp=FAKE, wp=FAKE, yp=FAKE):
+    p = ci8._params(a["pre"], a["post"], a["stride"], a["dil"], None)
+    return ci8.lib.conv_fprop_i8_ws(
+        ctypes.byref(a["x"]) if a["x"] is not None else None, xp,
+        ctypes.byref(a["w"]) if a["w"] is not None else None, wp,
+        ctypes.byref(a["y"]) if a["y"] is not None else None, yp,
+        *p, ws, ctypes.c_size_t(ws_bytes), None)
+
+
+@pytest.mark.parametrize("name", wl.CASE_ORDER)
+def test_out_dims_match_case_table(name):
+    c = wl.case(name)
+    d = _args(c)
+    assert ci8.conv_fprop_i8_out_dims(d["x"], d["w"], c.pre, c.post, c.stride, c.dilation) == c.out.dims
+
+
+def test_printed_shapes():
+    import json
+    with open(os.path.join(ROOT, "tests", "golden", "printed_shapes.json")) as f:
+        for g in json.load(f)["cases"]:
+            x = ci8.desc(g["image"], wl.contiguous_strides(g["image"]), ci8.DT_INT8)
+            w = ci8.desc(g["filter"], wl.contiguous_strides(g["filter"]), ci8.DT_INT8)
+            assert list(ci8.conv_fprop_i8_out_dims(x, w, g["pre"], g["post"], g["stride"],
+                                                    g["dilation"])) == g["out"]
+
+
+def test_int8_output_is_refused():
+    """The forum repro left Y at the graph's INT8 io type and got saturated
+    int8 bytes in its int32 buffer; here an INT8 output descriptor is an error."""
+    c = wl.case("tiny_5x5_r3")
+    a = _args(c, y=ci8.desc(c.out.dims, c.out.strides, ci8.DT_INT8))
+    assert _call_ws(a) == 2  # CONV_I8_ERR_DTYPE
+
+
+def test_forum_strides_are_equivalent():
+    """With C = 1 the channel stride never multiplies a nonzero index: the
+    repro's [25,1,5,1] and the answer's [25,25,5,1] describe the same tensor."""
+    c = wl.case("tiny_5x5_r3")
+    p1 = ci8.conv_fprop_i8_plan(ci8.desc((1, 1, 5, 5), (25, 1, 5, 1), 1), ci8.desc((1, 1, 3, 3), (9, 1, 3, 1), 1))
+    p2 = ci8.conv_fprop_i8_plan(ci8.desc((1, 1, 5, 5), (25, 25, 5, 1), 1), ci8.desc((1, 1, 3, 3), (9, 9, 3, 1), 1))
+    assert p1 == p2
+
+
+@pytest.mark.parametrize("over,code", [
+    (dict(x=None), 1),
+    (dict(y=None), 1),
+    (dict(pre=(-1, 0)), 5),
+    (dict(post=(0, -2)), 5),
+    (dict(stride=(0, 1)), 5),
+    (dict(dil=(1, 0)), 5),
+])
+def test_param_errors(over, code):
+    assert _call_ws(_args(wl.case("downsample_s2_n8_c64_56"), **over)) == code
+
+
+def test_descriptor_errors():
+    c = wl.case("downsample_s2_n8_c64_56")
+    x, w, y = c.image, c.filter, c.out
+    D = ci8.desc
+    cases = [
+        (dict(x=D(x.dims, x.strides, ci8.DT_INT8, ndim=3)), 3),
+        (dict(x=D(x.dims, x.strides, ci8.DT_INT32)), 2),
+        (dict(w=D(w.dims, w.strides, 0)), 2),
+        (dict(y=D(y.dims, y.strides, ci8.DT_INT8)), 2),
+        (dict(x=D((8, 64, -1, 56), x.strides, ci8.DT_INT8)), 4),
+        (dict(w=D((64, 64, 0, 3), w.strides, ci8.DT_INT8)), 4),
+        (dict(w=D((64, 32, 3, 3), w.strides, ci8.DT_INT8)), 6),
+        (dict(y=D((8, 64, 28, 29), y.strides, ci8.DT_INT32)), 7),
+        (dict(y=D((8, 32, 28, 28), y.strides, ci8.DT_INT32)), 7),
+        (dict(x=D((8, 64, 1, 1), (64, 1, 64, 64), ci8.DT_INT8), y=D((8, 64, 2, 2), (256, 1, 128, 64), ci8.DT_INT32)), 7),
+        (dict(x=D(x.dims, (200704, 1, 3584, -64), ci8.DT_INT8)), 8),
+        (dict(y=D(y.dims, (50176, 1, 1792, 32), ci8.DT_INT32)), 8),   # q and k overlap
+        (dict(y=D(y.dims, (0, 1, 1792, 64), ci8.DT_INT32)), 8),       # batch overlaps
+    ]
+    for over, code in cases:
+        assert _call_ws(_args(c, **over)) == code, (over, code)
+
+
+def test_reduction_range():
+    D = ci8.desc
+    ok_c, bad_c = 14563, 14564      # 14563*9 = 131067 <= 131071 < 14564*9
+    for C, code in [(ok_c, 10), (bad_c, 9)]:
+        a = dict(x=D((1, C, 3, 3), (9 * C, 9, 3, 1), 1), w=D((1, C, 3, 3), (9 * C, 9, 3, 1), 1),
+                 y=D((1, 1, 1, 1), (1, 1, 1, 1), 2), pre=0, post=0, stride=1, dil=1)
+        # the allowed size gets as far as the workspace check (NCHW needs a repack)
+        assert _call_ws(a) == code
+
+
+def test_workspace_errors():
+    c = wl.case("dilated_asym_n16_c96_64x48")
+    a = _args(c)
+    need = ci8.conv_fprop_i8_workspace_size(a["x"], a["w"], a["y"], c.pre, c.post, c.stride, c.dilation)
+    assert need >= 16 * 64 * 48 * 96 + 192 * 15 * 96
+    assert _call_ws(a, ws_bytes=need - 1, ws=FAKE) == 10
+    assert _call_ws(a, ws_bytes=need, ws=None) == 1
+    assert _call_ws(a, ws_bytes=need, ws=ctypes.c_void_p(0x1000010)) == 10   # misaligned
+
+
+@pytest.mark.parametrize("name,repack_image,repack_filter,order", [
+    ("tiny_5x5_r3", "1", "1", "flat"),
+    ("downsample_s2_n8_c64_56", "0", "0", "blocked"),
+    ("pointwise_1x1_n32_c256_56", "0", "0", "blocked"),
+    ("bottleneck_3x3_n32_c128_28", "0", "0", "blocked"),
+    ("large_channel_n64_c512_14", "0", "0", "blocked"),
+    ("dilated_asym_n16_c96_64x48", "1", "1", None),
+])
+def test_plans(name, repack_image, repack_filter, order):
+    c = wl.case(name)
+    a = _args(c)
+    f = ci8.plan_fields(ci8.conv_fprop_i8_plan(a["x"], a["w"], a["y"], c.pre, c.post, c.stride, c.dilation))
+    assert f["repack_image"] == repack_image and f["repack_filter"] == repack_filter
+    if order:
+        assert f["order"] == order
+    need = ci8.conv_fprop_i8_workspace_size(a["x"], a["w"], a["y"], c.pre, c.post, c.stride, c.dilation)
+    assert (need == 0) == (repack_image == "0" and repack_filter == "0")
+    # channel-innermost NHWC output -> lanes walk channels; NCHW -> pixels
+    assert f["lanes"] == ("channels" if c.out.strides[1] == 1 else "pixels")
+
+
+def test_empty_problems_are_ok_without_device_work():
+    D = ci8.desc
+    # N = 0: nothing to write, no pointers needed
+    a = dict(x=D((0, 16, 5, 5), (400, 1, 80, 16), 1), w=D((4, 16, 3, 3), (144, 1, 48, 16), 1),
+             y=D((0, 4, 3, 3), (36, 1, 12, 4), 2), pre=0, post=0, stride=1, dil=1)
+    assert _call_ws(a, xp=None, wp=None, yp=None) == 0
+    # K = 0
+    a = dict(x=D((2, 16, 5, 5), (400, 1, 80, 16), 1), w=D((0, 16, 3, 3), (144, 1, 48, 16), 1),
+             y=D((2, 0, 3, 3), (0, 1, 0, 0), 2), pre=0, post=0, stride=1, dil=1)
+    assert _call_ws(a, xp=None, wp=None, yp=None) == 0
+
+
+def test_window_larger_than_padded_image():
+    D = ci8.desc
+    x, w = D((1, 16, 2, 2), (64, 1, 32, 16), 1), D((1, 16, 3, 3), (144, 1, 48, 16), 1)
+    with pytest.raises(ci8.ConvI8Error) as e:
+        ci8.conv_fprop_i8_out_dims(x, w)
+    assert e.value.name == "CONV_I8_ERR_OUT_DIMS"
+    # C division would truncate (-1)/2 to 0 and claim one output row
+    x = D((1, 16, 2, 5), (160, 1, 80, 16), 1)
+    w = D((1, 16, 4, 3), (192, 1, 48, 16), 1)
+    with pytest.raises(ci8.ConvI8Error):
+        ci8.conv_fprop_i8_out_dims(x, w, stride=(2, 1))

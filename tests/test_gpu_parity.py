@@ -1,0 +1,311 @@
+"""GPU parity: the HIP library (through the C ABI) against the CPU oracle.
+
+Every comparison is bit-exact over the whole output, and the output buffer is
+pre-filled with a sentinel so that unwritten elements, and writes outside the
+descriptor's footprint (gaps of strided outputs, guard bands), are caught.
+"""
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads as wl
+
+pytestmark = pytest.mark.gpu
+
+GUARD = 64  # sentinel elements before and after every output footprint
+
+
+@pytest.fixture(scope="module")
+def ci8():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import int8_convolution_forward_amd as m
+    return m
+
+
+def _dev():
+    return torch.device("cuda:0")
+
+
+def _to_dev(storage: torch.Tensor, spec: wl.TensorSpec):
+    return wl.to_device(storage, spec, _dev())[1]
+
+
+def _out_with_guards(spec: wl.TensorSpec):
+    size = spec.storage_size
+    buf = torch.full((size + 2 * GUARD,), wl.SENTINEL, dtype=torch.int32, device=_dev())
+    view = torch.as_strided(buf, spec.dims, spec.strides, spec.offset + GUARD)
+    return buf, view
+
+
+def _covered_mask(spec: wl.TensorSpec) -> torch.Tensor:
+    size = spec.storage_size
+    mask = torch.zeros(size + 2 * GUARD, dtype=torch.bool)
+    if all(d > 0 for d in spec.dims):
+        idx = torch.as_strided(torch.arange(size + 2 * GUARD), spec.dims, spec.strides, spec.offset + GUARD)
+        mask[idx.reshape(-1)] = True
+    return mask
+
+
+def run_and_check(ci8, x_storage, xspec, w_storage, wspec, ospec, pre, post, stride, dil,
+                  label="", entry="ws"):
+    """Run the library on device copies and compare with the oracle on the CPU copies."""
+    x_cpu = torch.as_strided(x_storage, xspec.dims, xspec.strides, xspec.offset)
+    w_cpu = torch.as_strided(w_storage, wspec.dims, wspec.strides, wspec.offset)
+    xg = _to_dev(x_storage, xspec)
+    wg = _to_dev(w_storage, wspec)
+    buf, og = _out_with_guards(ospec)
+    print(f"[gpu] {label} x={xspec.dims}/{xspec.strides} w={wspec.dims}/{wspec.strides} "
+          f"y={ospec.dims}/{ospec.strides} pre={pre} post={post} stride={stride} dil={dil} "
+          f"entry={entry} tile={os.environ.get('CONV_I8_TILE', '-')}", flush=True)
+    if entry == "ws":
+        ci8.conv_fprop_i8(xg, wg, og, pre, post, stride, dil)
+    else:
+        ci8.conv_fprop_i8_plain(xg, wg, og, pre, post, stride, dil)
+    torch.cuda.synchronize()
+    got = buf.cpu()
+    ref_buf = torch.full_like(got, wl.SENTINEL)
+    ref_view = torch.as_strided(ref_buf, ospec.dims, ospec.strides, ospec.offset + GUARD)
+    if all(d > 0 for d in ospec.dims):
+        oracle.conv_fprop(x_cpu, w_cpu, pre, post, stride, dil, out=ref_view)
+    if not torch.equal(got, ref_buf):
+        mask = _covered_mask(ospec)
+        diff = got != ref_buf
+        raise AssertionError(
+            f"{label}: {int((diff & mask).sum())} computed outputs differ, "
+            f"{int((diff & ~mask).sum())} writes outside the footprint")
+    return got
+
+
+# ---------------------------------------------------------------------------
+# The workloads at full size, three seeds each.
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("j", [0, 1, 2])
+@pytest.mark.parametrize("name", wl.CASE_ORDER)
+def test_workload_parity(ci8, name, j):
+    c = wl.case(name)
+    d = wl.make_inputs(c, c.seed_base + j)
+    run_and_check(ci8, d["x_storage"], c.image, d["w_storage"], c.filter, c.out,
+                  c.pre, c.post, c.stride, c.dilation, label=f"{name} seed {c.seed_base + j}")
+
+
+@pytest.mark.parametrize("name", ["tiny_5x5_r3", "dilated_asym_n16_c96_64x48"])
+def test_plain_entry_allocates_its_workspace(ci8, name):
+    c = wl.case(name)
+    d = wl.make_inputs(c, c.seed_base)
+    run_and_check(ci8, d["x_storage"], c.image, d["w_storage"], c.filter, c.out,
+                  c.pre, c.post, c.stride, c.dilation, label=name, entry="plain")
+
+
+def test_forum_strides_give_identical_bytes(ci8):
+    c = wl.case("tiny_5x5_r3")
+    d = wl.make_inputs(c, c.seed_base)
+    a = run_and_check(ci8, d["x_storage"], wl.TensorSpec((1, 1, 5, 5), (25, 25, 5, 1)),
+                      d["w_storage"], wl.TensorSpec((1, 1, 3, 3), (9, 9, 3, 1)), c.out,
+                      c.pre, c.post, c.stride, c.dilation, label="forum answer strides")
+    b = run_and_check(ci8, d["x_storage"], wl.TensorSpec((1, 1, 5, 5), (25, 1, 5, 1)),
+                      d["w_storage"], wl.TensorSpec((1, 1, 3, 3), (9, 1, 3, 1)), c.out,
+                      c.pre, c.post, c.stride, c.dilation, label="forum repro strides")
+    assert torch.equal(a, b)
+
+
+def test_repeat_runs_identical(ci8):
+    c = wl.case("large_channel_n64_c512_14")
+    d = wl.make_inputs(c, c.seed_base)
+    xg = _to_dev(d["x_storage"], c.image)
+    wg = _to_dev(d["w_storage"], c.filter)
+    outs = []
+    for _ in range(3):
+        _, og = wl.alloc_output(c.out, _dev())
+        ci8.conv_fprop_i8(xg, wg, og, c.pre, c.post, c.stride, c.dilation)
+        outs.append(og)
+    torch.cuda.synchronize()
+    assert torch.equal(outs[0], outs[1]) and torch.equal(outs[0], outs[2])
+
+
+# ---------------------------------------------------------------------------
+# Every tile shape, on ragged problems (M and K not multiples of any tile),
+# blocked and flat inner order, channel- and pixel-innermost outputs.
+# ---------------------------------------------------------------------------
+TILES = ["64x64x64", "128x64x64", "64x128x64", "128x128x64", "128x128x128", "256x128x64",
+         "128x256x64"]
+
+
+@pytest.mark.parametrize("tile", TILES)
+@pytest.mark.parametrize("C,out_layout", [(128, "nhwc"), (48, "nchw"), (256, "nchw"), (80, "nhwc")])
+def test_tile_shapes(ci8, monkeypatch, tile, C, out_layout):
+    monkeypatch.setenv("CONV_I8_TILE", tile)
+    g = torch.Generator().manual_seed(C)
+    N, H, W, K = 3, 17, 13, 200
+    x = torch.randint(-128, 128, (N, C, H, W), dtype=torch.int8, generator=g)
+    w = torch.randint(-128, 128, (K, C, 3, 3), dtype=torch.int8, generator=g)
+    xs = wl.TensorSpec((N, C, H, W), wl.channels_last_strides((N, C, H, W)))
+    ws = wl.TensorSpec((K, C, 3, 3), wl.channels_last_strides((K, C, 3, 3)))
+    od = (N, K, 9, 13)
+    os_ = wl.TensorSpec(od, wl.channels_last_strides(od) if out_layout == "nhwc" else wl.contiguous_strides(od))
+    xst = torch.empty(xs.storage_size, dtype=torch.int8)
+    torch.as_strided(xst, xs.dims, xs.strides).copy_(x)
+    wst = torch.empty(ws.storage_size, dtype=torch.int8)
+    torch.as_strided(wst, ws.dims, ws.strides).copy_(w)
+    f = ci8.plan_fields(ci8.conv_fprop_i8_plan(ci8.desc(xs.dims, xs.strides, 1), ci8.desc(ws.dims, ws.strides, 1),
+                                               ci8.desc(os_.dims, os_.strides, 2), (2, 1), (0, 1), (2, 1), (1, 1)))
+    assert f["tile"] == tile
+    run_and_check(ci8, xst, xs, wst, ws, os_, (2, 1), (0, 1), (2, 1), (1, 1), label=f"tile {tile} C={C}")
+
+
+# ---------------------------------------------------------------------------
+# Random shapes, parameters and layouts.
+# ---------------------------------------------------------------------------
+def _layout(rng, dims, kind):
+    n, c, h, w = dims
+    if kind == "nchw":
+        return wl.TensorSpec(dims, wl.contiguous_strides(dims))
+    if kind == "nhwc":
+        return wl.TensorSpec(dims, wl.channels_last_strides(dims))
+    if kind == "nhwc_padded":       # channel-innermost rows with spare room
+        cp = c + 16 * int(rng.integers(0, 3))
+        wpad = w + int(rng.integers(0, 3))
+        st = (h * wpad * cp, 1, wpad * cp, cp)
+        return wl.TensorSpec(dims, st, offset=16 * int(rng.integers(0, 3)))
+    if kind == "wide_view":          # every other element along w
+        full = (n, c, h, 2 * w)
+        st = wl.contiguous_strides(full)
+        return wl.TensorSpec(dims, (st[0], st[1], st[2], 2), storage=n * c * h * 2 * w)
+    if kind == "bcast_n":            # one image repeated over the batch
+        st = wl.channels_last_strides(dims)
+        return wl.TensorSpec(dims, (0, st[1], st[2], st[3]))
+    if kind == "hwcn":               # batch innermost
+        return wl.TensorSpec(dims, (1, h * w * n, w * n, n))
+    raise ValueError(kind)
+
+
+def _out_layout(rng, dims, kind):
+    n, k, p, q = dims
+    if kind == "nchw":
+        return wl.TensorSpec(dims, wl.contiguous_strides(dims))
+    if kind == "nhwc":
+        return wl.TensorSpec(dims, wl.channels_last_strides(dims))
+    if kind == "gapped":             # output rows with unused gaps between them
+        kp = k + 3
+        return wl.TensorSpec(dims, (p * (q + 1) * kp, 1, (q + 1) * kp, kp), offset=5)
+    raise ValueError(kind)
+
+
+def _fill(spec, values, seed):
+    st = torch.randint(-128, 128, (spec.storage_size,), dtype=torch.int8,
+                       generator=torch.Generator().manual_seed(seed))
+    torch.as_strided(st, spec.dims, spec.strides, spec.offset).copy_(values)
+    return st
+
+
+def test_random_problems(ci8):
+    rng = np.random.default_rng(2024)
+    done = 0
+    while done < 120:
+        N = int(rng.integers(1, 5))
+        C = int(rng.choice([1, 3, 8, 16, 24, 32, 48, 64, 96, 100, 128, 160]))
+        K = int(rng.integers(1, 140))
+        H, W = int(rng.integers(1, 24)), int(rng.integers(1, 24))
+        R, S = int(rng.integers(1, 6)), int(rng.integers(1, 6))
+        st = tuple(int(v) for v in rng.integers(1, 4, 2))
+        dl = tuple(int(v) for v in rng.integers(1, 4, 2))
+        pre = tuple(int(v) for v in rng.integers(0, 4, 2))
+        post = tuple(int(v) for v in rng.integers(0, 4, 2))
+        try:
+            od = oracle.out_dims((N, C, H, W), (K, C, R, S), pre, post, st, dl)
+        except oracle.OracleError:
+            continue
+        xk = str(rng.choice(["nchw", "nhwc", "nhwc_padded", "wide_view", "bcast_n", "hwcn"]))
+        wk = str(rng.choice(["nchw", "nhwc", "nhwc_padded"]))
+        ok = str(rng.choice(["nchw", "nhwc", "gapped"]))
+        xs, ws, os_ = _layout(rng, (N, C, H, W), xk), _layout(rng, (K, C, R, S), wk), _out_layout(rng, od, ok)
+        g = torch.Generator().manual_seed(done)
+        xv = torch.randint(-128, 128, (1 if xk == "bcast_n" else N, C, H, W), dtype=torch.int8, generator=g)
+        xv = xv.expand(N, C, H, W)
+        wv = torch.randint(-128, 128, (K, C, R, S), dtype=torch.int8, generator=g)
+        if xk == "bcast_n":
+            st_ = torch.randint(-128, 128, (xs.storage_size,), dtype=torch.int8, generator=g)
+            torch.as_strided(st_, (1, C, H, W), xs.strides).copy_(xv[:1])
+            xst = st_
+        else:
+            xst = _fill(xs, xv, done + 1)
+        wst = _fill(ws, wv, done + 2)
+        run_and_check(ci8, xst, xs, wst, ws, os_, pre, post, st, dl,
+                      label=f"random #{done} image {xk} filter {wk} out {ok}")
+        done += 1
+
+
+# ---------------------------------------------------------------------------
+# Degenerate and limit cases.
+# ---------------------------------------------------------------------------
+def _dense_case(ci8, N, C, H, W, K, R, S, pre, post, st, dl, xval=None, wval=None, label=""):
+    od = oracle.out_dims((N, C, H, W), (K, C, R, S), pre, post, st, dl)
+    xs = wl.TensorSpec((N, C, H, W), wl.channels_last_strides((N, C, H, W)))
+    ws = wl.TensorSpec((K, C, R, S), wl.channels_last_strides((K, C, R, S)))
+    os_ = wl.TensorSpec(od, wl.channels_last_strides(od))
+    g = torch.Generator().manual_seed(N * 7 + C)
+    xv = torch.randint(-128, 128, (N, C, H, W), dtype=torch.int8, generator=g) if xval is None else \
+        torch.full((N, C, H, W), xval, dtype=torch.int8)
+    wv = torch.randint(-128, 128, (K, C, R, S), dtype=torch.int8, generator=g) if wval is None else \
+        torch.full((K, C, R, S), wval, dtype=torch.int8)
+    return run_and_check(ci8, _fill(xs, xv, 1), xs, _fill(ws, wv, 2), ws, os_, pre, post, st, dl, label=label)
+
+
+def test_zero_channels_give_zeros(ci8):
+    got = _dense_case(ci8, 2, 0, 5, 5, 3, 3, 3, (1, 1), (1, 1), (1, 1), (1, 1), label="C=0")
+    assert (got[GUARD:-GUARD] == 0).all()
+
+
+def test_image_without_pixels_gives_zeros(ci8):
+    got = _dense_case(ci8, 2, 16, 0, 4, 8, 1, 1, (1, 0), (1, 0), (1, 1), (1, 1), label="H=0 padded")
+    assert (got[GUARD:-GUARD] == 0).all()
+
+
+def test_empty_batch_and_filters_write_nothing(ci8):
+    for (N, K) in [(0, 4), (3, 0)]:
+        got = _dense_case(ci8, N, 16, 5, 5, K, 3, 3, (0, 0), (0, 0), (1, 1), (1, 1), label=f"N={N} K={K}")
+        assert (got == wl.SENTINEL).all()
+
+
+def test_largest_exact_reduction(ci8):
+    # C*R*S = 14563*9 = 131067, every product +16384: the largest sums the
+    # library accepts, 2147401728, just below 2^31
+    got = _dense_case(ci8, 1, 14563, 3, 3, 2, 3, 3, (0, 0), (0, 0), (1, 1), (1, 1),
+                      xval=-128, wval=-128, label="max reduction")
+    assert int(got[GUARD]) == 16384 * 131067
+
+
+def test_window_is_whole_image(ci8):
+    _dense_case(ci8, 2, 32, 7, 9, 5, 7, 9, (0, 0), (0, 0), (1, 1), (1, 1), label="window = image")
+
+
+def test_large_dilation_and_stride(ci8):
+    _dense_case(ci8, 2, 16, 30, 31, 33, 3, 2, (5, 0), (0, 7), (4, 3), (9, 11), label="dil 9/11")
+
+
+def test_single_output_channel_and_pixel_tails(ci8):
+    _dense_case(ci8, 1, 64, 1, 1, 1, 1, 1, (0, 0), (0, 0), (1, 1), (1, 1), label="1x1 everything")
+    _dense_case(ci8, 5, 16, 3, 3, 129, 3, 3, (1, 1), (1, 1), (1, 1), (1, 1), label="K=129")
+
+
+def test_batch_split_over_launches(ci8):
+    """Images almost 2 GiB apart: one launch per image keeps every buffer
+    offset below 2^31."""
+    gap = 1 << 31
+    N, C, H, W, K = 2, 32, 9, 10, 40
+    dims = (N, C, H, W)
+    cl = wl.channels_last_strides(dims)
+    xs = wl.TensorSpec(dims, (gap, cl[1], cl[2], cl[3]))
+    ws = wl.TensorSpec((K, C, 3, 3), wl.channels_last_strides((K, C, 3, 3)))
+    os_ = wl.TensorSpec((N, K, 9, 10), wl.contiguous_strides((N, K, 9, 10)))
+    x_storage = torch.zeros(xs.storage_size, dtype=torch.int8)
+    g = torch.Generator().manual_seed(5)
+    torch.as_strided(x_storage, dims, xs.strides).copy_(torch.randint(-128, 128, dims, dtype=torch.int8, generator=g))
+    w_storage = _fill(ws, torch.randint(-128, 128, (K, C, 3, 3), dtype=torch.int8, generator=g), 3)
+    f = ci8.plan_fields(ci8.conv_fprop_i8_plan(ci8.desc(xs.dims, xs.strides, 1), ci8.desc(ws.dims, ws.strides, 1),
+                                               ci8.desc(os_.dims, os_.strides, 2), 1, 1, 1, 1))
+    assert f["batch_chunk"] == "1"
+    run_and_check(ci8, x_storage, xs, w_storage, ws, os_, (1, 1), (1, 1), (1, 1), (1, 1), label="batch split")

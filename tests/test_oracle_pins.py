@@ -191,3 +191,17 @@ def test_mutants_are_caught(tmp_path):
         if r.returncode == 0:
             survivors.append(desc)
     assert not survivors, f"mutants not caught by any pin: {survivors}"
+
+
+def test_empty_operands(orc):
+    """C = 0 sums nothing and H = 0 leaves only padding: all outputs are 0,
+    as brute force gives."""
+    x = torch.empty((2, 0, 5, 5), dtype=torch.int8)
+    w = torch.empty((3, 0, 3, 3), dtype=torch.int8)
+    y = orc.conv_fprop(x, w, 1, 1)
+    assert tuple(y.shape) == (2, 3, 5, 5) and (y == 0).all()
+    x = torch.empty((2, 4, 0, 3), dtype=torch.int8)
+    w = torch.ones((3, 4, 1, 2), dtype=torch.int8)
+    y = orc.conv_fprop(x, w, (1, 0), (2, 1))
+    ref = pins.brute_force(x.numpy(), w.numpy(), (1, 0), (2, 1), (1, 1), (1, 1))
+    assert tuple(y.shape) == ref.shape == (2, 3, 3, 3) and (y == 0).all()
