@@ -19,7 +19,7 @@ HEADERS = [os.path.join(CSRC, f) for f in ("igemm_kernel.hpp", "repack_kernel.hp
 
 HIP_FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",
-    "-Wall", "-Wno-unused-function",
+    "-Wall", "-Wno-unused-function", "-Wno-inline-asm",
     # packed fp32 VALU forms are kept out of every device code object
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
 ]

@@ -195,35 +195,43 @@ conv_i8_status_t analyze(const conv_i8_desc_t *image, const conv_i8_desc_t *filt
 // Tile configurations instantiated for the implicit-GEMM kernel.
 // ---------------------------------------------------------------------------
 struct TileCfg {
-    int tm, tn, bk;
+    int tm, tn, bk, ns;
     double eff;  // relative per-CU throughput of this tile shape (cost model)
 };
 
 const TileCfg kTiles[] = {
-    {64, 64, 64, 0.55},   {128, 64, 64, 0.75},  {64, 128, 64, 0.75}, {128, 128, 64, 0.9},
-    {128, 128, 128, 0.95}, {256, 128, 64, 1.0}, {128, 256, 64, 1.0},
+    {64, 64, 64, 4, 0.55},   {128, 64, 64, 4, 0.75},  {64, 128, 64, 4, 0.75},
+    {128, 128, 64, 4, 0.9},  {128, 128, 128, 3, 0.95}, {256, 128, 64, 4, 1.0},
+    {128, 256, 64, 4, 1.0},
 };
 constexpr int kNumTiles = sizeof(kTiles) / sizeof(kTiles[0]);
 
-template <int TM, int TN, int BK>
-void launch_cfg(bool pix_j, dim3 grid, hipStream_t stream, const IgemmArgs &a)
+template <int TM, int TN, int BK, int NS>
+void launch_cfg(bool flat, bool pix_j, dim3 grid, hipStream_t stream, const IgemmArgs &a)
 {
-    if (pix_j)
-        hipLaunchKernelGGL((conv_igemm_kernel<TM, TN, BK, true>), grid, dim3(256), 0, stream, a);
-    else
-        hipLaunchKernelGGL((conv_igemm_kernel<TM, TN, BK, false>), grid, dim3(256), 0, stream, a);
+    if (flat) {
+        if (pix_j)
+            hipLaunchKernelGGL((conv_igemm_kernel<TM, TN, BK, NS, true, true>), grid, dim3(256), 0, stream, a);
+        else
+            hipLaunchKernelGGL((conv_igemm_kernel<TM, TN, BK, NS, true, false>), grid, dim3(256), 0, stream, a);
+    } else {
+        if (pix_j)
+            hipLaunchKernelGGL((conv_igemm_kernel<TM, TN, BK, NS, false, true>), grid, dim3(256), 0, stream, a);
+        else
+            hipLaunchKernelGGL((conv_igemm_kernel<TM, TN, BK, NS, false, false>), grid, dim3(256), 0, stream, a);
+    }
 }
 
-void launch_igemm(int cfg, bool pix_j, dim3 grid, hipStream_t stream, const IgemmArgs &a)
+void launch_igemm(int cfg, bool flat, bool pix_j, dim3 grid, hipStream_t stream, const IgemmArgs &a)
 {
     switch (cfg) {
-    case 0: launch_cfg<64, 64, 64>(pix_j, grid, stream, a); break;
-    case 1: launch_cfg<128, 64, 64>(pix_j, grid, stream, a); break;
-    case 2: launch_cfg<64, 128, 64>(pix_j, grid, stream, a); break;
-    case 3: launch_cfg<128, 128, 64>(pix_j, grid, stream, a); break;
-    case 4: launch_cfg<128, 128, 128>(pix_j, grid, stream, a); break;
-    case 5: launch_cfg<256, 128, 64>(pix_j, grid, stream, a); break;
-    case 6: launch_cfg<128, 256, 64>(pix_j, grid, stream, a); break;
+    case 0: launch_cfg<64, 64, 64, 4>(flat, pix_j, grid, stream, a); break;
+    case 1: launch_cfg<128, 64, 64, 4>(flat, pix_j, grid, stream, a); break;
+    case 2: launch_cfg<64, 128, 64, 4>(flat, pix_j, grid, stream, a); break;
+    case 3: launch_cfg<128, 128, 64, 4>(flat, pix_j, grid, stream, a); break;
+    case 4: launch_cfg<128, 128, 128, 3>(flat, pix_j, grid, stream, a); break;
+    case 5: launch_cfg<256, 128, 64, 4>(flat, pix_j, grid, stream, a); break;
+    case 6: launch_cfg<128, 256, 64, 4>(flat, pix_j, grid, stream, a); break;
     default: break;
     }
 }
@@ -240,6 +248,9 @@ struct Plan {
     bool blocked = true;
     int64_t nstages = 0;
     int64_t batch_chunk = 1;           // images per igemm launch
+    int64_t y_img_span = 0;            // output elements one image spans
+    bool pix_linear = false;           // output pixel m at m * pix_stride
+    int64_t pix_stride = 0;
 };
 
 size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
@@ -329,13 +340,24 @@ conv_i8_status_t make_plan(const Problem &pb, const void *x_ptr, const void *w_p
         pl->w_span = sp;
     }
 
-    // Images per launch: the image bytes one launch addresses, and its
-    // N*P*Q rows, must stay below 2^31.
+    // Output bytes one image addresses (its N stride aside).
+    {
+        T4 o = pb.y;
+        o.d[0] = 1;
+        int64_t sp;
+        if (!span_of(o, &sp) || sp > kI32Max / 4)
+            return CONV_I8_ERR_UNSUPPORTED;
+        pl->y_img_span = sp;
+    }
+    // Images per launch: the image bytes and output bytes one launch
+    // addresses, and its N*P*Q rows, must stay below 2^31.
     {
         const int64_t pq = pb.P * pb.Q;
         int64_t nb = std::max<int64_t>(1, pb.N);
         if (pl->xsN > 0)
             nb = std::min<int64_t>(nb, (kI32Max - pl->x_img_span) / pl->xsN + 1);
+        if (pb.y.s[0] > 0)
+            nb = std::min<int64_t>(nb, (kI32Max / 4 - pl->y_img_span) / pb.y.s[0] + 1);
         nb = std::min<int64_t>(nb, kI32Max / pq);
         if (nb < 1)
             return CONV_I8_ERR_UNSUPPORTED;
@@ -345,6 +367,15 @@ conv_i8_status_t make_plan(const Problem &pb, const void *x_ptr, const void *w_p
         pl->batch_chunk = nb;
     }
 
+    // Are output pixels equally spaced in (n, p, q) order?
+    {
+        const int64_t N = pb.N, P = pb.P, Q = pb.Q;
+        const int64_t oN = pb.y.s[0], oP = pb.y.s[2], oQ = pb.y.s[3];
+        int64_t ps = Q > 1 ? oQ : P > 1 ? oP : oN;
+        pl->pix_stride = ps;
+        pl->pix_linear = (Q == 1 || oQ == ps) && (P == 1 || oP == Q * ps) &&
+                         (N == 1 || oN == P * Q * ps);
+    }
     // Output layout: make the MFMA column (lanes) walk the contiguous dim.
     const int64_t oK = pb.y.s[1], oQ = pb.y.s[3];
     if (oK == 1)
@@ -481,19 +512,23 @@ conv_i8_status_t run(const Problem &pb, const Plan &pl, const void *x_ptr, const
     a.dilW = (int)pb.dil[1];
     a.padH = (int)pb.pre[0];
     a.padW = (int)pb.pre[1];
-    a.oN = pb.y.s[0];
-    a.oK = pb.y.s[1];
-    a.oP = pb.y.s[2];
-    a.oQ = pb.y.s[3];
+    a.oN = (int)pb.y.s[0];
+    a.oK = (int)pb.y.s[1];
+    a.oP = (int)pb.y.s[2];
+    a.oQ = (int)pb.y.s[3];
+    a.pix_linear = pl.pix_linear ? 1 : 0;
+    a.pix_stride = (int)pl.pix_stride;
     a.nstages = pb.C > 0 ? (int)pl.nstages : 0;
     a.cc = (int)(pl.Cp / 16);
-    a.blocked = pl.blocked ? 1 : 0;
+    a.inv_cc = a.cc > 0 ? 1.0f / (float)a.cc : 0.0f;
+    a.inv_s = 1.0f / (float)a.S;
     a.tiles_n = (int)((pb.K + c.tn - 1) / c.tn);
     for (int64_t n0 = 0; n0 < pb.N; n0 += pl.batch_chunk) {
         const int64_t nb = std::min(pl.batch_chunk, pb.N - n0);
         a.img = x + n0 * pl.xsN;
         a.img_range = (int)((nb - 1) * pl.xsN + pl.x_img_span);
         a.out = (int32_t *)y_ptr + n0 * pb.y.s[0];
+        a.out_range = (int)(((nb - 1) * pb.y.s[0] + pl.y_img_span) * 4);
         a.N = (int)nb;
         a.sN = (int)pl.xsN;
         a.M = (int)(nb * pb.P * pb.Q);
@@ -501,7 +536,7 @@ conv_i8_status_t run(const Problem &pb, const Plan &pl, const void *x_ptr, const
         if (tiles == 0)
             continue;
         a.tiles = (int)tiles;
-        launch_igemm(pl.cfg, pl.pix_j, dim3((unsigned)tiles), stream, a);
+        launch_igemm(pl.cfg, !pl.blocked, pl.pix_j, dim3((unsigned)tiles), stream, a);
         if (hipGetLastError() != hipSuccess)
             return CONV_I8_ERR_HIP;
     }
