@@ -18,6 +18,7 @@
 #include <algorithm>
 #include <string>
 
+#include "halo_kernel.hpp"
 #include "igemm_kernel.hpp"
 #include "repack_kernel.hpp"
 
@@ -192,34 +193,58 @@ conv_i8_status_t analyze(const conv_i8_desc_t *image, const conv_i8_desc_t *filt
 }
 
 // ---------------------------------------------------------------------------
-// Tile configurations instantiated for the implicit-GEMM kernel.
+// Tile configurations instantiated for the implicit-GEMM kernels.
 // ---------------------------------------------------------------------------
 struct TileCfg {
+    const char *name;  // CONV_I8_TILE value that forces this shape
     int tm, tn, bk, ns;
-    double eff;  // relative per-CU throughput of this tile shape (cost model)
+    int waves;         // 4 (2x2 wave grid) or 8 (4x2)
+    bool halo;         // footprint kernel (image loaded once per channel block)
+    int fls, fpix;     // halo: footprint loads per stage, footprint capacity (pixels)
+    double eff;        // relative MFMA efficiency of this tile shape (cost model)
 };
 
 const TileCfg kTiles[] = {
-    {64, 64, 64, 4, 0.55},   {128, 64, 64, 4, 0.75},  {64, 128, 64, 4, 0.75},
-    {128, 128, 64, 4, 0.9},  {128, 128, 128, 3, 0.95}, {256, 128, 64, 4, 1.0},
-    {128, 256, 64, 4, 1.0},
+    {"64x64x64", 64, 64, 64, 4, 4, false, 0, 0, 0.55},
+    {"128x64x64", 128, 64, 64, 4, 4, false, 0, 0, 0.75},
+    {"64x128x64", 64, 128, 64, 4, 4, false, 0, 0, 0.75},
+    {"128x128x64", 128, 128, 64, 4, 4, false, 0, 0, 0.9},
+    {"128x128x128", 128, 128, 128, 3, 4, false, 0, 0, 0.95},
+    {"256x128x64", 256, 128, 64, 4, 4, false, 0, 0, 1.0},
+    {"128x256x64", 128, 256, 64, 4, 4, false, 0, 0, 1.0},
+    {"h256x128", 256, 128, 64, 4, 4, true, 2, 512, 1.0},
+    {"h128x128", 128, 128, 64, 4, 4, true, 1, 256, 0.9},
+    {"h128x64", 128, 64, 64, 4, 4, true, 1, 256, 0.75},
+    {"w256x128x64", 256, 128, 64, 4, 8, false, 0, 0, 1.1},
+    {"w128x128x64", 128, 128, 64, 4, 8, false, 0, 0, 1.0},
+    {"w256x128x128", 256, 128, 128, 3, 8, false, 0, 0, 1.15},
 };
 constexpr int kNumTiles = sizeof(kTiles) / sizeof(kTiles[0]);
 
-template <int TM, int TN, int BK, int NS>
+template <int TM, int TN, int BK, int NS, int WGM = 2, int WGN = 2>
 void launch_cfg(bool flat, bool pix_j, dim3 grid, hipStream_t stream, const IgemmArgs &a)
 {
+    const dim3 block(64 * WGM * WGN);
     if (flat) {
         if (pix_j)
-            hipLaunchKernelGGL((conv_igemm_kernel<TM, TN, BK, NS, true, true>), grid, dim3(256), 0, stream, a);
+            hipLaunchKernelGGL((conv_igemm_kernel<TM, TN, BK, NS, WGM, WGN, true, true>), grid, block, 0, stream, a);
         else
-            hipLaunchKernelGGL((conv_igemm_kernel<TM, TN, BK, NS, true, false>), grid, dim3(256), 0, stream, a);
+            hipLaunchKernelGGL((conv_igemm_kernel<TM, TN, BK, NS, WGM, WGN, true, false>), grid, block, 0, stream, a);
     } else {
         if (pix_j)
-            hipLaunchKernelGGL((conv_igemm_kernel<TM, TN, BK, NS, false, true>), grid, dim3(256), 0, stream, a);
+            hipLaunchKernelGGL((conv_igemm_kernel<TM, TN, BK, NS, WGM, WGN, false, true>), grid, block, 0, stream, a);
         else
-            hipLaunchKernelGGL((conv_igemm_kernel<TM, TN, BK, NS, false, false>), grid, dim3(256), 0, stream, a);
+            hipLaunchKernelGGL((conv_igemm_kernel<TM, TN, BK, NS, WGM, WGN, false, false>), grid, block, 0, stream, a);
     }
+}
+
+template <int TM, int TN, int NS, int FLS, int FPIX>
+void launch_halo(bool pix_j, dim3 grid, hipStream_t stream, const IgemmArgs &a)
+{
+    if (pix_j)
+        hipLaunchKernelGGL((conv_halo_kernel<TM, TN, NS, FLS, FPIX, true>), grid, dim3(256), 0, stream, a);
+    else
+        hipLaunchKernelGGL((conv_halo_kernel<TM, TN, NS, FLS, FPIX, false>), grid, dim3(256), 0, stream, a);
 }
 
 void launch_igemm(int cfg, bool flat, bool pix_j, dim3 grid, hipStream_t stream, const IgemmArgs &a)
@@ -232,8 +257,57 @@ void launch_igemm(int cfg, bool flat, bool pix_j, dim3 grid, hipStream_t stream,
     case 4: launch_cfg<128, 128, 128, 3>(flat, pix_j, grid, stream, a); break;
     case 5: launch_cfg<256, 128, 64, 4>(flat, pix_j, grid, stream, a); break;
     case 6: launch_cfg<128, 256, 64, 4>(flat, pix_j, grid, stream, a); break;
+    case 7: launch_halo<256, 128, 4, 2, 512>(pix_j, grid, stream, a); break;
+    case 8: launch_halo<128, 128, 4, 1, 256>(pix_j, grid, stream, a); break;
+    case 9: launch_halo<128, 64, 4, 1, 256>(pix_j, grid, stream, a); break;
+    case 10: launch_cfg<256, 128, 64, 4, 4, 2>(flat, pix_j, grid, stream, a); break;
+    case 11: launch_cfg<128, 128, 64, 4, 4, 2>(flat, pix_j, grid, stream, a); break;
+    case 12: launch_cfg<256, 128, 128, 3, 4, 2>(flat, pix_j, grid, stream, a); break;
     default: break;
     }
+}
+
+// Division by a launch-invariant divisor d >= 1 for dividends below 2^31:
+// l = ceil(log2 d), m = floor(2^32 (2^l - d) / d) + 1.
+Divisor make_divisor(int64_t d)
+{
+    Divisor r{};
+    int l = 0;
+    while ((int64_t(1) << l) < d)
+        ++l;
+    r.l = l;
+    r.m = (unsigned)((((unsigned __int128)1 << 32) * (((unsigned __int128)1 << l) - (unsigned __int128)d)) /
+                     (unsigned __int128)d + 1);
+    return r;
+}
+
+// Largest footprint (input pixels, padded rows x padded width) any tile of
+// `tm` consecutive output pixels needs.  The footprint of a tile depends only
+// on its start modulo P*Q (and on truncation at M), so one period of tile
+// starts plus the last tile cover every case.
+int64_t max_footprint(int64_t M, int64_t PQ, int64_t Q, int64_t Hp, int64_t Wf, int64_t str_h,
+                      int64_t span_h, int64_t tm)
+{
+    auto fp_of = [&](int64_t m0) {
+        const int64_t ml = std::min(m0 + tm, M) - 1;
+        const int64_t na = m0 / PQ, pa = (m0 - na * PQ) / Q;
+        const int64_t nb = ml / PQ, pb = (ml - nb * PQ) / Q;
+        return ((nb - na) * Hp + pb * str_h + span_h - pa * str_h + 1) * Wf;
+    };
+    const int64_t tiles = (M + tm - 1) / tm;
+    int64_t g = PQ, b = tm;
+    while (b) {
+        const int64_t t = g % b;
+        g = b;
+        b = t;
+    }
+    const int64_t period = PQ / g;
+    int64_t best = 0;
+    for (int64_t t = 0; t < std::min(tiles, period); ++t)
+        best = std::max(best, fp_of(t * tm));
+    if (tiles > 0)
+        best = std::max(best, fp_of((tiles - 1) * tm));
+    return best;
 }
 
 struct Plan {
@@ -251,6 +325,7 @@ struct Plan {
     int64_t y_img_span = 0;            // output elements one image spans
     bool pix_linear = false;           // output pixel m at m * pix_stride
     int64_t pix_stride = 0;
+    int64_t Hp = 0, Wf = 0, npieces = 0;  // footprint kernel geometry
 };
 
 size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
@@ -385,42 +460,70 @@ conv_i8_status_t make_plan(const Problem &pb, const void *x_ptr, const void *w_p
     else
         pl->pix_j = oQ != 0 && (oK == 0 || oQ < oK);
 
-    // Tile choice: rounds of 256 tiles times tile work over relative efficiency.
+    // Tile choice.  Per tile, the MFMA time (tile work at one CU's share of
+    // the MFMA rate, over the shape's relative efficiency) and the operand
+    // load time (bytes streamed into LDS at one CU's share of the ~20 TB/s
+    // L2-to-LDS rate) overlap; tiles run in rounds of 256 (one per CU).
     const int64_t cc = pl->Cp / 16;
     const int64_t M = std::min(pb.N, pl->batch_chunk) * pb.P * pb.Q;
+    const int64_t RS = pb.R * pb.S;
+    const int64_t Hp = pb.H + pb.pre[0] + pb.post[0];
+    const int64_t Wf = (pb.Q - 1) * pb.str[1] + (pb.S - 1) * pb.dil[1] + 1;
+    const double mac_per_s_cu = 4.4e15 / 2 / kCUs, bytes_per_s_cu = 20e12 / kCUs;
     int best = -1;
     double best_cost = 0;
     const char *forced = env_tile();
     for (int i = 0; i < kNumTiles; ++i) {
         const TileCfg &c = kTiles[i];
-        if (forced) {
-            char name[32];
-            snprintf(name, sizeof name, "%dx%dx%d", c.tm, c.tn, c.bk);
-            if (strcmp(forced, name) != 0)
-                continue;
-        }
+        if (forced && strcmp(forced, c.name) != 0)
+            continue;
         const int cps = c.bk / 16;
-        double eff = c.eff;
-        if (cc % cps != 0) {
-            // flat order: the tail stage is partly empty
-            const int64_t chunks = pb.R * pb.S * cc;
-            const int64_t stages = (chunks + cps - 1) / cps;
-            eff *= chunks > 0 ? (double)chunks / (double)(stages * cps) : 1.0;
+        const int64_t chunks = RS * cc;
+        int64_t stages = cc % cps == 0 ? RS * (cc / cps) : (chunks + cps - 1) / cps;
+        double bytes;
+        if (c.halo) {
+            // footprint kernel: 64-channel blocks, enough taps to carry the
+            // footprint pieces, and a footprint that fits
+            if (cc % 4 != 0 || Hp >= (1 << 20) || Wf >= (1 << 20))
+                continue;
+            const int64_t np = std::min<int64_t>(RS - c.ns + 1, (int64_t)c.fpix * 64 / (c.fls * 4096));
+            if (np < 1)
+                continue;
+            const int64_t fmax = max_footprint(M, pb.P * pb.Q, pb.Q, Hp, Wf, pb.str[0],
+                                               (pb.R - 1) * pb.dil[0], c.tm);
+            if (fmax > std::min<int64_t>(np * c.fls * 64, c.fpix))
+                continue;
+            bytes = (double)c.tn * stages * 64 + (double)(cc / 4) * fmax * 64;
+        } else {
+            bytes = (double)(c.tm + c.tn) * stages * c.bk;
         }
+        double eff = c.eff;
+        if (!c.halo && cc % cps != 0)
+            eff *= chunks > 0 ? (double)chunks / (double)(stages * cps) : 1.0;
+        const double t_mfma = (double)c.tm * c.tn * stages * c.bk / mac_per_s_cu / eff;
+        const double t_load = bytes / bytes_per_s_cu;
         const int64_t tiles = ((M + c.tm - 1) / c.tm) * ((pb.K + c.tn - 1) / c.tn);
         const int64_t rounds = (tiles + kCUs - 1) / kCUs;
-        const double cost = (double)rounds * c.tm * c.tn / eff;
-        if (best < 0 || cost < best_cost - 1e-9) {
+        const double cost = (double)rounds * std::max(t_mfma, t_load);
+        if (best < 0 || cost < best_cost * (1 - 1e-9)) {
             best = i;
             best_cost = cost;
         }
     }
-    if (best < 0)
-        best = 3;  // unknown CONV_I8_TILE value: default shape
+    if (best < 0) {
+        // unknown or inapplicable CONV_I8_TILE value: default shape
+        best = 3;
+    }
     pl->cfg = best;
-    const int cps = kTiles[best].bk / 16;
+    const TileCfg &c = kTiles[best];
+    const int cps = c.bk / 16;
     pl->blocked = cc % cps == 0;
-    pl->nstages = pl->blocked ? pb.R * pb.S * (cc / cps) : (pb.R * pb.S * cc + cps - 1) / cps;
+    pl->nstages = pl->blocked ? RS * (cc / cps) : (RS * cc + cps - 1) / cps;
+    if (c.halo) {
+        pl->Hp = Hp;
+        pl->Wf = Wf;
+        pl->npieces = std::min<int64_t>(RS - c.ns + 1, (int64_t)c.fpix * 64 / (c.fls * 4096));
+    }
     return CONV_I8_OK;
 }
 
@@ -431,10 +534,10 @@ std::string describe(const Problem &pb, const Plan &pl)
     const int64_t tiles = ((M + c.tm - 1) / c.tm) * ((pb.K + c.tn - 1) / c.tn);
     char buf[512];
     snprintf(buf, sizeof buf,
-             "repack_image=%d repack_filter=%d Cp=%lld tile=%dx%dx%d order=%s stages=%lld "
+             "repack_image=%d repack_filter=%d Cp=%lld tile=%s kernel=%s order=%s stages=%lld "
              "lanes=%s tiles=%lld batch_chunk=%lld workspace=%zu",
-             (int)pl.repack_x, (int)pl.repack_w, (long long)pl.Cp, c.tm, c.tn, c.bk,
-             pl.blocked ? "blocked" : "flat", (long long)pl.nstages,
+             (int)pl.repack_x, (int)pl.repack_w, (long long)pl.Cp, c.name,
+             c.halo ? "footprint" : "im2col", pl.blocked ? "blocked" : "flat", (long long)pl.nstages,
              pl.pix_j ? "pixels" : "channels", (long long)tiles, (long long)pl.batch_chunk,
              pl.ws_bytes);
     return buf;
@@ -523,6 +626,14 @@ conv_i8_status_t run(const Problem &pb, const Plan &pl, const void *x_ptr, const
     a.inv_cc = a.cc > 0 ? 1.0f / (float)a.cc : 0.0f;
     a.inv_s = 1.0f / (float)a.S;
     a.tiles_n = (int)((pb.K + c.tn - 1) / c.tn);
+    a.d_pq = make_divisor(pb.P * pb.Q);
+    a.d_q = make_divisor(pb.Q);
+    a.Hp = (int)pl.Hp;
+    a.Wf = (int)pl.Wf;
+    a.inv_hp = pl.Hp > 0 ? 1.0f / (float)pl.Hp : 0.0f;
+    a.inv_wf = pl.Wf > 0 ? 1.0f / (float)pl.Wf : 0.0f;
+    a.npieces = (int)pl.npieces;
+    a.ncblk = (int)(pl.Cp / 64);
     for (int64_t n0 = 0; n0 < pb.N; n0 += pl.batch_chunk) {
         const int64_t nb = std::min(pl.batch_chunk, pb.N - n0);
         a.img = x + n0 * pl.xsN;

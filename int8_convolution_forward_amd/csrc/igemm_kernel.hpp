@@ -40,130 +40,28 @@
 // output, pixels for a pixel-innermost one — by swapping the MFMA operands.
 #pragma once
 
-#include <hip/hip_runtime.h>
-#include <stdint.h>
+#include "kernel_common.hpp"
 
 namespace convi8 {
 
-typedef int v4i __attribute__((ext_vector_type(4)));
-typedef int v16i __attribute__((ext_vector_type(16)));
-typedef __attribute__((address_space(3))) void lds_void;
-
-// Buffer offset that always lies outside a resource (ranges are < 2^31).
-constexpr int kOutOfRange = (int)0x80000000u;
-// Buffer resource word 3 for gfx9-family raw buffer access (32-bit data format).
-constexpr int kRsrcWord3 = 0x00020000;
-
-struct IgemmArgs {
-    const int8_t *img;   // image, channel-innermost; (0,0,0,0) at img
-    const int8_t *flt;   // filter K,R,S,C with C innermost
-    int32_t *out;        // output element (0,0,0,0)
-    int img_range;       // bytes addressable from img (buffer range)
-    int flt_range;       // bytes addressable from flt
-    int N, H, W, C;      // C: channels as stored (multiple of 16)
-    int sN, sH, sW;      // image strides in bytes (channel stride is 1)
-    int K, R, S;
-    int fK, fR, fS;      // filter strides in bytes (channel stride is 1)
-    int P, Q, PQ, M;     // M = N*P*Q
-    int strH, strW, dilH, dilW, padH, padW;
-    int oN, oK, oP, oQ;  // output strides in elements (one launch spans < 2^31 bytes)
-    int out_range;       // bytes addressable from out
-    int pix_linear;      // output pixel m = (n*P + p)*Q + q lives at m*pix_stride
-    int pix_stride;
-    int nstages;         // stages of BK bytes of the inner dimension
-    int cc;              // C / 16
-    float inv_cc, inv_s; // 1.0f / cc, 1.0f / S (flat order index split)
-    int tiles_n;         // column tiles
-    int tiles;           // total tiles
-};
-
-// s_waitcnt immediate (gfx9 encoding): wait until at most `vm` vector-memory
-// operations are outstanding and all LDS operations are done.
-template <int VM>
-__device__ __forceinline__ void wait_vm_lgkm0()
+template <int TM, int TN, int BK, int NS, int WGM, int WGN, bool FLAT, bool PIX_J>
+__global__ __launch_bounds__(64 * WGM * WGN) void conv_igemm_kernel(IgemmArgs a)
 {
-    static_assert(VM >= 0 && VM < 64, "vmcnt out of range");
-    __builtin_amdgcn_s_waitcnt((VM & 15) | ((VM >> 4) << 14) | (7 << 4) | (0 << 8));
-}
-
-template <int BK>
-__device__ __forceinline__ int swizzle_chunk(int row, int chunk)
-{
-    // 64-byte rows (4 chunks) use row bits 1..3, 128-byte rows (8 chunks) row
-    // bits 0..3: any 8 (32 banks) or 16 (64 banks) consecutive rows reading one
-    // logical chunk land on distinct banks.
-    if constexpr (BK == 64)
-        return chunk ^ (((row >> 1) ^ (row >> 2)) & 3);
-    else
-        return chunk ^ ((row ^ (row >> 1)) & 7);
-}
-
-// Buffer resource (gfx9 layout): base address, stride 0, byte range,
-// format word.  Built from kernel arguments, so it is wave-uniform.
-__device__ __forceinline__ v4i make_rsrc(const void *p, int range)
-{
-    const unsigned long long a = (unsigned long long)p;
-    v4i d;
-    d.x = (int)(unsigned)a;
-    d.y = (int)((a >> 32) & 0xFFFFu);
-    d.z = range;
-    d.w = kRsrcWord3;
-    return d;
-}
-
-// 16 bytes per lane from buffer offset `voff` straight into LDS: lane i's
-// bytes land at lds + 16*i (a wave fills one contiguous 1 KiB block).  An
-// offset outside the range writes zeros.  Written as inline assembly so the
-// compiler does not add a wait for these loads before every LDS read (it
-// cannot tell which ring slot they fill); the kernel counts them itself with
-// s_waitcnt vmcnt.
-__device__ __forceinline__ void load16_to_lds(v4i rsrc, unsigned lds_addr, int voff)
-{
-    asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
-                 :: "s"(lds_addr), "v"(voff), "s"(rsrc) : "memory", "m0");
-}
-
-// LDS byte address of a __shared__ object.
-__device__ __forceinline__ unsigned lds_address(const void *p)
-{
-    return (unsigned)(unsigned long long)(lds_void *)p;
-}
-
-// floor(n / d) for 0 <= n < 2^22 and 1 <= d < 2^22, with inv = 1.0f / d
-// rounded to float: the quotient of n + 1/2 stays more than 1/(2d) away
-// from the next integer while the float error is below n / (d * 2^23).
-__device__ __forceinline__ int fdiv(int n, int d, float inv)
-{
-    (void)d;
-    return (int)(((float)n + 0.5f) * inv);
-}
-
-// Workgroups are dealt round-robin to the 8 XCDs; give each XCD a contiguous
-// run of tiles (column tiles of one row tile are adjacent) so that the image
-// rows a run reads stay in that XCD's L2.
-__device__ __forceinline__ int xcd_tile(int bid, int tiles)
-{
-    const int per = tiles >> 3, rem = tiles & 7;
-    const int xcd = bid & 7, idx = bid >> 3;
-    return xcd < rem ? xcd * (per + 1) + idx : rem * (per + 1) + (xcd - rem) * per + idx;
-}
-
-template <int TM, int TN, int BK, int NS, bool FLAT, bool PIX_J>
-__global__ __launch_bounds__(256) void conv_igemm_kernel(IgemmArgs a)
-{
+    constexpr int NW = WGM * WGN;           // waves per workgroup (WGM x WGN grid)
     constexpr int CPS = BK / 16;            // 16-byte chunks per row per stage
     constexpr int RPI = 64 / CPS;           // rows one wave-wide load fills
-    constexpr int AL = TM / (4 * RPI);      // image-row loads per thread per stage
-    constexpr int BL = TN / (4 * RPI);      // filter-row loads per thread per stage
+    constexpr int AL = TM / (NW * RPI);     // image-row loads per thread per stage
+    constexpr int BL = TN / (NW * RPI);     // filter-row loads per thread per stage
     constexpr int LPS = AL + BL;            // loads per thread per stage
     constexpr int A_BYTES = TM * BK, STAGE = (TM + TN) * BK;
-    constexpr int WM = TM / 2, WN = TN / 2; // wave tile
+    constexpr int WM = TM / WGM, WN = TN / WGN; // wave tile
     constexpr int FM = WM / 32, FN = WN / 32;
     constexpr int KS = BK / 32;             // MFMA k-steps per stage
     constexpr int NMF = KS * FM * FN;       // MFMAs per stage per wave
     constexpr int NRD = KS * (FM + FN);     // fragment reads per stage per wave
     static_assert(AL >= 1 && BL >= 1 && FM >= 1 && FN >= 1, "tile too small");
-    static_assert(TM % (4 * RPI) == 0 && TN % (4 * RPI) == 0, "tile rows must fill wave loads");
+    static_assert(TM % (NW * RPI) == 0 && TN % (NW * RPI) == 0, "tile rows must fill wave loads");
+    static_assert(NW == 4 || NW == 8, "4 or 8 waves");
     static_assert(NS >= 2 && (NS - 2) * LPS < 64, "pipeline depth");
 
     __shared__ __attribute__((aligned(1024))) int8_t smem[NS * STAGE];
@@ -176,8 +74,8 @@ __global__ __launch_bounds__(256) void conv_igemm_kernel(IgemmArgs a)
     const int m0 = (tile / a.tiles_n) * TM;
     const int n0 = (tile % a.tiles_n) * TN;
 
-    // ---- load geometry: load i of this wave fills LDS block i*4+wave (rows
-    // (i*4+wave)*RPI ...), lane -> row + lane/CPS, physical chunk lane%CPS.
+    // ---- load geometry: load i of this wave fills LDS block i*NW+wave (rows
+    // (i*NW+wave)*RPI ...), lane -> row + lane/CPS, physical chunk lane%CPS.
     // The logical chunk j it must fetch depends only on row bits that are
     // the same for every i, so j is one per thread.
     const int row0 = wave * RPI + lane / CPS;
@@ -186,11 +84,11 @@ __global__ __launch_bounds__(256) void conv_igemm_kernel(IgemmArgs a)
     int a_h0[AL], a_w0[AL], a_off[AL];
 #pragma unroll
     for (int i = 0; i < AL; ++i) {
-        const int m = m0 + row0 + i * 4 * RPI;
+        const int m = m0 + row0 + i * NW * RPI;
         if (m < a.M) {
-            const int n = m / a.PQ;
+            const int n = udiv(m, a.d_pq);
             const int rem = m - n * a.PQ;
-            const int p = rem / a.Q;
+            const int p = udiv(rem, a.d_q);
             const int q = rem - p * a.Q;
             a_h0[i] = p * a.strH - a.padH;
             a_w0[i] = q * a.strW - a.padW;
@@ -204,24 +102,12 @@ __global__ __launch_bounds__(256) void conv_igemm_kernel(IgemmArgs a)
     int b_off[BL];
 #pragma unroll
     for (int i = 0; i < BL; ++i) {
-        const int k = n0 + row0 + i * 4 * RPI;
+        const int k = n0 + row0 + i * NW * RPI;
         b_off[i] = k < a.K ? k * a.fK + (FLAT ? 0 : j * 16) : kOutOfRange;
     }
     if constexpr (!PIX_J) {
-        if (!a.pix_linear) {
-            for (int i = tid; i < TM; i += 256) {
-                const int m = m0 + i;
-                int o = -1;
-                if (m < a.M) {
-                    const int n = m / a.PQ;
-                    const int rem = m - n * a.PQ;
-                    const int p = rem / a.Q;
-                    const int q = rem - p * a.Q;
-                    o = n * a.oN + p * a.oP + q * a.oQ;
-                }
-                out_row[i] = o;
-            }
-        }
+        if (!a.pix_linear)
+            fill_out_rows<TM, 64 * NW>(a, m0, out_row);
     }
 
     // ---- inner-dimension position of the next stage to load ---------------
@@ -262,11 +148,11 @@ __global__ __launch_bounds__(256) void conv_igemm_kernel(IgemmArgs a)
         if (i < AL) {
             const int h = a_h0[i] + rdh, w = a_w0[i] + sdw;
             const bool ok = ((unsigned)h < (unsigned)a.H) & ((unsigned)w < (unsigned)a.W);
-            load16_to_lds(img_rsrc, lbase + i * 4096, ok ? a_off[i] + itoff : kOutOfRange);
+            load16_to_lds(img_rsrc, lbase + i * NW * 1024, ok ? a_off[i] + itoff : kOutOfRange);
         } else {
             // b_off (column past K) or ftoff (dead stage) negative: out of range
             const int b = i - AL;
-            load16_to_lds(flt_rsrc, lbase + A_BYTES + b * 4096,
+            load16_to_lds(flt_rsrc, lbase + A_BYTES + b * NW * 1024,
                           (b_off[b] | ftoff) < 0 ? kOutOfRange : b_off[b] + ftoff);
         }
     };
@@ -290,8 +176,8 @@ __global__ __launch_bounds__(256) void conv_igemm_kernel(IgemmArgs a)
         end_stage();
     };
 
-    const int wm = (wave >> 1) * WM;
-    const int wn = (wave & 1) * WN;
+    const int wm = (wave / WGN) * WM;
+    const int wn = (wave % WGN) * WN;
 
     v16i acc[FM][FN];
 #pragma unroll
@@ -367,52 +253,7 @@ __global__ __launch_bounds__(256) void conv_igemm_kernel(IgemmArgs a)
     __syncthreads();
 
     // ---- epilogue ---------------------------------------------------------
-    // 32x32 accumulator layout: lane l, value v -> MFMA row 8*(v/4) + 4*(l/32) + v%4,
-    // MFMA column l%32.  Rows come from the first MFMA operand.  Elements past
-    // M or K get an out-of-range offset and the buffer store drops them.
-    const __amdgpu_buffer_rsrc_t out_rsrc =
-        __builtin_amdgcn_make_buffer_rsrc((void *)a.out, (short)0, a.out_range, kRsrcWord3);
-#pragma unroll
-    for (int x = 0; x < FM; ++x) {
-        int pix_off_j = 0;
-        bool pix_ok_j = true;
-        if constexpr (PIX_J) {
-            const int m = m0 + wm + x * 32 + (lane & 31);
-            pix_ok_j = m < a.M;
-            const int n = m / a.PQ;
-            const int rem = m - n * a.PQ;
-            const int p = rem / a.Q;
-            const int q = rem - p * a.Q;
-            pix_off_j = n * a.oN + p * a.oP + q * a.oQ;
-        }
-#pragma unroll
-        for (int y = 0; y < FN; ++y) {
-#pragma unroll
-            for (int v = 0; v < 16; ++v) {
-                const int mrow = 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
-                const int mcol = lane & 31;
-                int off;
-                if constexpr (PIX_J) {
-                    const int kk = n0 + wn + y * 32 + mrow;
-                    off = (pix_ok_j && kk < a.K) ? (pix_off_j + kk * a.oK) * 4 : kOutOfRange;
-                } else {
-                    const int prow = wm + x * 32 + mrow;
-                    const int kk = n0 + wn + y * 32 + mcol;
-                    int po;
-                    bool ok;
-                    if (a.pix_linear) {
-                        ok = m0 + prow < a.M;
-                        po = (m0 + prow) * a.pix_stride;
-                    } else {
-                        po = out_row[prow];
-                        ok = po >= 0;
-                    }
-                    off = (ok && kk < a.K) ? (po + kk * a.oK) * 4 : kOutOfRange;
-                }
-                __builtin_amdgcn_raw_buffer_store_b32(acc[x][y][v], out_rsrc, off, 0, 0);
-            }
-        }
-    }
+    store_tile<FM, FN, PIX_J>(a, acc, m0, n0, wm, wn, lane, out_row);
 }
 
 }  // namespace convi8

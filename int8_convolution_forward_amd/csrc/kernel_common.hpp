@@ -1,0 +1,226 @@
+// Shared pieces of the INT8 conv_fprop kernels for gfx950 (CDNA4): kernel
+// arguments, buffer-resource and direct-to-LDS load helpers, LDS swizzles,
+// division by launch-invariant divisors, the XCD-aware tile order and the
+// INT32 epilogue.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace convi8 {
+
+typedef int v4i __attribute__((ext_vector_type(4)));
+typedef int v16i __attribute__((ext_vector_type(16)));
+typedef __attribute__((address_space(3))) void lds_void;
+
+// Buffer offset that always lies outside a resource (ranges are < 2^31).
+constexpr int kOutOfRange = (int)0x80000000u;
+// Buffer resource word 3 for gfx9-family raw buffer access (32-bit data format).
+constexpr int kRsrcWord3 = 0x00020000;
+
+// floor(n / d) for 0 <= n < 2^31 as (umulhi(n, m) + n) >> l, with
+// l = ceil(log2 d) and m = floor(2^32 (2^l - d) / d) + 1 (computed on the host).
+struct Divisor {
+    unsigned m;
+    int l;
+};
+
+__device__ __forceinline__ int udiv(int n, Divisor d)
+{
+    return (int)((__umulhi((unsigned)n, d.m) + (unsigned)n) >> d.l);
+}
+
+struct IgemmArgs {
+    const int8_t *img;   // image, channel-innermost; (0,0,0,0) at img
+    const int8_t *flt;   // filter K,R,S,C with C innermost
+    int32_t *out;        // output element (0,0,0,0)
+    int img_range;       // bytes addressable from img (buffer range)
+    int flt_range;       // bytes addressable from flt
+    int N, H, W, C;      // C: channels as stored (multiple of 16)
+    int sN, sH, sW;      // image strides in bytes (channel stride is 1)
+    int K, R, S;
+    int fK, fR, fS;      // filter strides in bytes (channel stride is 1)
+    int P, Q, PQ, M;     // M = N*P*Q
+    int strH, strW, dilH, dilW, padH, padW;
+    int oN, oK, oP, oQ;  // output strides in elements (one launch spans < 2^31 bytes)
+    int out_range;       // bytes addressable from out
+    int pix_linear;      // output pixel m = (n*P + p)*Q + q lives at m*pix_stride
+    int pix_stride;
+    int nstages;         // stages of BK bytes of the inner dimension
+    int cc;              // C / 16
+    float inv_cc, inv_s; // 1.0f / cc, 1.0f / S (flat order index split)
+    int tiles_n;         // column tiles
+    int tiles;           // total tiles
+    Divisor d_pq, d_q;   // division by P*Q and by Q (pixel index -> n, p, q)
+    // footprint ("halo") kernel only
+    int Hp;              // padded image height H + pre_h + post_h
+    int Wf;              // footprint width (Q-1)*stride_w + (S-1)*dil_w + 1
+    float inv_wf, inv_hp;
+    int npieces;         // footprint pieces loaded per channel block
+    int ncblk;           // channel blocks of 64
+};
+
+// s_waitcnt immediate (gfx9 encoding): wait until at most `vm` vector-memory
+// operations are outstanding and all LDS operations are done.
+template <int VM>
+__device__ __forceinline__ void wait_vm_lgkm0()
+{
+    static_assert(VM >= 0 && VM < 64, "vmcnt out of range");
+    __builtin_amdgcn_s_waitcnt((VM & 15) | ((VM >> 4) << 14) | (7 << 4) | (0 << 8));
+}
+
+template <int BK>
+__device__ __forceinline__ int swizzle_chunk(int row, int chunk)
+{
+    // 64-byte rows (4 chunks) use row bits 1..3, 128-byte rows (8 chunks) row
+    // bits 0..3: any 8 (32 banks) or 16 (64 banks) consecutive rows reading one
+    // logical chunk land on distinct banks.
+    if constexpr (BK == 64)
+        return chunk ^ (((row >> 1) ^ (row >> 2)) & 3);
+    else
+        return chunk ^ ((row ^ (row >> 1)) & 7);
+}
+
+// Buffer resource (gfx9 layout): base address, stride 0, byte range,
+// format word.  Built from kernel arguments, so it is wave-uniform.
+__device__ __forceinline__ v4i make_rsrc(const void *p, int range)
+{
+    const unsigned long long a = (unsigned long long)p;
+    v4i d;
+    d.x = (int)(unsigned)a;
+    d.y = (int)((a >> 32) & 0xFFFFu);
+    d.z = range;
+    d.w = kRsrcWord3;
+    return d;
+}
+
+// 16 bytes per lane from buffer offset `voff` straight into LDS: lane i's
+// bytes land at lds + 16*i (a wave fills one contiguous 1 KiB block).  An
+// offset outside the range writes zeros.  Written as inline assembly so the
+// compiler does not add a wait for these loads before every LDS read (it
+// cannot tell which ring slot they fill); the kernel counts them itself with
+// s_waitcnt vmcnt.
+__device__ __forceinline__ void load16_to_lds(v4i rsrc, unsigned lds_addr, int voff)
+{
+    asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+                 :: "s"(lds_addr), "v"(voff), "s"(rsrc) : "memory", "m0");
+}
+
+// LDS byte address of a __shared__ object.
+__device__ __forceinline__ unsigned lds_address(const void *p)
+{
+    return (unsigned)(unsigned long long)(lds_void *)p;
+}
+
+// floor(n / d) for 0 <= n < 2^22 and 1 <= d < 2^22, with inv = 1.0f / d
+// rounded to float: the quotient of n + 1/2 stays more than 1/(2d) away
+// from the next integer while the float error is below n / (d * 2^23).
+__device__ __forceinline__ int fdiv(int n, int d, float inv)
+{
+    (void)d;
+    return (int)(((float)n + 0.5f) * inv);
+}
+
+
+// Workgroups are dealt round-robin to the 8 XCDs; give each XCD a contiguous
+// run of tiles (column tiles of one row tile are adjacent) so that the image
+// rows a run reads stay in that XCD's L2.
+__device__ __forceinline__ int xcd_tile(int bid, int tiles)
+{
+    const int per = tiles >> 3, rem = tiles & 7;
+    const int xcd = bid & 7, idx = bid >> 3;
+    return xcd < rem ? xcd * (per + 1) + idx : rem * (per + 1) + (xcd - rem) * per + idx;
+}
+
+// Output-row offsets (elements) of the tile's TM pixels, or -1 past M, for
+// outputs whose pixels are not equally spaced.
+template <int TM, int NT>
+__device__ __forceinline__ void fill_out_rows(const IgemmArgs &a, int m0, int *out_row)
+{
+    for (int i = threadIdx.x; i < TM; i += NT) {
+        const int m = m0 + i;
+        int o = -1;
+        if (m < a.M) {
+            const int n = udiv(m, a.d_pq);
+            const int rem = m - n * a.PQ;
+            const int p = udiv(rem, a.d_q);
+            const int q = rem - p * a.Q;
+            o = n * a.oN + p * a.oP + q * a.oQ;
+        }
+        out_row[i] = o;
+    }
+}
+
+// INT32 epilogue.  32x32 accumulator layout: lane l, value v -> MFMA row
+// 8*(v/4) + 4*(l/32) + v%4, MFMA column l%32; rows come from the first MFMA
+// operand.  Elements past M or K get an out-of-range offset and the buffer
+// store drops them, so no branch guards a store.
+template <int FM, int FN, bool PIX_J>
+__device__ __forceinline__ void store_tile(const IgemmArgs &a, v16i (&acc)[FM][FN], int m0, int n0,
+                                           int wm, int wn, int lane, const int *out_row)
+{
+    const __amdgpu_buffer_rsrc_t out_rsrc =
+        __builtin_amdgcn_make_buffer_rsrc((void *)a.out, (short)0, a.out_range, kRsrcWord3);
+    const int mcol = lane & 31;
+    const int mrow0 = 4 * (lane >> 5);
+    if constexpr (PIX_J) {
+        // lanes walk pixels: one pixel per (lane, x), channels along v
+#pragma unroll
+        for (int x = 0; x < FM; ++x) {
+            const int m = m0 + wm + x * 32 + mcol;
+            const bool pix_ok = m < a.M;
+            const int n = udiv(m, a.d_pq);
+            const int rem = m - n * a.PQ;
+            const int p = udiv(rem, a.d_q);
+            const int q = rem - p * a.Q;
+            const int pix_off = n * a.oN + p * a.oP + q * a.oQ;
+#pragma unroll
+            for (int y = 0; y < FN; ++y) {
+                const int kb = n0 + wn + y * 32 + mrow0;
+#pragma unroll
+                for (int v = 0; v < 16; ++v) {
+                    const int kk = kb + 8 * (v >> 2) + (v & 3);
+                    const int off = (pix_ok && kk < a.K) ? (pix_off + kk * a.oK) * 4 : kOutOfRange;
+                    __builtin_amdgcn_raw_buffer_store_b32(acc[x][y][v], out_rsrc, off, 0, 0);
+                }
+            }
+        }
+    } else if (a.pix_linear) {
+        // lanes walk channels; pixel m sits at m * pix_stride
+#pragma unroll
+        for (int y = 0; y < FN; ++y) {
+            const int kk = n0 + wn + y * 32 + mcol;
+            const bool k_ok = kk < a.K;
+            const int koff = kk * a.oK;
+#pragma unroll
+            for (int x = 0; x < FM; ++x) {
+                const int mb = m0 + wm + x * 32 + mrow0;
+#pragma unroll
+                for (int v = 0; v < 16; ++v) {
+                    const int m = mb + 8 * (v >> 2) + (v & 3);
+                    const int off = (k_ok && m < a.M) ? (m * a.pix_stride + koff) * 4 : kOutOfRange;
+                    __builtin_amdgcn_raw_buffer_store_b32(acc[x][y][v], out_rsrc, off, 0, 0);
+                }
+            }
+        }
+    } else {
+        // lanes walk channels; pixel offsets from the table
+#pragma unroll
+        for (int y = 0; y < FN; ++y) {
+            const int kk = n0 + wn + y * 32 + mcol;
+            const bool k_ok = kk < a.K;
+            const int koff = kk * a.oK;
+#pragma unroll
+            for (int x = 0; x < FM; ++x) {
+#pragma unroll
+                for (int v = 0; v < 16; ++v) {
+                    const int po = out_row[wm + x * 32 + mrow0 + 8 * (v >> 2) + (v & 3)];
+                    const int off = (k_ok && po >= 0) ? (po + koff) * 4 : kOutOfRange;
+                    __builtin_amdgcn_raw_buffer_store_b32(acc[x][y][v], out_rsrc, off, 0, 0);
+                }
+            }
+        }
+    }
+}
+
+}  // namespace convi8
