@@ -195,31 +195,7 @@ conv_i8_status_t analyze(const conv_i8_desc_t *image, const conv_i8_desc_t *filt
 // ---------------------------------------------------------------------------
 // Tile configurations instantiated for the implicit-GEMM kernels.
 // ---------------------------------------------------------------------------
-struct TileCfg {
-    const char *name;  // CONV_I8_TILE value that forces this shape
-    int tm, tn, bk, ns;
-    int waves;         // 4 (2x2 wave grid) or 8 (4x2)
-    bool halo;         // footprint kernel (image loaded once per channel block)
-    int fls, fpix;     // halo: footprint loads per stage, footprint capacity (pixels)
-    double eff;        // relative MFMA efficiency of this tile shape (cost model)
-};
-
-const TileCfg kTiles[] = {
-    {"64x64x64", 64, 64, 64, 4, 4, false, 0, 0, 0.55},
-    {"128x64x64", 128, 64, 64, 4, 4, false, 0, 0, 0.75},
-    {"64x128x64", 64, 128, 64, 4, 4, false, 0, 0, 0.75},
-    {"128x128x64", 128, 128, 64, 4, 4, false, 0, 0, 0.9},
-    {"128x128x128", 128, 128, 128, 3, 4, false, 0, 0, 0.95},
-    {"256x128x64", 256, 128, 64, 4, 4, false, 0, 0, 1.0},
-    {"128x256x64", 128, 256, 64, 4, 4, false, 0, 0, 1.0},
-    {"h256x128", 256, 128, 64, 4, 4, true, 2, 512, 1.0},
-    {"h128x128", 128, 128, 64, 4, 4, true, 1, 256, 0.9},
-    {"h128x64", 128, 64, 64, 4, 4, true, 1, 256, 0.75},
-    {"w256x128x64", 256, 128, 64, 4, 8, false, 0, 0, 1.1},
-    {"w128x128x64", 128, 128, 64, 4, 8, false, 0, 0, 1.0},
-    {"w256x128x128", 256, 128, 128, 3, 8, false, 0, 0, 1.15},
-};
-constexpr int kNumTiles = sizeof(kTiles) / sizeof(kTiles[0]);
+using Launcher = void (*)(bool flat, bool pix_j, dim3 grid, hipStream_t stream, const IgemmArgs &a);
 
 template <int TM, int TN, int BK, int NS, int WGM = 2, int WGN = 2>
 void launch_cfg(bool flat, bool pix_j, dim3 grid, hipStream_t stream, const IgemmArgs &a)
@@ -238,34 +214,44 @@ void launch_cfg(bool flat, bool pix_j, dim3 grid, hipStream_t stream, const Igem
     }
 }
 
-template <int TM, int TN, int NS, int FLS, int FPIX>
-void launch_halo(bool pix_j, dim3 grid, hipStream_t stream, const IgemmArgs &a)
+template <int TM, int TN, int NS, int FLS, int FPIX, int WGM = 2, int WGN = 2>
+void launch_halo(bool, bool pix_j, dim3 grid, hipStream_t stream, const IgemmArgs &a)
 {
+    const dim3 block(64 * WGM * WGN);
     if (pix_j)
-        hipLaunchKernelGGL((conv_halo_kernel<TM, TN, NS, FLS, FPIX, true>), grid, dim3(256), 0, stream, a);
+        hipLaunchKernelGGL((conv_halo_kernel<TM, TN, NS, FLS, FPIX, WGM, WGN, true>), grid, block, 0, stream, a);
     else
-        hipLaunchKernelGGL((conv_halo_kernel<TM, TN, NS, FLS, FPIX, false>), grid, dim3(256), 0, stream, a);
+        hipLaunchKernelGGL((conv_halo_kernel<TM, TN, NS, FLS, FPIX, WGM, WGN, false>), grid, block, 0, stream, a);
 }
 
-void launch_igemm(int cfg, bool flat, bool pix_j, dim3 grid, hipStream_t stream, const IgemmArgs &a)
-{
-    switch (cfg) {
-    case 0: launch_cfg<64, 64, 64, 4>(flat, pix_j, grid, stream, a); break;
-    case 1: launch_cfg<128, 64, 64, 4>(flat, pix_j, grid, stream, a); break;
-    case 2: launch_cfg<64, 128, 64, 4>(flat, pix_j, grid, stream, a); break;
-    case 3: launch_cfg<128, 128, 64, 4>(flat, pix_j, grid, stream, a); break;
-    case 4: launch_cfg<128, 128, 128, 3>(flat, pix_j, grid, stream, a); break;
-    case 5: launch_cfg<256, 128, 64, 4>(flat, pix_j, grid, stream, a); break;
-    case 6: launch_cfg<128, 256, 64, 4>(flat, pix_j, grid, stream, a); break;
-    case 7: launch_halo<256, 128, 4, 2, 512>(pix_j, grid, stream, a); break;
-    case 8: launch_halo<128, 128, 4, 1, 256>(pix_j, grid, stream, a); break;
-    case 9: launch_halo<128, 64, 4, 1, 256>(pix_j, grid, stream, a); break;
-    case 10: launch_cfg<256, 128, 64, 4, 4, 2>(flat, pix_j, grid, stream, a); break;
-    case 11: launch_cfg<128, 128, 64, 4, 4, 2>(flat, pix_j, grid, stream, a); break;
-    case 12: launch_cfg<256, 128, 128, 3, 4, 2>(flat, pix_j, grid, stream, a); break;
-    default: break;
-    }
-}
+struct TileCfg {
+    const char *name;  // CONV_I8_TILE value that forces this shape
+    int tm, tn, bk, ns;
+    int waves;         // 4 (2x2 wave grid) or 8 (4x2)
+    bool halo;         // footprint kernel (image loaded once per channel block)
+    int fls, fpix;     // halo: footprint loads per stage, footprint capacity (pixels)
+    double eff;        // relative MFMA efficiency of this tile shape (cost model)
+    Launcher launch;   // the kernel instantiation with exactly these parameters
+};
+
+const TileCfg kTiles[] = {
+    {"64x64x64", 64, 64, 64, 4, 4, false, 0, 0, 0.40, launch_cfg<64, 64, 64, 4>},
+    {"128x64x64", 128, 64, 64, 4, 4, false, 0, 0, 0.48, launch_cfg<128, 64, 64, 4>},
+    {"64x128x64", 64, 128, 64, 4, 4, false, 0, 0, 0.48, launch_cfg<64, 128, 64, 4>},
+    {"128x128x64", 128, 128, 64, 4, 4, false, 0, 0, 0.59, launch_cfg<128, 128, 64, 4>},
+    {"128x128x128", 128, 128, 128, 3, 4, false, 0, 0, 0.55, launch_cfg<128, 128, 128, 3>},
+    {"256x128x64", 256, 128, 64, 4, 4, false, 0, 0, 0.52, launch_cfg<256, 128, 64, 4>},
+    {"128x256x64", 128, 256, 64, 4, 4, false, 0, 0, 0.50, launch_cfg<128, 256, 64, 4>},
+    {"w256x128x64", 256, 128, 64, 4, 8, false, 0, 0, 0.56, launch_cfg<256, 128, 64, 4, 4, 2>},
+    {"w128x128x64", 128, 128, 64, 4, 8, false, 0, 0, 0.56, launch_cfg<128, 128, 64, 4, 4, 2>},
+    {"w256x128x128", 256, 128, 128, 3, 8, false, 0, 0, 0.76, launch_cfg<256, 128, 128, 3, 4, 2>},
+    {"h256x128", 256, 128, 64, 4, 4, true, 2, 512, 0.42, launch_halo<256, 128, 4, 2, 512>},
+    {"h128x128", 128, 128, 64, 4, 4, true, 1, 256, 0.43, launch_halo<128, 128, 4, 1, 256>},
+    {"h128x64", 128, 64, 64, 4, 4, true, 1, 256, 0.35, launch_halo<128, 64, 4, 1, 256>},
+    {"hw256x128", 256, 128, 64, 4, 8, true, 1, 512, 0.42, launch_halo<256, 128, 4, 1, 512, 4, 2>},
+    {"hw128x128", 128, 128, 64, 4, 8, true, 1, 256, 0.40, launch_halo<128, 128, 4, 1, 256, 4, 2>},
+};
+constexpr int kNumTiles = sizeof(kTiles) / sizeof(kTiles[0]);
 
 // Division by a launch-invariant divisor d >= 1 for dividends below 2^31:
 // l = ceil(log2 d), m = floor(2^32 (2^l - d) / d) + 1.
@@ -486,12 +472,12 @@ conv_i8_status_t make_plan(const Problem &pb, const void *x_ptr, const void *w_p
             // footprint pieces, and a footprint that fits
             if (cc % 4 != 0 || Hp >= (1 << 20) || Wf >= (1 << 20))
                 continue;
-            const int64_t np = std::min<int64_t>(RS - c.ns + 1, (int64_t)c.fpix * 64 / (c.fls * 4096));
+            const int64_t np = std::min<int64_t>(RS - c.ns + 1, (int64_t)c.fpix * 64 / (c.fls * 1024 * c.waves));
             if (np < 1)
                 continue;
             const int64_t fmax = max_footprint(M, pb.P * pb.Q, pb.Q, Hp, Wf, pb.str[0],
                                                (pb.R - 1) * pb.dil[0], c.tm);
-            if (fmax > std::min<int64_t>(np * c.fls * 64, c.fpix))
+            if (fmax > std::min<int64_t>(np * c.fls * 16 * c.waves, c.fpix))
                 continue;
             bytes = (double)c.tn * stages * 64 + (double)(cc / 4) * fmax * 64;
         } else {
@@ -500,11 +486,18 @@ conv_i8_status_t make_plan(const Problem &pb, const void *x_ptr, const void *w_p
         double eff = c.eff;
         if (!c.halo && cc % cps != 0)
             eff *= chunks > 0 ? (double)chunks / (double)(stages * cps) : 1.0;
+        // fitted to measured kernel times: MFMA time at the shape's efficiency
+        // plus half the operand-load time (the two overlap only partly) plus
+        // the tile's INT32 stores at one CU's share of ~5 TB/s
         const double t_mfma = (double)c.tm * c.tn * stages * c.bk / mac_per_s_cu / eff;
         const double t_load = bytes / bytes_per_s_cu;
+        const double t_store = (double)c.tm * c.tn * 4 / (5e12 / kCUs);
         const int64_t tiles = ((M + c.tm - 1) / c.tm) * ((pb.K + c.tn - 1) / c.tn);
         const int64_t rounds = (tiles + kCUs - 1) / kCUs;
-        const double cost = (double)rounds * std::max(t_mfma, t_load);
+        const double cost = (double)rounds * (t_mfma + 0.5 * t_load + t_store);
+        if (getenv("CONV_I8_COST"))
+            fprintf(stderr, "conv_i8 cost %-14s tiles %7lld rounds %4lld mfma %.2f load %.2f store %.2f -> %.2f us\n",
+                    c.name, (long long)tiles, (long long)rounds, t_mfma * 1e6, t_load * 1e6, t_store * 1e6, cost * 1e6);
         if (best < 0 || cost < best_cost * (1 - 1e-9)) {
             best = i;
             best_cost = cost;
@@ -512,7 +505,10 @@ conv_i8_status_t make_plan(const Problem &pb, const void *x_ptr, const void *w_p
     }
     if (best < 0) {
         // unknown or inapplicable CONV_I8_TILE value: default shape
-        best = 3;
+        best = 0;
+        for (int i = 0; i < kNumTiles; ++i)
+            if (strcmp(kTiles[i].name, "128x128x64") == 0)
+                best = i;
     }
     pl->cfg = best;
     const TileCfg &c = kTiles[best];
@@ -522,7 +518,7 @@ conv_i8_status_t make_plan(const Problem &pb, const void *x_ptr, const void *w_p
     if (c.halo) {
         pl->Hp = Hp;
         pl->Wf = Wf;
-        pl->npieces = std::min<int64_t>(RS - c.ns + 1, (int64_t)c.fpix * 64 / (c.fls * 4096));
+        pl->npieces = std::min<int64_t>(RS - c.ns + 1, (int64_t)c.fpix * 64 / (c.fls * 1024 * c.waves));
     }
     return CONV_I8_OK;
 }
@@ -647,7 +643,7 @@ conv_i8_status_t run(const Problem &pb, const Plan &pl, const void *x_ptr, const
         if (tiles == 0)
             continue;
         a.tiles = (int)tiles;
-        launch_igemm(pl.cfg, !pl.blocked, pl.pix_j, dim3((unsigned)tiles), stream, a);
+        c.launch(!pl.blocked, pl.pix_j, dim3((unsigned)tiles), stream, a);
         if (hipGetLastError() != hipSuccess)
             return CONV_I8_ERR_HIP;
     }

@@ -35,26 +35,28 @@ __device__ __forceinline__ int fp_swizzle(int fp, int chunk)
     return chunk ^ ((fp >> 2) & 3);
 }
 
-template <int TM, int TN, int NS, int FLS, int FPIX, bool PIX_J>
-__global__ __launch_bounds__(256) void conv_halo_kernel(IgemmArgs a)
+template <int TM, int TN, int NS, int FLS, int FPIX, int WGM, int WGN, bool PIX_J>
+__global__ __launch_bounds__(64 * WGM * WGN) void conv_halo_kernel(IgemmArgs a)
 {
+    constexpr int NW = WGM * WGN;           // waves per workgroup
+    constexpr int GB = NW * 1024;           // bytes one workgroup-wide load fills
     constexpr int BK = 64;                  // channels (bytes) per stage
-    constexpr int BL = TN / 64;             // filter-row loads per thread per stage
+    constexpr int BL = TN / (NW * 16);      // filter-row loads per thread per stage
     constexpr int LPS = BL + FLS;           // loads per thread per stage
     constexpr int B_BYTES = TN * BK;        // one ring slot
     constexpr int FBUF = FPIX * 64;         // one footprint buffer
-    constexpr int NG = FBUF / 4096;         // 4 KiB load groups per footprint buffer
-    constexpr int WM = TM / 2, WN = TN / 2;
+    constexpr int NG = FBUF / GB;           // load groups per footprint buffer
+    constexpr int WM = TM / WGM, WN = TN / WGN;
     constexpr int FM = WM / 32, FN = WN / 32;
     constexpr int KS = BK / 32;
     constexpr int NMF = KS * FM * FN;
     constexpr int NRD = KS * (FM + FN);
-    static_assert(BL >= 1 && FM >= 1 && FN >= 1 && NG % FLS == 0, "tile shape");
+    static_assert(BL >= 1 && FM >= 1 && FN >= 1 && NG % FLS == 0 && TN % (NW * 16) == 0, "tile shape");
     static_assert(NS >= 2 && (NS - 2) * LPS + NG < 64, "pipeline depth");
 
     __shared__ __attribute__((aligned(1024))) int8_t ring[NS * B_BYTES];
     __shared__ __attribute__((aligned(1024))) int8_t fbuf[2 * FBUF];
-    __shared__ __attribute__((aligned(1024))) int8_t scratch[4096];
+    __shared__ __attribute__((aligned(1024))) int8_t scratch[GB];
     __shared__ int out_row[PIX_J ? 1 : TM];
 
     const int tid = threadIdx.x;
@@ -63,8 +65,8 @@ __global__ __launch_bounds__(256) void conv_halo_kernel(IgemmArgs a)
     const int tile = xcd_tile(blockIdx.x, a.tiles);
     const int m0 = (tile / a.tiles_n) * TM;
     const int n0 = (tile % a.tiles_n) * TN;
-    const int wm = (wave >> 1) * WM;
-    const int wn = (wave & 1) * WN;
+    const int wm = (wave / WGN) * WM;
+    const int wn = (wave % WGN) * WN;
 
     // ---- footprint geometry of this tile (uniform) ------------------------
     const int m_last = min(m0 + TM, a.M) - 1;
@@ -93,13 +95,13 @@ __global__ __launch_bounds__(256) void conv_halo_kernel(IgemmArgs a)
     }
 
     // ---- footprint loads: group g of this wave fills LDS bytes
-    // g*4096 + wave*1024 + lane*16, i.e. pixel g*64 + wave*16 + lane/4,
+    // g*GB + wave*1024 + lane*16, i.e. pixel g*GB/64 + wave*16 + lane/4,
     // physical chunk lane%4; the logical chunk depends on pixel bits 2..3,
     // which are lane bits 4..5 for every g.
     const int jf = fp_swizzle(lane >> 2, lane & 3);
     // buffer offset of this thread's 16 bytes of group g for channel block c
     auto foot_off = [&](int c, int g) -> int {
-        const int fp = g * 64 + wave * 16 + (lane >> 2);
+        const int fp = g * (GB / 64) + wave * 16 + (lane >> 2);
         const int fr = fdiv(fp, a.Wf, a.inv_wf);
         const int fc = fp - fr * a.Wf;
         const int hr = hp_a + fr;
@@ -117,12 +119,12 @@ __global__ __launch_bounds__(256) void conv_halo_kernel(IgemmArgs a)
     int b_off[BL];
 #pragma unroll
     for (int i = 0; i < BL; ++i) {
-        const int k = n0 + row0 + i * 64;
+        const int k = n0 + row0 + i * NW * 16;
         b_off[i] = k < a.K ? k * a.fK + jb * 16 : kOutOfRange;
     }
     if constexpr (!PIX_J) {
         if (!a.pix_linear)
-            fill_out_rows<TM, 256>(a, m0, out_row);
+            fill_out_rows<TM, 64 * NW>(a, m0, out_row);
     }
 
     const v4i img_rsrc = make_rsrc(a.img, a.img_range);
@@ -134,7 +136,7 @@ __global__ __launch_bounds__(256) void conv_halo_kernel(IgemmArgs a)
 
     // footprint load of group g for channel block c into buffer c % 2
     auto foot_one = [&](int c, int g) {
-        load16_to_lds(img_rsrc, fbuf_lds + (c & 1) * FBUF + g * 4096 + wave * 1024, foot_off(c, g));
+        load16_to_lds(img_rsrc, fbuf_lds + (c & 1) * FBUF + g * GB + wave * 1024, foot_off(c, g));
     };
 
     // issue side: stage (ic, it_) = (channel block, tap index), tap (ir, is)
@@ -154,7 +156,7 @@ __global__ __launch_bounds__(256) void conv_halo_kernel(IgemmArgs a)
     };
     auto dma_one = [&](int i) {  // i < LPS
         if (i < BL) {
-            load16_to_lds(flt_rsrc, lslot + i * 4096,
+            load16_to_lds(flt_rsrc, lslot + i * GB,
                           (b_off[i] | ftoff) < 0 ? kOutOfRange : b_off[i] + ftoff);
         } else {
             // group pg+f of the next block's footprint, or an out-of-range
@@ -162,7 +164,7 @@ __global__ __launch_bounds__(256) void conv_halo_kernel(IgemmArgs a)
             // past the last block, where the channel test fails)
             const int f = i - BL;
             const int g = pg + f;
-            const unsigned dst = piece ? fbuf_lds + ((ic + 1) & 1) * FBUF + g * 4096 + wave * 1024
+            const unsigned dst = piece ? fbuf_lds + ((ic + 1) & 1) * FBUF + g * GB + wave * 1024
                                        : scratch_lds;
             load16_to_lds(img_rsrc, dst, piece ? foot_off(ic + 1, g) : kOutOfRange);
         }

@@ -132,7 +132,7 @@ def test_repeat_runs_identical(ci8):
 # ---------------------------------------------------------------------------
 TILES = ["64x64x64", "128x64x64", "64x128x64", "128x128x64", "128x128x128", "256x128x64",
          "128x256x64", "h256x128", "h128x128", "h128x64", "w256x128x64", "w128x128x64",
-         "w256x128x128"]
+         "w256x128x128", "hw256x128", "hw128x128"]
 
 
 @pytest.mark.parametrize("tile", TILES)
@@ -330,7 +330,7 @@ HALO_CASES = [
 ]
 
 
-@pytest.mark.parametrize("tile", ["h256x128", "h128x128", "h128x64"])
+@pytest.mark.parametrize("tile", ["h256x128", "h128x128", "h128x64", "hw256x128", "hw128x128"])
 @pytest.mark.parametrize("case_i", range(len(HALO_CASES)))
 @pytest.mark.parametrize("out_layout", ["nhwc", "nchw"])
 def test_footprint_kernel(ci8, monkeypatch, tile, case_i, out_layout):
