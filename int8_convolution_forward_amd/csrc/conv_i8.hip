@@ -18,7 +18,7 @@
 #include <algorithm>
 #include <string>
 
-#include "halo_kernel.hpp"
+#include "footprint_kernel.hpp"
 #include "igemm_kernel.hpp"
 #include "repack_kernel.hpp"
 
@@ -214,42 +214,40 @@ void launch_cfg(bool flat, bool pix_j, dim3 grid, hipStream_t stream, const Igem
     }
 }
 
-template <int TM, int TN, int NS, int FLS, int FPIX, int WGM = 2, int WGN = 2>
-void launch_halo(bool, bool pix_j, dim3 grid, hipStream_t stream, const IgemmArgs &a)
+template <int TM, int TN, int NS, int FPIX, int WGM = 2, int WGN = 2>
+void launch_fp3x3(bool, bool pix_j, dim3 grid, hipStream_t stream, const IgemmArgs &a)
 {
     const dim3 block(64 * WGM * WGN);
     if (pix_j)
-        hipLaunchKernelGGL((conv_halo_kernel<TM, TN, NS, FLS, FPIX, WGM, WGN, true>), grid, block, 0, stream, a);
+        hipLaunchKernelGGL((conv_footprint3x3_kernel<TM, TN, NS, FPIX, WGM, WGN, true>), grid, block, 0, stream, a);
     else
-        hipLaunchKernelGGL((conv_halo_kernel<TM, TN, NS, FLS, FPIX, WGM, WGN, false>), grid, block, 0, stream, a);
+        hipLaunchKernelGGL((conv_footprint3x3_kernel<TM, TN, NS, FPIX, WGM, WGN, false>), grid, block, 0, stream, a);
 }
 
 struct TileCfg {
     const char *name;  // CONV_I8_TILE value that forces this shape
     int tm, tn, bk, ns;
     int waves;         // 4 (2x2 wave grid) or 8 (4x2)
-    bool halo;         // footprint kernel (image loaded once per channel block)
-    int fls, fpix;     // halo: footprint loads per stage, footprint capacity (pixels)
+    bool footprint;    // 3x3 footprint kernel (image loaded once per 64-channel block)
+    int fpix;          // footprint capacity (pixels)
     double eff;        // relative MFMA efficiency of this tile shape (cost model)
     Launcher launch;   // the kernel instantiation with exactly these parameters
 };
 
 const TileCfg kTiles[] = {
-    {"64x64x64", 64, 64, 64, 4, 4, false, 0, 0, 0.40, launch_cfg<64, 64, 64, 4>},
-    {"128x64x64", 128, 64, 64, 4, 4, false, 0, 0, 0.48, launch_cfg<128, 64, 64, 4>},
-    {"64x128x64", 64, 128, 64, 4, 4, false, 0, 0, 0.48, launch_cfg<64, 128, 64, 4>},
-    {"128x128x64", 128, 128, 64, 4, 4, false, 0, 0, 0.59, launch_cfg<128, 128, 64, 4>},
-    {"128x128x128", 128, 128, 128, 3, 4, false, 0, 0, 0.55, launch_cfg<128, 128, 128, 3>},
-    {"256x128x64", 256, 128, 64, 4, 4, false, 0, 0, 0.52, launch_cfg<256, 128, 64, 4>},
-    {"128x256x64", 128, 256, 64, 4, 4, false, 0, 0, 0.50, launch_cfg<128, 256, 64, 4>},
-    {"w256x128x64", 256, 128, 64, 4, 8, false, 0, 0, 0.56, launch_cfg<256, 128, 64, 4, 4, 2>},
-    {"w128x128x64", 128, 128, 64, 4, 8, false, 0, 0, 0.56, launch_cfg<128, 128, 64, 4, 4, 2>},
-    {"w256x128x128", 256, 128, 128, 3, 8, false, 0, 0, 0.76, launch_cfg<256, 128, 128, 3, 4, 2>},
-    {"h256x128", 256, 128, 64, 4, 4, true, 2, 512, 0.42, launch_halo<256, 128, 4, 2, 512>},
-    {"h128x128", 128, 128, 64, 4, 4, true, 1, 256, 0.43, launch_halo<128, 128, 4, 1, 256>},
-    {"h128x64", 128, 64, 64, 4, 4, true, 1, 256, 0.35, launch_halo<128, 64, 4, 1, 256>},
-    {"hw256x128", 256, 128, 64, 4, 8, true, 1, 512, 0.42, launch_halo<256, 128, 4, 1, 512, 4, 2>},
-    {"hw128x128", 128, 128, 64, 4, 8, true, 1, 256, 0.40, launch_halo<128, 128, 4, 1, 256, 4, 2>},
+    {"64x64x64", 64, 64, 64, 4, 4, false, 0, 0.40, launch_cfg<64, 64, 64, 4>},
+    {"128x64x64", 128, 64, 64, 4, 4, false, 0, 0.48, launch_cfg<128, 64, 64, 4>},
+    {"64x128x64", 64, 128, 64, 4, 4, false, 0, 0.48, launch_cfg<64, 128, 64, 4>},
+    {"128x128x64", 128, 128, 64, 4, 4, false, 0, 0.59, launch_cfg<128, 128, 64, 4>},
+    {"128x128x128", 128, 128, 128, 3, 4, false, 0, 0.55, launch_cfg<128, 128, 128, 3>},
+    {"256x128x64", 256, 128, 64, 4, 4, false, 0, 0.52, launch_cfg<256, 128, 64, 4>},
+    {"128x256x64", 128, 256, 64, 4, 4, false, 0, 0.50, launch_cfg<128, 256, 64, 4>},
+    {"w256x128x64", 256, 128, 64, 4, 8, false, 0, 0.56, launch_cfg<256, 128, 64, 4, 4, 2>},
+    {"w128x128x64", 128, 128, 64, 4, 8, false, 0, 0.56, launch_cfg<128, 128, 64, 4, 4, 2>},
+    {"w256x128x128", 256, 128, 128, 3, 8, false, 0, 0.76, launch_cfg<256, 128, 128, 3, 4, 2>},
+    {"f256x128", 256, 128, 64, 6, 4, true, 448, 0.70, launch_fp3x3<256, 128, 6, 448>},
+    {"fw256x128", 256, 128, 64, 3, 8, true, 448, 0.68, launch_fp3x3<256, 128, 3, 448, 4, 2>},
+    {"f128x128", 128, 128, 64, 6, 4, true, 384, 0.62, launch_fp3x3<128, 128, 6, 384>},
 };
 constexpr int kNumTiles = sizeof(kTiles) / sizeof(kTiles[0]);
 
@@ -311,7 +309,7 @@ struct Plan {
     int64_t y_img_span = 0;            // output elements one image spans
     bool pix_linear = false;           // output pixel m at m * pix_stride
     int64_t pix_stride = 0;
-    int64_t Hp = 0, Wf = 0, npieces = 0;  // footprint kernel geometry
+    int64_t Hp = 0, Wf = 0;            // footprint kernel geometry
 };
 
 size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
@@ -467,24 +465,21 @@ conv_i8_status_t make_plan(const Problem &pb, const void *x_ptr, const void *w_p
         const int64_t chunks = RS * cc;
         int64_t stages = cc % cps == 0 ? RS * (cc / cps) : (chunks + cps - 1) / cps;
         double bytes;
-        if (c.halo) {
-            // footprint kernel: 64-channel blocks, enough taps to carry the
-            // footprint pieces, and a footprint that fits
-            if (cc % 4 != 0 || Hp >= (1 << 20) || Wf >= (1 << 20))
-                continue;
-            const int64_t np = std::min<int64_t>(RS - c.ns + 1, (int64_t)c.fpix * 64 / (c.fls * 1024 * c.waves));
-            if (np < 1)
+        if (c.footprint) {
+            // footprint kernel: a 3x3 filter, 64-channel blocks, and a tile
+            // footprint that fits its buffers
+            if (pb.R != 3 || pb.S != 3 || cc % 4 != 0 || Hp >= (1 << 20) || Wf >= (1 << 20))
                 continue;
             const int64_t fmax = max_footprint(M, pb.P * pb.Q, pb.Q, Hp, Wf, pb.str[0],
                                                (pb.R - 1) * pb.dil[0], c.tm);
-            if (fmax > std::min<int64_t>(np * c.fls * 16 * c.waves, c.fpix))
+            if (fmax > c.fpix)
                 continue;
-            bytes = (double)c.tn * stages * 64 + (double)(cc / 4) * fmax * 64;
+            bytes = (double)c.tn * stages * 64 + (double)(cc / 4) * fmax * 80;
         } else {
             bytes = (double)(c.tm + c.tn) * stages * c.bk;
         }
         double eff = c.eff;
-        if (!c.halo && cc % cps != 0)
+        if (!c.footprint && cc % cps != 0)
             eff *= chunks > 0 ? (double)chunks / (double)(stages * cps) : 1.0;
         // fitted to measured kernel times: MFMA time at the shape's efficiency
         // plus half the operand-load time (the two overlap only partly) plus
@@ -515,10 +510,9 @@ conv_i8_status_t make_plan(const Problem &pb, const void *x_ptr, const void *w_p
     const int cps = c.bk / 16;
     pl->blocked = cc % cps == 0;
     pl->nstages = pl->blocked ? RS * (cc / cps) : (RS * cc + cps - 1) / cps;
-    if (c.halo) {
+    if (c.footprint) {
         pl->Hp = Hp;
         pl->Wf = Wf;
-        pl->npieces = std::min<int64_t>(RS - c.ns + 1, (int64_t)c.fpix * 64 / (c.fls * 1024 * c.waves));
     }
     return CONV_I8_OK;
 }
@@ -533,7 +527,7 @@ std::string describe(const Problem &pb, const Plan &pl)
              "repack_image=%d repack_filter=%d Cp=%lld tile=%s kernel=%s order=%s stages=%lld "
              "lanes=%s tiles=%lld batch_chunk=%lld workspace=%zu",
              (int)pl.repack_x, (int)pl.repack_w, (long long)pl.Cp, c.name,
-             c.halo ? "footprint" : "im2col", pl.blocked ? "blocked" : "flat", (long long)pl.nstages,
+             c.footprint ? "footprint" : "im2col", pl.blocked ? "blocked" : "flat", (long long)pl.nstages,
              pl.pix_j ? "pixels" : "channels", (long long)tiles, (long long)pl.batch_chunk,
              pl.ws_bytes);
     return buf;
@@ -628,7 +622,6 @@ conv_i8_status_t run(const Problem &pb, const Plan &pl, const void *x_ptr, const
     a.Wf = (int)pl.Wf;
     a.inv_hp = pl.Hp > 0 ? 1.0f / (float)pl.Hp : 0.0f;
     a.inv_wf = pl.Wf > 0 ? 1.0f / (float)pl.Wf : 0.0f;
-    a.npieces = (int)pl.npieces;
     a.ncblk = (int)(pl.Cp / 64);
     for (int64_t n0 = 0; n0 < pb.N; n0 += pl.batch_chunk) {
         const int64_t nb = std::min(pl.batch_chunk, pb.N - n0);

@@ -52,11 +52,10 @@ struct IgemmArgs {
     int tiles_n;         // column tiles
     int tiles;           // total tiles
     Divisor d_pq, d_q;   // division by P*Q and by Q (pixel index -> n, p, q)
-    // footprint ("halo") kernel only
+    // footprint kernel only
     int Hp;              // padded image height H + pre_h + post_h
     int Wf;              // footprint width (Q-1)*stride_w + (S-1)*dil_w + 1
     float inv_wf, inv_hp;
-    int npieces;         // footprint pieces loaded per channel block
     int ncblk;           // channel blocks of 64
 };
 

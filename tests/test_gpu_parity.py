@@ -131,14 +131,15 @@ def test_repeat_runs_identical(ci8):
 # blocked and flat inner order, channel- and pixel-innermost outputs.
 # ---------------------------------------------------------------------------
 TILES = ["64x64x64", "128x64x64", "64x128x64", "128x128x64", "128x128x128", "256x128x64",
-         "128x256x64", "h256x128", "h128x128", "h128x64", "w256x128x64", "w128x128x64",
-         "w256x128x128", "hw256x128", "hw128x128"]
+         "128x256x64", "w256x128x64", "w128x128x64", "w256x128x128", "f256x128", "fw256x128",
+         "f128x128"]
+FOOTPRINT_TILES = [t for t in TILES if t.startswith("f")]
 
 
 @pytest.mark.parametrize("tile", TILES)
 @pytest.mark.parametrize("C,out_layout", [(128, "nhwc"), (48, "nchw"), (256, "nchw"), (80, "nhwc")])
 def test_tile_shapes(ci8, monkeypatch, tile, C, out_layout):
-    if tile.startswith("h") and C % 64:
+    if tile in FOOTPRINT_TILES and C % 64:
         pytest.skip("the footprint kernel takes whole 64-channel blocks")
     monkeypatch.setenv("CONV_I8_TILE", tile)
     g = torch.Generator().manual_seed(C)
@@ -155,7 +156,7 @@ def test_tile_shapes(ci8, monkeypatch, tile, C, out_layout):
     torch.as_strided(wst, ws.dims, ws.strides).copy_(w)
     f = ci8.plan_fields(ci8.conv_fprop_i8_plan(ci8.desc(xs.dims, xs.strides, 1), ci8.desc(ws.dims, ws.strides, 1),
                                                ci8.desc(os_.dims, os_.strides, 2), (2, 1), (0, 1), (2, 1), (1, 1)))
-    if tile.startswith("h") and f["tile"] != tile:
+    if tile in FOOTPRINT_TILES and f["tile"] != tile:
         pytest.skip("footprint does not fit this tile shape")
     assert f["tile"] == tile
     run_and_check(ci8, xst, xs, wst, ws, os_, (2, 1), (0, 1), (2, 1), (1, 1), label=f"tile {tile} C={C}")
@@ -317,24 +318,27 @@ def test_batch_split_over_launches(ci8):
 
 
 # ---------------------------------------------------------------------------
-# The footprint kernel: tiles that span several images, strides, dilations,
-# asymmetric padding, ragged M and K, both output layouts.
+# The 3x3 footprint kernel: tiles that span several images, strides,
+# dilations, asymmetric padding, an odd number of 64-channel blocks (the last
+# block pair runs one all-zero block), ragged M and K, both output layouts.
 # ---------------------------------------------------------------------------
-HALO_CASES = [
+FOOTPRINT_CASES = [
     # N, C, H, W, K, R, S, stride, dil, pre, post
     (5, 64, 14, 14, 70, 3, 3, (1, 1), (1, 1), (1, 1), (1, 1)),
     (2, 128, 9, 11, 130, 3, 3, (1, 1), (1, 1), (1, 1), (1, 1)),
     (3, 64, 7, 30, 64, 3, 3, (1, 2), (1, 1), (0, 2), (1, 0)),
-    (2, 192, 6, 6, 33, 5, 5, (1, 1), (1, 1), (2, 2), (2, 2)),
-    (4, 64, 10, 9, 64, 3, 2, (1, 1), (2, 1), (2, 0), (2, 1)),
+    (2, 192, 6, 6, 33, 3, 3, (1, 1), (2, 2), (2, 2), (2, 2)),
+    (4, 64, 10, 9, 64, 3, 3, (2, 1), (2, 1), (2, 0), (2, 1)),
+    (7, 256, 5, 5, 96, 3, 3, (1, 1), (1, 1), (0, 0), (0, 0)),
+    (1, 320, 40, 3, 128, 3, 3, (1, 1), (1, 1), (1, 1), (1, 1)),
 ]
 
 
-@pytest.mark.parametrize("tile", ["h256x128", "h128x128", "h128x64", "hw256x128", "hw128x128"])
-@pytest.mark.parametrize("case_i", range(len(HALO_CASES)))
+@pytest.mark.parametrize("tile", FOOTPRINT_TILES)
+@pytest.mark.parametrize("case_i", range(len(FOOTPRINT_CASES)))
 @pytest.mark.parametrize("out_layout", ["nhwc", "nchw"])
 def test_footprint_kernel(ci8, monkeypatch, tile, case_i, out_layout):
-    N, C, H, W, K, R, S, st, dl, pre, post = HALO_CASES[case_i]
+    N, C, H, W, K, R, S, st, dl, pre, post = FOOTPRINT_CASES[case_i]
     monkeypatch.setenv("CONV_I8_TILE", tile)
     od = oracle.out_dims((N, C, H, W), (K, C, R, S), pre, post, st, dl)
     xs = wl.TensorSpec((N, C, H, W), wl.channels_last_strides((N, C, H, W)))
