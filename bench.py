@@ -187,7 +187,7 @@ def main():
                 "unit": "GB/s"}
     roof["frac"] = roof["achieved"] / roof["peak"]
     roof["traffic"] = traffic_from_profiles(c.name, alg_bytes)
-    roof["kernel"] = "conv_halo_kernel" if kf.get("kernel") == "footprint" else "conv_igemm_kernel"
+    roof["kernel"] = "conv_footprint3x3_kernel" if kf.get("kernel") == "footprint" else "conv_igemm_kernel"
     roof["kernel_tile"] = kf.get("tile")
     roof["kernel_avg_us"] = k_avg_ms * 1e3
     roof["kernel_launches_timed"] = nk

@@ -294,6 +294,22 @@ int64_t max_footprint(int64_t M, int64_t PQ, int64_t Q, int64_t Hp, int64_t Wf, 
     return best;
 }
 
+// Footprint row pitch in 16-byte slots: at least 5 slots per pixel, padded
+// so that stride_h * Pr = 5 * stride_w * Q (mod 16) where stride_h is odd;
+// then the pixels of consecutive output rows keep distinct LDS bank groups.
+int64_t footprint_pitch(int64_t Wf, int64_t Q, int64_t str_h, int64_t str_w)
+{
+    const int64_t base = 5 * Wf;
+    if (str_h % 2 == 0)
+        return base;
+    int64_t inv = 1;
+    for (int64_t i = 1; i < 16; i += 2)
+        if ((str_h * i) % 16 == 1)
+            inv = i;
+    const int64_t target = (5 * str_w * Q % 16) * inv % 16;
+    return base + ((target - base) % 16 + 16) % 16;
+}
+
 struct Plan {
     bool repack_x = false, repack_w = false;
     int64_t Cp = 0;                    // channels as the kernel reads them
@@ -309,7 +325,7 @@ struct Plan {
     int64_t y_img_span = 0;            // output elements one image spans
     bool pix_linear = false;           // output pixel m at m * pix_stride
     int64_t pix_stride = 0;
-    int64_t Hp = 0, Wf = 0;            // footprint kernel geometry
+    int64_t Hp = 0, Wf = 0, Pr = 0;    // footprint kernel geometry
 };
 
 size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
@@ -472,9 +488,10 @@ conv_i8_status_t make_plan(const Problem &pb, const void *x_ptr, const void *w_p
                 continue;
             const int64_t fmax = max_footprint(M, pb.P * pb.Q, pb.Q, Hp, Wf, pb.str[0],
                                                (pb.R - 1) * pb.dil[0], c.tm);
-            if (fmax > c.fpix)
+            const int64_t pr = footprint_pitch(Wf, pb.Q, pb.str[0], pb.str[1]);
+            if ((fmax / Wf) * pr > (int64_t)c.fpix * 5)
                 continue;
-            bytes = (double)c.tn * stages * 64 + (double)(cc / 4) * fmax * 80;
+            bytes = (double)c.tn * stages * 64 + (double)(cc / 4) * (fmax / Wf) * pr * 16;
         } else {
             bytes = (double)(c.tm + c.tn) * stages * c.bk;
         }
@@ -513,6 +530,7 @@ conv_i8_status_t make_plan(const Problem &pb, const void *x_ptr, const void *w_p
     if (c.footprint) {
         pl->Hp = Hp;
         pl->Wf = Wf;
+        pl->Pr = footprint_pitch(Wf, pb.Q, pb.str[0], pb.str[1]);
     }
     return CONV_I8_OK;
 }
@@ -621,7 +639,8 @@ conv_i8_status_t run(const Problem &pb, const Plan &pl, const void *x_ptr, const
     a.Hp = (int)pl.Hp;
     a.Wf = (int)pl.Wf;
     a.inv_hp = pl.Hp > 0 ? 1.0f / (float)pl.Hp : 0.0f;
-    a.inv_wf = pl.Wf > 0 ? 1.0f / (float)pl.Wf : 0.0f;
+    a.Pr = (int)pl.Pr;
+    a.inv_pr = pl.Pr > 0 ? 1.0f / (float)pl.Pr : 0.0f;
     a.ncblk = (int)(pl.Cp / 64);
     for (int64_t n0 = 0; n0 < pb.N; n0 += pl.batch_chunk) {
         const int64_t nb = std::min(pl.batch_chunk, pb.N - n0);

@@ -22,11 +22,14 @@
 // issued after every wave has finished reading block c-1 (the previous user
 // of that buffer), and all of them land before the first read of block c+1.
 //
-// LDS layout of a footprint: pixel fp at byte fp*80 (64 channel bytes and a
-// 16-byte gap), so 16 consecutive pixels read with one 16-byte chunk each
-// fall on 16 distinct 16-byte bank groups (5 is odd), and the address of tap
-// (r, s) is a per-lane constant plus a uniform offset.  A wave-wide direct
-// load fills 1 KiB = 64 consecutive 16-byte slots; lanes whose slot is a gap
+// LDS layout of a footprint, in 16-byte slots: pixel (row fr, column fc) at
+// slot fr*Pr + fc*5 (64 channel bytes and a one-slot gap), so 16 output
+// pixels along a row, read with one 16-byte chunk each, fall on 16 distinct
+// bank groups (5 is odd), and the row pitch Pr is padded so that the next
+// output row continues the same progression (the host picks Pr with
+// stride_h*Pr = 5*stride_w*Q modulo 16 where it can).  The address of tap
+// (r, s) is then a per-lane constant plus a uniform offset.  A wave-wide
+// direct load fills 1 KiB = 64 consecutive slots; lanes whose slot is a gap
 // (or past the footprint, or in the padding) load out of range, i.e. zeros.
 #pragma once
 
@@ -95,7 +98,7 @@ __global__ __launch_bounds__(64 * WGM * WGN) void conv_footprint3x3_kernel(Igemm
     constexpr int NW = WGM * WGN;
     constexpr int GB = NW * 1024;            // bytes of one workgroup-wide load
     constexpr int BK = 64;                   // channels per stage
-    constexpr int PITCH = 80;                // footprint bytes per pixel
+    constexpr int PITCH = 80;                // footprint bytes per pixel (FPIX pixels fill a buffer)
     constexpr int BL = TN * BK / GB;         // filter loads per thread per stage
     constexpr int B_BYTES = TN * BK;         // one ring slot
     constexpr int NG = (FPIX * PITCH + GB - 1) / GB;
@@ -130,24 +133,26 @@ __global__ __launch_bounds__(64 * WGM * WGN) void conv_footprint3x3_kernel(Igemm
     const int hp_a = p_a * a.strH;           // first footprint row (padded coordinates of image n_a)
     const int n_b = udiv(m_last, a.d_pq);
     const int p_b = udiv(m_last - n_b * a.PQ, a.d_q);
-    const int frows = (n_b - n_a) * a.Hp + p_b * a.strH + 2 * a.dilH - hp_a + 1;
-    const int fpix = frows * a.Wf;           // footprint pixels (the host keeps it <= FPIX)
+    const int frows = (n_b - n_a) * a.Hp + p_b * a.strH + 2 * a.dilH - hp_a + 1;  // host keeps frows*Pr within the buffer
 
     // ---- footprint loads: group g, this thread -> 16-byte slot
-    // g*GB/16 + wave*64 + lane of the buffer = pixel slot/5, chunk slot%5
+    // g*GB/16 + wave*64 + lane of the buffer = footprint row slot/Pr, pixel
+    // (slot%Pr)/5 of that row, chunk (slot%Pr)%5 (chunk 4 and the row's
+    // tail slots are gaps)
     int foff[NG];
 #pragma unroll
     for (int g = 0; g < NG; ++g) {
         const int slot = g * (GB / 16) + wave * 64 + lane;
-        const int fp = slot / 5;
-        const int j = slot - fp * 5;
-        const int fr = fdiv(fp, a.Wf, a.inv_wf);
-        const int fc = fp - fr * a.Wf;
+        const int fr = fdiv(slot, a.Pr, a.inv_pr);
+        const int rem = slot - fr * a.Pr;
+        const int fc = rem / 5;
+        const int j = rem - fc * 5;
         const int hr = hp_a + fr;
         const int dn = fdiv(hr, a.Hp, a.inv_hp);
         const int h = hr - dn * a.Hp - a.padH;
         const int w = fc - a.padW;
-        const bool ok = (j < 4) & (fp < fpix) & ((unsigned)h < (unsigned)a.H) & ((unsigned)w < (unsigned)a.W);
+        const bool ok = (j < 4) & (fc < a.Wf) & (fr < frows) & ((unsigned)h < (unsigned)a.H) &
+                        ((unsigned)w < (unsigned)a.W);
         foff[g] = ok ? (n_a + dn) * a.sN + h * a.sH + w * a.sW + j * 16 : kOutOfRange;
     }
 
@@ -177,11 +182,11 @@ __global__ __launch_bounds__(64 * WGM * WGN) void conv_footprint3x3_kernel(Igemm
             const int rem = m - n * a.PQ;
             const int p = udiv(rem, a.d_q);
             const int q = rem - p * a.Q;
-            idx = ((n - n_a) * a.Hp + p * a.strH - hp_a) * a.Wf + q * a.strW;
+            idx = ((n - n_a) * a.Hp + p * a.strH - hp_a) * a.Pr + q * a.strW * 5;
         }
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks)
-            a_lane[x][ks] = idx * PITCH + (ks * 2 + (lane >> 5)) * 16;
+            a_lane[x][ks] = (idx + ks * 2 + (lane >> 5)) * 16;
     }
     int b_lane[FN][KS];
 #pragma unroll
@@ -199,7 +204,7 @@ __global__ __launch_bounds__(64 * WGM * WGN) void conv_footprint3x3_kernel(Igemm
     const int nblk = a.ncblk;
 
     // uniform per-tap offsets: footprint bytes (read side), filter bytes (load side)
-    auto tap_read = [&](int t) { return ((t / 3) * a.dilH * a.Wf + (t % 3) * a.dilW) * PITCH; };
+    auto tap_read = [&](int t) { return ((t / 3) * a.dilH * a.Pr + (t % 3) * a.dilW * 5) * 16; };
     auto tap_flt = [&](int t) { return (t / 3) * a.fR + (t % 3) * a.fS; };
 
     // Loads of stage (block cb, tap t) into ring slot `slot`, plus the

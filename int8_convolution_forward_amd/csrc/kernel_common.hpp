@@ -55,7 +55,8 @@ struct IgemmArgs {
     // footprint kernel only
     int Hp;              // padded image height H + pre_h + post_h
     int Wf;              // footprint width (Q-1)*stride_w + (S-1)*dil_w + 1
-    float inv_wf, inv_hp;
+    int Pr;              // footprint row pitch in LDS, 16-byte slots
+    float inv_pr, inv_hp;
     int ncblk;           // channel blocks of 64
 };
 
