@@ -349,6 +349,51 @@ bool direct_ok(const T4 &t, const void *ptr)
 
 const char *env_tile() { return getenv("CONV_I8_TILE"); }
 
+// One repack job: [A, C, Y, X] -> [A, Y, X, Cp].  Y and X merge into one
+// run of positions when their strides allow it (packed rows, or a size-1
+// dim), so the lines along x are as long as possible.
+RepackJob repack_job(const T4 &t, const int8_t *src, int8_t *dst, int64_t Cp, int64_t *tiles64 = nullptr)
+{
+    RepackJob j{};
+    j.src = src;
+    j.dst = dst;
+    int64_t A = t.d[0], C = t.d[1], Y = t.d[2], X = t.d[3];
+    int64_t s0 = t.s[0], s1 = t.s[1], sy = t.s[2], sx = t.s[3];
+    if (X == 1) {
+        X = Y;
+        sx = sy;
+        Y = 1;
+        sy = 0;
+    } else if (Y == 1 || sy == X * sx) {
+        X = X * Y;
+        Y = 1;
+        sy = 0;
+    }
+    j.s0 = s0;
+    j.s1 = s1;
+    j.sy = sy;
+    j.sx = sx;
+    j.A = (int)A;
+    j.C = (int)C;
+    j.Y = (int)Y;
+    j.X = (int)X;
+    j.Cp = (int)Cp;
+    if (X > 1 && sx <= 8 && (sx <= s1 || C == 1))
+        j.mode = kRepackXFast;
+    else if (C > 1 && s1 <= 8)
+        j.mode = kRepackCFast;
+    else
+        j.mode = kRepackGather;
+    const int64_t tx = (X + 63) / 64, tc = (Cp + 63) / 64;
+    const int64_t tiles = A * Y * tx * tc;
+    if (tiles64)
+        *tiles64 = tiles;
+    j.tiles_x = (int)tx;
+    j.tiles_c = (int)tc;
+    j.tiles = tiles <= kI32Max ? (int)tiles : 0;
+    return j;
+}
+
 conv_i8_status_t make_plan(const Problem &pb, const void *x_ptr, const void *w_ptr, Plan *pl)
 {
     pl->repack_x = !direct_ok(pb.x, x_ptr);
@@ -365,7 +410,9 @@ conv_i8_status_t make_plan(const Problem &pb, const void *x_ptr, const void *w_p
         pl->xsW = pl->Cp;
         pl->xsH = pb.W * pl->Cp;
         pl->xsN = pb.H * pb.W * pl->Cp;
-        if (pb.N * pb.H > kI32Max || pb.W > 65535 * 64LL || pl->Cp > 65535 * 64LL)
+        int64_t rt = 0;
+        repack_job(pb.x, nullptr, nullptr, pl->Cp, &rt);
+        if (rt > kI32Max || pb.H * pb.W > kI32Max || pl->Cp > kI32Max)
             return CONV_I8_ERR_UNSUPPORTED;
     } else {
         pl->xsN = pb.x.s[0];
@@ -381,7 +428,9 @@ conv_i8_status_t make_plan(const Problem &pb, const void *x_ptr, const void *w_p
         pl->wsS = pl->Cp;
         pl->wsR = pb.S * pl->Cp;
         pl->wsK = pb.R * pb.S * pl->Cp;
-        if (pb.K * pb.R > kI32Max || pb.S > 65535 * 64LL || pl->Cp > 65535 * 64LL)
+        int64_t rt = 0;
+        repack_job(pb.w, nullptr, nullptr, pl->Cp, &rt);
+        if (rt > kI32Max || pb.R * pb.S > kI32Max || pl->Cp > kI32Max)
             return CONV_I8_ERR_UNSUPPORTED;
     } else {
         pl->wsK = pb.w.s[0];
@@ -557,28 +606,19 @@ bool log_enabled()
     return e && *e && strcmp(e, "0") != 0;
 }
 
-conv_i8_status_t launch_repack(const T4 &t, const int8_t *src, int8_t *dst, int64_t Cp,
-                               hipStream_t stream)
+conv_i8_status_t launch_repacks(const RepackJob *jobs, int njobs, hipStream_t stream)
 {
     RepackArgs r{};
-    r.src = src;
-    r.s0 = t.s[0];
-    r.s1 = t.s[1];
-    r.s2 = t.s[2];
-    r.s3 = t.s[3];
-    r.A = (int)t.d[0];
-    r.C = (int)t.d[1];
-    r.Y = (int)t.d[2];
-    r.X = (int)t.d[3];
-    r.Cp = (int)Cp;
-    // Walk x with the lanes when it is the cheaper (smaller) stride.
-    r.x_fast = (t.d[1] <= 1) || (t.d[3] > 1 && t.s[3] <= t.s[1]);
-    r.dst = dst;
-    const int64_t ay = t.d[0] * t.d[2];
-    if (ay == 0 || t.d[3] == 0 || Cp == 0)
+    int64_t total = 0;
+    for (int i = 0; i < njobs; ++i) {
+        if (jobs[i].tiles == 0)
+            continue;
+        r.job[r.njobs++] = jobs[i];
+        total += jobs[i].tiles;
+    }
+    if (total == 0)
         return CONV_I8_OK;
-    dim3 grid((unsigned)ay, (unsigned)((t.d[3] + 63) / 64), (unsigned)((Cp + 63) / 64));
-    hipLaunchKernelGGL(repack_to_channels_last_kernel, grid, dim3(256), 0, stream, r);
+    hipLaunchKernelGGL(repack_to_channels_last_kernel, dim3((unsigned)total), dim3(256), 0, stream, r);
     return hipGetLastError() == hipSuccess ? CONV_I8_OK : CONV_I8_ERR_HIP;
 }
 
@@ -589,16 +629,18 @@ conv_i8_status_t run(const Problem &pb, const Plan &pl, const void *x_ptr, const
     const int8_t *w = (const int8_t *)w_ptr;
     int8_t *wsb = (int8_t *)ws;
     conv_i8_status_t st;
+    RepackJob jobs[2];
+    int njobs = 0;
     if (pl.repack_x && pb.C > 0) {
-        if ((st = launch_repack(pb.x, x, wsb + pl.ws_x_off, pl.Cp, stream)) != CONV_I8_OK)
-            return st;
+        jobs[njobs++] = repack_job(pb.x, x, wsb + pl.ws_x_off, pl.Cp);
         x = wsb + pl.ws_x_off;
     }
     if (pl.repack_w && pb.C > 0) {
-        if ((st = launch_repack(pb.w, w, wsb + pl.ws_w_off, pl.Cp, stream)) != CONV_I8_OK)
-            return st;
+        jobs[njobs++] = repack_job(pb.w, w, wsb + pl.ws_w_off, pl.Cp);
         w = wsb + pl.ws_w_off;
     }
+    if (njobs > 0 && (st = launch_repacks(jobs, njobs, stream)) != CONV_I8_OK)
+        return st;
     const TileCfg &c = kTiles[pl.cfg];
     IgemmArgs a{};
     a.flt = w;

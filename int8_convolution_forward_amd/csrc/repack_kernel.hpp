@@ -6,9 +6,14 @@
 // read with aligned 16-byte channel vectors (NCHW, strided views, C % 16 != 0).
 //
 // The memory layout decides the cost here ("Building a From-Scratch INT8
-// Strided Convolution Kernel", "Key Takeaways"): a 64(x) x 64(c) tile is read
-// with consecutive lanes walking whichever of x or c has the smaller stride,
-// transposed through LDS, and written as 16-byte channel vectors.
+// Strided Convolution Kernel", "Key Takeaways").  A workgroup moves a tile of
+// 64 positions x 64 channels of one (a, y) row.  When one of the two walks
+// (along x, or along c) has a small stride (at most 8 bytes), the tile's 64
+// lines along that walk are read as aligned 16-byte vectors into LDS (every
+// vector holds at least one wanted byte, so no vector leaves the pages the
+// tensor occupies), and the wanted bytes are picked out of LDS; otherwise
+// every element is read on its own.  Each thread then writes one 16-byte
+// vector of 16 consecutive channels.  One launch serves up to two tensors.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -16,59 +21,104 @@
 
 namespace convi8 {
 
-struct RepackArgs {
+enum RepackMode : int {
+    kRepackXFast = 0,   // stride along x <= 8 bytes: lines along x
+    kRepackCFast = 1,   // stride along c <= 8 bytes: lines along c
+    kRepackGather = 2,  // neither: one load per element
+};
+
+struct RepackJob {
     const int8_t *src;               // element (0,0,0,0)
-    long long s0, s1, s2, s3;        // element strides of [A, C, Y, X]
+    long long s0, s1, sy, sx;        // element strides of [A, C, Y, X]
     int A, C, Y, X, Cp;
-    int x_fast;                      // 1: lanes walk x when reading, else c
+    int mode;
+    int tiles_x, tiles_c;            // 64-wide tiles along x and along Cp
+    int tiles;                       // A * Y * tiles_x * tiles_c
     int8_t *dst;                     // packed [A][Y][X][Cp]
 };
 
-__global__ __launch_bounds__(256) void repack_to_channels_last_kernel(RepackArgs a)
+struct RepackArgs {
+    RepackJob job[2];
+    int njobs;
+};
+
+constexpr int kRepackLine = 544;     // LDS bytes per line: 34 vectors (63*8 bytes + alignment)
+
+__global__ __launch_bounds__(256) void repack_to_channels_last_kernel(RepackArgs args)
 {
-    constexpr int T = 64;
-    constexpr int LD = T + 4;  // row pitch in bytes (4-byte multiple, staggers banks)
-    __shared__ __attribute__((aligned(16))) int8_t tile[T * LD];  // [x][c]
+    __shared__ __attribute__((aligned(16))) int8_t raw[64 * kRepackLine];
+
+    unsigned bid = blockIdx.x;               // each job has fewer than 2^31 tiles
+    const bool second = args.njobs > 1 && bid >= (unsigned)args.job[0].tiles;
+    const RepackJob &j = second ? args.job[1] : args.job[0];
+    if (second)
+        bid -= (unsigned)args.job[0].tiles;
 
     const int tid = threadIdx.x;
-    const int ay = blockIdx.x;       // grid: (A*Y, ceil(X/64), ceil(Cp/64))
-    const int x0 = blockIdx.y * T;
-    const int c0 = blockIdx.z * T;
-    const int ai = ay / a.Y;
-    const int yi = ay - ai * a.Y;
-    const int8_t *base = a.src + ai * a.s0 + yi * a.s2;
+    const int ct = (int)(bid % (unsigned)j.tiles_c);
+    const int xt = (int)((bid / (unsigned)j.tiles_c) % (unsigned)j.tiles_x);
+    const int ay = (int)(bid / ((unsigned)j.tiles_c * (unsigned)j.tiles_x));
+    const int ai = ay / j.Y;
+    const int yi = ay - ai * j.Y;
+    const int x0 = xt * 64, c0 = ct * 64;
+    const int xn = min(64, j.X - x0);        // positions in this tile
+    const int cn = max(0, min(64, j.C - c0)); // real channels in this tile (the rest pad with zeros)
+    const int8_t *row = j.src + ai * j.s0 + yi * j.sy;
 
-#pragma unroll 4
-    for (int i = 0; i < (T * T) / 256; ++i) {
-        const int idx = i * 256 + tid;
-        int xl, cl;
-        if (a.x_fast) {
-            xl = idx & (T - 1);
-            cl = idx >> 6;
-        } else {
-            cl = idx & (T - 1);
-            xl = idx >> 6;
+    // output vector of this thread: position x0 + xl, channels c0 + cq*16 .. +16
+    const int xl = tid >> 2, cq = tid & 3;
+    const bool out_ok = xl < xn && c0 + cq * 16 < j.Cp;
+    int v[4] = {0, 0, 0, 0};
+
+    if (j.mode == kRepackGather) {
+        if (out_ok) {
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                const int cl = cq * 16 + i;
+                if (cl < cn)
+                    v[i >> 2] |= (int)(uint8_t)row[(long long)(c0 + cl) * j.s1 + (long long)(x0 + xl) * j.sx] << (8 * (i & 3));
+            }
         }
-        const int c = c0 + cl, x = x0 + xl;
-        int8_t v = 0;
-        if (c < a.C && x < a.X)
-            v = base[c * a.s1 + x * a.s3];
-        tile[xl * LD + cl] = v;
+    } else {
+        // line l of the tile: channel c0+l (x-fast) or position x0+l (c-fast);
+        // it runs over the other index with stride `step`.  Four threads
+        // share a line and fetch every fourth of its aligned vectors.
+        const bool xf = j.mode == kRepackXFast;
+        const long long lstride = xf ? j.s1 : j.sx;
+        const int step = (int)(xf ? j.sx : j.s1);
+        const int nlines = xf ? cn : xn;
+        const int nalong = xf ? xn : cn;
+        const int8_t *line0 = row + (long long)(xf ? x0 : c0) * step + (long long)(xf ? c0 : x0) * lstride;
+        {
+            const int l = tid >> 2, sub = tid & 3;
+            if (l < nlines && nalong > 0) {
+                const int8_t *first = line0 + (long long)l * lstride;
+                const uintptr_t a0 = (uintptr_t)first & ~(uintptr_t)15;
+                const int nv = (int)(((((uintptr_t)first & 15) + (uintptr_t)(nalong - 1) * step) >> 4) + 1);
+                for (int v16 = sub; v16 < nv; v16 += 4)
+                    *(int4 *)&raw[l * kRepackLine + v16 * 16] = *(const int4 *)(a0 + (uintptr_t)v16 * 16);
+            }
+        }
+        __syncthreads();
+        if (out_ok) {
+            // offset of line l's first byte within its first aligned vector:
+            // only the low four address bits matter
+            const unsigned b0 = (unsigned)(uintptr_t)line0, ls = (unsigned)lstride;
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                const int cl = cq * 16 + i;
+                if (cl < cn) {
+                    const int l = xf ? cl : xl;
+                    const int k = xf ? xl : cl;
+                    const int lead = (int)((b0 + (unsigned)l * ls) & 15u);
+                    v[i >> 2] |= (int)(uint8_t)raw[l * kRepackLine + lead + k * step] << (8 * (i & 3));
+                }
+            }
+        }
     }
-    __syncthreads();
-
-    const int xl = tid >> 2;
-    const int cl = (tid & 3) * 16;
-    const int x = x0 + xl, c = c0 + cl;
-    if (x < a.X && c < a.Cp) {
-        const int *srow = (const int *)&tile[xl * LD + cl];
-        int4 v;
-        v.x = srow[0];
-        v.y = srow[1];
-        v.z = srow[2];
-        v.w = srow[3];
-        int8_t *d = a.dst + (((long long)ai * a.Y + yi) * a.X + x) * a.Cp + c;
-        *(int4 *)d = v;
+    if (out_ok) {
+        int8_t *d = j.dst + (((long long)ai * j.Y + yi) * j.X + x0 + xl) * j.Cp + c0 + cq * 16;
+        *(int4 *)d = int4{v[0], v[1], v[2], v[3]};
     }
 }
 
