@@ -19,6 +19,7 @@
 #include <string>
 
 #include "footprint_kernel.hpp"
+#include "pointwise_kernel.hpp"
 #include "igemm_kernel.hpp"
 #include "repack_kernel.hpp"
 
@@ -224,30 +225,50 @@ void launch_fp3x3(bool, bool pix_j, dim3 grid, hipStream_t stream, const IgemmAr
         hipLaunchKernelGGL((conv_footprint3x3_kernel<TM, TN, NS, FPIX, WGM, WGN, false>), grid, block, 0, stream, a);
 }
 
+constexpr int kPointwiseTilesPerWave = 4;
+
+template <int FN, int KS>
+void launch_pw(bool, bool, dim3 grid, hipStream_t stream, const IgemmArgs &a)
+{
+    hipLaunchKernelGGL((conv_pointwise_kernel<FN, KS, kPointwiseTilesPerWave>), grid, dim3(256), 0, stream, a);
+}
+
+enum KernelKind { kIm2col = 0, kFootprint = 1, kPointwise = 2 };
+
 struct TileCfg {
     const char *name;  // CONV_I8_TILE value that forces this shape
     int tm, tn, bk, ns;
     int waves;         // 4 (2x2 wave grid) or 8 (4x2)
-    bool footprint;    // 3x3 footprint kernel (image loaded once per 64-channel block)
+    int kind;          // KernelKind: im2col, 3x3 footprint (image once per 64-channel block), 1x1 streaming
     int fpix;          // footprint capacity (pixels)
     double eff;        // relative MFMA efficiency of this tile shape (cost model)
     Launcher launch;   // the kernel instantiation with exactly these parameters
 };
 
 const TileCfg kTiles[] = {
-    {"64x64x64", 64, 64, 64, 4, 4, false, 0, 0.40, launch_cfg<64, 64, 64, 4>},
-    {"128x64x64", 128, 64, 64, 4, 4, false, 0, 0.48, launch_cfg<128, 64, 64, 4>},
-    {"64x128x64", 64, 128, 64, 4, 4, false, 0, 0.48, launch_cfg<64, 128, 64, 4>},
-    {"128x128x64", 128, 128, 64, 4, 4, false, 0, 0.59, launch_cfg<128, 128, 64, 4>},
-    {"128x128x128", 128, 128, 128, 3, 4, false, 0, 0.55, launch_cfg<128, 128, 128, 3>},
-    {"256x128x64", 256, 128, 64, 4, 4, false, 0, 0.52, launch_cfg<256, 128, 64, 4>},
-    {"128x256x64", 128, 256, 64, 4, 4, false, 0, 0.50, launch_cfg<128, 256, 64, 4>},
-    {"w256x128x64", 256, 128, 64, 4, 8, false, 0, 0.56, launch_cfg<256, 128, 64, 4, 4, 2>},
-    {"w128x128x64", 128, 128, 64, 4, 8, false, 0, 0.56, launch_cfg<128, 128, 64, 4, 4, 2>},
-    {"w256x128x128", 256, 128, 128, 3, 8, false, 0, 0.76, launch_cfg<256, 128, 128, 3, 4, 2>},
-    {"f256x128", 256, 128, 64, 6, 4, true, 448, 0.70, launch_fp3x3<256, 128, 6, 448>},
-    {"fw256x128", 256, 128, 64, 3, 8, true, 448, 0.68, launch_fp3x3<256, 128, 3, 448, 4, 2>},
-    {"f128x128", 128, 128, 64, 6, 4, true, 384, 0.62, launch_fp3x3<128, 128, 6, 384>},
+    {"64x64x64", 64, 64, 64, 4, 4, kIm2col, 0, 0.40, launch_cfg<64, 64, 64, 4>},
+    {"128x64x64", 128, 64, 64, 4, 4, kIm2col, 0, 0.48, launch_cfg<128, 64, 64, 4>},
+    {"64x128x64", 64, 128, 64, 4, 4, kIm2col, 0, 0.48, launch_cfg<64, 128, 64, 4>},
+    {"128x128x64", 128, 128, 64, 4, 4, kIm2col, 0, 0.59, launch_cfg<128, 128, 64, 4>},
+    {"128x128x128", 128, 128, 128, 3, 4, kIm2col, 0, 0.55, launch_cfg<128, 128, 128, 3>},
+    {"256x128x64", 256, 128, 64, 4, 4, kIm2col, 0, 0.52, launch_cfg<256, 128, 64, 4>},
+    {"128x256x64", 128, 256, 64, 4, 4, kIm2col, 0, 0.50, launch_cfg<128, 256, 64, 4>},
+    {"w256x128x64", 256, 128, 64, 4, 8, kIm2col, 0, 0.56, launch_cfg<256, 128, 64, 4, 4, 2>},
+    {"w128x128x64", 128, 128, 64, 4, 8, kIm2col, 0, 0.56, launch_cfg<128, 128, 64, 4, 4, 2>},
+    {"w256x128x128", 256, 128, 128, 3, 8, kIm2col, 0, 0.76, launch_cfg<256, 128, 128, 3, 4, 2>},
+    {"f256x128", 256, 128, 64, 6, 4, kFootprint, 448, 0.70, launch_fp3x3<256, 128, 6, 448>},
+    {"fw256x128", 256, 128, 64, 3, 8, kFootprint, 448, 0.68, launch_fp3x3<256, 128, 3, 448, 4, 2>},
+    {"f128x128", 128, 128, 64, 6, 4, kFootprint, 384, 0.62, launch_fp3x3<128, 128, 6, 384>},
+    // 1x1 streaming kernel: tm = pixels per wave tile, tn = output channels covered,
+    // bk = channels covered
+    {"pw32x64", 32, 32, 64, 0, 4, kPointwise, 0, 1.0, launch_pw<1, 2>},
+    {"pw32x128", 32, 32, 128, 0, 4, kPointwise, 0, 1.0, launch_pw<1, 4>},
+    {"pw32x256", 32, 32, 256, 0, 4, kPointwise, 0, 1.0, launch_pw<1, 8>},
+    {"pw64x64", 32, 64, 64, 0, 4, kPointwise, 0, 1.0, launch_pw<2, 2>},
+    {"pw64x128", 32, 64, 128, 0, 4, kPointwise, 0, 1.0, launch_pw<2, 4>},
+    {"pw64x256", 32, 64, 256, 0, 4, kPointwise, 0, 1.0, launch_pw<2, 8>},
+    {"pw128x64", 32, 128, 64, 0, 4, kPointwise, 0, 1.0, launch_pw<4, 2>},
+    {"pw128x128", 32, 128, 128, 0, 4, kPointwise, 0, 1.0, launch_pw<4, 4>},
 };
 constexpr int kNumTiles = sizeof(kTiles) / sizeof(kTiles[0]);
 
@@ -530,7 +551,23 @@ conv_i8_status_t make_plan(const Problem &pb, const void *x_ptr, const void *w_p
         const int64_t chunks = RS * cc;
         int64_t stages = cc % cps == 0 ? RS * (cc / cps) : (chunks + cps - 1) / cps;
         double bytes;
-        if (c.footprint) {
+        if (c.kind == kPointwise) {
+            // 1x1 streaming kernel: the filter fits its registers, the output
+            // is channel-innermost with equally spaced pixels
+            if (pb.R != 1 || pb.S != 1 || pb.K > c.tn || pl->Cp > c.bk || pl->pix_j || !pl->pix_linear)
+                continue;
+            // HBM-bound and measured ahead of every im2col tile on 1x1 layers
+            // (the tile model prices the im2col tiles' stores too low there):
+            // the first one that fits is taken
+            if (getenv("CONV_I8_COST"))
+                fprintf(stderr, "conv_i8 cost %-14s -> preferred for 1x1\n", c.name);
+            if (best < 0 || kTiles[best].kind != kPointwise) {
+                best = i;
+                best_cost = 0;
+            }
+            continue;
+        }
+        if (c.kind == kFootprint) {
             // footprint kernel: a 3x3 filter, 64-channel blocks, and a tile
             // footprint that fits its buffers
             if (pb.R != 3 || pb.S != 3 || cc % 4 != 0 || Hp >= (1 << 20) || Wf >= (1 << 20))
@@ -545,7 +582,7 @@ conv_i8_status_t make_plan(const Problem &pb, const void *x_ptr, const void *w_p
             bytes = (double)(c.tm + c.tn) * stages * c.bk;
         }
         double eff = c.eff;
-        if (!c.footprint && cc % cps != 0)
+        if (c.kind == kIm2col && cc % cps != 0)
             eff *= chunks > 0 ? (double)chunks / (double)(stages * cps) : 1.0;
         // fitted to measured kernel times: MFMA time at the shape's efficiency
         // plus half the operand-load time (the two overlap only partly) plus
@@ -576,7 +613,7 @@ conv_i8_status_t make_plan(const Problem &pb, const void *x_ptr, const void *w_p
     const int cps = c.bk / 16;
     pl->blocked = cc % cps == 0;
     pl->nstages = pl->blocked ? RS * (cc / cps) : (RS * cc + cps - 1) / cps;
-    if (c.footprint) {
+    if (c.kind == kFootprint) {
         pl->Hp = Hp;
         pl->Wf = Wf;
         pl->Pr = footprint_pitch(Wf, pb.Q, pb.str[0], pb.str[1]);
@@ -594,7 +631,7 @@ std::string describe(const Problem &pb, const Plan &pl)
              "repack_image=%d repack_filter=%d Cp=%lld tile=%s kernel=%s order=%s stages=%lld "
              "lanes=%s tiles=%lld batch_chunk=%lld workspace=%zu",
              (int)pl.repack_x, (int)pl.repack_w, (long long)pl.Cp, c.name,
-             c.footprint ? "footprint" : "im2col", pl.blocked ? "blocked" : "flat", (long long)pl.nstages,
+             c.kind == kFootprint ? "footprint" : c.kind == kPointwise ? "pointwise" : "im2col", pl.blocked ? "blocked" : "flat", (long long)pl.nstages,
              pl.pix_j ? "pixels" : "channels", (long long)tiles, (long long)pl.batch_chunk,
              pl.ws_bytes);
     return buf;
@@ -693,7 +730,9 @@ conv_i8_status_t run(const Problem &pb, const Plan &pl, const void *x_ptr, const
         a.N = (int)nb;
         a.sN = (int)pl.xsN;
         a.M = (int)(nb * pb.P * pb.Q);
-        const int64_t tiles = ((a.M + c.tm - 1) / c.tm) * (int64_t)a.tiles_n;
+        int64_t tiles = ((a.M + c.tm - 1) / c.tm) * (int64_t)a.tiles_n;
+        if (c.kind == kPointwise)  // workgroups of four waves, each with a run of 32-pixel tiles
+            tiles = ((a.M + 31) / 32 + 4 * kPointwiseTilesPerWave - 1) / (4 * kPointwiseTilesPerWave);
         if (tiles == 0)
             continue;
         a.tiles = (int)tiles;

@@ -354,3 +354,40 @@ def test_footprint_kernel(ci8, monkeypatch, tile, case_i, out_layout):
     wv = torch.randint(-128, 128, (K, C, R, S), dtype=torch.int8, generator=g)
     run_and_check(ci8, _fill(xs, xv, 1), xs, _fill(ws, wv, 2), ws, os_, pre, post, st, dl,
                   label=f"footprint {tile} case {case_i}")
+
+
+# ---------------------------------------------------------------------------
+# The 1x1 streaming kernel: ragged pixel counts (not a multiple of 32 or of a
+# wave's four tiles), ragged output channels and channels, stride and padding
+# (pixels that read only zeros), several images.
+# ---------------------------------------------------------------------------
+POINTWISE_CASES = [
+    # N, C, H, W, K, stride, pre, post
+    (3, 64, 13, 11, 64, (1, 1), (0, 0), (0, 0)),
+    (2, 256, 9, 7, 50, (1, 1), (0, 0), (0, 0)),
+    (4, 48, 10, 10, 33, (2, 2), (1, 0), (0, 1)),
+    (1, 112, 5, 37, 128, (1, 3), (2, 1), (1, 2)),
+    (5, 16, 6, 6, 7, (1, 1), (1, 1), (1, 1)),
+]
+
+
+@pytest.mark.parametrize("case_i", range(len(POINTWISE_CASES)))
+@pytest.mark.parametrize("layout", ["nhwc", "nchw"])
+def test_pointwise_kernel(ci8, monkeypatch, case_i, layout):
+    N, C, H, W, K, st, pre, post = POINTWISE_CASES[case_i]
+    fn = next(f for f in (1, 2, 4) if 32 * f >= K)
+    ks = next(k for k in (2, 4, 8) if 32 * k >= (C + 15) // 16 * 16)
+    monkeypatch.setenv("CONV_I8_TILE", f"pw{32 * fn}x{32 * ks}")
+    od = oracle.out_dims((N, C, H, W), (K, C, 1, 1), pre, post, st, (1, 1))
+    xs = wl.TensorSpec((N, C, H, W), wl.channels_last_strides((N, C, H, W)) if layout == "nhwc"
+                       else wl.contiguous_strides((N, C, H, W)))
+    ws = wl.TensorSpec((K, C, 1, 1), wl.contiguous_strides((K, C, 1, 1)))
+    os_ = wl.TensorSpec(od, wl.channels_last_strides(od))
+    plan = ci8.plan_fields(ci8.conv_fprop_i8_plan(ci8.desc(xs.dims, xs.strides, 1), ci8.desc(ws.dims, ws.strides, 1),
+                                                  ci8.desc(os_.dims, os_.strides, 2), pre, post, st, (1, 1)))
+    assert plan["kernel"] == "pointwise", plan
+    g = torch.Generator().manual_seed(100 + case_i)
+    xv = torch.randint(-128, 128, (N, C, H, W), dtype=torch.int8, generator=g)
+    wv = torch.randint(-128, 128, (K, C, 1, 1), dtype=torch.int8, generator=g)
+    run_and_check(ci8, _fill(xs, xv, 3), xs, _fill(ws, wv, 4), ws, os_, pre, post, st, (1, 1),
+                  label=f"pointwise case {case_i} {layout}")
