@@ -215,14 +215,14 @@ void launch_cfg(bool flat, bool pix_j, dim3 grid, hipStream_t stream, const Igem
     }
 }
 
-template <int TM, int TN, int NS, int FPIX, int WGM = 2, int WGN = 2>
+template <int TM, int TN, int NS, int FPIX, int WGM = 2, int WGN = 2, int KSPL = 1>
 void launch_fp3x3(bool, bool pix_j, dim3 grid, hipStream_t stream, const IgemmArgs &a)
 {
-    const dim3 block(64 * WGM * WGN);
+    const dim3 block(64 * WGM * WGN * KSPL);
     if (pix_j)
-        hipLaunchKernelGGL((conv_footprint3x3_kernel<TM, TN, NS, FPIX, WGM, WGN, true>), grid, block, 0, stream, a);
+        hipLaunchKernelGGL((conv_footprint3x3_kernel<TM, TN, NS, FPIX, WGM, WGN, true, KSPL>), grid, block, 0, stream, a);
     else
-        hipLaunchKernelGGL((conv_footprint3x3_kernel<TM, TN, NS, FPIX, WGM, WGN, false>), grid, block, 0, stream, a);
+        hipLaunchKernelGGL((conv_footprint3x3_kernel<TM, TN, NS, FPIX, WGM, WGN, false, KSPL>), grid, block, 0, stream, a);
 }
 
 constexpr int kPointwiseTilesPerWave = 4;
@@ -259,6 +259,8 @@ const TileCfg kTiles[] = {
     {"f256x128", 256, 128, 64, 6, 4, kFootprint, 448, 0.70, launch_fp3x3<256, 128, 6, 448>},
     {"fw256x128", 256, 128, 64, 3, 8, kFootprint, 448, 0.68, launch_fp3x3<256, 128, 3, 448, 4, 2>},
     {"f128x128", 128, 128, 64, 6, 4, kFootprint, 384, 0.62, launch_fp3x3<128, 128, 6, 384>},
+    {"fk256x128", 256, 128, 64, 6, 8, kFootprint, 448, 0.60, launch_fp3x3<256, 128, 6, 448, 2, 2, 2>},
+    {"fk128x128", 128, 128, 64, 6, 8, kFootprint, 384, 0.55, launch_fp3x3<128, 128, 6, 384, 2, 2, 2>},
     // 1x1 streaming kernel: tm = pixels per wave tile, tn = output channels covered,
     // bk = channels covered
     {"pw32x64", 32, 32, 64, 0, 4, kPointwise, 0, 1.0, launch_pw<1, 2>},

@@ -91,11 +91,15 @@ constexpr int outstanding_after_next(int t)
 
 }  // namespace fp3x3
 
-template <int TM, int TN, int NS, int FPIX, int WGM, int WGN, bool PIX_J>
-__global__ __launch_bounds__(64 * WGM * WGN) void conv_footprint3x3_kernel(IgemmArgs a)
+// KSPL = 2 runs two waves per wave tile, each on one 32-channel half of
+// every stage (so two waves share each SIMD with a 128x64 tile apiece); the
+// halves are added through LDS at the end, each wave storing half the columns.
+template <int TM, int TN, int NS, int FPIX, int WGM, int WGN, bool PIX_J, int KSPL = 1>
+__global__ __launch_bounds__(64 * WGM * WGN * KSPL) void conv_footprint3x3_kernel(IgemmArgs a)
 {
     using namespace fp3x3;
-    constexpr int NW = WGM * WGN;
+    constexpr int NQ = WGM * WGN;            // waves per channel half
+    constexpr int NW = NQ * KSPL;
     constexpr int GB = NW * 1024;            // bytes of one workgroup-wide load
     constexpr int BK = 64;                   // channels per stage
     constexpr int PITCH = 80;                // footprint bytes per pixel (FPIX pixels fill a buffer)
@@ -105,13 +109,15 @@ __global__ __launch_bounds__(64 * WGM * WGN) void conv_footprint3x3_kernel(Igemm
     constexpr int FBUF = NG * GB;            // one footprint buffer
     constexpr int WM = TM / WGM, WN = TN / WGN;
     constexpr int FM = WM / 32, FN = WN / 32;
-    constexpr int KS = BK / 32;
+    constexpr int KS = BK / 32 / KSPL;       // MFMA k-steps per stage of one wave
     constexpr int NMF = KS * FM * FN;
     constexpr int NRD = KS * (FM + FN);
     static_assert(BL >= 1 && TN * BK % GB == 0, "filter tile must fill workgroup loads");
     static_assert((2 * kTaps) % NS == 0 && NS >= 2 && NS <= kTaps, "ring depth must divide 18");
     static_assert(FM >= 1 && FN >= 1, "wave tile");
     static_assert(NW == 4 || NW == 8, "4 or 8 waves");
+    static_assert(KSPL == 1 || (KSPL == 2 && FN % 2 == 0 && NS * TN * BK >= NW * (FN / 2) * 4096),
+                  "channel split: even wave-tile columns, exchange fits the ring");
 
     __shared__ __attribute__((aligned(1024))) int8_t ring[NS * B_BYTES];
     __shared__ __attribute__((aligned(1024))) int8_t fbuf[2 * FBUF];
@@ -123,8 +129,10 @@ __global__ __launch_bounds__(64 * WGM * WGN) void conv_footprint3x3_kernel(Igemm
     const int tile = xcd_tile(blockIdx.x, a.tiles);
     const int m0 = (tile / a.tiles_n) * TM;
     const int n0 = (tile % a.tiles_n) * TN;
-    const int wm = (wave / WGN) * WM;
-    const int wn = (wave % WGN) * WN;
+    const int kg = wave / NQ;                // channel half (KSPL = 2)
+    const int wq = wave % NQ;
+    const int wm = (wq / WGN) * WM;
+    const int wn = (wq % WGN) * WN;
 
     // ---- footprint geometry of this tile (uniform) ------------------------
     const int m_last = min(m0 + TM, a.M) - 1;
@@ -186,7 +194,7 @@ __global__ __launch_bounds__(64 * WGM * WGN) void conv_footprint3x3_kernel(Igemm
         }
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks)
-            a_lane[x][ks] = (idx + ks * 2 + (lane >> 5)) * 16;
+            a_lane[x][ks] = (idx + (kg * KS + ks) * 2 + (lane >> 5)) * 16;
     }
     int b_lane[FN][KS];
 #pragma unroll
@@ -194,7 +202,7 @@ __global__ __launch_bounds__(64 * WGM * WGN) void conv_footprint3x3_kernel(Igemm
         const int row = wn + y * 32 + (lane & 31);
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks)
-            b_lane[y][ks] = row * BK + swizzle_chunk<64>(row, ks * 2 + (lane >> 5)) * 16;
+            b_lane[y][ks] = row * BK + swizzle_chunk<64>(row, (kg * KS + ks) * 2 + (lane >> 5)) * 16;
     }
 
     const v4i img_rsrc = make_rsrc(a.img, a.img_range);
@@ -325,7 +333,49 @@ __global__ __launch_bounds__(64 * WGM * WGN) void conv_footprint3x3_kernel(Igemm
     wait_vm_lgkm0<0>();
     __syncthreads();
 
-    store_tile<FM, FN, PIX_J>(a, acc, m0, n0, wm, wn, lane, out_row);
+    if constexpr (KSPL == 1) {
+        store_tile<FM, FN, PIX_J>(a, acc, m0, n0, wm, wn, lane, out_row);
+    } else {
+        // Wave (kg, wq) keeps column half kg of its tile and hands the other
+        // to wave (1-kg, wq) through the (now idle) ring, lane-major, one
+        // 32-row block at a time.
+        constexpr int FH = FN / 2;
+        v4i *const xch = (v4i *)ring;
+        auto finish = [&](auto kgc) {
+            constexpr int KG = decltype(kgc)::value;
+#pragma unroll
+            for (int x = 0; x < FM; ++x) {
+#pragma unroll
+                for (int yy = 0; yy < FH; ++yy)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        const v16i &c = acc[x][(1 - KG) * FH + yy];
+                        xch[((wave * FH + yy) * 4 + i) * 64 + lane] =
+                            v4i{c[4 * i], c[4 * i + 1], c[4 * i + 2], c[4 * i + 3]};
+                    }
+                __syncthreads();
+                v16i fin[1][FH];
+#pragma unroll
+                for (int yy = 0; yy < FH; ++yy) {
+                    fin[0][yy] = acc[x][KG * FH + yy];
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        const v4i p = xch[(((wave ^ NQ) * FH + yy) * 4 + i) * 64 + lane];
+                        fin[0][yy][4 * i] += p.x;
+                        fin[0][yy][4 * i + 1] += p.y;
+                        fin[0][yy][4 * i + 2] += p.z;
+                        fin[0][yy][4 * i + 3] += p.w;
+                    }
+                }
+                __syncthreads();
+                store_tile<1, FH, PIX_J>(a, fin, m0, n0, wm + x * 32, wn + KG * FH * 32, lane, out_row);
+            }
+        };
+        if (kg == 0)
+            finish(std::integral_constant<int, 0>{});
+        else
+            finish(std::integral_constant<int, 1>{});
+    }
 }
 
 
