@@ -733,8 +733,13 @@ conv_i8_status_t run(const Problem &pb, const Plan &pl, const void *x_ptr, const
         a.sN = (int)pl.xsN;
         a.M = (int)(nb * pb.P * pb.Q);
         int64_t tiles = ((a.M + c.tm - 1) / c.tm) * (int64_t)a.tiles_n;
-        if (c.kind == kPointwise)  // workgroups of four waves, each with a run of 32-pixel tiles
-            tiles = ((a.M + 31) / 32 + 4 * kPointwiseTilesPerWave - 1) / (4 * kPointwiseTilesPerWave);
+        if (c.kind == kPointwise) {
+            // workgroups of four waves, each wave up to kPointwiseTilesPerWave
+            // 32-pixel tiles; at least one workgroup per CU while there is work
+            const int64_t t32 = (a.M + 31) / 32;
+            tiles = std::max((t32 + 4 * kPointwiseTilesPerWave - 1) / (4 * kPointwiseTilesPerWave),
+                             std::min<int64_t>(kCUs, (t32 + 3) / 4));
+        }
         if (tiles == 0)
             continue;
         a.tiles = (int)tiles;

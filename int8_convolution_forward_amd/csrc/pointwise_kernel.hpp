@@ -6,7 +6,9 @@
 // channels of a pointwise (bottleneck) layer that is far below the MFMA rate
 // and bound by HBM: the job is to keep enough bytes in flight.
 //
-// Each wave owns TPW consecutive 32-pixel tiles.  It fetches the whole filter
+// Each wave owns up to TPW 32-pixel tiles, strided by the number of waves in
+// the grid (so that every CU gets work when there are fewer than 4*TPW tiles
+// per CU).  It fetches the whole filter
 // once into registers (the B operand of v_mfma_i32_32x32x32_i8: lane l holds
 // output channel y*32 + l%32, channels ks*32 + (l/32)*16 .. +16), issues the
 // 16-byte image loads of all its tiles up front (lane l: pixel l%32 of the
@@ -25,7 +27,7 @@ __global__ __launch_bounds__(256) void conv_pointwise_kernel(IgemmArgs a)
 {
     const int lane = threadIdx.x & 63;
     const int wave = blockIdx.x * 4 + (threadIdx.x >> 6);
-    const int t0 = wave * TPW;                    // first 32-pixel tile of this wave
+    const int nwaves = gridDim.x * 4;             // tile t of this wave: wave + t*nwaves
     const int chunk = (lane >> 5) * 16;           // channel offset of this lane within a k-step
 
     const __amdgpu_buffer_rsrc_t flt_rsrc =
@@ -50,7 +52,7 @@ __global__ __launch_bounds__(256) void conv_pointwise_kernel(IgemmArgs a)
     v4i afr[TPW][KS];
 #pragma unroll
     for (int t = 0; t < TPW; ++t) {
-        const int m = (t0 + t) * 32 + (lane & 31);
+        const int m = (wave + t * nwaves) * 32 + (lane & 31);
         int base = kOutOfRange;
         if (m < a.M) {
             const int n = udiv(m, a.d_pq);
@@ -87,7 +89,7 @@ __global__ __launch_bounds__(256) void conv_pointwise_kernel(IgemmArgs a)
         // 32x32 accumulator layout: lane l, value v -> pixel row
         // 8*(v/4) + 4*(l/32) + v%4, output channel column l%32; the output's
         // pixels are equally spaced (pix_stride elements apart)
-        const int mb = (t0 + t) * 32 + mrow0;
+        const int mb = (wave + t * nwaves) * 32 + mrow0;
 #pragma unroll
         for (int y = 0; y < FN; ++y) {
             const int kk = y * 32 + (lane & 31);
