@@ -657,7 +657,20 @@ conv_i8_status_t launch_repacks(const RepackJob *jobs, int njobs, hipStream_t st
     }
     if (total == 0)
         return CONV_I8_OK;
-    hipLaunchKernelGGL(repack_to_channels_last_kernel, dim3((unsigned)total), dim3(256), 0, stream, r);
+    // LDS line size for the largest stride a job walks its lines with
+    int64_t step = 1;
+    for (int i = 0; i < r.njobs; ++i) {
+        const RepackJob &j = r.job[i];
+        if (j.mode != kRepackGather)
+            step = std::max<int64_t>(step, j.mode == kRepackXFast ? j.sx : j.s1);
+    }
+    const dim3 grid((unsigned)total);
+    if (step <= 2)
+        hipLaunchKernelGGL(repack_to_channels_last_kernel<2>, grid, dim3(256), 0, stream, r);
+    else if (step <= 4)
+        hipLaunchKernelGGL(repack_to_channels_last_kernel<4>, grid, dim3(256), 0, stream, r);
+    else
+        hipLaunchKernelGGL(repack_to_channels_last_kernel<8>, grid, dim3(256), 0, stream, r);
     return hipGetLastError() == hipSuccess ? CONV_I8_OK : CONV_I8_ERR_HIP;
 }
 

@@ -42,10 +42,18 @@ struct RepackArgs {
     int njobs;
 };
 
-constexpr int kRepackLine = 544;     // LDS bytes per line: 34 vectors (63*8 bytes + alignment)
+// LDS bytes per line for a largest line stride of STEP bytes: 63 strides,
+// one byte, up to 15 bytes of alignment, rounded up to whole vectors
+template <int STEP>
+constexpr int repack_line()
+{
+    return (15 + 63 * STEP + 1 + 15) / 16 * 16;
+}
 
+template <int STEP>
 __global__ __launch_bounds__(256) void repack_to_channels_last_kernel(RepackArgs args)
 {
+    constexpr int kRepackLine = repack_line<STEP>();
     __shared__ __attribute__((aligned(16))) int8_t raw[64 * kRepackLine];
 
     unsigned bid = blockIdx.x;               // each job has fewer than 2^31 tiles
