@@ -16,6 +16,7 @@
 #include <string.h>
 
 #include <algorithm>
+#include <mutex>
 #include <string>
 
 #include "footprint_kernel.hpp"
@@ -763,6 +764,20 @@ conv_i8_status_t run(const Problem &pb, const Plan &pl, const void *x_ptr, const
     return CONV_I8_OK;
 }
 
+// Plans of recent problems.  A plan depends on the problem, on whether the
+// image and filter can be read in place (layout and 16-byte alignment) and on
+// a forced tile; repeated calls on one shape skip the tile search.
+struct PlanKey {
+    Problem pb;
+    int32_t x_direct, w_direct;
+    char tile[24];
+};
+constexpr int kPlanCache = 16;
+std::mutex g_plan_mutex;
+PlanKey g_plan_keys[kPlanCache];
+Plan g_plans[kPlanCache];
+int g_plan_count = 0, g_plan_next = 0;
+
 conv_i8_status_t prepare(const conv_i8_desc_t *image, const void *image_ptr,
                          const conv_i8_desc_t *filter, const void *filter_ptr,
                          const conv_i8_desc_t *out, const int64_t *pre, const int64_t *post,
@@ -771,7 +786,32 @@ conv_i8_status_t prepare(const conv_i8_desc_t *image, const void *image_ptr,
     conv_i8_status_t st = analyze(image, filter, out, pre, post, stride, dil, pb);
     if (st != CONV_I8_OK)
         return st;
-    return make_plan(*pb, image_ptr, filter_ptr, pl);
+    PlanKey key;
+    memset(&key, 0, sizeof key);  // padding takes part in the comparison
+    key.pb = *pb;
+    key.x_direct = direct_ok(pb->x, image_ptr) ? 1 : 0;
+    key.w_direct = direct_ok(pb->w, filter_ptr) ? 1 : 0;
+    const char *forced = env_tile();
+    if (forced)
+        strncpy(key.tile, forced, sizeof key.tile - 1);
+    const bool cache = getenv("CONV_I8_COST") == nullptr && (!forced || strlen(forced) < sizeof key.tile - 1);
+    if (cache) {
+        std::lock_guard<std::mutex> lock(g_plan_mutex);
+        for (int i = 0; i < g_plan_count; ++i)
+            if (memcmp(&g_plan_keys[i], &key, sizeof key) == 0) {
+                *pl = g_plans[i];
+                return CONV_I8_OK;
+            }
+    }
+    st = make_plan(*pb, image_ptr, filter_ptr, pl);
+    if (st == CONV_I8_OK && cache) {
+        std::lock_guard<std::mutex> lock(g_plan_mutex);
+        g_plan_keys[g_plan_next] = key;
+        g_plans[g_plan_next] = *pl;
+        g_plan_next = (g_plan_next + 1) % kPlanCache;
+        g_plan_count = std::min(g_plan_count + 1, kPlanCache);
+    }
+    return st;
 }
 
 conv_i8_status_t check_ptrs(const Problem &pb, const void *x, const void *w, const void *y)
