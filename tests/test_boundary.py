@@ -190,3 +190,44 @@ def test_window_larger_than_padded_image():
     w = D((1, 16, 4, 3), (192, 1, 48, 16), 1)
     with pytest.raises(ci8.ConvI8Error):
         ci8.conv_fprop_i8_out_dims(x, w, stride=(2, 1))
+
+
+def test_plan_cache_keys():
+    """Plans are cached per problem; the cache must tell apart what changes a
+    plan: a forced tile, the operands' alignment (in-place read or repack)
+    and the problem itself."""
+    c = wl.case("large_channel_n64_c512_14")
+    dx = ci8.desc(c.image.dims, c.image.strides, 1)
+    dw = ci8.desc(c.filter.dims, c.filter.strides, 1)
+    dy = ci8.desc(c.out.dims, c.out.strides, 2)
+    pre, post, st, dl = ci8._params(c.pre, c.post, c.stride, c.dilation, None)
+
+    def plan(xp, wp, tile=None):
+        old = os.environ.pop("CONV_I8_TILE", None)
+        if tile:
+            os.environ["CONV_I8_TILE"] = tile
+        try:
+            buf = ctypes.create_string_buffer(512)
+            rc = ci8.lib.conv_fprop_i8_plan(ctypes.byref(dx), ctypes.c_void_p(xp), ctypes.byref(dw),
+                                            ctypes.c_void_p(wp), ctypes.byref(dy), pre, post, st, dl, buf, 512)
+            assert rc == 0
+            return ci8.plan_fields(buf.value.decode())
+        finally:
+            os.environ.pop("CONV_I8_TILE", None)
+            if old is not None:
+                os.environ["CONV_I8_TILE"] = old
+
+    base = plan(4096, 8192)
+    assert plan(4096, 8192) == base                      # served from the cache
+    assert base["repack_image"] == "0" and base["repack_filter"] == "0"
+    assert plan(4096 + 8, 8192)["repack_image"] == "1"   # misaligned image: repacked
+    assert plan(4096, 8192 + 4)["repack_filter"] == "1"
+    assert plan(4096, 8192, "64x64x64")["tile"] == "64x64x64"
+    assert plan(4096, 8192) == base
+    # a different problem (one image fewer) is planned afresh
+    dx2 = ci8.desc((63,) + tuple(c.image.dims[1:]), c.image.strides, 1)
+    dy2 = ci8.desc((63,) + tuple(c.out.dims[1:]), c.out.strides, 2)
+    buf = ctypes.create_string_buffer(512)
+    assert ci8.lib.conv_fprop_i8_plan(ctypes.byref(dx2), ctypes.c_void_p(4096), ctypes.byref(dw),
+                                      ctypes.c_void_p(8192), ctypes.byref(dy2), pre, post, st, dl, buf, 512) == 0
+    assert ci8.plan_fields(buf.value.decode())["batch_chunk"] == "63"
