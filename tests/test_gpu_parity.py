@@ -297,24 +297,31 @@ def test_single_output_channel_and_pixel_tails(ci8):
     _dense_case(ci8, 5, 16, 3, 3, 129, 3, 3, (1, 1), (1, 1), (1, 1), (1, 1), label="K=129")
 
 
-def test_batch_split_over_launches(ci8):
-    """Images almost 2 GiB apart: one launch per image keeps every buffer
-    offset below 2^31."""
+@pytest.mark.parametrize("C,R,tile", [(32, 3, None), (64, 3, "f128x128"), (64, 1, "pw64x64")])
+def test_batch_split_over_launches(ci8, monkeypatch, C, R, tile):
+    """Images 2 GiB apart: one launch per image keeps every buffer offset
+    below 2^31 (im2col, footprint and 1x1 kernels)."""
+    if tile:
+        monkeypatch.setenv("CONV_I8_TILE", tile)
     gap = 1 << 31
-    N, C, H, W, K = 2, 32, 9, 10, 40
+    N, H, W, K = 2, 9, 10, 40
     dims = (N, C, H, W)
     cl = wl.channels_last_strides(dims)
     xs = wl.TensorSpec(dims, (gap, cl[1], cl[2], cl[3]))
-    ws = wl.TensorSpec((K, C, 3, 3), wl.channels_last_strides((K, C, 3, 3)))
-    os_ = wl.TensorSpec((N, K, 9, 10), wl.contiguous_strides((N, K, 9, 10)))
+    ws = wl.TensorSpec((K, C, R, R), wl.channels_last_strides((K, C, R, R)))
+    od = oracle.out_dims(dims, (K, C, R, R), (1, 1), (1, 1), (1, 1), (1, 1))
+    os_ = wl.TensorSpec(od, wl.contiguous_strides(od) if R == 3 else wl.channels_last_strides(od))
     x_storage = torch.zeros(xs.storage_size, dtype=torch.int8)
     g = torch.Generator().manual_seed(5)
     torch.as_strided(x_storage, dims, xs.strides).copy_(torch.randint(-128, 128, dims, dtype=torch.int8, generator=g))
-    w_storage = _fill(ws, torch.randint(-128, 128, (K, C, 3, 3), dtype=torch.int8, generator=g), 3)
+    w_storage = _fill(ws, torch.randint(-128, 128, (K, C, R, R), dtype=torch.int8, generator=g), 3)
     f = ci8.plan_fields(ci8.conv_fprop_i8_plan(ci8.desc(xs.dims, xs.strides, 1), ci8.desc(ws.dims, ws.strides, 1),
                                                ci8.desc(os_.dims, os_.strides, 2), 1, 1, 1, 1))
     assert f["batch_chunk"] == "1"
-    run_and_check(ci8, x_storage, xs, w_storage, ws, os_, (1, 1), (1, 1), (1, 1), (1, 1), label="batch split")
+    if tile:
+        assert f["tile"] == tile, f
+    run_and_check(ci8, x_storage, xs, w_storage, ws, os_, (1, 1), (1, 1), (1, 1), (1, 1),
+                  label=f"batch split {tile or 'im2col'}")
 
 
 # ---------------------------------------------------------------------------
