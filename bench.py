@@ -33,7 +33,8 @@ def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
-    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=1000,
+                    help="untimed steps first; the GPU needs some tens of ms of load to settle its clock")
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
     ap.add_argument("--rotate-mb", type=float, default=600.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
