@@ -1,4 +1,5 @@
-"""CPU oracle for INT8 conv_fprop (INT32 output) — test infrastructure only.
+"""CPU oracle for INT8 conv_fprop (INT32 output, or a requantising INT8
+epilogue) — test infrastructure only.
 
 Only ``tests/``, the smoke check and the benchmark's CPU-baseline leg use this
 package.  The product path never imports it.  It wraps the plain nested-loop C
@@ -24,7 +25,7 @@ import torch
 from . import build as _build
 
 __all__ = ["OracleError", "Oracle", "load", "out_dims", "conv_fprop", "conv_fprop_points",
-           "max_threads"]
+           "conv_fprop_requant", "requant_values", "max_threads"]
 
 _ERRORS = {
     1: "bad argument (null pointer, negative size, stride/dilation < 1, negative padding)",
@@ -70,6 +71,12 @@ class Oracle:
         lib.oracle_conv_fprop.restype = ctypes.c_int
         lib.oracle_conv_fprop_points.argtypes = [P] * 10 + [P, ctypes.c_int64, P]
         lib.oracle_conv_fprop_points.restype = ctypes.c_int
+        lib.oracle_conv_fprop_requant.argtypes = [P] * 13 + [P, ctypes.c_float, P, ctypes.c_int,
+                                                             ctypes.c_int]
+        lib.oracle_conv_fprop_requant.restype = ctypes.c_int
+        lib.oracle_requant_values.argtypes = [P, P, ctypes.c_int64, P, ctypes.c_float, P,
+                                              ctypes.c_int, P]
+        lib.oracle_requant_values.restype = ctypes.c_int
         lib.oracle_max_threads.argtypes = []
         lib.oracle_max_threads.restype = ctypes.c_int
         self.lib = lib
@@ -128,6 +135,76 @@ class Oracle:
         return res
 
 
+    def conv_fprop_requant(self, x: torch.Tensor, w: torch.Tensor, pre=0, post=0, stride=1,
+                           dil=1, scale=None, alpha: float = 1.0, bias=None, relu: bool = False,
+                           out: Optional[torch.Tensor] = None, threads: int = 0) -> torch.Tensor:
+        """int8 Y = saturate(rint(relu?(fma(float(conv(x, w)), s_k, b_k)))).
+
+        ``scale`` and ``bias`` are K floats (anything np.float32 accepts) or
+        None (alpha for every channel, no bias).  ``out`` (int8, CPU, any
+        non-overlapping strides) receives the result if given.
+        """
+        _check_cpu(x, torch.int8, "x")
+        _check_cpu(w, torch.int8, "w")
+        yd = self.out_dims(x.shape, w.shape, pre, post, stride, dil)
+        if out is None:
+            out = torch.empty(yd, dtype=torch.int8)
+        _check_cpu(out, torch.int8, "out")
+        if tuple(out.shape) != yd:
+            raise OracleError(3)
+        sc = _channel_floats(scale, yd[1], "scale")
+        bi = _channel_floats(bias, yd[1], "bias")
+        rc = self.lib.oracle_conv_fprop_requant(
+            ctypes.c_void_p(x.data_ptr()), _v4(x.shape), _v4(x.stride()),
+            ctypes.c_void_p(w.data_ptr()), _v4(w.shape), _v4(w.stride()),
+            ctypes.c_void_p(out.data_ptr()), _v4(out.shape), _v4(out.stride()),
+            _v2(pre), _v2(post), _v2(stride), _v2(dil),
+            _ptr(sc), ctypes.c_float(alpha), _ptr(bi), int(bool(relu)), int(threads))
+        if rc:
+            raise OracleError(rc)
+        return out
+
+    def requant_values(self, acc, ch, scale=None, alpha: float = 1.0, bias=None,
+                       relu: bool = False) -> np.ndarray:
+        """The requantising epilogue alone: int8 of each exact sum ``acc[i]``
+        taken as output channel ``ch[i]``."""
+        acc = np.ascontiguousarray(np.asarray(acc, dtype=np.int64).reshape(-1))
+        ch = np.ascontiguousarray(np.broadcast_to(np.asarray(ch, dtype=np.int64), acc.shape))
+        if acc.size and (ch.min() < 0 or ((scale is not None or bias is not None) and
+                                          ch.max() >= _nchan(scale, bias))):
+            raise OracleError(1)
+        sc = None if scale is None else np.ascontiguousarray(np.asarray(scale, dtype=np.float32))
+        bi = None if bias is None else np.ascontiguousarray(np.asarray(bias, dtype=np.float32))
+        res = np.empty(acc.shape, dtype=np.int8)
+        rc = self.lib.oracle_requant_values(
+            acc.ctypes.data_as(ctypes.c_void_p), ch.ctypes.data_as(ctypes.c_void_p),
+            ctypes.c_int64(acc.size), _ptr(sc), ctypes.c_float(alpha), _ptr(bi),
+            int(bool(relu)), res.ctypes.data_as(ctypes.c_void_p))
+        if rc:
+            raise OracleError(rc)
+        return res
+
+
+def _nchan(scale, bias) -> int:
+    n = [len(np.asarray(v).reshape(-1)) for v in (scale, bias) if v is not None]
+    return min(n)
+
+
+def _channel_floats(v, k: int, name: str) -> Optional[np.ndarray]:
+    if v is None:
+        return None
+    if isinstance(v, torch.Tensor):
+        v = v.detach().cpu().numpy()
+    a = np.ascontiguousarray(np.asarray(v, dtype=np.float32).reshape(-1))
+    if a.size != k:
+        raise ValueError(f"{name}: expected {k} values, got {a.size}")
+    return a
+
+
+def _ptr(a: Optional[np.ndarray]):
+    return None if a is None else a.ctypes.data_as(ctypes.c_void_p)
+
+
 def _check_cpu(t: torch.Tensor, dtype, name: str):
     if not isinstance(t, torch.Tensor) or t.device.type != "cpu" or t.dtype != dtype or t.dim() != 4:
         raise TypeError(f"{name}: expected a 4-D CPU tensor of {dtype}")
@@ -142,7 +219,8 @@ def load(path: Optional[str] = None) -> Oracle:
     if path is not None:
         return Oracle(path)
     if _DEFAULT is None:
-        if not os.path.exists(_build.LIB):
+        if (not os.path.exists(_build.LIB) or
+                os.path.getmtime(_build.SRC) > os.path.getmtime(_build.LIB)):
             _build.compile_oracle()
         _DEFAULT = Oracle(_build.LIB)
     return _DEFAULT
@@ -158,6 +236,14 @@ def conv_fprop(*a, **k):
 
 def conv_fprop_points(*a, **k):
     return load().conv_fprop_points(*a, **k)
+
+
+def conv_fprop_requant(*a, **k):
+    return load().conv_fprop_requant(*a, **k)
+
+
+def requant_values(*a, **k):
+    return load().requant_values(*a, **k)
 
 
 def max_threads() -> int:

@@ -19,7 +19,7 @@ def compile_oracle(src: str = SRC, out: str = LIB, extra=()) -> str:
     os.makedirs(os.path.dirname(out), exist_ok=True)
     tmp = out + ".tmp"
     cmd = ["gcc", "-O2", "-std=c11", "-fPIC", "-shared", "-fopenmp", "-Wall", "-Wextra",
-           *extra, src, "-o", tmp]
+           *extra, src, "-o", tmp, "-lm"]
     subprocess.run(cmd, check=True)
     os.replace(tmp, out)
     return out

@@ -1,5 +1,6 @@
 /*
- * Plain CPU oracle for INT8 convolution forward with INT32 output.
+ * Plain CPU oracle for INT8 convolution forward with INT32 output, and for
+ * the same convolution followed by a requantising INT8 epilogue.
  *
  * TEST INFRASTRUCTURE ONLY.  Only the tests, the smoke check and the
  * benchmark's CPU-baseline leg load this library.  It shares no source,
@@ -22,7 +23,8 @@
  *   - the filter is indexed [k, c, r, s]; the same loop on that page adds the
  *     channel stride twice for the filter, which is read as a slip for the
  *     output-channel stride plus the input-channel stride;
- *   - no clamp: the result is INT32, not the clamped INT8 of that loop;
+ *   - no clamp in the plain entry: its result is INT32, not the clamped INT8
+ *     of that loop (the clamp belongs to the requantising entry further down);
  *   - padding is zero; pre_padding is added before row/column 0, post_padding
  *     after the last one; spatial pairs are [h, w].
  *
@@ -38,6 +40,7 @@
  * splits only the (batch, output channel) pairs; each output element is
  * summed by one thread in that fixed order.
  */
+#include <math.h>
 #include <stdint.h>
 #include <stddef.h>
 
@@ -204,6 +207,110 @@ int oracle_conv_fprop_points(const int8_t *x, const int64_t xdims[4], const int6
                               pre, stride, dil);
     }
     return ORACLE_OK;
+}
+
+/*
+ * Requantising epilogue: INT8 output with saturation.
+ *
+ * "Building a From-Scratch INT8 Strided Convolution Kernel" clamps each sum
+ * to [-128, 127] before storing it as INT8 (step 2, the naive loop), and its
+ * roadmap ("Extending It") names fusing a ReLU and a quantisation step into
+ * the convolution; the cuDNN frontend tutorial fuses a bias add and a ReLU
+ * into a convolution and hangs an alpha scale off a matmul.  Where the pages
+ * leave the arithmetic open, the reading taken here is, per output element
+ * with exact integer sum acc and output channel k:
+ *
+ *   v = fmaf((float)acc, s_k, b_k)     one IEEE single rounding (fused)
+ *   v = max(v, 0)                      only with relu
+ *   r = nearbyintf(v)                  round half to even
+ *   y = min(max(r, -128), 127)         saturate to INT8
+ *
+ * with s_k = scale[k] (or alpha for every k when scale is NULL) and
+ * b_k = bias[k] (or 0 when bias is NULL).  (float)acc rounds to nearest
+ * even; sums here stay below 2^31.  With s = 1 and no bias or relu this is
+ * exactly the page's clamp.
+ */
+static int8_t oracle_requant(int64_t acc, float s, float b, int relu)
+{
+    float v = fmaf((float)acc, s, b);
+    if (relu && v < 0.0f)
+        v = 0.0f;
+    v = nearbyintf(v);
+    if (v > 127.0f)
+        v = 127.0f;
+    if (v < -128.0f)
+        v = -128.0f;
+    return (int8_t)v;
+}
+
+/* The epilogue above on given sums: acc[i] of output channel ch[i]. */
+int oracle_requant_values(const int64_t *acc, const int64_t *ch, int64_t n,
+                          const float *scale, float alpha, const float *bias, int relu,
+                          int8_t *out)
+{
+    if (n < 0 || (n > 0 && (!acc || !ch || !out)))
+        return ORACLE_ERR_ARG;
+    for (int64_t i = 0; i < n; ++i) {
+        const float s = scale ? scale[ch[i]] : alpha;
+        const float b = bias ? bias[ch[i]] : 0.0f;
+        out[i] = oracle_requant(acc[i], s, b, relu);
+    }
+    return ORACLE_OK;
+}
+
+/*
+ * Convolution followed by the requantising epilogue, INT8 output with any
+ * strides.  scale and bias hold K floats each (or are NULL).  Returns
+ * ORACLE_ERR_OVERFLOW if a sum leaves the int32 range (it is still
+ * requantised from the exact sum).
+ */
+int oracle_conv_fprop_requant(const int8_t *x, const int64_t xdims[4], const int64_t xstr[4],
+                              const int8_t *w, const int64_t wdims[4], const int64_t wstr[4],
+                              int8_t *y, const int64_t ydims[4], const int64_t ystr[4],
+                              const int64_t pre[2], const int64_t post[2],
+                              const int64_t stride[2], const int64_t dil[2],
+                              const float *scale, float alpha, const float *bias, int relu,
+                              int nthreads)
+{
+    int64_t want[4];
+    if (!xstr || !wstr || !ystr)
+        return ORACLE_ERR_ARG;
+    int rc = oracle_out_dims(xdims, wdims, pre, post, stride, dil, want);
+    if (rc != ORACLE_OK)
+        return rc;
+    if ((!x && oracle_elems(xdims) > 0) || (!w && oracle_elems(wdims) > 0) ||
+        (!y && oracle_elems(ydims) > 0))
+        return ORACLE_ERR_ARG;
+    for (int i = 0; i < 4; ++i)
+        if (ydims[i] != want[i])
+            return ORACLE_ERR_OUT_DIMS;
+
+    const int64_t N = ydims[0], K = ydims[1], P = ydims[2], Q = ydims[3];
+    int overflow = 0;
+#ifdef _OPENMP
+    if (nthreads > 0)
+        omp_set_num_threads(nthreads);
+#else
+    (void)nthreads;
+#endif
+#pragma omp parallel for collapse(2) schedule(dynamic, 1) reduction(| : overflow)
+    for (int64_t n = 0; n < N; ++n) {
+        for (int64_t k = 0; k < K; ++k) {
+            const float s = scale ? scale[k] : alpha;
+            const float b = bias ? bias[k] : 0.0f;
+            for (int64_t p = 0; p < P; ++p) {
+                for (int64_t q = 0; q < Q; ++q) {
+                    int64_t acc = oracle_point(x, xdims, xstr, w, wdims, wstr,
+                                               n, k, p, q, pre, stride, dil);
+                    if (acc < INT32_MIN || acc > INT32_MAX)
+                        overflow = 1;
+                    y[n * ystr[0] + k * ystr[1] + p * ystr[2] + q * ystr[3]] =
+                        oracle_requant(acc, s, b, relu);
+                }
+            }
+        }
+    }
+    return overflow ? ORACLE_ERR_OVERFLOW : ORACLE_OK;
 }
 
 /* Threads an OpenMP parallel region gets by default (1 without OpenMP). */

@@ -15,8 +15,17 @@ broken builds of the oracle.
 * the closed forms (delta filters, ones-by-ones counts, constant operands) come
   from the definition on the cuDNN "Convolutions" page, section
   "Convolution Fprop", worked out by hand.
+* ``exact_requant`` evaluates the requantising INT8 epilogue with exact
+  rational arithmetic (``fractions.Fraction``): the fused multiply-add is the
+  exact value ``acc*s + b`` rounded once to the nearest binary32 (ties to an
+  even significand, found by comparing the neighbouring binary32 values
+  exactly), then ReLU, Python's ``round`` (half to even) and the clamp to
+  [-128, 127] of the INT8 store in "Building a From-Scratch INT8 Strided
+  Convolution Kernel", step 2.
 """
 from __future__ import annotations
+
+from fractions import Fraction
 
 import numpy as np
 import torch
@@ -267,7 +276,135 @@ def check_points(orc) -> None:
     assert np.array_equal(v, y[idx[:, 0], idx[:, 1], idx[:, 2], idx[:, 3]].astype(np.int64))
 
 
+def _f32_nearest(fr: Fraction) -> np.float32:
+    """The binary32 value nearest to the exact rational ``fr``, ties to an
+    even significand (no overflow: |fr| stays far below 2**127 here)."""
+    if fr == 0:
+        return np.float32(0.0)
+    c = np.float32(float(fr))              # within one ulp of the answer
+    cands = {float(c), float(np.nextafter(c, np.float32(np.inf))),
+             float(np.nextafter(c, np.float32(-np.inf)))}
+
+    def key(v):
+        odd = int(np.array(v, dtype=np.float32).view(np.uint32)) & 1
+        return (abs(Fraction(v) - fr), odd)
+    return np.float32(min(cands, key=key))
+
+
+def exact_requant(acc: int, s: float, b: float, relu: bool) -> int:
+    """INT8 epilogue of one exact sum: binary32(acc) * s + b rounded once,
+    ReLU, round half to even, saturate."""
+    a = _f32_nearest(Fraction(int(acc)))   # the sum as a binary32 value
+    v = _f32_nearest(Fraction(float(a)) * Fraction(float(np.float32(s))) +
+                     Fraction(float(np.float32(b))))
+    v = float(v)
+    if relu and v < 0:
+        v = 0.0
+    r = round(v)                           # half to even
+    return max(-128, min(127, r))
+
+
+def check_requant_forum_bytes(orc, golden) -> None:
+    """Scale 1, no bias, no ReLU is the saturating INT8 store: the forum's
+    torch results become exactly the bytes its INT8 cuDNN output held."""
+    truth = np.array(golden["torch_conv2d_int32"], dtype=np.int64).reshape(-1)
+    got = orc.requant_values(truth, 0)
+    buf = np.zeros(len(truth) * 4, dtype=np.uint8)
+    buf[:len(truth)] = got.view(np.uint8)
+    assert buf.view("<i4").reshape(3, 3).tolist() == golden["cudnn_output_int32"]
+
+
+def _muladd_differs_cases(n: int = 200000, seed: int = 23):
+    """(acc, s, b) where one rounding (fused) and two roundings (multiply,
+    then add) give different INT8 results: acc*s lies just above some k+1/2
+    but rounds to it as binary32, and b = -floor(.) cancels the integer part.
+    All values are exact in float64 (acc < 2**17, s has 24 bits)."""
+    rng = np.random.default_rng(seed)
+    acc = rng.integers(1000, 1 << 17, n).astype(np.float64)
+    s = rng.uniform(0.25, 4.0, n).astype(np.float32).astype(np.float64)
+    p = acc * s                                   # exact
+    p32 = p.astype(np.float32).astype(np.float64)
+    hit = (p32 - np.floor(p32) == 0.5) & (p > p32)
+    b = -np.floor(p32[hit])
+    return acc[hit].astype(np.int64), s[hit].astype(np.float32), b.astype(np.float32)
+
+
+def check_requant_exact(orc) -> None:
+    """The epilogue equals the exact rational evaluation on ties, large sums
+    (beyond 2**24, where binary32 rounds the sum), cancellations that tell a
+    fused multiply-add from a multiply then an add, and random values; also
+    the ReLU identity and per-channel indexing."""
+    rng = np.random.default_rng(29)
+    accs, scales, biases = [], [], []
+    # exact ties k + 1/2 (scale 1/2, 1/4): half to even
+    t = np.arange(-301, 302, dtype=np.int64)
+    accs += [t, t]
+    scales += [np.full(t.size, 0.5, np.float32), np.full(t.size, 0.25, np.float32)]
+    biases += [np.zeros(t.size, np.float32), np.zeros(t.size, np.float32)]
+    # large sums: binary32 rounds them; tiny scales bring them into range
+    big = np.concatenate([rng.integers(1 << 24, (1 << 31) - 1, 300),
+                          -rng.integers(1 << 24, 1 << 31, 300),
+                          np.array([(1 << 24) + 1, (1 << 24) + 3, (1 << 25) + 2, 2147483647,
+                                    -2147483648])]).astype(np.int64)
+    accs.append(big)
+    scales.append((2.0 ** rng.integers(-26, -18, big.size)).astype(np.float32))
+    biases.append(rng.uniform(-3, 3, big.size).astype(np.float32))
+    # fused vs unfused
+    a, s_, b = _muladd_differs_cases()
+    assert a.size >= 20, "search found too few cancellation cases"
+    accs.append(a[:200])
+    scales.append(s_[:200])
+    biases.append(b[:200])
+    # random
+    r = rng.integers(-(1 << 27), 1 << 27, 2000).astype(np.int64)
+    accs.append(r)
+    scales.append((rng.choice([-1, 1], r.size) * 2.0 ** rng.uniform(-24, 0, r.size)).astype(np.float32))
+    biases.append(rng.uniform(-300, 300, r.size).astype(np.float32))
+    acc = np.concatenate(accs)
+    sc = np.concatenate(scales)
+    bi = np.concatenate(biases)
+    ch = np.arange(acc.size, dtype=np.int64)     # one channel per value: per-channel lookup
+    for relu in (False, True):
+        got = orc.requant_values(acc, ch, scale=sc, bias=bi, relu=relu)
+        want = np.array([exact_requant(int(x), float(y), float(z), relu)
+                         for x, y, z in zip(acc, sc, bi)], dtype=np.int8)
+        bad = np.nonzero(got != want)[0]
+        assert bad.size == 0, (relu, [(int(acc[i]), float(sc[i]), float(bi[i]), int(got[i]),
+                                       int(want[i])) for i in bad[:5]])
+        if relu:
+            assert np.array_equal(got, np.maximum(orc.requant_values(acc, ch, scale=sc, bias=bi), 0))
+    # alpha applies to every channel when there is no scale array
+    got = orc.requant_values(t, 0, alpha=0.5)
+    assert np.array_equal(got, np.array([exact_requant(int(x), 0.5, 0.0, False) for x in t], np.int8))
+
+
+def check_requant_conv(orc) -> None:
+    """The fused entry = the INT32 convolution followed by the exact epilogue,
+    with per-output-channel scale and bias, into a strided INT8 output."""
+    rng = np.random.default_rng(31)
+    x = rand_i8(rng, (2, 5, 7, 6))
+    w = rand_i8(rng, (6, 5, 3, 2))
+    a = dict(pre=(1, 0), post=(2, 1), stride=(2, 1), dil=(1, 2))
+    y = orc.conv_fprop(x, w, **a).numpy().astype(np.int64)
+    N, K, P, Q = y.shape
+    sc = (rng.choice([-1, 1], K) * 2.0 ** rng.uniform(-9, -4, K)).astype(np.float32)
+    bi = rng.uniform(-40, 40, K).astype(np.float32)
+    for relu in (False, True):
+        base = torch.full((N, P, Q, 2 * K), 99, dtype=torch.int8)
+        out = base[..., ::2].permute(0, 3, 1, 2)         # NHWC view with gaps
+        orc.conv_fprop_requant(x, w, scale=sc, bias=bi, relu=relu, out=out, **a)
+        want = np.array([[[[exact_requant(y[n, k, p, q], sc[k], bi[k], relu) for q in range(Q)]
+                           for p in range(P)] for k in range(K)] for n in range(N)], dtype=np.int8)
+        assert np.array_equal(out.numpy(), want)
+        assert (base[..., 1::2] == 99).all()
+    # alpha with no arrays
+    got = orc.conv_fprop_requant(x, w, alpha=0.125, **a).numpy()
+    want = np.vectorize(lambda v: exact_requant(int(v), 0.125, 0.0, False))(y).astype(np.int8)
+    assert np.array_equal(got, want)
+
+
 QUICK_CHECKS = [
     check_random_vs_brute_force, check_offcentre_delta, check_identity_1x1, check_ones_count,
-    check_constant_min, check_layouts, check_metamorphic, check_points,
+    check_constant_min, check_layouts, check_metamorphic, check_points, check_requant_exact,
+    check_requant_conv,
 ]

@@ -98,6 +98,20 @@ def test_forum_output_decode():
     assert as_i32.tolist() == g["cudnn_output_int32"]
 
 
+def test_requant_forum_bytes(orc):
+    """The requantising epilogue at scale 1 reproduces the bytes of the forum's
+    INT8 cuDNN output from its torch results."""
+    pins.check_requant_forum_bytes(orc, _golden("forum_5x5_r3.json"))
+
+
+def test_requant_exact(orc):
+    pins.check_requant_exact(orc)
+
+
+def test_requant_conv(orc):
+    pins.check_requant_conv(orc)
+
+
 @pytest.mark.parametrize("name", wl.CASE_ORDER)
 def test_workloads_vs_f64_library_conv(orc, name):
     """Oracle == float64 torch conv2d on every workload at full size."""
@@ -169,6 +183,14 @@ MUTATIONS = [
     ("output size ignores post padding", "in + pre + post - dil", "in + pre - dil"),
     ("output written transposed", "p * ystr[2] + q * ystr[3]", "q * ystr[2] + p * ystr[3]"),
     ("saturating int8 store", "(int32_t)(uint32_t)(uint64_t)acc", "(int32_t)(acc > 127 ? 127 : acc < -128 ? -128 : acc)"),
+    ("requant truncates", "v = nearbyintf(v);", "v = truncf(v);"),
+    ("requant rounds half away from zero", "v = nearbyintf(v);", "v = roundf(v);"),
+    ("requant multiplies then adds", "fmaf((float)acc, s, b)", "((float)acc * s + b)"),
+    ("requant ReLU dropped", "if (relu && v < 0.0f)", "if (0 && relu && v < 0.0f)"),
+    ("requant clamps at -127", "if (v < -128.0f)\n        v = -128.0f;", "if (v < -127.0f)\n        v = -127.0f;"),
+    ("requant per-tensor scale", "const float s = scale ? scale[k] : alpha;", "const float s = scale ? scale[0] : alpha;"),
+    ("requant bias ignored", "const float b = bias ? bias[k] : 0.0f;", "const float b = 0.0f;"),
+    ("requant channel from the wrong index", "scale ? scale[ch[i]] : alpha", "scale ? scale[i % 2] : alpha"),
 ]
 
 
