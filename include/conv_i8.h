@@ -15,10 +15,12 @@
  * From-Scratch INT8 Strided Convolution Kernel", "Step 2", reads the input at
  * oh*stride + kh against kernel tap kh).  The result is exact: every product
  * of two int8 values is summed in 32-bit integers, which cannot overflow while
- * C*R*S <= 131071 (|product| <= 16384); larger reductions are refused.  There
- * is no saturation and no int8 output (the forum thread "INT8 convolution
- * using cuDNN Python Frontend" shows what an int8 output descriptor produces:
- * the true sums clamped to int8 and packed into the int32 buffer).
+ * C*R*S <= 131071 (|product| <= 16384); larger reductions are refused.  The
+ * plain entries never saturate and refuse an int8 output (the forum thread
+ * "INT8 convolution using cuDNN Python Frontend" shows what an int8 output
+ * descriptor produces there: the true sums clamped to int8 and packed into
+ * the int32 buffer).  The separate requantising entries at the end of this
+ * file write int8 on purpose, through an explicit epilogue.
  *
  * Output size: P = floor((H + pre_h + post_h - dil_h*(R-1) - 1) / stride_h) + 1,
  * and Q likewise; a negative numerator is an error.
@@ -163,6 +165,84 @@ conv_i8_status_t conv_fprop_i8_plan(const conv_i8_desc_t *image, const void *ima
                                     const int64_t stride[2],
                                     const int64_t dilation[2],
                                     char *buf, size_t len);
+
+/*
+ * Requantising INT8 epilogue, fused into the convolution.
+ *
+ * The naive loop of "Building a From-Scratch INT8 Strided Convolution
+ * Kernel" (step 2) clamps each sum to [-128, 127] and stores it as INT8, and
+ * the page's roadmap ("Extending It") fuses a ReLU and a quantisation step
+ * into the convolution to save the DRAM round trip of the wide sums; the
+ * cuDNN frontend tutorial fuses a bias add and ReLU into a convolution and
+ * scales a matmul by a host scalar alpha.  Here, for output element
+ * (n, k, p, q) with exact sum acc (as in conv_fprop_i8):
+ *
+ *   v = fmaf((float)acc, s_k, b_k)   float conversion rounds to nearest even,
+ *                                    then one fused multiply-add (one rounding)
+ *   v = max(v, 0)                    only when relu != 0
+ *   y = clamp(rint(v), -128, 127)    round half to even, saturate
+ *
+ * s_k = scale[k] when scale != NULL, else alpha; b_k = bias[k] when
+ * bias != NULL, else 0.  scale and bias are device pointers to K floats,
+ * 4-byte aligned, owned by the caller and read by the kernels on `stream`.
+ * Non-finite scales or biases give unspecified bytes.  With alpha = 1 and no
+ * bias or relu the result is the page's saturating INT8 store.
+ */
+typedef struct {
+    const float *scale;  /* K per-output-channel scales, or NULL: alpha for all */
+    float alpha;         /* used when scale == NULL; must be finite then */
+    const float *bias;   /* K per-output-channel biases, or NULL: no bias */
+    int32_t relu;        /* nonzero: negative values become 0 before rounding */
+} conv_i8_requant_t;
+
+/*
+ * Workspace bytes for conv_fprop_i8_requant_ws: the same rules as
+ * conv_fprop_i8_workspace_size, for an INT8 output descriptor
+ * (CONV_I8_ERR_DTYPE otherwise).  Host-only.
+ */
+conv_i8_status_t conv_fprop_i8_requant_workspace_size(const conv_i8_desc_t *image,
+                                                      const void *image_ptr,
+                                                      const conv_i8_desc_t *filter,
+                                                      const void *filter_ptr,
+                                                      const conv_i8_desc_t *out,
+                                                      const int64_t pre_padding[2],
+                                                      const int64_t post_padding[2],
+                                                      const int64_t stride[2],
+                                                      const int64_t dilation[2],
+                                                      size_t *workspace_bytes);
+
+/*
+ * conv_fprop followed by the requantising epilogue above, INT8 output [N, K,
+ * P, Q] with any non-overlapping strides (CONV_I8_ERR_DTYPE for any other
+ * output dtype; CONV_I8_ERR_NULL for rq == NULL; CONV_I8_ERR_PARAM for a
+ * misaligned scale/bias array or a non-finite alpha without a scale array).
+ * Workspace, errors and stream behaviour as conv_fprop_i8_ws: never
+ * allocates, never synchronises.
+ */
+conv_i8_status_t conv_fprop_i8_requant_ws(const conv_i8_desc_t *image, const void *image_ptr,
+                                          const conv_i8_desc_t *filter, const void *filter_ptr,
+                                          const conv_i8_desc_t *out, void *out_ptr,
+                                          const int64_t pre_padding[2],
+                                          const int64_t post_padding[2],
+                                          const int64_t stride[2],
+                                          const int64_t dilation[2],
+                                          const conv_i8_requant_t *rq,
+                                          void *workspace, size_t workspace_bytes,
+                                          void *stream);
+
+/*
+ * Same as conv_fprop_i8_requant_ws, with any workspace taken and released
+ * stream-ordered (hipMallocAsync / hipFreeAsync) as in conv_fprop_i8.
+ */
+conv_i8_status_t conv_fprop_i8_requant(const conv_i8_desc_t *image, const void *image_ptr,
+                                       const conv_i8_desc_t *filter, const void *filter_ptr,
+                                       const conv_i8_desc_t *out, void *out_ptr,
+                                       const int64_t pre_padding[2],
+                                       const int64_t post_padding[2],
+                                       const int64_t stride[2],
+                                       const int64_t dilation[2],
+                                       const conv_i8_requant_t *rq,
+                                       void *stream);
 
 /* Static string naming a status code. */
 const char *conv_i8_status_string(conv_i8_status_t status);

@@ -8,8 +8,11 @@ PyTorch provides the device memory (outputs, workspace) and the stream.
 The operation is the one of the cuDNN "Convolutions" page ("Convolution
 Fprop"): image [N,C,H,W] int8, weight [K,C,R,S] int8 -> [N,K,P,Q] int32, with
 pre/post padding, stride and dilation as in its Python API list; the
-symmetric ``padding`` overload sets pre = post.  If the compiled library is
-missing this module raises on import: there is no fallback implementation.
+symmetric ``padding`` overload sets pre = post.  The requantising entries
+write int8 instead: fma(float(sum), scale[k], bias[k]), optional ReLU, round
+half to even, saturate (see ``conv_fprop_i8_requant``).  If the compiled
+library is missing this module raises on import: there is no fallback
+implementation.
 """
 from __future__ import annotations
 
@@ -25,6 +28,8 @@ from . import build as _build
 __all__ = [
     "ConvI8Error", "conv_fprop_i8", "conv_fprop_i8_ws", "conv_fprop_i8_plain",
     "conv_fprop_i8_out_dims", "conv_fprop_i8_workspace_size", "conv_fprop_i8_plan",
+    "conv_fprop_i8_requant", "conv_fprop_i8_requant_ws", "conv_fprop_i8_requant_plain",
+    "conv_fprop_i8_requant_workspace_size", "Requant",
     "status_string", "LIB_PATH", "DT_INT8", "DT_INT32", "MAX_REDUCTION", "lib",
 ]
 
@@ -44,6 +49,12 @@ STATUS = {
 class Desc(ctypes.Structure):
     _fields_ = [("dtype", ctypes.c_int32), ("ndim", ctypes.c_int32),
                 ("dims", ctypes.c_int64 * 4), ("strides", ctypes.c_int64 * 4)]
+
+
+class Requant(ctypes.Structure):
+    """conv_i8_requant_t: per-channel scale (or alpha), bias, ReLU flag."""
+    _fields_ = [("scale", ctypes.c_void_p), ("alpha", ctypes.c_float),
+                ("bias", ctypes.c_void_p), ("relu", ctypes.c_int32)]
 
 
 class ConvI8Error(RuntimeError):
@@ -71,10 +82,17 @@ lib.conv_fprop_i8_ws.argtypes = [_DP, _P, _DP, _P, _DP, _P, _V2, _V2, _V2, _V2, 
 lib.conv_fprop_i8.argtypes = [_DP, _P, _DP, _P, _DP, _P, _V2, _V2, _V2, _V2, _P]
 lib.conv_fprop_i8_plan.argtypes = [_DP, _P, _DP, _P, _DP, _V2, _V2, _V2, _V2,
                                    ctypes.c_char_p, ctypes.c_size_t]
+_RQ = ctypes.POINTER(Requant)
+lib.conv_fprop_i8_requant_workspace_size.argtypes = [_DP, _P, _DP, _P, _DP, _V2, _V2, _V2, _V2,
+                                                     ctypes.POINTER(ctypes.c_size_t)]
+lib.conv_fprop_i8_requant_ws.argtypes = [_DP, _P, _DP, _P, _DP, _P, _V2, _V2, _V2, _V2, _RQ, _P,
+                                         ctypes.c_size_t, _P]
+lib.conv_fprop_i8_requant.argtypes = [_DP, _P, _DP, _P, _DP, _P, _V2, _V2, _V2, _V2, _RQ, _P]
 lib.conv_i8_status_string.argtypes = [ctypes.c_int]
 lib.conv_i8_status_string.restype = ctypes.c_char_p
 for _f in ("conv_fprop_i8_out_dims", "conv_fprop_i8_workspace_size", "conv_fprop_i8_ws",
-           "conv_fprop_i8", "conv_fprop_i8_plan"):
+           "conv_fprop_i8", "conv_fprop_i8_plan", "conv_fprop_i8_requant_workspace_size",
+           "conv_fprop_i8_requant_ws", "conv_fprop_i8_requant"):
     getattr(lib, _f).restype = ctypes.c_int
 
 
@@ -143,11 +161,11 @@ def _as_desc(t) -> Desc:
     return t if isinstance(t, Desc) else desc(t)
 
 
-def _out_like(x: torch.Tensor, dims) -> torch.Tensor:
+def _out_like(x: torch.Tensor, dims, dtype=torch.int32) -> torch.Tensor:
     fmt = torch.contiguous_format
     if x.dim() == 4 and x.is_contiguous(memory_format=torch.channels_last) and not x.is_contiguous():
         fmt = torch.channels_last
-    return torch.empty(dims, dtype=torch.int32, device=x.device, memory_format=fmt)
+    return torch.empty(dims, dtype=dtype, device=x.device, memory_format=fmt)
 
 
 def conv_fprop_i8_workspace_size(x, w, out, pre_padding=0, post_padding=0, stride=1,
@@ -234,3 +252,85 @@ def conv_fprop_i8(x: torch.Tensor, w: torch.Tensor, out: Optional[torch.Tensor] 
     ws = torch.empty(n, dtype=torch.uint8, device=out.device) if n else None
     return conv_fprop_i8_ws(x, w, out, ws, pre_padding, post_padding, stride, dilation, padding,
                             stream)
+
+
+def _requant(scale, alpha, bias, relu) -> Requant:
+    """The C parameter block; scale and bias are float32 device tensors of K
+    values (the caller keeps them alive until the stream has run the call)."""
+    for name, t in (("scale", scale), ("bias", bias)):
+        if t is not None and (not isinstance(t, torch.Tensor) or t.dtype != torch.float32
+                              or not t.is_contiguous()):
+            raise TypeError(f"{name}: expected a contiguous float32 tensor")
+    return Requant(_ptr(scale), float(alpha), _ptr(bias), 1 if relu else 0)
+
+
+def _check_channels(w, t, name):
+    if t is not None and t.numel() != w.shape[0]:
+        raise ValueError(f"{name}: expected {w.shape[0]} values (one per output channel)")
+
+
+def conv_fprop_i8_requant_workspace_size(x, w, out, pre_padding=0, post_padding=0, stride=1,
+                                         dilation=1, padding=None) -> int:
+    pre, post, st, dl = _params(pre_padding, post_padding, stride, dilation, padding)
+    n = ctypes.c_size_t()
+    xp = _ptr(x) if isinstance(x, torch.Tensor) else None
+    wp = _ptr(w) if isinstance(w, torch.Tensor) else None
+    _check(lib.conv_fprop_i8_requant_workspace_size(
+        ctypes.byref(_as_desc(x)), xp, ctypes.byref(_as_desc(w)), wp, ctypes.byref(_as_desc(out)),
+        pre, post, st, dl, ctypes.byref(n)))
+    return int(n.value)
+
+
+def conv_fprop_i8_requant_ws(x: torch.Tensor, w: torch.Tensor, out: torch.Tensor,
+                             workspace: Optional[torch.Tensor], scale=None, alpha: float = 1.0,
+                             bias=None, relu: bool = False, pre_padding=0, post_padding=0,
+                             stride=1, dilation=1, padding=None, stream=None) -> torch.Tensor:
+    """Direct call of the requantising C entry with an explicit workspace."""
+    pre, post, st, dl = _params(pre_padding, post_padding, stride, dilation, padding)
+    rq = _requant(scale, alpha, bias, relu)
+    ws_ptr = _ptr(workspace)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(lib.conv_fprop_i8_requant_ws(
+        ctypes.byref(desc(x)), _ptr(x), ctypes.byref(desc(w)), _ptr(w), ctypes.byref(desc(out)),
+        _ptr(out), pre, post, st, dl, ctypes.byref(rq), ws_ptr, ctypes.c_size_t(ws_bytes),
+        _stream_handle(stream)))
+    return out
+
+
+def conv_fprop_i8_requant_plain(x: torch.Tensor, w: torch.Tensor, out: torch.Tensor, scale=None,
+                                alpha: float = 1.0, bias=None, relu: bool = False, pre_padding=0,
+                                post_padding=0, stride=1, dilation=1, padding=None,
+                                stream=None) -> torch.Tensor:
+    """The requantising C entry that takes its own workspace (hipMallocAsync)."""
+    pre, post, st, dl = _params(pre_padding, post_padding, stride, dilation, padding)
+    rq = _requant(scale, alpha, bias, relu)
+    _check(lib.conv_fprop_i8_requant(
+        ctypes.byref(desc(x)), _ptr(x), ctypes.byref(desc(w)), _ptr(w), ctypes.byref(desc(out)),
+        _ptr(out), pre, post, st, dl, ctypes.byref(rq), _stream_handle(stream)))
+    return out
+
+
+def conv_fprop_i8_requant(x: torch.Tensor, w: torch.Tensor, scale: Optional[torch.Tensor] = None,
+                          alpha: float = 1.0, bias: Optional[torch.Tensor] = None,
+                          relu: bool = False, out: Optional[torch.Tensor] = None, pre_padding=0,
+                          post_padding=0, stride=1, dilation=1, padding=None,
+                          stream=None) -> torch.Tensor:
+    """int8 Y = saturate(rint(relu?(fma(float(conv(x, w)), s_k, b_k)))).
+
+    ``scale`` and ``bias``: float32 device tensors of K values, or None
+    (``alpha`` for every channel; no bias).  ``out`` (int8 [N,K,P,Q], any
+    non-overlapping strides) is written if given; otherwise a new tensor in
+    x's memory format.  The fused epilogue of the from-scratch kernel page's
+    roadmap (ReLU and quantisation after the convolution, INT8 store with the
+    clamp of its naive loop).
+    """
+    _check_channels(w, scale, "scale")
+    _check_channels(w, bias, "bias")
+    if out is None:
+        dims = conv_fprop_i8_out_dims(x, w, pre_padding, post_padding, stride, dilation, padding)
+        out = _out_like(x, dims, torch.int8)
+    n = conv_fprop_i8_requant_workspace_size(x, w, out, pre_padding, post_padding, stride,
+                                             dilation, padding)
+    ws = torch.empty(n, dtype=torch.uint8, device=out.device) if n else None
+    return conv_fprop_i8_requant_ws(x, w, out, ws, scale, alpha, bias, relu, pre_padding,
+                                    post_padding, stride, dilation, padding, stream)

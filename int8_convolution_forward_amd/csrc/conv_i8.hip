@@ -173,14 +173,15 @@ conv_i8_status_t analyze_inputs(const conv_i8_desc_t *image, const conv_i8_desc_
 
 conv_i8_status_t analyze(const conv_i8_desc_t *image, const conv_i8_desc_t *filter,
                          const conv_i8_desc_t *out, const int64_t *pre, const int64_t *post,
-                         const int64_t *stride, const int64_t *dil, Problem *pb)
+                         const int64_t *stride, const int64_t *dil, int32_t out_dtype, Problem *pb)
 {
     conv_i8_status_t st = analyze_inputs(image, filter, pre, post, stride, dil, pb);
     if (st != CONV_I8_OK)
         return st;
-    // The output dtype is checked like every other field: an INT8 output
-    // descriptor is refused rather than written as saturated bytes.
-    if ((st = read_desc(out, CONV_I8_DT_INT32, &pb->y)) != CONV_I8_OK)
+    // The output dtype is checked like every other field: the plain entries
+    // refuse an INT8 output descriptor rather than write saturated bytes into
+    // it; only the requantising entries write INT8.
+    if ((st = read_desc(out, out_dtype, &pb->y)) != CONV_I8_OK)
         return st;
     const int64_t want[4] = {pb->N, pb->K, pb->P, pb->Q};
     for (int i = 0; i < 4; ++i)
@@ -676,8 +677,9 @@ conv_i8_status_t launch_repacks(const RepackJob *jobs, int njobs, hipStream_t st
 }
 
 conv_i8_status_t run(const Problem &pb, const Plan &pl, const void *x_ptr, const void *w_ptr,
-                     void *y_ptr, void *ws, hipStream_t stream)
+                     void *y_ptr, void *ws, hipStream_t stream, const conv_i8_requant_t *rq = nullptr)
 {
+    const int64_t esize = rq ? 1 : 4;        // bytes per output element
     const int8_t *x = (const int8_t *)x_ptr;
     const int8_t *w = (const int8_t *)w_ptr;
     int8_t *wsb = (int8_t *)ws;
@@ -737,12 +739,19 @@ conv_i8_status_t run(const Problem &pb, const Plan &pl, const void *x_ptr, const
     a.Pr = (int)pl.Pr;
     a.inv_pr = pl.Pr > 0 ? 1.0f / (float)pl.Pr : 0.0f;
     a.ncblk = (int)(pl.Cp / 64);
+    if (rq) {
+        a.q8 = 1;
+        a.q_scale = rq->scale;
+        a.q_bias = rq->bias;
+        a.q_alpha = rq->alpha;
+        a.q_relu = rq->relu ? 1 : 0;
+    }
     for (int64_t n0 = 0; n0 < pb.N; n0 += pl.batch_chunk) {
         const int64_t nb = std::min(pl.batch_chunk, pb.N - n0);
         a.img = x + n0 * pl.xsN;
         a.img_range = (int)((nb - 1) * pl.xsN + pl.x_img_span);
-        a.out = (int32_t *)y_ptr + n0 * pb.y.s[0];
-        a.out_range = (int)(((nb - 1) * pb.y.s[0] + pl.y_img_span) * 4);
+        a.out = (int32_t *)((int8_t *)y_ptr + n0 * pb.y.s[0] * esize);
+        a.out_range = (int)(((nb - 1) * pb.y.s[0] + pl.y_img_span) * esize);
         a.N = (int)nb;
         a.sN = (int)pl.xsN;
         a.M = (int)(nb * pb.P * pb.Q);
@@ -781,9 +790,11 @@ int g_plan_count = 0, g_plan_next = 0;
 conv_i8_status_t prepare(const conv_i8_desc_t *image, const void *image_ptr,
                          const conv_i8_desc_t *filter, const void *filter_ptr,
                          const conv_i8_desc_t *out, const int64_t *pre, const int64_t *post,
-                         const int64_t *stride, const int64_t *dil, Problem *pb, Plan *pl)
+                         const int64_t *stride, const int64_t *dil, Problem *pb, Plan *pl,
+                         int32_t out_dtype = CONV_I8_DT_INT32)
 {
-    conv_i8_status_t st = analyze(image, filter, out, pre, post, stride, dil, pb);
+    // The plan does not depend on the output dtype (it works in elements).
+    conv_i8_status_t st = analyze(image, filter, out, pre, post, stride, dil, out_dtype, pb);
     if (st != CONV_I8_OK)
         return st;
     PlanKey key;
@@ -812,6 +823,19 @@ conv_i8_status_t prepare(const conv_i8_desc_t *image, const void *image_ptr,
         g_plan_count = std::min(g_plan_count + 1, kPlanCache);
     }
     return st;
+}
+
+// Requantisation parameters: present, 4-byte aligned arrays, a finite alpha
+// when there is no scale array.
+conv_i8_status_t check_requant(const conv_i8_requant_t *rq)
+{
+    if (!rq)
+        return CONV_I8_ERR_NULL;
+    if (((uintptr_t)rq->scale & 3u) != 0 || ((uintptr_t)rq->bias & 3u) != 0)
+        return CONV_I8_ERR_PARAM;
+    if (!rq->scale && !(rq->alpha == rq->alpha && rq->alpha - rq->alpha == 0.0f))
+        return CONV_I8_ERR_PARAM;
+    return CONV_I8_OK;
 }
 
 conv_i8_status_t check_ptrs(const Problem &pb, const void *x, const void *w, const void *y)
@@ -946,15 +970,97 @@ conv_i8_status_t conv_fprop_i8(const conv_i8_desc_t *image, const void *image_pt
     return st;
 }
 
+conv_i8_status_t conv_fprop_i8_requant_workspace_size(
+    const conv_i8_desc_t *image, const void *image_ptr, const conv_i8_desc_t *filter,
+    const void *filter_ptr, const conv_i8_desc_t *out, const int64_t pre_padding[2],
+    const int64_t post_padding[2], const int64_t stride[2], const int64_t dilation[2],
+    size_t *workspace_bytes)
+{
+    if (!workspace_bytes)
+        return CONV_I8_ERR_NULL;
+    Problem pb;
+    Plan pl;
+    conv_i8_status_t st = prepare(image, image_ptr, filter, filter_ptr, out, pre_padding,
+                                  post_padding, stride, dilation, &pb, &pl, CONV_I8_DT_INT8);
+    if (st != CONV_I8_OK)
+        return st;
+    *workspace_bytes = pb.y.elems() == 0 || pb.C == 0 ? 0 : pl.ws_bytes;
+    return CONV_I8_OK;
+}
+
+conv_i8_status_t conv_fprop_i8_requant_ws(const conv_i8_desc_t *image, const void *image_ptr,
+                                          const conv_i8_desc_t *filter, const void *filter_ptr,
+                                          const conv_i8_desc_t *out, void *out_ptr,
+                                          const int64_t pre_padding[2],
+                                          const int64_t post_padding[2], const int64_t stride[2],
+                                          const int64_t dilation[2], const conv_i8_requant_t *rq,
+                                          void *workspace, size_t workspace_bytes, void *stream)
+{
+    Problem pb;
+    Plan pl;
+    conv_i8_status_t st = prepare(image, image_ptr, filter, filter_ptr, out, pre_padding,
+                                  post_padding, stride, dilation, &pb, &pl, CONV_I8_DT_INT8);
+    if (st != CONV_I8_OK)
+        return st;
+    if ((st = check_requant(rq)) != CONV_I8_OK)
+        return st;
+    if ((st = check_ptrs(pb, image_ptr, filter_ptr, out_ptr)) != CONV_I8_OK)
+        return st;
+    if (pb.y.elems() == 0)
+        return CONV_I8_OK;
+    const size_t need = pb.C == 0 ? 0 : pl.ws_bytes;
+    if (workspace_bytes < need)
+        return CONV_I8_ERR_WORKSPACE;
+    if (need > 0 && !workspace)
+        return CONV_I8_ERR_NULL;
+    if (need > 0 && ((uintptr_t)workspace & 255u) != 0)
+        return CONV_I8_ERR_WORKSPACE;
+    if (log_enabled())
+        fprintf(stderr, "conv_i8 (requant): %s\n", describe(pb, pl).c_str());
+    return run(pb, pl, image_ptr, filter_ptr, out_ptr, workspace, (hipStream_t)stream, rq);
+}
+
+conv_i8_status_t conv_fprop_i8_requant(const conv_i8_desc_t *image, const void *image_ptr,
+                                       const conv_i8_desc_t *filter, const void *filter_ptr,
+                                       const conv_i8_desc_t *out, void *out_ptr,
+                                       const int64_t pre_padding[2], const int64_t post_padding[2],
+                                       const int64_t stride[2], const int64_t dilation[2],
+                                       const conv_i8_requant_t *rq, void *stream)
+{
+    Problem pb;
+    Plan pl;
+    conv_i8_status_t st = prepare(image, image_ptr, filter, filter_ptr, out, pre_padding,
+                                  post_padding, stride, dilation, &pb, &pl, CONV_I8_DT_INT8);
+    if (st != CONV_I8_OK)
+        return st;
+    if ((st = check_requant(rq)) != CONV_I8_OK)
+        return st;
+    if ((st = check_ptrs(pb, image_ptr, filter_ptr, out_ptr)) != CONV_I8_OK)
+        return st;
+    if (pb.y.elems() == 0)
+        return CONV_I8_OK;
+    const size_t need = pb.C == 0 ? 0 : pl.ws_bytes;
+    hipStream_t s = (hipStream_t)stream;
+    void *ws = nullptr;
+    if (need > 0 && hipMallocAsync(&ws, need, s) != hipSuccess)
+        return CONV_I8_ERR_HIP;
+    if (log_enabled())
+        fprintf(stderr, "conv_i8 (requant): %s\n", describe(pb, pl).c_str());
+    st = run(pb, pl, image_ptr, filter_ptr, out_ptr, ws, s, rq);
+    if (ws && hipFreeAsync(ws, s) != hipSuccess && st == CONV_I8_OK)
+        st = CONV_I8_ERR_HIP;
+    return st;
+}
+
 const char *conv_i8_status_string(conv_i8_status_t status)
 {
     switch (status) {
     case CONV_I8_OK: return "CONV_I8_OK";
     case CONV_I8_ERR_NULL: return "CONV_I8_ERR_NULL: a required pointer is NULL";
-    case CONV_I8_ERR_DTYPE: return "CONV_I8_ERR_DTYPE: image/filter must be INT8 and the output INT32";
+    case CONV_I8_ERR_DTYPE: return "CONV_I8_ERR_DTYPE: image/filter must be INT8 and the output INT32 (INT8 for the requantising entries)";
     case CONV_I8_ERR_RANK: return "CONV_I8_ERR_RANK: descriptors must have ndim == 4";
     case CONV_I8_ERR_DIMS: return "CONV_I8_ERR_DIMS: negative dim, or filter R or S < 1";
-    case CONV_I8_ERR_PARAM: return "CONV_I8_ERR_PARAM: stride and dilation must be >= 1, padding >= 0";
+    case CONV_I8_ERR_PARAM: return "CONV_I8_ERR_PARAM: stride and dilation must be >= 1, padding >= 0; requantisation arrays 4-byte aligned, alpha finite";
     case CONV_I8_ERR_CHANNELS: return "CONV_I8_ERR_CHANNELS: image C != filter C";
     case CONV_I8_ERR_OUT_DIMS: return "CONV_I8_ERR_OUT_DIMS: output dims must be [N, K, P, Q] with P, Q >= 1";
     case CONV_I8_ERR_STRIDES: return "CONV_I8_ERR_STRIDES: negative stride or self-overlapping output";

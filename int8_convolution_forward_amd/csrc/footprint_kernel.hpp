@@ -334,7 +334,7 @@ __global__ __launch_bounds__(64 * WGM * WGN * KSPL) void conv_footprint3x3_kerne
     __syncthreads();
 
     if constexpr (KSPL == 1) {
-        store_tile<FM, FN, PIX_J>(a, acc, m0, n0, wm, wn, lane, out_row);
+        store_tile_any<FM, FN, PIX_J>(a, acc, m0, n0, wm, wn, lane, out_row);
     } else {
         // Wave (kg, wq) keeps column half kg of its tile and hands the other
         // to wave (1-kg, wq) through the (now idle) ring, lane-major, one
@@ -368,7 +368,7 @@ __global__ __launch_bounds__(64 * WGM * WGN * KSPL) void conv_footprint3x3_kerne
                     }
                 }
                 __syncthreads();
-                store_tile<1, FH, PIX_J>(a, fin, m0, n0, wm + x * 32, wn + KG * FH * 32, lane, out_row);
+                store_tile_any<1, FH, PIX_J>(a, fin, m0, n0, wm + x * 32, wn + KG * FH * 32, lane, out_row);
             }
         };
         if (kg == 0)

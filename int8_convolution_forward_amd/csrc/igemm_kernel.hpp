@@ -253,7 +253,7 @@ __global__ __launch_bounds__(64 * WGM * WGN) void conv_igemm_kernel(IgemmArgs a)
     __syncthreads();
 
     // ---- epilogue ---------------------------------------------------------
-    store_tile<FM, FN, PIX_J>(a, acc, m0, n0, wm, wn, lane, out_row);
+    store_tile_any<FM, FN, PIX_J>(a, acc, m0, n0, wm, wn, lane, out_row);
 }
 
 }  // namespace convi8

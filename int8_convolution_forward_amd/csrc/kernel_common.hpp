@@ -1,7 +1,7 @@
 // Shared pieces of the INT8 conv_fprop kernels for gfx950 (CDNA4): kernel
 // arguments, buffer-resource and direct-to-LDS load helpers, LDS swizzles,
 // division by launch-invariant divisors, the XCD-aware tile order and the
-// INT32 epilogue.
+// epilogues (INT32 sums, or requantised INT8).
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -33,7 +33,7 @@ __device__ __forceinline__ int udiv(int n, Divisor d)
 struct IgemmArgs {
     const int8_t *img;   // image, channel-innermost; (0,0,0,0) at img
     const int8_t *flt;   // filter K,R,S,C with C innermost
-    int32_t *out;        // output element (0,0,0,0)
+    int32_t *out;        // output element (0,0,0,0); int8_t when q8 is set
     int img_range;       // bytes addressable from img (buffer range)
     int flt_range;       // bytes addressable from flt
     int N, H, W, C;      // C: channels as stored (multiple of 16)
@@ -58,7 +58,37 @@ struct IgemmArgs {
     int Pr;              // footprint row pitch in LDS, 16-byte slots
     float inv_pr, inv_hp;
     int ncblk;           // channel blocks of 64
+    // requantising INT8 epilogue (q8 != 0)
+    const float *q_scale; // K per-channel scales, or null: q_alpha for every channel
+    const float *q_bias;  // K per-channel biases, or null: none
+    float q_alpha;
+    int q_relu;
+    int q8;
 };
+
+// Requantising INT8 epilogue of one exact sum: the sum as a float, one fused
+// multiply-add with the channel's scale and bias, ReLU if asked, round half to
+// even, saturate to [-128, 127].  With scale 1 it is the clamped INT8 store of
+// the naive loop in "Building a From-Scratch INT8 Strided Convolution Kernel"
+// (step 2); the ReLU and scale are the quantisation step its roadmap fuses.
+__device__ __forceinline__ int requant_i8(int acc, float s, float b, bool relu)
+{
+    float v = __builtin_fmaf((float)acc, s, b);
+    if (relu)
+        v = __builtin_fmaxf(v, 0.0f);
+    v = __builtin_rintf(v);
+    v = __builtin_fminf(__builtin_fmaxf(v, -128.0f), 127.0f);
+    return (int)v;
+}
+
+// Scale and bias of output channel kk (clamped into [0, K): lanes past K
+// compute a value that is never stored).
+__device__ __forceinline__ void requant_params(const IgemmArgs &a, int kk, float &s, float &b)
+{
+    const int k = kk < a.K ? kk : a.K - 1;
+    s = a.q_scale ? a.q_scale[k] : a.q_alpha;
+    b = a.q_bias ? a.q_bias[k] : 0.0f;
+}
 
 // s_waitcnt immediate (gfx9 encoding): wait until at most `vm` vector-memory
 // operations are outstanding and all LDS operations are done.
@@ -151,37 +181,62 @@ __device__ __forceinline__ void fill_out_rows(const IgemmArgs &a, int m0, int *o
     }
 }
 
-// INT32 epilogue.  32x32 accumulator layout: lane l, value v -> MFMA row
-// 8*(v/4) + 4*(l/32) + v%4, MFMA column l%32; rows come from the first MFMA
-// operand.  Elements past M or K get an out-of-range offset and the buffer
-// store drops them, so no branch guards a store.
-template <int FM, int FN, bool PIX_J>
+// Epilogue: INT32 sums, or (Q8) their requantised INT8 values.  32x32
+// accumulator layout: lane l, value v -> MFMA row 8*(v/4) + 4*(l/32) + v%4,
+// MFMA column l%32; rows come from the first MFMA operand.  Elements past M or
+// K get an out-of-range offset and the buffer store drops them, so no branch
+// guards a store.
+template <int FM, int FN, bool PIX_J, bool Q8 = false>
 __device__ __forceinline__ void store_tile(const IgemmArgs &a, v16i (&acc)[FM][FN], int m0, int n0,
                                            int wm, int wn, int lane, const int *out_row)
 {
     const __amdgpu_buffer_rsrc_t out_rsrc =
         __builtin_amdgcn_make_buffer_rsrc((void *)a.out, (short)0, a.out_range, kRsrcWord3);
+    constexpr int ES = Q8 ? 1 : 4;           // bytes per output element
+    const bool relu = a.q_relu != 0;
+    auto put = [&](int v, int off, float qs, float qb) {
+        if constexpr (Q8)
+            __builtin_amdgcn_raw_buffer_store_b8((unsigned char)requant_i8(v, qs, qb, relu), out_rsrc,
+                                                 off, 0, 0);
+        else
+            __builtin_amdgcn_raw_buffer_store_b32(v, out_rsrc, off, 0, 0);
+    };
     const int mcol = lane & 31;
     const int mrow0 = 4 * (lane >> 5);
     if constexpr (PIX_J) {
         // lanes walk pixels: one pixel per (lane, x), channels along v
+        int pix_off[FM];
+        bool pix_ok[FM];
 #pragma unroll
         for (int x = 0; x < FM; ++x) {
             const int m = m0 + wm + x * 32 + mcol;
-            const bool pix_ok = m < a.M;
+            pix_ok[x] = m < a.M;
             const int n = udiv(m, a.d_pq);
             const int rem = m - n * a.PQ;
             const int p = udiv(rem, a.d_q);
             const int q = rem - p * a.Q;
-            const int pix_off = n * a.oN + p * a.oP + q * a.oQ;
+            pix_off[x] = n * a.oN + p * a.oP + q * a.oQ;
+        }
 #pragma unroll
-            for (int y = 0; y < FN; ++y) {
-                const int kb = n0 + wn + y * 32 + mrow0;
+        for (int y = 0; y < FN; ++y) {
+            const int kb = n0 + wn + y * 32 + mrow0;
+            // the 16 channels of this lane in column block y, and (Q8) their
+            // scale and bias, shared by every row block x
+            float qs[16], qb[16];
+#pragma unroll
+            for (int v = 0; v < 16; ++v) {
+                qs[v] = 0.0f;
+                qb[v] = 0.0f;
+                if constexpr (Q8)
+                    requant_params(a, kb + 8 * (v >> 2) + (v & 3), qs[v], qb[v]);
+            }
+#pragma unroll
+            for (int x = 0; x < FM; ++x) {
 #pragma unroll
                 for (int v = 0; v < 16; ++v) {
                     const int kk = kb + 8 * (v >> 2) + (v & 3);
-                    const int off = (pix_ok && kk < a.K) ? (pix_off + kk * a.oK) * 4 : kOutOfRange;
-                    __builtin_amdgcn_raw_buffer_store_b32(acc[x][y][v], out_rsrc, off, 0, 0);
+                    const int off = (pix_ok[x] && kk < a.K) ? (pix_off[x] + kk * a.oK) * ES : kOutOfRange;
+                    put(acc[x][y][v], off, qs[v], qb[v]);
                 }
             }
         }
@@ -192,14 +247,17 @@ __device__ __forceinline__ void store_tile(const IgemmArgs &a, v16i (&acc)[FM][F
             const int kk = n0 + wn + y * 32 + mcol;
             const bool k_ok = kk < a.K;
             const int koff = kk * a.oK;
+            float qs = 0.0f, qb = 0.0f;
+            if constexpr (Q8)
+                requant_params(a, kk, qs, qb);
 #pragma unroll
             for (int x = 0; x < FM; ++x) {
                 const int mb = m0 + wm + x * 32 + mrow0;
 #pragma unroll
                 for (int v = 0; v < 16; ++v) {
                     const int m = mb + 8 * (v >> 2) + (v & 3);
-                    const int off = (k_ok && m < a.M) ? (m * a.pix_stride + koff) * 4 : kOutOfRange;
-                    __builtin_amdgcn_raw_buffer_store_b32(acc[x][y][v], out_rsrc, off, 0, 0);
+                    const int off = (k_ok && m < a.M) ? (m * a.pix_stride + koff) * ES : kOutOfRange;
+                    put(acc[x][y][v], off, qs, qb);
                 }
             }
         }
@@ -210,17 +268,31 @@ __device__ __forceinline__ void store_tile(const IgemmArgs &a, v16i (&acc)[FM][F
             const int kk = n0 + wn + y * 32 + mcol;
             const bool k_ok = kk < a.K;
             const int koff = kk * a.oK;
+            float qs = 0.0f, qb = 0.0f;
+            if constexpr (Q8)
+                requant_params(a, kk, qs, qb);
 #pragma unroll
             for (int x = 0; x < FM; ++x) {
 #pragma unroll
                 for (int v = 0; v < 16; ++v) {
                     const int po = out_row[wm + x * 32 + mrow0 + 8 * (v >> 2) + (v & 3)];
-                    const int off = (k_ok && po >= 0) ? (po + koff) * 4 : kOutOfRange;
-                    __builtin_amdgcn_raw_buffer_store_b32(acc[x][y][v], out_rsrc, off, 0, 0);
+                    const int off = (k_ok && po >= 0) ? (po + koff) * ES : kOutOfRange;
+                    put(acc[x][y][v], off, qs, qb);
                 }
             }
         }
     }
+}
+
+// store_tile with the epilogue the arguments ask for.
+template <int FM, int FN, bool PIX_J>
+__device__ __forceinline__ void store_tile_any(const IgemmArgs &a, v16i (&acc)[FM][FN], int m0, int n0,
+                                               int wm, int wn, int lane, const int *out_row)
+{
+    if (a.q8)
+        store_tile<FM, FN, PIX_J, true>(a, acc, m0, n0, wm, wn, lane, out_row);
+    else
+        store_tile<FM, FN, PIX_J, false>(a, acc, m0, n0, wm, wn, lane, out_row);
 }
 
 }  // namespace convi8

@@ -12,9 +12,9 @@
 // once into registers (the B operand of v_mfma_i32_32x32x32_i8: lane l holds
 // output channel y*32 + l%32, channels ks*32 + (l/32)*16 .. +16), issues the
 // 16-byte image loads of all its tiles up front (lane l: pixel l%32 of the
-// tile, the same channel split), then multiplies and stores tile by tile, so
-// the stores of the first tiles overlap the loads of the last.  No LDS and no
-// barrier.  Pixels outside the image (padding, stride) and channels past C
+// tile, the same channel split), then multiplies and stores tile by tile
+// (INT32 sums, or their requantised INT8 values), so the stores of the first
+// tiles overlap the loads of the last.  No LDS and no barrier.  Pixels outside the image (padding, stride) and channels past C
 // load out of range, i.e. zeros.
 #pragma once
 
@@ -75,6 +75,15 @@ __global__ __launch_bounds__(256) void conv_pointwise_kernel(IgemmArgs a)
     const __amdgpu_buffer_rsrc_t out_rsrc =
         __builtin_amdgcn_make_buffer_rsrc((void *)a.out, (short)0, a.out_range, kRsrcWord3);
     const int mrow0 = 4 * (lane >> 5);
+    const bool q8 = a.q8 != 0, relu = a.q_relu != 0;
+    float qs[FN], qb[FN];                         // requantising epilogue, per column block
+#pragma unroll
+    for (int y = 0; y < FN; ++y) {
+        qs[y] = 0.0f;
+        qb[y] = 0.0f;
+        if (q8)
+            requant_params(a, y * 32 + (lane & 31), qs[y], qb[y]);
+    }
 #pragma unroll
     for (int t = 0; t < TPW; ++t) {
         v16i acc[FN];
@@ -94,11 +103,21 @@ __global__ __launch_bounds__(256) void conv_pointwise_kernel(IgemmArgs a)
         for (int y = 0; y < FN; ++y) {
             const int kk = y * 32 + (lane & 31);
             const bool k_ok = kk < a.K;
+            if (q8) {
 #pragma unroll
-            for (int v = 0; v < 16; ++v) {
-                const int m = mb + 8 * (v >> 2) + (v & 3);
-                const int off = (k_ok && m < a.M) ? (m * a.pix_stride + kk * a.oK) * 4 : kOutOfRange;
-                __builtin_amdgcn_raw_buffer_store_b32(acc[y][v], out_rsrc, off, 0, 0);
+                for (int v = 0; v < 16; ++v) {
+                    const int m = mb + 8 * (v >> 2) + (v & 3);
+                    const int off = (k_ok && m < a.M) ? m * a.pix_stride + kk * a.oK : kOutOfRange;
+                    __builtin_amdgcn_raw_buffer_store_b8(
+                        (unsigned char)requant_i8(acc[y][v], qs[y], qb[y], relu), out_rsrc, off, 0, 0);
+                }
+            } else {
+#pragma unroll
+                for (int v = 0; v < 16; ++v) {
+                    const int m = mb + 8 * (v >> 2) + (v & 3);
+                    const int off = (k_ok && m < a.M) ? (m * a.pix_stride + kk * a.oK) * 4 : kOutOfRange;
+                    __builtin_amdgcn_raw_buffer_store_b32(acc[y][v], out_rsrc, off, 0, 0);
+                }
             }
         }
     }

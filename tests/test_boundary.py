@@ -231,3 +231,47 @@ def test_plan_cache_keys():
     assert ci8.lib.conv_fprop_i8_plan(ctypes.byref(dx2), ctypes.c_void_p(4096), ctypes.byref(dw),
                                       ctypes.c_void_p(8192), ctypes.byref(dy2), pre, post, st, dl, buf, 512) == 0
     assert ci8.plan_fields(buf.value.decode())["batch_chunk"] == "63"
+
+
+def _call_rq(a, rq, ws_bytes=0, ws=None, xp=FAKE, wp=FAKE, yp=FAKE):
+    p = ci8._params(a["pre"], a["post"], a["stride"], a["dil"], None)
+    return ci8.lib.conv_fprop_i8_requant_ws(
+        ctypes.byref(a["x"]), xp, ctypes.byref(a["w"]), wp, ctypes.byref(a["y"]), yp, *p,
+        ctypes.byref(rq) if rq is not None else None, ws, ctypes.c_size_t(ws_bytes), None)
+
+
+def test_requant_argument_errors():
+    """The requantising entry wants an INT8 output and a sane parameter block,
+    and checks both on the host before any device work."""
+    c = wl.case("bottleneck_3x3_n32_c128_28")
+    a8 = _args(c, y=ci8.desc(c.out.dims, c.out.strides, ci8.DT_INT8))
+    ok = ci8.Requant(None, 1.0, None, 0)
+    assert _call_rq(_args(c), ok) == 2                                   # INT32 output: DTYPE
+    assert _call_rq(a8, None) == 1                                       # no block: NULL
+    assert _call_rq(a8, ci8.Requant(0x1000002, 1.0, None, 0)) == 5      # misaligned scale
+    assert _call_rq(a8, ci8.Requant(None, 1.0, 0x1000001, 0)) == 5      # misaligned bias
+    assert _call_rq(a8, ci8.Requant(None, float("nan"), None, 0)) == 5  # alpha must be finite
+    assert _call_rq(a8, ci8.Requant(None, float("inf"), None, 1)) == 5
+    # with a scale array alpha is unused
+    bad_alpha = ci8.Requant(0x1000000, float("nan"), None, 0)
+    assert _call_rq(a8, bad_alpha, yp=None) == 1                         # passes the block check
+    need = ci8.conv_fprop_i8_requant_workspace_size(a8["x"], a8["w"], a8["y"], c.pre, c.post,
+                                                    c.stride, c.dilation)
+    assert need == ci8.conv_fprop_i8_workspace_size(_args(c)["x"], _args(c)["w"], _args(c)["y"],
+                                                    c.pre, c.post, c.stride, c.dilation)
+    with pytest.raises(ci8.ConvI8Error) as e:
+        ci8.conv_fprop_i8_requant_workspace_size(a8["x"], a8["w"], _args(c)["y"], c.pre, c.post,
+                                                 c.stride, c.dilation)
+    assert e.value.name == "CONV_I8_ERR_DTYPE"
+
+
+def test_requant_workspace_matches_plain():
+    """Repacks do not depend on the output dtype."""
+    c = wl.case("dilated_asym_n16_c96_64x48")
+    a = _args(c)
+    a8 = _args(c, y=ci8.desc(c.out.dims, c.out.strides, ci8.DT_INT8))
+    n32 = ci8.conv_fprop_i8_workspace_size(a["x"], a["w"], a["y"], c.pre, c.post, c.stride, c.dilation)
+    n8 = ci8.conv_fprop_i8_requant_workspace_size(a8["x"], a8["w"], a8["y"], c.pre, c.post,
+                                                  c.stride, c.dilation)
+    assert n8 == n32 > 0
+    assert _call_rq(a8, ci8.Requant(None, 1.0, None, 0), ws_bytes=n8 - 1, ws=FAKE) == 10
