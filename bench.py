@@ -2,7 +2,9 @@
 
 One step = one conv_fprop_i8 call (the whole path: layout normalisation if
 the operands need it, implicit-GEMM kernel with its epilogue) over one batch
-of seeded synthetic input that is already resident in HBM.  Inputs and
+of seeded synthetic input that is already resident in HBM.  With
+``--epilogue requant`` a step is one conv_fprop_i8_requant call instead (INT8
+output through the fused scale / bias / ReLU / saturation epilogue).  Inputs and
 outputs rotate over enough buffer sets (> 512 MB) that the 256 MB Infinity
 Cache cannot serve a step from a previous one.
 
@@ -36,6 +38,9 @@ def parse():
     ap.add_argument("--warmup", type=int, default=1000,
                     help="untimed steps first; the GPU needs some tens of ms of load to settle its clock")
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
+    ap.add_argument("--epilogue", choices=("int32", "requant"), default="int32",
+                    help="int32: the plain entry; requant: INT8 output with per-channel "
+                         "scale and bias and ReLU")
     ap.add_argument("--rotate-mb", type=float, default=600.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
@@ -79,6 +84,8 @@ def main():
     import workloads as wl
 
     c = wl.case(args.workload)
+    rq_on = args.epilogue == "requant"
+    esize = 1 if rq_on else 4
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     d = wl.make_inputs(c, c.seed_base)
@@ -89,21 +96,30 @@ def main():
     # ---- resident, rotating buffer sets --------------------------------
     x0_storage, _ = wl.to_device(d["x_storage"], c.image, dev)
     w0_storage, _ = wl.to_device(d["w_storage"], c.filter, dev)
-    set_bytes = (x0_storage.numel() + w0_storage.numel() + 4 * c.out.storage_size)
+    set_bytes = (x0_storage.numel() + w0_storage.numel() + esize * c.out.storage_size)
     nsets = max(2, min(128, int(args.rotate_mb * 2**20 // set_bytes) + 1))
     sets = []
     for i in range(nsets):
         xs = x0_storage.clone()
         ws_ = w0_storage.clone()
-        ys = torch.empty(c.out.storage_size, dtype=torch.int32, device=dev)
+        ys = torch.empty(c.out.storage_size, dtype=torch.int8 if rq_on else torch.int32, device=dev)
         x = torch.as_strided(xs, c.image.dims, c.image.strides, c.image.offset)
         w = torch.as_strided(ws_, c.filter.dims, c.filter.strides, c.filter.offset)
         y = torch.as_strided(ys, c.out.dims, c.out.strides, c.out.offset)
         sets.append((xs, ws_, ys, x, w, y))
-    ws_bytes = ci8.conv_fprop_i8_workspace_size(sets[0][3], sets[0][4], sets[0][5], c.pre, c.post,
-                                                c.stride, c.dilation)
+    # requantisation parameters: per-channel scales that keep typical sums of
+    # random operands around +-64, biases, ReLU (all on the device)
+    g = torch.Generator().manual_seed(c.seed_base + 77)
+    typical = (C * R * S) ** 0.5 * 128 * 128 / 3
+    q_scale = ((torch.rand(K, generator=g) + 0.5) * 64 / typical).to(dev)
+    q_bias = ((torch.rand(K, generator=g) - 0.5) * 40).to(dev)
+    rq = ci8.Requant(q_scale.data_ptr(), 1.0, q_bias.data_ptr(), 1)
+    # the plan depends on the output strides, not on its dtype
+    out32 = ci8.desc(c.out.dims, c.out.strides, ci8.DT_INT32)
+    wsize = ci8.conv_fprop_i8_requant_workspace_size if rq_on else ci8.conv_fprop_i8_workspace_size
+    ws_bytes = wsize(sets[0][3], sets[0][4], sets[0][5], c.pre, c.post, c.stride, c.dilation)
     workspace = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
-    plan = ci8.conv_fprop_i8_plan(sets[0][3], sets[0][4], sets[0][5], c.pre, c.post, c.stride,
+    plan = ci8.conv_fprop_i8_plan(sets[0][3], sets[0][4], out32, c.pre, c.post, c.stride,
                                   c.dilation)
 
     stream = torch.cuda.current_stream()
@@ -111,14 +127,15 @@ def main():
     params = ci8._params(c.pre, c.post, c.stride, c.dilation, None)
 
     def prebuilt(x, w, y):
+        extra = (ctypes.byref(rq),) if rq_on else ()
         return (ctypes.byref(ci8.desc(x)), ctypes.c_void_p(x.data_ptr()),
                 ctypes.byref(ci8.desc(w)), ctypes.c_void_p(w.data_ptr()),
-                ctypes.byref(ci8.desc(y)), ctypes.c_void_p(y.data_ptr()), *params,
+                ctypes.byref(ci8.desc(y)), ctypes.c_void_p(y.data_ptr()), *params, *extra,
                 ctypes.c_void_p(workspace.data_ptr()) if ws_bytes else None,
                 ctypes.c_size_t(ws_bytes), sh)
 
     calls = [prebuilt(s[3], s[4], s[5]) for s in sets]
-    fn = ci8.lib.conv_fprop_i8_ws
+    fn = ci8.lib.conv_fprop_i8_requant_ws if rq_on else ci8.lib.conv_fprop_i8_ws
 
     def step(i):
         rc = fn(*calls[i % nsets])
@@ -151,15 +168,16 @@ def main():
     kcalls = []
     for s in sets:
         x, w, y = s[3], s[4], s[5]
-        f = ci8.plan_fields(ci8.conv_fprop_i8_plan(x, w, y, c.pre, c.post, c.stride, c.dilation))
+        f = ci8.plan_fields(ci8.conv_fprop_i8_plan(x, w, out32, c.pre, c.post, c.stride, c.dilation))
         if f["repack_image"] == "1":
             x = x.contiguous(memory_format=torch.channels_last)
         if f["repack_filter"] == "1":
             w = w.contiguous(memory_format=torch.channels_last)
         kcalls.append((x, w, y))
-    kf = ci8.plan_fields(ci8.conv_fprop_i8_plan(*kcalls[0], c.pre, c.post, c.stride, c.dilation))
+    kf = ci8.plan_fields(ci8.conv_fprop_i8_plan(kcalls[0][0], kcalls[0][1], out32, c.pre, c.post,
+                                                c.stride, c.dilation))
     kernel_only = kf["repack_image"] == "0" and kf["repack_filter"] == "0" and \
-        ci8.conv_fprop_i8_workspace_size(*kcalls[0], c.pre, c.post, c.stride, c.dilation) == 0
+        wsize(*kcalls[0], c.pre, c.post, c.stride, c.dilation) == 0
     kpre = [prebuilt(*t) for t in kcalls]
     nk = max(args.steps, 50)
     for i in range(min(10, nk)):
@@ -176,8 +194,11 @@ def main():
     torch.cuda.synchronize()
     k_avg_ms = k_start.elapsed_time(k_end) / nk
 
-    # algorithmic bytes: image, filter read once, int32 output written once
-    alg_bytes = N * C * c.image.dims[2] * c.image.dims[3] + K * C * R * S + 4 * N * K * P * Q
+    # algorithmic bytes: image, filter read once, output written once (int32,
+    # or int8 plus the per-channel scale and bias)
+    alg_bytes = N * C * c.image.dims[2] * c.image.dims[3] + K * C * R * S + esize * N * K * P * Q
+    if rq_on:
+        alg_bytes += 8 * K
     ai = ops / alg_bytes
     ridge = INT8_PEAK_TOPS * 1e12 / (HBM_PEAK_GBS * 1e9)
     if ai >= ridge:
@@ -187,7 +208,7 @@ def main():
         roof = {"bound": "hbm", "achieved": alg_bytes / (k_avg_ms * 1e-3) / 1e9, "peak": HBM_PEAK_GBS,
                 "unit": "GB/s"}
     roof["frac"] = roof["achieved"] / roof["peak"]
-    roof["traffic"] = traffic_from_profiles(c.name, alg_bytes)
+    roof["traffic"] = traffic_from_profiles(c.name + ("_requant" if rq_on else ""), alg_bytes)
     roof["kernel"] = "conv_footprint3x3_kernel" if kf.get("kernel") == "footprint" else "conv_igemm_kernel"
     roof["kernel_tile"] = kf.get("tile")
     roof["kernel_avg_us"] = k_avg_ms * 1e3
@@ -204,8 +225,13 @@ def main():
         threads = orc.max_threads()
         t0 = time.perf_counter()
         reps = 0
+        sc_cpu, bi_cpu = q_scale.cpu().numpy(), q_bias.cpu().numpy()
         while True:
-            orc.conv_fprop(d["x"], d["w"], c.pre, c.post, c.stride, c.dilation, threads=threads)
+            if rq_on:
+                orc.conv_fprop_requant(d["x"], d["w"], c.pre, c.post, c.stride, c.dilation,
+                                       scale=sc_cpu, bias=bi_cpu, relu=True, threads=threads)
+            else:
+                orc.conv_fprop(d["x"], d["w"], c.pre, c.post, c.stride, c.dilation, threads=threads)
             reps += 1
             el = time.perf_counter() - t0
             if el >= args.cpu_seconds or reps >= 20:
@@ -232,7 +258,10 @@ def main():
                    "out": list(c.out.dims), "out_strides": list(c.out.strides),
                    "pre_padding": list(c.pre), "post_padding": list(c.post),
                    "stride": list(c.stride), "dilation": list(c.dilation),
-                   "accumulate": "int32", "output": "int32", "plan": plan,
+                   "accumulate": "int32",
+                   "output": ("int8: fma(sum, per-channel scale, bias), ReLU, round half to "
+                              "even, saturate") if rq_on else "int32",
+                   "plan": plan,
                    "buffer_sets": nsets},
         "frac_of_int8_peak": tops / INT8_PEAK_TOPS,
         "roofline": roof,

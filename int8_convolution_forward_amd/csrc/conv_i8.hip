@@ -745,6 +745,10 @@ conv_i8_status_t run(const Problem &pb, const Plan &pl, const void *x_ptr, const
         a.q_bias = rq->bias;
         a.q_alpha = rq->alpha;
         a.q_relu = rq->relu ? 1 : 0;
+        // dword stores of four channels: channel stride 1, equally spaced
+        // pixels, and every dword 4-byte aligned and inside one pixel's K
+        a.q8_pack = pl.pix_linear && !pl.pix_j && pb.y.s[1] == 1 && pl.pix_stride % 4 == 0 &&
+                    pb.K % 4 == 0 && ((uintptr_t)y_ptr & 3u) == 0 ? 1 : 0;
     }
     for (int64_t n0 = 0; n0 < pb.N; n0 += pl.batch_chunk) {
         const int64_t nb = std::min(pl.batch_chunk, pb.N - n0);

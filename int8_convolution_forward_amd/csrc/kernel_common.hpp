@@ -64,6 +64,8 @@ struct IgemmArgs {
     float q_alpha;
     int q_relu;
     int q8;
+    int q8_pack;          // channel stride 1, K, pix_stride and out 4-byte multiples:
+                          // four channels of a pixel go out as one dword
 };
 
 // Requantising INT8 epilogue of one exact sum: the sum as a float, one fused
@@ -79,6 +81,18 @@ __device__ __forceinline__ int requant_i8(int acc, float s, float b, bool relu)
     v = __builtin_rintf(v);
     v = __builtin_fminf(__builtin_fmaxf(v, -128.0f), 127.0f);
     return (int)v;
+}
+
+// 4x4 byte transpose within each quad of lanes: byte u of lane t's result is
+// byte t of lane u's input (two DPP lane swaps, t^1 then t^2, each followed
+// by a byte or half-word merge).
+__device__ __forceinline__ unsigned quad_transpose_bytes(unsigned x, int lane)
+{
+    const unsigned p = (unsigned)__builtin_amdgcn_update_dpp(0, (int)x, 0xB1, 0xF, 0xF, false);
+    const unsigned y = (lane & 1) ? (((p & 0xFF00FF00u) >> 8) | (x & 0xFF00FF00u))
+                                  : ((x & 0x00FF00FFu) | ((p & 0x00FF00FFu) << 8));
+    const unsigned q = (unsigned)__builtin_amdgcn_update_dpp(0, (int)y, 0x4E, 0xF, 0xF, false);
+    return (lane & 2) ? ((q >> 16) | (y & 0xFFFF0000u)) : ((y & 0x0000FFFFu) | (q << 16));
 }
 
 // Scale and bias of output channel kk (clamped into [0, K): lanes past K
@@ -237,6 +251,33 @@ __device__ __forceinline__ void store_tile(const IgemmArgs &a, v16i (&acc)[FM][F
                     const int kk = kb + 8 * (v >> 2) + (v & 3);
                     const int off = (pix_ok[x] && kk < a.K) ? (pix_off[x] + kk * a.oK) * ES : kOutOfRange;
                     put(acc[x][y][v], off, qs[v], qb[v]);
+                }
+            }
+        }
+    } else if (Q8 && a.pix_linear && a.q8_pack) {
+        // lanes walk channels, pixel m at m * pix_stride, channel stride 1:
+        // a lane's four consecutive rows become one dword, a quad of lanes
+        // transposes them, and lane 4j+t stores channels 4j..4j+3 of row t
+#pragma unroll
+        for (int y = 0; y < FN; ++y) {
+            const int kk = n0 + wn + y * 32 + mcol;
+            const int kq = kk & ~3;
+            const bool k_ok = kq < a.K;
+            float qs, qb;
+            requant_params(a, kk, qs, qb);
+#pragma unroll
+            for (int x = 0; x < FM; ++x) {
+                const int mb = m0 + wm + x * 32 + mrow0;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    unsigned wv = 0;
+#pragma unroll
+                    for (int u = 0; u < 4; ++u)
+                        wv |= ((unsigned)requant_i8(acc[x][y][4 * i + u], qs, qb, relu) & 0xFFu) << (8 * u);
+                    wv = quad_transpose_bytes(wv, lane);
+                    const int m = mb + 8 * i + (lane & 3);
+                    const int off = (k_ok && m < a.M) ? m * a.pix_stride + kq : kOutOfRange;
+                    __builtin_amdgcn_raw_buffer_store_b32((int)wv, out_rsrc, off, 0, 0);
                 }
             }
         }

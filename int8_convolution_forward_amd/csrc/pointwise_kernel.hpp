@@ -103,7 +103,22 @@ __global__ __launch_bounds__(256) void conv_pointwise_kernel(IgemmArgs a)
         for (int y = 0; y < FN; ++y) {
             const int kk = y * 32 + (lane & 31);
             const bool k_ok = kk < a.K;
-            if (q8) {
+            if (q8 && a.q8_pack) {
+                // four rows of a lane -> one dword; a quad transposes them so
+                // that lane 4j+t stores channels 4j..4j+3 of row t
+                const int kq = kk & ~3;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    unsigned wv = 0;
+#pragma unroll
+                    for (int u = 0; u < 4; ++u)
+                        wv |= ((unsigned)requant_i8(acc[y][4 * i + u], qs[y], qb[y], relu) & 0xFFu) << (8 * u);
+                    wv = quad_transpose_bytes(wv, lane);
+                    const int m = mb + 8 * i + (lane & 3);
+                    const int off = (kq < a.K && m < a.M) ? m * a.pix_stride + kq : kOutOfRange;
+                    __builtin_amdgcn_raw_buffer_store_b32((int)wv, out_rsrc, off, 0, 0);
+                }
+            } else if (q8) {
 #pragma unroll
                 for (int v = 0; v < 16; ++v) {
                     const int m = mb + 8 * (v >> 2) + (v & 3);

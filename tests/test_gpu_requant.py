@@ -129,17 +129,23 @@ def test_unit_scale_is_the_saturating_store(ci8):
 # Every tile shape on a ragged problem, channel- and pixel-innermost outputs.
 # ---------------------------------------------------------------------------
 @pytest.mark.parametrize("tile", TILES)
-@pytest.mark.parametrize("C,out_layout", [(128, "nhwc"), (64, "nchw"), (48, "gapped")])
-def test_tile_shapes_requant(ci8, monkeypatch, tile, C, out_layout):
+@pytest.mark.parametrize("C,K,out_layout", [(128, 200, "nhwc"), (64, 200, "nchw"), (48, 200, "gapped"),
+                                            (64, 202, "nhwc"), (128, 200, "nhwc_off1")])
+def test_tile_shapes_requant(ci8, monkeypatch, tile, C, K, out_layout):
+    """nhwc with K % 4 == 0 takes the dword-packed stores; K = 202 and an
+    output that starts at an odd byte take the byte stores."""
     if tile in FOOTPRINT_TILES and C % 64:
         pytest.skip("the footprint kernel takes whole 64-channel blocks")
     monkeypatch.setenv("CONV_I8_TILE", tile)
-    N, H, W, K = 3, 17, 13, 200
+    N, H, W = 3, 17, 13
     pre, post, st, dl = (2, 1), (0, 1), (2, 1), (1, 1)
     xs = wl.TensorSpec((N, C, H, W), wl.channels_last_strides((N, C, H, W)))
     ws = wl.TensorSpec((K, C, 3, 3), wl.channels_last_strides((K, C, 3, 3)))
     od = oracle.out_dims(xs.dims, ws.dims, pre, post, st, dl)
-    os_ = _out_layout(np.random.default_rng(0), od, out_layout)
+    if out_layout == "nhwc_off1":
+        os_ = wl.TensorSpec(od, wl.channels_last_strides(od), offset=1)
+    else:
+        os_ = _out_layout(np.random.default_rng(0), od, out_layout)
     f = ci8.plan_fields(ci8.conv_fprop_i8_plan(ci8.desc(xs.dims, xs.strides, 1),
                                                ci8.desc(ws.dims, ws.strides, 1),
                                                ci8.desc(os_.dims, os_.strides, 2), pre, post, st, dl))
@@ -150,7 +156,8 @@ def test_tile_shapes_requant(ci8, monkeypatch, tile, C, out_layout):
     wv = torch.randint(-128, 128, ws.dims, dtype=torch.int8, generator=g)
     sc, bi = channel_params(K, C * 9, seed=C)
     run_requant_check(ci8, _fill(xs, xv, 5), xs, _fill(ws, wv, 6), ws, os_, pre, post, st, dl,
-                      scale=sc, bias=bi, relu=(C == 64), label=f"tile {tile} C={C} {out_layout}")
+                      scale=sc, bias=bi, relu=(C == 64),
+                      label=f"tile {tile} C={C} K={K} {out_layout}")
 
 
 @pytest.mark.parametrize("case_i", range(len(POINTWISE_CASES)))
