@@ -38,6 +38,9 @@ def parse():
     ap.add_argument("--warmup", type=int, default=1000,
                     help="untimed steps first; the GPU needs some tens of ms of load to settle its clock")
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
+    ap.add_argument("--graph", action="store_true",
+                    help="record the timed steps into one HIP graph (captured through the "
+                         "workspace entry) and time its replay")
     ap.add_argument("--epilogue", choices=("int32", "requant"), default="int32",
                     help="int32: the plain entry; requant: INT8 output with per-channel "
                          "scale and bias and ReLU")
@@ -151,10 +154,25 @@ def main():
     # ---- timed region: exactly `steps` steps ---------------------------
     t_start = torch.cuda.Event(enable_timing=True)
     t_end = torch.cuda.Event(enable_timing=True)
+    if args.graph:
+        # the same calls, recorded on the capture stream, replayed as one graph
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            cap = torch.cuda.current_stream()
+            gcalls = [c_[:-1] + (ctypes.c_void_p(cap.cuda_stream),) for c_ in calls]
+            for i in range(args.steps):
+                rc = fn(*gcalls[i % nsets])
+                if rc != 0:
+                    raise RuntimeError(ci8.status_string(rc))
+        graph.replay()
+        torch.cuda.synchronize()
     torch.cuda.synchronize()
     t_start.record(stream)
-    for i in range(args.steps):
-        step(i)
+    if args.graph:
+        graph.replay()
+    else:
+        for i in range(args.steps):
+            step(i)
     t_end.record(stream)
     torch.cuda.synchronize()
     ms_per_step = t_start.elapsed_time(t_end) / args.steps
@@ -261,7 +279,7 @@ def main():
                    "accumulate": "int32",
                    "output": ("int8: fma(sum, per-channel scale, bias), ReLU, round half to "
                               "even, saturate") if rq_on else "int32",
-                   "plan": plan,
+                   "plan": plan, "launch": "hip graph replay" if args.graph else "eager",
                    "buffer_sets": nsets},
         "frac_of_int8_peak": tops / INT8_PEAK_TOPS,
         "roofline": roof,
