@@ -67,12 +67,12 @@ class Oracle:
         P = ctypes.c_void_p
         lib.oracle_out_dims.argtypes = [P] * 7
         lib.oracle_out_dims.restype = ctypes.c_int
-        lib.oracle_conv_fprop.argtypes = [P] * 13 + [ctypes.c_int]
+        lib.oracle_conv_fprop.argtypes = [P] * 13 + [ctypes.c_int, ctypes.c_int]
         lib.oracle_conv_fprop.restype = ctypes.c_int
-        lib.oracle_conv_fprop_points.argtypes = [P] * 10 + [P, ctypes.c_int64, P]
+        lib.oracle_conv_fprop_points.argtypes = [P] * 10 + [ctypes.c_int, P, ctypes.c_int64, P]
         lib.oracle_conv_fprop_points.restype = ctypes.c_int
         lib.oracle_conv_fprop_requant.argtypes = [P] * 13 + [P, ctypes.c_float, P, ctypes.c_int,
-                                                             ctypes.c_int]
+                                                             ctypes.c_int, ctypes.c_int]
         lib.oracle_conv_fprop_requant.restype = ctypes.c_int
         lib.oracle_requant_values.argtypes = [P, P, ctypes.c_int64, P, ctypes.c_float, P,
                                               ctypes.c_int, P]
@@ -94,8 +94,9 @@ class Oracle:
 
     def conv_fprop(self, x: torch.Tensor, w: torch.Tensor, pre=0, post=0, stride=1, dil=1,
                    out: Optional[torch.Tensor] = None, threads: int = 0,
-                   allow_overflow: bool = False) -> torch.Tensor:
+                   allow_overflow: bool = False, mode: int = 0) -> torch.Tensor:
         """Y = conv(x, w) as int32.  x, w: int8 CPU tensors with any strides.
+        ``mode`` 0 is cross-correlation, 1 true convolution (flipped taps).
 
         ``out`` (int32, CPU, any non-overlapping strides) receives the result
         if given; otherwise a contiguous N,K,P,Q tensor is returned.
@@ -112,13 +113,13 @@ class Oracle:
             ctypes.c_void_p(x.data_ptr()), _v4(x.shape), _v4(x.stride()),
             ctypes.c_void_p(w.data_ptr()), _v4(w.shape), _v4(w.stride()),
             ctypes.c_void_p(out.data_ptr()), _v4(out.shape), _v4(out.stride()),
-            _v2(pre), _v2(post), _v2(stride), _v2(dil), int(threads))
+            _v2(pre), _v2(post), _v2(stride), _v2(dil), int(mode), int(threads))
         if rc and not (rc == 4 and allow_overflow):
             raise OracleError(rc)
         return out
 
     def conv_fprop_points(self, x: torch.Tensor, w: torch.Tensor, idx, pre=0, post=0,
-                          stride=1, dil=1) -> np.ndarray:
+                          stride=1, dil=1, mode: int = 0) -> np.ndarray:
         """Exact int64 sums at the (n, k, p, q) rows of ``idx``."""
         _check_cpu(x, torch.int8, "x")
         _check_cpu(w, torch.int8, "w")
@@ -127,7 +128,7 @@ class Oracle:
         rc = self.lib.oracle_conv_fprop_points(
             ctypes.c_void_p(x.data_ptr()), _v4(x.shape), _v4(x.stride()),
             ctypes.c_void_p(w.data_ptr()), _v4(w.shape), _v4(w.stride()),
-            _v2(pre), _v2(post), _v2(stride), _v2(dil),
+            _v2(pre), _v2(post), _v2(stride), _v2(dil), int(mode),
             idx.ctypes.data_as(ctypes.c_void_p), ctypes.c_int64(idx.shape[0]),
             res.ctypes.data_as(ctypes.c_void_p))
         if rc:
@@ -137,7 +138,8 @@ class Oracle:
 
     def conv_fprop_requant(self, x: torch.Tensor, w: torch.Tensor, pre=0, post=0, stride=1,
                            dil=1, scale=None, alpha: float = 1.0, bias=None, relu: bool = False,
-                           out: Optional[torch.Tensor] = None, threads: int = 0) -> torch.Tensor:
+                           out: Optional[torch.Tensor] = None, threads: int = 0,
+                           mode: int = 0) -> torch.Tensor:
         """int8 Y = saturate(rint(relu?(fma(float(conv(x, w)), s_k, b_k)))).
 
         ``scale`` and ``bias`` are K floats (anything np.float32 accepts) or
@@ -159,7 +161,7 @@ class Oracle:
             ctypes.c_void_p(w.data_ptr()), _v4(w.shape), _v4(w.stride()),
             ctypes.c_void_p(out.data_ptr()), _v4(out.shape), _v4(out.stride()),
             _v2(pre), _v2(post), _v2(stride), _v2(dil),
-            _ptr(sc), ctypes.c_float(alpha), _ptr(bi), int(bool(relu)), int(threads))
+            _ptr(sc), ctypes.c_float(alpha), _ptr(bi), int(bool(relu)), int(mode), int(threads))
         if rc:
             raise OracleError(rc)
         return out

@@ -20,6 +20,10 @@
  *     naive loop of "Building a From-Scratch INT8 Strided Convolution Kernel",
  *     "Step 2: Implement the Naive Strided Loop", reads input[ih+kh] against
  *     kernel[kh], and the forum page takes torch's conv2d as the truth;
+ *     the cuDNN page's convolution_mode parameter (listed, never defined)
+ *     is read as the usual pair: cross-correlation (mode 0, the default) or
+ *     true convolution (mode 1), which reads filter tap (R-1-r, S-1-s) where
+ *     cross-correlation reads (r, s) -- every entry below takes the mode;
  *   - the filter is indexed [k, c, r, s]; the same loop on that page adds the
  *     channel stride twice for the filter, which is read as a slip for the
  *     output-channel stride plus the input-channel stride;
@@ -102,20 +106,22 @@ static int64_t oracle_point(const int8_t *x, const int64_t xd[4], const int64_t 
                             const int8_t *w, const int64_t wd[4], const int64_t ws[4],
                             int64_t n, int64_t k, int64_t p, int64_t q,
                             const int64_t pre[2], const int64_t stride[2],
-                            const int64_t dil[2])
+                            const int64_t dil[2], int mode)
 {
     const int64_t C = xd[1], H = xd[2], Wd = xd[3];
     const int64_t R = wd[2], S = wd[3];
     int64_t acc = 0;
     for (int64_t r = 0; r < R; ++r) {
         const int64_t h = p * stride[0] - pre[0] + r * dil[0];
+        const int64_t fr = mode ? R - 1 - r : r;   /* filter row read at this tap */
         for (int64_t s = 0; s < S; ++s) {
             const int64_t wc = q * stride[1] - pre[1] + s * dil[1];
+            const int64_t fs = mode ? S - 1 - s : s;
             if (h < 0 || h >= H || wc < 0 || wc >= Wd)
                 continue; /* zero padding: the term is 0 */
             for (int64_t c = 0; c < C; ++c) {
                 const int64_t xv = x[n * xs[0] + c * xs[1] + h * xs[2] + wc * xs[3]];
-                const int64_t wv = w[k * ws[0] + c * ws[1] + r * ws[2] + s * ws[3]];
+                const int64_t wv = w[k * ws[0] + c * ws[1] + fr * ws[2] + fs * ws[3]];
                 acc += xv * wv;
             }
         }
@@ -133,7 +139,7 @@ int oracle_conv_fprop(const int8_t *x, const int64_t xdims[4], const int64_t xst
                       const int8_t *w, const int64_t wdims[4], const int64_t wstr[4],
                       int32_t *y, const int64_t ydims[4], const int64_t ystr[4],
                       const int64_t pre[2], const int64_t post[2],
-                      const int64_t stride[2], const int64_t dil[2], int nthreads)
+                      const int64_t stride[2], const int64_t dil[2], int mode, int nthreads)
 {
     int64_t want[4];
     if (!xstr || !wstr || !ystr)
@@ -163,7 +169,7 @@ int oracle_conv_fprop(const int8_t *x, const int64_t xdims[4], const int64_t xst
             for (int64_t p = 0; p < P; ++p) {
                 for (int64_t q = 0; q < Q; ++q) {
                     int64_t acc = oracle_point(x, xdims, xstr, w, wdims, wstr,
-                                               n, k, p, q, pre, stride, dil);
+                                               n, k, p, q, pre, stride, dil, mode);
                     if (acc < INT32_MIN || acc > INT32_MAX)
                         overflow = 1;
                     y[n * ystr[0] + k * ystr[1] + p * ystr[2] + q * ystr[3]] =
@@ -183,7 +189,7 @@ int oracle_conv_fprop(const int8_t *x, const int64_t xdims[4], const int64_t xst
 int oracle_conv_fprop_points(const int8_t *x, const int64_t xdims[4], const int64_t xstr[4],
                              const int8_t *w, const int64_t wdims[4], const int64_t wstr[4],
                              const int64_t pre[2], const int64_t post[2],
-                             const int64_t stride[2], const int64_t dil[2],
+                             const int64_t stride[2], const int64_t dil[2], int mode,
                              const int64_t *idx, int64_t npts, int64_t *out)
 {
     int64_t yd[4];
@@ -204,7 +210,7 @@ int oracle_conv_fprop_points(const int8_t *x, const int64_t xdims[4], const int6
     for (int64_t i = 0; i < npts; ++i) {
         const int64_t *t = idx + 4 * i;
         out[i] = oracle_point(x, xdims, xstr, w, wdims, wstr, t[0], t[1], t[2], t[3],
-                              pre, stride, dil);
+                              pre, stride, dil, mode);
     }
     return ORACLE_OK;
 }
@@ -270,7 +276,7 @@ int oracle_conv_fprop_requant(const int8_t *x, const int64_t xdims[4], const int
                               const int64_t pre[2], const int64_t post[2],
                               const int64_t stride[2], const int64_t dil[2],
                               const float *scale, float alpha, const float *bias, int relu,
-                              int nthreads)
+                              int mode, int nthreads)
 {
     int64_t want[4];
     if (!xstr || !wstr || !ystr)
@@ -301,7 +307,7 @@ int oracle_conv_fprop_requant(const int8_t *x, const int64_t xdims[4], const int
             for (int64_t p = 0; p < P; ++p) {
                 for (int64_t q = 0; q < Q; ++q) {
                     int64_t acc = oracle_point(x, xdims, xstr, w, wdims, wstr,
-                                               n, k, p, q, pre, stride, dil);
+                                               n, k, p, q, pre, stride, dil, mode);
                     if (acc < INT32_MIN || acc > INT32_MAX)
                         overflow = 1;
                     y[n * ystr[0] + k * ystr[1] + p * ystr[2] + q * ystr[3]] =

@@ -15,6 +15,11 @@ broken builds of the oracle.
 * the closed forms (delta filters, ones-by-ones counts, constant operands) come
   from the definition on the cuDNN "Convolutions" page, section
   "Convolution Fprop", worked out by hand.
+* true convolution (mode 1) is checked against ``scipy.signal.convolve2d``,
+  the textbook 2-D convolution (it flips the kernel), summed over channels,
+  with padding by ``numpy.pad``, dilation by zero insertion and stride by
+  subsampling; and against the brute force above fed the filter reversed
+  along both spatial axes.
 * ``exact_requant`` evaluates the requantising INT8 epilogue with exact
   rational arithmetic (``fractions.Fraction``): the fused multiply-add is the
   exact value ``acc*s + b`` rounded once to the nearest binary32 (ties to an
@@ -403,8 +408,71 @@ def check_requant_conv(orc) -> None:
     assert np.array_equal(got, want)
 
 
+def _scipy_true_conv(x: np.ndarray, w: np.ndarray, pre, post, stride, dil) -> np.ndarray:
+    """Channel sums of scipy's 2-D convolution ('valid' after explicit zero
+    padding; dilation by zero insertion between taps; stride by subsampling)."""
+    from scipy.signal import convolve2d
+    x = np.asarray(x, dtype=np.int64)
+    w = np.asarray(w, dtype=np.int64)
+    N, C, H, W = x.shape
+    K, _, R, S = w.shape
+    xp = np.pad(x, ((0, 0), (0, 0), (pre[0], post[0]), (pre[1], post[1])))
+    wd = np.zeros((K, C, (R - 1) * dil[0] + 1, (S - 1) * dil[1] + 1), dtype=np.int64)
+    wd[:, :, ::dil[0], ::dil[1]] = w
+    out = None
+    for n in range(N):
+        rows = []
+        for k in range(K):
+            acc = sum(convolve2d(xp[n, c], wd[k, c], mode="valid") for c in range(C))
+            rows.append(acc[::stride[0], ::stride[1]])
+        out = np.stack(rows)[None] if out is None else np.concatenate([out, np.stack(rows)[None]])
+    return out
+
+
+def check_convolution_mode(orc) -> None:
+    """Mode 1 = textbook convolution (scipy) and = brute-force
+    cross-correlation with the filter reversed; mode 0 differs from it for
+    asymmetric filters; a delta filter moves the image the other way."""
+    rng = np.random.default_rng(37)
+    for t in range(40):
+        N, C, K = (int(v) for v in rng.integers(1, 4, 3))
+        H, W = (int(v) for v in rng.integers(2, 9, 2))
+        R, S = (int(v) for v in rng.integers(1, 4, 2))
+        pre = tuple(int(v) for v in rng.integers(0, 3, 2))
+        post = tuple(int(v) for v in rng.integers(0, 3, 2))
+        st = tuple(int(v) for v in rng.integers(1, 3, 2))
+        dl = tuple(int(v) for v in rng.integers(1, 3, 2))
+        if H + pre[0] + post[0] - dl[0] * (R - 1) - 1 < 0 or W + pre[1] + post[1] - dl[1] * (S - 1) - 1 < 0:
+            continue
+        x = rand_i8(rng, (N, C, H, W))
+        w = rand_i8(rng, (K, C, R, S))
+        y1 = orc.conv_fprop(x, w, pre, post, st, dl, mode=1).numpy().astype(np.int64)
+        assert np.array_equal(y1, _scipy_true_conv(x.numpy(), w.numpy(), pre, post, st, dl)), t
+        wf = np.ascontiguousarray(w.numpy()[:, :, ::-1, ::-1])
+        assert np.array_equal(y1, brute_force(x.numpy(), wf, pre, post, st, dl)), t
+    # delta at (r0, s0) = (0, 2) of a 3x3 filter, no padding: cross-correlation
+    # reads x[p + 0, q + 2], convolution x[p + 2, q + 0]
+    x = rand_i8(rng, (1, 1, 6, 7))
+    w = torch.zeros((1, 1, 3, 3), dtype=torch.int8)
+    w[0, 0, 0, 2] = 1
+    xn = x.numpy().astype(np.int64)[0, 0]
+    assert np.array_equal(orc.conv_fprop(x, w).numpy()[0, 0], xn[0:4, 2:7])
+    assert np.array_equal(orc.conv_fprop(x, w, mode=1).numpy()[0, 0], xn[2:6, 0:5])
+    # the points and requantising entries take the mode too
+    x = rand_i8(rng, (2, 3, 6, 5))
+    w = rand_i8(rng, (4, 3, 3, 2))
+    y1 = orc.conv_fprop(x, w, (1, 0), (0, 1), mode=1).numpy()
+    idx = np.array([[n, k, p, q] for n in range(2) for k in range(4) for p in range(y1.shape[2])
+                    for q in range(y1.shape[3])], dtype=np.int64)
+    v = orc.conv_fprop_points(x, w, idx, (1, 0), (0, 1), mode=1)
+    assert np.array_equal(v, y1[idx[:, 0], idx[:, 1], idx[:, 2], idx[:, 3]].astype(np.int64))
+    q8 = orc.conv_fprop_requant(x, w, (1, 0), (0, 1), alpha=0.01, mode=1).numpy()
+    want = np.vectorize(lambda a: exact_requant(int(a), 0.01, 0.0, False))(y1).astype(np.int8)
+    assert np.array_equal(q8, want)
+
+
 QUICK_CHECKS = [
     check_random_vs_brute_force, check_offcentre_delta, check_identity_1x1, check_ones_count,
     check_constant_min, check_layouts, check_metamorphic, check_points, check_requant_exact,
-    check_requant_conv,
+    check_requant_conv, check_convolution_mode,
 ]

@@ -112,6 +112,10 @@ def test_requant_conv(orc):
     pins.check_requant_conv(orc)
 
 
+def test_convolution_mode(orc):
+    pins.check_convolution_mode(orc)
+
+
 @pytest.mark.parametrize("name", wl.CASE_ORDER)
 def test_workloads_vs_f64_library_conv(orc, name):
     """Oracle == float64 torch conv2d on every workload at full size."""
@@ -172,10 +176,12 @@ MUTATIONS = [
     ("column pre-padding ignored", "q * stride[1] - pre[1]", "q * stride[1]"),
     ("row dilation dropped", "r * dil[0];", "r;"),
     ("column stride dropped", "q * stride[1] - pre[1] + s * dil[1]", "q - pre[1] + s * dil[1]"),
-    ("filter taps transposed", "r * ws[2] + s * ws[3]", "s * ws[2] + r * ws[3]"),
+    ("filter taps transposed", "fr * ws[2] + fs * ws[3]", "fs * ws[2] + fr * ws[3]"),
     ("filter read with the channel stride twice", "k * ws[0] + c * ws[1]", "k * ws[1] + c * ws[1]"),
     ("image h/w strides swapped", "h * xs[2] + wc * xs[3]", "h * xs[3] + wc * xs[2]"),
-    ("filter flipped (true convolution)", "r * ws[2] + s * ws[3]", "(R - 1 - r) * ws[2] + (S - 1 - s) * ws[3]"),
+    ("filter flipped in cross-correlation", "fr = mode ? R - 1 - r : r;", "fr = R - 1 - r;"),
+    ("convolution mode flips rows only", "fs = mode ? S - 1 - s : s;", "fs = s;"),
+    ("convolution mode flips nothing", "fr = mode ? R - 1 - r : r;", "fr = r;"),
     ("unsigned widening of int8", "const int64_t xv = x[", "const int64_t xv = (uint8_t)x["),
     ("last channel dropped", "for (int64_t c = 0; c < C; ++c)", "for (int64_t c = 0; c + 1 < C; ++c)"),
     ("first filter row dropped", "for (int64_t r = 0; r < R; ++r)", "for (int64_t r = 1; r < R; ++r)"),
