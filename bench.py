@@ -41,6 +41,10 @@ def parse():
     ap.add_argument("--graph", action="store_true",
                     help="record the timed steps into one HIP graph (captured through the "
                          "workspace entry) and time its replay")
+    ap.add_argument("--mode", choices=("cross_correlation", "convolution"),
+                    default="cross_correlation",
+                    help="convolution: true convolution (filter taps reversed) through the "
+                         "general entry conv_fprop_i8_ex_ws")
     ap.add_argument("--epilogue", choices=("int32", "requant"), default="int32",
                     help="int32: the plain entry; requant: INT8 output with per-channel "
                          "scale and bias and ReLU")
@@ -129,8 +133,13 @@ def main():
     sh = ctypes.c_void_p(stream.cuda_stream)
     params = ci8._params(c.pre, c.post, c.stride, c.dilation, None)
 
+    conv_mode = 1 if args.mode == "convolution" else 0
+
     def prebuilt(x, w, y):
-        extra = (ctypes.byref(rq),) if rq_on else ()
+        if conv_mode:
+            extra = (ctypes.c_int32(conv_mode), ctypes.byref(rq) if rq_on else None)
+        else:
+            extra = (ctypes.byref(rq),) if rq_on else ()
         return (ctypes.byref(ci8.desc(x)), ctypes.c_void_p(x.data_ptr()),
                 ctypes.byref(ci8.desc(w)), ctypes.c_void_p(w.data_ptr()),
                 ctypes.byref(ci8.desc(y)), ctypes.c_void_p(y.data_ptr()), *params, *extra,
@@ -138,7 +147,10 @@ def main():
                 ctypes.c_size_t(ws_bytes), sh)
 
     calls = [prebuilt(s[3], s[4], s[5]) for s in sets]
-    fn = ci8.lib.conv_fprop_i8_requant_ws if rq_on else ci8.lib.conv_fprop_i8_ws
+    if conv_mode:
+        fn = ci8.lib.conv_fprop_i8_ex_ws
+    else:
+        fn = ci8.lib.conv_fprop_i8_requant_ws if rq_on else ci8.lib.conv_fprop_i8_ws
 
     def step(i):
         rc = fn(*calls[i % nsets])
@@ -247,9 +259,11 @@ def main():
         while True:
             if rq_on:
                 orc.conv_fprop_requant(d["x"], d["w"], c.pre, c.post, c.stride, c.dilation,
-                                       scale=sc_cpu, bias=bi_cpu, relu=True, threads=threads)
+                                       scale=sc_cpu, bias=bi_cpu, relu=True, threads=threads,
+                                       mode=conv_mode)
             else:
-                orc.conv_fprop(d["x"], d["w"], c.pre, c.post, c.stride, c.dilation, threads=threads)
+                orc.conv_fprop(d["x"], d["w"], c.pre, c.post, c.stride, c.dilation, threads=threads,
+                               mode=conv_mode)
             reps += 1
             el = time.perf_counter() - t0
             if el >= args.cpu_seconds or reps >= 20:
@@ -280,6 +294,7 @@ def main():
                    "output": ("int8: fma(sum, per-channel scale, bias), ReLU, round half to "
                               "even, saturate") if rq_on else "int32",
                    "plan": plan, "launch": "hip graph replay" if args.graph else "eager",
+                   "mode": args.mode,
                    "buffer_sets": nsets},
         "frac_of_int8_peak": tops / INT8_PEAK_TOPS,
         "roofline": roof,

@@ -13,7 +13,8 @@
  * where X reads as 0 outside 0 <= h < H, 0 <= w < W (zero padding).  It is a
  * cross-correlation: the filter is not flipped (the naive loop of "Building a
  * From-Scratch INT8 Strided Convolution Kernel", "Step 2", reads the input at
- * oh*stride + kh against kernel tap kh).  The result is exact: every product
+ * oh*stride + kh against kernel tap kh); true convolution is available
+ * through conv_fprop_i8_ex_ws.  The result is exact: every product
  * of two int8 values is summed in 32-bit integers, which cannot overflow while
  * C*R*S <= 131071 (|product| <= 16384); larger reductions are refused.  The
  * plain entries never saturate and refuse an int8 output (the forum thread
@@ -243,6 +244,61 @@ conv_i8_status_t conv_fprop_i8_requant(const conv_i8_desc_t *image, const void *
                                        const int64_t dilation[2],
                                        const conv_i8_requant_t *rq,
                                        void *stream);
+
+/*
+ * Convolution mode.  The cuDNN "Convolutions" page lists a convolution_mode
+ * parameter for "Convolution Fprop" without defining its values; read as the
+ * usual pair: cross-correlation (the operation above, what every other entry
+ * computes) and true convolution, which reads filter tap (R-1-r, S-1-s)
+ * where cross-correlation reads (r, s):
+ *
+ *   Y[n,k,p,q] = sum_{c,r,s} X[n, c, p*stride_h - pre_h + r*dil_h,
+ *                                q*stride_w - pre_w + s*dil_w]
+ *                            * W[k, c, R-1-r, S-1-s]
+ */
+typedef enum {
+    CONV_I8_MODE_CROSS_CORRELATION = 0,
+    CONV_I8_MODE_CONVOLUTION = 1
+} conv_i8_mode_t;
+
+/*
+ * Workspace bytes for conv_fprop_i8_ex_ws (the same rules as
+ * conv_fprop_i8_workspace_size; the mode does not change them).  The output
+ * descriptor may be INT32 or INT8.  CONV_I8_ERR_PARAM for an unknown mode.
+ */
+conv_i8_status_t conv_fprop_i8_ex_workspace_size(const conv_i8_desc_t *image,
+                                                 const void *image_ptr,
+                                                 const conv_i8_desc_t *filter,
+                                                 const void *filter_ptr,
+                                                 const conv_i8_desc_t *out,
+                                                 const int64_t pre_padding[2],
+                                                 const int64_t post_padding[2],
+                                                 const int64_t stride[2],
+                                                 const int64_t dilation[2],
+                                                 int32_t mode,
+                                                 size_t *workspace_bytes);
+
+/*
+ * The general entry: either mode (conv_i8_mode_t), and the epilogue chosen by
+ * the output descriptor -- INT32 sums with rq == NULL (CONV_I8_ERR_PARAM
+ * otherwise), or the requantising INT8 epilogue with rq != NULL
+ * (CONV_I8_ERR_NULL otherwise); any other output dtype is
+ * CONV_I8_ERR_DTYPE.  Workspace, errors and stream behaviour as
+ * conv_fprop_i8_ws: never allocates, never synchronises.  With
+ * CONV_I8_MODE_CROSS_CORRELATION it computes exactly what conv_fprop_i8_ws
+ * or conv_fprop_i8_requant_ws compute.
+ */
+conv_i8_status_t conv_fprop_i8_ex_ws(const conv_i8_desc_t *image, const void *image_ptr,
+                                     const conv_i8_desc_t *filter, const void *filter_ptr,
+                                     const conv_i8_desc_t *out, void *out_ptr,
+                                     const int64_t pre_padding[2],
+                                     const int64_t post_padding[2],
+                                     const int64_t stride[2],
+                                     const int64_t dilation[2],
+                                     int32_t mode,
+                                     const conv_i8_requant_t *rq,
+                                     void *workspace, size_t workspace_bytes,
+                                     void *stream);
 
 /* Static string naming a status code. */
 const char *conv_i8_status_string(conv_i8_status_t status);

@@ -29,7 +29,9 @@ __all__ = [
     "ConvI8Error", "conv_fprop_i8", "conv_fprop_i8_ws", "conv_fprop_i8_plain",
     "conv_fprop_i8_out_dims", "conv_fprop_i8_workspace_size", "conv_fprop_i8_plan",
     "conv_fprop_i8_requant", "conv_fprop_i8_requant_ws", "conv_fprop_i8_requant_plain",
-    "conv_fprop_i8_requant_workspace_size", "Requant",
+    "conv_fprop_i8_requant_workspace_size", "Requant", "conv_fprop_i8_ex_ws",
+    "conv_fprop_i8_ex_workspace_size", "conv_fprop_i8_mode", "MODE_CROSS_CORRELATION",
+    "MODE_CONVOLUTION",
     "status_string", "LIB_PATH", "DT_INT8", "DT_INT32", "MAX_REDUCTION", "lib",
 ]
 
@@ -37,6 +39,8 @@ LIB_PATH = _build.LIB
 DT_INT8 = 1
 DT_INT32 = 2
 MAX_REDUCTION = 131071
+MODE_CROSS_CORRELATION = 0
+MODE_CONVOLUTION = 1
 
 STATUS = {
     0: "CONV_I8_OK", 1: "CONV_I8_ERR_NULL", 2: "CONV_I8_ERR_DTYPE", 3: "CONV_I8_ERR_RANK",
@@ -88,11 +92,16 @@ lib.conv_fprop_i8_requant_workspace_size.argtypes = [_DP, _P, _DP, _P, _DP, _V2,
 lib.conv_fprop_i8_requant_ws.argtypes = [_DP, _P, _DP, _P, _DP, _P, _V2, _V2, _V2, _V2, _RQ, _P,
                                          ctypes.c_size_t, _P]
 lib.conv_fprop_i8_requant.argtypes = [_DP, _P, _DP, _P, _DP, _P, _V2, _V2, _V2, _V2, _RQ, _P]
+lib.conv_fprop_i8_ex_workspace_size.argtypes = [_DP, _P, _DP, _P, _DP, _V2, _V2, _V2, _V2,
+                                                ctypes.c_int32, ctypes.POINTER(ctypes.c_size_t)]
+lib.conv_fprop_i8_ex_ws.argtypes = [_DP, _P, _DP, _P, _DP, _P, _V2, _V2, _V2, _V2, ctypes.c_int32,
+                                    _RQ, _P, ctypes.c_size_t, _P]
 lib.conv_i8_status_string.argtypes = [ctypes.c_int]
 lib.conv_i8_status_string.restype = ctypes.c_char_p
 for _f in ("conv_fprop_i8_out_dims", "conv_fprop_i8_workspace_size", "conv_fprop_i8_ws",
            "conv_fprop_i8", "conv_fprop_i8_plan", "conv_fprop_i8_requant_workspace_size",
-           "conv_fprop_i8_requant_ws", "conv_fprop_i8_requant"):
+           "conv_fprop_i8_requant_ws", "conv_fprop_i8_requant", "conv_fprop_i8_ex_workspace_size",
+           "conv_fprop_i8_ex_ws"):
     getattr(lib, _f).restype = ctypes.c_int
 
 
@@ -334,3 +343,53 @@ def conv_fprop_i8_requant(x: torch.Tensor, w: torch.Tensor, scale: Optional[torc
     ws = torch.empty(n, dtype=torch.uint8, device=out.device) if n else None
     return conv_fprop_i8_requant_ws(x, w, out, ws, scale, alpha, bias, relu, pre_padding,
                                     post_padding, stride, dilation, padding, stream)
+
+
+def conv_fprop_i8_ex_workspace_size(x, w, out, pre_padding=0, post_padding=0, stride=1,
+                                    dilation=1, padding=None, mode: int = 0) -> int:
+    pre, post, st, dl = _params(pre_padding, post_padding, stride, dilation, padding)
+    n = ctypes.c_size_t()
+    xp = _ptr(x) if isinstance(x, torch.Tensor) else None
+    wp = _ptr(w) if isinstance(w, torch.Tensor) else None
+    _check(lib.conv_fprop_i8_ex_workspace_size(
+        ctypes.byref(_as_desc(x)), xp, ctypes.byref(_as_desc(w)), wp, ctypes.byref(_as_desc(out)),
+        pre, post, st, dl, int(mode), ctypes.byref(n)))
+    return int(n.value)
+
+
+def conv_fprop_i8_ex_ws(x: torch.Tensor, w: torch.Tensor, out: torch.Tensor,
+                        workspace: Optional[torch.Tensor], mode: int = 0,
+                        requant: Optional[Requant] = None, pre_padding=0, post_padding=0, stride=1,
+                        dilation=1, padding=None, stream=None) -> torch.Tensor:
+    """The general C entry: ``mode`` (0 cross-correlation, 1 true convolution)
+    and, for an int8 ``out``, the requantisation block from ``_requant``."""
+    pre, post, st, dl = _params(pre_padding, post_padding, stride, dilation, padding)
+    ws_ptr = _ptr(workspace)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(lib.conv_fprop_i8_ex_ws(
+        ctypes.byref(desc(x)), _ptr(x), ctypes.byref(desc(w)), _ptr(w), ctypes.byref(desc(out)),
+        _ptr(out), pre, post, st, dl, int(mode),
+        ctypes.byref(requant) if requant is not None else None, ws_ptr,
+        ctypes.c_size_t(ws_bytes), _stream_handle(stream)))
+    return out
+
+
+def conv_fprop_i8_mode(x: torch.Tensor, w: torch.Tensor, mode: int, out: Optional[torch.Tensor] = None,
+                       scale: Optional[torch.Tensor] = None, alpha: Optional[float] = None,
+                       bias: Optional[torch.Tensor] = None, relu: bool = False, pre_padding=0,
+                       post_padding=0, stride=1, dilation=1, padding=None,
+                       stream=None) -> torch.Tensor:
+    """conv_fprop in either mode.  INT32 output unless a requantisation is
+    asked for (scale, alpha, bias or relu given), then INT8."""
+    rq_on = scale is not None or alpha is not None or bias is not None or relu
+    _check_channels(w, scale, "scale")
+    _check_channels(w, bias, "bias")
+    if out is None:
+        dims = conv_fprop_i8_out_dims(x, w, pre_padding, post_padding, stride, dilation, padding)
+        out = _out_like(x, dims, torch.int8 if rq_on else torch.int32)
+    rq = _requant(scale, 1.0 if alpha is None else alpha, bias, relu) if rq_on else None
+    n = conv_fprop_i8_ex_workspace_size(x, w, out, pre_padding, post_padding, stride, dilation,
+                                        padding, mode)
+    ws = torch.empty(n, dtype=torch.uint8, device=out.device) if n else None
+    return conv_fprop_i8_ex_ws(x, w, out, ws, mode, rq, pre_padding, post_padding, stride,
+                               dilation, padding, stream)

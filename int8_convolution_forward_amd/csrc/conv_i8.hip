@@ -103,6 +103,7 @@ struct Problem {
     T4 x, w, y;
     int64_t N, C, H, W, K, R, S, P, Q;
     int64_t pre[2], post[2], str[2], dil[2];
+    int64_t mode;  // CONV_I8_MODE_*: 1 reads filter tap (R-1-r, S-1-s)
 };
 
 conv_i8_status_t read_params(const int64_t *pre, const int64_t *post, const int64_t *stride,
@@ -173,11 +174,15 @@ conv_i8_status_t analyze_inputs(const conv_i8_desc_t *image, const conv_i8_desc_
 
 conv_i8_status_t analyze(const conv_i8_desc_t *image, const conv_i8_desc_t *filter,
                          const conv_i8_desc_t *out, const int64_t *pre, const int64_t *post,
-                         const int64_t *stride, const int64_t *dil, int32_t out_dtype, Problem *pb)
+                         const int64_t *stride, const int64_t *dil, int32_t out_dtype, int32_t mode,
+                         Problem *pb)
 {
     conv_i8_status_t st = analyze_inputs(image, filter, pre, post, stride, dil, pb);
     if (st != CONV_I8_OK)
         return st;
+    if (mode != CONV_I8_MODE_CROSS_CORRELATION && mode != CONV_I8_MODE_CONVOLUTION)
+        return CONV_I8_ERR_PARAM;
+    pb->mode = mode;
     // The output dtype is checked like every other field: the plain entries
     // refuse an INT8 output descriptor rather than write saturated bytes into
     // it; only the requantising entries write INT8.
@@ -711,6 +716,14 @@ conv_i8_status_t run(const Problem &pb, const Plan &pl, const void *x_ptr, const
     a.fK = (int)pl.wsK;
     a.fR = (int)pl.wsR;
     a.fS = (int)pl.wsS;
+    if (pb.mode == CONV_I8_MODE_CONVOLUTION) {
+        // true convolution: tap (r, s) reads filter tap (R-1-r, S-1-s), i.e.
+        // the taps from the far corner with negated strides (the offsets stay
+        // inside [0, w_span))
+        a.flt0 = (int)((pb.R - 1) * pl.wsR + (pb.S - 1) * pl.wsS);
+        a.fR = -a.fR;
+        a.fS = -a.fS;
+    }
     a.P = (int)pb.P;
     a.Q = (int)pb.Q;
     a.PQ = (int)(pb.P * pb.Q);
@@ -795,14 +808,17 @@ conv_i8_status_t prepare(const conv_i8_desc_t *image, const void *image_ptr,
                          const conv_i8_desc_t *filter, const void *filter_ptr,
                          const conv_i8_desc_t *out, const int64_t *pre, const int64_t *post,
                          const int64_t *stride, const int64_t *dil, Problem *pb, Plan *pl,
-                         int32_t out_dtype = CONV_I8_DT_INT32)
+                         int32_t out_dtype = CONV_I8_DT_INT32,
+                         int32_t mode = CONV_I8_MODE_CROSS_CORRELATION)
 {
-    // The plan does not depend on the output dtype (it works in elements).
-    conv_i8_status_t st = analyze(image, filter, out, pre, post, stride, dil, out_dtype, pb);
+    // The plan does not depend on the output dtype (it works in elements) nor
+    // on the mode (the kernels read the taps in either order).
+    conv_i8_status_t st = analyze(image, filter, out, pre, post, stride, dil, out_dtype, mode, pb);
     if (st != CONV_I8_OK)
         return st;
     PlanKey key;
     memset(&key, 0, sizeof key);  // padding takes part in the comparison
+    static_assert(sizeof(Problem) % 8 == 0, "Problem has no tail padding to clear");
     key.pb = *pb;
     key.x_direct = direct_ok(pb->x, image_ptr) ? 1 : 0;
     key.w_direct = direct_ok(pb->w, filter_ptr) ? 1 : 0;
@@ -878,6 +894,101 @@ conv_i8_status_t conv_fprop_i8_out_dims(const conv_i8_desc_t *image, const conv_
     return CONV_I8_OK;
 }
 
+}  // extern "C"
+
+namespace convi8 {
+namespace {
+
+// Shared body of the workspace-size entries.
+conv_i8_status_t entry_workspace_size(const conv_i8_desc_t *image, const void *image_ptr,
+                                      const conv_i8_desc_t *filter, const void *filter_ptr,
+                                      const conv_i8_desc_t *out, const int64_t *pre,
+                                      const int64_t *post, const int64_t *stride,
+                                      const int64_t *dil, int32_t out_dtype, int32_t mode,
+                                      size_t *workspace_bytes)
+{
+    if (!workspace_bytes)
+        return CONV_I8_ERR_NULL;
+    Problem pb;
+    Plan pl;
+    conv_i8_status_t st = prepare(image, image_ptr, filter, filter_ptr, out, pre, post, stride,
+                                  dil, &pb, &pl, out_dtype, mode);
+    if (st != CONV_I8_OK)
+        return st;
+    *workspace_bytes = pb.y.elems() == 0 || pb.C == 0 ? 0 : pl.ws_bytes;
+    return CONV_I8_OK;
+}
+
+// Shared body of the compute entries.  rq is set exactly when out_dtype is
+// INT8.  With alloc, the workspace is taken stream-ordered here; otherwise
+// the caller's is checked and used.
+conv_i8_status_t entry_run(const conv_i8_desc_t *image, const void *image_ptr,
+                           const conv_i8_desc_t *filter, const void *filter_ptr,
+                           const conv_i8_desc_t *out, void *out_ptr, const int64_t *pre,
+                           const int64_t *post, const int64_t *stride, const int64_t *dil,
+                           int32_t out_dtype, int32_t mode, const conv_i8_requant_t *rq, bool alloc,
+                           void *workspace, size_t workspace_bytes, void *stream)
+{
+    Problem pb;
+    Plan pl;
+    conv_i8_status_t st = prepare(image, image_ptr, filter, filter_ptr, out, pre, post, stride,
+                                  dil, &pb, &pl, out_dtype, mode);
+    if (st != CONV_I8_OK)
+        return st;
+    if (out_dtype == CONV_I8_DT_INT8 && (st = check_requant(rq)) != CONV_I8_OK)
+        return st;
+    if ((st = check_ptrs(pb, image_ptr, filter_ptr, out_ptr)) != CONV_I8_OK)
+        return st;
+    if (pb.y.elems() == 0)
+        return CONV_I8_OK;
+    const size_t need = pb.C == 0 ? 0 : pl.ws_bytes;
+    hipStream_t s = (hipStream_t)stream;
+    void *ws = workspace;
+    if (alloc) {
+        ws = nullptr;
+        if (need > 0 && hipMallocAsync(&ws, need, s) != hipSuccess)
+            return CONV_I8_ERR_HIP;
+    } else {
+        if (workspace_bytes < need)
+            return CONV_I8_ERR_WORKSPACE;
+        if (need > 0 && !workspace)
+            return CONV_I8_ERR_NULL;
+        if (need > 0 && ((uintptr_t)workspace & 255u) != 0)
+            return CONV_I8_ERR_WORKSPACE;
+    }
+    if (log_enabled())
+        fprintf(stderr, "conv_i8%s%s: %s\n", rq ? " (requant)" : "",
+                mode == CONV_I8_MODE_CONVOLUTION ? " (convolution)" : "", describe(pb, pl).c_str());
+    st = run(pb, pl, image_ptr, filter_ptr, out_ptr, ws, s, out_dtype == CONV_I8_DT_INT8 ? rq : nullptr);
+    if (alloc && ws && hipFreeAsync(ws, s) != hipSuccess && st == CONV_I8_OK)
+        st = CONV_I8_ERR_HIP;
+    return st;
+}
+
+// Output dtype and requantisation block of the extended entries: INT32
+// without a block, INT8 with one.
+conv_i8_status_t ex_out_dtype(const conv_i8_desc_t *out, const conv_i8_requant_t *rq, int32_t *dt)
+{
+    if (!out)
+        return CONV_I8_ERR_NULL;
+    if (out->dtype == CONV_I8_DT_INT32) {
+        if (rq)
+            return CONV_I8_ERR_PARAM;
+        *dt = CONV_I8_DT_INT32;
+        return CONV_I8_OK;
+    }
+    if (out->dtype == CONV_I8_DT_INT8) {
+        *dt = CONV_I8_DT_INT8;
+        return CONV_I8_OK;
+    }
+    return CONV_I8_ERR_DTYPE;
+}
+
+}  // namespace
+}  // namespace convi8
+
+extern "C" {
+
 conv_i8_status_t conv_fprop_i8_workspace_size(const conv_i8_desc_t *image, const void *image_ptr,
                                               const conv_i8_desc_t *filter, const void *filter_ptr,
                                               const conv_i8_desc_t *out,
@@ -886,16 +997,9 @@ conv_i8_status_t conv_fprop_i8_workspace_size(const conv_i8_desc_t *image, const
                                               const int64_t stride[2], const int64_t dilation[2],
                                               size_t *workspace_bytes)
 {
-    if (!workspace_bytes)
-        return CONV_I8_ERR_NULL;
-    Problem pb;
-    Plan pl;
-    conv_i8_status_t st = prepare(image, image_ptr, filter, filter_ptr, out, pre_padding,
-                                  post_padding, stride, dilation, &pb, &pl);
-    if (st != CONV_I8_OK)
-        return st;
-    *workspace_bytes = pb.y.elems() == 0 || pb.C == 0 ? 0 : pl.ws_bytes;
-    return CONV_I8_OK;
+    return entry_workspace_size(image, image_ptr, filter, filter_ptr, out, pre_padding, post_padding,
+                                stride, dilation, CONV_I8_DT_INT32, CONV_I8_MODE_CROSS_CORRELATION,
+                                workspace_bytes);
 }
 
 conv_i8_status_t conv_fprop_i8_plan(const conv_i8_desc_t *image, const void *image_ptr,
@@ -923,26 +1027,9 @@ conv_i8_status_t conv_fprop_i8_ws(const conv_i8_desc_t *image, const void *image
                                   const int64_t stride[2], const int64_t dilation[2],
                                   void *workspace, size_t workspace_bytes, void *stream)
 {
-    Problem pb;
-    Plan pl;
-    conv_i8_status_t st = prepare(image, image_ptr, filter, filter_ptr, out, pre_padding,
-                                  post_padding, stride, dilation, &pb, &pl);
-    if (st != CONV_I8_OK)
-        return st;
-    if ((st = check_ptrs(pb, image_ptr, filter_ptr, out_ptr)) != CONV_I8_OK)
-        return st;
-    if (pb.y.elems() == 0)
-        return CONV_I8_OK;
-    const size_t need = pb.C == 0 ? 0 : pl.ws_bytes;
-    if (workspace_bytes < need)
-        return CONV_I8_ERR_WORKSPACE;
-    if (need > 0 && !workspace)
-        return CONV_I8_ERR_NULL;
-    if (need > 0 && ((uintptr_t)workspace & 255u) != 0)
-        return CONV_I8_ERR_WORKSPACE;
-    if (log_enabled())
-        fprintf(stderr, "conv_i8: %s\n", describe(pb, pl).c_str());
-    return run(pb, pl, image_ptr, filter_ptr, out_ptr, workspace, (hipStream_t)stream);
+    return entry_run(image, image_ptr, filter, filter_ptr, out, out_ptr, pre_padding, post_padding,
+                     stride, dilation, CONV_I8_DT_INT32, CONV_I8_MODE_CROSS_CORRELATION, nullptr,
+                     false, workspace, workspace_bytes, stream);
 }
 
 conv_i8_status_t conv_fprop_i8(const conv_i8_desc_t *image, const void *image_ptr,
@@ -951,27 +1038,9 @@ conv_i8_status_t conv_fprop_i8(const conv_i8_desc_t *image, const void *image_pt
                                const int64_t pre_padding[2], const int64_t post_padding[2],
                                const int64_t stride[2], const int64_t dilation[2], void *stream)
 {
-    Problem pb;
-    Plan pl;
-    conv_i8_status_t st = prepare(image, image_ptr, filter, filter_ptr, out, pre_padding,
-                                  post_padding, stride, dilation, &pb, &pl);
-    if (st != CONV_I8_OK)
-        return st;
-    if ((st = check_ptrs(pb, image_ptr, filter_ptr, out_ptr)) != CONV_I8_OK)
-        return st;
-    if (pb.y.elems() == 0)
-        return CONV_I8_OK;
-    const size_t need = pb.C == 0 ? 0 : pl.ws_bytes;
-    hipStream_t s = (hipStream_t)stream;
-    void *ws = nullptr;
-    if (need > 0 && hipMallocAsync(&ws, need, s) != hipSuccess)
-        return CONV_I8_ERR_HIP;
-    if (log_enabled())
-        fprintf(stderr, "conv_i8: %s\n", describe(pb, pl).c_str());
-    st = run(pb, pl, image_ptr, filter_ptr, out_ptr, ws, s);
-    if (ws && hipFreeAsync(ws, s) != hipSuccess && st == CONV_I8_OK)
-        st = CONV_I8_ERR_HIP;
-    return st;
+    return entry_run(image, image_ptr, filter, filter_ptr, out, out_ptr, pre_padding, post_padding,
+                     stride, dilation, CONV_I8_DT_INT32, CONV_I8_MODE_CROSS_CORRELATION, nullptr,
+                     true, nullptr, 0, stream);
 }
 
 conv_i8_status_t conv_fprop_i8_requant_workspace_size(
@@ -980,16 +1049,9 @@ conv_i8_status_t conv_fprop_i8_requant_workspace_size(
     const int64_t post_padding[2], const int64_t stride[2], const int64_t dilation[2],
     size_t *workspace_bytes)
 {
-    if (!workspace_bytes)
-        return CONV_I8_ERR_NULL;
-    Problem pb;
-    Plan pl;
-    conv_i8_status_t st = prepare(image, image_ptr, filter, filter_ptr, out, pre_padding,
-                                  post_padding, stride, dilation, &pb, &pl, CONV_I8_DT_INT8);
-    if (st != CONV_I8_OK)
-        return st;
-    *workspace_bytes = pb.y.elems() == 0 || pb.C == 0 ? 0 : pl.ws_bytes;
-    return CONV_I8_OK;
+    return entry_workspace_size(image, image_ptr, filter, filter_ptr, out, pre_padding, post_padding,
+                                stride, dilation, CONV_I8_DT_INT8, CONV_I8_MODE_CROSS_CORRELATION,
+                                workspace_bytes);
 }
 
 conv_i8_status_t conv_fprop_i8_requant_ws(const conv_i8_desc_t *image, const void *image_ptr,
@@ -1000,28 +1062,9 @@ conv_i8_status_t conv_fprop_i8_requant_ws(const conv_i8_desc_t *image, const voi
                                           const int64_t dilation[2], const conv_i8_requant_t *rq,
                                           void *workspace, size_t workspace_bytes, void *stream)
 {
-    Problem pb;
-    Plan pl;
-    conv_i8_status_t st = prepare(image, image_ptr, filter, filter_ptr, out, pre_padding,
-                                  post_padding, stride, dilation, &pb, &pl, CONV_I8_DT_INT8);
-    if (st != CONV_I8_OK)
-        return st;
-    if ((st = check_requant(rq)) != CONV_I8_OK)
-        return st;
-    if ((st = check_ptrs(pb, image_ptr, filter_ptr, out_ptr)) != CONV_I8_OK)
-        return st;
-    if (pb.y.elems() == 0)
-        return CONV_I8_OK;
-    const size_t need = pb.C == 0 ? 0 : pl.ws_bytes;
-    if (workspace_bytes < need)
-        return CONV_I8_ERR_WORKSPACE;
-    if (need > 0 && !workspace)
-        return CONV_I8_ERR_NULL;
-    if (need > 0 && ((uintptr_t)workspace & 255u) != 0)
-        return CONV_I8_ERR_WORKSPACE;
-    if (log_enabled())
-        fprintf(stderr, "conv_i8 (requant): %s\n", describe(pb, pl).c_str());
-    return run(pb, pl, image_ptr, filter_ptr, out_ptr, workspace, (hipStream_t)stream, rq);
+    return entry_run(image, image_ptr, filter, filter_ptr, out, out_ptr, pre_padding, post_padding,
+                     stride, dilation, CONV_I8_DT_INT8, CONV_I8_MODE_CROSS_CORRELATION, rq, false,
+                     workspace, workspace_bytes, stream);
 }
 
 conv_i8_status_t conv_fprop_i8_requant(const conv_i8_desc_t *image, const void *image_ptr,
@@ -1031,29 +1074,43 @@ conv_i8_status_t conv_fprop_i8_requant(const conv_i8_desc_t *image, const void *
                                        const int64_t stride[2], const int64_t dilation[2],
                                        const conv_i8_requant_t *rq, void *stream)
 {
-    Problem pb;
-    Plan pl;
-    conv_i8_status_t st = prepare(image, image_ptr, filter, filter_ptr, out, pre_padding,
-                                  post_padding, stride, dilation, &pb, &pl, CONV_I8_DT_INT8);
+    return entry_run(image, image_ptr, filter, filter_ptr, out, out_ptr, pre_padding, post_padding,
+                     stride, dilation, CONV_I8_DT_INT8, CONV_I8_MODE_CROSS_CORRELATION, rq, true,
+                     nullptr, 0, stream);
+}
+
+conv_i8_status_t conv_fprop_i8_ex_workspace_size(const conv_i8_desc_t *image, const void *image_ptr,
+                                                 const conv_i8_desc_t *filter,
+                                                 const void *filter_ptr, const conv_i8_desc_t *out,
+                                                 const int64_t pre_padding[2],
+                                                 const int64_t post_padding[2],
+                                                 const int64_t stride[2],
+                                                 const int64_t dilation[2], int32_t mode,
+                                                 size_t *workspace_bytes)
+{
+    int32_t dt = 0;
+    // the output dtype decides the epilogue; either is fine for the size
+    if (!out)
+        return CONV_I8_ERR_NULL;
+    dt = out->dtype == CONV_I8_DT_INT8 ? CONV_I8_DT_INT8 : CONV_I8_DT_INT32;
+    return entry_workspace_size(image, image_ptr, filter, filter_ptr, out, pre_padding, post_padding,
+                                stride, dilation, dt, mode, workspace_bytes);
+}
+
+conv_i8_status_t conv_fprop_i8_ex_ws(const conv_i8_desc_t *image, const void *image_ptr,
+                                     const conv_i8_desc_t *filter, const void *filter_ptr,
+                                     const conv_i8_desc_t *out, void *out_ptr,
+                                     const int64_t pre_padding[2], const int64_t post_padding[2],
+                                     const int64_t stride[2], const int64_t dilation[2],
+                                     int32_t mode, const conv_i8_requant_t *rq, void *workspace,
+                                     size_t workspace_bytes, void *stream)
+{
+    int32_t dt = 0;
+    conv_i8_status_t st = ex_out_dtype(out, rq, &dt);
     if (st != CONV_I8_OK)
         return st;
-    if ((st = check_requant(rq)) != CONV_I8_OK)
-        return st;
-    if ((st = check_ptrs(pb, image_ptr, filter_ptr, out_ptr)) != CONV_I8_OK)
-        return st;
-    if (pb.y.elems() == 0)
-        return CONV_I8_OK;
-    const size_t need = pb.C == 0 ? 0 : pl.ws_bytes;
-    hipStream_t s = (hipStream_t)stream;
-    void *ws = nullptr;
-    if (need > 0 && hipMallocAsync(&ws, need, s) != hipSuccess)
-        return CONV_I8_ERR_HIP;
-    if (log_enabled())
-        fprintf(stderr, "conv_i8 (requant): %s\n", describe(pb, pl).c_str());
-    st = run(pb, pl, image_ptr, filter_ptr, out_ptr, ws, s, rq);
-    if (ws && hipFreeAsync(ws, s) != hipSuccess && st == CONV_I8_OK)
-        st = CONV_I8_ERR_HIP;
-    return st;
+    return entry_run(image, image_ptr, filter, filter_ptr, out, out_ptr, pre_padding, post_padding,
+                     stride, dilation, dt, mode, rq, false, workspace, workspace_bytes, stream);
 }
 
 const char *conv_i8_status_string(conv_i8_status_t status)

@@ -213,7 +213,7 @@ __global__ __launch_bounds__(64 * WGM * WGN * KSPL) void conv_footprint3x3_kerne
 
     // uniform per-tap offsets: footprint bytes (read side), filter bytes (load side)
     auto tap_read = [&](int t) { return ((t / 3) * a.dilH * a.Pr + (t % 3) * a.dilW * 5) * 16; };
-    auto tap_flt = [&](int t) { return (t / 3) * a.fR + (t % 3) * a.fS; };
+    auto tap_flt = [&](int t) { return a.flt0 + (t / 3) * a.fR + (t % 3) * a.fS; };
 
     // Loads of stage (block cb, tap t) into ring slot `slot`, plus the
     // footprint pieces of block cb+1 that ride on tap t.  Past the last block

@@ -141,7 +141,7 @@ __global__ __launch_bounds__(64 * WGM * WGN) void conv_igemm_kernel(IgemmArgs a)
         rdh = live ? r * a.dilH : -0x20000000;  // dead stage: every row fails the bounds test
         sdw = s * a.dilW;
         itoff = rdh * a.sH + sdw * a.sW + cpos;
-        ftoff = live ? r * a.fR + s * a.fS + cpos : kOutOfRange;
+        ftoff = live ? a.flt0 + r * a.fR + s * a.fS + cpos : kOutOfRange;
         lbase = smem_lds + slot * STAGE + wave * 1024;
     };
     auto dma_one = [&](int i) {  // i < LPS, compile-time after unrolling

@@ -39,7 +39,10 @@ struct IgemmArgs {
     int N, H, W, C;      // C: channels as stored (multiple of 16)
     int sN, sH, sW;      // image strides in bytes (channel stride is 1)
     int K, R, S;
-    int fK, fR, fS;      // filter strides in bytes (channel stride is 1)
+    int fK, fR, fS;      // filter strides in bytes (channel stride is 1); fR, fS are
+                         // negative for true convolution (taps read in reverse)
+    int flt0;            // byte offset of tap (r, s) = (0, 0) as the kernels read it:
+                         // 0, or (R-1)*|fR| + (S-1)*|fS| for true convolution
     int P, Q, PQ, M;     // M = N*P*Q
     int strH, strW, dilH, dilW, padH, padW;
     int oN, oK, oP, oQ;  // output strides in elements (one launch spans < 2^31 bytes)

@@ -275,3 +275,42 @@ def test_requant_workspace_matches_plain():
                                                   c.stride, c.dilation)
     assert n8 == n32 > 0
     assert _call_rq(a8, ci8.Requant(None, 1.0, None, 0), ws_bytes=n8 - 1, ws=FAKE) == 10
+
+
+def _call_ex(a, mode, rq, ws_bytes=0, ws=None, xp=FAKE, wp=FAKE, yp=FAKE):
+    p = ci8._params(a["pre"], a["post"], a["stride"], a["dil"], None)
+    return ci8.lib.conv_fprop_i8_ex_ws(
+        ctypes.byref(a["x"]), xp, ctypes.byref(a["w"]), wp, ctypes.byref(a["y"]), yp, *p, mode,
+        ctypes.byref(rq) if rq is not None else None, ws, ctypes.c_size_t(ws_bytes), None)
+
+
+def test_ex_entry_argument_errors():
+    """The general entry: a known mode, INT32 output without a requantisation
+    block, INT8 output with one; all checked on the host."""
+    c = wl.case("bottleneck_3x3_n32_c128_28")
+    a32 = _args(c)
+    a8 = _args(c, y=ci8.desc(c.out.dims, c.out.strides, ci8.DT_INT8))
+    rq = ci8.Requant(None, 1.0, None, 0)
+    assert _call_ex(a32, 2, None) == 5                    # unknown mode
+    assert _call_ex(a32, -1, None) == 5
+    assert _call_ex(a32, 0, rq) == 5                      # INT32 output with a block
+    assert _call_ex(a8, 1, None) == 1                     # INT8 output without one
+    a16 = _args(c, y=ci8.desc(c.out.dims, c.out.strides, 3))
+    assert _call_ex(a16, 0, None) == 2                    # neither INT32 nor INT8
+    # null output pointer is reported after the arguments check out
+    assert _call_ex(a32, 1, None, yp=None) == 1
+    for mode in (0, 1):
+        for a in (a32, a8):
+            n = ci8.conv_fprop_i8_ex_workspace_size(a["x"], a["w"], a["y"], c.pre, c.post,
+                                                    c.stride, c.dilation, mode=mode)
+            assert n == 0
+    c = wl.case("dilated_asym_n16_c96_64x48")
+    a = _args(c)
+    n0 = ci8.conv_fprop_i8_workspace_size(a["x"], a["w"], a["y"], c.pre, c.post, c.stride, c.dilation)
+    n1 = ci8.conv_fprop_i8_ex_workspace_size(a["x"], a["w"], a["y"], c.pre, c.post, c.stride,
+                                             c.dilation, mode=1)
+    assert n1 == n0 > 0
+    with pytest.raises(ci8.ConvI8Error) as e:
+        ci8.conv_fprop_i8_ex_workspace_size(a["x"], a["w"], a["y"], c.pre, c.post, c.stride,
+                                            c.dilation, mode=3)
+    assert e.value.name == "CONV_I8_ERR_PARAM"
