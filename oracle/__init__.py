@@ -25,7 +25,7 @@ import torch
 from . import build as _build
 
 __all__ = ["OracleError", "Oracle", "load", "out_dims", "conv_fprop", "conv_fprop_points",
-           "conv_fprop_requant", "requant_values", "max_threads"]
+           "conv_fprop_requant", "requant_values", "conv_dgrad", "max_threads"]
 
 _ERRORS = {
     1: "bad argument (null pointer, negative size, stride/dilation < 1, negative padding)",
@@ -77,6 +77,8 @@ class Oracle:
         lib.oracle_requant_values.argtypes = [P, P, ctypes.c_int64, P, ctypes.c_float, P,
                                               ctypes.c_int, P]
         lib.oracle_requant_values.restype = ctypes.c_int
+        lib.oracle_conv_dgrad.argtypes = [P] * 13 + [ctypes.c_int, ctypes.c_int]
+        lib.oracle_conv_dgrad.restype = ctypes.c_int
         lib.oracle_max_threads.argtypes = []
         lib.oracle_max_threads.restype = ctypes.c_int
         self.lib = lib
@@ -187,6 +189,29 @@ class Oracle:
         return res
 
 
+    def conv_dgrad(self, dy: torch.Tensor, w: torch.Tensor, dx_dims=None, pre=0, post=0,
+                   stride=1, dil=1, out: Optional[torch.Tensor] = None, threads: int = 0,
+                   mode: int = 0) -> torch.Tensor:
+        """dX (int32 [N,C,H,W]) of the loss dY (int8 [N,K,P,Q]) through
+        filter w (int8 [K,C,R,S]).  The image size comes from ``out`` or
+        ``dx_dims`` (several H give the same P when the stride exceeds 1)."""
+        _check_cpu(dy, torch.int8, "dy")
+        _check_cpu(w, torch.int8, "w")
+        if out is None:
+            if dx_dims is None:
+                raise ValueError("give dx_dims or out")
+            out = torch.empty(tuple(dx_dims), dtype=torch.int32)
+        _check_cpu(out, torch.int32, "out")
+        rc = self.lib.oracle_conv_dgrad(
+            ctypes.c_void_p(dy.data_ptr()), _v4(dy.shape), _v4(dy.stride()),
+            ctypes.c_void_p(w.data_ptr()), _v4(w.shape), _v4(w.stride()),
+            ctypes.c_void_p(out.data_ptr()), _v4(out.shape), _v4(out.stride()),
+            _v2(pre), _v2(post), _v2(stride), _v2(dil), int(mode), int(threads))
+        if rc:
+            raise OracleError(rc)
+        return out
+
+
 def _nchan(scale, bias) -> int:
     n = [len(np.asarray(v).reshape(-1)) for v in (scale, bias) if v is not None]
     return min(n)
@@ -246,6 +271,10 @@ def conv_fprop_requant(*a, **k):
 
 def requant_values(*a, **k):
     return load().requant_values(*a, **k)
+
+
+def conv_dgrad(*a, **k):
+    return load().conv_dgrad(*a, **k)
 
 
 def max_threads() -> int:

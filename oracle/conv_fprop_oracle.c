@@ -319,6 +319,96 @@ int oracle_conv_fprop_requant(const int8_t *x, const int64_t xdims[4], const int
     return overflow ? ORACLE_ERR_OVERFLOW : ORACLE_OK;
 }
 
+/*
+ * Data gradient (cuDNN "Convolutions" page, section "Convolution Dgrad": the
+ * gradient of the loss with respect to the image, for the same padding,
+ * stride, dilation and mode as the forward pass).  Read as the adjoint of
+ * the forward sum above: each forward term X[n,c,h,w] * W[k,c,r,s] added to
+ * Y[n,k,p,q] sends dY[n,k,p,q] * W[k,c,r,s] back to dX[n,c,h,w]:
+ *
+ *   dX[n,c,h,w] = sum_{k,r,s} dY[n,k,p,q] * W[k,c,r',s']
+ *     over the taps with h + pre_h - r*dil_h = p*stride_h, 0 <= p < P
+ *     (and likewise for w, q), (r',s') = (r,s), or (R-1-r,S-1-s) in mode 1.
+ *
+ * dy is [N,K,P,Q] int8, w [K,C,R,S] int8, dx [N,C,H,W] int32; P and Q must
+ * be the forward output size for H and W.  One output element is summed by
+ * one thread over k, then r, then s; 64-bit sums.
+ */
+static int64_t oracle_dgrad_point(const int8_t *dy, const int64_t dd[4], const int64_t ds[4],
+                                  const int8_t *w, const int64_t wd[4], const int64_t ws[4],
+                                  int64_t n, int64_t c, int64_t h, int64_t x,
+                                  const int64_t pre[2], const int64_t stride[2],
+                                  const int64_t dil[2], int mode)
+{
+    const int64_t K = wd[0], R = wd[2], S = wd[3], P = dd[2], Q = dd[3];
+    int64_t acc = 0;
+    for (int64_t k = 0; k < K; ++k) {
+        for (int64_t r = 0; r < R; ++r) {
+            const int64_t pn = h + pre[0] - r * dil[0];     /* = p * stride_h */
+            if (pn < 0 || pn % stride[0] != 0 || pn / stride[0] >= P)
+                continue;
+            const int64_t p = pn / stride[0];
+            const int64_t fr = mode ? R - 1 - r : r;
+            for (int64_t s = 0; s < S; ++s) {
+                const int64_t qn = x + pre[1] - s * dil[1];
+                if (qn < 0 || qn % stride[1] != 0 || qn / stride[1] >= Q)
+                    continue;
+                const int64_t q = qn / stride[1];
+                const int64_t fs = mode ? S - 1 - s : s;
+                acc += (int64_t)dy[n * ds[0] + k * ds[1] + p * ds[2] + q * ds[3]] *
+                       (int64_t)w[k * ws[0] + c * ws[1] + fr * ws[2] + fs * ws[3]];
+            }
+        }
+    }
+    return acc;
+}
+
+int oracle_conv_dgrad(const int8_t *dy, const int64_t dydims[4], const int64_t dystr[4],
+                      const int8_t *w, const int64_t wdims[4], const int64_t wstr[4],
+                      int32_t *dx, const int64_t dxdims[4], const int64_t dxstr[4],
+                      const int64_t pre[2], const int64_t post[2],
+                      const int64_t stride[2], const int64_t dil[2], int mode, int nthreads)
+{
+    int64_t fwd[4];
+    if (!dydims || !dystr || !wstr || !dxdims || !dxstr)
+        return ORACLE_ERR_ARG;
+    /* the forward problem dX would give: its output must be dY's shape */
+    int rc = oracle_out_dims(dxdims, wdims, pre, post, stride, dil, fwd);
+    if (rc != ORACLE_OK)
+        return rc;
+    for (int i = 0; i < 4; ++i)
+        if (dydims[i] != fwd[i])
+            return ORACLE_ERR_OUT_DIMS;
+    if ((!dy && oracle_elems(dydims) > 0) || (!w && oracle_elems(wdims) > 0) ||
+        (!dx && oracle_elems(dxdims) > 0))
+        return ORACLE_ERR_ARG;
+
+    const int64_t N = dxdims[0], C = dxdims[1], H = dxdims[2], W = dxdims[3];
+    int overflow = 0;
+#ifdef _OPENMP
+    if (nthreads > 0)
+        omp_set_num_threads(nthreads);
+#else
+    (void)nthreads;
+#endif
+#pragma omp parallel for collapse(2) schedule(dynamic, 1) reduction(| : overflow)
+    for (int64_t n = 0; n < N; ++n) {
+        for (int64_t ci = 0; ci < C; ++ci) {
+            for (int64_t h = 0; h < H; ++h) {
+                for (int64_t x = 0; x < W; ++x) {
+                    int64_t acc = oracle_dgrad_point(dy, dydims, dystr, w, wdims, wstr,
+                                                     n, ci, h, x, pre, stride, dil, mode);
+                    if (acc < INT32_MIN || acc > INT32_MAX)
+                        overflow = 1;
+                    dx[n * dxstr[0] + ci * dxstr[1] + h * dxstr[2] + x * dxstr[3]] =
+                        (int32_t)(uint32_t)(uint64_t)acc;
+                }
+            }
+        }
+    }
+    return overflow ? ORACLE_ERR_OVERFLOW : ORACLE_OK;
+}
+
 /* Threads an OpenMP parallel region gets by default (1 without OpenMP). */
 int oracle_max_threads(void)
 {

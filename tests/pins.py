@@ -20,6 +20,10 @@ broken builds of the oracle.
   with padding by ``numpy.pad``, dilation by zero insertion and stride by
   subsampling; and against the brute force above fed the filter reversed
   along both spatial axes.
+* the data gradient (dgrad) is checked against float64 autograd of torch's
+  conv2d with respect to the image (exact for these integer sums), and by the
+  adjoint identity <fprop(X, W), dY> = <X, dgrad(dY, W)> in int64 against
+  the pinned forward oracle, in both modes.
 * ``exact_requant`` evaluates the requantising INT8 epilogue with exact
   rational arithmetic (``fractions.Fraction``): the fused multiply-add is the
   exact value ``acc*s + b`` rounded once to the nearest binary32 (ties to an
@@ -471,8 +475,58 @@ def check_convolution_mode(orc) -> None:
     assert np.array_equal(q8, want)
 
 
+def autograd_dgrad(dy: torch.Tensor, w: torch.Tensor, xdims, pre, post, stride, dil) -> torch.Tensor:
+    """d/dX of sum(conv2d(pad(X), W) * dY) in float64 (cross-correlation)."""
+    x = torch.zeros(tuple(xdims), dtype=torch.float64, requires_grad=True)
+    y = F.conv2d(F.pad(x, (pre[1], post[1], pre[0], post[0])), w.to(torch.float64),
+                 stride=tuple(stride), dilation=tuple(dil))
+    (g,) = torch.autograd.grad(y, x, dy.to(torch.float64))
+    return g.round().to(torch.int64)
+
+
+def check_dgrad(orc) -> None:
+    """dgrad = float64 autograd of the forward (mode 0; mode 1 with the filter
+    reversed), and the adjoint identity against the forward oracle, on random
+    problems with padding, stride (up to 3) and dilation."""
+    rng = np.random.default_rng(41)
+    done = 0
+    while done < 40:
+        N, C, K = (int(v) for v in rng.integers(1, 4, 3))
+        H, W = (int(v) for v in rng.integers(1, 10, 2))
+        R, S = (int(v) for v in rng.integers(1, 4, 2))
+        pre = tuple(int(v) for v in rng.integers(0, 3, 2))
+        post = tuple(int(v) for v in rng.integers(0, 3, 2))
+        st = tuple(int(v) for v in rng.integers(1, 4, 2))
+        dl = tuple(int(v) for v in rng.integers(1, 3, 2))
+        if H + pre[0] + post[0] - dl[0] * (R - 1) - 1 < 0 or W + pre[1] + post[1] - dl[1] * (S - 1) - 1 < 0:
+            continue
+        done += 1
+        x = rand_i8(rng, (N, C, H, W))
+        w = rand_i8(rng, (K, C, R, S))
+        yd = orc.out_dims(x.shape, w.shape, pre, post, st, dl)
+        dy = rand_i8(rng, yd)
+        for mode in (0, 1):
+            dx = orc.conv_dgrad(dy, w, x.shape, pre, post, st, dl, mode=mode).to(torch.int64)
+            wm = w if mode == 0 else w.flip(2, 3).contiguous()
+            assert torch.equal(dx, autograd_dgrad(dy, wm, x.shape, pre, post, st, dl)), (done, mode)
+            y = orc.conv_fprop(x, w, pre, post, st, dl, mode=mode).to(torch.int64)
+            assert int((y * dy.to(torch.int64)).sum()) == int((x.to(torch.int64) * dx).sum())
+    # strided output and a dy view with gaps
+    x = rand_i8(rng, (2, 3, 7, 6))
+    w = rand_i8(rng, (4, 3, 3, 3))
+    yd = orc.out_dims(x.shape, w.shape, (1, 1), (1, 1), (2, 2), (1, 1))
+    big = rand_i8(rng, (yd[0], yd[1], yd[2], 2 * yd[3]))
+    dy = big[..., ::2]
+    base = torch.full((2, 7, 6, 2 * 3), 5, dtype=torch.int32)
+    out = base[..., ::2].permute(0, 3, 1, 2)
+    orc.conv_dgrad(dy, w, None, (1, 1), (1, 1), (2, 2), (1, 1), out=out)
+    assert torch.equal(out.to(torch.int64),
+                       autograd_dgrad(dy.contiguous(), w, x.shape, (1, 1), (1, 1), (2, 2), (1, 1)))
+    assert (base[..., 1::2] == 5).all()
+
+
 QUICK_CHECKS = [
     check_random_vs_brute_force, check_offcentre_delta, check_identity_1x1, check_ones_count,
     check_constant_min, check_layouts, check_metamorphic, check_points, check_requant_exact,
-    check_requant_conv, check_convolution_mode,
+    check_requant_conv, check_convolution_mode, check_dgrad,
 ]

@@ -116,6 +116,10 @@ def test_convolution_mode(orc):
     pins.check_convolution_mode(orc)
 
 
+def test_dgrad(orc):
+    pins.check_dgrad(orc)
+
+
 @pytest.mark.parametrize("name", wl.CASE_ORDER)
 def test_workloads_vs_f64_library_conv(orc, name):
     """Oracle == float64 torch conv2d on every workload at full size."""
@@ -182,6 +186,11 @@ MUTATIONS = [
     ("filter flipped in cross-correlation", "fr = mode ? R - 1 - r : r;", "fr = R - 1 - r;"),
     ("convolution mode flips rows only", "fs = mode ? S - 1 - s : s;", "fs = s;"),
     ("convolution mode flips nothing", "fr = mode ? R - 1 - r : r;", "fr = r;"),
+    ("dgrad ignores the stride divisibility", "pn % stride[0] != 0 || ", ""),
+    ("dgrad pre-padding sign", "h + pre[0] - r * dil[0]", "h - pre[0] - r * dil[0]"),
+    ("dgrad column dilation dropped", "x + pre[1] - s * dil[1]", "x + pre[1] - s"),
+    ("dgrad last row of dY dropped", "pn / stride[0] >= P", "pn / stride[0] >= P - 1"),
+    ("dgrad mode ignored", "const int64_t fs = mode ? S - 1 - s : s;\n                acc", "const int64_t fs = s;\n                acc"),
     ("unsigned widening of int8", "const int64_t xv = x[", "const int64_t xv = (uint8_t)x["),
     ("last channel dropped", "for (int64_t c = 0; c < C; ++c)", "for (int64_t c = 0; c + 1 < C; ++c)"),
     ("first filter row dropped", "for (int64_t r = 0; r < R; ++r)", "for (int64_t r = 1; r < R; ++r)"),
