@@ -300,6 +300,63 @@ conv_i8_status_t conv_fprop_i8_ex_ws(const conv_i8_desc_t *image, const void *im
                                      void *workspace, size_t workspace_bytes,
                                      void *stream);
 
+/*
+ * Data gradient (cuDNN "Convolutions" page, section "Convolution Dgrad": the
+ * gradient with respect to the image during backpropagation, with the same
+ * pre/post padding, stride, dilation and convolution mode as the forward
+ * pass).  Read as the adjoint of conv_fprop: every forward term
+ * X[n,c,h,w] * W[k,c,r,s] added to Y[n,k,p,q] returns dY[n,k,p,q] * W[k,c,r,s]
+ * to dX[n,c,h,w]:
+ *
+ *   dX[n,c,h,w] = sum_{k,r,s} dY[n,k,p,q] * W[k,c,r',s']
+ *       over the taps with h + pre_h - r*dil_h = p*stride_h, 0 <= p < P,
+ *       and w + pre_w - s*dil_w = q*stride_w, 0 <= q < Q;
+ *       (r',s') = (r,s), or (R-1-r, S-1-s) for CONV_I8_MODE_CONVOLUTION.
+ *
+ * loss (dY) is INT8 [N,K,P,Q], filter INT8 [K,C,R,S], dx INT32 [N,C,H,W];
+ * [P, Q] must be the forward output size of [H, W] (CONV_I8_ERR_OUT_DIMS
+ * otherwise; with stride > 1 several H give one P, so dx's dims decide).
+ * Exact int32 sums while K*R*S <= 131071 (CONV_I8_ERR_RANGE otherwise).  Any
+ * strides; dx must not overlap itself.  The work is stride_h*stride_w
+ * forward convolutions, one per residue class of (h, w), each a stride-1
+ * true convolution of dY with the filter transposed to [C, K, ...] and
+ * subsampled to the taps that reach that class; they run one after another
+ * on `stream` and share the workspace.  Errors and stream behaviour as
+ * conv_fprop_i8_ws; never allocates, never synchronises.
+ */
+conv_i8_status_t conv_dgrad_i8_workspace_size(const conv_i8_desc_t *loss, const void *loss_ptr,
+                                              const conv_i8_desc_t *filter,
+                                              const void *filter_ptr,
+                                              const conv_i8_desc_t *dx,
+                                              const int64_t pre_padding[2],
+                                              const int64_t post_padding[2],
+                                              const int64_t stride[2],
+                                              const int64_t dilation[2],
+                                              int32_t mode,
+                                              size_t *workspace_bytes);
+
+conv_i8_status_t conv_dgrad_i8_ws(const conv_i8_desc_t *loss, const void *loss_ptr,
+                                  const conv_i8_desc_t *filter, const void *filter_ptr,
+                                  const conv_i8_desc_t *dx, void *dx_ptr,
+                                  const int64_t pre_padding[2],
+                                  const int64_t post_padding[2],
+                                  const int64_t stride[2],
+                                  const int64_t dilation[2],
+                                  int32_t mode,
+                                  void *workspace, size_t workspace_bytes,
+                                  void *stream);
+
+/* conv_dgrad_i8_ws with its workspace taken stream-ordered (hipMallocAsync). */
+conv_i8_status_t conv_dgrad_i8(const conv_i8_desc_t *loss, const void *loss_ptr,
+                               const conv_i8_desc_t *filter, const void *filter_ptr,
+                               const conv_i8_desc_t *dx, void *dx_ptr,
+                               const int64_t pre_padding[2],
+                               const int64_t post_padding[2],
+                               const int64_t stride[2],
+                               const int64_t dilation[2],
+                               int32_t mode,
+                               void *stream);
+
 /* Static string naming a status code. */
 const char *conv_i8_status_string(conv_i8_status_t status);
 

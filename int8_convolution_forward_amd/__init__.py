@@ -30,7 +30,8 @@ __all__ = [
     "conv_fprop_i8_out_dims", "conv_fprop_i8_workspace_size", "conv_fprop_i8_plan",
     "conv_fprop_i8_requant", "conv_fprop_i8_requant_ws", "conv_fprop_i8_requant_plain",
     "conv_fprop_i8_requant_workspace_size", "Requant", "conv_fprop_i8_ex_ws",
-    "conv_fprop_i8_ex_workspace_size", "conv_fprop_i8_mode", "MODE_CROSS_CORRELATION",
+    "conv_fprop_i8_ex_workspace_size", "conv_fprop_i8_mode", "conv_dgrad_i8",
+    "conv_dgrad_i8_ws", "conv_dgrad_i8_workspace_size", "conv_dgrad_i8_plain", "MODE_CROSS_CORRELATION",
     "MODE_CONVOLUTION",
     "status_string", "LIB_PATH", "DT_INT8", "DT_INT32", "MAX_REDUCTION", "lib",
 ]
@@ -96,12 +97,17 @@ lib.conv_fprop_i8_ex_workspace_size.argtypes = [_DP, _P, _DP, _P, _DP, _V2, _V2,
                                                 ctypes.c_int32, ctypes.POINTER(ctypes.c_size_t)]
 lib.conv_fprop_i8_ex_ws.argtypes = [_DP, _P, _DP, _P, _DP, _P, _V2, _V2, _V2, _V2, ctypes.c_int32,
                                     _RQ, _P, ctypes.c_size_t, _P]
+lib.conv_dgrad_i8_workspace_size.argtypes = [_DP, _P, _DP, _P, _DP, _V2, _V2, _V2, _V2,
+                                             ctypes.c_int32, ctypes.POINTER(ctypes.c_size_t)]
+lib.conv_dgrad_i8_ws.argtypes = [_DP, _P, _DP, _P, _DP, _P, _V2, _V2, _V2, _V2, ctypes.c_int32, _P,
+                                 ctypes.c_size_t, _P]
+lib.conv_dgrad_i8.argtypes = [_DP, _P, _DP, _P, _DP, _P, _V2, _V2, _V2, _V2, ctypes.c_int32, _P]
 lib.conv_i8_status_string.argtypes = [ctypes.c_int]
 lib.conv_i8_status_string.restype = ctypes.c_char_p
 for _f in ("conv_fprop_i8_out_dims", "conv_fprop_i8_workspace_size", "conv_fprop_i8_ws",
            "conv_fprop_i8", "conv_fprop_i8_plan", "conv_fprop_i8_requant_workspace_size",
            "conv_fprop_i8_requant_ws", "conv_fprop_i8_requant", "conv_fprop_i8_ex_workspace_size",
-           "conv_fprop_i8_ex_ws"):
+           "conv_fprop_i8_ex_ws", "conv_dgrad_i8_workspace_size", "conv_dgrad_i8_ws", "conv_dgrad_i8"):
     getattr(lib, _f).restype = ctypes.c_int
 
 
@@ -393,3 +399,52 @@ def conv_fprop_i8_mode(x: torch.Tensor, w: torch.Tensor, mode: int, out: Optiona
     ws = torch.empty(n, dtype=torch.uint8, device=out.device) if n else None
     return conv_fprop_i8_ex_ws(x, w, out, ws, mode, rq, pre_padding, post_padding, stride,
                                dilation, padding, stream)
+
+
+def conv_dgrad_i8_workspace_size(dy, w, dx, pre_padding=0, post_padding=0, stride=1, dilation=1,
+                                 padding=None, mode: int = 0) -> int:
+    pre, post, st, dl = _params(pre_padding, post_padding, stride, dilation, padding)
+    n = ctypes.c_size_t()
+    dp = _ptr(dy) if isinstance(dy, torch.Tensor) else None
+    wp = _ptr(w) if isinstance(w, torch.Tensor) else None
+    _check(lib.conv_dgrad_i8_workspace_size(
+        ctypes.byref(_as_desc(dy)), dp, ctypes.byref(_as_desc(w)), wp, ctypes.byref(_as_desc(dx)),
+        pre, post, st, dl, int(mode), ctypes.byref(n)))
+    return int(n.value)
+
+
+def conv_dgrad_i8_ws(dy: torch.Tensor, w: torch.Tensor, dx: torch.Tensor,
+                     workspace: Optional[torch.Tensor], pre_padding=0, post_padding=0, stride=1,
+                     dilation=1, padding=None, mode: int = 0, stream=None) -> torch.Tensor:
+    """Direct call of the dgrad C entry with an explicit workspace."""
+    pre, post, st, dl = _params(pre_padding, post_padding, stride, dilation, padding)
+    ws_ptr = _ptr(workspace)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(lib.conv_dgrad_i8_ws(
+        ctypes.byref(desc(dy)), _ptr(dy), ctypes.byref(desc(w)), _ptr(w), ctypes.byref(desc(dx)),
+        _ptr(dx), pre, post, st, dl, int(mode), ws_ptr, ctypes.c_size_t(ws_bytes),
+        _stream_handle(stream)))
+    return dx
+
+
+def conv_dgrad_i8_plain(dy: torch.Tensor, w: torch.Tensor, dx: torch.Tensor, pre_padding=0,
+                        post_padding=0, stride=1, dilation=1, padding=None, mode: int = 0,
+                        stream=None) -> torch.Tensor:
+    """The dgrad C entry that takes its own workspace (hipMallocAsync)."""
+    pre, post, st, dl = _params(pre_padding, post_padding, stride, dilation, padding)
+    _check(lib.conv_dgrad_i8(
+        ctypes.byref(desc(dy)), _ptr(dy), ctypes.byref(desc(w)), _ptr(w), ctypes.byref(desc(dx)),
+        _ptr(dx), pre, post, st, dl, int(mode), _stream_handle(stream)))
+    return dx
+
+
+def conv_dgrad_i8(dy: torch.Tensor, w: torch.Tensor, dx: torch.Tensor, pre_padding=0,
+                  post_padding=0, stride=1, dilation=1, padding=None, mode: int = 0,
+                  stream=None) -> torch.Tensor:
+    """dX (int32 [N,C,H,W], written into ``dx``, which fixes H and W) of the
+    loss dY (int8 [N,K,P,Q]) through the filter w (int8 [K,C,R,S])."""
+    n = conv_dgrad_i8_workspace_size(dy, w, dx, pre_padding, post_padding, stride, dilation,
+                                     padding, mode)
+    ws = torch.empty(n, dtype=torch.uint8, device=dx.device) if n else None
+    return conv_dgrad_i8_ws(dy, w, dx, ws, pre_padding, post_padding, stride, dilation, padding,
+                            mode, stream)

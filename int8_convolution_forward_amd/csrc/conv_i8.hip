@@ -17,6 +17,7 @@
 
 #include <algorithm>
 #include <mutex>
+#include <numeric>
 #include <string>
 
 #include "footprint_kernel.hpp"
@@ -984,6 +985,273 @@ conv_i8_status_t ex_out_dtype(const conv_i8_desc_t *out, const conv_i8_requant_t
     return CONV_I8_ERR_DTYPE;
 }
 
+// ---------------------------------------------------------------------------
+// Data gradient (dgrad) as forward convolutions over stride phases.
+//
+// dX[n,c,h,w] sums dY[n,k,p,q] * W[k,c,r,s] over the taps with
+// h + pre_h - r*dil_h = p*stride_h (and likewise along w).  For the rows h of
+// one residue ph = h mod stride_h, the taps that reach them are
+// r = r0 + t*j (t = stride_h / g, g = gcd(dil_h, stride_h)), and row
+// i = (h - ph) / stride_h reads dY row i + e - j*(dil_h / g): a stride-1
+// cross-correlation of dY with the reversed sub-filter, dilation dil_h / g.
+// Each (ph, pw) phase is one forward call on views: image = dY (channels K),
+// filter = W transposed to [C, K, .., ..] and subsampled by t, output = the
+// phase's rows and columns of dX.
+// ---------------------------------------------------------------------------
+struct DgradDim {
+    bool zero = false;             // no tap reaches these rows: they are 0
+    int64_t rows = 0;              // dX rows of the phase (Hi)
+    int64_t base = 0, step = 1;    // filter taps used: base + step*j, j < taps
+    int64_t taps = 0;
+    int64_t dil = 1;               // dilation of the phase call
+    int64_t crop = 0, used = 0;    // dY rows [crop, crop + used) are read
+    int64_t pre = 0, post = 0;     // padding of the phase call
+};
+
+// One spatial dim of one phase.  flip: the dgrad is of the true-convolution
+// forward (taps reversed), so the sub-filter is read forwards.
+DgradDim dgrad_dim(int64_t ph, int64_t len, int64_t out_len_, int64_t pre, int64_t st, int64_t dil,
+                   int64_t R, bool flip)
+{
+    DgradDim d;
+    d.rows = ph < len ? (len - ph + st - 1) / st : 0;
+    if (d.rows == 0)
+        return d;
+    const int64_t g = std::gcd(dil, st);
+    const int64_t t = st / g;
+    int64_t r0 = -1;
+    for (int64_t r = 0; r < std::min(R, t); ++r)
+        if ((ph + pre - r * dil) % st == 0) {
+            r0 = r;
+            break;
+        }
+    if (r0 < 0) {
+        d.zero = true;
+        return d;
+    }
+    d.taps = (R - r0 + t - 1) / t;
+    d.step = t;
+    d.dil = dil / g;
+    // forward call read in reverse (convolution mode) for the plain dgrad;
+    // with flip the reversed filter reverses back: read from the far end
+    d.base = flip ? R - 1 - r0 - t * (d.taps - 1) : r0;
+    const int64_t e = (ph + pre - r0 * dil) / st;       // exact
+    int64_t pad = (d.taps - 1) * d.dil - e;
+    int64_t used = out_len_;
+    if (pad < 0) {
+        d.crop = -pad;
+        used -= d.crop;
+        pad = 0;
+    }
+    if (used <= 0) {
+        d.zero = true;
+        return d;
+    }
+    int64_t post = d.rows - used - pad + d.dil * (d.taps - 1);
+    if (post < 0) {
+        used += post;
+        post = 0;
+    }
+    if (used <= 0) {
+        d.zero = true;
+        return d;
+    }
+    d.used = used;
+    d.pre = pad;
+    d.post = post;
+    return d;
+}
+
+conv_i8_desc_t make_desc(int32_t dtype, const int64_t d[4], const int64_t st[4])
+{
+    conv_i8_desc_t r;
+    r.dtype = dtype;
+    r.ndim = 4;
+    for (int i = 0; i < 4; ++i) {
+        r.dims[i] = d[i];
+        r.strides[i] = st[i];
+    }
+    return r;
+}
+
+struct DgradProblem {
+    T4 dy, w, dx;
+    int64_t N, K, C, R, S, H, W, P, Q;
+    int64_t pre[2], post[2], str[2], dil[2];
+};
+
+conv_i8_status_t dgrad_analyze(const conv_i8_desc_t *loss, const conv_i8_desc_t *filter,
+                               const conv_i8_desc_t *dx, const int64_t *pre, const int64_t *post,
+                               const int64_t *stride, const int64_t *dil, int32_t mode,
+                               DgradProblem *dp)
+{
+    conv_i8_status_t st;
+    if ((st = read_desc(loss, CONV_I8_DT_INT8, &dp->dy)) != CONV_I8_OK ||
+        (st = read_desc(filter, CONV_I8_DT_INT8, &dp->w)) != CONV_I8_OK ||
+        (st = read_desc(dx, CONV_I8_DT_INT32, &dp->dx)) != CONV_I8_OK)
+        return st;
+    Problem tmp;
+    if ((st = read_params(pre, post, stride, dil, &tmp)) != CONV_I8_OK)
+        return st;
+    if (mode != CONV_I8_MODE_CROSS_CORRELATION && mode != CONV_I8_MODE_CONVOLUTION)
+        return CONV_I8_ERR_PARAM;
+    for (int i = 0; i < 2; ++i) {
+        dp->pre[i] = tmp.pre[i];
+        dp->post[i] = tmp.post[i];
+        dp->str[i] = tmp.str[i];
+        dp->dil[i] = tmp.dil[i];
+    }
+    dp->N = dp->dx.d[0];
+    dp->C = dp->dx.d[1];
+    dp->H = dp->dx.d[2];
+    dp->W = dp->dx.d[3];
+    dp->K = dp->w.d[0];
+    dp->R = dp->w.d[2];
+    dp->S = dp->w.d[3];
+    if (dp->R < 1 || dp->S < 1)
+        return CONV_I8_ERR_DIMS;
+    if (dp->w.d[1] != dp->C)
+        return CONV_I8_ERR_CHANNELS;
+    for (int i = 0; i < 4; ++i)
+        if (dp->dx.d[i] > kI32Max / 4 || dp->w.d[i] > kI32Max / 4 || dp->dy.d[i] > kI32Max / 4)
+            return CONV_I8_ERR_UNSUPPORTED;
+    int64_t krs;
+    if (!mul_ok(dp->K, dp->R * dp->S, &krs) || krs > CONV_I8_MAX_REDUCTION)
+        return CONV_I8_ERR_RANGE;
+    dp->P = out_len(dp->H, dp->pre[0], dp->post[0], dp->R, dp->str[0], dp->dil[0]);
+    dp->Q = out_len(dp->W, dp->pre[1], dp->post[1], dp->S, dp->str[1], dp->dil[1]);
+    if (dp->P < 1 || dp->Q < 1)
+        return CONV_I8_ERR_OUT_DIMS;
+    const int64_t want[4] = {dp->N, dp->K, dp->P, dp->Q};
+    for (int i = 0; i < 4; ++i)
+        if (dp->dy.d[i] != want[i])
+            return CONV_I8_ERR_OUT_DIMS;
+    int64_t sp;
+    if (!span_of(dp->dy, &sp) || !span_of(dp->w, &sp) || !span_of(dp->dx, &sp))
+        return CONV_I8_ERR_UNSUPPORTED;
+    if (!non_overlapping(dp->dx))
+        return CONV_I8_ERR_STRIDES;
+    return CONV_I8_OK;
+}
+
+// Visit the forward calls of a dgrad: fn(image, x_ptr, filter, w_ptr, out,
+// y_ptr, pre, post, stride, dil, mode) for every phase in order.
+template <class Fn>
+conv_i8_status_t dgrad_phases(const DgradProblem &dp, const void *dy_ptr, const void *w_ptr,
+                              void *dx_ptr, int32_t mode, Fn &&fn)
+{
+    const bool flip = mode == CONV_I8_MODE_CONVOLUTION;
+    const int32_t sub_mode = flip ? CONV_I8_MODE_CROSS_CORRELATION : CONV_I8_MODE_CONVOLUTION;
+    for (int64_t ph = 0; ph < dp.str[0]; ++ph) {
+        const DgradDim a = dgrad_dim(ph, dp.H, dp.P, dp.pre[0], dp.str[0], dp.dil[0], dp.R, flip);
+        if (a.rows == 0)
+            continue;
+        for (int64_t pw = 0; pw < dp.str[1]; ++pw) {
+            const DgradDim b = dgrad_dim(pw, dp.W, dp.Q, dp.pre[1], dp.str[1], dp.dil[1], dp.S, flip);
+            if (b.rows == 0)
+                continue;
+            const int64_t od[4] = {dp.N, dp.C, a.rows, b.rows};
+            const int64_t os[4] = {dp.dx.s[0], dp.dx.s[1], dp.str[0] * dp.dx.s[2], dp.str[1] * dp.dx.s[3]};
+            const conv_i8_desc_t out = make_desc(CONV_I8_DT_INT32, od, os);
+            void *y = dx_ptr ? (void *)((int32_t *)dx_ptr + ph * dp.dx.s[2] + pw * dp.dx.s[3]) : nullptr;
+            const int64_t one[2] = {1, 1}, zero[2] = {0, 0};
+            conv_i8_status_t st;
+            if (a.zero || b.zero) {
+                // no tap reaches this phase: a convolution over zero channels
+                // writes its zeros
+                const int64_t xd[4] = {dp.N, 0, a.rows, b.rows}, xs[4] = {0, 0, 0, 0};
+                const int64_t wd[4] = {dp.C, 0, 1, 1};
+                const conv_i8_desc_t img = make_desc(CONV_I8_DT_INT8, xd, xs);
+                const conv_i8_desc_t flt = make_desc(CONV_I8_DT_INT8, wd, xs);
+                st = fn(&img, nullptr, &flt, nullptr, &out, y, zero, zero, one, one,
+                        (int32_t)CONV_I8_MODE_CROSS_CORRELATION);
+            } else {
+                const int64_t xd[4] = {dp.N, dp.K, a.used, b.used};
+                const int64_t xs[4] = {dp.dy.s[0], dp.dy.s[1], dp.dy.s[2], dp.dy.s[3]};
+                const int64_t wd[4] = {dp.C, dp.K, a.taps, b.taps};
+                const int64_t ws[4] = {dp.w.s[1], dp.w.s[0], a.step * dp.w.s[2], b.step * dp.w.s[3]};
+                const conv_i8_desc_t img = make_desc(CONV_I8_DT_INT8, xd, xs);
+                const conv_i8_desc_t flt = make_desc(CONV_I8_DT_INT8, wd, ws);
+                const void *x = dy_ptr ? (const void *)((const int8_t *)dy_ptr + a.crop * dp.dy.s[2] +
+                                                        b.crop * dp.dy.s[3]) : nullptr;
+                const void *wp = w_ptr ? (const void *)((const int8_t *)w_ptr + a.base * dp.w.s[2] +
+                                                        b.base * dp.w.s[3]) : nullptr;
+                const int64_t pre2[2] = {a.pre, b.pre}, post2[2] = {a.post, b.post};
+                const int64_t dil2[2] = {a.dil, b.dil};
+                st = fn(&img, x, &flt, wp, &out, y, pre2, post2, one, dil2, sub_mode);
+            }
+            if (st != CONV_I8_OK)
+                return st;
+        }
+    }
+    return CONV_I8_OK;
+}
+
+conv_i8_status_t dgrad_workspace(const DgradProblem &dp, const void *dy_ptr, const void *w_ptr,
+                                 int32_t mode, size_t *bytes)
+{
+    size_t most = 0;
+    conv_i8_status_t st = dgrad_phases(
+        dp, dy_ptr, w_ptr, nullptr, mode,
+        [&](const conv_i8_desc_t *img, const void *x, const conv_i8_desc_t *flt, const void *w,
+            const conv_i8_desc_t *out, void *, const int64_t *pre, const int64_t *post,
+            const int64_t *stride, const int64_t *dil, int32_t m) {
+            size_t n = 0;
+            conv_i8_status_t s = entry_workspace_size(img, x, flt, w, out, pre, post, stride, dil,
+                                                      CONV_I8_DT_INT32, m, &n);
+            most = std::max(most, n);
+            return s;
+        });
+    *bytes = most;
+    return st;
+}
+
+conv_i8_status_t dgrad_entry(const conv_i8_desc_t *loss, const void *loss_ptr,
+                             const conv_i8_desc_t *filter, const void *filter_ptr,
+                             const conv_i8_desc_t *dx, void *dx_ptr, const int64_t *pre,
+                             const int64_t *post, const int64_t *stride, const int64_t *dil,
+                             int32_t mode, bool alloc, void *workspace, size_t workspace_bytes,
+                             void *stream)
+{
+    DgradProblem dp;
+    conv_i8_status_t st = dgrad_analyze(loss, filter, dx, pre, post, stride, dil, mode, &dp);
+    if (st != CONV_I8_OK)
+        return st;
+    if (dp.dx.elems() == 0)
+        return CONV_I8_OK;
+    if (!dx_ptr || (dp.K > 0 && ((dp.dy.elems() > 0 && !loss_ptr) || (dp.w.elems() > 0 && !filter_ptr))))
+        return CONV_I8_ERR_NULL;
+    size_t need = 0;
+    if ((st = dgrad_workspace(dp, loss_ptr, filter_ptr, mode, &need)) != CONV_I8_OK)
+        return st;
+    hipStream_t s = (hipStream_t)stream;
+    void *ws = workspace;
+    if (alloc) {
+        ws = nullptr;
+        if (need > 0 && hipMallocAsync(&ws, need, s) != hipSuccess)
+            return CONV_I8_ERR_HIP;
+    } else {
+        if (workspace_bytes < need)
+            return CONV_I8_ERR_WORKSPACE;
+        if (need > 0 && !workspace)
+            return CONV_I8_ERR_NULL;
+        if (need > 0 && ((uintptr_t)workspace & 255u) != 0)
+            return CONV_I8_ERR_WORKSPACE;
+    }
+    // the phases run one after another on the stream and share the workspace
+    st = dgrad_phases(dp, loss_ptr, filter_ptr, dx_ptr, mode,
+                      [&](const conv_i8_desc_t *img, const void *x, const conv_i8_desc_t *flt,
+                          const void *w, const conv_i8_desc_t *out, void *y, const int64_t *pre_,
+                          const int64_t *post_, const int64_t *stride_, const int64_t *dil_,
+                          int32_t m) {
+                          return entry_run(img, x, flt, w, out, y, pre_, post_, stride_, dil_,
+                                           CONV_I8_DT_INT32, m, nullptr, false, ws, need, stream);
+                      });
+    if (alloc && ws && hipFreeAsync(ws, s) != hipSuccess && st == CONV_I8_OK)
+        st = CONV_I8_ERR_HIP;
+    return st;
+}
+
 }  // namespace
 }  // namespace convi8
 
@@ -1111,6 +1379,50 @@ conv_i8_status_t conv_fprop_i8_ex_ws(const conv_i8_desc_t *image, const void *im
         return st;
     return entry_run(image, image_ptr, filter, filter_ptr, out, out_ptr, pre_padding, post_padding,
                      stride, dilation, dt, mode, rq, false, workspace, workspace_bytes, stream);
+}
+
+conv_i8_status_t conv_dgrad_i8_workspace_size(const conv_i8_desc_t *loss, const void *loss_ptr,
+                                              const conv_i8_desc_t *filter, const void *filter_ptr,
+                                              const conv_i8_desc_t *dx,
+                                              const int64_t pre_padding[2],
+                                              const int64_t post_padding[2],
+                                              const int64_t stride[2], const int64_t dilation[2],
+                                              int32_t mode, size_t *workspace_bytes)
+{
+    if (!workspace_bytes)
+        return CONV_I8_ERR_NULL;
+    DgradProblem dp;
+    conv_i8_status_t st = dgrad_analyze(loss, filter, dx, pre_padding, post_padding, stride, dilation,
+                                        mode, &dp);
+    if (st != CONV_I8_OK)
+        return st;
+    if (dp.dx.elems() == 0) {
+        *workspace_bytes = 0;
+        return CONV_I8_OK;
+    }
+    return dgrad_workspace(dp, loss_ptr, filter_ptr, mode, workspace_bytes);
+}
+
+conv_i8_status_t conv_dgrad_i8_ws(const conv_i8_desc_t *loss, const void *loss_ptr,
+                                  const conv_i8_desc_t *filter, const void *filter_ptr,
+                                  const conv_i8_desc_t *dx, void *dx_ptr,
+                                  const int64_t pre_padding[2], const int64_t post_padding[2],
+                                  const int64_t stride[2], const int64_t dilation[2], int32_t mode,
+                                  void *workspace, size_t workspace_bytes, void *stream)
+{
+    return dgrad_entry(loss, loss_ptr, filter, filter_ptr, dx, dx_ptr, pre_padding, post_padding,
+                       stride, dilation, mode, false, workspace, workspace_bytes, stream);
+}
+
+conv_i8_status_t conv_dgrad_i8(const conv_i8_desc_t *loss, const void *loss_ptr,
+                               const conv_i8_desc_t *filter, const void *filter_ptr,
+                               const conv_i8_desc_t *dx, void *dx_ptr,
+                               const int64_t pre_padding[2], const int64_t post_padding[2],
+                               const int64_t stride[2], const int64_t dilation[2], int32_t mode,
+                               void *stream)
+{
+    return dgrad_entry(loss, loss_ptr, filter, filter_ptr, dx, dx_ptr, pre_padding, post_padding,
+                       stride, dilation, mode, true, nullptr, 0, stream);
 }
 
 const char *conv_i8_status_string(conv_i8_status_t status)

@@ -314,3 +314,50 @@ def test_ex_entry_argument_errors():
         ci8.conv_fprop_i8_ex_workspace_size(a["x"], a["w"], a["y"], c.pre, c.post, c.stride,
                                             c.dilation, mode=3)
     assert e.value.name == "CONV_I8_ERR_PARAM"
+
+
+def _dgrad_args(N=2, K=8, C=16, H=9, W=7, R=3, S=3, pre=(1, 1), post=(1, 1), st=(2, 2), dl=(1, 1)):
+    D = ci8.desc
+    P = (H + pre[0] + post[0] - dl[0] * (R - 1) - 1) // st[0] + 1
+    Q = (W + pre[1] + post[1] - dl[1] * (S - 1) - 1) // st[1] + 1
+    dy = D((N, K, P, Q), (K * P * Q, 1, Q * K, K), ci8.DT_INT8)
+    w = D((K, C, R, S), (C * R * S, 1, S * C, C), ci8.DT_INT8)
+    dx = D((N, C, H, W), (C * H * W, 1, W * C, C), ci8.DT_INT32)
+    return dy, w, dx, pre, post, st, dl
+
+
+def _call_dgrad(dy, w, dx, pre, post, st, dl, mode=0, ws_bytes=0, ws=None, yp=FAKE):
+    p = ci8._params(pre, post, st, dl, None)
+    return ci8.lib.conv_dgrad_i8_ws(ctypes.byref(dy), FAKE, ctypes.byref(w), FAKE, ctypes.byref(dx),
+                                    yp, *p, mode, ws, ctypes.c_size_t(ws_bytes), None)
+
+
+def test_dgrad_argument_errors():
+    dy, w, dx, pre, post, st, dl = _dgrad_args()
+    D = ci8.desc
+    # dx INT8 or dy INT32: dtype
+    assert _call_dgrad(dy, w, D(dx.dims, dx.strides, ci8.DT_INT8), pre, post, st, dl) == 2
+    assert _call_dgrad(D(dy.dims, dy.strides, ci8.DT_INT32), w, dx, pre, post, st, dl) == 2
+    # dY's spatial size must be the forward output size of dX's
+    bad = D((2, 8, 4, 4), (128, 1, 32, 8), ci8.DT_INT8)
+    assert _call_dgrad(bad, w, dx, pre, post, st, dl) == 7
+    # channel mismatch between filter and dX
+    assert _call_dgrad(dy, w, D((2, 12, 9, 7), (756, 1, 84, 12), ci8.DT_INT32), pre, post, st, dl) == 6
+    # K*R*S beyond the exact range
+    a = _dgrad_args(K=15000, C=16)
+    assert _call_dgrad(*a) == 9
+    # unknown mode, overlapping dX
+    assert _call_dgrad(dy, w, dx, pre, post, st, dl, mode=2) == 5
+    assert _call_dgrad(dy, w, D(dx.dims, (0, 1, 7, 1), ci8.DT_INT32), pre, post, st, dl) == 8
+    # null dX pointer once everything else is right
+    assert _call_dgrad(dy, w, dx, pre, post, st, dl, yp=None) == 1
+
+
+@pytest.mark.parametrize("st,dl", [((1, 1), (1, 1)), ((2, 2), (1, 1)), ((2, 3), (2, 1)), ((4, 4), (2, 2))])
+def test_dgrad_workspace(st, dl):
+    """One forward call per stride phase; the transposed filter always needs a
+    repack, so the workspace is at least the packed filter."""
+    dy, w, dx, pre, post, _, _ = _dgrad_args(st=st, dl=dl)
+    n = ci8.conv_dgrad_i8_workspace_size(dy, w, dx, pre, post, st, dl)
+    assert n >= 16 * 8 * 9 // max(1, st[0] * st[1])
+    assert _call_dgrad(dy, w, dx, pre, post, st, dl, ws_bytes=n - 1, ws=FAKE) == 10

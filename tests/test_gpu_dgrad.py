@@ -1,0 +1,97 @@
+"""GPU parity of the data gradient (conv_dgrad_i8) against the oracle's
+dgrad (pinned to float64 autograd and the adjoint identity): bit-exact over
+the whole dX buffer, guard bands included."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads as wl
+
+pytestmark = pytest.mark.gpu
+
+GUARD = 64
+
+
+@pytest.fixture(scope="module")
+def ci8():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import int8_convolution_forward_amd as m
+    return m
+
+
+def _dev():
+    return torch.device("cuda:0")
+
+
+def run_dgrad_check(ci8, dy_storage, dyspec, w_storage, wspec, dxspec, pre, post, st, dl, mode=0,
+                    label="", entry="ws"):
+    dy_cpu = torch.as_strided(dy_storage, dyspec.dims, dyspec.strides, dyspec.offset)
+    w_cpu = torch.as_strided(w_storage, wspec.dims, wspec.strides, wspec.offset)
+    dyg = wl.to_device(dy_storage, dyspec, _dev())[1]
+    wg = wl.to_device(w_storage, wspec, _dev())[1]
+    size = dxspec.storage_size + 2 * GUARD
+    buf = torch.full((size,), wl.SENTINEL, dtype=torch.int32, device=_dev())
+    dxg = torch.as_strided(buf, dxspec.dims, dxspec.strides, dxspec.offset + GUARD)
+    print(f"[gpu] dgrad {label} dy={dyspec.dims}/{dyspec.strides} w={wspec.dims}/{wspec.strides} "
+          f"dx={dxspec.dims}/{dxspec.strides} pre={pre} post={post} stride={st} dil={dl} "
+          f"mode={mode} entry={entry}", flush=True)
+    if entry == "ws":
+        ci8.conv_dgrad_i8(dyg, wg, dxg, pre, post, st, dl, mode=mode)
+    else:
+        ci8.conv_dgrad_i8_plain(dyg, wg, dxg, pre, post, st, dl, mode=mode)
+    torch.cuda.synchronize()
+    got = buf.cpu()
+    ref = torch.full((size,), wl.SENTINEL, dtype=torch.int32)
+    rv = torch.as_strided(ref, dxspec.dims, dxspec.strides, dxspec.offset + GUARD)
+    oracle.conv_dgrad(dy_cpu, w_cpu, None, pre, post, st, dl, out=rv, mode=mode)
+    if not torch.equal(got, ref):
+        diff = (got != ref).nonzero().reshape(-1)
+        raise AssertionError(f"{label}: {diff.numel()} elements differ, first at {diff[:5].tolist()}: "
+                             f"got {got[diff[:5]].tolist()} want {ref[diff[:5]].tolist()}")
+
+
+def _rand_storage(spec, seed):
+    g = torch.Generator().manual_seed(seed)
+    return torch.randint(-128, 128, (spec.storage_size,), dtype=torch.int8, generator=g)
+
+
+@pytest.mark.parametrize("name", wl.CASE_ORDER)
+@pytest.mark.parametrize("mode", [0, 1])
+def test_workload_dgrad(ci8, name, mode):
+    """The data gradient of every workload: dY in the forward output's layout,
+    the workload's filter, dX in the image's logical dims (channels_last)."""
+    c = wl.case(name)
+    d = wl.make_inputs(c, c.seed_base + 3)
+    dyspec = wl.TensorSpec(c.out.dims, c.out.strides)
+    dxspec = wl.TensorSpec(c.image.dims, wl.channels_last_strides(c.image.dims))
+    run_dgrad_check(ci8, _rand_storage(dyspec, 5 + mode), dyspec, d["w_storage"], c.filter, dxspec,
+                    c.pre, c.post, c.stride, c.dilation, mode=mode, label=name)
+
+
+def test_random_dgrad_problems(ci8):
+    """Strides up to 4 (phases with no taps), dilation, padding larger than the
+    filter reach (cropped dY rows), non-square filters, NCHW and NHWC."""
+    rng = np.random.default_rng(43)
+    done = 0
+    while done < 40:
+        N, K, C = int(rng.integers(1, 4)), int(rng.integers(1, 70)), int(rng.integers(1, 70))
+        H, W = (int(v) for v in rng.integers(1, 20, 2))
+        R, S = (int(v) for v in rng.integers(1, 6, 2))
+        pre = tuple(int(v) for v in rng.integers(0, 5, 2))
+        post = tuple(int(v) for v in rng.integers(0, 5, 2))
+        st = tuple(int(v) for v in rng.integers(1, 5, 2))
+        dl = tuple(int(v) for v in rng.integers(1, 4, 2))
+        try:
+            od = oracle.out_dims((N, C, H, W), (K, C, R, S), pre, post, st, dl)
+        except oracle.OracleError:
+            continue
+        lay = lambda d: (wl.channels_last_strides(d) if rng.integers(0, 2) else wl.contiguous_strides(d))
+        dyspec = wl.TensorSpec(od, lay(od))
+        wspec = wl.TensorSpec((K, C, R, S), lay((K, C, R, S)))
+        dxspec = wl.TensorSpec((N, C, H, W), lay((N, C, H, W)))
+        run_dgrad_check(ci8, _rand_storage(dyspec, 100 + done), dyspec, _rand_storage(wspec, 200 + done),
+                        wspec, dxspec, pre, post, st, dl, mode=done % 2, label=f"random {done}",
+                        entry="plain" if done % 5 == 0 else "ws")
+        done += 1
