@@ -45,6 +45,9 @@ def parse():
                     default="cross_correlation",
                     help="convolution: true convolution (filter taps reversed) through the "
                          "general entry conv_fprop_i8_ex_ws")
+    ap.add_argument("--op", choices=("fprop", "dgrad"), default="fprop",
+                    help="dgrad: the data gradient of the workload (loss shaped like its output, "
+                         "INT32 result shaped like its image) through conv_dgrad_i8_ws")
     ap.add_argument("--epilogue", choices=("int32", "requant"), default="int32",
                     help="int32: the plain entry; requant: INT8 output with per-channel "
                          "scale and bias and ReLU")
@@ -77,6 +80,117 @@ def traffic_from_profiles(workload: str, launch_bytes_alg: float):
     return t.get("hbm_bytes_per_launch")
 
 
+def bench_dgrad(args, c):
+    """Whole-call timing of the data gradient: dY (INT8, the forward output's
+    dims and strides), the workload's filter, dX (INT32, the image dims,
+    channels_last); every call repacks the transposed filter and runs one
+    forward convolution per stride phase."""
+    import torch
+
+    import int8_convolution_forward_amd as ci8
+    import workloads as wl
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    d = wl.make_inputs(c, c.seed_base)
+    N, K, P, Q = c.out.dims
+    _, C, R, S = c.filter.dims
+    H, W = c.image.dims[2], c.image.dims[3]
+    ops = c.ops
+    mode = 1 if args.mode == "convolution" else 0
+    g = torch.Generator().manual_seed(c.seed_base + 91)
+    dy0 = torch.randint(-128, 128, (c.out.storage_size,), dtype=torch.int8, generator=g).to(dev)
+    w0, _ = wl.to_device(d["w_storage"], c.filter, dev)
+    dx_strides = wl.channels_last_strides(c.image.dims)
+    dx_size = wl.TensorSpec(c.image.dims, dx_strides).storage_size
+    set_bytes = dy0.numel() + w0.numel() + 4 * dx_size
+    nsets = max(2, min(128, int(args.rotate_mb * 2**20 // set_bytes) + 1))
+    sets = []
+    for _ in range(nsets):
+        dys, ws_ = dy0.clone(), w0.clone()
+        dxs = torch.empty(dx_size, dtype=torch.int32, device=dev)
+        sets.append((dys, ws_, dxs, torch.as_strided(dys, c.out.dims, c.out.strides),
+                     torch.as_strided(ws_, c.filter.dims, c.filter.strides, c.filter.offset),
+                     torch.as_strided(dxs, c.image.dims, dx_strides)))
+    ws_bytes = ci8.conv_dgrad_i8_workspace_size(sets[0][3], sets[0][4], sets[0][5], c.pre, c.post,
+                                                c.stride, c.dilation, mode=mode)
+    workspace = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream()
+    sh = ctypes.c_void_p(stream.cuda_stream)
+    params = ci8._params(c.pre, c.post, c.stride, c.dilation, None)
+    calls = [(ctypes.byref(ci8.desc(s_[3])), ctypes.c_void_p(s_[3].data_ptr()),
+              ctypes.byref(ci8.desc(s_[4])), ctypes.c_void_p(s_[4].data_ptr()),
+              ctypes.byref(ci8.desc(s_[5])), ctypes.c_void_p(s_[5].data_ptr()), *params,
+              ctypes.c_int32(mode), ctypes.c_void_p(workspace.data_ptr()) if ws_bytes else None,
+              ctypes.c_size_t(ws_bytes), sh) for s_ in sets]
+    fn = ci8.lib.conv_dgrad_i8_ws
+
+    def step(i):
+        rc = fn(*calls[i % nsets])
+        if rc != 0:
+            raise RuntimeError(ci8.status_string(rc))
+
+    print(f"bench: dgrad of {c.name}; {nsets} buffer sets of {set_bytes / 2**20:.1f} MiB, "
+          f"workspace {ws_bytes} B", file=sys.stderr, flush=True)
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    t0.record(stream)
+    for i in range(args.steps):
+        step(i)
+    t1.record(stream)
+    torch.cuda.synchronize()
+    ms = t0.elapsed_time(t1) / args.steps
+    tops = ops / (ms * 1e-3) / 1e12
+    alg_bytes = N * K * P * Q + K * C * R * S + 4 * N * C * H * W
+    ridge = INT8_PEAK_TOPS * 1e12 / (HBM_PEAK_GBS * 1e9)
+    if ops / alg_bytes >= ridge:
+        roof = {"bound": "mfma", "achieved": tops, "peak": INT8_PEAK_TOPS, "unit": "TOP/s"}
+    else:
+        roof = {"bound": "hbm", "achieved": alg_bytes / (ms * 1e-3) / 1e9, "peak": HBM_PEAK_GBS,
+                "unit": "GB/s"}
+    roof.update({"frac": roof["achieved"] / roof["peak"], "traffic": None,
+                 "kernel": "whole dgrad call (filter repack + one forward kernel per stride phase)",
+                 "kernel_avg_us": ms * 1e3, "kernel_only_launch": False,
+                 "algorithmic_bytes": alg_bytes, "algorithmic_ops": ops})
+    cpu = None
+    if not args.no_cpu_baseline:
+        import oracle
+        orc = oracle.load()
+        threads = orc.max_threads()
+        dy_cpu = torch.as_strided(dy0.cpu(), c.out.dims, c.out.strides)
+        tt = time.perf_counter()
+        reps = 0
+        while True:
+            orc.conv_dgrad(dy_cpu, d["w"], c.image.dims, c.pre, c.post, c.stride, c.dilation,
+                           threads=threads, mode=mode)
+            reps += 1
+            el = time.perf_counter() - tt
+            if el >= args.cpu_seconds or reps >= 20:
+                break
+        cpu = {"value": ops * reps / el / 1e12, "unit": "TOPS", "cores": threads, "kind": "oracle",
+               "sample": f"the whole dgrad of {c.name}, {reps} run(s), {el:.1f} s wall, "
+                         f"{threads} OpenMP threads"}
+    out = {
+        "metric": METRIC, "value": tops, "unit": "TOPS", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "int8", "data": "synthetic",
+        "config": {"workload": c.name, "op": "dgrad", "mode": args.mode,
+                   "loss": list(c.out.dims), "loss_strides": list(c.out.strides),
+                   "filter": list(c.filter.dims), "filter_strides": list(c.filter.strides),
+                   "dx": list(c.image.dims), "dx_strides": list(dx_strides),
+                   "pre_padding": list(c.pre), "post_padding": list(c.post),
+                   "stride": list(c.stride), "dilation": list(c.dilation),
+                   "accumulate": "int32", "output": "int32", "buffer_sets": nsets},
+        "frac_of_int8_peak": tops / INT8_PEAK_TOPS,
+        "roofline": roof,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -91,6 +205,8 @@ def main():
     import workloads as wl
 
     c = wl.case(args.workload)
+    if args.op == "dgrad":
+        return bench_dgrad(args, c)
     rq_on = args.epilogue == "requant"
     esize = 1 if rq_on else 4
     dev = torch.device("cuda:0")
