@@ -25,7 +25,7 @@ import torch
 from . import build as _build
 
 __all__ = ["OracleError", "Oracle", "load", "out_dims", "conv_fprop", "conv_fprop_points",
-           "conv_fprop_requant", "requant_values", "conv_dgrad", "max_threads"]
+           "conv_fprop_requant", "requant_values", "conv_dgrad", "conv_wgrad", "max_threads"]
 
 _ERRORS = {
     1: "bad argument (null pointer, negative size, stride/dilation < 1, negative padding)",
@@ -79,6 +79,8 @@ class Oracle:
         lib.oracle_requant_values.restype = ctypes.c_int
         lib.oracle_conv_dgrad.argtypes = [P] * 13 + [ctypes.c_int, ctypes.c_int]
         lib.oracle_conv_dgrad.restype = ctypes.c_int
+        lib.oracle_conv_wgrad.argtypes = [P] * 13 + [ctypes.c_int, ctypes.c_int]
+        lib.oracle_conv_wgrad.restype = ctypes.c_int
         lib.oracle_max_threads.argtypes = []
         lib.oracle_max_threads.restype = ctypes.c_int
         self.lib = lib
@@ -212,6 +214,28 @@ class Oracle:
         return out
 
 
+    def conv_wgrad(self, x: torch.Tensor, dy: torch.Tensor, dw_dims=None, pre=0, post=0,
+                   stride=1, dil=1, out: Optional[torch.Tensor] = None, threads: int = 0,
+                   mode: int = 0) -> torch.Tensor:
+        """dW (int32 [K,C,R,S]; R, S from ``out`` or ``dw_dims``) of the loss
+        dY (int8 [N,K,P,Q]) for the image x (int8 [N,C,H,W])."""
+        _check_cpu(x, torch.int8, "x")
+        _check_cpu(dy, torch.int8, "dy")
+        if out is None:
+            if dw_dims is None:
+                raise ValueError("give dw_dims or out")
+            out = torch.empty(tuple(dw_dims), dtype=torch.int32)
+        _check_cpu(out, torch.int32, "out")
+        rc = self.lib.oracle_conv_wgrad(
+            ctypes.c_void_p(x.data_ptr()), _v4(x.shape), _v4(x.stride()),
+            ctypes.c_void_p(dy.data_ptr()), _v4(dy.shape), _v4(dy.stride()),
+            ctypes.c_void_p(out.data_ptr()), _v4(out.shape), _v4(out.stride()),
+            _v2(pre), _v2(post), _v2(stride), _v2(dil), int(mode), int(threads))
+        if rc:
+            raise OracleError(rc)
+        return out
+
+
 def _nchan(scale, bias) -> int:
     n = [len(np.asarray(v).reshape(-1)) for v in (scale, bias) if v is not None]
     return min(n)
@@ -275,6 +299,10 @@ def requant_values(*a, **k):
 
 def conv_dgrad(*a, **k):
     return load().conv_dgrad(*a, **k)
+
+
+def conv_wgrad(*a, **k):
+    return load().conv_wgrad(*a, **k)
 
 
 def max_threads() -> int:

@@ -409,6 +409,81 @@ int oracle_conv_dgrad(const int8_t *dy, const int64_t dydims[4], const int64_t d
     return overflow ? ORACLE_ERR_OVERFLOW : ORACLE_OK;
 }
 
+/*
+ * Weight gradient (cuDNN "Convolutions" page, section "Convolution Wgrad":
+ * the gradient with respect to the filter, from the image and the loss, for
+ * the forward's padding, stride, dilation and mode).  The adjoint of the
+ * forward sum with respect to W: each forward term X[n,c,h,w] * W[k,c,r',s']
+ * added to Y[n,k,p,q] sends X[n,c,h,w] * dY[n,k,p,q] to dW[k,c,r',s']:
+ *
+ *   dW[k,c,r',s'] = sum_{n,p,q} dY[n,k,p,q] * X[n,c, p*stride_h - pre_h + r*dil_h,
+ *                                                     q*stride_w - pre_w + s*dil_w]
+ *
+ * (X is 0 outside the image), (r',s') = (r,s), or (R-1-r,S-1-s) in mode 1.
+ * x is [N,C,H,W] int8, dy [N,K,P,Q] int8, dw [K,C,R,S] int32; dY's dims must
+ * be the forward output dims.  Summed over n, then p, then q; 64-bit sums.
+ */
+int oracle_conv_wgrad(const int8_t *x, const int64_t xdims[4], const int64_t xstr[4],
+                      const int8_t *dy, const int64_t dydims[4], const int64_t dystr[4],
+                      int32_t *dw, const int64_t dwdims[4], const int64_t dwstr[4],
+                      const int64_t pre[2], const int64_t post[2],
+                      const int64_t stride[2], const int64_t dil[2], int mode, int nthreads)
+{
+    int64_t fwd[4];
+    if (!xstr || !dydims || !dystr || !dwdims || !dwstr)
+        return ORACLE_ERR_ARG;
+    int rc = oracle_out_dims(xdims, dwdims, pre, post, stride, dil, fwd);
+    if (rc != ORACLE_OK)
+        return rc;
+    for (int i = 0; i < 4; ++i)
+        if (dydims[i] != fwd[i])
+            return ORACLE_ERR_OUT_DIMS;
+    if ((!x && oracle_elems(xdims) > 0) || (!dy && oracle_elems(dydims) > 0) ||
+        (!dw && oracle_elems(dwdims) > 0))
+        return ORACLE_ERR_ARG;
+
+    const int64_t N = xdims[0], H = xdims[2], W = xdims[3];
+    const int64_t K = dwdims[0], C = dwdims[1], R = dwdims[2], S = dwdims[3];
+    const int64_t P = dydims[2], Q = dydims[3];
+    int overflow = 0;
+#ifdef _OPENMP
+    if (nthreads > 0)
+        omp_set_num_threads(nthreads);
+#else
+    (void)nthreads;
+#endif
+#pragma omp parallel for collapse(2) schedule(dynamic, 1) reduction(| : overflow)
+    for (int64_t k = 0; k < K; ++k) {
+        for (int64_t ci = 0; ci < C; ++ci) {
+            for (int64_t r = 0; r < R; ++r) {
+                for (int64_t s = 0; s < S; ++s) {
+                    int64_t acc = 0;
+                    for (int64_t n = 0; n < N; ++n) {
+                        for (int64_t p = 0; p < P; ++p) {
+                            const int64_t h = p * stride[0] - pre[0] + r * dil[0];
+                            if (h < 0 || h >= H)
+                                continue;
+                            for (int64_t q = 0; q < Q; ++q) {
+                                const int64_t wc = q * stride[1] - pre[1] + s * dil[1];
+                                if (wc < 0 || wc >= W)
+                                    continue;
+                                acc += (int64_t)dy[n * dystr[0] + k * dystr[1] + p * dystr[2] + q * dystr[3]] *
+                                       (int64_t)x[n * xstr[0] + ci * xstr[1] + h * xstr[2] + wc * xstr[3]];
+                            }
+                        }
+                    }
+                    if (acc < INT32_MIN || acc > INT32_MAX)
+                        overflow = 1;
+                    const int64_t gr = mode ? R - 1 - r : r, gs = mode ? S - 1 - s : s;
+                    dw[k * dwstr[0] + ci * dwstr[1] + gr * dwstr[2] + gs * dwstr[3]] =
+                        (int32_t)(uint32_t)(uint64_t)acc;
+                }
+            }
+        }
+    }
+    return overflow ? ORACLE_ERR_OVERFLOW : ORACLE_OK;
+}
+
 /* Threads an OpenMP parallel region gets by default (1 without OpenMP). */
 int oracle_max_threads(void)
 {

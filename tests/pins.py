@@ -24,6 +24,8 @@ broken builds of the oracle.
   conv2d with respect to the image (exact for these integer sums), and by the
   adjoint identity <fprop(X, W), dY> = <X, dgrad(dY, W)> in int64 against
   the pinned forward oracle, in both modes.
+* the weight gradient (wgrad) likewise: float64 autograd with respect to the
+  filter, and <fprop(X, W), dY> = <W, wgrad(X, dY)> in int64.
 * ``exact_requant`` evaluates the requantising INT8 epilogue with exact
   rational arithmetic (``fractions.Fraction``): the fused multiply-add is the
   exact value ``acc*s + b`` rounded once to the nearest binary32 (ties to an
@@ -525,8 +527,55 @@ def check_dgrad(orc) -> None:
     assert (base[..., 1::2] == 5).all()
 
 
+def autograd_wgrad(x: torch.Tensor, dy: torch.Tensor, wdims, pre, post, stride, dil) -> torch.Tensor:
+    """d/dW of sum(conv2d(pad(X), W) * dY) in float64 (cross-correlation)."""
+    w = torch.zeros(tuple(wdims), dtype=torch.float64, requires_grad=True)
+    y = F.conv2d(F.pad(x.to(torch.float64), (pre[1], post[1], pre[0], post[0])), w,
+                 stride=tuple(stride), dilation=tuple(dil))
+    (g,) = torch.autograd.grad(y, w, dy.to(torch.float64))
+    return g.round().to(torch.int64)
+
+
+def check_wgrad(orc) -> None:
+    """wgrad = float64 autograd of the forward with respect to the filter
+    (mode 1: reversed taps), and <fprop(X, W), dY> = <W, wgrad(X, dY)>."""
+    rng = np.random.default_rng(47)
+    done = 0
+    while done < 40:
+        N, C, K = (int(v) for v in rng.integers(1, 4, 3))
+        H, W = (int(v) for v in rng.integers(1, 10, 2))
+        R, S = (int(v) for v in rng.integers(1, 4, 2))
+        pre = tuple(int(v) for v in rng.integers(0, 3, 2))
+        post = tuple(int(v) for v in rng.integers(0, 3, 2))
+        st = tuple(int(v) for v in rng.integers(1, 4, 2))
+        dl = tuple(int(v) for v in rng.integers(1, 3, 2))
+        if H + pre[0] + post[0] - dl[0] * (R - 1) - 1 < 0 or W + pre[1] + post[1] - dl[1] * (S - 1) - 1 < 0:
+            continue
+        done += 1
+        x = rand_i8(rng, (N, C, H, W))
+        w = rand_i8(rng, (K, C, R, S))
+        dy = rand_i8(rng, orc.out_dims(x.shape, w.shape, pre, post, st, dl))
+        for mode in (0, 1):
+            dw = orc.conv_wgrad(x, dy, w.shape, pre, post, st, dl, mode=mode).to(torch.int64)
+            ref = autograd_wgrad(x, dy, w.shape, pre, post, st, dl)
+            if mode:
+                ref = ref.flip(2, 3)
+            assert torch.equal(dw, ref), (done, mode)
+            y = orc.conv_fprop(x, w, pre, post, st, dl, mode=mode).to(torch.int64)
+            assert int((y * dy.to(torch.int64)).sum()) == int((w.to(torch.int64) * dw).sum())
+    # strided views in and out
+    x = rand_i8(rng, (3, 4, 8, 7))
+    dy_full = rand_i8(rng, (3, 5, 8, 2 * 7))
+    dy = dy_full[..., ::2]                           # 3x5x8x7: 3x3 filter, pad 1, stride 1
+    base = torch.full((4, 5, 3, 3), 9, dtype=torch.int32)
+    out = base.permute(1, 0, 2, 3)                   # [K, C, R, S] view of a [C, K, R, S] buffer
+    orc.conv_wgrad(x, dy, None, 1, 1, 1, 1, out=out)
+    assert torch.equal(out.to(torch.int64), autograd_wgrad(x, dy.contiguous(), (5, 4, 3, 3), (1, 1),
+                                                          (1, 1), (1, 1), (1, 1)))
+
+
 QUICK_CHECKS = [
     check_random_vs_brute_force, check_offcentre_delta, check_identity_1x1, check_ones_count,
     check_constant_min, check_layouts, check_metamorphic, check_points, check_requant_exact,
-    check_requant_conv, check_convolution_mode, check_dgrad,
+    check_requant_conv, check_convolution_mode, check_dgrad, check_wgrad,
 ]

@@ -120,6 +120,10 @@ def test_dgrad(orc):
     pins.check_dgrad(orc)
 
 
+def test_wgrad(orc):
+    pins.check_wgrad(orc)
+
+
 @pytest.mark.parametrize("name", wl.CASE_ORDER)
 def test_workloads_vs_f64_library_conv(orc, name):
     """Oracle == float64 torch conv2d on every workload at full size."""
@@ -190,6 +194,9 @@ MUTATIONS = [
     ("dgrad pre-padding sign", "h + pre[0] - r * dil[0]", "h - pre[0] - r * dil[0]"),
     ("dgrad column dilation dropped", "x + pre[1] - s * dil[1]", "x + pre[1] - s"),
     ("dgrad last row of dY dropped", "pn / stride[0] >= P", "pn / stride[0] >= P - 1"),
+    ("wgrad row stride dropped", "const int64_t h = p * stride[0] - pre[0] + r * dil[0];\n                            if (h < 0 || h >= H)", "const int64_t h = p - pre[0] + r * dil[0];\n                            if (h < 0 || h >= H)"),
+    ("wgrad ignores the image's right edge", "if (wc < 0 || wc >= W)\n                                    continue;\n                                acc += (int64_t)dy", "if (wc < 0)\n                                    continue;\n                                acc += (int64_t)dy"),
+    ("wgrad mode ignored", "const int64_t gr = mode ? R - 1 - r : r, gs", "const int64_t gr = r, gs"),
     ("dgrad mode ignored", "const int64_t fs = mode ? S - 1 - s : s;\n                acc", "const int64_t fs = s;\n                acc"),
     ("unsigned widening of int8", "const int64_t xv = x[", "const int64_t xv = (uint8_t)x["),
     ("last channel dropped", "for (int64_t c = 0; c < C; ++c)", "for (int64_t c = 0; c + 1 < C; ++c)"),
