@@ -45,9 +45,11 @@ def parse():
                     default="cross_correlation",
                     help="convolution: true convolution (filter taps reversed) through the "
                          "general entry conv_fprop_i8_ex_ws")
-    ap.add_argument("--op", choices=("fprop", "dgrad"), default="fprop",
+    ap.add_argument("--op", choices=("fprop", "dgrad", "wgrad"), default="fprop",
                     help="dgrad: the data gradient of the workload (loss shaped like its output, "
-                         "INT32 result shaped like its image) through conv_dgrad_i8_ws")
+                         "INT32 result shaped like its image) through conv_dgrad_i8_ws; wgrad: "
+                         "the weight gradient (the workload's image and such a loss, INT32 "
+                         "result shaped like its filter) through conv_wgrad_i8_ws")
     ap.add_argument("--epilogue", choices=("int32", "requant"), default="int32",
                     help="int32: the plain entry; requant: INT8 output with per-channel "
                          "scale and bias and ReLU")
@@ -80,11 +82,13 @@ def traffic_from_profiles(workload: str, launch_bytes_alg: float):
     return t.get("hbm_bytes_per_launch")
 
 
-def bench_dgrad(args, c):
-    """Whole-call timing of the data gradient: dY (INT8, the forward output's
+def bench_grad(args, c):
+    """Whole-call timing of a gradient.  dgrad: dY (INT8, the forward output's
     dims and strides), the workload's filter, dX (INT32, the image dims,
     channels_last); every call repacks the transposed filter and runs one
-    forward convolution per stride phase."""
+    forward convolution per stride phase.  wgrad: the workload's image, such a
+    dY, dW (INT32, the filter's dims and strides); one forward convolution of
+    the transposed operands (both repacked)."""
     import torch
 
     import int8_convolution_forward_amd as ci8
@@ -100,20 +104,31 @@ def bench_dgrad(args, c):
     mode = 1 if args.mode == "convolution" else 0
     g = torch.Generator().manual_seed(c.seed_base + 91)
     dy0 = torch.randint(-128, 128, (c.out.storage_size,), dtype=torch.int8, generator=g).to(dev)
-    w0, _ = wl.to_device(d["w_storage"], c.filter, dev)
-    dx_strides = wl.channels_last_strides(c.image.dims)
-    dx_size = wl.TensorSpec(c.image.dims, dx_strides).storage_size
+    wg = args.op == "wgrad"
+    if wg:
+        w0, _ = wl.to_device(d["x_storage"], c.image, dev)     # the image
+        in_spec = c.image
+        res_dims, res_strides = c.filter.dims, c.filter.strides
+    else:
+        w0, _ = wl.to_device(d["w_storage"], c.filter, dev)
+        in_spec = c.filter
+        res_dims, res_strides = c.image.dims, wl.channels_last_strides(c.image.dims)
+    dx_strides = res_strides
+    dx_size = wl.TensorSpec(res_dims, res_strides).storage_size
     set_bytes = dy0.numel() + w0.numel() + 4 * dx_size
     nsets = max(2, min(128, int(args.rotate_mb * 2**20 // set_bytes) + 1))
     sets = []
     for _ in range(nsets):
         dys, ws_ = dy0.clone(), w0.clone()
         dxs = torch.empty(dx_size, dtype=torch.int32, device=dev)
-        sets.append((dys, ws_, dxs, torch.as_strided(dys, c.out.dims, c.out.strides),
-                     torch.as_strided(ws_, c.filter.dims, c.filter.strides, c.filter.offset),
-                     torch.as_strided(dxs, c.image.dims, dx_strides)))
-    ws_bytes = ci8.conv_dgrad_i8_workspace_size(sets[0][3], sets[0][4], sets[0][5], c.pre, c.post,
-                                                c.stride, c.dilation, mode=mode)
+        dyv = torch.as_strided(dys, c.out.dims, c.out.strides)
+        inv = torch.as_strided(ws_, in_spec.dims, in_spec.strides, in_spec.offset)
+        resv = torch.as_strided(dxs, res_dims, res_strides)
+        # argument order of the C entry: dgrad (loss, filter, dx), wgrad (image, loss, dw)
+        sets.append((dys, ws_, dxs, inv, dyv, resv) if wg else (dys, ws_, dxs, dyv, inv, resv))
+    wsize = ci8.conv_wgrad_i8_workspace_size if wg else ci8.conv_dgrad_i8_workspace_size
+    ws_bytes = wsize(sets[0][3], sets[0][4], sets[0][5], c.pre, c.post, c.stride, c.dilation,
+                     mode=mode)
     workspace = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream()
     sh = ctypes.c_void_p(stream.cuda_stream)
@@ -123,14 +138,14 @@ def bench_dgrad(args, c):
               ctypes.byref(ci8.desc(s_[5])), ctypes.c_void_p(s_[5].data_ptr()), *params,
               ctypes.c_int32(mode), ctypes.c_void_p(workspace.data_ptr()) if ws_bytes else None,
               ctypes.c_size_t(ws_bytes), sh) for s_ in sets]
-    fn = ci8.lib.conv_dgrad_i8_ws
+    fn = ci8.lib.conv_wgrad_i8_ws if wg else ci8.lib.conv_dgrad_i8_ws
 
     def step(i):
         rc = fn(*calls[i % nsets])
         if rc != 0:
             raise RuntimeError(ci8.status_string(rc))
 
-    print(f"bench: dgrad of {c.name}; {nsets} buffer sets of {set_bytes / 2**20:.1f} MiB, "
+    print(f"bench: {args.op} of {c.name}; {nsets} buffer sets of {set_bytes / 2**20:.1f} MiB, "
           f"workspace {ws_bytes} B", file=sys.stderr, flush=True)
     for i in range(args.warmup):
         step(i)
@@ -144,7 +159,8 @@ def bench_dgrad(args, c):
     torch.cuda.synchronize()
     ms = t0.elapsed_time(t1) / args.steps
     tops = ops / (ms * 1e-3) / 1e12
-    alg_bytes = N * K * P * Q + K * C * R * S + 4 * N * C * H * W
+    alg_bytes = (N * K * P * Q + N * C * H * W + 4 * K * C * R * S) if wg else \
+        (N * K * P * Q + K * C * R * S + 4 * N * C * H * W)
     ridge = INT8_PEAK_TOPS * 1e12 / (HBM_PEAK_GBS * 1e9)
     if ops / alg_bytes >= ridge:
         roof = {"bound": "mfma", "achieved": tops, "peak": INT8_PEAK_TOPS, "unit": "TOP/s"}
@@ -152,7 +168,9 @@ def bench_dgrad(args, c):
         roof = {"bound": "hbm", "achieved": alg_bytes / (ms * 1e-3) / 1e9, "peak": HBM_PEAK_GBS,
                 "unit": "GB/s"}
     roof.update({"frac": roof["achieved"] / roof["peak"], "traffic": None,
-                 "kernel": "whole dgrad call (filter repack + one forward kernel per stride phase)",
+                 "kernel": ("whole wgrad call (repacks of both transposed operands + one forward "
+                            "kernel)") if wg else
+                           "whole dgrad call (filter repack + one forward kernel per stride phase)",
                  "kernel_avg_us": ms * 1e3, "kernel_only_launch": False,
                  "algorithmic_bytes": alg_bytes, "algorithmic_ops": ops})
     cpu = None
@@ -164,23 +182,29 @@ def bench_dgrad(args, c):
         tt = time.perf_counter()
         reps = 0
         while True:
-            orc.conv_dgrad(dy_cpu, d["w"], c.image.dims, c.pre, c.post, c.stride, c.dilation,
-                           threads=threads, mode=mode)
+            if wg:
+                orc.conv_wgrad(d["x"], dy_cpu, c.filter.dims, c.pre, c.post, c.stride, c.dilation,
+                               threads=threads, mode=mode)
+            else:
+                orc.conv_dgrad(dy_cpu, d["w"], c.image.dims, c.pre, c.post, c.stride, c.dilation,
+                               threads=threads, mode=mode)
             reps += 1
             el = time.perf_counter() - tt
             if el >= args.cpu_seconds or reps >= 20:
                 break
         cpu = {"value": ops * reps / el / 1e12, "unit": "TOPS", "cores": threads, "kind": "oracle",
-               "sample": f"the whole dgrad of {c.name}, {reps} run(s), {el:.1f} s wall, "
+               "sample": f"the whole {args.op} of {c.name}, {reps} run(s), {el:.1f} s wall, "
                          f"{threads} OpenMP threads"}
     out = {
         "metric": METRIC, "value": tops, "unit": "TOPS", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": "int8", "data": "synthetic",
-        "config": {"workload": c.name, "op": "dgrad", "mode": args.mode,
+        "config": {"workload": c.name, "op": args.op, "mode": args.mode,
                    "loss": list(c.out.dims), "loss_strides": list(c.out.strides),
-                   "filter": list(c.filter.dims), "filter_strides": list(c.filter.strides),
-                   "dx": list(c.image.dims), "dx_strides": list(dx_strides),
+                   ("image" if wg else "filter"): list(in_spec.dims),
+                   ("image_strides" if wg else "filter_strides"): list(in_spec.strides),
+                   ("dw" if wg else "dx"): list(res_dims),
+                   ("dw_strides" if wg else "dx_strides"): list(dx_strides),
                    "pre_padding": list(c.pre), "post_padding": list(c.post),
                    "stride": list(c.stride), "dilation": list(c.dilation),
                    "accumulate": "int32", "output": "int32", "buffer_sets": nsets},
@@ -205,8 +229,8 @@ def main():
     import workloads as wl
 
     c = wl.case(args.workload)
-    if args.op == "dgrad":
-        return bench_dgrad(args, c)
+    if args.op in ("dgrad", "wgrad"):
+        return bench_grad(args, c)
     rq_on = args.epilogue == "requant"
     esize = 1 if rq_on else 4
     dev = torch.device("cuda:0")

@@ -357,6 +357,58 @@ conv_i8_status_t conv_dgrad_i8(const conv_i8_desc_t *loss, const void *loss_ptr,
                                int32_t mode,
                                void *stream);
 
+/*
+ * Weight gradient (cuDNN "Convolutions" page, section "Convolution Wgrad":
+ * the gradient with respect to the filter from the image and the loss, with
+ * the forward's padding, stride, dilation and convolution mode).  Read as
+ * the adjoint of conv_fprop with respect to W:
+ *
+ *   dW[k,c,r',s'] = sum_{n,p,q} dY[n,k,p,q]
+ *                      * X[n, c, p*stride_h - pre_h + r*dil_h, q*stride_w - pre_w + s*dil_w]
+ *
+ * (X is 0 outside the image), (r',s') = (r,s), or (R-1-r,S-1-s) for
+ * CONV_I8_MODE_CONVOLUTION.  image INT8 [N,C,H,W], loss (dY) INT8 [N,K,P,Q]
+ * with [P,Q] the forward output size, dw INT32 [K,C,R,S] (its dims give R
+ * and S).  Exact int32 sums while N*P*Q <= 131071 (CONV_I8_ERR_RANGE
+ * otherwise).  Any strides; dw must not overlap itself.  The work is one
+ * forward convolution: the image transposed to [C, N, H, W] convolved with the
+ * loss transposed to [K, N, P, Q] at stride = dilation and dilation = stride,
+ * written to dW transposed to [C, K, R, S] (reversed along R and S for true
+ * convolution).  Errors and stream behaviour as conv_fprop_i8_ws; never
+ * allocates, never synchronises.
+ */
+conv_i8_status_t conv_wgrad_i8_workspace_size(const conv_i8_desc_t *image, const void *image_ptr,
+                                              const conv_i8_desc_t *loss, const void *loss_ptr,
+                                              const conv_i8_desc_t *dw,
+                                              const int64_t pre_padding[2],
+                                              const int64_t post_padding[2],
+                                              const int64_t stride[2],
+                                              const int64_t dilation[2],
+                                              int32_t mode,
+                                              size_t *workspace_bytes);
+
+conv_i8_status_t conv_wgrad_i8_ws(const conv_i8_desc_t *image, const void *image_ptr,
+                                  const conv_i8_desc_t *loss, const void *loss_ptr,
+                                  const conv_i8_desc_t *dw, void *dw_ptr,
+                                  const int64_t pre_padding[2],
+                                  const int64_t post_padding[2],
+                                  const int64_t stride[2],
+                                  const int64_t dilation[2],
+                                  int32_t mode,
+                                  void *workspace, size_t workspace_bytes,
+                                  void *stream);
+
+/* conv_wgrad_i8_ws with its workspace taken stream-ordered (hipMallocAsync). */
+conv_i8_status_t conv_wgrad_i8(const conv_i8_desc_t *image, const void *image_ptr,
+                               const conv_i8_desc_t *loss, const void *loss_ptr,
+                               const conv_i8_desc_t *dw, void *dw_ptr,
+                               const int64_t pre_padding[2],
+                               const int64_t post_padding[2],
+                               const int64_t stride[2],
+                               const int64_t dilation[2],
+                               int32_t mode,
+                               void *stream);
+
 /* Static string naming a status code. */
 const char *conv_i8_status_string(conv_i8_status_t status);
 

@@ -31,7 +31,8 @@ __all__ = [
     "conv_fprop_i8_requant", "conv_fprop_i8_requant_ws", "conv_fprop_i8_requant_plain",
     "conv_fprop_i8_requant_workspace_size", "Requant", "conv_fprop_i8_ex_ws",
     "conv_fprop_i8_ex_workspace_size", "conv_fprop_i8_mode", "conv_dgrad_i8",
-    "conv_dgrad_i8_ws", "conv_dgrad_i8_workspace_size", "conv_dgrad_i8_plain", "MODE_CROSS_CORRELATION",
+    "conv_dgrad_i8_ws", "conv_dgrad_i8_workspace_size", "conv_dgrad_i8_plain", "conv_wgrad_i8",
+    "conv_wgrad_i8_ws", "conv_wgrad_i8_workspace_size", "conv_wgrad_i8_plain", "MODE_CROSS_CORRELATION",
     "MODE_CONVOLUTION",
     "status_string", "LIB_PATH", "DT_INT8", "DT_INT32", "MAX_REDUCTION", "lib",
 ]
@@ -102,12 +103,18 @@ lib.conv_dgrad_i8_workspace_size.argtypes = [_DP, _P, _DP, _P, _DP, _V2, _V2, _V
 lib.conv_dgrad_i8_ws.argtypes = [_DP, _P, _DP, _P, _DP, _P, _V2, _V2, _V2, _V2, ctypes.c_int32, _P,
                                  ctypes.c_size_t, _P]
 lib.conv_dgrad_i8.argtypes = [_DP, _P, _DP, _P, _DP, _P, _V2, _V2, _V2, _V2, ctypes.c_int32, _P]
+lib.conv_wgrad_i8_workspace_size.argtypes = [_DP, _P, _DP, _P, _DP, _V2, _V2, _V2, _V2,
+                                             ctypes.c_int32, ctypes.POINTER(ctypes.c_size_t)]
+lib.conv_wgrad_i8_ws.argtypes = [_DP, _P, _DP, _P, _DP, _P, _V2, _V2, _V2, _V2, ctypes.c_int32, _P,
+                                 ctypes.c_size_t, _P]
+lib.conv_wgrad_i8.argtypes = [_DP, _P, _DP, _P, _DP, _P, _V2, _V2, _V2, _V2, ctypes.c_int32, _P]
 lib.conv_i8_status_string.argtypes = [ctypes.c_int]
 lib.conv_i8_status_string.restype = ctypes.c_char_p
 for _f in ("conv_fprop_i8_out_dims", "conv_fprop_i8_workspace_size", "conv_fprop_i8_ws",
            "conv_fprop_i8", "conv_fprop_i8_plan", "conv_fprop_i8_requant_workspace_size",
            "conv_fprop_i8_requant_ws", "conv_fprop_i8_requant", "conv_fprop_i8_ex_workspace_size",
-           "conv_fprop_i8_ex_ws", "conv_dgrad_i8_workspace_size", "conv_dgrad_i8_ws", "conv_dgrad_i8"):
+           "conv_fprop_i8_ex_ws", "conv_dgrad_i8_workspace_size", "conv_dgrad_i8_ws", "conv_dgrad_i8",
+           "conv_wgrad_i8_workspace_size", "conv_wgrad_i8_ws", "conv_wgrad_i8"):
     getattr(lib, _f).restype = ctypes.c_int
 
 
@@ -447,4 +454,53 @@ def conv_dgrad_i8(dy: torch.Tensor, w: torch.Tensor, dx: torch.Tensor, pre_paddi
                                      padding, mode)
     ws = torch.empty(n, dtype=torch.uint8, device=dx.device) if n else None
     return conv_dgrad_i8_ws(dy, w, dx, ws, pre_padding, post_padding, stride, dilation, padding,
+                            mode, stream)
+
+
+def conv_wgrad_i8_workspace_size(x, dy, dw, pre_padding=0, post_padding=0, stride=1, dilation=1,
+                                 padding=None, mode: int = 0) -> int:
+    pre, post, st, dl = _params(pre_padding, post_padding, stride, dilation, padding)
+    n = ctypes.c_size_t()
+    xp = _ptr(x) if isinstance(x, torch.Tensor) else None
+    dp = _ptr(dy) if isinstance(dy, torch.Tensor) else None
+    _check(lib.conv_wgrad_i8_workspace_size(
+        ctypes.byref(_as_desc(x)), xp, ctypes.byref(_as_desc(dy)), dp, ctypes.byref(_as_desc(dw)),
+        pre, post, st, dl, int(mode), ctypes.byref(n)))
+    return int(n.value)
+
+
+def conv_wgrad_i8_ws(x: torch.Tensor, dy: torch.Tensor, dw: torch.Tensor,
+                     workspace: Optional[torch.Tensor], pre_padding=0, post_padding=0, stride=1,
+                     dilation=1, padding=None, mode: int = 0, stream=None) -> torch.Tensor:
+    """Direct call of the wgrad C entry with an explicit workspace."""
+    pre, post, st, dl = _params(pre_padding, post_padding, stride, dilation, padding)
+    ws_ptr = _ptr(workspace)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(lib.conv_wgrad_i8_ws(
+        ctypes.byref(desc(x)), _ptr(x), ctypes.byref(desc(dy)), _ptr(dy), ctypes.byref(desc(dw)),
+        _ptr(dw), pre, post, st, dl, int(mode), ws_ptr, ctypes.c_size_t(ws_bytes),
+        _stream_handle(stream)))
+    return dw
+
+
+def conv_wgrad_i8_plain(x: torch.Tensor, dy: torch.Tensor, dw: torch.Tensor, pre_padding=0,
+                        post_padding=0, stride=1, dilation=1, padding=None, mode: int = 0,
+                        stream=None) -> torch.Tensor:
+    """The wgrad C entry that takes its own workspace (hipMallocAsync)."""
+    pre, post, st, dl = _params(pre_padding, post_padding, stride, dilation, padding)
+    _check(lib.conv_wgrad_i8(
+        ctypes.byref(desc(x)), _ptr(x), ctypes.byref(desc(dy)), _ptr(dy), ctypes.byref(desc(dw)),
+        _ptr(dw), pre, post, st, dl, int(mode), _stream_handle(stream)))
+    return dw
+
+
+def conv_wgrad_i8(x: torch.Tensor, dy: torch.Tensor, dw: torch.Tensor, pre_padding=0,
+                  post_padding=0, stride=1, dilation=1, padding=None, mode: int = 0,
+                  stream=None) -> torch.Tensor:
+    """dW (int32 [K,C,R,S], written into ``dw``, which fixes R and S) from the
+    image x (int8 [N,C,H,W]) and the loss dY (int8 [N,K,P,Q])."""
+    n = conv_wgrad_i8_workspace_size(x, dy, dw, pre_padding, post_padding, stride, dilation,
+                                     padding, mode)
+    ws = torch.empty(n, dtype=torch.uint8, device=dw.device) if n else None
+    return conv_wgrad_i8_ws(x, dy, dw, ws, pre_padding, post_padding, stride, dilation, padding,
                             mode, stream)

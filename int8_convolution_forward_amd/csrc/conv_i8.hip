@@ -104,7 +104,9 @@ struct Problem {
     T4 x, w, y;
     int64_t N, C, H, W, K, R, S, P, Q;
     int64_t pre[2], post[2], str[2], dil[2];
-    int64_t mode;  // CONV_I8_MODE_*: 1 reads filter tap (R-1-r, S-1-s)
+    int64_t mode;      // CONV_I8_MODE_*: 1 reads filter tap (R-1-r, S-1-s)
+    int64_t flip_out;  // 1: output (p, q) is written at (P-1-p, Q-1-q) (weight gradient
+                       // of true convolution); never set by a caller's descriptor
 };
 
 conv_i8_status_t read_params(const int64_t *pre, const int64_t *post, const int64_t *stride,
@@ -184,6 +186,7 @@ conv_i8_status_t analyze(const conv_i8_desc_t *image, const conv_i8_desc_t *filt
     if (mode != CONV_I8_MODE_CROSS_CORRELATION && mode != CONV_I8_MODE_CONVOLUTION)
         return CONV_I8_ERR_PARAM;
     pb->mode = mode;
+    pb->flip_out = 0;
     // The output dtype is checked like every other field: the plain entries
     // refuse an INT8 output descriptor rather than write saturated bytes into
     // it; only the requantising entries write INT8.
@@ -529,7 +532,7 @@ conv_i8_status_t make_plan(const Problem &pb, const void *x_ptr, const void *w_p
         int64_t ps = Q > 1 ? oQ : P > 1 ? oP : oN;
         pl->pix_stride = ps;
         pl->pix_linear = (Q == 1 || oQ == ps) && (P == 1 || oP == Q * ps) &&
-                         (N == 1 || oN == P * Q * ps);
+                         (N == 1 || oN == P * Q * ps) && !pb.flip_out;
     }
     // Output layout: make the MFMA column (lanes) walk the contiguous dim.
     const int64_t oK = pb.y.s[1], oQ = pb.y.s[3];
@@ -738,6 +741,12 @@ conv_i8_status_t run(const Problem &pb, const Plan &pl, const void *x_ptr, const
     a.oK = (int)pb.y.s[1];
     a.oP = (int)pb.y.s[2];
     a.oQ = (int)pb.y.s[3];
+    if (pb.flip_out) {
+        // reversed rows and columns: offsets stay inside the image's span
+        a.out0 = (int)((pb.P - 1) * pb.y.s[2] + (pb.Q - 1) * pb.y.s[3]);
+        a.oP = -a.oP;
+        a.oQ = -a.oQ;
+    }
     a.pix_linear = pl.pix_linear ? 1 : 0;
     a.pix_stride = (int)pl.pix_stride;
     a.nstages = pb.C > 0 ? (int)pl.nstages : 0;
@@ -810,13 +819,14 @@ conv_i8_status_t prepare(const conv_i8_desc_t *image, const void *image_ptr,
                          const conv_i8_desc_t *out, const int64_t *pre, const int64_t *post,
                          const int64_t *stride, const int64_t *dil, Problem *pb, Plan *pl,
                          int32_t out_dtype = CONV_I8_DT_INT32,
-                         int32_t mode = CONV_I8_MODE_CROSS_CORRELATION)
+                         int32_t mode = CONV_I8_MODE_CROSS_CORRELATION, bool flip_out = false)
 {
     // The plan does not depend on the output dtype (it works in elements) nor
     // on the mode (the kernels read the taps in either order).
     conv_i8_status_t st = analyze(image, filter, out, pre, post, stride, dil, out_dtype, mode, pb);
     if (st != CONV_I8_OK)
         return st;
+    pb->flip_out = flip_out ? 1 : 0;
     PlanKey key;
     memset(&key, 0, sizeof key);  // padding takes part in the comparison
     static_assert(sizeof(Problem) % 8 == 0, "Problem has no tail padding to clear");
@@ -906,14 +916,14 @@ conv_i8_status_t entry_workspace_size(const conv_i8_desc_t *image, const void *i
                                       const conv_i8_desc_t *out, const int64_t *pre,
                                       const int64_t *post, const int64_t *stride,
                                       const int64_t *dil, int32_t out_dtype, int32_t mode,
-                                      size_t *workspace_bytes)
+                                      size_t *workspace_bytes, bool flip_out = false)
 {
     if (!workspace_bytes)
         return CONV_I8_ERR_NULL;
     Problem pb;
     Plan pl;
     conv_i8_status_t st = prepare(image, image_ptr, filter, filter_ptr, out, pre, post, stride,
-                                  dil, &pb, &pl, out_dtype, mode);
+                                  dil, &pb, &pl, out_dtype, mode, flip_out);
     if (st != CONV_I8_OK)
         return st;
     *workspace_bytes = pb.y.elems() == 0 || pb.C == 0 ? 0 : pl.ws_bytes;
@@ -928,12 +938,13 @@ conv_i8_status_t entry_run(const conv_i8_desc_t *image, const void *image_ptr,
                            const conv_i8_desc_t *out, void *out_ptr, const int64_t *pre,
                            const int64_t *post, const int64_t *stride, const int64_t *dil,
                            int32_t out_dtype, int32_t mode, const conv_i8_requant_t *rq, bool alloc,
-                           void *workspace, size_t workspace_bytes, void *stream)
+                           void *workspace, size_t workspace_bytes, void *stream,
+                           bool flip_out = false)
 {
     Problem pb;
     Plan pl;
     conv_i8_status_t st = prepare(image, image_ptr, filter, filter_ptr, out, pre, post, stride,
-                                  dil, &pb, &pl, out_dtype, mode);
+                                  dil, &pb, &pl, out_dtype, mode, flip_out);
     if (st != CONV_I8_OK)
         return st;
     if (out_dtype == CONV_I8_DT_INT8 && (st = check_requant(rq)) != CONV_I8_OK)
@@ -1252,6 +1263,156 @@ conv_i8_status_t dgrad_entry(const conv_i8_desc_t *loss, const void *loss_ptr,
     return st;
 }
 
+// ---------------------------------------------------------------------------
+// Weight gradient (wgrad) as one forward convolution.
+//
+// dW[k,c,r,s] = sum_{n,p,q} X[n,c, p*st_h - pre_h + r*dil_h, ..] * dY[n,k,p,q]
+// is a forward convolution of the image transposed to [C, N, H, W] (batch C,
+// channels N) with the loss transposed to [K, N, P, Q] (a P x Q filter),
+// stride dil, dilation st, the same pre-padding, written to dW transposed to
+// [C, K, R, S].  Its post-padding is cut so that exactly R x S outputs come
+// out (rows no output reads are cropped off the image).  The weight gradient
+// of true convolution writes tap (r, s) to (R-1-r, S-1-s): the same call with
+// reversed output rows and columns.
+// ---------------------------------------------------------------------------
+struct WgradProblem {
+    T4 x, dy, dw;
+    int64_t N, C, H, W, K, R, S, P, Q;
+    int64_t pre[2], post[2], str[2], dil[2];
+};
+
+conv_i8_status_t wgrad_analyze(const conv_i8_desc_t *image, const conv_i8_desc_t *loss,
+                               const conv_i8_desc_t *dw, const int64_t *pre, const int64_t *post,
+                               const int64_t *stride, const int64_t *dil, int32_t mode,
+                               WgradProblem *wp)
+{
+    conv_i8_status_t st;
+    if ((st = read_desc(image, CONV_I8_DT_INT8, &wp->x)) != CONV_I8_OK ||
+        (st = read_desc(loss, CONV_I8_DT_INT8, &wp->dy)) != CONV_I8_OK ||
+        (st = read_desc(dw, CONV_I8_DT_INT32, &wp->dw)) != CONV_I8_OK)
+        return st;
+    Problem tmp;
+    if ((st = read_params(pre, post, stride, dil, &tmp)) != CONV_I8_OK)
+        return st;
+    if (mode != CONV_I8_MODE_CROSS_CORRELATION && mode != CONV_I8_MODE_CONVOLUTION)
+        return CONV_I8_ERR_PARAM;
+    for (int i = 0; i < 2; ++i) {
+        wp->pre[i] = tmp.pre[i];
+        wp->post[i] = tmp.post[i];
+        wp->str[i] = tmp.str[i];
+        wp->dil[i] = tmp.dil[i];
+    }
+    wp->N = wp->x.d[0];
+    wp->C = wp->x.d[1];
+    wp->H = wp->x.d[2];
+    wp->W = wp->x.d[3];
+    wp->K = wp->dw.d[0];
+    wp->R = wp->dw.d[2];
+    wp->S = wp->dw.d[3];
+    if (wp->R < 1 || wp->S < 1)
+        return CONV_I8_ERR_DIMS;
+    if (wp->dw.d[1] != wp->C)
+        return CONV_I8_ERR_CHANNELS;
+    for (int i = 0; i < 4; ++i)
+        if (wp->x.d[i] > kI32Max / 4 || wp->dw.d[i] > kI32Max / 4 || wp->dy.d[i] > kI32Max / 4)
+            return CONV_I8_ERR_UNSUPPORTED;
+    wp->P = out_len(wp->H, wp->pre[0], wp->post[0], wp->R, wp->str[0], wp->dil[0]);
+    wp->Q = out_len(wp->W, wp->pre[1], wp->post[1], wp->S, wp->str[1], wp->dil[1]);
+    if (wp->P < 1 || wp->Q < 1)
+        return CONV_I8_ERR_OUT_DIMS;
+    const int64_t want[4] = {wp->N, wp->K, wp->P, wp->Q};
+    for (int i = 0; i < 4; ++i)
+        if (wp->dy.d[i] != want[i])
+            return CONV_I8_ERR_OUT_DIMS;
+    int64_t npq;
+    if (!mul_ok(wp->N, wp->P * wp->Q, &npq) || npq > CONV_I8_MAX_REDUCTION)
+        return CONV_I8_ERR_RANGE;
+    int64_t sp;
+    if (!span_of(wp->x, &sp) || !span_of(wp->dy, &sp) || !span_of(wp->dw, &sp))
+        return CONV_I8_ERR_UNSUPPORTED;
+    if (!non_overlapping(wp->dw))
+        return CONV_I8_ERR_STRIDES;
+    return CONV_I8_OK;
+}
+
+// The forward call of a wgrad: fn(image, x, filter, w, out, y, pre, post,
+// stride, dil, flip_out).
+template <class Fn>
+conv_i8_status_t wgrad_call(const WgradProblem &wp, const void *x_ptr, const void *dy_ptr,
+                            void *dw_ptr, int32_t mode, Fn &&fn)
+{
+    // image rows [0, need) are the ones the outputs read: the last output row
+    // reads row (P-1)*st - pre + (R-1)*dil
+    int64_t len[2], post2[2];
+    bool reads = true;
+    const int64_t in[2] = {wp.H, wp.W}, taps[2] = {wp.R, wp.S}, outn[2] = {wp.P, wp.Q};
+    for (int i = 0; i < 2; ++i) {
+        const int64_t need = (outn[i] - 1) * wp.str[i] + (taps[i] - 1) * wp.dil[i] + 1 - wp.pre[i];
+        reads = reads && need > 0;
+        len[i] = std::min(need, in[i]);
+        post2[i] = need > in[i] ? need - in[i] : 0;
+    }
+    const int64_t od[4] = {wp.C, wp.K, wp.R, wp.S};
+    const int64_t os[4] = {wp.dw.s[1], wp.dw.s[0], wp.dw.s[2], wp.dw.s[3]};
+    const conv_i8_desc_t out = make_desc(CONV_I8_DT_INT32, od, os);
+    const int64_t one[2] = {1, 1}, zero[2] = {0, 0};
+    if (!reads) {
+        // every tap lies in the padding: a convolution over zero channels
+        // writes the zeros
+        const int64_t xd[4] = {wp.C, 0, wp.R, wp.S}, z4[4] = {0, 0, 0, 0};
+        const int64_t fd[4] = {wp.K, 0, 1, 1};
+        const conv_i8_desc_t img = make_desc(CONV_I8_DT_INT8, xd, z4);
+        const conv_i8_desc_t flt = make_desc(CONV_I8_DT_INT8, fd, z4);
+        return fn(&img, nullptr, &flt, nullptr, &out, dw_ptr, zero, zero, one, one, false);
+    }
+    const int64_t xd[4] = {wp.C, wp.N, len[0], len[1]};
+    const int64_t xs[4] = {wp.x.s[1], wp.x.s[0], wp.x.s[2], wp.x.s[3]};
+    const int64_t fd[4] = {wp.K, wp.N, wp.P, wp.Q};
+    const int64_t fs[4] = {wp.dy.s[1], wp.dy.s[0], wp.dy.s[2], wp.dy.s[3]};
+    const conv_i8_desc_t img = make_desc(CONV_I8_DT_INT8, xd, xs);
+    const conv_i8_desc_t flt = make_desc(CONV_I8_DT_INT8, fd, fs);
+    const int64_t pre2[2] = {wp.pre[0], wp.pre[1]};
+    const int64_t st2[2] = {wp.dil[0], wp.dil[1]}, dl2[2] = {wp.str[0], wp.str[1]};
+    return fn(&img, x_ptr, &flt, dy_ptr, &out, dw_ptr, pre2, post2, st2, dl2,
+              mode == CONV_I8_MODE_CONVOLUTION);
+}
+
+conv_i8_status_t wgrad_entry(const conv_i8_desc_t *image, const void *image_ptr,
+                             const conv_i8_desc_t *loss, const void *loss_ptr,
+                             const conv_i8_desc_t *dw, void *dw_ptr, const int64_t *pre,
+                             const int64_t *post, const int64_t *stride, const int64_t *dil,
+                             int32_t mode, bool size_only, size_t *ws_size, bool alloc,
+                             void *workspace, size_t workspace_bytes, void *stream)
+{
+    WgradProblem wp;
+    conv_i8_status_t st = wgrad_analyze(image, loss, dw, pre, post, stride, dil, mode, &wp);
+    if (st != CONV_I8_OK)
+        return st;
+    if (wp.dw.elems() == 0) {
+        if (ws_size)
+            *ws_size = 0;
+        return CONV_I8_OK;
+    }
+    if (size_only)
+        return wgrad_call(wp, image_ptr, loss_ptr, nullptr, mode,
+                          [&](const conv_i8_desc_t *i, const void *x, const conv_i8_desc_t *f,
+                              const void *w, const conv_i8_desc_t *o, void *, const int64_t *a,
+                              const int64_t *b, const int64_t *c, const int64_t *d, bool fl) {
+                              return entry_workspace_size(i, x, f, w, o, a, b, c, d,
+                                                          CONV_I8_DT_INT32,
+                                                          CONV_I8_MODE_CROSS_CORRELATION, ws_size,
+                                                          fl);
+                          });
+    return wgrad_call(wp, image_ptr, loss_ptr, dw_ptr, mode,
+                      [&](const conv_i8_desc_t *i, const void *x, const conv_i8_desc_t *f,
+                          const void *w, const conv_i8_desc_t *o, void *y, const int64_t *a,
+                          const int64_t *b, const int64_t *c, const int64_t *d, bool fl) {
+                          return entry_run(i, x, f, w, o, y, a, b, c, d, CONV_I8_DT_INT32,
+                                           CONV_I8_MODE_CROSS_CORRELATION, nullptr, alloc,
+                                           workspace, workspace_bytes, stream, fl);
+                      });
+}
+
 }  // namespace
 }  // namespace convi8
 
@@ -1423,6 +1584,43 @@ conv_i8_status_t conv_dgrad_i8(const conv_i8_desc_t *loss, const void *loss_ptr,
 {
     return dgrad_entry(loss, loss_ptr, filter, filter_ptr, dx, dx_ptr, pre_padding, post_padding,
                        stride, dilation, mode, true, nullptr, 0, stream);
+}
+
+conv_i8_status_t conv_wgrad_i8_workspace_size(const conv_i8_desc_t *image, const void *image_ptr,
+                                              const conv_i8_desc_t *loss, const void *loss_ptr,
+                                              const conv_i8_desc_t *dw,
+                                              const int64_t pre_padding[2],
+                                              const int64_t post_padding[2],
+                                              const int64_t stride[2], const int64_t dilation[2],
+                                              int32_t mode, size_t *workspace_bytes)
+{
+    if (!workspace_bytes)
+        return CONV_I8_ERR_NULL;
+    return wgrad_entry(image, image_ptr, loss, loss_ptr, dw, nullptr, pre_padding, post_padding,
+                       stride, dilation, mode, true, workspace_bytes, false, nullptr, 0, nullptr);
+}
+
+conv_i8_status_t conv_wgrad_i8_ws(const conv_i8_desc_t *image, const void *image_ptr,
+                                  const conv_i8_desc_t *loss, const void *loss_ptr,
+                                  const conv_i8_desc_t *dw, void *dw_ptr,
+                                  const int64_t pre_padding[2], const int64_t post_padding[2],
+                                  const int64_t stride[2], const int64_t dilation[2], int32_t mode,
+                                  void *workspace, size_t workspace_bytes, void *stream)
+{
+    return wgrad_entry(image, image_ptr, loss, loss_ptr, dw, dw_ptr, pre_padding, post_padding,
+                       stride, dilation, mode, false, nullptr, false, workspace, workspace_bytes,
+                       stream);
+}
+
+conv_i8_status_t conv_wgrad_i8(const conv_i8_desc_t *image, const void *image_ptr,
+                               const conv_i8_desc_t *loss, const void *loss_ptr,
+                               const conv_i8_desc_t *dw, void *dw_ptr,
+                               const int64_t pre_padding[2], const int64_t post_padding[2],
+                               const int64_t stride[2], const int64_t dilation[2], int32_t mode,
+                               void *stream)
+{
+    return wgrad_entry(image, image_ptr, loss, loss_ptr, dw, dw_ptr, pre_padding, post_padding,
+                       stride, dilation, mode, false, nullptr, true, nullptr, 0, stream);
 }
 
 const char *conv_i8_status_string(conv_i8_status_t status)

@@ -45,7 +45,10 @@ struct IgemmArgs {
                          // 0, or (R-1)*|fR| + (S-1)*|fS| for true convolution
     int P, Q, PQ, M;     // M = N*P*Q
     int strH, strW, dilH, dilW, padH, padW;
-    int oN, oK, oP, oQ;  // output strides in elements (one launch spans < 2^31 bytes)
+    int oN, oK, oP, oQ;  // output strides in elements (one launch spans < 2^31 bytes);
+                         // oP, oQ negative when rows and columns are written reversed
+    int out0;            // element offset of output (p, q) = (0, 0) within its image:
+                         // 0, or (P-1)*|oP| + (Q-1)*|oQ| for reversed rows and columns
     int out_range;       // bytes addressable from out
     int pix_linear;      // output pixel m = (n*P + p)*Q + q lives at m*pix_stride
     int pix_stride;
@@ -192,7 +195,7 @@ __device__ __forceinline__ void fill_out_rows(const IgemmArgs &a, int m0, int *o
             const int rem = m - n * a.PQ;
             const int p = udiv(rem, a.d_q);
             const int q = rem - p * a.Q;
-            o = n * a.oN + p * a.oP + q * a.oQ;
+            o = n * a.oN + p * a.oP + q * a.oQ + a.out0;
         }
         out_row[i] = o;
     }
@@ -232,7 +235,7 @@ __device__ __forceinline__ void store_tile(const IgemmArgs &a, v16i (&acc)[FM][F
             const int rem = m - n * a.PQ;
             const int p = udiv(rem, a.d_q);
             const int q = rem - p * a.Q;
-            pix_off[x] = n * a.oN + p * a.oP + q * a.oQ;
+            pix_off[x] = n * a.oN + p * a.oP + q * a.oQ + a.out0;
         }
 #pragma unroll
         for (int y = 0; y < FN; ++y) {

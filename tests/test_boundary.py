@@ -361,3 +361,29 @@ def test_dgrad_workspace(st, dl):
     n = ci8.conv_dgrad_i8_workspace_size(dy, w, dx, pre, post, st, dl)
     assert n >= 16 * 8 * 9 // max(1, st[0] * st[1])
     assert _call_dgrad(dy, w, dx, pre, post, st, dl, ws_bytes=n - 1, ws=FAKE) == 10
+
+
+def test_wgrad_argument_errors():
+    D = ci8.desc
+    dy, w, dx, pre, post, st, dl = _dgrad_args()
+    x = D(dx.dims, dx.strides, ci8.DT_INT8)        # the image
+    dw = D(w.dims, w.strides, ci8.DT_INT32)        # the filter gradient
+
+    def call(x_, dy_, dw_, mode=0, yp=FAKE, ws_bytes=0, ws=None, stv=st):
+        p = ci8._params(pre, post, stv, dl, None)
+        return ci8.lib.conv_wgrad_i8_ws(ctypes.byref(x_), FAKE, ctypes.byref(dy_), FAKE,
+                                        ctypes.byref(dw_), yp, *p, mode, ws, ctypes.c_size_t(ws_bytes), None)
+    assert call(x, dy, D(dw.dims, dw.strides, ci8.DT_INT8)) == 2          # dW must be INT32
+    assert call(D(x.dims, x.strides, ci8.DT_INT32), dy, dw) == 2
+    assert call(x, D((2, 8, 4, 4), (128, 1, 32, 8), ci8.DT_INT8), dw) == 7  # dY not the output size
+    assert call(x, dy, D((8, 12, 3, 3), (108, 1, 36, 12), ci8.DT_INT32)) == 6
+    assert call(x, dy, dw, mode=5) == 5
+    assert call(x, dy, D(dw.dims, (0, 1, 0, 0), ci8.DT_INT32)) == 8        # overlapping dW
+    assert call(x, dy, dw, yp=None) == 1
+    # N*P*Q beyond the exact range: 600 images of 15x15 outputs
+    big_x = D((600, 16, 15, 15), (3600, 1, 240, 16), ci8.DT_INT8)
+    big_dy = D((600, 8, 15, 15), (1800, 1, 120, 8), ci8.DT_INT8)
+    assert call(big_x, big_dy, dw, stv=(1, 1)) == 9
+    n = ci8.conv_wgrad_i8_workspace_size(x, dy, dw, pre, post, st, dl)
+    assert n > 0                                 # both transposed operands are repacked
+    assert call(x, dy, dw, ws_bytes=n - 1, ws=FAKE) == 10

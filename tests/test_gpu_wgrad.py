@@ -1,0 +1,98 @@
+"""GPU parity of the weight gradient (conv_wgrad_i8) against the oracle's
+wgrad (pinned to float64 autograd and the adjoint identity): bit-exact over
+the whole dW buffer, guard bands included."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads as wl
+
+pytestmark = pytest.mark.gpu
+
+GUARD = 64
+
+
+@pytest.fixture(scope="module")
+def ci8():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import int8_convolution_forward_amd as m
+    return m
+
+
+def _dev():
+    return torch.device("cuda:0")
+
+
+def _rand_storage(spec, seed):
+    g = torch.Generator().manual_seed(seed)
+    return torch.randint(-128, 128, (spec.storage_size,), dtype=torch.int8, generator=g)
+
+
+def run_wgrad_check(ci8, x_storage, xspec, dy_storage, dyspec, dwspec, pre, post, st, dl, mode=0,
+                    label="", entry="ws"):
+    x_cpu = torch.as_strided(x_storage, xspec.dims, xspec.strides, xspec.offset)
+    dy_cpu = torch.as_strided(dy_storage, dyspec.dims, dyspec.strides, dyspec.offset)
+    xg = wl.to_device(x_storage, xspec, _dev())[1]
+    dyg = wl.to_device(dy_storage, dyspec, _dev())[1]
+    size = dwspec.storage_size + 2 * GUARD
+    buf = torch.full((size,), wl.SENTINEL, dtype=torch.int32, device=_dev())
+    dwg = torch.as_strided(buf, dwspec.dims, dwspec.strides, dwspec.offset + GUARD)
+    print(f"[gpu] wgrad {label} x={xspec.dims}/{xspec.strides} dy={dyspec.dims}/{dyspec.strides} "
+          f"dw={dwspec.dims}/{dwspec.strides} pre={pre} post={post} stride={st} dil={dl} "
+          f"mode={mode} entry={entry}", flush=True)
+    if entry == "ws":
+        ci8.conv_wgrad_i8(xg, dyg, dwg, pre, post, st, dl, mode=mode)
+    else:
+        ci8.conv_wgrad_i8_plain(xg, dyg, dwg, pre, post, st, dl, mode=mode)
+    torch.cuda.synchronize()
+    got = buf.cpu()
+    ref = torch.full((size,), wl.SENTINEL, dtype=torch.int32)
+    rv = torch.as_strided(ref, dwspec.dims, dwspec.strides, dwspec.offset + GUARD)
+    oracle.conv_wgrad(x_cpu, dy_cpu, None, pre, post, st, dl, out=rv, mode=mode)
+    if not torch.equal(got, ref):
+        diff = (got != ref).nonzero().reshape(-1)
+        raise AssertionError(f"{label}: {diff.numel()} elements differ, first at {diff[:5].tolist()}: "
+                             f"got {got[diff[:5]].tolist()} want {ref[diff[:5]].tolist()}")
+
+
+@pytest.mark.parametrize("name,mode", [(n, 0) for n in wl.CASE_ORDER] +
+                         [("tiny_5x5_r3", 1), ("downsample_s2_n8_c64_56", 1),
+                          ("dilated_asym_n16_c96_64x48", 1)])
+def test_workload_wgrad(ci8, name, mode):
+    """The weight gradient of every workload: the workload's image, a loss in
+    the forward output's layout, dW in the filter's layout."""
+    c = wl.case(name)
+    d = wl.make_inputs(c, c.seed_base + 4)
+    dyspec = wl.TensorSpec(c.out.dims, c.out.strides)
+    dwspec = wl.TensorSpec(c.filter.dims, c.filter.strides)
+    run_wgrad_check(ci8, d["x_storage"], c.image, _rand_storage(dyspec, 7 + mode), dyspec, dwspec,
+                    c.pre, c.post, c.stride, c.dilation, mode=mode, label=name)
+
+
+def test_random_wgrad_problems(ci8):
+    """Strides, dilations, padding beyond the taps' reach (all-padding taps),
+    non-square filters, NCHW/NHWC/KCRS/KRSC layouts, both modes."""
+    rng = np.random.default_rng(53)
+    done = 0
+    while done < 40:
+        N, K, C = int(rng.integers(1, 5)), int(rng.integers(1, 70)), int(rng.integers(1, 70))
+        H, W = (int(v) for v in rng.integers(1, 20, 2))
+        R, S = (int(v) for v in rng.integers(1, 6, 2))
+        pre = tuple(int(v) for v in rng.integers(0, 6, 2))
+        post = tuple(int(v) for v in rng.integers(0, 5, 2))
+        st = tuple(int(v) for v in rng.integers(1, 5, 2))
+        dl = tuple(int(v) for v in rng.integers(1, 4, 2))
+        try:
+            od = oracle.out_dims((N, C, H, W), (K, C, R, S), pre, post, st, dl)
+        except oracle.OracleError:
+            continue
+        lay = lambda d: (wl.channels_last_strides(d) if rng.integers(0, 2) else wl.contiguous_strides(d))
+        xspec = wl.TensorSpec((N, C, H, W), lay((N, C, H, W)))
+        dyspec = wl.TensorSpec(od, lay(od))
+        dwspec = wl.TensorSpec((K, C, R, S), lay((K, C, R, S)))
+        run_wgrad_check(ci8, _rand_storage(xspec, 300 + done), xspec, _rand_storage(dyspec, 400 + done),
+                        dyspec, dwspec, pre, post, st, dl, mode=done % 2, label=f"random {done}",
+                        entry="plain" if done % 5 == 0 else "ws")
+        done += 1
