@@ -416,10 +416,12 @@ RepackJob repack_job(const T4 &t, const int8_t *src, int8_t *dst, int64_t Cp, in
         j.mode = kRepackXFast;
     else if (C > 1 && s1 <= 8)
         j.mode = kRepackCFast;
+    else if (A > 1 && s0 >= 1 && s0 <= 8)
+        j.mode = kRepackAFast;  // a transposed view: tiles walk a at each (y, x)
     else
         j.mode = kRepackGather;
-    const int64_t tx = (X + 63) / 64, tc = (Cp + 63) / 64;
-    const int64_t tiles = A * Y * tx * tc;
+    const int64_t tx = ((j.mode == kRepackAFast ? A : X) + 63) / 64, tc = (Cp + 63) / 64;
+    const int64_t tiles = (j.mode == kRepackAFast ? Y * X : A * Y) * tx * tc;
     if (tiles64)
         *tiles64 = tiles;
     j.tiles_x = (int)tx;
@@ -673,7 +675,8 @@ conv_i8_status_t launch_repacks(const RepackJob *jobs, int njobs, hipStream_t st
     for (int i = 0; i < r.njobs; ++i) {
         const RepackJob &j = r.job[i];
         if (j.mode != kRepackGather)
-            step = std::max<int64_t>(step, j.mode == kRepackXFast ? j.sx : j.s1);
+            step = std::max<int64_t>(step, j.mode == kRepackXFast ? j.sx
+                                           : j.mode == kRepackAFast ? j.s0 : j.s1);
     }
     const dim3 grid((unsigned)total);
     if (step <= 2)

@@ -7,13 +7,15 @@
 //
 // The memory layout decides the cost here ("Building a From-Scratch INT8
 // Strided Convolution Kernel", "Key Takeaways").  A workgroup moves a tile of
-// 64 positions x 64 channels of one (a, y) row.  When one of the two walks
-// (along x, or along c) has a small stride (at most 8 bytes), the tile's 64
-// lines along that walk are read as aligned 16-byte vectors into LDS (every
-// vector holds at least one wanted byte, so no vector leaves the pages the
-// tensor occupies), and the wanted bytes are picked out of LDS; otherwise
-// every element is read on its own.  Each thread then writes one 16-byte
-// vector of 16 consecutive channels.  One launch serves up to two tensors.
+// 64 positions x 64 channels: 64 x-positions of one (a, y) row, or, for a
+// transposed view whose first dim is the contiguous one, 64 a-values at one
+// (y, x).  When one walk (along x, along c, or along a) has a small stride
+// (at most 8 bytes), the tile's 64 lines along that walk are read as aligned
+// 16-byte vectors into LDS (every vector holds at least one wanted byte, so
+// no vector leaves the pages the tensor occupies), and the wanted bytes are
+// picked out of LDS; otherwise every element is read on its own.  Each
+// thread then writes one 16-byte vector of 16 consecutive channels.  One
+// launch serves up to two tensors.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -24,7 +26,9 @@ namespace convi8 {
 enum RepackMode : int {
     kRepackXFast = 0,   // stride along x <= 8 bytes: lines along x
     kRepackCFast = 1,   // stride along c <= 8 bytes: lines along c
-    kRepackGather = 2,  // neither: one load per element
+    kRepackGather = 2,  // none: one load per element
+    kRepackAFast = 3,   // stride along a <= 8 bytes: tiles of 64 a-values at one (y, x),
+                        // lines along a (a transposed view)
 };
 
 struct RepackJob {
@@ -32,7 +36,7 @@ struct RepackJob {
     long long s0, s1, sy, sx;        // element strides of [A, C, Y, X]
     int A, C, Y, X, Cp;
     int mode;
-    int tiles_x, tiles_c;            // 64-wide tiles along x and along Cp
+    int tiles_x, tiles_c;            // 64-wide tiles along x (along a for kRepackAFast) and Cp
     int tiles;                       // A * Y * tiles_x * tiles_c
     int8_t *dst;                     // packed [A][Y][X][Cp]
 };
@@ -63,15 +67,19 @@ __global__ __launch_bounds__(256) void repack_to_channels_last_kernel(RepackArgs
         bid -= (unsigned)args.job[0].tiles;
 
     const int tid = threadIdx.x;
+    const bool af = j.mode == kRepackAFast;
     const int ct = (int)(bid % (unsigned)j.tiles_c);
-    const int xt = (int)((bid / (unsigned)j.tiles_c) % (unsigned)j.tiles_x);
-    const int ay = (int)(bid / ((unsigned)j.tiles_c * (unsigned)j.tiles_x));
-    const int ai = ay / j.Y;
-    const int yi = ay - ai * j.Y;
-    const int x0 = xt * 64, c0 = ct * 64;
-    const int xn = min(64, j.X - x0);        // positions in this tile
+    const int pt = (int)((bid / (unsigned)j.tiles_c) % (unsigned)j.tiles_x);
+    const int outer = (int)(bid / ((unsigned)j.tiles_c * (unsigned)j.tiles_x));
+    // x-tiles: outer = (a, y), the tile walks x; a-tiles: outer = (y, x), it walks a
+    const int o_hi = af ? outer / j.X : outer / j.Y;
+    const int o_lo = af ? outer - o_hi * j.X : outer - o_hi * j.Y;
+    const int ai = af ? 0 : o_hi, yi = af ? o_hi : o_lo, xi = af ? o_lo : 0;
+    const int x0 = pt * 64, c0 = ct * 64;    // x0: first x (or first a) of the tile
+    const int xn = min(64, (af ? j.A : j.X) - x0);  // positions in this tile
     const int cn = max(0, min(64, j.C - c0)); // real channels in this tile (the rest pad with zeros)
-    const int8_t *row = j.src + ai * j.s0 + yi * j.sy;
+    const int8_t *row = j.src + (long long)ai * j.s0 + (long long)yi * j.sy + (long long)xi * j.sx;
+    const long long pstride = af ? j.s0 : j.sx;  // stride between the tile's positions
 
     // output vector of this thread: position x0 + xl, channels c0 + cq*16 .. +16
     const int xl = tid >> 2, cq = tid & 3;
@@ -84,16 +92,16 @@ __global__ __launch_bounds__(256) void repack_to_channels_last_kernel(RepackArgs
             for (int i = 0; i < 16; ++i) {
                 const int cl = cq * 16 + i;
                 if (cl < cn)
-                    v[i >> 2] |= (int)(uint8_t)row[(long long)(c0 + cl) * j.s1 + (long long)(x0 + xl) * j.sx] << (8 * (i & 3));
+                    v[i >> 2] |= (int)(uint8_t)row[(long long)(c0 + cl) * j.s1 + (long long)(x0 + xl) * pstride] << (8 * (i & 3));
             }
         }
     } else {
-        // line l of the tile: channel c0+l (x-fast) or position x0+l (c-fast);
-        // it runs over the other index with stride `step`.  Four threads
-        // share a line and fetch every fourth of its aligned vectors.
-        const bool xf = j.mode == kRepackXFast;
-        const long long lstride = xf ? j.s1 : j.sx;
-        const int step = (int)(xf ? j.sx : j.s1);
+        // line l of the tile: channel c0+l (x-fast, a-fast) or position x0+l
+        // (c-fast); it runs over the other index with stride `step`.  Four
+        // threads share a line and fetch every fourth of its aligned vectors.
+        const bool xf = j.mode != kRepackCFast;
+        const long long lstride = xf ? j.s1 : pstride;
+        const int step = (int)(xf ? pstride : j.s1);
         const int nlines = xf ? cn : xn;
         const int nalong = xf ? xn : cn;
         const int8_t *line0 = row + (long long)(xf ? x0 : c0) * step + (long long)(xf ? c0 : x0) * lstride;
@@ -125,7 +133,9 @@ __global__ __launch_bounds__(256) void repack_to_channels_last_kernel(RepackArgs
         }
     }
     if (out_ok) {
-        int8_t *d = j.dst + (((long long)ai * j.Y + yi) * j.X + x0 + xl) * j.Cp + c0 + cq * 16;
+        const long long pos = af ? ((long long)(x0 + xl) * j.Y + yi) * j.X + xi
+                                 : ((long long)ai * j.Y + yi) * j.X + x0 + xl;
+        int8_t *d = j.dst + pos * j.Cp + c0 + cq * 16;
         *(int4 *)d = int4{v[0], v[1], v[2], v[3]};
     }
 }
