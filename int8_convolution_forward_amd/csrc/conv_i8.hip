@@ -107,6 +107,9 @@ struct Problem {
     int64_t mode;      // CONV_I8_MODE_*: 1 reads filter tap (R-1-r, S-1-s)
     int64_t flip_out;  // 1: output (p, q) is written at (P-1-p, Q-1-q) (weight gradient
                        // of true convolution); never set by a caller's descriptor
+    int64_t split_ok;  // 1: an im2col launch with few tiles and a long inner dimension may
+                       // split it over gridDim.y (the output is zeroed first, partial
+                       // sums added atomically); set only for the weight gradient
 };
 
 conv_i8_status_t read_params(const int64_t *pre, const int64_t *post, const int64_t *stride,
@@ -187,6 +190,7 @@ conv_i8_status_t analyze(const conv_i8_desc_t *image, const conv_i8_desc_t *filt
         return CONV_I8_ERR_PARAM;
     pb->mode = mode;
     pb->flip_out = 0;
+    pb->split_ok = 0;
     // The output dtype is checked like every other field: the plain entries
     // refuse an INT8 output descriptor rather than write saturated bytes into
     // it; only the requantising entries write INT8.
@@ -765,6 +769,8 @@ conv_i8_status_t run(const Problem &pb, const Plan &pl, const void *x_ptr, const
     a.Pr = (int)pl.Pr;
     a.inv_pr = pl.Pr > 0 ? 1.0f / (float)pl.Pr : 0.0f;
     a.ncblk = (int)(pl.Cp / 64);
+    a.ksplit = 1;
+    a.kchunk = 0x7fffffff;
     if (rq) {
         a.q8 = 1;
         a.q_scale = rq->scale;
@@ -796,7 +802,31 @@ conv_i8_status_t run(const Problem &pb, const Plan &pl, const void *x_ptr, const
         if (tiles == 0)
             continue;
         a.tiles = (int)tiles;
-        c.launch(!pl.blocked, pl.pix_j, dim3((unsigned)tiles), stream, a);
+        unsigned ksplit = 1;
+        if (pb.split_ok && !rq && c.kind == kIm2col && tiles < kCUs / 2 && a.nstages >= 32) {
+            // a few tiles over a long inner dimension (the weight gradient):
+            // split it so that about one workgroup runs per CU, at least 16
+            // stages each; partial sums meet in the zeroed output atomically.
+            // (With more than half of the CUs busy, the atomics and their
+            // contention on one tile's lines cost more than the split gains:
+            // 75 -> 167 us on the large-channel weight gradient, 144 tiles.)
+            const int64_t want = std::min<int64_t>((kCUs + tiles - 1) / tiles, a.nstages / 16);
+            if (want > 1) {
+                const int64_t chunk = (a.nstages + want - 1) / want;
+                ksplit = (unsigned)((a.nstages + chunk - 1) / chunk);
+                // zeros first: the same kernel with no stages stores zeros
+                IgemmArgs z = a;
+                z.nstages = 0;
+                c.launch(!pl.blocked, pl.pix_j, dim3((unsigned)tiles), stream, z);
+                if (hipGetLastError() != hipSuccess)
+                    return CONV_I8_ERR_HIP;
+                a.kchunk = (int)chunk;
+                a.ksplit = (int)ksplit;
+            }
+        }
+        c.launch(!pl.blocked, pl.pix_j, dim3((unsigned)tiles, ksplit), stream, a);
+        a.ksplit = 1;
+        a.kchunk = 0x7fffffff;
         if (hipGetLastError() != hipSuccess)
             return CONV_I8_ERR_HIP;
     }
@@ -822,7 +852,8 @@ conv_i8_status_t prepare(const conv_i8_desc_t *image, const void *image_ptr,
                          const conv_i8_desc_t *out, const int64_t *pre, const int64_t *post,
                          const int64_t *stride, const int64_t *dil, Problem *pb, Plan *pl,
                          int32_t out_dtype = CONV_I8_DT_INT32,
-                         int32_t mode = CONV_I8_MODE_CROSS_CORRELATION, bool flip_out = false)
+                         int32_t mode = CONV_I8_MODE_CROSS_CORRELATION, bool flip_out = false,
+                         bool split_ok = false)
 {
     // The plan does not depend on the output dtype (it works in elements) nor
     // on the mode (the kernels read the taps in either order).
@@ -830,6 +861,7 @@ conv_i8_status_t prepare(const conv_i8_desc_t *image, const void *image_ptr,
     if (st != CONV_I8_OK)
         return st;
     pb->flip_out = flip_out ? 1 : 0;
+    pb->split_ok = split_ok ? 1 : 0;
     PlanKey key;
     memset(&key, 0, sizeof key);  // padding takes part in the comparison
     static_assert(sizeof(Problem) % 8 == 0, "Problem has no tail padding to clear");
@@ -942,12 +974,12 @@ conv_i8_status_t entry_run(const conv_i8_desc_t *image, const void *image_ptr,
                            const int64_t *post, const int64_t *stride, const int64_t *dil,
                            int32_t out_dtype, int32_t mode, const conv_i8_requant_t *rq, bool alloc,
                            void *workspace, size_t workspace_bytes, void *stream,
-                           bool flip_out = false)
+                           bool flip_out = false, bool split_ok = false)
 {
     Problem pb;
     Plan pl;
     conv_i8_status_t st = prepare(image, image_ptr, filter, filter_ptr, out, pre, post, stride,
-                                  dil, &pb, &pl, out_dtype, mode, flip_out);
+                                  dil, &pb, &pl, out_dtype, mode, flip_out, split_ok);
     if (st != CONV_I8_OK)
         return st;
     if (out_dtype == CONV_I8_DT_INT8 && (st = check_requant(rq)) != CONV_I8_OK)
@@ -1410,9 +1442,11 @@ conv_i8_status_t wgrad_entry(const conv_i8_desc_t *image, const void *image_ptr,
                       [&](const conv_i8_desc_t *i, const void *x, const conv_i8_desc_t *f,
                           const void *w, const conv_i8_desc_t *o, void *y, const int64_t *a,
                           const int64_t *b, const int64_t *c, const int64_t *d, bool fl) {
+                          // split_ok: the long inner dimension may be split over
+                          // workgroups that add into the output (zeroed first)
                           return entry_run(i, x, f, w, o, y, a, b, c, d, CONV_I8_DT_INT32,
                                            CONV_I8_MODE_CROSS_CORRELATION, nullptr, alloc,
-                                           workspace, workspace_bytes, stream, fl);
+                                           workspace, workspace_bytes, stream, fl, true);
                       });
 }
 

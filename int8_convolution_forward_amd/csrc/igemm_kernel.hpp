@@ -114,8 +114,18 @@ __global__ __launch_bounds__(64 * WGM * WGN) void conv_igemm_kernel(IgemmArgs a)
     // blocked: (r, s, cpos) uniform, cpos = channel-block byte offset, stepped
     // with selects; flat: each thread's chunk index g = stage*CPS + j is split
     // into (r, s, c16) afresh for every stage.
+    // split z of the inner dimension: stages [stage0, stage_end)
+    const int stage0 = (int)blockIdx.y * a.kchunk;
+    const int stage_end = min(a.nstages, stage0 + a.kchunk);
     int r = 0, s = 0, cpos = 0;
-    int issued = 0;
+    int issued = stage0;
+    if constexpr (!FLAT) {
+        // blocked order: stage = (channel block * R + r) * S + s
+        const int rs = stage0 % (a.R * a.S);
+        s = rs % a.S;
+        r = rs / a.S;
+        cpos = stage0 / (a.R * a.S) * BK;
+    }
 
     const unsigned smem_lds = lds_address(smem);
     const v4i img_rsrc = make_rsrc(a.img, a.img_range);
@@ -137,7 +147,7 @@ __global__ __launch_bounds__(64 * WGM * WGN) void conv_igemm_kernel(IgemmArgs a)
             s = rs - r * a.S;
             cpos = c16 * 16;
         }
-        const bool live = issued < a.nstages && (!FLAT || r < a.R);
+        const bool live = issued < stage_end && (!FLAT || r < a.R);
         rdh = live ? r * a.dilH : -0x20000000;  // dead stage: every row fails the bounds test
         sdw = s * a.dilW;
         itoff = rdh * a.sH + sdw * a.sW + cpos;
@@ -233,7 +243,7 @@ __global__ __launch_bounds__(64 * WGM * WGN) void conv_igemm_kernel(IgemmArgs a)
     // ---- main loop --------------------------------------------------------
     // An odd stage count runs one extra all-zero stage, so the loop body
     // (two stages, one per fragment buffer) has no branch inside it.
-    const int nloop = (a.nstages + 1) & ~1;
+    const int nloop = (max(stage_end - stage0, 0) + 1) & ~1;
     if (nloop > 0) {
 #pragma unroll
         for (int st = 0; st < NS; ++st)
@@ -253,7 +263,7 @@ __global__ __launch_bounds__(64 * WGM * WGN) void conv_igemm_kernel(IgemmArgs a)
     __syncthreads();
 
     // ---- epilogue ---------------------------------------------------------
-    store_tile_any<FM, FN, PIX_J>(a, acc, m0, n0, wm, wn, lane, out_row);
+    store_tile_any<FM, FN, PIX_J, true>(a, acc, m0, n0, wm, wn, lane, out_row);
 }
 
 }  // namespace convi8

@@ -72,6 +72,11 @@ struct IgemmArgs {
     int q8;
     int q8_pack;          // channel stride 1, K, pix_stride and out 4-byte multiples:
                           // four channels of a pixel go out as one dword
+    // split of the inner dimension over gridDim.y (im2col kernel): split z
+    // runs stages [z*kchunk, min((z+1)*kchunk, nstages)) and adds its partial
+    // sums to the (zeroed) output with int32 atomics; ksplit 1: plain stores
+    int ksplit;
+    int kchunk;
 };
 
 // Requantising INT8 epilogue of one exact sum: the sum as a float, one fused
@@ -206,7 +211,7 @@ __device__ __forceinline__ void fill_out_rows(const IgemmArgs &a, int m0, int *o
 // MFMA column l%32; rows come from the first MFMA operand.  Elements past M or
 // K get an out-of-range offset and the buffer store drops them, so no branch
 // guards a store.
-template <int FM, int FN, bool PIX_J, bool Q8 = false>
+template <int FM, int FN, bool PIX_J, bool Q8 = false, bool ATOM = false>
 __device__ __forceinline__ void store_tile(const IgemmArgs &a, v16i (&acc)[FM][FN], int m0, int n0,
                                            int wm, int wn, int lane, const int *out_row)
 {
@@ -218,6 +223,8 @@ __device__ __forceinline__ void store_tile(const IgemmArgs &a, v16i (&acc)[FM][F
         if constexpr (Q8)
             __builtin_amdgcn_raw_buffer_store_b8((unsigned char)requant_i8(v, qs, qb, relu), out_rsrc,
                                                  off, 0, 0);
+        else if constexpr (ATOM)
+            (void)__builtin_amdgcn_raw_ptr_buffer_atomic_add_i32(v, out_rsrc, off, 0, 0);
         else
             __builtin_amdgcn_raw_buffer_store_b32(v, out_rsrc, off, 0, 0);
     };
@@ -331,13 +338,17 @@ __device__ __forceinline__ void store_tile(const IgemmArgs &a, v16i (&acc)[FM][F
     }
 }
 
-// store_tile with the epilogue the arguments ask for.
-template <int FM, int FN, bool PIX_J>
+// store_tile with the epilogue the arguments ask for (SPLIT: the kernel may
+// run with a split inner dimension, whose partial sums are added atomically;
+// integer adds make the result independent of their order).
+template <int FM, int FN, bool PIX_J, bool SPLIT = false>
 __device__ __forceinline__ void store_tile_any(const IgemmArgs &a, v16i (&acc)[FM][FN], int m0, int n0,
                                                int wm, int wn, int lane, const int *out_row)
 {
     if (a.q8)
         store_tile<FM, FN, PIX_J, true>(a, acc, m0, n0, wm, wn, lane, out_row);
+    else if (SPLIT && a.ksplit > 1)
+        store_tile<FM, FN, PIX_J, false, SPLIT>(a, acc, m0, n0, wm, wn, lane, out_row);
     else
         store_tile<FM, FN, PIX_J, false>(a, acc, m0, n0, wm, wn, lane, out_row);
 }

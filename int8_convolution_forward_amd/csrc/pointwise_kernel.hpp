@@ -84,7 +84,9 @@ __global__ __launch_bounds__(256) void conv_pointwise_kernel(IgemmArgs a)
         if (q8)
             requant_params(a, y * 32 + (lane & 31), qs[y], qb[y]);
     }
-#pragma unroll
+    // fully unrolled (afr[t] must stay in registers): the loop body is long
+    // enough that a plain unroll hint is not always taken
+#pragma clang loop unroll(full)
     for (int t = 0; t < TPW; ++t) {
         v16i acc[FN];
 #pragma unroll
