@@ -17,6 +17,9 @@ typedef __attribute__((address_space(3))) void lds_void;
 constexpr int kOutOfRange = (int)0x80000000u;
 // Buffer resource word 3 for gfx9-family raw buffer access (32-bit data format).
 constexpr int kRsrcWord3 = 0x00020000;
+// Cache policy of the output stores: non-temporal (the results are not read
+// again by this kernel; streaming them shortens the write-back at the end)
+constexpr int kOutStorePolicy = 2;
 
 // floor(n / d) for 0 <= n < 2^31 as (umulhi(n, m) + n) >> l, with
 // l = ceil(log2 d) and m = floor(2^32 (2^l - d) / d) + 1 (computed on the host).
@@ -222,11 +225,11 @@ __device__ __forceinline__ void store_tile(const IgemmArgs &a, v16i (&acc)[FM][F
     auto put = [&](int v, int off, float qs, float qb) {
         if constexpr (Q8)
             __builtin_amdgcn_raw_buffer_store_b8((unsigned char)requant_i8(v, qs, qb, relu), out_rsrc,
-                                                 off, 0, 0);
+                                                 off, 0, kOutStorePolicy);
         else if constexpr (ATOM)
             (void)__builtin_amdgcn_raw_ptr_buffer_atomic_add_i32(v, out_rsrc, off, 0, 0);
         else
-            __builtin_amdgcn_raw_buffer_store_b32(v, out_rsrc, off, 0, 0);
+            __builtin_amdgcn_raw_buffer_store_b32(v, out_rsrc, off, 0, kOutStorePolicy);
     };
     const int mcol = lane & 31;
     const int mrow0 = 4 * (lane >> 5);
@@ -290,7 +293,7 @@ __device__ __forceinline__ void store_tile(const IgemmArgs &a, v16i (&acc)[FM][F
                     wv = quad_transpose_bytes(wv, lane);
                     const int m = mb + 8 * i + (lane & 3);
                     const int off = (k_ok && m < a.M) ? m * a.pix_stride + kq : kOutOfRange;
-                    __builtin_amdgcn_raw_buffer_store_b32((int)wv, out_rsrc, off, 0, 0);
+                    __builtin_amdgcn_raw_buffer_store_b32((int)wv, out_rsrc, off, 0, kOutStorePolicy);
                 }
             }
         }

@@ -118,7 +118,7 @@ __global__ __launch_bounds__(256) void conv_pointwise_kernel(IgemmArgs a)
                     wv = quad_transpose_bytes(wv, lane);
                     const int m = mb + 8 * i + (lane & 3);
                     const int off = (kq < a.K && m < a.M) ? m * a.pix_stride + kq : kOutOfRange;
-                    __builtin_amdgcn_raw_buffer_store_b32((int)wv, out_rsrc, off, 0, 0);
+                    __builtin_amdgcn_raw_buffer_store_b32((int)wv, out_rsrc, off, 0, kOutStorePolicy);
                 }
             } else if (q8) {
 #pragma unroll
@@ -126,14 +126,14 @@ __global__ __launch_bounds__(256) void conv_pointwise_kernel(IgemmArgs a)
                     const int m = mb + 8 * (v >> 2) + (v & 3);
                     const int off = (k_ok && m < a.M) ? m * a.pix_stride + kk * a.oK : kOutOfRange;
                     __builtin_amdgcn_raw_buffer_store_b8(
-                        (unsigned char)requant_i8(acc[y][v], qs[y], qb[y], relu), out_rsrc, off, 0, 0);
+                        (unsigned char)requant_i8(acc[y][v], qs[y], qb[y], relu), out_rsrc, off, 0, kOutStorePolicy);
                 }
             } else {
 #pragma unroll
                 for (int v = 0; v < 16; ++v) {
                     const int m = mb + 8 * (v >> 2) + (v & 3);
                     const int off = (k_ok && m < a.M) ? (m * a.pix_stride + kk * a.oK) * 4 : kOutOfRange;
-                    __builtin_amdgcn_raw_buffer_store_b32(acc[y][v], out_rsrc, off, 0, 0);
+                    __builtin_amdgcn_raw_buffer_store_b32(acc[y][v], out_rsrc, off, 0, kOutStorePolicy);
                 }
             }
         }
