@@ -136,7 +136,10 @@ __global__ __launch_bounds__(256) void repack_to_channels_last_kernel(RepackArgs
         const long long pos = af ? ((long long)(x0 + xl) * j.Y + yi) * j.X + xi
                                  : ((long long)ai * j.Y + yi) * j.X + x0 + xl;
         int8_t *d = j.dst + pos * j.Cp + c0 + cq * 16;
-        *(int4 *)d = int4{v[0], v[1], v[2], v[3]};
+        // non-temporal: the packed copy is read by the next kernel, after the
+        // write-back at this kernel's end, not from this CU's caches
+        typedef int i32x4 __attribute__((ext_vector_type(4)));
+        __builtin_nontemporal_store(i32x4{v[0], v[1], v[2], v[3]}, (i32x4 *)d);
     }
 }
 
