@@ -271,6 +271,8 @@ const TileCfg kTiles[] = {
     {"w256x128x64", 256, 128, 64, 4, 8, kIm2col, 0, 0.56, launch_cfg<256, 128, 64, 4, 4, 2>},
     {"w128x128x64", 128, 128, 64, 4, 8, kIm2col, 0, 0.56, launch_cfg<128, 128, 64, 4, 4, 2>},
     {"w256x128x128", 256, 128, 128, 3, 8, kIm2col, 0, 0.76, launch_cfg<256, 128, 128, 3, 4, 2>},
+    // 192 output channels in one column tile (no half-empty second tile)
+    {"w128x192x128", 128, 192, 128, 3, 8, kIm2col, 0, 0.62, launch_cfg<128, 192, 128, 3, 4, 2>},
     {"f256x128", 256, 128, 64, 6, 4, kFootprint, 448, 0.70, launch_fp3x3<256, 128, 6, 448>},
     {"fw256x128", 256, 128, 64, 3, 8, kFootprint, 448, 0.68, launch_fp3x3<256, 128, 3, 448, 4, 2>},
     {"f128x128", 128, 128, 64, 6, 4, kFootprint, 384, 0.62, launch_fp3x3<128, 128, 6, 384>},

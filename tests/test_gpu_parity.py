@@ -131,7 +131,7 @@ def test_repeat_runs_identical(ci8):
 # blocked and flat inner order, channel- and pixel-innermost outputs.
 # ---------------------------------------------------------------------------
 TILES = ["64x64x64", "128x64x64", "64x128x64", "128x128x64", "128x128x128", "256x128x64",
-         "128x256x64", "w256x128x64", "w128x128x64", "w256x128x128", "f256x128", "fw256x128",
+         "128x256x64", "w256x128x64", "w128x128x64", "w256x128x128", "w128x192x128", "f256x128", "fw256x128",
          "f128x128", "fk256x128", "fk128x128"]
 FOOTPRINT_TILES = [t for t in TILES if t.startswith("f")]
 
