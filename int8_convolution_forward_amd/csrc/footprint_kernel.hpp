@@ -114,7 +114,7 @@ __global__ __launch_bounds__(64 * WGM * WGN * KSPL) void conv_footprint3x3_kerne
     constexpr int NRD = KS * (FM + FN);
     static_assert(BL >= 1 && TN * BK % GB == 0, "filter tile must fill workgroup loads");
     static_assert((2 * kTaps) % NS == 0 && NS >= 2 && NS <= kTaps, "ring depth must divide 18");
-    static_assert(FM >= 1 && FN >= 1, "wave tile");
+    static_assert(FM >= 1 && FN >= 1 && NMF >= 2, "wave tile");
     static_assert(NW == 4 || NW == 8, "4 or 8 waves");
     static_assert(KSPL == 1 || (KSPL == 2 && FN % 2 == 0 && NS * TN * BK >= NW * (FN / 2) * 4096),
                   "channel split: even wave-tile columns, exchange fits the ring");
@@ -308,18 +308,27 @@ __global__ __launch_bounds__(64 * WGM * WGN * KSPL) void conv_footprint3x3_kerne
             const int rtoff = tap_read(rt);
             constexpr int npc = pieces_at<NS, NG>(lt);
             constexpr int gp0 = first_piece<NS, NG>(lt);
-            constexpr int nother = BL + npc + NRD;
 #pragma unroll
             for (int q = 0; q < NMF; ++q) {
                 mfma_one(buf, q);
+                // the fragment reads of stage u+1 ride on the first half of
+                // the MFMAs, so the last of them has half a stage to land
+                // before the wait at the top of the next stage; the loads of
+                // stage u+NS (long latency, awaited NS-1 stages later) take
+                // the second half
+                constexpr int H = NMF / 2, NL = BL + npc;
+                if (q < H) {
 #pragma unroll
-                for (int o = q * nother / NMF; o < (q + 1) * nother / NMF; ++o) {
-                    if (o < BL)
-                        dma_filter(slot, lcb, lt, o);
-                    else if (o < BL + npc)
-                        dma_piece(lcb + 1, (lv / kTaps + 1) & 1, gp0 + (o - BL));
-                    else
-                        read_one(buf ^ 1, rslot, rfb, rtoff, o - BL - npc);
+                    for (int o = q * NRD / H; o < (q + 1) * NRD / H; ++o)
+                        read_one(buf ^ 1, rslot, rfb, rtoff, o);
+                } else {
+#pragma unroll
+                    for (int o = (q - H) * NL / (NMF - H); o < (q - H + 1) * NL / (NMF - H); ++o) {
+                        if (o < BL)
+                            dma_filter(slot, lcb, lt, o);
+                        else
+                            dma_piece(lcb + 1, (lv / kTaps + 1) & 1, gp0 + (o - BL));
+                    }
                 }
                 // keep the loads and reads where they are: spread between the
                 // MFMAs (left to itself the scheduler bunches the reads at the
