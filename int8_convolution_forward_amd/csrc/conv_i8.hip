@@ -773,6 +773,10 @@ conv_i8_status_t run(const Problem &pb, const Plan &pl, const void *x_ptr, const
     a.ncblk = (int)(pl.Cp / 64);
     a.ksplit = 1;
     a.kchunk = 0x7fffffff;
+    // stream the output past the L2 only when each store's lanes cover
+    // consecutive elements (whole lines); scattered stores are merged in L2
+    a.out_nt = (pl.pix_j ? (pb.y.s[3] == 1 || pb.Q == 1) && (pb.Q > 1 || pb.y.s[2] == 1)
+                         : pb.y.s[1] == 1) ? 1 : 0;
     if (rq) {
         a.q8 = 1;
         a.q_scale = rq->scale;

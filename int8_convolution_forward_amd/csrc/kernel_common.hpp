@@ -17,9 +17,15 @@ typedef __attribute__((address_space(3))) void lds_void;
 constexpr int kOutOfRange = (int)0x80000000u;
 // Buffer resource word 3 for gfx9-family raw buffer access (32-bit data format).
 constexpr int kRsrcWord3 = 0x00020000;
-// Cache policy of the output stores: non-temporal (the results are not read
-// again by this kernel; streaming them shortens the write-back at the end)
-constexpr int kOutStorePolicy = 2;
+// Cache policy of the output stores when the lanes of a store walk a
+// unit-stride output dimension (IgemmArgs::out_nt): non-temporal, since the
+// results are not read again by this kernel and streaming whole lines
+// shortens the write-back at the end.  Stores scattered over many lines
+// (e.g. a weight gradient written through a filter layout whose contiguous
+// dim is the slowest part of the row index) keep the default policy, so the
+// L2 merges the pieces of each line before it writes them back.
+constexpr int kOutStoreStream = 2;
+constexpr int kOutStoreDefault = 0;
 
 // floor(n / d) for 0 <= n < 2^31 as (umulhi(n, m) + n) >> l, with
 // l = ceil(log2 d) and m = floor(2^32 (2^l - d) / d) + 1 (computed on the host).
@@ -80,6 +86,7 @@ struct IgemmArgs {
     // sums to the (zeroed) output with int32 atomics; ksplit 1: plain stores
     int ksplit;
     int kchunk;
+    int out_nt;           // output stores non-temporal (lanes walk a unit-stride dim)
 };
 
 // Requantising INT8 epilogue of one exact sum: the sum as a float, one fused
@@ -214,7 +221,7 @@ __device__ __forceinline__ void fill_out_rows(const IgemmArgs &a, int m0, int *o
 // MFMA column l%32; rows come from the first MFMA operand.  Elements past M or
 // K get an out-of-range offset and the buffer store drops them, so no branch
 // guards a store.
-template <int FM, int FN, bool PIX_J, bool Q8 = false, bool ATOM = false>
+template <int FM, int FN, bool PIX_J, bool Q8 = false, bool ATOM = false, int POL = kOutStoreStream>
 __device__ __forceinline__ void store_tile(const IgemmArgs &a, v16i (&acc)[FM][FN], int m0, int n0,
                                            int wm, int wn, int lane, const int *out_row)
 {
@@ -225,11 +232,11 @@ __device__ __forceinline__ void store_tile(const IgemmArgs &a, v16i (&acc)[FM][F
     auto put = [&](int v, int off, float qs, float qb) {
         if constexpr (Q8)
             __builtin_amdgcn_raw_buffer_store_b8((unsigned char)requant_i8(v, qs, qb, relu), out_rsrc,
-                                                 off, 0, kOutStorePolicy);
+                                                 off, 0, POL);
         else if constexpr (ATOM)
             (void)__builtin_amdgcn_raw_ptr_buffer_atomic_add_i32(v, out_rsrc, off, 0, 0);
         else
-            __builtin_amdgcn_raw_buffer_store_b32(v, out_rsrc, off, 0, kOutStorePolicy);
+            __builtin_amdgcn_raw_buffer_store_b32(v, out_rsrc, off, 0, POL);
     };
     const int mcol = lane & 31;
     const int mrow0 = 4 * (lane >> 5);
@@ -293,7 +300,7 @@ __device__ __forceinline__ void store_tile(const IgemmArgs &a, v16i (&acc)[FM][F
                     wv = quad_transpose_bytes(wv, lane);
                     const int m = mb + 8 * i + (lane & 3);
                     const int off = (k_ok && m < a.M) ? m * a.pix_stride + kq : kOutOfRange;
-                    __builtin_amdgcn_raw_buffer_store_b32((int)wv, out_rsrc, off, 0, kOutStorePolicy);
+                    __builtin_amdgcn_raw_buffer_store_b32((int)wv, out_rsrc, off, 0, POL);
                 }
             }
         }
@@ -348,12 +355,19 @@ template <int FM, int FN, bool PIX_J, bool SPLIT = false>
 __device__ __forceinline__ void store_tile_any(const IgemmArgs &a, v16i (&acc)[FM][FN], int m0, int n0,
                                                int wm, int wn, int lane, const int *out_row)
 {
-    if (a.q8)
-        store_tile<FM, FN, PIX_J, true>(a, acc, m0, n0, wm, wn, lane, out_row);
-    else if (SPLIT && a.ksplit > 1)
+    if (a.q8) {
+        if (a.out_nt)
+            store_tile<FM, FN, PIX_J, true, false, kOutStoreStream>(a, acc, m0, n0, wm, wn, lane, out_row);
+        else
+            store_tile<FM, FN, PIX_J, true, false, kOutStoreDefault>(a, acc, m0, n0, wm, wn, lane, out_row);
+    } else if (SPLIT && a.ksplit > 1) {
         store_tile<FM, FN, PIX_J, false, SPLIT>(a, acc, m0, n0, wm, wn, lane, out_row);
-    else
-        store_tile<FM, FN, PIX_J, false>(a, acc, m0, n0, wm, wn, lane, out_row);
+    } else {
+        if (a.out_nt)
+            store_tile<FM, FN, PIX_J, false, false, kOutStoreStream>(a, acc, m0, n0, wm, wn, lane, out_row);
+        else
+            store_tile<FM, FN, PIX_J, false, false, kOutStoreDefault>(a, acc, m0, n0, wm, wn, lane, out_row);
+    }
 }
 
 }  // namespace convi8

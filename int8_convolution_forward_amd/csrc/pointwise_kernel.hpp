@@ -74,6 +74,21 @@ __global__ __launch_bounds__(256) void conv_pointwise_kernel(IgemmArgs a)
     // ---- multiply and store, tile by tile ----------------------------------
     const __amdgpu_buffer_rsrc_t out_rsrc =
         __builtin_amdgcn_make_buffer_rsrc((void *)a.out, (short)0, a.out_range, kRsrcWord3);
+    // stores with the cache policy the output layout calls for (non-temporal
+    // when the lanes walk unit-stride channels)
+    const bool nt = a.out_nt != 0;
+    auto st32 = [&](int v, int off) {
+        if (nt)
+            __builtin_amdgcn_raw_buffer_store_b32(v, out_rsrc, off, 0, kOutStoreStream);
+        else
+            __builtin_amdgcn_raw_buffer_store_b32(v, out_rsrc, off, 0, kOutStoreDefault);
+    };
+    auto st8 = [&](unsigned char v, int off) {
+        if (nt)
+            __builtin_amdgcn_raw_buffer_store_b8(v, out_rsrc, off, 0, kOutStoreStream);
+        else
+            __builtin_amdgcn_raw_buffer_store_b8(v, out_rsrc, off, 0, kOutStoreDefault);
+    };
     const int mrow0 = 4 * (lane >> 5);
     const bool q8 = a.q8 != 0, relu = a.q_relu != 0;
     float qs[FN], qb[FN];                         // requantising epilogue, per column block
@@ -118,22 +133,21 @@ __global__ __launch_bounds__(256) void conv_pointwise_kernel(IgemmArgs a)
                     wv = quad_transpose_bytes(wv, lane);
                     const int m = mb + 8 * i + (lane & 3);
                     const int off = (kq < a.K && m < a.M) ? m * a.pix_stride + kq : kOutOfRange;
-                    __builtin_amdgcn_raw_buffer_store_b32((int)wv, out_rsrc, off, 0, kOutStorePolicy);
+                    st32((int)wv, off);
                 }
             } else if (q8) {
 #pragma unroll
                 for (int v = 0; v < 16; ++v) {
                     const int m = mb + 8 * (v >> 2) + (v & 3);
                     const int off = (k_ok && m < a.M) ? m * a.pix_stride + kk * a.oK : kOutOfRange;
-                    __builtin_amdgcn_raw_buffer_store_b8(
-                        (unsigned char)requant_i8(acc[y][v], qs[y], qb[y], relu), out_rsrc, off, 0, kOutStorePolicy);
+                    st8((unsigned char)requant_i8(acc[y][v], qs[y], qb[y], relu), off);
                 }
             } else {
 #pragma unroll
                 for (int v = 0; v < 16; ++v) {
                     const int m = mb + 8 * (v >> 2) + (v & 3);
                     const int off = (k_ok && m < a.M) ? (m * a.pix_stride + kk * a.oK) * 4 : kOutOfRange;
-                    __builtin_amdgcn_raw_buffer_store_b32(acc[y][v], out_rsrc, off, 0, kOutStorePolicy);
+                    st32(acc[y][v], off);
                 }
             }
         }
