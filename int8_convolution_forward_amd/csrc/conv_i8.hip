@@ -213,21 +213,32 @@ conv_i8_status_t analyze(const conv_i8_desc_t *image, const conv_i8_desc_t *filt
 // ---------------------------------------------------------------------------
 using Launcher = void (*)(bool flat, bool pix_j, dim3 grid, hipStream_t stream, const IgemmArgs &a);
 
-template <int TM, int TN, int BK, int NS, int WGM = 2, int WGN = 2>
-void launch_cfg(bool flat, bool pix_j, dim3 grid, hipStream_t stream, const IgemmArgs &a)
+template <int TM, int TN, int BK, int NS, int WGM, int WGN, int POL>
+void launch_cfg_pol(bool flat, bool pix_j, dim3 grid, hipStream_t stream, const IgemmArgs &a)
 {
     const dim3 block(64 * WGM * WGN);
     if (flat) {
         if (pix_j)
-            hipLaunchKernelGGL((conv_igemm_kernel<TM, TN, BK, NS, WGM, WGN, true, true>), grid, block, 0, stream, a);
+            hipLaunchKernelGGL((conv_igemm_kernel<TM, TN, BK, NS, WGM, WGN, true, true, POL>), grid, block, 0, stream, a);
         else
-            hipLaunchKernelGGL((conv_igemm_kernel<TM, TN, BK, NS, WGM, WGN, true, false>), grid, block, 0, stream, a);
+            hipLaunchKernelGGL((conv_igemm_kernel<TM, TN, BK, NS, WGM, WGN, true, false, POL>), grid, block, 0, stream, a);
     } else {
         if (pix_j)
-            hipLaunchKernelGGL((conv_igemm_kernel<TM, TN, BK, NS, WGM, WGN, false, true>), grid, block, 0, stream, a);
+            hipLaunchKernelGGL((conv_igemm_kernel<TM, TN, BK, NS, WGM, WGN, false, true, POL>), grid, block, 0, stream, a);
         else
-            hipLaunchKernelGGL((conv_igemm_kernel<TM, TN, BK, NS, WGM, WGN, false, false>), grid, block, 0, stream, a);
+            hipLaunchKernelGGL((conv_igemm_kernel<TM, TN, BK, NS, WGM, WGN, false, false, POL>), grid, block, 0, stream, a);
     }
+}
+
+// streaming output stores when each store's lanes cover consecutive
+// elements, the default policy (L2 merges the lines) when they scatter
+template <int TM, int TN, int BK, int NS, int WGM = 2, int WGN = 2>
+void launch_cfg(bool flat, bool pix_j, dim3 grid, hipStream_t stream, const IgemmArgs &a)
+{
+    if (a.out_nt)
+        launch_cfg_pol<TM, TN, BK, NS, WGM, WGN, kOutStoreStream>(flat, pix_j, grid, stream, a);
+    else
+        launch_cfg_pol<TM, TN, BK, NS, WGM, WGN, kOutStoreDefault>(flat, pix_j, grid, stream, a);
 }
 
 template <int TM, int TN, int NS, int FPIX, int WGM = 2, int WGN = 2, int KSPL = 1>
@@ -245,7 +256,12 @@ constexpr int kPointwiseTilesPerWave = 4;
 template <int FN, int KS>
 void launch_pw(bool, bool, dim3 grid, hipStream_t stream, const IgemmArgs &a)
 {
-    hipLaunchKernelGGL((conv_pointwise_kernel<FN, KS, kPointwiseTilesPerWave>), grid, dim3(256), 0, stream, a);
+    if (a.out_nt)
+        hipLaunchKernelGGL((conv_pointwise_kernel<FN, KS, kPointwiseTilesPerWave, kOutStoreStream>), grid, dim3(256), 0,
+                           stream, a);
+    else
+        hipLaunchKernelGGL((conv_pointwise_kernel<FN, KS, kPointwiseTilesPerWave, kOutStoreDefault>), grid, dim3(256), 0,
+                           stream, a);
 }
 
 enum KernelKind { kIm2col = 0, kFootprint = 1, kPointwise = 2 };

@@ -342,6 +342,9 @@ __global__ __launch_bounds__(64 * WGM * WGN * KSPL) void conv_footprint3x3_kerne
     wait_vm_lgkm0<0>();
     __syncthreads();
 
+    // streaming stores whatever the layout: the outputs this kernel serves
+    // (forward and data gradient) have a unit-stride channel or column dim,
+    // and for any other layout the policy costs speed, not correctness
     if constexpr (KSPL == 1) {
         store_tile_any<FM, FN, PIX_J>(a, acc, m0, n0, wm, wn, lane, out_row);
     } else {

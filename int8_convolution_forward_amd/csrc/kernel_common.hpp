@@ -86,7 +86,8 @@ struct IgemmArgs {
     // sums to the (zeroed) output with int32 atomics; ksplit 1: plain stores
     int ksplit;
     int kchunk;
-    int out_nt;           // output stores non-temporal (lanes walk a unit-stride dim)
+    int out_nt;           // lanes of a store walk a unit-stride output dim: the
+                          // im2col and 1x1 kernels are launched with streaming stores
 };
 
 // Requantising INT8 epilogue of one exact sum: the sum as a float, one fused
@@ -350,24 +351,18 @@ __device__ __forceinline__ void store_tile(const IgemmArgs &a, v16i (&acc)[FM][F
 
 // store_tile with the epilogue the arguments ask for (SPLIT: the kernel may
 // run with a split inner dimension, whose partial sums are added atomically;
-// integer adds make the result independent of their order).
-template <int FM, int FN, bool PIX_J, bool SPLIT = false>
+// integer adds make the result independent of their order), its stores with
+// cache policy POL.
+template <int FM, int FN, bool PIX_J, bool SPLIT = false, int POL = kOutStoreStream>
 __device__ __forceinline__ void store_tile_any(const IgemmArgs &a, v16i (&acc)[FM][FN], int m0, int n0,
                                                int wm, int wn, int lane, const int *out_row)
 {
-    if (a.q8) {
-        if (a.out_nt)
-            store_tile<FM, FN, PIX_J, true, false, kOutStoreStream>(a, acc, m0, n0, wm, wn, lane, out_row);
-        else
-            store_tile<FM, FN, PIX_J, true, false, kOutStoreDefault>(a, acc, m0, n0, wm, wn, lane, out_row);
-    } else if (SPLIT && a.ksplit > 1) {
+    if (a.q8)
+        store_tile<FM, FN, PIX_J, true, false, POL>(a, acc, m0, n0, wm, wn, lane, out_row);
+    else if (SPLIT && a.ksplit > 1)
         store_tile<FM, FN, PIX_J, false, SPLIT>(a, acc, m0, n0, wm, wn, lane, out_row);
-    } else {
-        if (a.out_nt)
-            store_tile<FM, FN, PIX_J, false, false, kOutStoreStream>(a, acc, m0, n0, wm, wn, lane, out_row);
-        else
-            store_tile<FM, FN, PIX_J, false, false, kOutStoreDefault>(a, acc, m0, n0, wm, wn, lane, out_row);
-    }
+    else
+        store_tile<FM, FN, PIX_J, false, false, POL>(a, acc, m0, n0, wm, wn, lane, out_row);
 }
 
 }  // namespace convi8

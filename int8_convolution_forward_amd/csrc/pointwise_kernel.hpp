@@ -22,7 +22,9 @@
 
 namespace convi8 {
 
-template <int FN, int KS, int TPW>
+// POL: cache policy of the output stores (kOutStoreStream when the launch's
+// output has unit channel stride, else kOutStoreDefault)
+template <int FN, int KS, int TPW, int POL>
 __global__ __launch_bounds__(256) void conv_pointwise_kernel(IgemmArgs a)
 {
     const int lane = threadIdx.x & 63;
@@ -74,21 +76,9 @@ __global__ __launch_bounds__(256) void conv_pointwise_kernel(IgemmArgs a)
     // ---- multiply and store, tile by tile ----------------------------------
     const __amdgpu_buffer_rsrc_t out_rsrc =
         __builtin_amdgcn_make_buffer_rsrc((void *)a.out, (short)0, a.out_range, kRsrcWord3);
-    // stores with the cache policy the output layout calls for (non-temporal
-    // when the lanes walk unit-stride channels)
-    const bool nt = a.out_nt != 0;
-    auto st32 = [&](int v, int off) {
-        if (nt)
-            __builtin_amdgcn_raw_buffer_store_b32(v, out_rsrc, off, 0, kOutStoreStream);
-        else
-            __builtin_amdgcn_raw_buffer_store_b32(v, out_rsrc, off, 0, kOutStoreDefault);
-    };
-    auto st8 = [&](unsigned char v, int off) {
-        if (nt)
-            __builtin_amdgcn_raw_buffer_store_b8(v, out_rsrc, off, 0, kOutStoreStream);
-        else
-            __builtin_amdgcn_raw_buffer_store_b8(v, out_rsrc, off, 0, kOutStoreDefault);
-    };
+    // stores with the cache policy the launch picked for this output layout
+    auto st32 = [&](int v, int off) { __builtin_amdgcn_raw_buffer_store_b32(v, out_rsrc, off, 0, POL); };
+    auto st8 = [&](unsigned char v, int off) { __builtin_amdgcn_raw_buffer_store_b8(v, out_rsrc, off, 0, POL); };
     const int mrow0 = 4 * (lane >> 5);
     const bool q8 = a.q8 != 0, relu = a.q_relu != 0;
     float qs[FN], qb[FN];                         // requantising epilogue, per column block
