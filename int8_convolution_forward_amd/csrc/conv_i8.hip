@@ -382,6 +382,11 @@ struct Plan {
     bool pix_linear = false;           // output pixel m at m * pix_stride
     int64_t pix_stride = 0;
     int64_t Hp = 0, Wf = 0, Pr = 0;    // footprint kernel geometry
+    // split of a long inner dimension over gridDim.y (weight gradient)
+    int64_t ksplit = 1, kchunk = 0;    // splits, stages per split
+    bool part = false;                 // partial outputs in the workspace + reduction
+    size_t ws_part_off = 0;
+    int64_t part_span = 0;             // elements of one partial copy (one launch's output span)
 };
 
 size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
@@ -655,6 +660,38 @@ conv_i8_status_t make_plan(const Problem &pb, const void *x_ptr, const void *w_p
         pl->Wf = Wf;
         pl->Pr = footprint_pitch(Wf, pb.Q, pb.str[0], pb.str[1]);
     }
+
+    // A few tiles over a long inner dimension (the weight gradient): split it
+    // over gridDim.y so that about one workgroup runs per CU, at least 16
+    // stages each.  With a dense output each split writes its partial sums
+    // into its own copy of the output in the workspace and a reduction kernel
+    // adds the copies; otherwise the splits add into the zeroed output with
+    // int32 atomics.  (Device-scope atomics are slow here: with more than half
+    // of the CUs busy they cost more than the split gains, 75 -> 167 us on the
+    // large-channel weight gradient's 144 tiles.)
+    pl->ksplit = 1;
+    pl->kchunk = 0;
+    pl->part = false;
+    if (pb.split_ok && c.kind == kIm2col && pb.C > 0 && pl->nstages >= 32) {
+        const int64_t tiles = ((M + c.tm - 1) / c.tm) * ((pb.K + c.tn - 1) / c.tn);
+        const int64_t want = tiles > 0 ? std::min<int64_t>((kCUs + tiles - 1) / tiles, pl->nstages / 16) : 1;
+        if (tiles < kCUs / 2 && want > 1) {
+            pl->kchunk = (pl->nstages + want - 1) / want;
+            pl->ksplit = (pl->nstages + pl->kchunk - 1) / pl->kchunk;
+        }
+    }
+    if (pl->ksplit > 1 && pl->batch_chunk >= pb.N) {
+        // one launch covers the whole output, which must be dense: every
+        // element of its span is one of its elements, written by every split
+        const int64_t span = (pb.N - 1) * pb.y.s[0] + pl->y_img_span;
+        int64_t bytes;
+        if (span == pb.N * pb.K * pb.P * pb.Q && mul_ok(span * 4, pl->ksplit, &bytes)) {
+            pl->part = true;
+            pl->part_span = span;
+            pl->ws_part_off = align_up(pl->ws_bytes, 256);
+            pl->ws_bytes = pl->ws_part_off + (size_t)bytes;
+        }
+    }
     return CONV_I8_OK;
 }
 
@@ -825,32 +862,49 @@ conv_i8_status_t run(const Problem &pb, const Plan &pl, const void *x_ptr, const
             continue;
         a.tiles = (int)tiles;
         unsigned ksplit = 1;
-        if (pb.split_ok && !rq && c.kind == kIm2col && tiles < kCUs / 2 && a.nstages >= 32) {
-            // a few tiles over a long inner dimension (the weight gradient):
-            // split it so that about one workgroup runs per CU, at least 16
-            // stages each; partial sums meet in the zeroed output atomically.
-            // (With more than half of the CUs busy, the atomics and their
-            // contention on one tile's lines cost more than the split gains:
-            // 75 -> 167 us on the large-channel weight gradient, 144 tiles.)
-            const int64_t want = std::min<int64_t>((kCUs + tiles - 1) / tiles, a.nstages / 16);
-            if (want > 1) {
-                const int64_t chunk = (a.nstages + want - 1) / want;
-                ksplit = (unsigned)((a.nstages + chunk - 1) / chunk);
+        int32_t *const out_chunk = a.out;
+        const int64_t chunk_span = (nb - 1) * pb.y.s[0] + pl.y_img_span;
+        if (pl.ksplit > 1 && !rq && c.kind == kIm2col) {
+            ksplit = (unsigned)pl.ksplit;
+            a.kchunk = (int)pl.kchunk;
+            a.ksplit = (int)ksplit;
+            if (pl.part) {
+                // partial copies in the workspace, one per split
+                a.part = 1;
+                a.part_stride = pl.part_span;
+                a.out = (int32_t *)(wsb + pl.ws_part_off);
+            } else {
                 // zeros first: the same kernel with no stages stores zeros
                 IgemmArgs z = a;
                 z.nstages = 0;
+                z.ksplit = 1;
                 c.launch(!pl.blocked, pl.pix_j, dim3((unsigned)tiles), stream, z);
                 if (hipGetLastError() != hipSuccess)
                     return CONV_I8_ERR_HIP;
-                a.kchunk = (int)chunk;
-                a.ksplit = (int)ksplit;
             }
         }
         c.launch(!pl.blocked, pl.pix_j, dim3((unsigned)tiles, ksplit), stream, a);
-        a.ksplit = 1;
-        a.kchunk = 0x7fffffff;
         if (hipGetLastError() != hipSuccess)
             return CONV_I8_ERR_HIP;
+        if (a.part) {
+            const int32_t *part = a.out;
+            const bool v4 = chunk_span % 4 == 0 && pl.part_span % 4 == 0 && ((uintptr_t)out_chunk & 15u) == 0 &&
+                            ((uintptr_t)part & 15u) == 0;
+            const int64_t items = v4 ? chunk_span / 4 : chunk_span;
+            const dim3 grid((unsigned)std::min<int64_t>(std::max<int64_t>((items + 255) / 256, 1), 4 * kCUs));
+            if (v4)
+                hipLaunchKernelGGL(split_reduce_kernel<true>, grid, dim3(256), 0, stream, part,
+                                   (long long)pl.part_span, (int)ksplit, out_chunk, (long long)chunk_span);
+            else
+                hipLaunchKernelGGL(split_reduce_kernel<false>, grid, dim3(256), 0, stream, part,
+                                   (long long)pl.part_span, (int)ksplit, out_chunk, (long long)chunk_span);
+            if (hipGetLastError() != hipSuccess)
+                return CONV_I8_ERR_HIP;
+            a.part = 0;
+            a.out = out_chunk;
+        }
+        a.ksplit = 1;
+        a.kchunk = 0x7fffffff;
     }
     return CONV_I8_OK;
 }
@@ -973,14 +1027,15 @@ conv_i8_status_t entry_workspace_size(const conv_i8_desc_t *image, const void *i
                                       const conv_i8_desc_t *out, const int64_t *pre,
                                       const int64_t *post, const int64_t *stride,
                                       const int64_t *dil, int32_t out_dtype, int32_t mode,
-                                      size_t *workspace_bytes, bool flip_out = false)
+                                      size_t *workspace_bytes, bool flip_out = false,
+                                      bool split_ok = false)
 {
     if (!workspace_bytes)
         return CONV_I8_ERR_NULL;
     Problem pb;
     Plan pl;
     conv_i8_status_t st = prepare(image, image_ptr, filter, filter_ptr, out, pre, post, stride,
-                                  dil, &pb, &pl, out_dtype, mode, flip_out);
+                                  dil, &pb, &pl, out_dtype, mode, flip_out, split_ok);
     if (st != CONV_I8_OK)
         return st;
     *workspace_bytes = pb.y.elems() == 0 || pb.C == 0 ? 0 : pl.ws_bytes;
@@ -1455,17 +1510,20 @@ conv_i8_status_t wgrad_entry(const conv_i8_desc_t *image, const void *image_ptr,
                           [&](const conv_i8_desc_t *i, const void *x, const conv_i8_desc_t *f,
                               const void *w, const conv_i8_desc_t *o, void *, const int64_t *a,
                               const int64_t *b, const int64_t *c, const int64_t *d, bool fl) {
+                              // the same plan as the call below (split_ok: its
+                              // partial outputs live in the workspace)
                               return entry_workspace_size(i, x, f, w, o, a, b, c, d,
                                                           CONV_I8_DT_INT32,
                                                           CONV_I8_MODE_CROSS_CORRELATION, ws_size,
-                                                          fl);
+                                                          fl, true);
                           });
     return wgrad_call(wp, image_ptr, loss_ptr, dw_ptr, mode,
                       [&](const conv_i8_desc_t *i, const void *x, const conv_i8_desc_t *f,
                           const void *w, const conv_i8_desc_t *o, void *y, const int64_t *a,
                           const int64_t *b, const int64_t *c, const int64_t *d, bool fl) {
                           // split_ok: the long inner dimension may be split over
-                          // workgroups that add into the output (zeroed first)
+                          // workgroups whose partial outputs a reduction adds (or,
+                          // for an output with gaps, that add into it atomically)
                           return entry_run(i, x, f, w, o, y, a, b, c, d, CONV_I8_DT_INT32,
                                            CONV_I8_MODE_CROSS_CORRELATION, nullptr, alloc,
                                            workspace, workspace_bytes, stream, fl, true);

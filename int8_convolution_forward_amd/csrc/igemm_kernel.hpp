@@ -266,4 +266,34 @@ __global__ __launch_bounds__(64 * WGM * WGN) void conv_igemm_kernel(IgemmArgs a)
     store_tile_any<FM, FN, PIX_J, true, POL>(a, acc, m0, n0, wm, wn, lane, out_row);
 }
 
+// Sum of the partial outputs of a split inner dimension: out[i] = the sum
+// over z < nsplit of part[z*stride + i], for every i < n.  The output is
+// dense, so i walks each of its elements once; int32 addition is exact and
+// independent of order.  V4: n, stride and both pointers allow 16-byte
+// vectors.
+template <bool V4>
+__global__ __launch_bounds__(256) void split_reduce_kernel(const int32_t *part, long long stride, int nsplit,
+                                                           int32_t *out, long long n)
+{
+    typedef int i32x4 __attribute__((ext_vector_type(4)));
+    const long long step = (long long)gridDim.x * 256;
+    if constexpr (V4) {
+        const long long n4 = n / 4, s4 = stride / 4;
+        const i32x4 *p4 = (const i32x4 *)part;
+        for (long long i = (long long)blockIdx.x * 256 + threadIdx.x; i < n4; i += step) {
+            i32x4 s = p4[i];
+            for (int z = 1; z < nsplit; ++z)
+                s += p4[z * s4 + i];
+            ((i32x4 *)out)[i] = s;
+        }
+    } else {
+        for (long long i = (long long)blockIdx.x * 256 + threadIdx.x; i < n; i += step) {
+            int s = part[i];
+            for (int z = 1; z < nsplit; ++z)
+                s += part[z * stride + i];
+            out[i] = s;
+        }
+    }
+}
+
 }  // namespace convi8

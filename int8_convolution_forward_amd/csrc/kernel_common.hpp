@@ -88,6 +88,11 @@ struct IgemmArgs {
     int kchunk;
     int out_nt;           // lanes of a store walk a unit-stride output dim: the
                           // im2col and 1x1 kernels are launched with streaming stores
+    // split with partial outputs (part != 0): split z stores plain partial
+    // sums into its own copy of the output at out + z*part_stride elements
+    // (a reduction kernel adds the copies); part == 0: atomics into out
+    int part;
+    long long part_stride;
 };
 
 // Requantising INT8 epilogue of one exact sum: the sum as a float, one fused
@@ -224,10 +229,11 @@ __device__ __forceinline__ void fill_out_rows(const IgemmArgs &a, int m0, int *o
 // guards a store.
 template <int FM, int FN, bool PIX_J, bool Q8 = false, bool ATOM = false, int POL = kOutStoreStream>
 __device__ __forceinline__ void store_tile(const IgemmArgs &a, v16i (&acc)[FM][FN], int m0, int n0,
-                                           int wm, int wn, int lane, const int *out_row)
+                                           int wm, int wn, int lane, const int *out_row,
+                                           long long zoff = 0)
 {
     const __amdgpu_buffer_rsrc_t out_rsrc =
-        __builtin_amdgcn_make_buffer_rsrc((void *)a.out, (short)0, a.out_range, kRsrcWord3);
+        __builtin_amdgcn_make_buffer_rsrc((void *)(a.out + zoff), (short)0, a.out_range, kRsrcWord3);
     constexpr int ES = Q8 ? 1 : 4;           // bytes per output element
     const bool relu = a.q_relu != 0;
     auto put = [&](int v, int off, float qs, float qb) {
@@ -359,6 +365,9 @@ __device__ __forceinline__ void store_tile_any(const IgemmArgs &a, v16i (&acc)[F
 {
     if (a.q8)
         store_tile<FM, FN, PIX_J, true, false, POL>(a, acc, m0, n0, wm, wn, lane, out_row);
+    else if (SPLIT && a.ksplit > 1 && a.part)
+        store_tile<FM, FN, PIX_J, false, false, kOutStoreDefault>(a, acc, m0, n0, wm, wn, lane, out_row,
+                                                                  (long long)blockIdx.y * a.part_stride);
     else if (SPLIT && a.ksplit > 1)
         store_tile<FM, FN, PIX_J, false, SPLIT>(a, acc, m0, n0, wm, wn, lane, out_row);
     else
