@@ -673,23 +673,25 @@ conv_i8_status_t make_plan(const Problem &pb, const void *x_ptr, const void *w_p
     pl->kchunk = 0;
     pl->part = false;
     if (pb.split_ok && c.kind == kIm2col && pb.C > 0 && pl->nstages >= 32) {
+        // partial copies need one launch over a dense output: every element
+        // of its span is one of its elements, written by every split
+        const int64_t span = (pb.N - 1) * pb.y.s[0] + pl->y_img_span;
+        const bool dense = pl->batch_chunk >= pb.N && span == pb.N * pb.K * pb.P * pb.Q;
         const int64_t tiles = ((M + c.tm - 1) / c.tm) * ((pb.K + c.tn - 1) / c.tn);
         const int64_t want = tiles > 0 ? std::min<int64_t>((kCUs + tiles - 1) / tiles, pl->nstages / 16) : 1;
-        if (tiles < kCUs / 2 && want > 1) {
+        // with partial copies a split pays while some CU is idle (large-channel
+        // weight gradient, 144 tiles: 81 -> 78 us); with atomics only below
+        // half of the CUs
+        if (tiles < (dense ? kCUs : kCUs / 2) && want > 1) {
             pl->kchunk = (pl->nstages + want - 1) / want;
             pl->ksplit = (pl->nstages + pl->kchunk - 1) / pl->kchunk;
-        }
-    }
-    if (pl->ksplit > 1 && pl->batch_chunk >= pb.N) {
-        // one launch covers the whole output, which must be dense: every
-        // element of its span is one of its elements, written by every split
-        const int64_t span = (pb.N - 1) * pb.y.s[0] + pl->y_img_span;
-        int64_t bytes;
-        if (span == pb.N * pb.K * pb.P * pb.Q && mul_ok(span * 4, pl->ksplit, &bytes)) {
-            pl->part = true;
-            pl->part_span = span;
-            pl->ws_part_off = align_up(pl->ws_bytes, 256);
-            pl->ws_bytes = pl->ws_part_off + (size_t)bytes;
+            int64_t bytes;
+            if (dense && mul_ok(span * 4, pl->ksplit, &bytes)) {
+                pl->part = true;
+                pl->part_span = span;
+                pl->ws_part_off = align_up(pl->ws_bytes, 256);
+                pl->ws_bytes = pl->ws_part_off + (size_t)bytes;
+            }
         }
     }
     return CONV_I8_OK;
