@@ -375,7 +375,11 @@ conv_i8_status_t conv_dgrad_i8(const conv_i8_desc_t *loss, const void *loss_ptr,
  * loss transposed to [K, N, P, Q] at stride = dilation and dilation = stride,
  * written to dW transposed to [C, K, R, S] (reversed along R and S for true
  * convolution).  Errors and stream behaviour as conv_fprop_i8_ws; never
- * allocates, never synchronises.
+ * allocates, never synchronises.  The workspace holds the packed transposed
+ * operands and, when the long N*P*Q reduction is split over workgroups and dw
+ * is dense, one int32 partial copy of dw per split (added into dw by a
+ * reduction kernel on the same stream); its contents on return are
+ * unspecified.
  */
 conv_i8_status_t conv_wgrad_i8_workspace_size(const conv_i8_desc_t *image, const void *image_ptr,
                                               const conv_i8_desc_t *loss, const void *loss_ptr,
