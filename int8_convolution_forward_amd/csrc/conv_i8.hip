@@ -705,11 +705,11 @@ std::string describe(const Problem &pb, const Plan &pl)
     char buf[512];
     snprintf(buf, sizeof buf,
              "repack_image=%d repack_filter=%d Cp=%lld tile=%s kernel=%s order=%s stages=%lld "
-             "lanes=%s tiles=%lld batch_chunk=%lld workspace=%zu",
+             "lanes=%s tiles=%lld batch_chunk=%lld workspace=%zu ksplit=%lld split_sum=%s",
              (int)pl.repack_x, (int)pl.repack_w, (long long)pl.Cp, c.name,
              c.kind == kFootprint ? "footprint" : c.kind == kPointwise ? "pointwise" : "im2col", pl.blocked ? "blocked" : "flat", (long long)pl.nstages,
              pl.pix_j ? "pixels" : "channels", (long long)tiles, (long long)pl.batch_chunk,
-             pl.ws_bytes);
+             pl.ws_bytes, (long long)pl.ksplit, pl.ksplit < 2 ? "none" : pl.part ? "partial" : "atomic");
     return buf;
 }
 

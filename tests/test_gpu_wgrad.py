@@ -96,3 +96,25 @@ def test_random_wgrad_problems(ci8):
                         dyspec, dwspec, pre, post, st, dl, mode=done % 2, label=f"random {done}",
                         entry="plain" if done % 5 == 0 else "ws")
         done += 1
+
+
+@pytest.mark.parametrize("layout,split_sum", [("kcrs_dense", "partial"), ("krsc_gaps", "atomic")])
+def test_wgrad_split_paths(ci8, monkeypatch, capfd, layout, split_sum):
+    """A weight gradient whose long N*P*Q reduction is split over workgroups
+    (the bottleneck workload: 36 tiles, 7 splits): a dense dW takes the
+    partial copies plus reduction, a dW with gaps between its pixels (a view
+    into a buffer twice as wide) takes the zero-fill plus atomics path."""
+    c = wl.case("bottleneck_3x3_n32_c128_28")
+    d = wl.make_inputs(c, c.seed_base + 6)
+    dyspec = wl.TensorSpec(c.out.dims, c.out.strides)
+    K, C, R, S = c.filter.dims
+    if layout == "kcrs_dense":
+        dwspec = wl.TensorSpec((K, C, R, S), wl.contiguous_strides((K, C, R, S)))
+    else:
+        dwspec = wl.TensorSpec((K, C, R, S), (R * S * 2 * C, 1, S * 2 * C, 2 * C))
+    monkeypatch.setenv("CONV_I8_LOG", "1")
+    run_wgrad_check(ci8, d["x_storage"], c.image, _rand_storage(dyspec, 21), dyspec, dwspec,
+                    c.pre, c.post, c.stride, c.dilation, label=f"split {layout}")
+    logged = capfd.readouterr().err
+    plans = [ci8.plan_fields(l) for l in logged.splitlines() if "ksplit=" in l]
+    assert plans and all(p["split_sum"] == split_sum and int(p["ksplit"]) > 1 for p in plans), logged
