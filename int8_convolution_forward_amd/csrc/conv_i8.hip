@@ -213,32 +213,36 @@ conv_i8_status_t analyze(const conv_i8_desc_t *image, const conv_i8_desc_t *filt
 // ---------------------------------------------------------------------------
 using Launcher = void (*)(bool flat, bool pix_j, dim3 grid, hipStream_t stream, const IgemmArgs &a);
 
-template <int TM, int TN, int BK, int NS, int WGM, int WGN, int POL>
-void launch_cfg_pol(bool flat, bool pix_j, dim3 grid, hipStream_t stream, const IgemmArgs &a)
+template <int TM, int TN, int BK, int NS, int WGM, int WGN, int EPI>
+void launch_cfg_epi(bool flat, bool pix_j, dim3 grid, hipStream_t stream, const IgemmArgs &a)
 {
     const dim3 block(64 * WGM * WGN);
     if (flat) {
         if (pix_j)
-            hipLaunchKernelGGL((conv_igemm_kernel<TM, TN, BK, NS, WGM, WGN, true, true, POL>), grid, block, 0, stream, a);
+            hipLaunchKernelGGL((conv_igemm_kernel<TM, TN, BK, NS, WGM, WGN, true, true, EPI>), grid, block, 0, stream, a);
         else
-            hipLaunchKernelGGL((conv_igemm_kernel<TM, TN, BK, NS, WGM, WGN, true, false, POL>), grid, block, 0, stream, a);
+            hipLaunchKernelGGL((conv_igemm_kernel<TM, TN, BK, NS, WGM, WGN, true, false, EPI>), grid, block, 0, stream, a);
     } else {
         if (pix_j)
-            hipLaunchKernelGGL((conv_igemm_kernel<TM, TN, BK, NS, WGM, WGN, false, true, POL>), grid, block, 0, stream, a);
+            hipLaunchKernelGGL((conv_igemm_kernel<TM, TN, BK, NS, WGM, WGN, false, true, EPI>), grid, block, 0, stream, a);
         else
-            hipLaunchKernelGGL((conv_igemm_kernel<TM, TN, BK, NS, WGM, WGN, false, false, POL>), grid, block, 0, stream, a);
+            hipLaunchKernelGGL((conv_igemm_kernel<TM, TN, BK, NS, WGM, WGN, false, false, EPI>), grid, block, 0, stream, a);
     }
 }
 
-// streaming output stores when each store's lanes cover consecutive
-// elements, the default policy (L2 merges the lines) when they scatter
+// the epilogue a launch needs: the stores of one split of a split inner
+// dimension; else streaming output stores when each store's lanes cover
+// consecutive elements, the default policy (L2 merges the lines) when they
+// scatter
 template <int TM, int TN, int BK, int NS, int WGM = 2, int WGN = 2>
 void launch_cfg(bool flat, bool pix_j, dim3 grid, hipStream_t stream, const IgemmArgs &a)
 {
-    if (a.out_nt)
-        launch_cfg_pol<TM, TN, BK, NS, WGM, WGN, kOutStoreStream>(flat, pix_j, grid, stream, a);
+    if (a.ksplit > 1)
+        launch_cfg_epi<TM, TN, BK, NS, WGM, WGN, kEpiSplit>(flat, pix_j, grid, stream, a);
+    else if (a.out_nt)
+        launch_cfg_epi<TM, TN, BK, NS, WGM, WGN, kEpiStream>(flat, pix_j, grid, stream, a);
     else
-        launch_cfg_pol<TM, TN, BK, NS, WGM, WGN, kOutStoreDefault>(flat, pix_j, grid, stream, a);
+        launch_cfg_epi<TM, TN, BK, NS, WGM, WGN, kEpiDefault>(flat, pix_j, grid, stream, a);
 }
 
 template <int TM, int TN, int NS, int FPIX, int WGM = 2, int WGN = 2, int KSPL = 1>
@@ -719,9 +723,10 @@ bool log_enabled()
     return e && *e && strcmp(e, "0") != 0;
 }
 
-conv_i8_status_t launch_repacks(const RepackJob *jobs, int njobs, hipStream_t stream)
+template <int NJ>
+conv_i8_status_t launch_repacks_n(const RepackJob *jobs, int njobs, hipStream_t stream)
 {
-    RepackArgs r{};
+    RepackArgs<NJ> r{};
     int64_t total = 0;
     for (int i = 0; i < njobs; ++i) {
         if (jobs[i].tiles == 0)
@@ -729,6 +734,8 @@ conv_i8_status_t launch_repacks(const RepackJob *jobs, int njobs, hipStream_t st
         r.job[r.njobs++] = jobs[i];
         total += jobs[i].tiles;
     }
+    if (total > kI32Max)
+        return CONV_I8_ERR_UNSUPPORTED;
     if (total == 0)
         return CONV_I8_OK;
     // LDS line size for the largest stride a job walks its lines with
@@ -741,12 +748,20 @@ conv_i8_status_t launch_repacks(const RepackJob *jobs, int njobs, hipStream_t st
     }
     const dim3 grid((unsigned)total);
     if (step <= 2)
-        hipLaunchKernelGGL(repack_to_channels_last_kernel<2>, grid, dim3(256), 0, stream, r);
+        hipLaunchKernelGGL((repack_to_channels_last_kernel<2, NJ>), grid, dim3(256), 0, stream, r);
     else if (step <= 4)
-        hipLaunchKernelGGL(repack_to_channels_last_kernel<4>, grid, dim3(256), 0, stream, r);
+        hipLaunchKernelGGL((repack_to_channels_last_kernel<4, NJ>), grid, dim3(256), 0, stream, r);
     else
-        hipLaunchKernelGGL(repack_to_channels_last_kernel<8>, grid, dim3(256), 0, stream, r);
+        hipLaunchKernelGGL((repack_to_channels_last_kernel<8, NJ>), grid, dim3(256), 0, stream, r);
     return hipGetLastError() == hipSuccess ? CONV_I8_OK : CONV_I8_ERR_HIP;
+}
+
+conv_i8_status_t launch_repacks(const RepackJob *jobs, int njobs, hipStream_t stream)
+{
+    if (njobs > kRepackMaxJobs)
+        return CONV_I8_ERR_UNSUPPORTED;
+    return njobs <= 2 ? launch_repacks_n<2>(jobs, njobs, stream)
+                      : launch_repacks_n<kRepackMaxJobs>(jobs, njobs, stream);
 }
 
 conv_i8_status_t run(const Problem &pb, const Plan &pl, const void *x_ptr, const void *w_ptr,
@@ -1312,22 +1327,122 @@ conv_i8_status_t dgrad_phases(const DgradProblem &dp, const void *dy_ptr, const 
     return CONV_I8_OK;
 }
 
-conv_i8_status_t dgrad_workspace(const DgradProblem &dp, const void *dy_ptr, const void *w_ptr,
-                                 int32_t mode, size_t *bytes)
+// The filter views of a strided layer's phases, packed once for all phases.
+// With several phases each phase's convolution would repack its own
+// (transposed, subsampled) filter view in a launch of its own; when every
+// view needs a repack, the packed copies are directly readable (K a multiple
+// of 16) and the phases read the loss in place (else each phase repacks its
+// part of the loss, and that launch carries its filter too), one repack
+// launch writes all the views into regions at the start of the workspace and
+// each phase reads its region in place.
+struct DgradPack {
+    bool on = false;
+    int n = 0;                             // phases with taps, in dgrad_phases order
+    T4 view[kRepackMaxJobs];
+    const void *src[kRepackMaxJobs];
+    size_t off[kRepackMaxJobs];
+    size_t bytes = 0;                      // all regions, 256-byte aligned
+    int64_t Kp = 0;
+};
+
+conv_i8_status_t dgrad_pack_plan(const DgradProblem &dp, const void *dy_ptr, const void *w_ptr,
+                                 int32_t mode, DgradPack *pk)
 {
-    size_t most = 0;
+    *pk = DgradPack{};
+    if (dp.str[0] * dp.str[1] < 2)
+        return CONV_I8_OK;                 // one phase: nothing to share
+    if (dp.K % 16 != 0 || (dp.K > 1 && dp.dy.s[1] != 1))
+        return CONV_I8_OK;                 // packed views not readable in place, or the
+                                           // phases repack their part of the loss anyway
+    bool ok = true;
+    int n = 0;
     conv_i8_status_t st = dgrad_phases(
+        dp, dy_ptr, w_ptr, nullptr, mode,
+        [&](const conv_i8_desc_t *img, const void *x, const conv_i8_desc_t *flt, const void *w,
+            const conv_i8_desc_t *, void *, const int64_t *, const int64_t *, const int64_t *,
+            const int64_t *, int32_t) {
+            if (flt->dims[1] == 0)
+                return CONV_I8_OK;         // a phase no tap reaches: zero channels, no filter
+            T4 ti;
+            conv_i8_status_t s1 = read_desc(img, CONV_I8_DT_INT8, &ti);
+            if (s1 != CONV_I8_OK)
+                return s1;
+            if (!direct_ok(ti, x))
+                ok = false;                // the phase repacks its image anyway: one launch
+                                           // carries both of its repacks
+            if (n >= kRepackMaxJobs) {
+                ok = false;
+                ++n;
+                return CONV_I8_OK;
+            }
+            T4 t;
+            conv_i8_status_t s2 = read_desc(flt, CONV_I8_DT_INT8, &t);
+            if (s2 != CONV_I8_OK)
+                return s2;
+            if (direct_ok(t, w))
+                ok = false;                // already readable in place
+            pk->view[n] = t;
+            pk->src[n] = w;
+            ++n;
+            return CONV_I8_OK;
+        });
+    if (st != CONV_I8_OK)
+        return st;
+    if (!ok || n < 2 || n > kRepackMaxJobs)
+        return CONV_I8_OK;
+    pk->Kp = dp.K;
+    size_t off = 0;
+    for (int i = 0; i < n; ++i) {
+        const T4 &t = pk->view[i];
+        int64_t b;
+        if (!mul_ok(t.d[0] * t.d[2], t.d[3] * pk->Kp, &b))
+            return CONV_I8_OK;
+        pk->off[i] = off;
+        off = align_up(off + (size_t)b, 256);
+    }
+    pk->n = n;
+    pk->bytes = off;
+    pk->on = true;
+    return CONV_I8_OK;
+}
+
+// Descriptor of phase i's packed filter: [C, K, taps_h, taps_w] with K innermost.
+conv_i8_desc_t dgrad_packed_desc(const DgradPack &pk, int i)
+{
+    const T4 &t = pk.view[i];
+    const int64_t d[4] = {t.d[0], t.d[1], t.d[2], t.d[3]};
+    const int64_t st[4] = {t.d[2] * t.d[3] * pk.Kp, 1, t.d[3] * pk.Kp, pk.Kp};
+    return make_desc(CONV_I8_DT_INT8, d, st);
+}
+
+conv_i8_status_t dgrad_workspace(const DgradProblem &dp, const void *dy_ptr, const void *w_ptr,
+                                 int32_t mode, size_t *bytes, DgradPack *pack = nullptr)
+{
+    DgradPack own;
+    DgradPack &pk = pack ? *pack : own;
+    conv_i8_status_t st = dgrad_pack_plan(dp, dy_ptr, w_ptr, mode, &pk);
+    if (st != CONV_I8_OK)
+        return st;
+    size_t most = 0;
+    int i = 0;
+    st = dgrad_phases(
         dp, dy_ptr, w_ptr, nullptr, mode,
         [&](const conv_i8_desc_t *img, const void *x, const conv_i8_desc_t *flt, const void *w,
             const conv_i8_desc_t *out, void *, const int64_t *pre, const int64_t *post,
             const int64_t *stride, const int64_t *dil, int32_t m) {
             size_t n = 0;
+            conv_i8_desc_t packed;
+            if (pk.on && flt->dims[1] > 0) {
+                packed = dgrad_packed_desc(pk, i++);
+                flt = &packed;
+                w = nullptr;               // the region is 256-byte aligned
+            }
             conv_i8_status_t s = entry_workspace_size(img, x, flt, w, out, pre, post, stride, dil,
                                                       CONV_I8_DT_INT32, m, &n);
             most = std::max(most, n);
             return s;
         });
-    *bytes = most;
+    *bytes = pk.bytes + most;
     return st;
 }
 
@@ -1347,7 +1462,8 @@ conv_i8_status_t dgrad_entry(const conv_i8_desc_t *loss, const void *loss_ptr,
     if (!dx_ptr || (dp.K > 0 && ((dp.dy.elems() > 0 && !loss_ptr) || (dp.w.elems() > 0 && !filter_ptr))))
         return CONV_I8_ERR_NULL;
     size_t need = 0;
-    if ((st = dgrad_workspace(dp, loss_ptr, filter_ptr, mode, &need)) != CONV_I8_OK)
+    DgradPack pk;
+    if ((st = dgrad_workspace(dp, loss_ptr, filter_ptr, mode, &need, &pk)) != CONV_I8_OK)
         return st;
     hipStream_t s = (hipStream_t)stream;
     void *ws = workspace;
@@ -1363,15 +1479,32 @@ conv_i8_status_t dgrad_entry(const conv_i8_desc_t *loss, const void *loss_ptr,
         if (need > 0 && ((uintptr_t)workspace & 255u) != 0)
             return CONV_I8_ERR_WORKSPACE;
     }
+    if (pk.on) {
+        // every phase's filter view packed in one launch
+        RepackJob jobs[kRepackMaxJobs];
+        for (int i = 0; i < pk.n; ++i)
+            jobs[i] = repack_job(pk.view[i], (const int8_t *)pk.src[i], (int8_t *)ws + pk.off[i], pk.Kp);
+        st = launch_repacks(jobs, pk.n, s);
+    }
     // the phases run one after another on the stream and share the workspace
-    st = dgrad_phases(dp, loss_ptr, filter_ptr, dx_ptr, mode,
-                      [&](const conv_i8_desc_t *img, const void *x, const conv_i8_desc_t *flt,
-                          const void *w, const conv_i8_desc_t *out, void *y, const int64_t *pre_,
-                          const int64_t *post_, const int64_t *stride_, const int64_t *dil_,
-                          int32_t m) {
-                          return entry_run(img, x, flt, w, out, y, pre_, post_, stride_, dil_,
-                                           CONV_I8_DT_INT32, m, nullptr, false, ws, need, stream);
-                      });
+    // past the packed filters
+    int i = 0;
+    if (st == CONV_I8_OK)
+        st = dgrad_phases(dp, loss_ptr, filter_ptr, dx_ptr, mode,
+                          [&](const conv_i8_desc_t *img, const void *x, const conv_i8_desc_t *flt,
+                              const void *w, const conv_i8_desc_t *out, void *y, const int64_t *pre_,
+                              const int64_t *post_, const int64_t *stride_, const int64_t *dil_,
+                              int32_t m) {
+                              conv_i8_desc_t packed;
+                              if (pk.on && flt->dims[1] > 0) {
+                                  w = (const int8_t *)ws + pk.off[i];
+                                  packed = dgrad_packed_desc(pk, i++);
+                                  flt = &packed;
+                              }
+                              return entry_run(img, x, flt, w, out, y, pre_, post_, stride_, dil_,
+                                               CONV_I8_DT_INT32, m, nullptr, false,
+                                               (int8_t *)ws + pk.bytes, need - pk.bytes, stream);
+                          });
     if (alloc && ws && hipFreeAsync(ws, s) != hipSuccess && st == CONV_I8_OK)
         st = CONV_I8_ERR_HIP;
     return st;

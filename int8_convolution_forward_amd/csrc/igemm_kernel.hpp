@@ -44,7 +44,7 @@
 
 namespace convi8 {
 
-template <int TM, int TN, int BK, int NS, int WGM, int WGN, bool FLAT, bool PIX_J, int POL>
+template <int TM, int TN, int BK, int NS, int WGM, int WGN, bool FLAT, bool PIX_J, int EPI>
 __global__ __launch_bounds__(64 * WGM * WGN) void conv_igemm_kernel(IgemmArgs a)
 {
     constexpr int NW = WGM * WGN;           // waves per workgroup (WGM x WGN grid)
@@ -263,7 +263,7 @@ __global__ __launch_bounds__(64 * WGM * WGN) void conv_igemm_kernel(IgemmArgs a)
     __syncthreads();
 
     // ---- epilogue ---------------------------------------------------------
-    store_tile_any<FM, FN, PIX_J, true, POL>(a, acc, m0, n0, wm, wn, lane, out_row);
+    store_tile_any<FM, FN, PIX_J, EPI>(a, acc, m0, n0, wm, wn, lane, out_row);
 }
 
 // Sum of the partial outputs of a split inner dimension: out[i] = the sum

@@ -355,23 +355,32 @@ __device__ __forceinline__ void store_tile(const IgemmArgs &a, v16i (&acc)[FM][F
     }
 }
 
-// store_tile with the epilogue the arguments ask for (SPLIT: the kernel may
-// run with a split inner dimension, whose partial sums are added atomically;
-// integer adds make the result independent of their order), its stores with
-// cache policy POL.
-template <int FM, int FN, bool PIX_J, bool SPLIT = false, int POL = kOutStoreStream>
+// Epilogue kinds a kernel is instantiated with: plain stores with the
+// streaming or the default cache policy, or the stores of one split of a
+// split inner dimension (partial copies, or int32 atomics into the zeroed
+// output; integer adds make the result independent of their order).
+constexpr int kEpiStream = 0;
+constexpr int kEpiDefault = 1;
+constexpr int kEpiSplit = 2;
+
+// store_tile with the epilogue the arguments ask for
+template <int FM, int FN, bool PIX_J, int EPI = kEpiStream>
 __device__ __forceinline__ void store_tile_any(const IgemmArgs &a, v16i (&acc)[FM][FN], int m0, int n0,
                                                int wm, int wn, int lane, const int *out_row)
 {
-    if (a.q8)
-        store_tile<FM, FN, PIX_J, true, false, POL>(a, acc, m0, n0, wm, wn, lane, out_row);
-    else if (SPLIT && a.ksplit > 1 && a.part)
-        store_tile<FM, FN, PIX_J, false, false, kOutStoreDefault>(a, acc, m0, n0, wm, wn, lane, out_row,
-                                                                  (long long)blockIdx.y * a.part_stride);
-    else if (SPLIT && a.ksplit > 1)
-        store_tile<FM, FN, PIX_J, false, SPLIT>(a, acc, m0, n0, wm, wn, lane, out_row);
-    else
-        store_tile<FM, FN, PIX_J, false, false, POL>(a, acc, m0, n0, wm, wn, lane, out_row);
+    constexpr int POL = EPI == kEpiStream ? kOutStoreStream : kOutStoreDefault;
+    if constexpr (EPI == kEpiSplit) {
+        if (a.part)
+            store_tile<FM, FN, PIX_J, false, false, kOutStoreDefault>(a, acc, m0, n0, wm, wn, lane, out_row,
+                                                                      (long long)blockIdx.y * a.part_stride);
+        else
+            store_tile<FM, FN, PIX_J, false, true>(a, acc, m0, n0, wm, wn, lane, out_row);
+    } else {
+        if (a.q8)
+            store_tile<FM, FN, PIX_J, true, false, POL>(a, acc, m0, n0, wm, wn, lane, out_row);
+        else
+            store_tile<FM, FN, PIX_J, false, false, POL>(a, acc, m0, n0, wm, wn, lane, out_row);
+    }
 }
 
 }  // namespace convi8

@@ -41,8 +41,14 @@ struct RepackJob {
     int8_t *dst;                     // packed [A][Y][X][Cp]
 };
 
+constexpr int kRepackMaxJobs = 8;
+
+// NJ job slots: 2 for a convolution's image and filter, kRepackMaxJobs for
+// the filter views of a strided layer's data-gradient phases (a smaller
+// argument block keeps the common launch as cheap as it can be)
+template <int NJ>
 struct RepackArgs {
-    RepackJob job[2];
+    RepackJob job[NJ];               // tiles of job i follow those of jobs 0 .. i-1
     int njobs;
 };
 
@@ -54,17 +60,19 @@ constexpr int repack_line()
     return (15 + 63 * STEP + 1 + 15) / 16 * 16;
 }
 
-template <int STEP>
-__global__ __launch_bounds__(256) void repack_to_channels_last_kernel(RepackArgs args)
+template <int STEP, int NJ>
+__global__ __launch_bounds__(256) void repack_to_channels_last_kernel(RepackArgs<NJ> args)
 {
     constexpr int kRepackLine = repack_line<STEP>();
     __shared__ __attribute__((aligned(16))) int8_t raw[64 * kRepackLine];
 
     unsigned bid = blockIdx.x;               // each job has fewer than 2^31 tiles
-    const bool second = args.njobs > 1 && bid >= (unsigned)args.job[0].tiles;
-    const RepackJob &j = second ? args.job[1] : args.job[0];
-    if (second)
-        bid -= (unsigned)args.job[0].tiles;
+    int ji = 0;                              // uniform: the job this workgroup serves
+    while (ji + 1 < args.njobs && bid >= (unsigned)args.job[ji].tiles) {
+        bid -= (unsigned)args.job[ji].tiles;
+        ++ji;
+    }
+    const RepackJob &j = args.job[ji];
 
     const int tid = threadIdx.x;
     const bool af = j.mode == kRepackAFast;
