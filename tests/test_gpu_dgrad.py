@@ -95,3 +95,26 @@ def test_random_dgrad_problems(ci8):
                         wspec, dxspec, pre, post, st, dl, mode=done % 2, label=f"random {done}",
                         entry="plain" if done % 5 == 0 else "ws")
         done += 1
+
+
+@pytest.mark.parametrize("dy_layout,packed", [("nhwc", True), ("nchw", False)])
+@pytest.mark.parametrize("mode", [0, 1])
+def test_dgrad_phase_filters_packed_once(ci8, monkeypatch, capfd, dy_layout, packed, mode):
+    """A stride-2 layer (the downsample workload: 4 phases).  With a
+    channels-last loss every phase's filter view is packed by one repack
+    launch before the phases, so each phase plan reads its filter in place;
+    with an NCHW loss each phase repacks its part of the loss and its filter
+    in one launch of its own.  Both bit-exact."""
+    c = wl.case("downsample_s2_n8_c64_56")
+    d = wl.make_inputs(c, c.seed_base + 8)
+    dims = c.out.dims
+    strides = wl.channels_last_strides(dims) if dy_layout == "nhwc" else wl.contiguous_strides(dims)
+    dyspec = wl.TensorSpec(dims, strides)
+    dxspec = wl.TensorSpec(c.image.dims, wl.channels_last_strides(c.image.dims))
+    monkeypatch.setenv("CONV_I8_LOG", "1")
+    run_dgrad_check(ci8, _rand_storage(dyspec, 31 + mode), dyspec, d["w_storage"], c.filter, dxspec,
+                    c.pre, c.post, c.stride, c.dilation, mode=mode, label=f"packed {dy_layout}")
+    logged = capfd.readouterr().err
+    plans = [ci8.plan_fields(l) for l in logged.splitlines() if "repack_filter=" in l]
+    assert len(plans) == 4, logged
+    assert all(p["repack_filter"] == ("0" if packed else "1") for p in plans), logged
