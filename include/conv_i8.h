@@ -95,8 +95,11 @@ typedef enum {
 
 /*
  * Output dims [N, K, P, Q] for an image and filter descriptor and the conv
- * parameters.  Validates the same fields conv_fprop_i8 does except the output.
- * Host-only: touches no device.
+ * parameters: the output-size formula above (cuDNN "Convolutions",
+ * "Convolution Fprop", whose Python API returns the response tensor of the
+ * padded, strided, dilated window; the blog's "Correctness Testing" checks a
+ * 32x32 image with a 3x3 filter gives 30x30).  Validates the same fields
+ * conv_fprop_i8 does except the output.  Host-only: touches no device.
  */
 conv_i8_status_t conv_fprop_i8_out_dims(const conv_i8_desc_t *image,
                                         const conv_i8_desc_t *filter,
@@ -107,6 +110,11 @@ conv_i8_status_t conv_fprop_i8_out_dims(const conv_i8_desc_t *image,
                                         int64_t out_dims[4]);
 
 /*
+ * The workspace query of the forum thread "INT8 convolution using cuDNN
+ * Python Frontend" (question post: the graph reports its workspace size, the
+ * caller allocates that many bytes and passes them to the execute call), here
+ * without a graph object.
+ *
  * Bytes of device workspace conv_fprop_i8_ws needs for this problem (0 when
  * both the image and the filter are already channel-innermost with C a
  * multiple of 16 and 16-byte aligned rows; otherwise room for their packed
@@ -124,6 +132,10 @@ conv_i8_status_t conv_fprop_i8_workspace_size(const conv_i8_desc_t *image, const
                                               size_t *workspace_bytes);
 
 /*
+ * The execute call of the same forum question post (operands, output and the
+ * caller's workspace passed together), for the operation of cuDNN
+ * "Convolutions", "Convolution Fprop" (parameters of its Python API list).
+ *
  * Y = conv_fprop(image, filter) into `out_ptr`, with caller-provided device
  * workspace of `workspace_bytes` bytes, 256-byte aligned (may be NULL when the
  * size needed is 0; CONV_I8_ERR_WORKSPACE if too small or misaligned).  Never
@@ -141,6 +153,10 @@ conv_i8_status_t conv_fprop_i8_ws(const conv_i8_desc_t *image, const void *image
                                   void *stream);
 
 /*
+ * cuDNN "Convolutions", "Convolution Fprop" as one call (the Python API's
+ * parameter list: image, weight, pre_padding, post_padding, stride,
+ * dilation), for callers that do not manage a workspace.
+ *
  * Same as conv_fprop_i8_ws, but any workspace needed is taken with
  * hipMallocAsync on `stream` and released with hipFreeAsync after the work.
  */
@@ -154,6 +170,10 @@ conv_i8_status_t conv_fprop_i8(const conv_i8_desc_t *image, const void *image_pt
                                void *stream);
 
 /*
+ * Counterpart of the plan list of the cuDNN frontend tutorial page
+ * (autotuning paragraph: plans from the heuristic modes, each one built and
+ * timed): here the single plan this library picks, for inspection.
+ *
  * A one-line, human-readable description of how conv_fprop_i8_ws would run
  * this problem (which operands are repacked, the tile shape, the grid).
  * Writes at most `len` bytes including the terminating NUL.  Host-only.
@@ -186,7 +206,9 @@ conv_i8_status_t conv_fprop_i8_plan(const conv_i8_desc_t *image, const void *ima
  * s_k = scale[k] when scale != NULL, else alpha; b_k = bias[k] when
  * bias != NULL, else 0.  scale and bias are device pointers to K floats,
  * 4-byte aligned, owned by the caller and read by the kernels on `stream`.
- * Non-finite scales or biases give unspecified bytes.  With alpha = 1 and no
+ * Non-finite factors: a value that is NaN after the multiply-add (an
+ * infinite scale times a zero sum, or infinities of opposite sign) is written
+ * as 0, and an infinite value saturates to -128 or 127.  With alpha = 1 and no
  * bias or relu the result is the page's saturating INT8 store.
  */
 typedef struct {
@@ -418,7 +440,13 @@ conv_i8_status_t conv_wgrad_i8(const conv_i8_desc_t *image, const void *image_pt
                                int32_t mode,
                                void *stream);
 
-/* Static string naming a status code. */
+/*
+ * Static string naming a status code.  The forum thread's answer post traces
+ * the question's wrong output to a descriptor mistake (strides that do not
+ * match the NCHW layout); each refusal above is reported by name instead of
+ * running on a descriptor the library cannot honour.  Unknown codes give a
+ * string containing "unknown".
+ */
 const char *conv_i8_status_string(conv_i8_status_t status);
 
 #ifdef __cplusplus

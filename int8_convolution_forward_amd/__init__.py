@@ -170,6 +170,37 @@ def _ptr(t: Optional[torch.Tensor]):
     return None if t is None else ctypes.c_void_p(t.data_ptr())
 
 
+def _on_one_gpu(**tensors) -> Optional[torch.device]:
+    """Every tensor handed to a C entry that the kernels read or write must be
+    GPU memory of one device: a host pointer dereferenced by a kernel faults
+    the GPU.  Raises before any C call; returns the device."""
+    dev = None
+    for name, t in tensors.items():
+        if t is None:
+            continue
+        if not isinstance(t, torch.Tensor):
+            raise TypeError(f"{name}: expected a torch.Tensor, got {type(t).__name__}")
+        if not t.is_cuda:
+            raise ValueError(f"{name}: expected a GPU tensor, got one on {t.device}")
+        if dev is None:
+            dev = t.device
+        elif t.device != dev:
+            raise ValueError(f"{name}: on {t.device}, but the other operands are on {dev}")
+    return dev
+
+
+def _workspace(n: int, device, stream) -> Optional[torch.Tensor]:
+    """n bytes of workspace from torch's caching allocator, allocated on the
+    stream the kernels run on, so the block is not handed to other work
+    before that stream has run the call."""
+    if not n:
+        return None
+    if stream is None:
+        return torch.empty(n, dtype=torch.uint8, device=device)
+    with torch.cuda.stream(stream):
+        return torch.empty(n, dtype=torch.uint8, device=device)
+
+
 def conv_fprop_i8_out_dims(x, w, pre_padding=0, post_padding=0, stride=1, dilation=1,
                            padding=None) -> Tuple[int, int, int, int]:
     pre, post, st, dl = _params(pre_padding, post_padding, stride, dilation, padding)
@@ -238,6 +269,7 @@ def conv_fprop_i8_ws(x: torch.Tensor, w: torch.Tensor, out: torch.Tensor, worksp
                      pre_padding=0, post_padding=0, stride=1, dilation=1, padding=None,
                      stream=None) -> torch.Tensor:
     """Direct call of the C entry with an explicit workspace tensor."""
+    _on_one_gpu(x=x, w=w, out=out, workspace=workspace)
     pre, post, st, dl = _params(pre_padding, post_padding, stride, dilation, padding)
     ws_ptr = _ptr(workspace)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
@@ -250,6 +282,7 @@ def conv_fprop_i8_ws(x: torch.Tensor, w: torch.Tensor, out: torch.Tensor, worksp
 def conv_fprop_i8_plain(x: torch.Tensor, w: torch.Tensor, out: torch.Tensor, pre_padding=0,
                         post_padding=0, stride=1, dilation=1, padding=None, stream=None) -> torch.Tensor:
     """The C entry that takes its own workspace with hipMallocAsync."""
+    _on_one_gpu(x=x, w=w, out=out)
     pre, post, st, dl = _params(pre_padding, post_padding, stride, dilation, padding)
     _check(lib.conv_fprop_i8(ctypes.byref(desc(x)), _ptr(x), ctypes.byref(desc(w)), _ptr(w),
                              ctypes.byref(desc(out)), _ptr(out), pre, post, st, dl,
@@ -265,13 +298,14 @@ def conv_fprop_i8(x: torch.Tensor, w: torch.Tensor, out: Optional[torch.Tensor] 
     x: int8 [N,C,H,W], w: int8 [K,C,R,S], any strides.  ``out`` (int32
     [N,K,P,Q], any non-overlapping strides) is written if given; otherwise a
     new tensor in x's memory format is returned.  The workspace, if needed, is
-    a torch allocation on the same stream.
+    a torch allocation on the stream the call runs on.
     """
+    _on_one_gpu(x=x, w=w, out=out)
     if out is None:
         dims = conv_fprop_i8_out_dims(x, w, pre_padding, post_padding, stride, dilation, padding)
         out = _out_like(x, dims)
     n = conv_fprop_i8_workspace_size(x, w, out, pre_padding, post_padding, stride, dilation, padding)
-    ws = torch.empty(n, dtype=torch.uint8, device=out.device) if n else None
+    ws = _workspace(n, out.device, stream)
     return conv_fprop_i8_ws(x, w, out, ws, pre_padding, post_padding, stride, dilation, padding,
                             stream)
 
@@ -308,6 +342,7 @@ def conv_fprop_i8_requant_ws(x: torch.Tensor, w: torch.Tensor, out: torch.Tensor
                              bias=None, relu: bool = False, pre_padding=0, post_padding=0,
                              stride=1, dilation=1, padding=None, stream=None) -> torch.Tensor:
     """Direct call of the requantising C entry with an explicit workspace."""
+    _on_one_gpu(x=x, w=w, out=out, workspace=workspace, scale=scale, bias=bias)
     pre, post, st, dl = _params(pre_padding, post_padding, stride, dilation, padding)
     rq = _requant(scale, alpha, bias, relu)
     ws_ptr = _ptr(workspace)
@@ -324,6 +359,7 @@ def conv_fprop_i8_requant_plain(x: torch.Tensor, w: torch.Tensor, out: torch.Ten
                                 post_padding=0, stride=1, dilation=1, padding=None,
                                 stream=None) -> torch.Tensor:
     """The requantising C entry that takes its own workspace (hipMallocAsync)."""
+    _on_one_gpu(x=x, w=w, out=out, scale=scale, bias=bias)
     pre, post, st, dl = _params(pre_padding, post_padding, stride, dilation, padding)
     rq = _requant(scale, alpha, bias, relu)
     _check(lib.conv_fprop_i8_requant(
@@ -346,6 +382,7 @@ def conv_fprop_i8_requant(x: torch.Tensor, w: torch.Tensor, scale: Optional[torc
     roadmap (ReLU and quantisation after the convolution, INT8 store with the
     clamp of its naive loop).
     """
+    _on_one_gpu(x=x, w=w, out=out, scale=scale, bias=bias)
     _check_channels(w, scale, "scale")
     _check_channels(w, bias, "bias")
     if out is None:
@@ -353,7 +390,7 @@ def conv_fprop_i8_requant(x: torch.Tensor, w: torch.Tensor, scale: Optional[torc
         out = _out_like(x, dims, torch.int8)
     n = conv_fprop_i8_requant_workspace_size(x, w, out, pre_padding, post_padding, stride,
                                              dilation, padding)
-    ws = torch.empty(n, dtype=torch.uint8, device=out.device) if n else None
+    ws = _workspace(n, out.device, stream)
     return conv_fprop_i8_requant_ws(x, w, out, ws, scale, alpha, bias, relu, pre_padding,
                                     post_padding, stride, dilation, padding, stream)
 
@@ -375,7 +412,9 @@ def conv_fprop_i8_ex_ws(x: torch.Tensor, w: torch.Tensor, out: torch.Tensor,
                         requant: Optional[Requant] = None, pre_padding=0, post_padding=0, stride=1,
                         dilation=1, padding=None, stream=None) -> torch.Tensor:
     """The general C entry: ``mode`` (0 cross-correlation, 1 true convolution)
-    and, for an int8 ``out``, the requantisation block from ``_requant``."""
+    and, for an int8 ``out``, the requantisation block from ``_requant`` (whose
+    scale and bias arrays must be GPU memory of the same device)."""
+    _on_one_gpu(x=x, w=w, out=out, workspace=workspace)
     pre, post, st, dl = _params(pre_padding, post_padding, stride, dilation, padding)
     ws_ptr = _ptr(workspace)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
@@ -395,6 +434,7 @@ def conv_fprop_i8_mode(x: torch.Tensor, w: torch.Tensor, mode: int, out: Optiona
     """conv_fprop in either mode.  INT32 output unless a requantisation is
     asked for (scale, alpha, bias or relu given), then INT8."""
     rq_on = scale is not None or alpha is not None or bias is not None or relu
+    _on_one_gpu(x=x, w=w, out=out, scale=scale, bias=bias)
     _check_channels(w, scale, "scale")
     _check_channels(w, bias, "bias")
     if out is None:
@@ -403,7 +443,7 @@ def conv_fprop_i8_mode(x: torch.Tensor, w: torch.Tensor, mode: int, out: Optiona
     rq = _requant(scale, 1.0 if alpha is None else alpha, bias, relu) if rq_on else None
     n = conv_fprop_i8_ex_workspace_size(x, w, out, pre_padding, post_padding, stride, dilation,
                                         padding, mode)
-    ws = torch.empty(n, dtype=torch.uint8, device=out.device) if n else None
+    ws = _workspace(n, out.device, stream)
     return conv_fprop_i8_ex_ws(x, w, out, ws, mode, rq, pre_padding, post_padding, stride,
                                dilation, padding, stream)
 
@@ -424,6 +464,7 @@ def conv_dgrad_i8_ws(dy: torch.Tensor, w: torch.Tensor, dx: torch.Tensor,
                      workspace: Optional[torch.Tensor], pre_padding=0, post_padding=0, stride=1,
                      dilation=1, padding=None, mode: int = 0, stream=None) -> torch.Tensor:
     """Direct call of the dgrad C entry with an explicit workspace."""
+    _on_one_gpu(dy=dy, w=w, dx=dx, workspace=workspace)
     pre, post, st, dl = _params(pre_padding, post_padding, stride, dilation, padding)
     ws_ptr = _ptr(workspace)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
@@ -438,6 +479,7 @@ def conv_dgrad_i8_plain(dy: torch.Tensor, w: torch.Tensor, dx: torch.Tensor, pre
                         post_padding=0, stride=1, dilation=1, padding=None, mode: int = 0,
                         stream=None) -> torch.Tensor:
     """The dgrad C entry that takes its own workspace (hipMallocAsync)."""
+    _on_one_gpu(dy=dy, w=w, dx=dx)
     pre, post, st, dl = _params(pre_padding, post_padding, stride, dilation, padding)
     _check(lib.conv_dgrad_i8(
         ctypes.byref(desc(dy)), _ptr(dy), ctypes.byref(desc(w)), _ptr(w), ctypes.byref(desc(dx)),
@@ -450,9 +492,10 @@ def conv_dgrad_i8(dy: torch.Tensor, w: torch.Tensor, dx: torch.Tensor, pre_paddi
                   stream=None) -> torch.Tensor:
     """dX (int32 [N,C,H,W], written into ``dx``, which fixes H and W) of the
     loss dY (int8 [N,K,P,Q]) through the filter w (int8 [K,C,R,S])."""
+    _on_one_gpu(dy=dy, w=w, dx=dx)
     n = conv_dgrad_i8_workspace_size(dy, w, dx, pre_padding, post_padding, stride, dilation,
                                      padding, mode)
-    ws = torch.empty(n, dtype=torch.uint8, device=dx.device) if n else None
+    ws = _workspace(n, dx.device, stream)
     return conv_dgrad_i8_ws(dy, w, dx, ws, pre_padding, post_padding, stride, dilation, padding,
                             mode, stream)
 
@@ -473,6 +516,7 @@ def conv_wgrad_i8_ws(x: torch.Tensor, dy: torch.Tensor, dw: torch.Tensor,
                      workspace: Optional[torch.Tensor], pre_padding=0, post_padding=0, stride=1,
                      dilation=1, padding=None, mode: int = 0, stream=None) -> torch.Tensor:
     """Direct call of the wgrad C entry with an explicit workspace."""
+    _on_one_gpu(x=x, dy=dy, dw=dw, workspace=workspace)
     pre, post, st, dl = _params(pre_padding, post_padding, stride, dilation, padding)
     ws_ptr = _ptr(workspace)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
@@ -487,6 +531,7 @@ def conv_wgrad_i8_plain(x: torch.Tensor, dy: torch.Tensor, dw: torch.Tensor, pre
                         post_padding=0, stride=1, dilation=1, padding=None, mode: int = 0,
                         stream=None) -> torch.Tensor:
     """The wgrad C entry that takes its own workspace (hipMallocAsync)."""
+    _on_one_gpu(x=x, dy=dy, dw=dw)
     pre, post, st, dl = _params(pre_padding, post_padding, stride, dilation, padding)
     _check(lib.conv_wgrad_i8(
         ctypes.byref(desc(x)), _ptr(x), ctypes.byref(desc(dy)), _ptr(dy), ctypes.byref(desc(dw)),
@@ -499,8 +544,9 @@ def conv_wgrad_i8(x: torch.Tensor, dy: torch.Tensor, dw: torch.Tensor, pre_paddi
                   stream=None) -> torch.Tensor:
     """dW (int32 [K,C,R,S], written into ``dw``, which fixes R and S) from the
     image x (int8 [N,C,H,W]) and the loss dY (int8 [N,K,P,Q])."""
+    _on_one_gpu(x=x, dy=dy, dw=dw)
     n = conv_wgrad_i8_workspace_size(x, dy, dw, pre_padding, post_padding, stride, dilation,
                                      padding, mode)
-    ws = torch.empty(n, dtype=torch.uint8, device=dw.device) if n else None
+    ws = _workspace(n, dw.device, stream)
     return conv_wgrad_i8_ws(x, dy, dw, ws, pre_padding, post_padding, stride, dilation, padding,
                             mode, stream)

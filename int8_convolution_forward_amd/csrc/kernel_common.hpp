@@ -97,12 +97,16 @@ struct IgemmArgs {
 
 // Requantising INT8 epilogue of one exact sum: the sum as a float, one fused
 // multiply-add with the channel's scale and bias, ReLU if asked, round half to
-// even, saturate to [-128, 127].  With scale 1 it is the clamped INT8 store of
-// the naive loop in "Building a From-Scratch INT8 Strided Convolution Kernel"
-// (step 2); the ReLU and scale are the quantisation step its roadmap fuses.
+// even, saturate to [-128, 127] (a NaN becomes 0).  With scale 1 it is the
+// clamped INT8 store of the naive loop in "Building a From-Scratch INT8
+// Strided Convolution Kernel" (step 2); the ReLU and scale are the
+// quantisation step its roadmap fuses.
 __device__ __forceinline__ int requant_i8(int acc, float s, float b, bool relu)
 {
     float v = __builtin_fmaf((float)acc, s, b);
+    // a NaN (an infinite scale or bias meeting a zero or opposite term) is
+    // written as 0; infinities saturate below
+    v = __builtin_isnan(v) ? 0.0f : v;
     if (relu)
         v = __builtin_fmaxf(v, 0.0f);
     v = __builtin_rintf(v);

@@ -234,11 +234,16 @@ int oracle_conv_fprop_points(const int8_t *x, const int64_t xdims[4], const int6
  * with s_k = scale[k] (or alpha for every k when scale is NULL) and
  * b_k = bias[k] (or 0 when bias is NULL).  (float)acc rounds to nearest
  * even; sums here stay below 2^31.  With s = 1 and no bias or relu this is
- * exactly the page's clamp.
+ * exactly the page's clamp.  The pages say nothing of non-finite factors;
+ * the reading taken: a NaN after the multiply-add (an infinite scale times a
+ * zero sum, or infinities of opposite sign) is written as 0, and an infinity
+ * saturates like any large value.
  */
 static int8_t oracle_requant(int64_t acc, float s, float b, int relu)
 {
     float v = fmaf((float)acc, s, b);
+    if (v != v)
+        v = 0.0f;  /* NaN (an infinite scale or bias): written as 0 */
     if (relu && v < 0.0f)
         v = 0.0f;
     v = nearbyintf(v);

@@ -389,6 +389,36 @@ def check_requant_exact(orc) -> None:
     assert np.array_equal(got, np.array([exact_requant(int(x), 0.5, 0.0, False) for x in t], np.int8))
 
 
+def check_requant_nonfinite(orc) -> None:
+    """Non-finite scale or bias: the pages are silent; the reading taken is
+    that a NaN after the multiply-add is written as 0 and an infinity
+    saturates.  Expected values written out by hand from that rule (IEEE:
+    inf * 0 and inf + -inf are NaN; inf * x for x != 0 is an infinity of the
+    product's sign)."""
+    inf, nan = float("inf"), float("nan")
+    # (acc, scale, bias, relu, expected)
+    cases = [
+        (0, inf, 0.0, False, 0), (0, -inf, 0.0, True, 0),          # inf * 0 = NaN
+        (5, inf, 0.0, False, 127), (-5, inf, 0.0, False, -128),    # signed infinities
+        (-5, inf, 0.0, True, 0), (5, -inf, 0.0, False, -128),
+        (7, nan, 0.0, False, 0), (7, nan, 3.0, True, 0),           # NaN scale
+        (3, 0.5, nan, False, 0), (-3, 0.5, nan, True, 0),          # NaN bias
+        (3, 0.5, inf, False, 127), (3, 0.5, -inf, False, -128),   # infinite bias
+        (3, 0.5, -inf, True, 0),
+        (4, inf, -inf, False, 0), (-4, inf, inf, True, 0),         # inf - inf = NaN
+        (100, 1e30, 1.0, False, 127), (-100, 1e30, 1.0, False, -128),  # overflow to inf
+    ]
+    acc = np.array([c[0] for c in cases], dtype=np.int64)
+    sc = np.array([c[1] for c in cases], dtype=np.float32)
+    bi = np.array([c[2] for c in cases], dtype=np.float32)
+    ch = np.arange(acc.size, dtype=np.int64)
+    for relu in (False, True):
+        got = orc.requant_values(acc, ch, scale=sc, bias=bi, relu=relu)
+        for i, (a, s_, b, r, want) in enumerate(cases):
+            if r == relu:
+                assert int(got[i]) == want, (a, s_, b, relu, int(got[i]), want)
+
+
 def check_requant_conv(orc) -> None:
     """The fused entry = the INT32 convolution followed by the exact epilogue,
     with per-output-channel scale and bias, into a strided INT8 output."""
@@ -577,5 +607,5 @@ def check_wgrad(orc) -> None:
 QUICK_CHECKS = [
     check_random_vs_brute_force, check_offcentre_delta, check_identity_1x1, check_ones_count,
     check_constant_min, check_layouts, check_metamorphic, check_points, check_requant_exact,
-    check_requant_conv, check_convolution_mode, check_dgrad, check_wgrad,
+    check_requant_nonfinite, check_requant_conv, check_convolution_mode, check_dgrad, check_wgrad,
 ]

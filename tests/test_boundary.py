@@ -387,3 +387,50 @@ def test_wgrad_argument_errors():
     n = ci8.conv_wgrad_i8_workspace_size(x, dy, dw, pre, post, st, dl)
     assert n > 0                                 # both transposed operands are repacked
     assert call(x, dy, dw, ws_bytes=n - 1, ws=FAKE) == 10
+
+
+class _NoCalls:
+    """Stands in for the loaded library: any use of an entry fails the test."""
+
+    def __getattr__(self, name):
+        raise AssertionError(f"the wrapper reached the C entry {name}")
+
+
+def _cpu_case():
+    x = torch.zeros((1, 16, 5, 5), dtype=torch.int8)
+    w = torch.zeros((4, 16, 3, 3), dtype=torch.int8)
+    y = torch.zeros((1, 4, 3, 3), dtype=torch.int32)
+    return x, w, y
+
+
+@pytest.mark.parametrize("call", [
+    lambda x, w, y: ci8.conv_fprop_i8(x, w, y),
+    lambda x, w, y: ci8.conv_fprop_i8(x, w),
+    lambda x, w, y: ci8.conv_fprop_i8_ws(x, w, y, None),
+    lambda x, w, y: ci8.conv_fprop_i8_plain(x, w, y),
+    lambda x, w, y: ci8.conv_fprop_i8_requant(x, w),
+    lambda x, w, y: ci8.conv_fprop_i8_requant_ws(x, w, y.to(torch.int8), None),
+    lambda x, w, y: ci8.conv_fprop_i8_requant_plain(x, w, y.to(torch.int8)),
+    lambda x, w, y: ci8.conv_fprop_i8_ex_ws(x, w, y, None),
+    lambda x, w, y: ci8.conv_fprop_i8_mode(x, w, ci8.MODE_CONVOLUTION),
+    lambda x, w, y: ci8.conv_dgrad_i8(y.to(torch.int8), w, torch.zeros((1, 16, 5, 5), dtype=torch.int32)),
+    lambda x, w, y: ci8.conv_dgrad_i8_ws(y.to(torch.int8), w, torch.zeros((1, 16, 5, 5), dtype=torch.int32), None),
+    lambda x, w, y: ci8.conv_dgrad_i8_plain(y.to(torch.int8), w, torch.zeros((1, 16, 5, 5), dtype=torch.int32)),
+    lambda x, w, y: ci8.conv_wgrad_i8(x, y.to(torch.int8), torch.zeros((4, 16, 3, 3), dtype=torch.int32)),
+    lambda x, w, y: ci8.conv_wgrad_i8_ws(x, y.to(torch.int8), torch.zeros((4, 16, 3, 3), dtype=torch.int32), None),
+    lambda x, w, y: ci8.conv_wgrad_i8_plain(x, y.to(torch.int8), torch.zeros((4, 16, 3, 3), dtype=torch.int32)),
+])
+def test_wrappers_refuse_host_tensors_before_any_c_call(monkeypatch, call):
+    """Host tensors would hand host pointers to the kernels: every wrapper
+    refuses them before it reaches the library."""
+    x, w, y = _cpu_case()
+    monkeypatch.setattr(ci8, "lib", _NoCalls())
+    with pytest.raises(ValueError, match="expected a GPU tensor"):
+        call(x, w, y)
+
+
+def test_wrappers_refuse_non_tensors(monkeypatch):
+    x, w, y = _cpu_case()
+    monkeypatch.setattr(ci8, "lib", _NoCalls())
+    with pytest.raises(TypeError, match="expected a torch.Tensor"):
+        ci8.conv_fprop_i8_ws(x.numpy(), w, y, None)

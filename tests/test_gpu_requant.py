@@ -181,3 +181,37 @@ def test_pointwise_requant(ci8, monkeypatch, case_i):
     sc, bi = channel_params(K, C, seed=case_i)
     run_requant_check(ci8, _fill(xs, xv, 7), xs, _fill(ws, wv, 8), ws, os_, pre, post, st, (1, 1),
                       scale=sc, bias=bi, relu=bool(case_i % 2), label=f"pointwise case {case_i}")
+
+
+@pytest.mark.parametrize("tile", [None, "f128x128", "pw64x128"])
+@pytest.mark.parametrize("relu", [False, True])
+def test_nonfinite_scale_and_bias(ci8, monkeypatch, tile, relu):
+    """Infinite and NaN scales and biases: a NaN after the multiply-add is
+    written as 0, infinities saturate (the oracle's reading, pinned on the
+    CPU).  Channel 0's filter is all zeros, so inf * 0 = NaN occurs; the
+    other channels see signed infinities, NaN scales and biases, and
+    infinities of opposite sign."""
+    if tile:
+        monkeypatch.setenv("CONV_I8_TILE", tile)
+    R = 1 if tile and tile.startswith("pw") else 3
+    N, C, H, W, K = 2, 64, 9, 7, 16
+    pad = (R - 1) // 2
+    xs = wl.TensorSpec((N, C, H, W), wl.channels_last_strides((N, C, H, W)))
+    ws = wl.TensorSpec((K, C, R, R), wl.channels_last_strides((K, C, R, R)))
+    od = oracle.out_dims(xs.dims, ws.dims, (pad, pad), (pad, pad), (1, 1), (1, 1))
+    os_ = wl.TensorSpec(od, wl.channels_last_strides(od))
+    g = torch.Generator().manual_seed(41)
+    xv = torch.randint(-128, 128, xs.dims, dtype=torch.int8, generator=g)
+    wv = torch.randint(-128, 128, ws.dims, dtype=torch.int8, generator=g)
+    wv[0] = 0
+    inf, nan = np.float32("inf"), np.float32("nan")
+    sc = np.array([inf, inf, -inf, nan, 0.01, 0.01, 0.01, inf, -inf, nan, 1e30, -1e30, 0.02, inf, 0.0, inf],
+                  dtype=np.float32)
+    bi = np.array([0, 0, 1, 0, nan, inf, -inf, -inf, -inf, 5, 0, 0, nan, nan, inf, inf], dtype=np.float32)
+    f = ci8.plan_fields(ci8.conv_fprop_i8_plan(ci8.desc(xs.dims, xs.strides, 1), ci8.desc(ws.dims, ws.strides, 1),
+                                               ci8.desc(os_.dims, os_.strides, 2), (pad, pad), (pad, pad),
+                                               (1, 1), (1, 1)))
+    if tile:
+        assert f["tile"] == tile, f
+    run_requant_check(ci8, _fill(xs, xv, 7), xs, _fill(ws, wv, 8), ws, os_, (pad, pad), (pad, pad),
+                      (1, 1), (1, 1), scale=sc, bias=bi, relu=relu, label=f"nonfinite {tile}")

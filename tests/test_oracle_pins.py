@@ -108,6 +108,10 @@ def test_requant_exact(orc):
     pins.check_requant_exact(orc)
 
 
+def test_requant_nonfinite(orc):
+    pins.check_requant_nonfinite(orc)
+
+
 def test_requant_conv(orc):
     pins.check_requant_conv(orc)
 
@@ -213,6 +217,7 @@ MUTATIONS = [
     ("requant per-tensor scale", "const float s = scale ? scale[k] : alpha;", "const float s = scale ? scale[0] : alpha;"),
     ("requant bias ignored", "const float b = bias ? bias[k] : 0.0f;", "const float b = 0.0f;"),
     ("requant channel from the wrong index", "scale ? scale[ch[i]] : alpha", "scale ? scale[i % 2] : alpha"),
+    ("requant NaN written as -128", "v = 0.0f;  /* NaN", "v = -128.0f;  /* NaN"),
 ]
 
 
