@@ -399,3 +399,30 @@ def test_pointwise_kernel(ci8, monkeypatch, case_i, layout):
     wv = torch.randint(-128, 128, (K, C, 1, 1), dtype=torch.int8, generator=g)
     run_and_check(ci8, _fill(xs, xv, 3), xs, _fill(ws, wv, 4), ws, os_, pre, post, st, (1, 1),
                   label=f"pointwise case {case_i} {layout}")
+
+
+def test_side_stream_workspace(ci8):
+    """A call on a side stream whose operands need repacking: the wrapper's
+    workspace belongs to that stream, so work queued on the current stream
+    right after the call cannot be handed the same block while the side
+    stream still uses it.  Repeated calls with a busy current stream in
+    between all give the oracle's bytes."""
+    c = wl.case("dilated_asym_n16_c96_64x48")
+    d = wl.make_inputs(c, c.seed_base + 3)
+    xg = _to_dev(d["x_storage"], c.image)
+    wg = _to_dev(d["w_storage"], c.filter)
+    ref = oracle.conv_fprop(d["x"], d["w"], c.pre, c.post, c.stride, c.dilation)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    outs = []
+    print(f"[gpu] side-stream calls on {c.name}", flush=True)
+    for i in range(4):
+        y = ci8.conv_fprop_i8(xg, wg, None, c.pre, c.post, c.stride, c.dilation, stream=side)
+        y.record_stream(side)
+        # allocations and writes on the current stream while the side stream runs
+        junk = torch.full((8 << 20,), i + 1, dtype=torch.uint8, device=_dev())
+        junk.add_(1)
+        outs.append(y)
+    torch.cuda.synchronize()
+    for y in outs:
+        assert torch.equal(y.cpu(), ref)
