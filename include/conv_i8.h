@@ -87,7 +87,8 @@ typedef enum {
     CONV_I8_ERR_RANGE = 9,       /* C*R*S > 131071: int32 sums no longer exact */
     CONV_I8_ERR_WORKSPACE = 10,  /* workspace smaller than conv_fprop_i8_workspace_size */
     CONV_I8_ERR_UNSUPPORTED = 11,/* one image or the filter spans >= 2 GiB */
-    CONV_I8_ERR_HIP = 12         /* a HIP runtime call failed */
+    CONV_I8_ERR_HIP = 12,        /* a HIP runtime call failed */
+    CONV_I8_ERR_SCRATCH = 13     /* conv_fprop_i8_noalloc: workspace needed exceeds its scratch array */
 } conv_i8_status_t;
 
 /* Largest C*R*S for which the int32 sum is exact for all int8 inputs. */
@@ -168,6 +169,36 @@ conv_i8_status_t conv_fprop_i8(const conv_i8_desc_t *image, const void *image_pt
                                const int64_t stride[2],
                                const int64_t dilation[2],
                                void *stream);
+
+/*
+ * For callers that cannot allocate device memory: code being recorded into a
+ * HIP graph, tight serving loops, harnesses that forbid hipMalloc.
+ *
+ * Same operation, arguments and errors as conv_fprop_i8 (no workspace
+ * argument), but any workspace the problem needs (the packed channel-innermost
+ * copies of an image or filter the kernels cannot read in place) comes from a
+ * static device array of CONV_I8_NOALLOC_SCRATCH_BYTES bytes, one per GPU,
+ * held from the first call on that GPU until the process ends.  Calls no
+ * hipMalloc/hipFree and no allocating library routine.  A problem needing
+ * more returns CONV_I8_ERR_SCRATCH before any device work (the
+ * conv_fprop_i8_workspace_size of the same arguments tells the need).  The
+ * calling thread's current device must be the device of `stream`
+ * (CONV_I8_ERR_PARAM otherwise).  Every call on one GPU shares that GPU's
+ * array: calls that overlap in time on one GPU (other streams, other host
+ * threads) race on it and must be serialised by the caller; consecutive calls
+ * on one stream are fine.  The array keeps the last call's contents; nothing
+ * in it needs to start at zero.
+ */
+#define CONV_I8_NOALLOC_SCRATCH_BYTES (16u << 20)
+
+conv_i8_status_t conv_fprop_i8_noalloc(const conv_i8_desc_t *image, const void *image_ptr,
+                                       const conv_i8_desc_t *filter, const void *filter_ptr,
+                                       const conv_i8_desc_t *out, void *out_ptr,
+                                       const int64_t pre_padding[2],
+                                       const int64_t post_padding[2],
+                                       const int64_t stride[2],
+                                       const int64_t dilation[2],
+                                       void *stream);
 
 /*
  * Counterpart of the plan list of the cuDNN frontend tutorial page

@@ -26,7 +26,7 @@ import torch
 from . import build as _build
 
 __all__ = [
-    "ConvI8Error", "conv_fprop_i8", "conv_fprop_i8_ws", "conv_fprop_i8_plain",
+    "ConvI8Error", "conv_fprop_i8", "conv_fprop_i8_ws", "conv_fprop_i8_plain", "conv_fprop_i8_noalloc",
     "conv_fprop_i8_out_dims", "conv_fprop_i8_workspace_size", "conv_fprop_i8_plan",
     "conv_fprop_i8_requant", "conv_fprop_i8_requant_ws", "conv_fprop_i8_requant_plain",
     "conv_fprop_i8_requant_workspace_size", "Requant", "conv_fprop_i8_ex_ws",
@@ -49,7 +49,9 @@ STATUS = {
     4: "CONV_I8_ERR_DIMS", 5: "CONV_I8_ERR_PARAM", 6: "CONV_I8_ERR_CHANNELS",
     7: "CONV_I8_ERR_OUT_DIMS", 8: "CONV_I8_ERR_STRIDES", 9: "CONV_I8_ERR_RANGE",
     10: "CONV_I8_ERR_WORKSPACE", 11: "CONV_I8_ERR_UNSUPPORTED", 12: "CONV_I8_ERR_HIP",
+    13: "CONV_I8_ERR_SCRATCH",
 }
+NOALLOC_SCRATCH_BYTES = 16 << 20
 
 
 class Desc(ctypes.Structure):
@@ -86,6 +88,7 @@ lib.conv_fprop_i8_workspace_size.argtypes = [_DP, _P, _DP, _P, _DP, _V2, _V2, _V
 lib.conv_fprop_i8_ws.argtypes = [_DP, _P, _DP, _P, _DP, _P, _V2, _V2, _V2, _V2, _P,
                                  ctypes.c_size_t, _P]
 lib.conv_fprop_i8.argtypes = [_DP, _P, _DP, _P, _DP, _P, _V2, _V2, _V2, _V2, _P]
+lib.conv_fprop_i8_noalloc.argtypes = [_DP, _P, _DP, _P, _DP, _P, _V2, _V2, _V2, _V2, _P]
 lib.conv_fprop_i8_plan.argtypes = [_DP, _P, _DP, _P, _DP, _V2, _V2, _V2, _V2,
                                    ctypes.c_char_p, ctypes.c_size_t]
 _RQ = ctypes.POINTER(Requant)
@@ -111,7 +114,7 @@ lib.conv_wgrad_i8.argtypes = [_DP, _P, _DP, _P, _DP, _P, _V2, _V2, _V2, _V2, cty
 lib.conv_i8_status_string.argtypes = [ctypes.c_int]
 lib.conv_i8_status_string.restype = ctypes.c_char_p
 for _f in ("conv_fprop_i8_out_dims", "conv_fprop_i8_workspace_size", "conv_fprop_i8_ws",
-           "conv_fprop_i8", "conv_fprop_i8_plan", "conv_fprop_i8_requant_workspace_size",
+           "conv_fprop_i8", "conv_fprop_i8_noalloc", "conv_fprop_i8_plan", "conv_fprop_i8_requant_workspace_size",
            "conv_fprop_i8_requant_ws", "conv_fprop_i8_requant", "conv_fprop_i8_ex_workspace_size",
            "conv_fprop_i8_ex_ws", "conv_dgrad_i8_workspace_size", "conv_dgrad_i8_ws", "conv_dgrad_i8",
            "conv_wgrad_i8_workspace_size", "conv_wgrad_i8_ws", "conv_wgrad_i8"):
@@ -287,6 +290,19 @@ def conv_fprop_i8_plain(x: torch.Tensor, w: torch.Tensor, out: torch.Tensor, pre
     _check(lib.conv_fprop_i8(ctypes.byref(desc(x)), _ptr(x), ctypes.byref(desc(w)), _ptr(w),
                              ctypes.byref(desc(out)), _ptr(out), pre, post, st, dl,
                              _stream_handle(stream)))
+    return out
+
+
+def conv_fprop_i8_noalloc(x: torch.Tensor, w: torch.Tensor, out: torch.Tensor, pre_padding=0,
+                          post_padding=0, stride=1, dilation=1, padding=None,
+                          stream=None) -> torch.Tensor:
+    """The C entry that allocates nothing: its workspace is the library's
+    static per-GPU scratch array (calls overlapping on one GPU race on it)."""
+    _on_one_gpu(x=x, w=w, out=out)
+    pre, post, st, dl = _params(pre_padding, post_padding, stride, dilation, padding)
+    _check(lib.conv_fprop_i8_noalloc(ctypes.byref(desc(x)), _ptr(x), ctypes.byref(desc(w)), _ptr(w),
+                                     ctypes.byref(desc(out)), _ptr(out), pre, post, st, dl,
+                                     _stream_handle(stream)))
     return out
 
 

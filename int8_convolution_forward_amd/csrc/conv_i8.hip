@@ -1106,6 +1106,52 @@ conv_i8_status_t entry_run(const conv_i8_desc_t *image, const void *image_ptr,
     return st;
 }
 
+// ---------------------------------------------------------------------------
+// Allocation-free entry: the workspace is a static device array (one copy per
+// GPU, alive until the process ends) instead of caller memory or
+// hipMallocAsync.  Host code never passes the array's name to a kernel or a
+// copy: the name is a host-side stand-in; the device address comes from
+// hipGetSymbolAddress, taken once per device with that device current.
+// ---------------------------------------------------------------------------
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mutex;
+void *g_scratch_ptr[kMaxDevices] = {};
+
+}  // namespace
+}  // namespace convi8
+
+static __device__ __align__(256) uint8_t scratch[CONV_I8_NOALLOC_SCRATCH_BYTES];
+
+namespace convi8 {
+namespace {
+
+// Device address of this device's scratch array (the device current on the
+// calling thread, which must be the device of the stream the call uses).
+conv_i8_status_t scratch_address(void *stream, void **addr)
+{
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess)
+        return CONV_I8_ERR_HIP;
+    if (dev < 0 || dev >= kMaxDevices)
+        return CONV_I8_ERR_UNSUPPORTED;
+    if (stream) {
+        int sdev = -1;
+        if (hipStreamGetDevice((hipStream_t)stream, &sdev) != hipSuccess)
+            return CONV_I8_ERR_HIP;
+        if (sdev != dev)
+            return CONV_I8_ERR_PARAM;
+    }
+    std::lock_guard<std::mutex> lock(g_scratch_mutex);
+    if (!g_scratch_ptr[dev]) {
+        void *p = nullptr;
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p)
+            return CONV_I8_ERR_HIP;
+        g_scratch_ptr[dev] = p;
+    }
+    *addr = g_scratch_ptr[dev];
+    return CONV_I8_OK;
+}
+
 // Output dtype and requantisation block of the extended entries: INT32
 // without a block, INT8 with one.
 conv_i8_status_t ex_out_dtype(const conv_i8_desc_t *out, const conv_i8_requant_t *rq, int32_t *dt)
@@ -1724,6 +1770,30 @@ conv_i8_status_t conv_fprop_i8(const conv_i8_desc_t *image, const void *image_pt
                      true, nullptr, 0, stream);
 }
 
+conv_i8_status_t conv_fprop_i8_noalloc(const conv_i8_desc_t *image, const void *image_ptr,
+                                       const conv_i8_desc_t *filter, const void *filter_ptr,
+                                       const conv_i8_desc_t *out, void *out_ptr,
+                                       const int64_t pre_padding[2], const int64_t post_padding[2],
+                                       const int64_t stride[2], const int64_t dilation[2],
+                                       void *stream)
+{
+    using namespace convi8;
+    size_t need = 0;
+    conv_i8_status_t st = entry_workspace_size(image, image_ptr, filter, filter_ptr, out, pre_padding,
+                                               post_padding, stride, dilation, CONV_I8_DT_INT32,
+                                               CONV_I8_MODE_CROSS_CORRELATION, &need);
+    if (st != CONV_I8_OK)
+        return st;
+    if (need > (size_t)CONV_I8_NOALLOC_SCRATCH_BYTES)
+        return CONV_I8_ERR_SCRATCH;
+    void *ws = nullptr;
+    if ((st = scratch_address(stream, &ws)) != CONV_I8_OK)
+        return st;
+    return entry_run(image, image_ptr, filter, filter_ptr, out, out_ptr, pre_padding, post_padding,
+                     stride, dilation, CONV_I8_DT_INT32, CONV_I8_MODE_CROSS_CORRELATION, nullptr,
+                     false, ws, (size_t)CONV_I8_NOALLOC_SCRATCH_BYTES, stream);
+}
+
 conv_i8_status_t conv_fprop_i8_requant_workspace_size(
     const conv_i8_desc_t *image, const void *image_ptr, const conv_i8_desc_t *filter,
     const void *filter_ptr, const conv_i8_desc_t *out, const int64_t pre_padding[2],
@@ -1891,6 +1961,7 @@ const char *conv_i8_status_string(conv_i8_status_t status)
     case CONV_I8_ERR_WORKSPACE: return "CONV_I8_ERR_WORKSPACE: workspace too small or not 256-byte aligned";
     case CONV_I8_ERR_UNSUPPORTED: return "CONV_I8_ERR_UNSUPPORTED: a single image or the filter spans >= 2 GiB";
     case CONV_I8_ERR_HIP: return "CONV_I8_ERR_HIP: a HIP runtime call failed";
+    case CONV_I8_ERR_SCRATCH: return "CONV_I8_ERR_SCRATCH: the problem needs more workspace than conv_fprop_i8_noalloc's static scratch array holds (CONV_I8_NOALLOC_SCRATCH_BYTES); call conv_fprop_i8_ws with a caller workspace instead";
     }
     return "unknown conv_i8 status";
 }

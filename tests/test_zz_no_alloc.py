@@ -1,0 +1,76 @@
+"""The allocation-free entry conv_fprop_i8_noalloc (static per-GPU scratch
+array) against conv_fprop_i8_ws with a caller workspace: byte-identical
+outputs on two calls in a row, the second on a smaller problem, and a
+problem too large for the array refused before any device work."""
+import ctypes
+
+import pytest
+import torch
+
+import oracle
+import workloads as wl
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def ci8():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import int8_convolution_forward_amd as m
+    return m
+
+
+def _dev():
+    return torch.device("cuda:0")
+
+
+def _pair(ci8, c, seed):
+    """(x, w, out via the _ws entry, out via the noalloc entry) for a case."""
+    d = wl.make_inputs(c, seed)
+    xg = wl.to_device(d["x_storage"], c.image, _dev())[1]
+    wg = wl.to_device(d["w_storage"], c.filter, _dev())[1]
+    need = ci8.conv_fprop_i8_workspace_size(xg, wg, ci8.desc(c.out.dims, c.out.strides, ci8.DT_INT32),
+                                            c.pre, c.post, c.stride, c.dilation)
+    assert 0 < need <= ci8.NOALLOC_SCRATCH_BYTES, need
+    ys = wl.alloc_output(c.out, _dev())[1]
+    yn = wl.alloc_output(c.out, _dev(), fill=-12345)[1]
+    ws = torch.empty(need, dtype=torch.uint8, device=_dev())
+    print(f"[gpu] noalloc vs ws: {c.name} seed {seed} workspace {need} bytes", flush=True)
+    ci8.conv_fprop_i8_ws(xg, wg, ys, ws, c.pre, c.post, c.stride, c.dilation)
+    ci8.conv_fprop_i8_noalloc(xg, wg, yn, c.pre, c.post, c.stride, c.dilation)
+    torch.cuda.synchronize()
+    return d, ys.cpu(), yn.cpu()
+
+
+def test_noalloc_matches_workspace_entry(ci8):
+    # first call: the dilated case (both operands repacked, ~5 MB of scratch)
+    big = wl.case("dilated_asym_n16_c96_64x48")
+    d, ys, yn = _pair(ci8, big, big.seed_base)
+    assert torch.equal(ys, yn)
+    # second call, smaller problem: the tiny case (repacks of a few hundred
+    # bytes into the same array, which still holds the first call's bytes)
+    tiny = wl.case("tiny_5x5_r3")
+    d2, ys2, yn2 = _pair(ci8, tiny, tiny.seed_base + 1)
+    assert torch.equal(ys2, yn2)
+    ref = oracle.conv_fprop(d2["x"], d2["w"], tiny.pre, tiny.post, tiny.stride, tiny.dilation)
+    assert torch.equal(yn2, ref)
+    # and the first problem again after the smaller one
+    d3, ys3, yn3 = _pair(ci8, big, big.seed_base + 2)
+    assert torch.equal(ys3, yn3)
+
+
+def test_noalloc_refuses_problems_beyond_its_scratch(ci8):
+    """An NCHW image of 25.7 MB must be repacked into more than the array
+    holds: refused with CONV_I8_ERR_SCRATCH, output untouched."""
+    N, C, H, W, K = 256, 512, 14, 14, 16
+    x = torch.zeros((N, C, H, W), dtype=torch.int8, device=_dev())
+    w = torch.zeros((K, C, 3, 3), dtype=torch.int8, device=_dev())
+    y = torch.full((N, K, H, W), 7, dtype=torch.int32, device=_dev())
+    need = ci8.conv_fprop_i8_workspace_size(x, w, y, 1, 1, 1, 1)
+    assert need > ci8.NOALLOC_SCRATCH_BYTES
+    with pytest.raises(ci8.ConvI8Error) as e:
+        ci8.conv_fprop_i8_noalloc(x, w, y, 1, 1, 1, 1)
+    assert e.value.name == "CONV_I8_ERR_SCRATCH"
+    torch.cuda.synchronize()
+    assert bool((y == 7).all())
