@@ -255,6 +255,15 @@ void launch_fp3x3(bool, bool pix_j, dim3 grid, hipStream_t stream, const IgemmAr
         hipLaunchKernelGGL((conv_footprint3x3_kernel<TM, TN, NS, FPIX, WGM, WGN, false, KSPL>), grid, block, 0, stream, a);
 }
 
+template <int TM, int TN, int FPIX, bool TAIL>
+void launch_fp9(bool, bool pix_j, dim3 grid, hipStream_t stream, const IgemmArgs &a)
+{
+    if (pix_j)
+        hipLaunchKernelGGL((conv_fp3x3_ring9_kernel<TM, TN, FPIX, 2, 2, true, TAIL>), grid, dim3(256), 0, stream, a);
+    else
+        hipLaunchKernelGGL((conv_fp3x3_ring9_kernel<TM, TN, FPIX, 2, 2, false, TAIL>), grid, dim3(256), 0, stream, a);
+}
+
 constexpr int kPointwiseTilesPerWave = 4;
 
 template <int FN, int KS>
@@ -298,6 +307,11 @@ const TileCfg kTiles[] = {
     {"f128x128", 128, 128, 64, 6, 4, kFootprint, 384, 0.62, launch_fp3x3<128, 128, 6, 384>},
     {"fk256x128", 256, 128, 64, 6, 8, kFootprint, 448, 0.60, launch_fp3x3<256, 128, 6, 448, 2, 2, 2>},
     {"fk128x128", 128, 128, 64, 6, 8, kFootprint, 384, 0.55, launch_fp3x3<128, 128, 6, 384, 2, 2, 2>},
+    // nine-slot ring; "t": the last channel block row block by row block,
+    // each row block stored as soon as it is done
+    {"r256x128", 256, 128, 64, 9, 4, kFootprint, 448, 0.70, launch_fp9<256, 128, 448, false>},
+    {"t256x128", 256, 128, 64, 9, 4, kFootprint, 448, 0.77, launch_fp9<256, 128, 448, true>},
+    {"t128x128", 128, 128, 64, 9, 4, kFootprint, 384, 0.60, launch_fp9<128, 128, 384, true>},
     // 1x1 streaming kernel: tm = pixels per wave tile, tn = output channels covered,
     // bk = channels covered
     {"pw32x64", 32, 32, 64, 0, 4, kPointwise, 0, 1.0, launch_pw<1, 2>},
@@ -833,6 +847,7 @@ conv_i8_status_t run(const Problem &pb, const Plan &pl, const void *x_ptr, const
     a.inv_cc = a.cc > 0 ? 1.0f / (float)a.cc : 0.0f;
     a.inv_s = 1.0f / (float)a.S;
     a.tiles_n = (int)((pb.K + c.tn - 1) / c.tn);
+    a.d_tn = make_divisor(a.tiles_n > 0 ? a.tiles_n : 1);
     a.d_pq = make_divisor(pb.P * pb.Q);
     a.d_q = make_divisor(pb.Q);
     a.Hp = (int)pl.Hp;

@@ -391,5 +391,469 @@ __global__ __launch_bounds__(64 * WGM * WGN * KSPL) void conv_footprint3x3_kerne
 }
 
 
+namespace fp9 {
+
+// Schedule of the nine-slot variant below.  Ring slot = filter tap, so the
+// load of stage (block b, tap t) for block b+1 goes into the slot it vacates.
+// The footprint of block b+1 (buffer (b+1)&1, free since block b-1's last
+// read) rides in kChunks pieces: the first on tap 8 of block b-1, the rest on
+// taps 0 .. kChunks-2 of block b, so the last piece has 8-(kChunks-2) stages
+// to land before tap 8 of block b reads block b+1.
+constexpr int kChunks = 6;
+
+// index of the footprint chunk issued at tap t (-1: none)
+constexpr int chunk_at(int t)
+{
+    return t == 8 ? 0 : (t < kChunks - 1 ? t + 1 : -1);
+}
+
+template <int NG>
+constexpr int chunk_lo(int c)
+{
+    return c * NG / kChunks;
+}
+
+// loads a thread issues at tap t
+template <int NG, int BL>
+constexpr int loads_at(int t)
+{
+    const int c = chunk_at(t);
+    return BL + (c < 0 ? 0 : chunk_lo<NG>(c + 1) - chunk_lo<NG>(c));
+}
+
+// Loads that may still be in flight at the wait on top of the stage at tap t.
+// That stage reads the fragments of the next stage: for t < 8 the filter of
+// (b, t+1), issued at (b-1, t+1), so the loads of taps t+2 .. 8 of the
+// previous block and 0 .. t-1 of this one may be outstanding; for t = 8 the
+// filter of (b+1, 0) and the whole footprint of block b+1, whose last piece
+// goes out at tap kChunks-2, so only taps kChunks-1 .. 7 may be outstanding.
+template <int NG, int BL>
+constexpr int allowed_at(int t)
+{
+    int n = 0;
+    if (t < 8) {
+        for (int u = t + 2; u <= 8; ++u)
+            n += loads_at<NG, BL>(u);
+        for (int u = 0; u < t; ++u)
+            n += loads_at<NG, BL>(u);
+    } else {
+        for (int u = kChunks - 1; u <= 7; ++u)
+            n += loads_at<NG, BL>(u);
+    }
+    return n;
+}
+
+// Footprint pieces a thread issues at tap t.
+template <int NG>
+constexpr int pieces_at(int t)
+{
+    const int c = chunk_at(t);
+    return c < 0 ? 0 : chunk_lo<NG>(c + 1) - chunk_lo<NG>(c);
+}
+
+// Block 0.  The prologue issues the filter of (0, 0), the footprint of block
+// 0, the filters of (0, 1) and (0, 2) and chunk 0 of block 1; stage (0, t)
+// then issues, in this order, the filter of (0, t+3) (t <= 5), the filter of
+// (1, t) and its footprint chunk.  Loads that may be outstanding at the wait
+// on top of stage (0, t), which needs the filter of (0, t+1) (for t = 8: the
+// filter of (1, 0) and the footprint of block 1, whose last chunk goes out at
+// tap kChunks-2):
+template <int NG, int BL>
+constexpr int allowed_first(int t)
+{
+    if (t == 0)
+        return BL + chunk_lo<NG>(1);
+    if (t == 1)
+        return chunk_lo<NG>(1) + 2 * BL + pieces_at<NG>(0);
+    if (t < 8)
+        return BL + pieces_at<NG>(t - 2) + (t - 1 <= 5 ? BL : 0) + BL + pieces_at<NG>(t - 1);
+    int n = 0;
+    for (int u = kChunks - 1; u <= 7; ++u)
+        n += (u <= 5 ? BL : 0) + BL + pieces_at<NG>(u);
+    return n;
+}
+
+}  // namespace fp9
+
+// 3x3 footprint kernel with a nine-slot filter ring (one slot per tap) and a
+// per-block loop.  With TAIL, the last 64-channel block runs row block by row
+// block: every filter fragment of that block is read once into registers,
+// then for each 32-row block x of the wave tile the nine taps' image
+// fragments are multiplied and row block x is stored at once, so its INT32
+// stores drain while the MFMAs of the next row blocks run (instead of the
+// whole tile's stores after the last MFMA).  Four waves, 2 x 2 (WGM x WGN).
+template <int TM, int TN, int FPIX, int WGM, int WGN, bool PIX_J, bool TAIL>
+__global__ __launch_bounds__(64 * WGM * WGN) void conv_fp3x3_ring9_kernel(IgemmArgs a)
+{
+    using namespace fp3x3;
+    using namespace fp9;
+    constexpr int NW = WGM * WGN;
+    constexpr int GB = NW * 1024;            // bytes of one workgroup-wide load
+    constexpr int BK = 64;                   // channels per stage
+    constexpr int PITCH = 80;                // footprint bytes per pixel
+    constexpr int BL = TN * BK / GB;         // filter loads per thread per stage
+    constexpr int B_BYTES = TN * BK;         // one ring slot
+    constexpr int NG = (FPIX * PITCH + GB - 1) / GB;
+    constexpr int FBUF = NG * GB;
+    constexpr int WM = TM / WGM, WN = TN / WGN;
+    constexpr int FM = WM / 32, FN = WN / 32;
+    constexpr int KS = 2;                    // k-steps of 32 channels per stage
+    constexpr int NMF = KS * FM * FN;
+    constexpr int NRD = KS * (FM + FN);
+    static_assert(BL >= 1 && TN * BK % GB == 0, "filter tile must fill workgroup loads");
+    static_assert(NW == 4, "four waves");
+    static_assert(FM >= 1 && FN >= 1, "wave tile");
+    static_assert(allowed_at<NG, BL>(0) < 64 && allowed_at<NG, BL>(7) < 64 && allowed_first<NG, BL>(8) < 64 &&
+                      2 * BL + chunk_lo<NG>(1) < 64,
+                  "vmcnt range");
+
+    __shared__ __attribute__((aligned(1024))) int8_t ring[kTaps * B_BYTES];
+    __shared__ __attribute__((aligned(1024))) int8_t fbuf[2 * FBUF];
+    __shared__ int out_row[PIX_J ? 1 : TM];
+
+    // every argument the prologue needs, loaded in one round trip (left to
+    // itself the compiler loads some of them only where they are first used,
+    // a second round trip before the first load can be issued)
+    asm volatile("" ::"s"(a.img), "s"(a.flt), "s"(a.img_range), "s"(a.flt_range), "s"(a.fK), "s"(a.flt0),
+                 "s"(a.fR), "s"(a.fS), "s"(a.K), "s"(a.tiles), "s"(a.tiles_n), "s"(a.ncblk), "s"(a.sN), "s"(a.sH),
+                 "s"(a.sW), "s"(a.H), "s"(a.W), "s"(a.Pr), "s"(a.Hp), "s"(a.Wf));
+    asm volatile("" ::"s"(a.Q), "s"(a.PQ), "s"(a.M), "s"(a.strH), "s"(a.strW), "s"(a.dilH), "s"(a.dilW),
+                 "s"(a.padH), "s"(a.padW), "s"(a.d_pq.m), "s"(a.d_pq.l), "s"(a.d_q.m), "s"(a.d_q.l),
+                 "s"(a.d_tn.m), "s"(a.d_tn.l), "s"(a.inv_pr), "s"(a.inv_hp));
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int tile = xcd_tile(blockIdx.x, a.tiles);
+    const int tm = udiv(tile, a.d_tn);
+    const int m0 = tm * TM;
+    const int n0 = (tile - tm * a.tiles_n) * TN;
+    const int wm = (wave / WGN) * WM;
+    const int wn = (wave % WGN) * WN;
+
+    // ---- footprint geometry of this tile (uniform) ------------------------
+    const int m_last = min(m0 + TM, a.M) - 1;
+    const int n_a = udiv(m0, a.d_pq);
+    const int p_a = udiv(m0 - n_a * a.PQ, a.d_q);
+    const int hp_a = p_a * a.strH;
+    const int n_b = udiv(m_last, a.d_pq);
+    const int p_b = udiv(m_last - n_b * a.PQ, a.d_q);
+    const int frows = (n_b - n_a) * a.Hp + p_b * a.strH + 2 * a.dilH - hp_a + 1;
+
+    int foff[NG];
+#pragma unroll
+    for (int g = 0; g < NG; ++g) {
+        const int slot = g * (GB / 16) + wave * 64 + lane;
+        const int fr = fdiv(slot, a.Pr, a.inv_pr);
+        const int rem = slot - fr * a.Pr;
+        const int fc = rem / 5;
+        const int j = rem - fc * 5;
+        const int hr = hp_a + fr;
+        const int dn = fdiv(hr, a.Hp, a.inv_hp);
+        const int h = hr - dn * a.Hp - a.padH;
+        const int w = fc - a.padW;
+        const bool ok = (j < 4) & (fc < a.Wf) & (fr < frows) & ((unsigned)h < (unsigned)a.H) &
+                        ((unsigned)w < (unsigned)a.W);
+        foff[g] = ok ? (n_a + dn) * a.sN + h * a.sH + w * a.sW + j * 16 : kOutOfRange;
+    }
+
+    const int row0 = wave * 16 + (lane >> 2);
+    const int jb = swizzle_chunk<64>(row0, lane & 3);
+    int b_off[BL];
+#pragma unroll
+    for (int i = 0; i < BL; ++i) {
+        const int k = n0 + row0 + i * NW * 16;
+        b_off[i] = k < a.K ? k * a.fK + jb * 16 : kOutOfRange;
+    }
+    int a_lane[FM][KS];
+    int b_lane[FN][KS];
+
+    const v4i img_rsrc = make_rsrc(a.img, a.img_range);
+    const v4i flt_rsrc = make_rsrc(a.flt, a.flt_range);
+    const unsigned ring_lds = lds_address(ring) + wave * 1024;
+    const unsigned fbuf_lds = lds_address(fbuf) + wave * 1024;
+    const int nblk = a.ncblk;
+    const bool tail = TAIL && nblk > 0;
+    const int nend = tail ? nblk - 1 : nblk;   // blocks run by the main loop
+
+    auto tap_read = [&](int t) { return ((t / 3) * a.dilH * a.Pr + (t % 3) * a.dilW * 5) * 16; };
+    auto tap_flt = [&](int t) { return a.flt0 + (t / 3) * a.fR + (t % 3) * a.fS; };
+    // filter of (block cb, tap t) into ring slot t; past the last block the
+    // offsets leave the range (zeros)
+    auto dma_filter = [&](int cb, int t, int i) {
+        const int ftoff = cb < nblk ? tap_flt(t) + cb * BK : a.flt_range;
+        load16_to_lds(flt_rsrc, ring_lds + t * B_BYTES + i * GB, b_off[i] + ftoff);
+    };
+    auto dma_piece = [&](int cb, int g) {  // footprint group g of block cb into buffer cb&1
+        const int coff = cb < nblk ? cb * BK : a.img_range;
+        load16_to_lds(img_rsrc, fbuf_lds + (cb & 1) * FBUF + g * GB, foff[g] + coff);
+    };
+
+    v16i acc[FM][FN];
+#pragma unroll
+    for (int x = 0; x < FM; ++x)
+#pragma unroll
+        for (int y = 0; y < FN; ++y)
+            acc[x][y] = v16i{};
+
+    v4i frag[2][KS][FM + FN];
+    auto read_one = [&](int buf, int t, int fb, int i) {
+        const int ks = i / (FM + FN), f = i % (FM + FN);
+        if (f < FM)
+            frag[buf][ks][f] = *(const v4i *)&fbuf[fb * FBUF + a_lane[f][ks] + tap_read(t)];
+        else
+            frag[buf][ks][f] = *(const v4i *)&ring[t * B_BYTES + b_lane[f - FM][ks]];
+    };
+    // MFMA q of a stage: k-step major, row blocks in order, column blocks
+    // snaking (consecutive MFMAs share one operand)
+    auto mfma_one = [&](int buf, int q) {
+        const int ks = q / (FM * FN), x = (q / FN) % FM, yy = q % FN;
+        const int y = (x & 1) ? FN - 1 - yy : yy;
+        acc[x][y] = PIX_J
+            ? __builtin_amdgcn_mfma_i32_32x32x32_i8(frag[buf][ks][FM + y], frag[buf][ks][x], acc[x][y], 0, 0, 0)
+            : __builtin_amdgcn_mfma_i32_32x32x32_i8(frag[buf][ks][x], frag[buf][ks][FM + y], acc[x][y], 0, 0, 0);
+    };
+
+    // ---- prologue: the filter of (0, 0), the footprint of block 0, the
+    // filters of (0, 1), (0, 2) and chunk 0 of block 1 (the other taps of
+    // block 0 go out during its first stages); then the addresses the LDS
+    // reads need, while the loads are in flight ------------------------------
+#pragma unroll
+    for (int i = 0; i < BL; ++i)
+        dma_filter(0, 0, i);
+#pragma unroll
+    for (int g = 0; g < NG; ++g)
+        dma_piece(0, g);
+#pragma unroll
+    for (int t = 1; t < 3; ++t)
+#pragma unroll
+        for (int i = 0; i < BL; ++i)
+            dma_filter(0, t, i);
+#pragma unroll
+    for (int g = chunk_lo<NG>(0); g < chunk_lo<NG>(1); ++g)
+        dma_piece(1, g);
+    if constexpr (!PIX_J) {
+        if (!a.pix_linear)
+            fill_out_rows<TM, 64 * NW>(a, m0, out_row);
+    }
+
+#pragma unroll
+    for (int x = 0; x < FM; ++x) {
+        const int m = m0 + wm + x * 32 + (lane & 31);
+        int idx = 0;
+        if (m < a.M) {
+            const int n = udiv(m, a.d_pq);
+            const int rem = m - n * a.PQ;
+            const int p = udiv(rem, a.d_q);
+            const int q = rem - p * a.Q;
+            idx = ((n - n_a) * a.Hp + p * a.strH - hp_a) * a.Pr + q * a.strW * 5;
+        }
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks)
+            a_lane[x][ks] = (idx + ks * 2 + (lane >> 5)) * 16;
+    }
+#pragma unroll
+    for (int y = 0; y < FN; ++y) {
+        const int row = wn + y * 32 + (lane & 31);
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks)
+            b_lane[y][ks] = row * BK + swizzle_chunk<64>(row, ks * 2 + (lane >> 5)) * 16;
+    }
+
+    wait_vm_lgkm0<2 * BL + chunk_lo<NG>(1)>();
+    __builtin_amdgcn_s_barrier();
+#pragma unroll
+    for (int i = 0; i < NRD; ++i)
+        read_one(0, 0, 0, i);
+
+    // ---- main loop ----------------------------------------------------------
+    // Stage (cb, t) runs MFMAs on fragments read during the previous stage,
+    // loads the filter of (cb+1, t) into slot t plus the footprint chunk that
+    // rides on tap t, and reads the fragments of the next stage.  Stage u =
+    // 9 cb + t keeps its fragments in buffer u & 1; blocks go in pairs so
+    // that buffer, footprint buffer and every wait count are compile-time.
+    auto run_block = [&](int cb, auto parc, auto firstc) {
+        constexpr int PAR = decltype(parc)::value;   // cb & 1
+        constexpr bool FIRST = decltype(firstc)::value;
+        static_for<0, kTaps>([&](auto tc) {
+            constexpr int t = decltype(tc)::value;
+            constexpr int buf = (t + PAR) & 1;
+            constexpr int rt = (t + 1) % kTaps;
+            constexpr int rfb = t == 8 ? PAR ^ 1 : PAR;
+            constexpr int ck = chunk_at(t);
+            constexpr int g0 = ck < 0 ? 0 : chunk_lo<NG>(ck);
+            constexpr int g1 = ck < 0 ? 0 : chunk_lo<NG>(ck + 1);
+            constexpr int XL = FIRST && t + 3 < kTaps ? BL : 0;   // block 0: the filter of (0, t+3)
+            constexpr int NL = XL + BL + (g1 - g0);
+            const int pcb = t == 8 ? cb + 2 : cb + 1;   // block of this tap's footprint chunk
+
+            wait_vm_lgkm0<FIRST ? allowed_first<NG, BL>(t) : allowed_at<NG, BL>(t)>();
+            __builtin_amdgcn_s_barrier();
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int q = 0; q < NMF; ++q) {
+                mfma_one(buf, q);
+                // the fragment reads of the next stage ride on the first half
+                // of the MFMAs, the loads on the second half
+                constexpr int H = NMF / 2;
+                if (q < H) {
+#pragma unroll
+                    for (int o = q * NRD / H; o < (q + 1) * NRD / H; ++o)
+                        read_one(buf ^ 1, rt, rfb, o);
+                } else {
+#pragma unroll
+                    for (int o = (q - H) * NL / (NMF - H); o < (q - H + 1) * NL / (NMF - H); ++o) {
+                        if (o < XL)
+                            dma_filter(0, t + 3, o);
+                        else if (o < XL + BL)
+                            dma_filter(cb + 1, t, o - XL);
+                        else
+                            dma_piece(pcb, g0 + (o - XL - BL));
+                    }
+                }
+                __builtin_amdgcn_sched_barrier(0);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+        });
+    };
+    using I0 = std::integral_constant<int, 0>;
+    using I1 = std::integral_constant<int, 1>;
+    using First = std::integral_constant<bool, true>;
+    using Steady = std::integral_constant<bool, false>;
+    if (nend > 0)
+        run_block(0, I0{}, First{});
+    int cb = 1;
+    for (; cb + 1 < nend; cb += 2) {
+        run_block(cb, I1{}, Steady{});
+        run_block(cb + 1, I0{}, Steady{});
+    }
+    if (cb < nend)
+        run_block(cb, I1{}, Steady{});
+
+    if (!tail) {
+        wait_vm_lgkm0<0>();
+        store_tile_any<FM, FN, PIX_J>(a, acc, m0, n0, wm, wn, lane, out_row);
+    } else {
+        // ---- last block, row block by row block --------------------------
+        // Steps s = x * 18 + (t * 2 + ks): row block x, tap t, k-step ks.
+        // Image fragments are read D steps ahead; the filter fragments of
+        // step (t, ks) are read during row block 0 and kept for the others.
+        // The stores of row block x-1 go out two per step of row block x.
+        const int fb = (nblk - 1) & 1;
+        if (nend == 0) {
+            // a single block: the main loop, which loads taps 3 .. 8 of block
+            // 0, did not run
+#pragma unroll
+            for (int t = 3; t < kTaps; ++t)
+#pragma unroll
+                for (int i = 0; i < BL; ++i)
+                    dma_filter(0, t, i);
+        }
+        wait_vm_lgkm0<0>();
+        __builtin_amdgcn_s_barrier();
+        constexpr int NSTEP = kTaps * KS;
+        constexpr int TOTAL = FM * NSTEP;
+        constexpr int D = 4;
+        constexpr int NAB = D + 1;   // the read D steps ahead must not land in the slot in use
+        v4i ab[NAB];
+        v4i bc[kTaps][KS][FN];
+        auto read_a = [&](int st2) {
+            const int x = st2 / NSTEP, r = st2 % NSTEP;
+            ab[st2 % NAB] = *(const v4i *)&fbuf[fb * FBUF + a_lane[x][r % KS] + tap_read(r / KS)];
+        };
+        auto read_b = [&](int r) {
+#pragma unroll
+            for (int y = 0; y < FN; ++y)
+                bc[r / KS][r % KS][y] = *(const v4i *)&ring[(r / KS) * B_BYTES + b_lane[y][r % KS]];
+        };
+        // Store of element (y, v) of row block x.  MODE 0: lanes walk
+        // channels, equally spaced pixels; MODE 1: lanes walk channels, pixel
+        // offsets from the table; MODE 2: lanes walk pixels.
+        auto store_one = [&](auto modec, int x, int y, int v, int value) {
+            constexpr int MODE = decltype(modec)::value;
+            const __amdgpu_buffer_rsrc_t out_rsrc =
+                __builtin_amdgcn_make_buffer_rsrc((void *)a.out, (short)0, a.out_range, kRsrcWord3);
+            int off;
+            if constexpr (MODE == 2) {
+                const int m = m0 + wm + x * 32 + (lane & 31);
+                const int kk = n0 + wn + y * 32 + 4 * (lane >> 5) + 8 * (v >> 2) + (v & 3);
+                const int n = udiv(m, a.d_pq);
+                const int rem = m - n * a.PQ;
+                const int p = udiv(rem, a.d_q);
+                const int q = rem - p * a.Q;
+                off = (m < a.M && kk < a.K) ? (n * a.oN + p * a.oP + q * a.oQ + a.out0 + kk * a.oK) * 4 : kOutOfRange;
+            } else {
+                const int kk = n0 + wn + y * 32 + (lane & 31);
+                const int r = wm + x * 32 + 4 * (lane >> 5) + 8 * (v >> 2) + (v & 3);
+                if constexpr (MODE == 0) {
+                    const int m = m0 + r;
+                    off = (kk < a.K && m < a.M) ? (m * a.pix_stride + kk * a.oK) * 4 : kOutOfRange;
+                } else {
+                    const int po = out_row[r];
+                    off = (kk < a.K && po >= 0) ? (po + kk * a.oK) * 4 : kOutOfRange;
+                }
+            }
+            __builtin_amdgcn_raw_buffer_store_b32(value, out_rsrc, off, 0, kOutStoreStream);
+        };
+        // MODE 3: requantised INT8 output, each row block through the
+        // ordinary epilogue once it is done
+        auto run_tail = [&](auto modec) {
+            constexpr int MODE = decltype(modec)::value;
+#pragma unroll
+            for (int s2 = 0; s2 < D; ++s2) {
+                read_a(s2);
+                read_b(s2);
+            }
+            static_for<0, TOTAL>([&](auto sc) {
+                constexpr int st = decltype(sc)::value;
+                constexpr int x = st / NSTEP, r = st % NSTEP;
+                constexpr int t = r / KS, ks = r % KS;
+                if constexpr (st + D < TOTAL) {
+                    read_a(st + D);
+                    if constexpr (st + D < NSTEP)
+                        read_b(st + D);
+                }
+#pragma unroll
+                for (int yy = 0; yy < FN; ++yy) {
+                    const int y = (r & 1) ? FN - 1 - yy : yy;
+                    acc[x][y] = PIX_J
+                        ? __builtin_amdgcn_mfma_i32_32x32x32_i8(bc[t][ks][y], ab[st % NAB], acc[x][y], 0, 0, 0)
+                        : __builtin_amdgcn_mfma_i32_32x32x32_i8(ab[st % NAB], bc[t][ks][y], acc[x][y], 0, 0, 0);
+                }
+                if constexpr (MODE < 3) {
+                    // stores of the previous row block: 16 * FN values over 18 steps
+                    if constexpr (x >= 1) {
+                        constexpr int NV = 16 * FN;
+                        constexpr int lo = r * NV / NSTEP, hi = (r + 1) * NV / NSTEP;
+#pragma unroll
+                        for (int e = lo; e < hi; ++e)
+                            store_one(modec, x - 1, e / 16, e % 16, acc[x - 1][e / 16][e % 16]);
+                    }
+                } else if constexpr (r == NSTEP - 1) {
+                    v16i row[1][FN];
+#pragma unroll
+                    for (int y = 0; y < FN; ++y)
+                        row[0][y] = acc[x][y];
+                    store_tile_any<1, FN, PIX_J>(a, row, m0, n0, wm + x * 32, wn, lane, out_row);
+                }
+            });
+            if constexpr (MODE < 3) {
+#pragma unroll
+                for (int e = 0; e < 16 * FN; ++e)
+                    store_one(modec, FM - 1, e / 16, e % 16, acc[FM - 1][e / 16][e % 16]);
+            }
+        };
+        if (a.q8)
+            run_tail(std::integral_constant<int, 3>{});
+        else if (PIX_J)
+            run_tail(std::integral_constant<int, 2>{});
+        else if (a.pix_linear)
+            run_tail(std::integral_constant<int, 0>{});
+        else
+            run_tail(std::integral_constant<int, 1>{});
+    }
+}
+
+
+
 
 }  // namespace convi8

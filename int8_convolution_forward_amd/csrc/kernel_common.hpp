@@ -67,6 +67,7 @@ struct IgemmArgs {
     int tiles_n;         // column tiles
     int tiles;           // total tiles
     Divisor d_pq, d_q;   // division by P*Q and by Q (pixel index -> n, p, q)
+    Divisor d_tn;        // division by tiles_n (tile index -> row tile, column tile)
     // footprint kernel only
     int Hp;              // padded image height H + pre_h + post_h
     int Wf;              // footprint width (Q-1)*stride_w + (S-1)*dil_w + 1
@@ -202,9 +203,11 @@ __device__ __forceinline__ int fdiv(int n, int d, float inv)
 // rows a run reads stay in that XCD's L2.
 __device__ __forceinline__ int xcd_tile(int bid, int tiles)
 {
+    // XCDs below rem hold per + 1 tiles, the others per (no branch, so the
+    // kernel's argument loads are not held back behind it)
     const int per = tiles >> 3, rem = tiles & 7;
     const int xcd = bid & 7, idx = bid >> 3;
-    return xcd < rem ? xcd * (per + 1) + idx : rem * (per + 1) + (xcd - rem) * per + idx;
+    return xcd * per + min(xcd, rem) + idx;
 }
 
 // Output-row offsets (elements) of the tile's TM pixels, or -1 past M, for

@@ -132,8 +132,8 @@ def test_repeat_runs_identical(ci8):
 # ---------------------------------------------------------------------------
 TILES = ["64x64x64", "128x64x64", "64x128x64", "128x128x64", "128x128x128", "256x128x64",
          "128x256x64", "w256x128x64", "w128x128x64", "w256x128x128", "w128x192x128", "f256x128", "fw256x128",
-         "f128x128", "fk256x128", "fk128x128"]
-FOOTPRINT_TILES = [t for t in TILES if t.startswith("f")]
+         "f128x128", "fk256x128", "fk128x128", "r256x128", "t256x128", "t128x128"]
+FOOTPRINT_TILES = [t for t in TILES if t[0] in "frt"]
 
 
 @pytest.mark.parametrize("tile", TILES)
