@@ -477,11 +477,10 @@ constexpr int allowed_first(int t)
 
 // 3x3 footprint kernel with a nine-slot filter ring (one slot per tap) and a
 // per-block loop.  With TAIL, the last 64-channel block runs row block by row
-// block: every filter fragment of that block is read once into registers,
-// then for each 32-row block x of the wave tile the nine taps' image
-// fragments are multiplied and row block x is stored at once, so its INT32
-// stores drain while the MFMAs of the next row blocks run (instead of the
-// whole tile's stores after the last MFMA).  Four waves, 2 x 2 (WGM x WGN).
+// block: each row block of the wave tile (64 rows when the wave has 128)
+// goes through all nine taps, and its INT32 stores drain while the MFMAs of
+// the next row block run (instead of the whole tile's stores after the last
+// MFMA).  Four waves, 2 x 2 (WGM x WGN).
 template <int TM, int TN, int FPIX, int WGM, int WGN, bool PIX_J, bool TAIL>
 __global__ __launch_bounds__(64 * WGM * WGN) void conv_fp3x3_ring9_kernel(IgemmArgs a)
 {
@@ -530,32 +529,6 @@ __global__ __launch_bounds__(64 * WGM * WGN) void conv_fp3x3_ring9_kernel(IgemmA
     const int wm = (wave / WGN) * WM;
     const int wn = (wave % WGN) * WN;
 
-    // ---- footprint geometry of this tile (uniform) ------------------------
-    const int m_last = min(m0 + TM, a.M) - 1;
-    const int n_a = udiv(m0, a.d_pq);
-    const int p_a = udiv(m0 - n_a * a.PQ, a.d_q);
-    const int hp_a = p_a * a.strH;
-    const int n_b = udiv(m_last, a.d_pq);
-    const int p_b = udiv(m_last - n_b * a.PQ, a.d_q);
-    const int frows = (n_b - n_a) * a.Hp + p_b * a.strH + 2 * a.dilH - hp_a + 1;
-
-    int foff[NG];
-#pragma unroll
-    for (int g = 0; g < NG; ++g) {
-        const int slot = g * (GB / 16) + wave * 64 + lane;
-        const int fr = fdiv(slot, a.Pr, a.inv_pr);
-        const int rem = slot - fr * a.Pr;
-        const int fc = rem / 5;
-        const int j = rem - fc * 5;
-        const int hr = hp_a + fr;
-        const int dn = fdiv(hr, a.Hp, a.inv_hp);
-        const int h = hr - dn * a.Hp - a.padH;
-        const int w = fc - a.padW;
-        const bool ok = (j < 4) & (fc < a.Wf) & (fr < frows) & ((unsigned)h < (unsigned)a.H) &
-                        ((unsigned)w < (unsigned)a.W);
-        foff[g] = ok ? (n_a + dn) * a.sN + h * a.sH + w * a.sW + j * 16 : kOutOfRange;
-    }
-
     const int row0 = wave * 16 + (lane >> 2);
     const int jb = swizzle_chunk<64>(row0, lane & 3);
     int b_off[BL];
@@ -572,7 +545,9 @@ __global__ __launch_bounds__(64 * WGM * WGN) void conv_fp3x3_ring9_kernel(IgemmA
     const unsigned ring_lds = lds_address(ring) + wave * 1024;
     const unsigned fbuf_lds = lds_address(fbuf) + wave * 1024;
     const int nblk = a.ncblk;
-    const bool tail = TAIL && nblk > 0;
+    // the requantising epilogue keeps the plain order (its stores are a
+    // quarter of the bytes)
+    const bool tail = TAIL && nblk > 0 && !a.q8;
     const int nend = tail ? nblk - 1 : nblk;   // blocks run by the main loop
 
     auto tap_read = [&](int t) { return ((t / 3) * a.dilH * a.Pr + (t % 3) * a.dilW * 5) * 16; };
@@ -583,10 +558,62 @@ __global__ __launch_bounds__(64 * WGM * WGN) void conv_fp3x3_ring9_kernel(IgemmA
         const int ftoff = cb < nblk ? tap_flt(t) + cb * BK : a.flt_range;
         load16_to_lds(flt_rsrc, ring_lds + t * B_BYTES + i * GB, b_off[i] + ftoff);
     };
+    int foff[NG];
     auto dma_piece = [&](int cb, int g) {  // footprint group g of block cb into buffer cb&1
         const int coff = cb < nblk ? cb * BK : a.img_range;
         load16_to_lds(img_rsrc, fbuf_lds + (cb & 1) * FBUF + g * GB, foff[g] + coff);
     };
+
+    // ---- prologue: the filter of (0, 0) goes out first (its offsets are
+    // ready); then the footprint of block 0, each group as soon as its
+    // offsets are known, so that the address arithmetic overlaps the loads;
+    // then the filters of (0, 1), (0, 2) and chunk 0 of block 1 (the other
+    // taps of block 0 go out during its first stages); then the addresses
+    // the LDS reads need, while the loads are in flight
+#pragma unroll
+    for (int i = 0; i < BL; ++i)
+        dma_filter(0, 0, i);
+
+    // footprint geometry of this tile (uniform)
+    const int m_last = min(m0 + TM, a.M) - 1;
+    const int n_a = udiv(m0, a.d_pq);
+    const int p_a = udiv(m0 - n_a * a.PQ, a.d_q);
+    const int hp_a = p_a * a.strH;
+    const int n_b = udiv(m_last, a.d_pq);
+    const int p_b = udiv(m_last - n_b * a.PQ, a.d_q);
+    const int frows = (n_b - n_a) * a.Hp + p_b * a.strH + 2 * a.dilH - hp_a + 1;
+    // Slot (16 bytes) s of the footprint is footprint row fr = s / Pr, pixel
+    // column fc and 16-byte piece j of that row; footprint row fr is padded
+    // row hr = hp_a + fr counted from image n_a, i.e. row h of image n_a + dn
+    // with hr = dn * Hp + h + padH.  Its bytes start at
+    //   (n_a + dn) sN + h sH + (fc - padW) sW + 16 j
+    //   = base + dn (sN - Hp sH) + fr sH + fc sW + 16 j
+    // with the uniform base = n_a sN + (hp_a - padH) sH - padW sW.  The
+    // planner keeps sH, sW, the footprint's rows and columns (below 2^20)
+    // and, when a launch holds several images, sN - Hp sH within 23 bits (dn
+    // is 0 otherwise), so the products are 24-bit multiplies.
+    const int fbase = n_a * a.sN + (hp_a - a.padH) * a.sH - a.padW * a.sW;
+    const int fE = a.sN - a.Hp * a.sH;
+#pragma unroll
+    for (int g = 0; g < NG; ++g) {
+        const int slot = g * (GB / 16) + wave * 64 + lane;
+        const int fr = fdiv(slot, a.Pr, a.inv_pr);
+        const int rem = slot - __mul24(fr, a.Pr);
+        const int fc = (int)(__umul24((unsigned)rem, 52429u) >> 18);   // rem / 5 (rem < 2^16)
+        const int j = rem - fc * 5;
+        const int hr = hp_a + fr;
+        const int dn = fdiv(hr, a.Hp, a.inv_hp);
+        const int h = hr - __mul24(dn, a.Hp) - a.padH;
+        const int w = fc - a.padW;
+        // slots past the footprint's rows, the fifth piece of a pixel and
+        // the row padding are never read: they are skipped (or filled with
+        // whatever lies there); rows and columns outside the image read
+        // zeros
+        const bool ok = (j < 4) & (fr < frows) & ((unsigned)h < (unsigned)a.H) & ((unsigned)w < (unsigned)a.W);
+        foff[g] = ok ? fbase + __mul24(dn, fE) + __mul24(fr, a.sH) + __mul24(fc, a.sW) + j * 16 : kOutOfRange;
+        dma_piece(0, g);
+        __builtin_amdgcn_sched_barrier(0);
+    }
 
     v16i acc[FM][FN];
 #pragma unroll
@@ -613,16 +640,6 @@ __global__ __launch_bounds__(64 * WGM * WGN) void conv_fp3x3_ring9_kernel(IgemmA
             : __builtin_amdgcn_mfma_i32_32x32x32_i8(frag[buf][ks][x], frag[buf][ks][FM + y], acc[x][y], 0, 0, 0);
     };
 
-    // ---- prologue: the filter of (0, 0), the footprint of block 0, the
-    // filters of (0, 1), (0, 2) and chunk 0 of block 1 (the other taps of
-    // block 0 go out during its first stages); then the addresses the LDS
-    // reads need, while the loads are in flight ------------------------------
-#pragma unroll
-    for (int i = 0; i < BL; ++i)
-        dma_filter(0, 0, i);
-#pragma unroll
-    for (int g = 0; g < NG; ++g)
-        dma_piece(0, g);
 #pragma unroll
     for (int t = 1; t < 3; ++t)
 #pragma unroll
@@ -734,10 +751,14 @@ __global__ __launch_bounds__(64 * WGM * WGN) void conv_fp3x3_ring9_kernel(IgemmA
         store_tile_any<FM, FN, PIX_J>(a, acc, m0, n0, wm, wn, lane, out_row);
     } else {
         // ---- last block, row block by row block --------------------------
-        // Steps s = x * 18 + (t * 2 + ks): row block x, tap t, k-step ks.
-        // Image fragments are read D steps ahead; the filter fragments of
-        // step (t, ks) are read during row block 0 and kept for the others.
-        // The stores of row block x-1 go out two per step of row block x.
+        // A row block is RBX 32-row fragments of the wave's rows (two when the
+        // wave has four or more: each step then reads two image and FN filter
+        // fragments for 2 * FN products, which keeps the LDS read rate under
+        // what the CU serves).  Steps s = x * 18 + (t * 2 + ks): row block x,
+        // tap t, k-step ks.  The image and filter fragments of step s+D are
+        // read during step s (all nine taps of the block are in the ring).
+        // The stores of row block x-1 go out spread over the steps of row
+        // block x.
         const int fb = (nblk - 1) & 1;
         if (nend == 0) {
             // a single block: the main loop, which loads taps 3 .. 8 of block
@@ -750,103 +771,137 @@ __global__ __launch_bounds__(64 * WGM * WGN) void conv_fp3x3_ring9_kernel(IgemmA
         }
         wait_vm_lgkm0<0>();
         __builtin_amdgcn_s_barrier();
+        constexpr int RBX = FM >= 4 ? 2 : 1;
+        constexpr int NRB = FM / RBX;
         constexpr int NSTEP = kTaps * KS;
-        constexpr int TOTAL = FM * NSTEP;
-        constexpr int D = 4;
-        constexpr int NAB = D + 1;   // the read D steps ahead must not land in the slot in use
-        v4i ab[NAB];
-        v4i bc[kTaps][KS][FN];
-        auto read_a = [&](int st2) {
-            const int x = st2 / NSTEP, r = st2 % NSTEP;
-            ab[st2 % NAB] = *(const v4i *)&fbuf[fb * FBUF + a_lane[x][r % KS] + tap_read(r / KS)];
-        };
-        auto read_b = [&](int r) {
+        constexpr int TOTAL = NRB * NSTEP;
+        constexpr int D = RBX == 1 ? 3 : 2;
+        constexpr int NR = D + 1;   // the reads D steps ahead must not land in the slot in use
+        v4i ab[NR][RBX];
+        v4i bb[NR][FN];
+        auto read_step = [&](int s2) {
+            const int x = s2 / NSTEP, r = s2 % NSTEP;
+            const int t = r / KS, ks = r % KS;
+#pragma unroll
+            for (int i = 0; i < RBX; ++i)
+                ab[s2 % NR][i] = *(const v4i *)&fbuf[fb * FBUF + a_lane[x * RBX + i][ks] + tap_read(t)];
 #pragma unroll
             for (int y = 0; y < FN; ++y)
-                bc[r / KS][r % KS][y] = *(const v4i *)&ring[(r / KS) * B_BYTES + b_lane[y][r % KS]];
+                bb[s2 % NR][y] = *(const v4i *)&ring[t * B_BYTES + b_lane[y][ks]];
         };
-        // Store of element (y, v) of row block x.  MODE 0: lanes walk
-        // channels, equally spaced pixels; MODE 1: lanes walk channels, pixel
-        // offsets from the table; MODE 2: lanes walk pixels.
-        auto store_one = [&](auto modec, int x, int y, int v, int value) {
-            constexpr int MODE = decltype(modec)::value;
-            const __amdgpu_buffer_rsrc_t out_rsrc =
-                __builtin_amdgcn_make_buffer_rsrc((void *)a.out, (short)0, a.out_range, kRsrcWord3);
-            int off;
-            if constexpr (MODE == 2) {
+        const __amdgpu_buffer_rsrc_t out_rsrc =
+            __builtin_amdgcn_make_buffer_rsrc((void *)a.out, (short)0, a.out_range, kRsrcWord3);
+        // MODE 0: lanes walk channels, equally spaced pixels, every row of the
+        // tile inside the problem: a lane base plus a uniform offset per store.
+        // MODE 1: lanes walk channels, pixel offsets from the table (or rows
+        // past the problem).  MODE 2: lanes walk pixels.
+        const int kk0 = n0 + wn + (lane & 31);
+        const int mrow0 = wm + 4 * (lane >> 5);
+        // MODE 0 lane bases, computed once (the opaque asm keeps the compiler
+        // from recomputing them at every store)
+        int obase[FN];
+#pragma unroll
+        for (int y = 0; y < FN; ++y) {
+            const int kk = kk0 + y * 32;
+            obase[y] = kk < a.K ? ((m0 + mrow0) * a.pix_stride + kk * a.oK) * 4 : kOutOfRange;
+            asm volatile("" : "+v"(obase[y]));
+        }
+        // MODE 2 (lanes walk pixels): each lane's pixel offset per row block,
+        // or -1 past the problem
+        int pixo[PIX_J ? FM : 1];
+        if constexpr (PIX_J) {
+#pragma unroll
+            for (int x = 0; x < FM; ++x) {
                 const int m = m0 + wm + x * 32 + (lane & 31);
-                const int kk = n0 + wn + y * 32 + 4 * (lane >> 5) + 8 * (v >> 2) + (v & 3);
                 const int n = udiv(m, a.d_pq);
                 const int rem = m - n * a.PQ;
                 const int p = udiv(rem, a.d_q);
                 const int q = rem - p * a.Q;
-                off = (m < a.M && kk < a.K) ? (n * a.oN + p * a.oP + q * a.oQ + a.out0 + kk * a.oK) * 4 : kOutOfRange;
-            } else {
-                const int kk = n0 + wn + y * 32 + (lane & 31);
-                const int r = wm + x * 32 + 4 * (lane >> 5) + 8 * (v >> 2) + (v & 3);
-                if constexpr (MODE == 0) {
+                pixo[x] = m < a.M ? n * a.oN + p * a.oP + q * a.oQ + a.out0 : -1;
+                asm volatile("" : "+v"(pixo[x]));
+            }
+        }
+        auto store_one = [&](auto modec, int x, int y, int v, int value) {
+            constexpr int MODE = decltype(modec)::value;
+            const int rv = 8 * (v >> 2) + (v & 3);   // row of value v within its 32-row block
+            if constexpr (MODE == 0) {
+                __builtin_amdgcn_raw_buffer_store_b32(value, out_rsrc, obase[y], (x * 32 + rv) * a.pix_stride * 4,
+                                                      kOutStoreStream);
+            } else if constexpr (MODE == 1) {
+                const int kk = kk0 + y * 32;
+                const int r = mrow0 + x * 32 + rv;
+                int off = kOutOfRange;
+                if (a.pix_linear) {
                     const int m = m0 + r;
                     off = (kk < a.K && m < a.M) ? (m * a.pix_stride + kk * a.oK) * 4 : kOutOfRange;
                 } else {
                     const int po = out_row[r];
                     off = (kk < a.K && po >= 0) ? (po + kk * a.oK) * 4 : kOutOfRange;
                 }
+                __builtin_amdgcn_raw_buffer_store_b32(value, out_rsrc, off, 0, kOutStoreStream);
+            } else {
+                const int kk = n0 + wn + y * 32 + 4 * (lane >> 5) + rv;
+                const int off = (pixo[x] >= 0 && kk < a.K) ? (pixo[x] + kk * a.oK) * 4 : kOutOfRange;
+                __builtin_amdgcn_raw_buffer_store_b32(value, out_rsrc, off, 0, kOutStoreStream);
             }
-            __builtin_amdgcn_raw_buffer_store_b32(value, out_rsrc, off, 0, kOutStoreStream);
         };
-        // MODE 3: requantised INT8 output, each row block through the
-        // ordinary epilogue once it is done
+        // With one fragment per row block, odd steps accumulate into a second
+        // set (added in at the end of the row block): the row block has only
+        // FN accumulators, and alternating two sets keeps dependent MFMAs
+        // 2 * FN issues apart.
+        v16i acc2[FN];
         auto run_tail = [&](auto modec) {
-            constexpr int MODE = decltype(modec)::value;
 #pragma unroll
-            for (int s2 = 0; s2 < D; ++s2) {
-                read_a(s2);
-                read_b(s2);
-            }
+            for (int s2 = 0; s2 < D; ++s2)
+                read_step(s2);
             static_for<0, TOTAL>([&](auto sc) {
                 constexpr int st = decltype(sc)::value;
                 constexpr int x = st / NSTEP, r = st % NSTEP;
-                constexpr int t = r / KS, ks = r % KS;
-                if constexpr (st + D < TOTAL) {
-                    read_a(st + D);
-                    if constexpr (st + D < NSTEP)
-                        read_b(st + D);
-                }
+                if constexpr (st + D < TOTAL)
+                    read_step(st + D);
 #pragma unroll
-                for (int yy = 0; yy < FN; ++yy) {
-                    const int y = (r & 1) ? FN - 1 - yy : yy;
-                    acc[x][y] = PIX_J
-                        ? __builtin_amdgcn_mfma_i32_32x32x32_i8(bc[t][ks][y], ab[st % NAB], acc[x][y], 0, 0, 0)
-                        : __builtin_amdgcn_mfma_i32_32x32x32_i8(ab[st % NAB], bc[t][ks][y], acc[x][y], 0, 0, 0);
-                }
-                if constexpr (MODE < 3) {
-                    // stores of the previous row block: 16 * FN values over 18 steps
-                    if constexpr (x >= 1) {
-                        constexpr int NV = 16 * FN;
-                        constexpr int lo = r * NV / NSTEP, hi = (r + 1) * NV / NSTEP;
+                for (int i = 0; i < RBX; ++i)
 #pragma unroll
-                        for (int e = lo; e < hi; ++e)
-                            store_one(modec, x - 1, e / 16, e % 16, acc[x - 1][e / 16][e % 16]);
+                    for (int y = 0; y < FN; ++y) {
+                        const v4i &fa = ab[st % NR][i];
+                        const v4i &fbm = bb[st % NR][y];
+                        v16i &c0 = acc[x * RBX + i][y];
+                        if constexpr (RBX > 1 || r % 2 == 0) {
+                            c0 = PIX_J ? __builtin_amdgcn_mfma_i32_32x32x32_i8(fbm, fa, c0, 0, 0, 0)
+                                       : __builtin_amdgcn_mfma_i32_32x32x32_i8(fa, fbm, c0, 0, 0, 0);
+                        } else {
+                            const v16i c = r == 1 ? v16i{} : acc2[y];
+                            acc2[y] = PIX_J ? __builtin_amdgcn_mfma_i32_32x32x32_i8(fbm, fa, c, 0, 0, 0)
+                                            : __builtin_amdgcn_mfma_i32_32x32x32_i8(fa, fbm, c, 0, 0, 0);
+                        }
                     }
-                } else if constexpr (r == NSTEP - 1) {
-                    v16i row[1][FN];
+                if constexpr (RBX == 1 && r == NSTEP - 1) {
 #pragma unroll
                     for (int y = 0; y < FN; ++y)
-                        row[0][y] = acc[x][y];
-                    store_tile_any<1, FN, PIX_J>(a, row, m0, n0, wm + x * 32, wn, lane, out_row);
+                        acc[x][y] += acc2[y];
                 }
-            });
-            if constexpr (MODE < 3) {
+                // stores of the previous row block: 16 * FN * RBX values over
+                // 18 steps
+                if constexpr (x >= 1) {
+                    constexpr int NV = 16 * FN * RBX;
+                    constexpr int lo = r * NV / NSTEP, hi = (r + 1) * NV / NSTEP;
 #pragma unroll
-                for (int e = 0; e < 16 * FN; ++e)
-                    store_one(modec, FM - 1, e / 16, e % 16, acc[FM - 1][e / 16][e % 16]);
+                    for (int e = lo; e < hi; ++e) {
+                        const int f = (x - 1) * RBX + e / (16 * FN), y = e / 16 % FN;
+                        store_one(modec, f, y, e % 16, acc[f][y][e % 16]);
+                    }
+                }
+                __builtin_amdgcn_sched_barrier(0);
+            });
+#pragma unroll
+            for (int e = 0; e < 16 * FN * RBX; ++e) {
+                const int f = (NRB - 1) * RBX + e / (16 * FN), y = e / 16 % FN;
+                store_one(modec, f, y, e % 16, acc[f][y][e % 16]);
             }
         };
-        if (a.q8)
-            run_tail(std::integral_constant<int, 3>{});
-        else if (PIX_J)
+        if (PIX_J)
             run_tail(std::integral_constant<int, 2>{});
-        else if (a.pix_linear)
+        else if (a.pix_linear && m0 + TM <= a.M)
             run_tail(std::integral_constant<int, 0>{});
         else
             run_tail(std::integral_constant<int, 1>{});
