@@ -10,7 +10,10 @@ Cache cannot serve a step from a previous one.
 
 Prints one JSON line: the metric (TOPS = 2*N*K*P*Q*C*R*S / s), ms per step,
 the roofline of the implicit-GEMM kernel timed alone with HIP events on the
-launch stream, and the CPU oracle timed on the host as a baseline.
+launch stream, and the CPU oracle timed on the host as a baseline.  Each GPU
+figure is the median of five timed batches of ``--steps`` steps (every batch
+between two device synchronisations, its events on the launch stream); the
+five batch times are reported beside it.
 """
 from __future__ import annotations
 
@@ -29,6 +32,69 @@ METRIC = "INT8 conv_fprop TOPS (2·NKPQ·CRS/s) and % of MI355X INT8 MFMA peak"
 INT8_PEAK_TOPS = 5000.0     # MI355X dense int8 MFMA, published
 HBM_PEAK_GBS = 8000.0       # MI355X HBM3E, published
 DEFAULT_WORKLOAD = "large_channel_n64_c512_14"
+TIMED_BATCHES = 5
+# kernel names as the profiler lists them, by plan tile
+RING9_TILES = ("r256x128", "t256x128", "t128x128")
+
+
+def timed_batches(run, stream, steps):
+    """ms per step of TIMED_BATCHES batches, each of `steps` steps run by
+    run(), timed with events on the launch stream between device
+    synchronisations."""
+    import torch
+
+    out = []
+    for _ in range(TIMED_BATCHES):
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        run()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        out.append(e0.elapsed_time(e1) / steps)
+    return out
+
+
+def median(v):
+    v = sorted(v)
+    n = len(v)
+    return v[n // 2] if n % 2 else 0.5 * (v[n // 2 - 1] + v[n // 2])
+
+
+def host_description(orc):
+    """nproc, the CPU model and the oracle's thread count."""
+    model = None
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    try:
+        usable = len(os.sched_getaffinity(0))
+    except AttributeError:
+        usable = os.cpu_count()
+    return {"nproc": os.cpu_count(), "usable_cpus": usable, "cpu_model": model,
+            "oracle_threads": orc.max_threads()}
+
+
+def single_core_small_configs(orc):
+    """The oracle on one thread over the two smallest workloads (the tiny
+    5x5 and the stride-2 downsample layer), whole problem once each."""
+    import workloads as wl
+
+    res = {}
+    for name in ("tiny_5x5_r3", "downsample_s2_n8_c64_56"):
+        c = wl.case(name)
+        d = wl.make_inputs(c, c.seed_base)
+        t0 = time.perf_counter()
+        orc.conv_fprop(d["x"], d["w"], c.pre, c.post, c.stride, c.dilation, threads=1)
+        el = time.perf_counter() - t0
+        res[name] = {"seconds": el, "GOPS": c.ops / el / 1e9}
+    return res
 
 
 def parse():
@@ -150,14 +216,13 @@ def bench_grad(args, c):
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
-    t0 = torch.cuda.Event(enable_timing=True)
-    t1 = torch.cuda.Event(enable_timing=True)
-    t0.record(stream)
-    for i in range(args.steps):
-        step(i)
-    t1.record(stream)
-    torch.cuda.synchronize()
-    ms = t0.elapsed_time(t1) / args.steps
+
+    def run():
+        for i in range(args.steps):
+            step(i)
+
+    batches = timed_batches(run, stream, args.steps)
+    ms = median(batches)
     tops = ops / (ms * 1e-3) / 1e12
     alg_bytes = (N * K * P * Q + N * C * H * W + 4 * K * C * R * S) if wg else \
         (N * K * P * Q + K * C * R * S + 4 * N * C * H * W)
@@ -172,6 +237,7 @@ def bench_grad(args, c):
                             "kernel)") if wg else
                            "whole dgrad call (filter repack + one forward kernel per stride phase)",
                  "kernel_avg_us": ms * 1e3, "kernel_only_launch": False,
+                 "timed_batches_ms_per_step": batches,
                  "algorithmic_bytes": alg_bytes, "algorithmic_ops": ops})
     cpu = None
     if not args.no_cpu_baseline:
@@ -194,10 +260,12 @@ def bench_grad(args, c):
                 break
         cpu = {"value": ops * reps / el / 1e12, "unit": "TOPS", "cores": threads, "kind": "oracle",
                "sample": f"the whole {args.op} of {c.name}, {reps} run(s), {el:.1f} s wall, "
-                         f"{threads} OpenMP threads"}
+                         f"{threads} OpenMP threads",
+               "host": host_description(orc)}
     out = {
         "metric": METRIC, "value": tops, "unit": "TOPS", "n_gpus": 1, "steps": args.steps,
-        "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True, "scaling": "weak",
+        "warmup": args.warmup, "ms_per_step": ms, "timed_batches_ms_per_step": batches,
+        "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": "int8", "data": "synthetic",
         "config": {"workload": c.name, "op": args.op, "mode": args.mode,
                    "loss": list(c.out.dims), "loss_strides": list(c.out.strides),
@@ -303,9 +371,7 @@ def main():
         step(i)
     torch.cuda.synchronize()
 
-    # ---- timed region: exactly `steps` steps ---------------------------
-    t_start = torch.cuda.Event(enable_timing=True)
-    t_end = torch.cuda.Event(enable_timing=True)
+    # ---- timed region: exactly `steps` steps per batch ------------------
     if args.graph:
         # the same calls, recorded on the capture stream, replayed as one graph
         graph = torch.cuda.CUDAGraph()
@@ -319,15 +385,16 @@ def main():
         graph.replay()
         torch.cuda.synchronize()
     torch.cuda.synchronize()
-    t_start.record(stream)
-    if args.graph:
-        graph.replay()
-    else:
-        for i in range(args.steps):
-            step(i)
-    t_end.record(stream)
-    torch.cuda.synchronize()
-    ms_per_step = t_start.elapsed_time(t_end) / args.steps
+
+    def run():
+        if args.graph:
+            graph.replay()
+        else:
+            for i in range(args.steps):
+                step(i)
+
+    batches = timed_batches(run, stream, args.steps)
+    ms_per_step = median(batches)
     tops = ops / (ms_per_step * 1e-3) / 1e12
     print(f"bench: {ms_per_step * 1e3:.2f} us/step, {tops:.1f} TOPS", file=sys.stderr, flush=True)
 
@@ -353,16 +420,15 @@ def main():
     for i in range(min(10, nk)):
         fn(*kpre[i % nsets])
     torch.cuda.synchronize()
-    k_start = torch.cuda.Event(enable_timing=True)
-    k_end = torch.cuda.Event(enable_timing=True)
-    k_start.record(stream)
-    for i in range(nk):
-        rc = fn(*kpre[i % nsets])
-        if rc:
-            raise RuntimeError(ci8.status_string(rc))
-    k_end.record(stream)
-    torch.cuda.synchronize()
-    k_avg_ms = k_start.elapsed_time(k_end) / nk
+
+    def krun():
+        for i in range(nk):
+            rc = fn(*kpre[i % nsets])
+            if rc:
+                raise RuntimeError(ci8.status_string(rc))
+
+    kbatches = timed_batches(krun, stream, nk)
+    k_avg_ms = median(kbatches)
 
     # algorithmic bytes: image, filter read once, output written once (int32,
     # or int8 plus the per-channel scale and bias)
@@ -379,9 +445,17 @@ def main():
                 "unit": "GB/s"}
     roof["frac"] = roof["achieved"] / roof["peak"]
     roof["traffic"] = traffic_from_profiles(c.name + ("_requant" if rq_on else ""), alg_bytes)
-    roof["kernel"] = "conv_footprint3x3_kernel" if kf.get("kernel") == "footprint" else "conv_igemm_kernel"
+    if kf.get("tile") in RING9_TILES:
+        roof["kernel"] = "conv_fp3x3_ring9_kernel"
+    elif kf.get("kernel") == "footprint":
+        roof["kernel"] = "conv_footprint3x3_kernel"
+    elif kf.get("kernel") == "pointwise":
+        roof["kernel"] = "conv_pointwise_kernel"
+    else:
+        roof["kernel"] = "conv_igemm_kernel"
     roof["kernel_tile"] = kf.get("tile")
     roof["kernel_avg_us"] = k_avg_ms * 1e3
+    roof["kernel_timed_batches_us"] = [v * 1e3 for v in kbatches]
     roof["kernel_launches_timed"] = nk
     roof["kernel_only_launch"] = kernel_only
     roof["algorithmic_bytes"] = alg_bytes
@@ -410,7 +484,9 @@ def main():
                 break
         cpu = {"value": ops * reps / el / 1e12, "unit": "TOPS", "cores": threads, "kind": "oracle",
                "sample": f"the whole {c.name} workload, {reps} run(s), {el:.1f} s wall, "
-                         f"{threads} OpenMP threads, plain -O2 C with int64 sums"}
+                         f"{threads} OpenMP threads, plain -O2 C with int64 sums",
+               "host": host_description(orc),
+               "single_core": single_core_small_configs(orc)}
 
     out = {
         "metric": METRIC,
@@ -420,6 +496,7 @@ def main():
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": ms_per_step,
+        "timed_batches_ms_per_step": batches,
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
