@@ -219,6 +219,21 @@ conv_i8_status_t conv_fprop_i8_plan(const conv_i8_desc_t *image, const void *ima
                                     char *buf, size_t len);
 
 /*
+ * The candidate plans of the cuDNN frontend tutorial page (autotuning
+ * paragraph: every plan the heuristics offer is built and timed, and the
+ * index of the fastest is kept): here the names of every tile shape the
+ * library can run, comma-separated, in the order the planner considers
+ * them.  Setting the environment variable CONV_I8_TILE to one of them makes
+ * the planner use that tile wherever it applies (the plan string then names
+ * it); a problem it does not fit falls back to the default tile.  Measured
+ * choices for known problems are compiled into the library and take
+ * precedence over its cost model.  Writes at most `len` bytes including the
+ * terminating NUL (CONV_I8_ERR_PARAM if that is too short, CONV_I8_ERR_NULL
+ * for a NULL buf).  Host-only.
+ */
+conv_i8_status_t conv_i8_tile_names(char *buf, size_t len);
+
+/*
  * Requantising INT8 epilogue, fused into the convolution.
  *
  * The naive loop of "Building a From-Scratch INT8 Strided Convolution

@@ -91,6 +91,7 @@ lib.conv_fprop_i8.argtypes = [_DP, _P, _DP, _P, _DP, _P, _V2, _V2, _V2, _V2, _P]
 lib.conv_fprop_i8_noalloc.argtypes = [_DP, _P, _DP, _P, _DP, _P, _V2, _V2, _V2, _V2, _P]
 lib.conv_fprop_i8_plan.argtypes = [_DP, _P, _DP, _P, _DP, _V2, _V2, _V2, _V2,
                                    ctypes.c_char_p, ctypes.c_size_t]
+lib.conv_i8_tile_names.argtypes = [ctypes.c_char_p, ctypes.c_size_t]
 _RQ = ctypes.POINTER(Requant)
 lib.conv_fprop_i8_requant_workspace_size.argtypes = [_DP, _P, _DP, _P, _DP, _V2, _V2, _V2, _V2,
                                                      ctypes.POINTER(ctypes.c_size_t)]
@@ -117,7 +118,7 @@ for _f in ("conv_fprop_i8_out_dims", "conv_fprop_i8_workspace_size", "conv_fprop
            "conv_fprop_i8", "conv_fprop_i8_noalloc", "conv_fprop_i8_plan", "conv_fprop_i8_requant_workspace_size",
            "conv_fprop_i8_requant_ws", "conv_fprop_i8_requant", "conv_fprop_i8_ex_workspace_size",
            "conv_fprop_i8_ex_ws", "conv_dgrad_i8_workspace_size", "conv_dgrad_i8_ws", "conv_dgrad_i8",
-           "conv_wgrad_i8_workspace_size", "conv_wgrad_i8_ws", "conv_wgrad_i8"):
+           "conv_wgrad_i8_workspace_size", "conv_wgrad_i8_ws", "conv_wgrad_i8", "conv_i8_tile_names"):
     getattr(lib, _f).restype = ctypes.c_int
 
 
@@ -248,6 +249,12 @@ def conv_fprop_i8_plan(x, w, out=None, pre_padding=0, post_padding=0, stride=1, 
     _check(lib.conv_fprop_i8_plan(ctypes.byref(_as_desc(x)), xp, ctypes.byref(_as_desc(w)), wp,
                                   ctypes.byref(_as_desc(out)), pre, post, st, dl, buf, 512))
     return buf.value.decode()
+
+
+def conv_i8_tile_names() -> list:
+    buf = ctypes.create_string_buffer(4096)
+    _check(lib.conv_i8_tile_names(buf, 4096))
+    return buf.value.decode().split(",")
 
 
 def plan_fields(plan: str) -> dict:

@@ -325,6 +325,33 @@ const TileCfg kTiles[] = {
 };
 constexpr int kNumTiles = sizeof(kTiles) / sizeof(kTiles[0]);
 
+// Measured tile choices (the autotuning step: every applicable tile timed on
+// one problem, the fastest kept).  The table is written by the package's
+// tune module; a forward problem that matches an entry exactly takes its tile
+// ahead of the cost model (a forced CONV_I8_TILE still wins).
+struct TunedTile {
+    int64_t N, C, H, W, K, R, S, pre_h, pre_w, post_h, post_w, str_h, str_w, dil_h, dil_w;
+    int lanes;         // output lanes: 0 walk channels, 1 walk pixels
+    const char *tile;  // nullptr ends the table
+};
+const TunedTile kTuned[] = {
+#include "tuned_tiles.inc"
+    {0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, nullptr},
+};
+
+const char *tuned_tile(const Problem &pb, bool pix_j)
+{
+    if (pb.flip_out || pb.split_ok)
+        return nullptr;
+    for (const TunedTile *t = kTuned; t->tile; ++t)
+        if (t->N == pb.N && t->C == pb.C && t->H == pb.H && t->W == pb.W && t->K == pb.K && t->R == pb.R &&
+            t->S == pb.S && t->pre_h == pb.pre[0] && t->pre_w == pb.pre[1] && t->post_h == pb.post[0] &&
+            t->post_w == pb.post[1] && t->str_h == pb.str[0] && t->str_w == pb.str[1] && t->dil_h == pb.dil[0] &&
+            t->dil_w == pb.dil[1] && t->lanes == (pix_j ? 1 : 0))
+            return t->tile;
+    return nullptr;
+}
+
 // Division by a launch-invariant divisor d >= 1 for dividends below 2^31:
 // l = ceil(log2 d), m = floor(2^32 (2^l - d) / d) + 1.
 Divisor make_divisor(int64_t d)
@@ -603,6 +630,8 @@ conv_i8_status_t make_plan(const Problem &pb, const void *x_ptr, const void *w_p
     int best = -1;
     double best_cost = 0;
     const char *forced = env_tile();
+    const char *tuned = forced ? nullptr : tuned_tile(pb, pl->pix_j);
+    int tuned_idx = -1;
     for (int i = 0; i < kNumTiles; ++i) {
         const TileCfg &c = kTiles[i];
         if (forced && strcmp(forced, c.name) != 0)
@@ -616,6 +645,8 @@ conv_i8_status_t make_plan(const Problem &pb, const void *x_ptr, const void *w_p
             // is channel-innermost with equally spaced pixels
             if (pb.R != 1 || pb.S != 1 || pb.K > c.tn || pl->Cp > c.bk || pl->pix_j || !pl->pix_linear)
                 continue;
+            if (tuned && strcmp(tuned, c.name) == 0)
+                tuned_idx = i;
             // HBM-bound and measured ahead of every im2col tile on 1x1 layers
             // (the tile model prices the im2col tiles' stores too low there):
             // the first one that fits is taken
@@ -647,6 +678,8 @@ conv_i8_status_t make_plan(const Problem &pb, const void *x_ptr, const void *w_p
         } else {
             bytes = (double)(c.tm + c.tn) * stages * c.bk;
         }
+        if (tuned && strcmp(tuned, c.name) == 0)
+            tuned_idx = i;
         double eff = c.eff;
         if (c.kind == kIm2col && cc % cps != 0)
             eff *= chunks > 0 ? (double)chunks / (double)(stages * cps) : 1.0;
@@ -666,6 +699,11 @@ conv_i8_status_t make_plan(const Problem &pb, const void *x_ptr, const void *w_p
             best = i;
             best_cost = cost;
         }
+    }
+    if (tuned_idx >= 0) {
+        if (getenv("CONV_I8_COST"))
+            fprintf(stderr, "conv_i8 cost: measured choice %s for this problem\n", kTiles[tuned_idx].name);
+        best = tuned_idx;
     }
     if (best < 0) {
         // unknown or inapplicable CONV_I8_TILE value: default shape
@@ -1964,6 +2002,26 @@ conv_i8_status_t conv_wgrad_i8(const conv_i8_desc_t *image, const void *image_pt
 {
     return wgrad_entry(image, image_ptr, loss, loss_ptr, dw, dw_ptr, pre_padding, post_padding,
                        stride, dilation, mode, false, nullptr, true, nullptr, 0, stream);
+}
+
+conv_i8_status_t conv_i8_tile_names(char *buf, size_t len)
+{
+    if (!buf)
+        return CONV_I8_ERR_NULL;
+    size_t used = 0;
+    for (int i = 0; i < kNumTiles; ++i) {
+        const size_t n = strlen(kTiles[i].name) + (i ? 1 : 0);
+        if (used + n + 1 > len)
+            return CONV_I8_ERR_PARAM;
+        if (i)
+            buf[used++] = ',';
+        memcpy(buf + used, kTiles[i].name, n - (i ? 1 : 0));
+        used += n - (i ? 1 : 0);
+    }
+    if (used + 1 > len)
+        return CONV_I8_ERR_PARAM;
+    buf[used] = 0;
+    return CONV_I8_OK;
 }
 
 const char *conv_i8_status_string(conv_i8_status_t status)

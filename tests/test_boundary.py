@@ -190,6 +190,41 @@ def test_footprint_offsets_fit_24_bits(monkeypatch):
     assert apart["batch_chunk"] == "1" and apart["tile"] == "f128x128"
 
 
+def _tuned_entries():
+    path = os.path.join(os.path.dirname(os.path.abspath(ci8.__file__)), "csrc", "tuned_tiles.inc")
+    rows = []
+    for line in open(path):
+        m = re.match(r"\{([-\d, ]+), \"([\w]+)\"\},", line.strip())
+        if m:
+            rows.append((tuple(int(v) for v in m.group(1).split(",")), m.group(2)))
+    return rows
+
+
+def test_tuned_tiles_are_planned(monkeypatch):
+    """The measured tile table compiled into the library covers every
+    workload, and the planner takes its tile (ahead of the cost model)."""
+    monkeypatch.delenv("CONV_I8_TILE", raising=False)
+    rows = dict(_tuned_entries())
+    names = set(ci8.conv_i8_tile_names())
+    assert set(rows.values()) <= names
+    for name in wl.CASES:
+        c = wl.case(name)
+        a = _args(c)
+        f = ci8.plan_fields(ci8.conv_fprop_i8_plan(a["x"], a["w"], a["y"], c.pre, c.post, c.stride, c.dilation))
+        key = (*c.image.dims, c.filter.dims[0], *c.filter.dims[2:], *c.pre, *c.post, *c.stride, *c.dilation,
+               1 if f["lanes"] == "pixels" else 0)
+        assert key in rows, name
+        assert f["tile"] == rows[key], (name, f["tile"], rows[key])
+
+
+def test_tile_names():
+    names = ci8.conv_i8_tile_names()
+    assert len(names) == len(set(names)) and "t256x128" in names and "128x128x64" in names
+    buf = ctypes.create_string_buffer(8)
+    assert ci8.STATUS[ci8.lib.conv_i8_tile_names(buf, 8)] == "CONV_I8_ERR_PARAM"
+    assert ci8.STATUS[ci8.lib.conv_i8_tile_names(None, 8)] == "CONV_I8_ERR_NULL"
+
+
 def test_empty_problems_are_ok_without_device_work():
     D = ci8.desc
     # N = 0: nothing to write, no pointers needed
