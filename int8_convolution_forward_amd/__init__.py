@@ -37,7 +37,9 @@ __all__ = [
     "status_string", "LIB_PATH", "DT_INT8", "DT_INT32", "MAX_REDUCTION", "lib",
 ]
 
-LIB_PATH = _build.LIB
+# CONV_I8_LIB names another build of the library (the host-sanitizer test
+# loads a host-only build with AddressSanitizer through it)
+LIB_PATH = os.environ.get("CONV_I8_LIB") or _build.LIB
 DT_INT8 = 1
 DT_INT32 = 2
 MAX_REDUCTION = 131071

@@ -25,6 +25,14 @@
 #include "igemm_kernel.hpp"
 #include "repack_kernel.hpp"
 
+#ifdef CONV_I8_HOST_ONLY
+// Host-only build of the validation and planning code (built with the host
+// sanitizers on a machine without a GPU): no kernel is instantiated, so no
+// device code exists, and a launch does nothing.  Never a product build.
+#undef hipLaunchKernelGGL
+#define hipLaunchKernelGGL(...) ((void)0)
+#endif
+
 namespace convi8 {
 namespace {
 
@@ -1179,7 +1187,9 @@ void *g_scratch_ptr[kMaxDevices] = {};
 }  // namespace
 }  // namespace convi8
 
+#ifndef CONV_I8_HOST_ONLY
 static __device__ __align__(256) uint8_t scratch[CONV_I8_NOALLOC_SCRATCH_BYTES];
+#endif
 
 namespace convi8 {
 namespace {
@@ -1203,8 +1213,12 @@ conv_i8_status_t scratch_address(void *stream, void **addr)
     std::lock_guard<std::mutex> lock(g_scratch_mutex);
     if (!g_scratch_ptr[dev]) {
         void *p = nullptr;
+#ifdef CONV_I8_HOST_ONLY
+        return CONV_I8_ERR_HIP;
+#else
         if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p)
             return CONV_I8_ERR_HIP;
+#endif
         g_scratch_ptr[dev] = p;
     }
     *addr = g_scratch_ptr[dev];
@@ -2026,7 +2040,12 @@ conv_i8_status_t conv_i8_tile_names(char *buf, size_t len)
 
 const char *conv_i8_status_string(conv_i8_status_t status)
 {
-    switch (status) {
+    // a caller may pass any int: read its bits, never the enum value (a value
+    // outside the enumerators' range is undefined behaviour in C++)
+    static_assert(sizeof(conv_i8_status_t) == sizeof(int), "the status enum is int-sized");
+    int code;
+    memcpy(&code, &status, sizeof code);
+    switch (code) {
     case CONV_I8_OK: return "CONV_I8_OK";
     case CONV_I8_ERR_NULL: return "CONV_I8_ERR_NULL: a required pointer is NULL";
     case CONV_I8_ERR_DTYPE: return "CONV_I8_ERR_DTYPE: image/filter must be INT8 and the output INT32 (INT8 for the requantising entries)";
