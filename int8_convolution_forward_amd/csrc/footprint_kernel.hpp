@@ -703,18 +703,25 @@ __global__ __launch_bounds__(64 * WGM * WGN) void conv_fp3x3_ring9_kernel(IgemmA
             constexpr int NL = XL + BL + (g1 - g0);
             const int pcb = t == 8 ? cb + 2 : cb + 1;   // block of this tap's footprint chunk
 
-            wait_vm_lgkm0<FIRST ? allowed_first<NG, BL>(t) : allowed_at<NG, BL>(t)>();
-            __builtin_amdgcn_s_barrier();
-            __builtin_amdgcn_sched_barrier(0);
+            // The first PRE MFMAs need only this wave's registers: they go
+            // out before the wait and the barrier, so the matrix unit has
+            // work while the waves line up.  Then the fragment reads of the
+            // next stage ride on half of the remaining MFMAs, the loads on
+            // the other half.
+            constexpr int PRE = NMF / 4;
+            constexpr int H = PRE + (NMF - PRE) / 2;
 #pragma unroll
             for (int q = 0; q < NMF; ++q) {
+                if (q == PRE) {
+                    wait_vm_lgkm0<FIRST ? allowed_first<NG, BL>(t) : allowed_at<NG, BL>(t)>();
+                    __builtin_amdgcn_s_barrier();
+                    __builtin_amdgcn_sched_barrier(0);
+                }
                 mfma_one(buf, q);
-                // the fragment reads of the next stage ride on the first half
-                // of the MFMAs, the loads on the second half
-                constexpr int H = NMF / 2;
-                if (q < H) {
+                if (q < PRE) {
+                } else if (q < H) {
 #pragma unroll
-                    for (int o = q * NRD / H; o < (q + 1) * NRD / H; ++o)
+                    for (int o = (q - PRE) * NRD / (H - PRE); o < (q - PRE + 1) * NRD / (H - PRE); ++o)
                         read_one(buf ^ 1, rt, rfb, o);
                 } else {
 #pragma unroll
