@@ -62,6 +62,27 @@ def median(v):
     return v[n // 2] if n % 2 else 0.5 * (v[n // 2 - 1] + v[n // 2])
 
 
+def mfma_ceiling(ci8, stream, workgroup_counts, iters=2048, launches=10):
+    """TOP/s of the matrix-core calibration kernel (random INT8 operands in
+    registers, back-to-back v_mfma_i32_32x32x32_i8, one workgroup of four
+    waves per CU) on each workgroup count: median of five timed batches."""
+    import torch
+
+    out = torch.empty(max(workgroup_counts) * 256, dtype=torch.int32, device="cuda")
+    seed = 0x9E3779B9
+    res = {}
+    for wg in workgroup_counts:
+        def run():
+            for _ in range(launches):
+                ci8.conv_i8_mfma_ceiling(wg, iters, seed, out, stream)
+
+        run()
+        torch.cuda.synchronize()
+        ms = median(timed_batches(run, stream, launches))
+        res[str(wg)] = wg * 4 * iters * 8 * 65536 / (ms * 1e-3) / 1e12
+    return res
+
+
 def host_description(orc):
     """nproc, the CPU model and the oracle's thread count."""
     model = None
@@ -444,6 +465,15 @@ def main():
         roof = {"bound": "hbm", "achieved": alg_bytes / (k_avg_ms * 1e-3) / 1e9, "peak": HBM_PEAK_GBS,
                 "unit": "GB/s"}
     roof["frac"] = roof["achieved"] / roof["peak"]
+    if roof["bound"] == "mfma":
+        # the measured ceiling beside the published peak: the rate the matrix
+        # cores reach with random operands on as many CUs as the kernel's
+        # grid covers, and on all 256 (the clock falls under the power limit)
+        wgs = min(int(kf.get("tiles", "256")), 256)
+        ceil = mfma_ceiling(ci8, stream, sorted({wgs, 256}))
+        roof["mfma_ceiling"] = {"unit": "TOP/s", "operands": "random int8 in registers",
+                                "tops_by_busy_cus": ceil}
+        roof["frac_of_ceiling"] = roof["achieved"] / ceil[str(wgs)]
     roof["traffic"] = traffic_from_profiles(c.name + ("_requant" if rq_on else ""), alg_bytes)
     if kf.get("tile") in RING9_TILES:
         roof["kernel"] = "conv_fp3x3_ring9_kernel"

@@ -234,6 +234,23 @@ conv_i8_status_t conv_fprop_i8_plan(const conv_i8_desc_t *image, const void *ima
 conv_i8_status_t conv_i8_tile_names(char *buf, size_t len);
 
 /*
+ * Calibration for the compute side of the roofline (the blog "Building a
+ * From-Scratch INT8 Strided Convolution Kernel" measures GOPS in its
+ * "Benchmarking" section and asks for hardware observability in "Extending
+ * It"): the INT8 matrix-core rate this GPU reaches under load, to set beside
+ * the published peak.  Launches `workgroups` workgroups of four waves on
+ * `stream`; each wave issues `iters` x 8 v_mfma_i32_32x32x32_i8 back to back
+ * on register operands (random bytes drawn from `seed`, or all zeros when
+ * seed is 0) and every thread writes one checksum to out[] (device memory,
+ * workgroups * 256 int32 elements, caller-owned).  One launch performs
+ * workgroups * 4 * iters * 8 * 65536 INT8 operations; time it with events
+ * on the stream.  CONV_I8_ERR_NULL for a NULL out, CONV_I8_ERR_PARAM for
+ * workgroups outside [1, 2^20] or iters < 1, CONV_I8_ERR_HIP if the launch
+ * fails.
+ */
+conv_i8_status_t conv_i8_mfma_ceiling(int workgroups, int iters, uint32_t seed, int32_t *out, void *stream);
+
+/*
  * Requantising INT8 epilogue, fused into the convolution.
  *
  * The naive loop of "Building a From-Scratch INT8 Strided Convolution

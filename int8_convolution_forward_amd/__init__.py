@@ -94,6 +94,7 @@ lib.conv_fprop_i8_noalloc.argtypes = [_DP, _P, _DP, _P, _DP, _P, _V2, _V2, _V2, 
 lib.conv_fprop_i8_plan.argtypes = [_DP, _P, _DP, _P, _DP, _V2, _V2, _V2, _V2,
                                    ctypes.c_char_p, ctypes.c_size_t]
 lib.conv_i8_tile_names.argtypes = [ctypes.c_char_p, ctypes.c_size_t]
+lib.conv_i8_mfma_ceiling.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_uint32, _P, _P]
 _RQ = ctypes.POINTER(Requant)
 lib.conv_fprop_i8_requant_workspace_size.argtypes = [_DP, _P, _DP, _P, _DP, _V2, _V2, _V2, _V2,
                                                      ctypes.POINTER(ctypes.c_size_t)]
@@ -120,7 +121,7 @@ for _f in ("conv_fprop_i8_out_dims", "conv_fprop_i8_workspace_size", "conv_fprop
            "conv_fprop_i8", "conv_fprop_i8_noalloc", "conv_fprop_i8_plan", "conv_fprop_i8_requant_workspace_size",
            "conv_fprop_i8_requant_ws", "conv_fprop_i8_requant", "conv_fprop_i8_ex_workspace_size",
            "conv_fprop_i8_ex_ws", "conv_dgrad_i8_workspace_size", "conv_dgrad_i8_ws", "conv_dgrad_i8",
-           "conv_wgrad_i8_workspace_size", "conv_wgrad_i8_ws", "conv_wgrad_i8", "conv_i8_tile_names"):
+           "conv_wgrad_i8_workspace_size", "conv_wgrad_i8_ws", "conv_wgrad_i8", "conv_i8_tile_names", "conv_i8_mfma_ceiling"):
     getattr(lib, _f).restype = ctypes.c_int
 
 
@@ -257,6 +258,16 @@ def conv_i8_tile_names() -> list:
     buf = ctypes.create_string_buffer(4096)
     _check(lib.conv_i8_tile_names(buf, 4096))
     return buf.value.decode().split(",")
+
+
+def conv_i8_mfma_ceiling(workgroups: int, iters: int, seed: int, out: torch.Tensor, stream=None) -> None:
+    """One launch of the matrix-core calibration kernel (out: int32 GPU
+    tensor of at least workgroups * 256 elements)."""
+    _on_one_gpu(out=out)
+    if out.dtype != torch.int32 or out.numel() < workgroups * 256:
+        raise ValueError("out must hold workgroups * 256 int32 elements")
+    _check(lib.conv_i8_mfma_ceiling(int(workgroups), int(iters), int(seed) & 0xffffffff, _ptr(out),
+                                    _stream_handle(stream)))
 
 
 def plan_fields(plan: str) -> dict:

@@ -24,6 +24,7 @@
 #include "pointwise_kernel.hpp"
 #include "igemm_kernel.hpp"
 #include "repack_kernel.hpp"
+#include "mfma_ceiling_kernel.hpp"
 
 #ifdef CONV_I8_HOST_ONLY
 // Host-only build of the validation and planning code (built with the host
@@ -2016,6 +2017,17 @@ conv_i8_status_t conv_wgrad_i8(const conv_i8_desc_t *image, const void *image_pt
 {
     return wgrad_entry(image, image_ptr, loss, loss_ptr, dw, dw_ptr, pre_padding, post_padding,
                        stride, dilation, mode, false, nullptr, true, nullptr, 0, stream);
+}
+
+conv_i8_status_t conv_i8_mfma_ceiling(int workgroups, int iters, uint32_t seed, int32_t *out, void *stream)
+{
+    if (!out)
+        return CONV_I8_ERR_NULL;
+    if (workgroups < 1 || workgroups > (1 << 20) || iters < 1)
+        return CONV_I8_ERR_PARAM;
+    hipLaunchKernelGGL(convi8::mfma_ceiling_kernel, dim3(workgroups), dim3(256), 0, (hipStream_t)stream, iters,
+                       (unsigned)seed, (int *)out);
+    return hipGetLastError() == hipSuccess ? CONV_I8_OK : CONV_I8_ERR_HIP;
 }
 
 conv_i8_status_t conv_i8_tile_names(char *buf, size_t len)

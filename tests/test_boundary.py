@@ -225,6 +225,14 @@ def test_tile_names():
     assert ci8.STATUS[ci8.lib.conv_i8_tile_names(None, 8)] == "CONV_I8_ERR_NULL"
 
 
+def test_mfma_ceiling_argument_errors():
+    S = ci8.STATUS
+    assert S[ci8.lib.conv_i8_mfma_ceiling(4, 1, 1, None, None)] == "CONV_I8_ERR_NULL"
+    assert S[ci8.lib.conv_i8_mfma_ceiling(0, 1, 1, FAKE, None)] == "CONV_I8_ERR_PARAM"
+    assert S[ci8.lib.conv_i8_mfma_ceiling(4, 0, 1, FAKE, None)] == "CONV_I8_ERR_PARAM"
+    assert S[ci8.lib.conv_i8_mfma_ceiling((1 << 20) + 1, 1, 1, FAKE, None)] == "CONV_I8_ERR_PARAM"
+
+
 def test_empty_problems_are_ok_without_device_work():
     D = ci8.desc
     # N = 0: nothing to write, no pointers needed

@@ -143,3 +143,4 @@ def test_graph_replay_wgrad(ci8, name, layout):
     ws = torch.empty(max(size, 1), dtype=torch.uint8, device=dev)
     print(f"[gpu] graph wgrad {name} {layout} workspace={size}", flush=True)
     _replays_match(lambda: ci8.conv_wgrad_i8_ws(x, dy, dw, ws if size else None, *args), buf, dw)
+
