@@ -25,6 +25,7 @@
 #include "igemm_kernel.hpp"
 #include "repack_kernel.hpp"
 #include "mfma_ceiling_kernel.hpp"
+#include "direct_kernel.hpp"
 
 #ifdef CONV_I8_HOST_ONLY
 // Host-only build of the validation and planning code (built with the host
@@ -286,13 +287,14 @@ void launch_pw(bool, bool, dim3 grid, hipStream_t stream, const IgemmArgs &a)
                            stream, a);
 }
 
-enum KernelKind { kIm2col = 0, kFootprint = 1, kPointwise = 2 };
+enum KernelKind { kIm2col = 0, kFootprint = 1, kPointwise = 2, kDirect = 3 };
 
 struct TileCfg {
     const char *name;  // CONV_I8_TILE value that forces this shape
     int tm, tn, bk, ns;
     int waves;         // 4 (2x2 wave grid) or 8 (4x2)
-    int kind;          // KernelKind: im2col, 3x3 footprint (image once per 64-channel block), 1x1 streaming
+    int kind;          // KernelKind: im2col, 3x3 footprint (image once per 64-channel block), 1x1
+                       // streaming, direct (tiny problems, operands read in place)
     int fpix;          // footprint capacity (pixels)
     double eff;        // relative MFMA efficiency of this tile shape (cost model)
     Launcher launch;   // the kernel instantiation with exactly these parameters
@@ -331,7 +333,15 @@ const TileCfg kTiles[] = {
     {"pw64x256", 32, 64, 256, 0, 4, kPointwise, 0, 1.0, launch_pw<2, 8>},
     {"pw128x64", 32, 128, 64, 0, 4, kPointwise, 0, 1.0, launch_pw<4, 2>},
     {"pw128x128", 32, 128, 128, 0, 4, kPointwise, 0, 1.0, launch_pw<4, 4>},
+    // one thread per output element, any layout read in place (no repack)
+    {"direct", 1, 1, 0, 0, 4, kDirect, 0, 1.0, nullptr},
 };
+
+// The direct kernel: applicable up to kDirectMaxMacs multiply-adds (and
+// kDirectMaxCRS per output element); chosen unasked up to kDirectTinyMacs
+// when the implicit-GEMM path would need a repack launch first.
+constexpr double kDirectMaxMacs = 268435456.0, kDirectTinyMacs = 65536.0;
+constexpr int64_t kDirectMaxCRS = 4608;
 constexpr int kNumTiles = sizeof(kTiles) / sizeof(kTiles[0]);
 
 // Measured tile choices (the autotuning step: every applicable tile timed on
@@ -641,10 +651,23 @@ conv_i8_status_t make_plan(const Problem &pb, const void *x_ptr, const void *w_p
     const char *forced = env_tile();
     const char *tuned = forced ? nullptr : tuned_tile(pb, pl->pix_j);
     int tuned_idx = -1;
+    const double macs = (double)pb.N * pb.K * pb.P * pb.Q * pb.C * pb.R * pb.S;
+    const bool direct_fits = macs <= kDirectMaxMacs && pb.C * RS <= kDirectMaxCRS;
+    int direct_idx = -1;
     for (int i = 0; i < kNumTiles; ++i) {
         const TileCfg &c = kTiles[i];
         if (forced && strcmp(forced, c.name) != 0)
             continue;
+        if (c.kind == kDirect) {
+            if (!direct_fits)
+                continue;
+            if (tuned && strcmp(tuned, c.name) == 0)
+                tuned_idx = i;
+            direct_idx = i;
+            if (forced)
+                best = i;
+            continue;
+        }
         const int cps = c.bk / 16;
         const int64_t chunks = RS * cc;
         int64_t stages = cc % cps == 0 ? RS * (cc / cps) : (chunks + cps - 1) / cps;
@@ -713,6 +736,8 @@ conv_i8_status_t make_plan(const Problem &pb, const void *x_ptr, const void *w_p
         if (getenv("CONV_I8_COST"))
             fprintf(stderr, "conv_i8 cost: measured choice %s for this problem\n", kTiles[tuned_idx].name);
         best = tuned_idx;
+    } else if (!forced && direct_idx >= 0 && macs <= kDirectTinyMacs && (pl->repack_x || pl->repack_w)) {
+        best = direct_idx;   // one launch instead of a repack and a convolution
     }
     if (best < 0) {
         // unknown or inapplicable CONV_I8_TILE value: default shape
@@ -723,6 +748,19 @@ conv_i8_status_t make_plan(const Problem &pb, const void *x_ptr, const void *w_p
     }
     pl->cfg = best;
     const TileCfg &c = kTiles[best];
+    if (c.kind == kDirect) {
+        // operands read in place through their strides: no repack, no
+        // workspace, no batch chunks (64-bit offsets)
+        pl->repack_x = pl->repack_w = false;
+        pl->ws_bytes = 0;
+        pl->ksplit = 1;
+        pl->kchunk = 0;
+        pl->part = false;
+        pl->blocked = true;
+        pl->nstages = 0;
+        pl->batch_chunk = std::max<int64_t>(pb.N, 1);
+        return CONV_I8_OK;
+    }
     const int cps = c.bk / 16;
     pl->blocked = cc % cps == 0;
     pl->nstages = pl->blocked ? RS * (cc / cps) : (RS * cc + cps - 1) / cps;
@@ -768,17 +806,70 @@ conv_i8_status_t make_plan(const Problem &pb, const void *x_ptr, const void *w_p
     return CONV_I8_OK;
 }
 
+// Workgroups of the direct kernel: one thread per output element, at most
+// four workgroups per CU (the rest is a grid-stride loop).
+int64_t direct_blocks(const Problem &pb)
+{
+    const int64_t total = pb.N * pb.K * pb.P * pb.Q;
+    return std::min<int64_t>((total + 255) / 256, 4 * kCUs);
+}
+
+conv_i8_status_t launch_direct(const Problem &pb, const void *x_ptr, const void *w_ptr, void *y_ptr,
+                               hipStream_t stream, const conv_i8_requant_t *rq)
+{
+    const int64_t total = pb.N * pb.K * pb.P * pb.Q;
+    if (total == 0)
+        return CONV_I8_OK;
+    DirectArgs d{};
+    d.x = (const int8_t *)x_ptr;
+    d.w = (const int8_t *)w_ptr;
+    d.y = y_ptr;
+    for (int i = 0; i < 4; ++i) {
+        d.xs[i] = pb.x.s[i];
+        d.ws[i] = pb.w.s[i];
+        d.ys[i] = pb.y.s[i];
+    }
+    d.total = total;
+    d.K = (int)pb.K;
+    d.C = (int)pb.C;
+    d.R = (int)pb.R;
+    d.S = (int)pb.S;
+    d.P = (int)pb.P;
+    d.Q = (int)pb.Q;
+    d.H = (int)pb.H;
+    d.W = (int)pb.W;
+    d.preH = (int)pb.pre[0];
+    d.preW = (int)pb.pre[1];
+    d.strH = (int)pb.str[0];
+    d.strW = (int)pb.str[1];
+    d.dilH = (int)pb.dil[0];
+    d.dilW = (int)pb.dil[1];
+    d.conv_mode = pb.mode == CONV_I8_MODE_CONVOLUTION ? 1 : 0;
+    d.flip_out = pb.flip_out ? 1 : 0;
+    if (rq) {
+        d.q8 = 1;
+        d.q_scale = rq->scale;
+        d.q_bias = rq->bias;
+        d.q_alpha = rq->alpha;
+        d.q_relu = rq->relu ? 1 : 0;
+    }
+    hipLaunchKernelGGL(conv_direct_kernel<0>, dim3((unsigned)direct_blocks(pb)), dim3(256), 0, stream, d);
+    return hipGetLastError() == hipSuccess ? CONV_I8_OK : CONV_I8_ERR_HIP;
+}
+
 std::string describe(const Problem &pb, const Plan &pl)
 {
     const TileCfg &c = kTiles[pl.cfg];
     const int64_t M = pb.N * pb.P * pb.Q;
-    const int64_t tiles = ((M + c.tm - 1) / c.tm) * ((pb.K + c.tn - 1) / c.tn);
+    const int64_t tiles = c.kind == kDirect ? direct_blocks(pb)
+                                            : ((M + c.tm - 1) / c.tm) * ((pb.K + c.tn - 1) / c.tn);
     char buf[512];
     snprintf(buf, sizeof buf,
              "repack_image=%d repack_filter=%d Cp=%lld tile=%s kernel=%s order=%s stages=%lld "
              "lanes=%s tiles=%lld batch_chunk=%lld workspace=%zu ksplit=%lld split_sum=%s",
              (int)pl.repack_x, (int)pl.repack_w, (long long)pl.Cp, c.name,
-             c.kind == kFootprint ? "footprint" : c.kind == kPointwise ? "pointwise" : "im2col", pl.blocked ? "blocked" : "flat", (long long)pl.nstages,
+             c.kind == kFootprint ? "footprint" : c.kind == kPointwise ? "pointwise" : c.kind == kDirect ? "direct" : "im2col",
+             pl.blocked ? "blocked" : "flat", (long long)pl.nstages,
              pl.pix_j ? "pixels" : "channels", (long long)tiles, (long long)pl.batch_chunk,
              pl.ws_bytes, (long long)pl.ksplit, pl.ksplit < 2 ? "none" : pl.part ? "partial" : "atomic");
     return buf;
@@ -834,6 +925,8 @@ conv_i8_status_t launch_repacks(const RepackJob *jobs, int njobs, hipStream_t st
 conv_i8_status_t run(const Problem &pb, const Plan &pl, const void *x_ptr, const void *w_ptr,
                      void *y_ptr, void *ws, hipStream_t stream, const conv_i8_requant_t *rq = nullptr)
 {
+    if (kTiles[pl.cfg].kind == kDirect)
+        return launch_direct(pb, x_ptr, w_ptr, y_ptr, stream, rq);
     const int64_t esize = rq ? 1 : 4;        // bytes per output element
     const int8_t *x = (const int8_t *)x_ptr;
     const int8_t *w = (const int8_t *)w_ptr;
@@ -2025,7 +2118,7 @@ conv_i8_status_t conv_i8_mfma_ceiling(int workgroups, int iters, uint32_t seed, 
         return CONV_I8_ERR_NULL;
     if (workgroups < 1 || workgroups > (1 << 20) || iters < 1)
         return CONV_I8_ERR_PARAM;
-    hipLaunchKernelGGL(convi8::mfma_ceiling_kernel, dim3(workgroups), dim3(256), 0, (hipStream_t)stream, iters,
+    hipLaunchKernelGGL(convi8::mfma_ceiling_kernel<0>, dim3(workgroups), dim3(256), 0, (hipStream_t)stream, iters,
                        (unsigned)seed, (int *)out);
     return hipGetLastError() == hipSuccess ? CONV_I8_OK : CONV_I8_ERR_HIP;
 }

@@ -147,7 +147,7 @@ def test_workspace_errors():
 
 
 @pytest.mark.parametrize("name,repack_image,repack_filter,order", [
-    ("tiny_5x5_r3", "1", "1", "flat"),
+    ("tiny_5x5_r3", "0", "0", None),      # the direct kernel reads both in place
     ("downsample_s2_n8_c64_56", "0", "0", "blocked"),
     ("pointwise_1x1_n32_c256_56", "0", "0", "blocked"),
     ("bottleneck_3x3_n32_c128_28", "0", "0", "blocked"),
@@ -163,6 +163,8 @@ def test_plans(name, repack_image, repack_filter, order):
         assert f["order"] == order
     need = ci8.conv_fprop_i8_workspace_size(a["x"], a["w"], a["y"], c.pre, c.post, c.stride, c.dilation)
     assert (need == 0) == (repack_image == "0" and repack_filter == "0")
+    if f["kernel"] == "direct":
+        return
     # channel-innermost NHWC output -> lanes walk channels; NCHW -> pixels
     assert f["lanes"] == ("channels" if c.out.strides[1] == 1 else "pixels")
 
@@ -231,6 +233,24 @@ def test_mfma_ceiling_argument_errors():
     assert S[ci8.lib.conv_i8_mfma_ceiling(0, 1, 1, FAKE, None)] == "CONV_I8_ERR_PARAM"
     assert S[ci8.lib.conv_i8_mfma_ceiling(4, 0, 1, FAKE, None)] == "CONV_I8_ERR_PARAM"
     assert S[ci8.lib.conv_i8_mfma_ceiling((1 << 20) + 1, 1, 1, FAKE, None)] == "CONV_I8_ERR_PARAM"
+
+
+def test_direct_kernel_plans(monkeypatch):
+    """Tiny problems whose operands need a repack run on the direct kernel
+    (one launch, no workspace); a forced "direct" is refused above its size
+    limit and the default tile runs instead."""
+    monkeypatch.delenv("CONV_I8_TILE", raising=False)
+    D = ci8.desc
+    x, w = D((2, 3, 6, 7), (126, 42, 7, 1), 1), D((4, 3, 3, 3), (27, 9, 3, 1), 1)   # NCHW, KCRS
+    y = D((2, 4, 4, 5), (80, 20, 5, 1), 2)
+    f = ci8.plan_fields(ci8.conv_fprop_i8_plan(x, w, y))
+    assert f["kernel"] == "direct" and f["workspace"] == "0" and f["repack_image"] == "0"
+    assert ci8.conv_fprop_i8_workspace_size(x, w, y) == 0
+    c = wl.case("large_channel_n64_c512_14")
+    a = _args(c)
+    monkeypatch.setenv("CONV_I8_TILE", "direct")
+    f = ci8.plan_fields(ci8.conv_fprop_i8_plan(a["x"], a["w"], a["y"], c.pre, c.post, c.stride, c.dilation))
+    assert f["tile"] == "128x128x64"
 
 
 def test_empty_problems_are_ok_without_device_work():
@@ -421,11 +441,12 @@ def test_dgrad_argument_errors():
 
 @pytest.mark.parametrize("st,dl", [((1, 1), (1, 1)), ((2, 2), (1, 1)), ((2, 3), (2, 1)), ((4, 4), (2, 2))])
 def test_dgrad_workspace(st, dl):
-    """One forward call per stride phase; the transposed filter always needs a
-    repack, so the workspace is at least the packed filter."""
-    dy, w, dx, pre, post, _, _ = _dgrad_args(st=st, dl=dl)
+    """One forward call per stride phase; above the direct kernel's size the
+    transposed filter always needs a repack, so the workspace is at least the
+    packed filter."""
+    dy, w, dx, pre, post, _, _ = _dgrad_args(K=32, C=64, st=st, dl=dl)
     n = ci8.conv_dgrad_i8_workspace_size(dy, w, dx, pre, post, st, dl)
-    assert n >= 16 * 8 * 9 // max(1, st[0] * st[1])
+    assert n >= 64 * 32 * 9 // max(1, st[0] * st[1])
     assert _call_dgrad(dy, w, dx, pre, post, st, dl, ws_bytes=n - 1, ws=FAKE) == 10
 
 
@@ -450,6 +471,11 @@ def test_wgrad_argument_errors():
     big_x = D((600, 16, 15, 15), (3600, 1, 240, 16), ci8.DT_INT8)
     big_dy = D((600, 8, 15, 15), (1800, 1, 120, 8), ci8.DT_INT8)
     assert call(big_x, big_dy, dw, stv=(1, 1)) == 9
+    # a tiny problem: the direct kernel reads the transposed operands in place
+    assert ci8.conv_wgrad_i8_workspace_size(x, dy, dw, pre, post, st, dl) == 0
+    dy, w, dx, pre, post, st, dl = _dgrad_args(K=32, C=64)
+    x = D(dx.dims, dx.strides, ci8.DT_INT8)
+    dw = D(w.dims, w.strides, ci8.DT_INT32)
     n = ci8.conv_wgrad_i8_workspace_size(x, dy, dw, pre, post, st, dl)
     assert n > 0                                 # both transposed operands are repacked
     assert call(x, dy, dw, ws_bytes=n - 1, ws=FAKE) == 10

@@ -132,7 +132,7 @@ def test_repeat_runs_identical(ci8):
 # ---------------------------------------------------------------------------
 TILES = ["64x64x64", "128x64x64", "64x128x64", "128x128x64", "128x128x128", "256x128x64",
          "128x256x64", "w256x128x64", "w128x128x64", "w256x128x128", "w128x192x128", "f256x128", "fw256x128",
-         "f128x128", "fk256x128", "fk128x128", "r256x128", "t256x128", "t128x128"]
+         "f128x128", "fk256x128", "fk128x128", "r256x128", "t256x128", "t128x128", "direct"]
 FOOTPRINT_TILES = [t for t in TILES if t[0] in "frt"]
 
 
@@ -207,8 +207,14 @@ def _fill(spec, values, seed):
     return st
 
 
-def test_random_problems(ci8):
-    rng = np.random.default_rng(2024)
+@pytest.mark.parametrize("tile", [None, "direct"])
+def test_random_problems(ci8, monkeypatch, tile):
+    """Random shapes, parameters and layouts; with "direct" forced, the
+    problems small enough for the direct kernel run on it (the others on the
+    tile the planner picks)."""
+    if tile:
+        monkeypatch.setenv("CONV_I8_TILE", tile)
+    rng = np.random.default_rng(2024 if tile is None else 77)
     done = 0
     while done < 120:
         N = int(rng.integers(1, 5))

@@ -48,12 +48,16 @@ def test_noalloc_matches_workspace_entry(ci8):
     big = wl.case("dilated_asym_n16_c96_64x48")
     d, ys, yn = _pair(ci8, big, big.seed_base)
     assert torch.equal(ys, yn)
-    # second call, smaller problem: the tiny case (repacks of a few hundred
-    # bytes into the same array, which still holds the first call's bytes)
-    tiny = wl.case("tiny_5x5_r3")
-    d2, ys2, yn2 = _pair(ci8, tiny, tiny.seed_base + 1)
+    # second call, smaller problem: the same layer on two images (smaller
+    # repacks into the same array, which still holds the first call's bytes)
+    small = wl.ConvCase(name="dilated_n2", image=wl.TensorSpec((2, 96, 64, 48), big.image.strides,
+                                                               storage=2 * 96 * 64 * 96),
+                        filter=big.filter, out=wl.TensorSpec((2, 192, 32, 44), wl.contiguous_strides((2, 192, 32, 44))),
+                        pre=big.pre, post=big.post, stride=big.stride, dilation=big.dilation,
+                        recipe=big.recipe, seed_base=big.seed_base + 1)
+    d2, ys2, yn2 = _pair(ci8, small, small.seed_base)
     assert torch.equal(ys2, yn2)
-    ref = oracle.conv_fprop(d2["x"], d2["w"], tiny.pre, tiny.post, tiny.stride, tiny.dilation)
+    ref = oracle.conv_fprop(d2["x"], d2["w"], small.pre, small.post, small.stride, small.dilation)
     assert torch.equal(yn2, ref)
     # and the first problem again after the smaller one
     d3, ys3, yn3 = _pair(ci8, big, big.seed_base + 2)
