@@ -481,6 +481,8 @@ def main():
         roof["kernel"] = "conv_footprint3x3_kernel"
     elif kf.get("kernel") == "pointwise":
         roof["kernel"] = "conv_pointwise_kernel"
+    elif kf.get("kernel") == "direct":
+        roof["kernel"] = "conv_direct_kernel"
     else:
         roof["kernel"] = "conv_igemm_kernel"
     roof["kernel_tile"] = kf.get("tile")

@@ -545,9 +545,7 @@ __global__ __launch_bounds__(64 * WGM * WGN) void conv_fp3x3_ring9_kernel(IgemmA
     const unsigned ring_lds = lds_address(ring) + wave * 1024;
     const unsigned fbuf_lds = lds_address(fbuf) + wave * 1024;
     const int nblk = a.ncblk;
-    // the requantising epilogue keeps the plain order (its stores are a
-    // quarter of the bytes)
-    const bool tail = TAIL && nblk > 0 && !a.q8;
+    const bool tail = TAIL && nblk > 0;
     const int nend = tail ? nblk - 1 : nblk;   // blocks run by the main loop
 
     auto tap_read = [&](int t) { return ((t / 3) * a.dilH * a.Pr + (t % 3) * a.dilW * 5) * 16; };
@@ -804,14 +802,31 @@ __global__ __launch_bounds__(64 * WGM * WGN) void conv_fp3x3_ring9_kernel(IgemmA
         // past the problem).  MODE 2: lanes walk pixels.
         const int kk0 = n0 + wn + (lane & 31);
         const int mrow0 = wm + 4 * (lane >> 5);
+        // bytes per output element: INT32 sums, or INT8 through the
+        // requantising epilogue (one byte store per value)
+        const int es = a.q8 ? 1 : 4;
+        const bool relu = a.q_relu != 0;
         // MODE 0 lane bases, computed once (the opaque asm keeps the compiler
         // from recomputing them at every store)
         int obase[FN];
 #pragma unroll
         for (int y = 0; y < FN; ++y) {
             const int kk = kk0 + y * 32;
-            obase[y] = kk < a.K ? ((m0 + mrow0) * a.pix_stride + kk * a.oK) * 4 : kOutOfRange;
+            obase[y] = kk < a.K ? ((m0 + mrow0) * a.pix_stride + kk * a.oK) * es : kOutOfRange;
             asm volatile("" : "+v"(obase[y]));
+        }
+        // requantisation of a lane's channel columns (lanes walk channels;
+        // lanes past K read channel K-1 and store nothing)
+        float qs[FN], qb[FN];
+#pragma unroll
+        for (int y = 0; y < FN; ++y) {
+            qs[y] = 0.0f;
+            qb[y] = 0.0f;
+            if (!PIX_J && a.q8) {
+                const int kc = min(kk0 + y * 32, a.K - 1);
+                qs[y] = a.q_scale ? a.q_scale[kc] : a.q_alpha;
+                qb[y] = a.q_bias ? a.q_bias[kc] : 0.0f;
+            }
         }
         // MODE 2 (lanes walk pixels): each lane's pixel offset per row block,
         // or -1 past the problem
@@ -828,28 +843,43 @@ __global__ __launch_bounds__(64 * WGM * WGN) void conv_fp3x3_ring9_kernel(IgemmA
                 asm volatile("" : "+v"(pixo[x]));
             }
         }
-        auto store_one = [&](auto modec, int x, int y, int v, int value) {
+        auto store_one = [&](auto modec, auto q8c, int x, int y, int v, int value) {
             constexpr int MODE = decltype(modec)::value;
+            constexpr bool Q8 = decltype(q8c)::value;
+            constexpr int ES = Q8 ? 1 : 4;
             const int rv = 8 * (v >> 2) + (v & 3);   // row of value v within its 32-row block
+            auto put = [&](int voff, int soff, float sc, float bi) {
+                if constexpr (Q8)
+                    __builtin_amdgcn_raw_buffer_store_b8((unsigned char)requant_i8(value, sc, bi, relu), out_rsrc,
+                                                         voff, soff, kOutStoreStream);
+                else
+                    __builtin_amdgcn_raw_buffer_store_b32(value, out_rsrc, voff, soff, kOutStoreStream);
+            };
             if constexpr (MODE == 0) {
-                __builtin_amdgcn_raw_buffer_store_b32(value, out_rsrc, obase[y], (x * 32 + rv) * a.pix_stride * 4,
-                                                      kOutStoreStream);
+                put(obase[y], (x * 32 + rv) * a.pix_stride * ES, qs[y], qb[y]);
             } else if constexpr (MODE == 1) {
                 const int kk = kk0 + y * 32;
                 const int r = mrow0 + x * 32 + rv;
                 int off = kOutOfRange;
                 if (a.pix_linear) {
                     const int m = m0 + r;
-                    off = (kk < a.K && m < a.M) ? (m * a.pix_stride + kk * a.oK) * 4 : kOutOfRange;
+                    off = (kk < a.K && m < a.M) ? (m * a.pix_stride + kk * a.oK) * ES : kOutOfRange;
                 } else {
                     const int po = out_row[r];
-                    off = (kk < a.K && po >= 0) ? (po + kk * a.oK) * 4 : kOutOfRange;
+                    off = (kk < a.K && po >= 0) ? (po + kk * a.oK) * ES : kOutOfRange;
                 }
-                __builtin_amdgcn_raw_buffer_store_b32(value, out_rsrc, off, 0, kOutStoreStream);
+                put(off, 0, qs[y], qb[y]);
             } else {
                 const int kk = n0 + wn + y * 32 + 4 * (lane >> 5) + rv;
-                const int off = (pixo[x] >= 0 && kk < a.K) ? (pixo[x] + kk * a.oK) * 4 : kOutOfRange;
-                __builtin_amdgcn_raw_buffer_store_b32(value, out_rsrc, off, 0, kOutStoreStream);
+                const int off = (pixo[x] >= 0 && kk < a.K) ? (pixo[x] + kk * a.oK) * ES : kOutOfRange;
+                float sc = 0.0f, bi = 0.0f;
+                if constexpr (Q8) {
+                    // lanes walk pixels: the channel changes with the value
+                    const int kc = min(kk, a.K - 1);
+                    sc = a.q_scale ? a.q_scale[kc] : a.q_alpha;
+                    bi = a.q_bias ? a.q_bias[kc] : 0.0f;
+                }
+                put(off, 0, sc, bi);
             }
         };
         // With one fragment per row block, odd steps accumulate into a second
@@ -857,7 +887,7 @@ __global__ __launch_bounds__(64 * WGM * WGN) void conv_fp3x3_ring9_kernel(IgemmA
         // FN accumulators, and alternating two sets keeps dependent MFMAs
         // 2 * FN issues apart.
         v16i acc2[FN];
-        auto run_tail = [&](auto modec) {
+        auto run_tail = [&](auto modec, auto q8c) {
 #pragma unroll
             for (int s2 = 0; s2 < D; ++s2)
                 read_step(s2);
@@ -895,7 +925,7 @@ __global__ __launch_bounds__(64 * WGM * WGN) void conv_fp3x3_ring9_kernel(IgemmA
 #pragma unroll
                     for (int e = lo; e < hi; ++e) {
                         const int f = (x - 1) * RBX + e / (16 * FN), y = e / 16 % FN;
-                        store_one(modec, f, y, e % 16, acc[f][y][e % 16]);
+                        store_one(modec, q8c, f, y, e % 16, acc[f][y][e % 16]);
                     }
                 }
                 __builtin_amdgcn_sched_barrier(0);
@@ -903,15 +933,21 @@ __global__ __launch_bounds__(64 * WGM * WGN) void conv_fp3x3_ring9_kernel(IgemmA
 #pragma unroll
             for (int e = 0; e < 16 * FN * RBX; ++e) {
                 const int f = (NRB - 1) * RBX + e / (16 * FN), y = e / 16 % FN;
-                store_one(modec, f, y, e % 16, acc[f][y][e % 16]);
+                store_one(modec, q8c, f, y, e % 16, acc[f][y][e % 16]);
             }
         };
-        if (PIX_J)
-            run_tail(std::integral_constant<int, 2>{});
-        else if (a.pix_linear && m0 + TM <= a.M)
-            run_tail(std::integral_constant<int, 0>{});
+        auto run_mode = [&](auto q8c) {
+            if (PIX_J)
+                run_tail(std::integral_constant<int, 2>{}, q8c);
+            else if (a.pix_linear && m0 + TM <= a.M)
+                run_tail(std::integral_constant<int, 0>{}, q8c);
+            else
+                run_tail(std::integral_constant<int, 1>{}, q8c);
+        };
+        if (a.q8)
+            run_mode(std::true_type{});
         else
-            run_tail(std::integral_constant<int, 1>{});
+            run_mode(std::false_type{});
     }
 }
 
