@@ -473,6 +473,13 @@ constexpr int allowed_first(int t)
     return n;
 }
 
+// Row blocks of the tail for a wave tile of FM 32-row fragments: two
+// fragments first, then one at a time, so the last row block (whose stores
+// no MFMAs hide) is a single fragment; with FM < 4 one fragment each.
+constexpr int tail_blocks(int FM) { return FM >= 4 ? FM - 1 : FM; }
+constexpr int tail_first(int FM, int x) { return FM >= 4 && x > 0 ? x + 1 : x; }
+constexpr int tail_len(int FM, int x) { return FM >= 4 && x == 0 ? 2 : 1; }
+
 }  // namespace fp9
 
 // 3x3 footprint kernel with a nine-slot filter ring (one slot per tap) and a
@@ -756,10 +763,12 @@ __global__ __launch_bounds__(64 * WGM * WGN) void conv_fp3x3_ring9_kernel(IgemmA
         store_tile_any<FM, FN, PIX_J>(a, acc, m0, n0, wm, wn, lane, out_row);
     } else {
         // ---- last block, row block by row block --------------------------
-        // A row block is RBX 32-row fragments of the wave's rows (two when the
-        // wave has four or more: each step then reads two image and FN filter
-        // fragments for 2 * FN products, which keeps the LDS read rate under
-        // what the CU serves).  Steps s = x * 18 + (t * 2 + ks): row block x,
+        // Row blocks of the wave's 32-row fragments (tail_first, tail_len):
+        // with four or more fragments the first row block takes two (each
+        // step then reads two image and FN filter fragments for 2 * FN
+        // products, which keeps the LDS read rate under what the CU serves)
+        // and the others one, so the last row block, whose stores are
+        // exposed, is small.  Steps s = x * 18 + (t * 2 + ks): row block x,
         // tap t, k-step ks.  The image and filter fragments of step s+D are
         // read during step s (all nine taps of the block are in the ring).
         // The stores of row block x-1 go out spread over the steps of row
@@ -776,20 +785,21 @@ __global__ __launch_bounds__(64 * WGM * WGN) void conv_fp3x3_ring9_kernel(IgemmA
         }
         wait_vm_lgkm0<0>();
         __builtin_amdgcn_s_barrier();
-        constexpr int RBX = FM >= 4 ? 2 : 1;
-        constexpr int NRB = FM / RBX;
+        constexpr int NRB = tail_blocks(FM);
+        constexpr int RBM = tail_len(FM, 0);   // fragments of the largest row block
         constexpr int NSTEP = kTaps * KS;
         constexpr int TOTAL = NRB * NSTEP;
-        constexpr int D = RBX == 1 ? 3 : 2;
+        constexpr int D = PIX_J ? 2 : 3;   // (three would spill with the pixel-lane epilogue)
         constexpr int NR = D + 1;   // the reads D steps ahead must not land in the slot in use
-        v4i ab[NR][RBX];
+        v4i ab[NR][RBM];
         v4i bb[NR][FN];
-        auto read_step = [&](int s2) {
-            const int x = s2 / NSTEP, r = s2 % NSTEP;
-            const int t = r / KS, ks = r % KS;
+        auto read_step = [&](auto sc) {
+            constexpr int s2 = decltype(sc)::value;
+            constexpr int x = s2 / NSTEP, r = s2 % NSTEP;
+            constexpr int t = r / KS, ks = r % KS;
 #pragma unroll
-            for (int i = 0; i < RBX; ++i)
-                ab[s2 % NR][i] = *(const v4i *)&fbuf[fb * FBUF + a_lane[x * RBX + i][ks] + tap_read(t)];
+            for (int i = 0; i < tail_len(FM, x); ++i)
+                ab[s2 % NR][i] = *(const v4i *)&fbuf[fb * FBUF + a_lane[tail_first(FM, x) + i][ks] + tap_read(t)];
 #pragma unroll
             for (int y = 0; y < FN; ++y)
                 bb[s2 % NR][y] = *(const v4i *)&ring[t * B_BYTES + b_lane[y][ks]];
@@ -882,28 +892,27 @@ __global__ __launch_bounds__(64 * WGM * WGN) void conv_fp3x3_ring9_kernel(IgemmA
                 put(off, 0, sc, bi);
             }
         };
-        // With one fragment per row block, odd steps accumulate into a second
+        // In a row block of one fragment, odd steps accumulate into a second
         // set (added in at the end of the row block): the row block has only
         // FN accumulators, and alternating two sets keeps dependent MFMAs
         // 2 * FN issues apart.
         v16i acc2[FN];
         auto run_tail = [&](auto modec, auto q8c) {
-#pragma unroll
-            for (int s2 = 0; s2 < D; ++s2)
-                read_step(s2);
+            static_for<0, D>([&](auto sc) { read_step(sc); });
             static_for<0, TOTAL>([&](auto sc) {
                 constexpr int st = decltype(sc)::value;
                 constexpr int x = st / NSTEP, r = st % NSTEP;
+                constexpr int L = tail_len(FM, x), F = tail_first(FM, x);
                 if constexpr (st + D < TOTAL)
-                    read_step(st + D);
+                    read_step(std::integral_constant<int, st + D>{});
 #pragma unroll
-                for (int i = 0; i < RBX; ++i)
+                for (int i = 0; i < L; ++i)
 #pragma unroll
                     for (int y = 0; y < FN; ++y) {
                         const v4i &fa = ab[st % NR][i];
                         const v4i &fbm = bb[st % NR][y];
-                        v16i &c0 = acc[x * RBX + i][y];
-                        if constexpr (RBX > 1 || r % 2 == 0) {
+                        v16i &c0 = acc[F + i][y];
+                        if constexpr (L > 1 || r % 2 == 0) {
                             c0 = PIX_J ? __builtin_amdgcn_mfma_i32_32x32x32_i8(fbm, fa, c0, 0, 0, 0)
                                        : __builtin_amdgcn_mfma_i32_32x32x32_i8(fa, fbm, c0, 0, 0, 0);
                         } else {
@@ -912,27 +921,28 @@ __global__ __launch_bounds__(64 * WGM * WGN) void conv_fp3x3_ring9_kernel(IgemmA
                                             : __builtin_amdgcn_mfma_i32_32x32x32_i8(fa, fbm, c, 0, 0, 0);
                         }
                     }
-                if constexpr (RBX == 1 && r == NSTEP - 1) {
+                if constexpr (L == 1 && r == NSTEP - 1) {
 #pragma unroll
                     for (int y = 0; y < FN; ++y)
-                        acc[x][y] += acc2[y];
+                        acc[F][y] += acc2[y];
                 }
-                // stores of the previous row block: 16 * FN * RBX values over
-                // 18 steps
+                // stores of the previous row block: 16 * FN values per
+                // fragment, spread over the 18 steps
                 if constexpr (x >= 1) {
-                    constexpr int NV = 16 * FN * RBX;
+                    constexpr int PF = tail_first(FM, x - 1);
+                    constexpr int NV = 16 * FN * tail_len(FM, x - 1);
                     constexpr int lo = r * NV / NSTEP, hi = (r + 1) * NV / NSTEP;
 #pragma unroll
                     for (int e = lo; e < hi; ++e) {
-                        const int f = (x - 1) * RBX + e / (16 * FN), y = e / 16 % FN;
+                        const int f = PF + e / (16 * FN), y = e / 16 % FN;
                         store_one(modec, q8c, f, y, e % 16, acc[f][y][e % 16]);
                     }
                 }
                 __builtin_amdgcn_sched_barrier(0);
             });
 #pragma unroll
-            for (int e = 0; e < 16 * FN * RBX; ++e) {
-                const int f = (NRB - 1) * RBX + e / (16 * FN), y = e / 16 % FN;
+            for (int e = 0; e < 16 * FN * tail_len(FM, NRB - 1); ++e) {
+                const int f = tail_first(FM, NRB - 1) + e / (16 * FN), y = e / 16 % FN;
                 store_one(modec, q8c, f, y, e % 16, acc[f][y][e % 16]);
             }
         };
