@@ -787,10 +787,28 @@ conv_i8_status_t make_plan(const Problem &pb, const void *x_ptr, const void *w_p
         const int64_t span = (pb.N - 1) * pb.y.s[0] + pl->y_img_span;
         const bool dense = pl->batch_chunk >= pb.N && span == pb.N * pb.K * pb.P * pb.Q;
         const int64_t tiles = ((M + c.tm - 1) / c.tm) * ((pb.K + c.tn - 1) / c.tn);
-        const int64_t want = tiles > 0 ? std::min<int64_t>((kCUs + tiles - 1) / tiles, pl->nstages / 16) : 1;
-        // with partial copies a split pays while some CU is idle (large-channel
-        // weight gradient, 144 tiles: 81 -> 78 us); with atomics only below
-        // half of the CUs
+        int64_t want = tiles > 0 ? std::min<int64_t>((kCUs + tiles - 1) / tiles, pl->nstages / 16) : 1;
+        if (dense && tiles > 0) {
+            // With partial copies: the split count that minimises the busiest
+            // CU's stages (workgroups share CUs evenly: ceil(tiles*k/CUs)
+            // workgroups of ceil(stages/k) stages each) plus the reduction
+            // (k copies read and the output written at ~5 TB/s, one launch).
+            // A split that leaves some CUs with two workgroups and others
+            // with one gains nothing over no split.
+            const double t_stage = (double)c.tm * c.tn * c.bk / (4.4e15 / 2 / kCUs) / c.eff;
+            double best_t = 0;
+            want = 1;
+            for (int64_t k = 1; k <= std::min<int64_t>(pl->nstages / 16, 32); ++k) {
+                const int64_t per_cu = (tiles * k + kCUs - 1) / kCUs;
+                const int64_t st = (pl->nstages + k - 1) / k;
+                const double t = (double)per_cu * st * t_stage + (k > 1 ? (k + 1) * (double)span * 4 / 5e12 + 2.5e-6 : 0);
+                if (k == 1 || t < best_t * (1 - 1e-9)) {
+                    best_t = t;
+                    want = k;
+                }
+            }
+        }
+        // with atomics a split pays only below half of the CUs busy
         if (tiles < (dense ? kCUs : kCUs / 2) && want > 1) {
             pl->kchunk = (pl->nstages + want - 1) / want;
             pl->ksplit = (pl->nstages + pl->kchunk - 1) / pl->kchunk;
