@@ -695,11 +695,8 @@ conv_i8_status_t make_plan(const Problem &pb, const void *x_ptr, const void *w_p
             // footprint that fits its buffers
             if (pb.R != 3 || pb.S != 3 || cc % 4 != 0 || Hp >= (1 << 20) || Wf >= (1 << 20))
                 continue;
-            // footprint offsets are formed with 24-bit multiplies (the image
-            // step sN - Hp sH is multiplied by 0 when a launch holds one image)
-            const int64_t fE = pl->xsN - Hp * pl->xsH;
-            if (pl->xsH < 0 || pl->xsH >= (1 << 23) || pl->xsW < 0 || pl->xsW >= (1 << 23) ||
-                (M > pb.P * pb.Q && (fE <= -(1 << 23) || fE >= (1 << 23))))
+            // the nine-slot kernel forms column offsets with a 24-bit multiply
+            if (pl->xsW < 0 || pl->xsW >= (1 << 23))
                 continue;
             const int64_t fmax = max_footprint(M, pb.P * pb.Q, pb.Q, Hp, Wf, pb.str[0],
                                                (pb.R - 1) * pb.dil[0], c.tm);

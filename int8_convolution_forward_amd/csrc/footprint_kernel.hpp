@@ -473,6 +473,9 @@ constexpr int allowed_first(int t)
     return n;
 }
 
+// footprint row outside the image or past the footprint (prologue table)
+constexpr int kRowOutside = -0x7fffffff - 1;
+
 // Row blocks of the tail for a wave tile of FM 32-row fragments: two
 // fragments first, then one at a time, so the last row block (whose stores
 // no MFMAs hide) is a single fragment; with FM < 4 one fragment each.
@@ -516,6 +519,7 @@ __global__ __launch_bounds__(64 * WGM * WGN) void conv_fp3x3_ring9_kernel(IgemmA
     __shared__ __attribute__((aligned(1024))) int8_t ring[kTaps * B_BYTES];
     __shared__ __attribute__((aligned(1024))) int8_t fbuf[2 * FBUF];
     __shared__ int out_row[PIX_J ? 1 : TM];
+    __shared__ int frow_off[64 * NW];   // byte offset of each footprint row (prologue)
 
     // every argument the prologue needs, loaded in one round trip (left to
     // itself the compiler loads some of them only where they are first used,
@@ -591,31 +595,44 @@ __global__ __launch_bounds__(64 * WGM * WGN) void conv_fp3x3_ring9_kernel(IgemmA
     // column fc and 16-byte piece j of that row; footprint row fr is padded
     // row hr = hp_a + fr counted from image n_a, i.e. row h of image n_a + dn
     // with hr = dn * Hp + h + padH.  Its bytes start at
-    //   (n_a + dn) sN + h sH + (fc - padW) sW + 16 j
-    //   = base + dn (sN - Hp sH) + fr sH + fc sW + 16 j
-    // with the uniform base = n_a sN + (hp_a - padH) sH - padW sW.  The
-    // planner keeps sH, sW, the footprint's rows and columns (below 2^20)
-    // and, when a launch holds several images, sN - Hp sH within 23 bits (dn
-    // is 0 otherwise), so the products are 24-bit multiplies.
-    const int fbase = n_a * a.sN + (hp_a - a.padH) * a.sH - a.padW * a.sW;
-    const int fE = a.sN - a.Hp * a.sH;
+    //   (n_a + dn) sN + h sH + (fc - padW) sW + 16 j.
+    // Thread t first forms the row part for footprint row t (or marks a row
+    // past the footprint or outside the image) in LDS; the slots then need
+    // only their column and piece, and the chains stay short: the address
+    // arithmetic of all groups, and the table reads, go out before the first
+    // footprint load, each group's load right after its last few operations.
+    // (The slots span fewer than 64 * NW rows: Pr >= 15.)  The planner keeps
+    // sW below 2^23, so fc * sW is a 24-bit multiply.
+    {
+        const int t = tid;
+        const int hr = hp_a + t;
+        const int dn = fdiv(hr, a.Hp, a.inv_hp);
+        const int h = hr - dn * a.Hp - a.padH;
+        frow_off[t] = (t < frows && (unsigned)h < (unsigned)a.H) ? (n_a + dn) * a.sN + h * a.sH - a.padW * a.sW
+                                                                 : kRowOutside;
+    }
+    // the table is written (the filter loads of (0, 0) stay in flight)
+    wait_vm_lgkm0<BL>();
+    __builtin_amdgcn_s_barrier();
+    int fcg[NG], jg[NG], rog[NG];
 #pragma unroll
     for (int g = 0; g < NG; ++g) {
         const int slot = g * (GB / 16) + wave * 64 + lane;
         const int fr = fdiv(slot, a.Pr, a.inv_pr);
         const int rem = slot - __mul24(fr, a.Pr);
-        const int fc = (int)(__umul24((unsigned)rem, 52429u) >> 18);   // rem / 5 (rem < 2^16)
-        const int j = rem - fc * 5;
-        const int hr = hp_a + fr;
-        const int dn = fdiv(hr, a.Hp, a.inv_hp);
-        const int h = hr - __mul24(dn, a.Hp) - a.padH;
-        const int w = fc - a.padW;
+        fcg[g] = (int)(__umul24((unsigned)rem, 52429u) >> 18);   // rem / 5 (rem < 2^16)
+        jg[g] = rem - fcg[g] * 5;
+        rog[g] = frow_off[min(fr, 64 * NW - 1)];
+    }
+#pragma unroll
+    for (int g = 0; g < NG; ++g) {
         // slots past the footprint's rows, the fifth piece of a pixel and
         // the row padding are never read: they are skipped (or filled with
         // whatever lies there); rows and columns outside the image read
         // zeros
-        const bool ok = (j < 4) & (fr < frows) & ((unsigned)h < (unsigned)a.H) & ((unsigned)w < (unsigned)a.W);
-        foff[g] = ok ? fbase + __mul24(dn, fE) + __mul24(fr, a.sH) + __mul24(fc, a.sW) + j * 16 : kOutOfRange;
+        const int w = fcg[g] - a.padW;
+        const bool ok = (rog[g] != kRowOutside) & (jg[g] < 4) & ((unsigned)w < (unsigned)a.W);
+        foff[g] = ok ? rog[g] + __mul24(fcg[g], a.sW) + jg[g] * 16 : kOutOfRange;
         dma_piece(0, g);
         __builtin_amdgcn_sched_barrier(0);
     }

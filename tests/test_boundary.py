@@ -170,26 +170,25 @@ def test_plans(name, repack_image, repack_filter, order):
 
 
 def test_footprint_offsets_fit_24_bits(monkeypatch):
-    """The 3x3 footprint kernels form image offsets with 24-bit products: a
-    launch over several images whose image step, net of the padded rows,
-    leaves 23 bits is planned on another kernel; one image per launch never
-    takes that step."""
+    """The 3x3 footprint kernels form column offsets with a 24-bit product:
+    a W stride of 2^23 bytes or more is planned on another kernel; image
+    steps of any size across a launch's images are fine."""
     monkeypatch.setenv("CONV_I8_TILE", "f128x128")
     N, C, H, W, K = 2, 64, 9, 10, 40
     cl = wl.channels_last_strides((N, C, H, W))
     w = ci8.desc((K, C, 3, 3), wl.channels_last_strides((K, C, 3, 3)), 1)
     y = ci8.desc((N, K, H, W), wl.channels_last_strides((N, K, H, W)), 2)
 
-    def fields(sn):
-        x = ci8.desc((N, C, H, W), (sn,) + tuple(cl[1:]), 1)
+    def fields(strides):
+        x = ci8.desc((N, C, H, W), strides, 1)
         return ci8.plan_fields(ci8.conv_fprop_i8_plan(x, w, y, 1, 1, 1, 1))
 
-    dense = fields(cl[0])
+    dense = fields(cl)
     assert dense["tile"] == "f128x128" and dense["batch_chunk"] == "2"
-    far = fields(1 << 24)
-    assert far["batch_chunk"] == "2" and far["kernel"] == "im2col"
-    apart = fields(1 << 31)
-    assert apart["batch_chunk"] == "1" and apart["tile"] == "f128x128"
+    far = fields((1 << 24,) + tuple(cl[1:]))
+    assert far["batch_chunk"] == "2" and far["tile"] == "f128x128"
+    wide = fields((H * W << 23, 1, W << 23, 1 << 23))  # W stride 2^23 bytes
+    assert wide["kernel"] != "footprint"
 
 
 def _tuned_entries():
