@@ -518,6 +518,9 @@ RepackJob repack_job(const T4 &t, const int8_t *src, int8_t *dst, int64_t Cp, in
     j.tiles_x = (int)tx;
     j.tiles_c = (int)tc;
     j.tiles = tiles <= kI32Max ? (int)tiles : 0;
+    j.d_tc = make_divisor(std::max<int64_t>(tc, 1));
+    j.d_tx = make_divisor(std::max<int64_t>(tx, 1));
+    j.d_o = make_divisor(std::max<int64_t>(j.mode == kRepackAFast ? X : Y, 1));
     return j;
 }
 

@@ -21,6 +21,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "kernel_common.hpp"
+
 namespace convi8 {
 
 enum RepackMode : int {
@@ -38,6 +40,7 @@ struct RepackJob {
     int mode;
     int tiles_x, tiles_c;            // 64-wide tiles along x (along a for kRepackAFast) and Cp
     int tiles;                       // A * Y * tiles_x * tiles_c
+    Divisor d_tc, d_tx, d_o;         // tiles_c, tiles_x, and X (kRepackAFast) or Y
     int8_t *dst;                     // packed [A][Y][X][Cp]
 };
 
@@ -76,12 +79,15 @@ __global__ __launch_bounds__(256) void repack_to_channels_last_kernel(RepackArgs
 
     const int tid = threadIdx.x;
     const bool af = j.mode == kRepackAFast;
-    const int ct = (int)(bid % (unsigned)j.tiles_c);
-    const int pt = (int)((bid / (unsigned)j.tiles_c) % (unsigned)j.tiles_x);
-    const int outer = (int)(bid / ((unsigned)j.tiles_c * (unsigned)j.tiles_x));
+    // tile index -> (outer, x-tile, c-tile) and outer -> (o_hi, o_lo) with
+    // the host's magic-number divisors (no division chain before the loads)
+    const int q1 = udiv((int)bid, j.d_tc);
+    const int ct = (int)bid - q1 * j.tiles_c;
+    const int outer = udiv(q1, j.d_tx);
+    const int pt = q1 - outer * j.tiles_x;
     // x-tiles: outer = (a, y), the tile walks x; a-tiles: outer = (y, x), it walks a
-    const int o_hi = af ? outer / j.X : outer / j.Y;
-    const int o_lo = af ? outer - o_hi * j.X : outer - o_hi * j.Y;
+    const int o_hi = udiv(outer, j.d_o);
+    const int o_lo = outer - o_hi * (af ? j.X : j.Y);
     const int ai = af ? 0 : o_hi, yi = af ? o_hi : o_lo, xi = af ? o_lo : 0;
     const int x0 = pt * 64, c0 = ct * 64;    // x0: first x (or first a) of the tile
     const int xn = min(64, (af ? j.A : j.X) - x0);  // positions in this tile
@@ -125,18 +131,36 @@ __global__ __launch_bounds__(256) void repack_to_channels_last_kernel(RepackArgs
         }
         __syncthreads();
         if (out_ok) {
-            // offset of line l's first byte within its first aligned vector:
-            // only the low four address bits matter
+            // The offset of line l's first byte within its first aligned
+            // vector (only the low four address bits matter) steps by the
+            // line stride from one line to the next, and the byte of channel
+            // i sits at a fixed distance from the previous one.  All sixteen
+            // reads stay inside their lines (the lines past C hold whatever
+            // the buffer held), so they go out unconditionally, back to back,
+            // and the bytes past C are masked off afterwards.
             const unsigned b0 = (unsigned)(uintptr_t)line0, ls = (unsigned)lstride;
+            if (xf) {
+                // line cq*16 + i, position xl
+                unsigned lead = (b0 + (unsigned)(cq * 16) * ls) & 15u;
+                const int8_t *p = &raw[cq * 16 * kRepackLine + xl * step];
 #pragma unroll
-            for (int i = 0; i < 16; ++i) {
-                const int cl = cq * 16 + i;
-                if (cl < cn) {
-                    const int l = xf ? cl : xl;
-                    const int k = xf ? xl : cl;
-                    const int lead = (int)((b0 + (unsigned)l * ls) & 15u);
-                    v[i >> 2] |= (int)(uint8_t)raw[l * kRepackLine + lead + k * step] << (8 * (i & 3));
+                for (int i = 0; i < 16; ++i) {
+                    v[i >> 2] |= (int)(uint8_t)p[i * kRepackLine + (int)lead] << (8 * (i & 3));
+                    lead = (lead + ls) & 15u;
                 }
+            } else {
+                // line xl, position cq*16 + i
+                const unsigned lead = (b0 + (unsigned)xl * ls) & 15u;
+                const int8_t *p = &raw[xl * kRepackLine + (int)lead + cq * 16 * step];
+#pragma unroll
+                for (int i = 0; i < 16; ++i)
+                    v[i >> 2] |= (int)(uint8_t)p[i * step] << (8 * (i & 3));
+            }
+            const int nvalid = min(max(cn - cq * 16, 0), 16);   // real channels of this vector
+#pragma unroll
+            for (int w = 0; w < 4; ++w) {
+                const int nb = min(max(nvalid - 4 * w, 0), 4);
+                v[w] &= nb == 4 ? -1 : (int)((1u << (8 * nb)) - 1u);
             }
         }
     }
