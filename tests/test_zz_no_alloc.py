@@ -78,3 +78,22 @@ def test_noalloc_refuses_problems_beyond_its_scratch(ci8):
     assert e.value.name == "CONV_I8_ERR_SCRATCH"
     torch.cuda.synchronize()
     assert bool((y == 7).all())
+
+
+def test_noalloc_without_workspace(ci8):
+    """Problems that need no workspace (operands read in place: the tiny
+    layer on the direct kernel, the large-channel layer on the 3x3 kernel)
+    go through the allocation-free entry unchanged."""
+    for name in ("tiny_5x5_r3", "large_channel_n64_c512_14"):
+        c = wl.case(name)
+        d = wl.make_inputs(c, c.seed_base + 3)
+        xg = wl.to_device(d["x_storage"], c.image, _dev())[1]
+        wg = wl.to_device(d["w_storage"], c.filter, _dev())[1]
+        assert ci8.conv_fprop_i8_workspace_size(xg, wg, ci8.desc(c.out.dims, c.out.strides, ci8.DT_INT32),
+                                                c.pre, c.post, c.stride, c.dilation) == 0
+        yn = wl.alloc_output(c.out, _dev(), fill=-7)[1]
+        print(f"[gpu] noalloc without workspace: {name}", flush=True)
+        ci8.conv_fprop_i8_noalloc(xg, wg, yn, c.pre, c.post, c.stride, c.dilation)
+        torch.cuda.synchronize()
+        ref = oracle.conv_fprop(d["x"], d["w"], c.pre, c.post, c.stride, c.dilation)
+        assert torch.equal(yn.cpu(), ref), name
