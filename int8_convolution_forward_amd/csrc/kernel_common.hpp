@@ -108,11 +108,10 @@ __device__ __forceinline__ int requant_i8(int acc, float s, float b, bool relu)
     // a NaN (an infinite scale or bias meeting a zero or opposite term) is
     // written as 0; infinities saturate below
     v = __builtin_isnan(v) ? 0.0f : v;
-    if (relu)
-        v = __builtin_fmaxf(v, 0.0f);
-    v = __builtin_rintf(v);
-    v = __builtin_fminf(__builtin_fmaxf(v, -128.0f), 127.0f);
-    return (int)v;
+    // ReLU and the clamp in one median: rounding first gives the same
+    // integer (max(rint(v), 0) and rint(max(v, 0)) differ only in the sign
+    // of a zero)
+    return (int)__builtin_amdgcn_fmed3f(__builtin_rintf(v), relu ? 0.0f : -128.0f, 127.0f);
 }
 
 // 4x4 byte transpose within each quad of lanes: byte u of lane t's result is
