@@ -216,19 +216,27 @@ __global__ __launch_bounds__(64 * WGM * WGN) void conv_igemm_kernel(IgemmArgs a)
     // One stage: the MFMAs of stage `it` (fragments in registers `buf`) are
     // interleaved with the loads of stage it+NS into the slot stage `it` has
     // just vacated and the fragment reads of stage it+1 into `buf^1`.
+    // The first PRE MFMAs need only this wave's registers: they go out
+    // before the wait and the barrier, so the matrix unit has work while the
+    // waves line up; the loads and reads ride on the others.
     constexpr int NOTHER = LPS + NRD;
+    constexpr int PRE = NMF / 4;
     int cur_slot = 0;
     auto body = [&](int buf) {
+#pragma unroll
+        for (int t = 0; t < PRE; ++t)
+            mfma_one(buf, t);
+        __builtin_amdgcn_sched_barrier(0);
         wait_vm_lgkm0<(NS - 2) * LPS>();  // own loads of stage it+1 landed; frag[buf] read
         __builtin_amdgcn_s_barrier();       // all waves: stage it+1 visible, slot it%NS free
         __builtin_amdgcn_sched_barrier(0);
         begin_stage(cur_slot);
         const int nslot = cur_slot + 1 == NS ? 0 : cur_slot + 1;
 #pragma unroll
-        for (int t = 0; t < NMF; ++t) {
+        for (int t = PRE; t < NMF; ++t) {
             mfma_one(buf, t);
 #pragma unroll
-            for (int o = t * NOTHER / NMF; o < (t + 1) * NOTHER / NMF; ++o) {
+            for (int o = (t - PRE) * NOTHER / (NMF - PRE); o < (t - PRE + 1) * NOTHER / (NMF - PRE); ++o) {
                 if (o < LPS)
                     dma_one(o);
                 else
