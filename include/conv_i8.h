@@ -504,6 +504,25 @@ conv_i8_status_t conv_wgrad_i8(const conv_i8_desc_t *image, const void *image_pt
                                void *stream);
 
 /*
+ * Counterpart of conv_fprop_i8_plan for the weight gradient (cuDNN
+ * "Convolutions" page, section "Convolution Wgrad"; the plan list of the
+ * cuDNN frontend tutorial page, autotuning paragraph): the description of
+ * the one forward call conv_wgrad_i8_ws makes (tile, split of the N*P*Q
+ * reduction, workspace), or "empty" for a dw with no elements.  Arguments
+ * and errors as conv_wgrad_i8_workspace_size; writes at most `len` bytes
+ * including the terminating NUL.  Host-only.
+ */
+conv_i8_status_t conv_wgrad_i8_plan(const conv_i8_desc_t *image, const void *image_ptr,
+                                    const conv_i8_desc_t *loss, const void *loss_ptr,
+                                    const conv_i8_desc_t *dw,
+                                    const int64_t pre_padding[2],
+                                    const int64_t post_padding[2],
+                                    const int64_t stride[2],
+                                    const int64_t dilation[2],
+                                    int32_t mode,
+                                    char *buf, size_t len);
+
+/*
  * Static string naming a status code.  The forum thread's answer post traces
  * the question's wrong output to a descriptor mistake (strides that do not
  * match the NCHW layout); each refusal above is reported by name instead of

@@ -32,7 +32,7 @@ __all__ = [
     "conv_fprop_i8_requant_workspace_size", "Requant", "conv_fprop_i8_ex_ws",
     "conv_fprop_i8_ex_workspace_size", "conv_fprop_i8_mode", "conv_dgrad_i8",
     "conv_dgrad_i8_ws", "conv_dgrad_i8_workspace_size", "conv_dgrad_i8_plain", "conv_wgrad_i8",
-    "conv_wgrad_i8_ws", "conv_wgrad_i8_workspace_size", "conv_wgrad_i8_plain", "MODE_CROSS_CORRELATION",
+    "conv_wgrad_i8_ws", "conv_wgrad_i8_workspace_size", "conv_wgrad_i8_plain", "conv_wgrad_i8_plan", "MODE_CROSS_CORRELATION",
     "MODE_CONVOLUTION",
     "status_string", "LIB_PATH", "DT_INT8", "DT_INT32", "MAX_REDUCTION", "lib",
 ]
@@ -115,13 +115,16 @@ lib.conv_wgrad_i8_workspace_size.argtypes = [_DP, _P, _DP, _P, _DP, _V2, _V2, _V
 lib.conv_wgrad_i8_ws.argtypes = [_DP, _P, _DP, _P, _DP, _P, _V2, _V2, _V2, _V2, ctypes.c_int32, _P,
                                  ctypes.c_size_t, _P]
 lib.conv_wgrad_i8.argtypes = [_DP, _P, _DP, _P, _DP, _P, _V2, _V2, _V2, _V2, ctypes.c_int32, _P]
+lib.conv_wgrad_i8_plan.argtypes = [_DP, _P, _DP, _P, _DP, _V2, _V2, _V2, _V2, ctypes.c_int32,
+                                   ctypes.c_char_p, ctypes.c_size_t]
 lib.conv_i8_status_string.argtypes = [ctypes.c_int]
 lib.conv_i8_status_string.restype = ctypes.c_char_p
 for _f in ("conv_fprop_i8_out_dims", "conv_fprop_i8_workspace_size", "conv_fprop_i8_ws",
            "conv_fprop_i8", "conv_fprop_i8_noalloc", "conv_fprop_i8_plan", "conv_fprop_i8_requant_workspace_size",
            "conv_fprop_i8_requant_ws", "conv_fprop_i8_requant", "conv_fprop_i8_ex_workspace_size",
            "conv_fprop_i8_ex_ws", "conv_dgrad_i8_workspace_size", "conv_dgrad_i8_ws", "conv_dgrad_i8",
-           "conv_wgrad_i8_workspace_size", "conv_wgrad_i8_ws", "conv_wgrad_i8", "conv_i8_tile_names", "conv_i8_mfma_ceiling"):
+           "conv_wgrad_i8_workspace_size", "conv_wgrad_i8_ws", "conv_wgrad_i8", "conv_wgrad_i8_plan",
+           "conv_i8_tile_names", "conv_i8_mfma_ceiling"):
     getattr(lib, _f).restype = ctypes.c_int
 
 
@@ -546,6 +549,18 @@ def conv_wgrad_i8_workspace_size(x, dy, dw, pre_padding=0, post_padding=0, strid
         ctypes.byref(_as_desc(x)), xp, ctypes.byref(_as_desc(dy)), dp, ctypes.byref(_as_desc(dw)),
         pre, post, st, dl, int(mode), ctypes.byref(n)))
     return int(n.value)
+
+
+def conv_wgrad_i8_plan(x, dy, dw, pre_padding=0, post_padding=0, stride=1, dilation=1,
+                       padding=None, mode: int = 0) -> str:
+    pre, post, st, dl = _params(pre_padding, post_padding, stride, dilation, padding)
+    buf = ctypes.create_string_buffer(512)
+    xp = _ptr(x) if isinstance(x, torch.Tensor) else None
+    dp = _ptr(dy) if isinstance(dy, torch.Tensor) else None
+    _check(lib.conv_wgrad_i8_plan(
+        ctypes.byref(_as_desc(x)), xp, ctypes.byref(_as_desc(dy)), dp, ctypes.byref(_as_desc(dw)),
+        pre, post, st, dl, int(mode), buf, 512))
+    return buf.value.decode()
 
 
 def conv_wgrad_i8_ws(x: torch.Tensor, dy: torch.Tensor, dw: torch.Tensor,

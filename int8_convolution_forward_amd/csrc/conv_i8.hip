@@ -349,26 +349,37 @@ constexpr int kNumTiles = sizeof(kTiles) / sizeof(kTiles[0]);
 // tune module; a forward problem that matches an entry exactly takes its tile
 // ahead of the cost model (a forced CONV_I8_TILE still wins).
 struct TunedTile {
+    int op;            // 0: forward convolution, 1: weight gradient (its one forward call)
     int64_t N, C, H, W, K, R, S, pre_h, pre_w, post_h, post_w, str_h, str_w, dil_h, dil_w;
-    int lanes;         // output lanes: 0 walk channels, 1 walk pixels
+    int lanes;         // forward: output lanes walk channels (0) or pixels (1);
+                       // weight gradient: dW channel-innermost (0) or not (1)
     const char *tile;  // nullptr ends the table
 };
 const TunedTile kTuned[] = {
 #include "tuned_tiles.inc"
-    {0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, nullptr},
+    {0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, nullptr},
 };
+
+// The table's tile for a problem (its own dims, padding, stride and dilation
+// as the caller gave them), or nullptr.
+const char *tuned_lookup(int op, const int64_t d[7], const int64_t *pre, const int64_t *post,
+                         const int64_t *str, const int64_t *dil, int lanes)
+{
+    for (const TunedTile *t = kTuned; t->tile; ++t)
+        if (t->op == op && t->N == d[0] && t->C == d[1] && t->H == d[2] && t->W == d[3] && t->K == d[4] &&
+            t->R == d[5] && t->S == d[6] && t->pre_h == pre[0] && t->pre_w == pre[1] && t->post_h == post[0] &&
+            t->post_w == post[1] && t->str_h == str[0] && t->str_w == str[1] && t->dil_h == dil[0] &&
+            t->dil_w == dil[1] && t->lanes == lanes)
+            return t->tile;
+    return nullptr;
+}
 
 const char *tuned_tile(const Problem &pb, bool pix_j)
 {
     if (pb.flip_out || pb.split_ok)
         return nullptr;
-    for (const TunedTile *t = kTuned; t->tile; ++t)
-        if (t->N == pb.N && t->C == pb.C && t->H == pb.H && t->W == pb.W && t->K == pb.K && t->R == pb.R &&
-            t->S == pb.S && t->pre_h == pb.pre[0] && t->pre_w == pb.pre[1] && t->post_h == pb.post[0] &&
-            t->post_w == pb.post[1] && t->str_h == pb.str[0] && t->str_w == pb.str[1] && t->dil_h == pb.dil[0] &&
-            t->dil_w == pb.dil[1] && t->lanes == (pix_j ? 1 : 0))
-            return t->tile;
-    return nullptr;
+    const int64_t d[7] = {pb.N, pb.C, pb.H, pb.W, pb.K, pb.R, pb.S};
+    return tuned_lookup(0, d, pb.pre, pb.post, pb.str, pb.dil, pix_j ? 1 : 0);
 }
 
 // Division by a launch-invariant divisor d >= 1 for dividends below 2^31:
@@ -524,7 +535,8 @@ RepackJob repack_job(const T4 &t, const int8_t *src, int8_t *dst, int64_t Cp, in
     return j;
 }
 
-conv_i8_status_t make_plan(const Problem &pb, const void *x_ptr, const void *w_ptr, Plan *pl)
+conv_i8_status_t make_plan(const Problem &pb, const void *x_ptr, const void *w_ptr, Plan *pl,
+                           const char *tuned_override = nullptr)
 {
     pl->repack_x = !direct_ok(pb.x, x_ptr);
     pl->repack_w = !direct_ok(pb.w, w_ptr);
@@ -652,7 +664,7 @@ conv_i8_status_t make_plan(const Problem &pb, const void *x_ptr, const void *w_p
     int best = -1;
     double best_cost = 0;
     const char *forced = env_tile();
-    const char *tuned = forced ? nullptr : tuned_tile(pb, pl->pix_j);
+    const char *tuned = forced ? nullptr : tuned_override ? tuned_override : tuned_tile(pb, pl->pix_j);
     int tuned_idx = -1;
     const double macs = (double)pb.N * pb.K * pb.P * pb.Q * pb.C * pb.R * pb.S;
     const bool direct_fits = macs <= kDirectMaxMacs && pb.C * RS <= kDirectMaxCRS;
@@ -1125,7 +1137,7 @@ conv_i8_status_t prepare(const conv_i8_desc_t *image, const void *image_ptr,
                          const int64_t *stride, const int64_t *dil, Problem *pb, Plan *pl,
                          int32_t out_dtype = CONV_I8_DT_INT32,
                          int32_t mode = CONV_I8_MODE_CROSS_CORRELATION, bool flip_out = false,
-                         bool split_ok = false)
+                         bool split_ok = false, const char *tuned = nullptr)
 {
     // The plan does not depend on the output dtype (it works in elements) nor
     // on the mode (the kernels read the taps in either order).
@@ -1141,9 +1153,10 @@ conv_i8_status_t prepare(const conv_i8_desc_t *image, const void *image_ptr,
     key.x_direct = direct_ok(pb->x, image_ptr) ? 1 : 0;
     key.w_direct = direct_ok(pb->w, filter_ptr) ? 1 : 0;
     const char *forced = env_tile();
-    if (forced)
-        strncpy(key.tile, forced, sizeof key.tile - 1);
-    const bool cache = getenv("CONV_I8_COST") == nullptr && (!forced || strlen(forced) < sizeof key.tile - 1);
+    const char *name = forced ? forced : tuned;   // a tile chosen outside the planner
+    if (name)
+        strncpy(key.tile, name, sizeof key.tile - 1);
+    const bool cache = getenv("CONV_I8_COST") == nullptr && (!name || strlen(name) < sizeof key.tile - 1);
     if (cache) {
         std::lock_guard<std::mutex> lock(g_plan_mutex);
         for (int i = 0; i < g_plan_count; ++i)
@@ -1152,7 +1165,7 @@ conv_i8_status_t prepare(const conv_i8_desc_t *image, const void *image_ptr,
                 return CONV_I8_OK;
             }
     }
-    st = make_plan(*pb, image_ptr, filter_ptr, pl);
+    st = make_plan(*pb, image_ptr, filter_ptr, pl, tuned);
     if (st == CONV_I8_OK && cache) {
         std::lock_guard<std::mutex> lock(g_plan_mutex);
         g_plan_keys[g_plan_next] = key;
@@ -1224,14 +1237,14 @@ conv_i8_status_t entry_workspace_size(const conv_i8_desc_t *image, const void *i
                                       const int64_t *post, const int64_t *stride,
                                       const int64_t *dil, int32_t out_dtype, int32_t mode,
                                       size_t *workspace_bytes, bool flip_out = false,
-                                      bool split_ok = false)
+                                      bool split_ok = false, const char *tuned = nullptr)
 {
     if (!workspace_bytes)
         return CONV_I8_ERR_NULL;
     Problem pb;
     Plan pl;
     conv_i8_status_t st = prepare(image, image_ptr, filter, filter_ptr, out, pre, post, stride,
-                                  dil, &pb, &pl, out_dtype, mode, flip_out, split_ok);
+                                  dil, &pb, &pl, out_dtype, mode, flip_out, split_ok, tuned);
     if (st != CONV_I8_OK)
         return st;
     *workspace_bytes = pb.y.elems() == 0 || pb.C == 0 ? 0 : pl.ws_bytes;
@@ -1247,12 +1260,12 @@ conv_i8_status_t entry_run(const conv_i8_desc_t *image, const void *image_ptr,
                            const int64_t *post, const int64_t *stride, const int64_t *dil,
                            int32_t out_dtype, int32_t mode, const conv_i8_requant_t *rq, bool alloc,
                            void *workspace, size_t workspace_bytes, void *stream,
-                           bool flip_out = false, bool split_ok = false)
+                           bool flip_out = false, bool split_ok = false, const char *tuned = nullptr)
 {
     Problem pb;
     Plan pl;
     conv_i8_status_t st = prepare(image, image_ptr, filter, filter_ptr, out, pre, post, stride,
-                                  dil, &pb, &pl, out_dtype, mode, flip_out, split_ok);
+                                  dil, &pb, &pl, out_dtype, mode, flip_out, split_ok, tuned);
     if (st != CONV_I8_OK)
         return st;
     if (out_dtype == CONV_I8_DT_INT8 && (st = check_requant(rq)) != CONV_I8_OK)
@@ -1759,6 +1772,14 @@ struct WgradProblem {
     int64_t pre[2], post[2], str[2], dil[2];
 };
 
+// The measured table's tile for a weight gradient, keyed by the gradient's
+// own problem (the forward layer's dims and parameters, dW's layout).
+const char *tuned_wgrad_tile(const WgradProblem &wp)
+{
+    const int64_t d[7] = {wp.N, wp.C, wp.H, wp.W, wp.K, wp.R, wp.S};
+    return tuned_lookup(1, d, wp.pre, wp.post, wp.str, wp.dil, wp.dw.s[1] == 1 ? 0 : 1);
+}
+
 conv_i8_status_t wgrad_analyze(const conv_i8_desc_t *image, const conv_i8_desc_t *loss,
                                const conv_i8_desc_t *dw, const int64_t *pre, const int64_t *post,
                                const int64_t *stride, const int64_t *dil, int32_t mode,
@@ -1871,6 +1892,7 @@ conv_i8_status_t wgrad_entry(const conv_i8_desc_t *image, const void *image_ptr,
             *ws_size = 0;
         return CONV_I8_OK;
     }
+    const char *tuned = tuned_wgrad_tile(wp);
     if (size_only)
         return wgrad_call(wp, image_ptr, loss_ptr, nullptr, mode,
                           [&](const conv_i8_desc_t *i, const void *x, const conv_i8_desc_t *f,
@@ -1881,7 +1903,7 @@ conv_i8_status_t wgrad_entry(const conv_i8_desc_t *image, const void *image_ptr,
                               return entry_workspace_size(i, x, f, w, o, a, b, c, d,
                                                           CONV_I8_DT_INT32,
                                                           CONV_I8_MODE_CROSS_CORRELATION, ws_size,
-                                                          fl, true);
+                                                          fl, true, tuned);
                           });
     return wgrad_call(wp, image_ptr, loss_ptr, dw_ptr, mode,
                       [&](const conv_i8_desc_t *i, const void *x, const conv_i8_desc_t *f,
@@ -1892,7 +1914,7 @@ conv_i8_status_t wgrad_entry(const conv_i8_desc_t *image, const void *image_ptr,
                           // for an output with gaps, that add into it atomically)
                           return entry_run(i, x, f, w, o, y, a, b, c, d, CONV_I8_DT_INT32,
                                            CONV_I8_MODE_CROSS_CORRELATION, nullptr, alloc,
-                                           workspace, workspace_bytes, stream, fl, true);
+                                           workspace, workspace_bytes, stream, fl, true, tuned);
                       });
 }
 
@@ -2091,6 +2113,40 @@ conv_i8_status_t conv_dgrad_i8(const conv_i8_desc_t *loss, const void *loss_ptr,
 {
     return dgrad_entry(loss, loss_ptr, filter, filter_ptr, dx, dx_ptr, pre_padding, post_padding,
                        stride, dilation, mode, true, nullptr, 0, stream);
+}
+
+conv_i8_status_t conv_wgrad_i8_plan(const conv_i8_desc_t *image, const void *image_ptr,
+                                    const conv_i8_desc_t *loss, const void *loss_ptr,
+                                    const conv_i8_desc_t *dw, const int64_t pre_padding[2],
+                                    const int64_t post_padding[2], const int64_t stride[2],
+                                    const int64_t dilation[2], int32_t mode, char *buf, size_t len)
+{
+    if (!buf || len == 0)
+        return CONV_I8_ERR_NULL;
+    WgradProblem wp;
+    conv_i8_status_t st = wgrad_analyze(image, loss, dw, pre_padding, post_padding, stride, dilation,
+                                        mode, &wp);
+    if (st != CONV_I8_OK)
+        return st;
+    if (wp.dw.elems() == 0) {
+        snprintf(buf, len, "empty");
+        return CONV_I8_OK;
+    }
+    const char *tuned = tuned_wgrad_tile(wp);
+    return wgrad_call(wp, image_ptr, loss_ptr, nullptr, mode,
+                      [&](const conv_i8_desc_t *i, const void *x, const conv_i8_desc_t *f,
+                          const void *w, const conv_i8_desc_t *o, void *, const int64_t *a,
+                          const int64_t *b, const int64_t *c, const int64_t *d, bool fl) {
+                          Problem pb;
+                          Plan pl;
+                          conv_i8_status_t r = prepare(i, x, f, w, o, a, b, c, d, &pb, &pl,
+                                                       CONV_I8_DT_INT32,
+                                                       CONV_I8_MODE_CROSS_CORRELATION, fl, true,
+                                                       tuned);
+                          if (r == CONV_I8_OK)
+                              snprintf(buf, len, "%s", describe(pb, pl).c_str());
+                          return r;
+                      });
 }
 
 conv_i8_status_t conv_wgrad_i8_workspace_size(const conv_i8_desc_t *image, const void *image_ptr,

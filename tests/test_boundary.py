@@ -212,10 +212,57 @@ def test_tuned_tiles_are_planned(monkeypatch):
         c = wl.case(name)
         a = _args(c)
         f = ci8.plan_fields(ci8.conv_fprop_i8_plan(a["x"], a["w"], a["y"], c.pre, c.post, c.stride, c.dilation))
-        key = (*c.image.dims, c.filter.dims[0], *c.filter.dims[2:], *c.pre, *c.post, *c.stride, *c.dilation,
-               1 if f["lanes"] == "pixels" else 0)
+        key = (0, *c.image.dims, c.filter.dims[0], *c.filter.dims[2:], *c.pre, *c.post, *c.stride,
+               *c.dilation, 1 if f["lanes"] == "pixels" else 0)
         assert key in rows, name
         assert f["tile"] == rows[key], (name, f["tile"], rows[key])
+
+
+def test_wgrad_tuned_tiles_are_planned(monkeypatch):
+    """Weight-gradient rows of the table (keyed by the layer and dW's layout)
+    give the tile of the gradient's one forward call; the split of its
+    reduction stays the planner's.  A forced tile still wins."""
+    monkeypatch.delenv("CONV_I8_TILE", raising=False)
+    rows = {k: t for k, t in _tuned_entries() if k[0] == 1}
+    assert rows, "no weight-gradient rows in the table"
+    seen = 0
+    for name in wl.CASES:
+        c = wl.case(name)
+        key = (1, *c.image.dims, c.filter.dims[0], *c.filter.dims[2:], *c.pre, *c.post, *c.stride,
+               *c.dilation, 0 if c.filter.strides[1] == 1 else 1)
+        if key not in rows:
+            continue
+        seen += 1
+        x = ci8.desc(c.image.dims, c.image.strides, ci8.DT_INT8)
+        dy = ci8.desc(c.out.dims, c.out.strides, ci8.DT_INT8)
+        dw = ci8.desc(c.filter.dims, c.filter.strides, ci8.DT_INT32)
+        f = ci8.plan_fields(ci8.conv_wgrad_i8_plan(x, dy, dw, c.pre, c.post, c.stride, c.dilation))
+        assert f["tile"] == rows[key], (name, f["tile"], rows[key])
+        assert int(f["workspace"]) == ci8.conv_wgrad_i8_workspace_size(x, dy, dw, c.pre, c.post, c.stride,
+                                                                       c.dilation)
+        other = "128x128x64" if rows[key] != "128x128x64" else "w256x128x64"
+        monkeypatch.setenv("CONV_I8_TILE", other)
+        f2 = ci8.plan_fields(ci8.conv_wgrad_i8_plan(x, dy, dw, c.pre, c.post, c.stride, c.dilation))
+        monkeypatch.delenv("CONV_I8_TILE")
+        assert f2["tile"] == other, (name, f2)
+    assert seen == len(rows)
+
+
+def test_wgrad_plan_arguments():
+    D = ci8.desc
+    x, dy = D((2, 3, 6, 7), (126, 42, 7, 1), 1), D((2, 4, 4, 5), (80, 20, 5, 1), 1)
+    dw = D((4, 3, 3, 3), (27, 9, 3, 1), 2)
+    pre, post, st, dl = ci8._params(0, 0, 1, 1, None)
+    S = ci8.STATUS
+    assert S[ci8.lib.conv_wgrad_i8_plan(ctypes.byref(x), None, ctypes.byref(dy), None, ctypes.byref(dw),
+                                        pre, post, st, dl, 0, None, 64)] == "CONV_I8_ERR_NULL"
+    f = ci8.plan_fields(ci8.conv_wgrad_i8_plan(x, dy, dw))
+    assert f["ksplit"] == "1" and "tile" in f
+    bad = D((2, 4, 4, 6), (96, 24, 6, 1), 1)       # loss dims do not match the forward output
+    with pytest.raises(ci8.ConvI8Error) as e:
+        ci8.conv_wgrad_i8_plan(x, bad, dw)
+    assert e.value.name == "CONV_I8_ERR_OUT_DIMS"
+    assert ci8.conv_wgrad_i8_plan(x, D((2, 0, 4, 5), (0, 20, 5, 1), 1), D((0, 3, 3, 3), (27, 9, 3, 1), 2)) == "empty"
 
 
 def test_tile_names():
