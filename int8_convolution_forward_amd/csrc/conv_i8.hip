@@ -523,12 +523,15 @@ RepackJob repack_job(const T4 &t, const int8_t *src, int8_t *dst, int64_t Cp, in
     else
         j.mode = kRepackGather;
     const int64_t tx = ((j.mode == kRepackAFast ? A : X) + 63) / 64, tc = (Cp + 63) / 64;
-    const int64_t tiles = (j.mode == kRepackAFast ? Y * X : A * Y) * tx * tc;
+    // a-fast tiles with 16 or 32 packed channels cover 4 or 2 (y, x) positions
+    // (the kernel indexes the Y*X positions with 32-bit ints)
+    j.pp_shift = j.mode == kRepackAFast && Cp <= 32 && Y * X <= kI32Max - 4 ? (Cp <= 16 ? 2 : 1) : 0;
+    const int64_t tiles = (j.mode == kRepackAFast ? (Y * X + (1 << j.pp_shift) - 1) >> j.pp_shift : A * Y) * tx * tc;
     if (tiles64)
         *tiles64 = tiles;
     j.tiles_x = (int)tx;
     j.tiles_c = (int)tc;
-    j.tiles = tiles <= kI32Max ? (int)tiles : 0;
+    j.tiles = tiles <= kI32Max ? (int)tiles : -1;   // -1: refused at launch
     j.d_tc = make_divisor(std::max<int64_t>(tc, 1));
     j.d_tx = make_divisor(std::max<int64_t>(tx, 1));
     j.d_o = make_divisor(std::max<int64_t>(j.mode == kRepackAFast ? X : Y, 1));
@@ -917,6 +920,8 @@ conv_i8_status_t launch_repacks_n(const RepackJob *jobs, int njobs, hipStream_t 
     RepackArgs<NJ> r{};
     int64_t total = 0;
     for (int i = 0; i < njobs; ++i) {
+        if (jobs[i].tiles < 0)
+            return CONV_I8_ERR_UNSUPPORTED;
         if (jobs[i].tiles == 0)
             continue;
         r.job[r.njobs++] = jobs[i];
