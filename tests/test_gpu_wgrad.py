@@ -98,6 +98,22 @@ def test_random_wgrad_problems(ci8):
         done += 1
 
 
+@pytest.mark.parametrize("N", [3, 6, 20, 32])
+def test_wgrad_small_batch_transposes(ci8, N):
+    """Channels-last operands with a small batch: the transposed views have
+    the batch as their channels (16 or 32 packed), so one repack tile covers
+    4 or 2 image positions, including a ragged last tile.  Stride 2 along W
+    leaves the last image column unread, so the image view is cropped and its
+    rows and columns do not merge into one run."""
+    C, K, H, W = 24, 40, 7, 10
+    xspec = wl.TensorSpec((N, C, H, W), wl.channels_last_strides((N, C, H, W)))
+    od = oracle.out_dims((N, C, H, W), (K, C, 3, 3), (0, 0), (0, 0), (1, 2), (1, 1))
+    dyspec = wl.TensorSpec(od, wl.channels_last_strides(od))
+    dwspec = wl.TensorSpec((K, C, 3, 3), wl.channels_last_strides((K, C, 3, 3)))
+    run_wgrad_check(ci8, _rand_storage(xspec, 700 + N), xspec, _rand_storage(dyspec, 800 + N), dyspec, dwspec,
+                    (0, 0), (0, 0), (1, 2), (1, 1), mode=N % 2, label=f"small batch {N}", entry="ws")
+
+
 @pytest.mark.parametrize("layout,split_sum", [("kcrs_dense", "partial"), ("krsc_gaps", "atomic")])
 def test_wgrad_split_paths(ci8, monkeypatch, capfd, layout, split_sum):
     """A weight gradient whose long N*P*Q reduction is split over workgroups
