@@ -268,6 +268,18 @@ void launch_fp3x3(bool, bool pix_j, dim3 grid, hipStream_t stream, const IgemmAr
 template <int TM, int TN, int FPIX, bool TAIL>
 void launch_fp9(bool, bool pix_j, dim3 grid, hipStream_t stream, const IgemmArgs &a)
 {
+    if constexpr (TAIL) {
+        // k-major filter reads: the tail tiles only (the planner asks no other)
+        if (a.kmaj) {
+            if (pix_j)
+                hipLaunchKernelGGL((conv_fp3x3_ring9_kernel<TM, TN, FPIX, 2, 2, true, TAIL, true>), grid, dim3(256),
+                                   0, stream, a);
+            else
+                hipLaunchKernelGGL((conv_fp3x3_ring9_kernel<TM, TN, FPIX, 2, 2, false, TAIL, true>), grid, dim3(256),
+                                   0, stream, a);
+            return;
+        }
+    }
     if (pix_j)
         hipLaunchKernelGGL((conv_fp3x3_ring9_kernel<TM, TN, FPIX, 2, 2, true, TAIL>), grid, dim3(256), 0, stream, a);
     else
@@ -457,6 +469,9 @@ struct Plan {
     bool pix_linear = false;           // output pixel m at m * pix_stride
     int64_t pix_stride = 0;
     int64_t Hp = 0, Wf = 0, Pr = 0;    // footprint kernel geometry
+    bool kmaj = false;                 // filter read in place with its output channels
+                                       // contiguous (3x3 tail tiles; wsK is then the
+                                       // stride of one input channel)
     // split of a long inner dimension over gridDim.y (weight gradient)
     int64_t ksplit = 1, kchunk = 0;    // splits, stages per split
     bool part = false;                 // partial outputs in the workspace + reduction
@@ -482,6 +497,24 @@ bool direct_ok(const T4 &t, const void *ptr)
             return false;
     return ptr == nullptr || aligned16(ptr);
 }
+
+// Can the 3x3 tail tiles read this filter in place k-major: output channels
+// contiguous (the data gradient's view [C, K, R, S] of a KRSC filter, or an
+// R, S, C, K filter), K a multiple of 16, 64-channel blocks of input
+// channels, and every 16-channel run 16-byte aligned?  The kernel loads rows
+// of 128 output channels per input channel and transposes them in LDS.
+bool kmajor_ok(const Problem &pb, const void *ptr)
+{
+    const T4 &t = pb.w;
+    if (pb.K % 16 != 0 || pb.C % 64 != 0 || pb.C == 0 || t.s[0] != 1 || t.s[1] > kI32Max / 64)
+        return false;
+    for (int i : {1, 2, 3})
+        if (t.s[i] % 16 != 0)
+            return false;
+    return ptr == nullptr || aligned16(ptr);
+}
+
+bool tile_reads_kmajor(const TileCfg &c) { return c.kind == kFootprint && c.ns == 9 && c.name[0] == 't'; }
 
 const char *env_tile() { return getenv("CONV_I8_TILE"); }
 
@@ -776,6 +809,20 @@ conv_i8_status_t make_plan(const Problem &pb, const void *x_ptr, const void *w_p
         pl->batch_chunk = std::max<int64_t>(pb.N, 1);
         return CONV_I8_OK;
     }
+    if (pl->repack_w && tile_reads_kmajor(c) && kmajor_ok(pb, w_ptr)) {
+        // the filter is read in place (no repack, its workspace region
+        // dropped: it was the last one)
+        int64_t sp;
+        if (span_of(pb.w, &sp) && sp <= kI32Max) {
+            pl->repack_w = false;
+            pl->kmaj = true;
+            pl->ws_bytes = pl->ws_w_off;
+            pl->wsK = pb.w.s[1];
+            pl->wsR = pb.w.s[2];
+            pl->wsS = pb.w.s[3];
+            pl->w_span = sp;
+        }
+    }
     const int cps = c.bk / 16;
     pl->blocked = cc % cps == 0;
     pl->nstages = pl->blocked ? RS * (cc / cps) : (RS * cc + cps - 1) / cps;
@@ -898,9 +945,10 @@ std::string describe(const Problem &pb, const Plan &pl)
                                             : ((M + c.tm - 1) / c.tm) * ((pb.K + c.tn - 1) / c.tn);
     char buf[512];
     snprintf(buf, sizeof buf,
-             "repack_image=%d repack_filter=%d Cp=%lld tile=%s kernel=%s order=%s stages=%lld "
+             "repack_image=%d repack_filter=%d filter_read=%s Cp=%lld tile=%s kernel=%s order=%s stages=%lld "
              "lanes=%s tiles=%lld batch_chunk=%lld workspace=%zu ksplit=%lld split_sum=%s",
-             (int)pl.repack_x, (int)pl.repack_w, (long long)pl.Cp, c.name,
+             (int)pl.repack_x, (int)pl.repack_w, pl.kmaj ? "kmajor" : pl.repack_w ? "packed" : "in_place",
+             (long long)pl.Cp, c.name,
              c.kind == kFootprint ? "footprint" : c.kind == kPointwise ? "pointwise" : c.kind == kDirect ? "direct" : "im2col",
              pl.blocked ? "blocked" : "flat", (long long)pl.nstages,
              pl.pix_j ? "pixels" : "channels", (long long)tiles, (long long)pl.batch_chunk,
@@ -994,6 +1042,7 @@ conv_i8_status_t run(const Problem &pb, const Plan &pl, const void *x_ptr, const
     a.fK = (int)pl.wsK;
     a.fR = (int)pl.wsR;
     a.fS = (int)pl.wsS;
+    a.kmaj = pl.kmaj ? 1 : 0;
     if (pb.mode == CONV_I8_MODE_CONVOLUTION) {
         // true convolution: tap (r, s) reads filter tap (R-1-r, S-1-s), i.e.
         // the taps from the far corner with negated strides (the offsets stay
@@ -1127,7 +1176,7 @@ conv_i8_status_t run(const Problem &pb, const Plan &pl, const void *x_ptr, const
 // a forced tile; repeated calls on one shape skip the tile search.
 struct PlanKey {
     Problem pb;
-    int32_t x_direct, w_direct;
+    int32_t x_direct, w_direct, w_kmajor;
     char tile[24];
 };
 constexpr int kPlanCache = 16;
@@ -1157,6 +1206,7 @@ conv_i8_status_t prepare(const conv_i8_desc_t *image, const void *image_ptr,
     key.pb = *pb;
     key.x_direct = direct_ok(pb->x, image_ptr) ? 1 : 0;
     key.w_direct = direct_ok(pb->w, filter_ptr) ? 1 : 0;
+    key.w_kmajor = kmajor_ok(*pb, filter_ptr) ? 1 : 0;
     const char *forced = env_tile();
     const char *name = forced ? forced : tuned;   // a tile chosen outside the planner
     if (name)

@@ -491,7 +491,7 @@ constexpr int tail_len(int FM, int x) { return FM >= 4 && x == 0 ? 2 : 1; }
 // goes through all nine taps, and its INT32 stores drain while the MFMAs of
 // the next row block run (instead of the whole tile's stores after the last
 // MFMA).  Four waves, 2 x 2 (WGM x WGN).
-template <int TM, int TN, int FPIX, int WGM, int WGN, bool PIX_J, bool TAIL>
+template <int TM, int TN, int FPIX, int WGM, int WGN, bool PIX_J, bool TAIL, bool KMAJ = false>
 __global__ __launch_bounds__(64 * WGM * WGN) void conv_fp3x3_ring9_kernel(IgemmArgs a)
 {
     using namespace fp3x3;
@@ -512,6 +512,7 @@ __global__ __launch_bounds__(64 * WGM * WGN) void conv_fp3x3_ring9_kernel(IgemmA
     static_assert(BL >= 1 && TN * BK % GB == 0, "filter tile must fill workgroup loads");
     static_assert(NW == 4, "four waves");
     static_assert(FM >= 1 && FN >= 1, "wave tile");
+    static_assert(!KMAJ || TN == 128, "a k-major filter slot holds 64 rows of 128 output channels");
     static_assert(allowed_at<NG, BL>(0) < 64 && allowed_at<NG, BL>(7) < 64 && allowed_first<NG, BL>(8) < 64 &&
                       2 * BL + chunk_lo<NG>(1) < 64,
                   "vmcnt range");
@@ -545,8 +546,21 @@ __global__ __launch_bounds__(64 * WGM * WGN) void conv_fp3x3_ring9_kernel(IgemmA
     int b_off[BL];
 #pragma unroll
     for (int i = 0; i < BL; ++i) {
-        const int k = n0 + row0 + i * NW * 16;
-        b_off[i] = k < a.K ? k * a.fK + jb * 16 : kOutOfRange;
+        if constexpr (KMAJ) {
+            // k-major filter (output channels contiguous, a.fK the stride of
+            // one of the block's 64 reduction rows): byte p = lane*16 of load
+            // i lands at slot byte i*GB + wave*1024 + p, i.e. row kr, 16-byte
+            // chunk q of 128 output channels, and holds global chunk
+            // q ^ (kr & 7) of that row, so that the transposing reads of a
+            // fragment (eight consecutive rows of one chunk) hit eight
+            // different chunk positions
+            const int kr = i * (GB / 128) + wave * 8 + (lane >> 3);
+            const int col = n0 + (((lane & 7) ^ (kr & 7)) << 4);
+            b_off[i] = col < a.K ? kr * a.fK + col : kOutOfRange;
+        } else {
+            const int k = n0 + row0 + i * NW * 16;
+            b_off[i] = k < a.K ? k * a.fK + jb * 16 : kOutOfRange;
+        }
     }
     int a_lane[FM][KS];
     int b_lane[FN][KS];
@@ -556,6 +570,7 @@ __global__ __launch_bounds__(64 * WGM * WGN) void conv_fp3x3_ring9_kernel(IgemmA
     const unsigned ring_lds = lds_address(ring) + wave * 1024;
     const unsigned fbuf_lds = lds_address(fbuf) + wave * 1024;
     const int nblk = a.ncblk;
+    const int cb_bytes = KMAJ ? BK * a.fK : BK;   // filter bytes from one channel block to the next
     const bool tail = TAIL && nblk > 0;
     const int nend = tail ? nblk - 1 : nblk;   // blocks run by the main loop
 
@@ -564,7 +579,7 @@ __global__ __launch_bounds__(64 * WGM * WGN) void conv_fp3x3_ring9_kernel(IgemmA
     // filter of (block cb, tap t) into ring slot t; past the last block the
     // offsets leave the range (zeros)
     auto dma_filter = [&](int cb, int t, int i) {
-        const int ftoff = cb < nblk ? tap_flt(t) + cb * BK : a.flt_range;
+        const int ftoff = cb < nblk ? tap_flt(t) + cb * cb_bytes : a.flt_range;
         load16_to_lds(flt_rsrc, ring_lds + t * B_BYTES + i * GB, b_off[i] + ftoff);
     };
     int foff[NG];
@@ -644,13 +659,25 @@ __global__ __launch_bounds__(64 * WGM * WGN) void conv_fp3x3_ring9_kernel(IgemmA
         for (int y = 0; y < FN; ++y)
             acc[x][y] = v16i{};
 
+    // filter fragment y of k-step ks of tap t
+    auto b_frag = [&](int t, int y, int ks) {
+        const int8_t *p = &ring[t * B_BYTES + b_lane[y][ks]];
+        if constexpr (KMAJ) {
+            // two transposing reads: rows kr .. kr+7, then kr+8 .. kr+15
+            const v2i lo = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_v2i *)p);
+            const v2i hi = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_v2i *)(p + 8 * TN));
+            return v4i{lo.x, lo.y, hi.x, hi.y};
+        } else {
+            return *(const v4i *)p;
+        }
+    };
     v4i frag[2][KS][FM + FN];
     auto read_one = [&](int buf, int t, int fb, int i) {
         const int ks = i / (FM + FN), f = i % (FM + FN);
         if (f < FM)
             frag[buf][ks][f] = *(const v4i *)&fbuf[fb * FBUF + a_lane[f][ks] + tap_read(t)];
         else
-            frag[buf][ks][f] = *(const v4i *)&ring[t * B_BYTES + b_lane[f - FM][ks]];
+            frag[buf][ks][f] = b_frag(t, f - FM, ks);
     };
     // MFMA q of a stage: k-step major, row blocks in order, column blocks
     // snaking (consecutive MFMAs share one operand)
@@ -692,10 +719,26 @@ __global__ __launch_bounds__(64 * WGM * WGN) void conv_fp3x3_ring9_kernel(IgemmA
     }
 #pragma unroll
     for (int y = 0; y < FN; ++y) {
-        const int row = wn + y * 32 + (lane & 31);
+        if constexpr (KMAJ) {
+            // ds_read_b64_tr_b8 hands lane i of each 16-lane group byte i % 8
+            // of the eight rows that lanes 2b + i / 8 (b = 0..7) address: lane
+            // j addresses row kr + j / 2 at output channel col + 8 (j & 1),
+            // so that lane i receives reduction rows kr .. kr+7 of output
+            // channel col + i, the fragment an MFMA lane needs (channel
+            // lane % 32, rows 16 (lane / 32) .. +16 of the k-step)
+            const int j = lane & 15;
+            const int col = wn + y * 32 + ((lane >> 4) & 1) * 16 + (j & 1) * 8;
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks)
-            b_lane[y][ks] = row * BK + swizzle_chunk<64>(row, ks * 2 + (lane >> 5)) * 16;
+            for (int ks = 0; ks < KS; ++ks) {
+                const int kr = ks * 32 + (lane >> 5) * 16 + (j >> 1);
+                b_lane[y][ks] = kr * TN + (((col >> 4) ^ (kr & 7)) << 4) + (col & 8);
+            }
+        } else {
+            const int row = wn + y * 32 + (lane & 31);
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks)
+                b_lane[y][ks] = row * BK + swizzle_chunk<64>(row, ks * 2 + (lane >> 5)) * 16;
+        }
     }
 
     wait_vm_lgkm0<2 * BL + chunk_lo<NG>(1)>();
@@ -819,7 +862,7 @@ __global__ __launch_bounds__(64 * WGM * WGN) void conv_fp3x3_ring9_kernel(IgemmA
                 ab[s2 % NR][i] = *(const v4i *)&fbuf[fb * FBUF + a_lane[tail_first(FM, x) + i][ks] + tap_read(t)];
 #pragma unroll
             for (int y = 0; y < FN; ++y)
-                bb[s2 % NR][y] = *(const v4i *)&ring[t * B_BYTES + b_lane[y][ks]];
+                bb[s2 % NR][y] = b_frag(t, y, ks);
         };
         const __amdgpu_buffer_rsrc_t out_rsrc =
             __builtin_amdgcn_make_buffer_rsrc((void *)a.out, (short)0, a.out_range, kRsrcWord3);

@@ -10,6 +10,8 @@
 namespace convi8 {
 
 typedef int v4i __attribute__((ext_vector_type(4)));
+typedef int v2i __attribute__((ext_vector_type(2)));
+typedef __attribute__((address_space(3))) v2i lds_v2i;
 typedef int v16i __attribute__((ext_vector_type(16)));
 typedef __attribute__((address_space(3))) void lds_void;
 
@@ -74,6 +76,9 @@ struct IgemmArgs {
     int Pr;              // footprint row pitch in LDS, 16-byte slots
     float inv_pr, inv_hp;
     int ncblk;           // channel blocks of 64
+    int kmaj;            // 3x3 ring kernel: the filter is read k-major (output channels
+                         // contiguous, fK the stride of one input channel); picks the
+                         // instantiation on the host
     // requantising INT8 epilogue (q8 != 0)
     const float *q_scale; // K per-channel scales, or null: q_alpha for every channel
     const float *q_bias;  // K per-channel biases, or null: none

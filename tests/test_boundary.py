@@ -248,6 +248,46 @@ def test_wgrad_tuned_tiles_are_planned(monkeypatch):
     assert seen == len(rows)
 
 
+def _plan_raw(x, w, y, wptr, pre=(1, 1), post=(1, 1), st=(1, 1), dl=(1, 1)):
+    pre_, post_, st_, dl_ = ci8._params(pre, post, st, dl, None)
+    buf = ctypes.create_string_buffer(512)
+    rc = ci8.lib.conv_fprop_i8_plan(ctypes.byref(x), None, ctypes.byref(w), wptr, ctypes.byref(y),
+                                    pre_, post_, st_, dl_, buf, 512)
+    assert rc == 0, ci8.STATUS[rc]
+    return ci8.plan_fields(buf.value.decode())
+
+
+def test_kmajor_filter_plans(monkeypatch):
+    """A filter whose output channels are contiguous (an R, S, C, K filter, or
+    the data gradient's view of a KRSC filter) is read in place by the 3x3
+    tail tiles (no repack, no filter workspace); a misaligned pointer, K not a
+    multiple of 16, C not a multiple of 64 or another tile repack it."""
+    monkeypatch.delenv("CONV_I8_TILE", raising=False)
+    D = ci8.desc
+    N, C, H, W, K = 8, 128, 14, 14, 96
+    x = D((N, C, H, W), wl.channels_last_strides((N, C, H, W)), 1)
+    y = D((N, K, H, W), wl.channels_last_strides((N, K, H, W)), 2)
+    hwio = lambda k, c: D((k, c, 3, 3), (1, k, 3 * c * k, c * k), 1)       # [R][S][C][K] storage
+    for tile in ("t256x128", "t128x128"):
+        monkeypatch.setenv("CONV_I8_TILE", tile)
+        f = _plan_raw(x, hwio(K, C), y, FAKE)
+        assert (f["tile"], f["filter_read"], f["repack_filter"], f["workspace"]) == (tile, "kmajor", "0", "0"), f
+        f = _plan_raw(x, hwio(K, C), y, ctypes.c_void_p(FAKE.value + 8))
+        assert (f["filter_read"], f["repack_filter"]) == ("packed", "1") and int(f["workspace"]) > 0, f
+        yk = D((N, 88, H, W), wl.channels_last_strides((N, 88, H, W)), 2)
+        assert _plan_raw(x, hwio(88, C), yk, FAKE)["filter_read"] == "packed"
+        x96 = D((N, 96, H, W), wl.channels_last_strides((N, 96, H, W)), 1)
+        assert _plan_raw(x96, hwio(K, 96), y, FAKE)["filter_read"] == "packed"
+    monkeypatch.setenv("CONV_I8_TILE", "r256x128")
+    assert _plan_raw(x, hwio(K, C), y, FAKE)["filter_read"] == "packed"
+    monkeypatch.setenv("CONV_I8_TILE", "128x128x64")
+    assert _plan_raw(x, hwio(K, C), y, FAKE)["filter_read"] == "packed"
+    # a channels-innermost filter stays read in place as before
+    monkeypatch.setenv("CONV_I8_TILE", "t256x128")
+    f = _plan_raw(x, D((K, C, 3, 3), wl.channels_last_strides((K, C, 3, 3)), 1), y, FAKE)
+    assert (f["filter_read"], f["repack_filter"]) == ("in_place", "0"), f
+
+
 def test_wgrad_plan_arguments():
     D = ci8.desc
     x, dy = D((2, 3, 6, 7), (126, 42, 7, 1), 1), D((2, 4, 4, 5), (80, 20, 5, 1), 1)

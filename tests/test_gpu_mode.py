@@ -126,3 +126,31 @@ def test_tile_shapes_convolution_mode(ci8, monkeypatch, tile, R, S, C, out_layou
     wv = torch.randint(-128, 128, ws.dims, dtype=torch.int8, generator=g)
     run_mode_check(ci8, _fill(xs, xv, 9), xs, _fill(ws, wv, 10), ws, os_, pre, post, st, dl,
                    label=f"tile {tile} {R}x{S} C={C} {out_layout}")
+
+
+@pytest.mark.parametrize("tile", ["t256x128", "t128x128"])
+@pytest.mark.parametrize("mode", [0, 1])
+@pytest.mark.parametrize("out_layout", ["nhwc", "nchw"])
+def test_kmajor_filter_modes_and_requant(ci8, monkeypatch, tile, mode, out_layout):
+    """Filters stored R, S, C, K, read k-major by the 3x3 tail tiles: both tap
+    orders, INT32 output and the requantising tail, a ragged second column
+    tile (K = 144)."""
+    monkeypatch.setenv("CONV_I8_TILE", tile)
+    N, C, H, W, K = 3, 128, 9, 12, 144
+    pre, post, st, dl = (1, 1), (1, 1), (1, 1), (1, 1)
+    xs = wl.TensorSpec((N, C, H, W), wl.channels_last_strides((N, C, H, W)))
+    ws = wl.TensorSpec((K, C, 3, 3), (1, K, 3 * C * K, C * K))
+    od = oracle.out_dims(xs.dims, ws.dims, pre, post, st, dl)
+    os_ = wl.TensorSpec(od, wl.channels_last_strides(od) if out_layout == "nhwc" else wl.contiguous_strides(od))
+    f = ci8.plan_fields(ci8.conv_fprop_i8_plan(ci8.desc(xs.dims, xs.strides, 1), ci8.desc(ws.dims, ws.strides, 1),
+                                               ci8.desc(os_.dims, os_.strides, 2), pre, post, st, dl))
+    assert (f["tile"], f["filter_read"]) == (tile, "kmajor"), f
+    g = torch.Generator().manual_seed(60 + mode)
+    xv = torch.randint(-128, 128, xs.dims, dtype=torch.int8, generator=g)
+    wv = torch.randint(-128, 128, ws.dims, dtype=torch.int8, generator=g)
+    xst, wst = _fill(xs, xv, 11), _fill(ws, wv, 12)
+    run_mode_check(ci8, xst, xs, wst, ws, os_, pre, post, st, dl, mode=mode,
+                   label=f"k-major {tile} {out_layout}")
+    sc, bi = channel_params(K, C * 9, seed=6)
+    run_mode_check(ci8, xst, xs, wst, ws, os_, pre, post, st, dl, mode=mode, requant=(sc, bi, True),
+                   label=f"k-major requant {tile} {out_layout}")

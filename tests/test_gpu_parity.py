@@ -370,6 +370,39 @@ def test_footprint_kernel(ci8, monkeypatch, tile, case_i, out_layout):
                   label=f"footprint {tile} case {case_i}")
 
 
+# Filters stored R, S, C, K (output channels contiguous, as the data
+# gradient's view of a KRSC filter is): the 3x3 tail tiles read them in place,
+# 128 output channels per input-channel row, and transpose them in LDS.  The
+# cases with K % 16 == 0 and C % 64 == 0, plus a ragged column tile (K = 80).
+KMAJOR_CASES = [FOOTPRINT_CASES[i] for i in (2, 4, 6, 7)] + [
+    (3, 128, 11, 13, 80, 3, 3, (1, 1), (1, 1), (1, 1), (1, 1)),
+]
+
+
+def _rsck_strides(K, C, R, S):
+    return (1, K, S * C * K, C * K)
+
+
+@pytest.mark.parametrize("tile", ["t256x128", "t128x128"])
+@pytest.mark.parametrize("case_i", range(len(KMAJOR_CASES)))
+@pytest.mark.parametrize("out_layout", ["nhwc", "nchw"])
+def test_footprint_kernel_kmajor_filter(ci8, monkeypatch, tile, case_i, out_layout):
+    N, C, H, W, K, R, S, st, dl, pre, post = KMAJOR_CASES[case_i]
+    monkeypatch.setenv("CONV_I8_TILE", tile)
+    od = oracle.out_dims((N, C, H, W), (K, C, R, S), pre, post, st, dl)
+    xs = wl.TensorSpec((N, C, H, W), wl.channels_last_strides((N, C, H, W)))
+    ws = wl.TensorSpec((K, C, R, S), _rsck_strides(K, C, R, S))
+    os_ = wl.TensorSpec(od, wl.channels_last_strides(od) if out_layout == "nhwc" else wl.contiguous_strides(od))
+    plan = ci8.plan_fields(ci8.conv_fprop_i8_plan(ci8.desc(xs.dims, xs.strides, 1), ci8.desc(ws.dims, ws.strides, 1),
+                                                  ci8.desc(os_.dims, os_.strides, 2), pre, post, st, dl))
+    assert (plan["tile"], plan["filter_read"], plan["workspace"]) == (tile, "kmajor", "0"), plan
+    g = torch.Generator().manual_seed(50 + case_i)
+    xv = torch.randint(-128, 128, (N, C, H, W), dtype=torch.int8, generator=g)
+    wv = torch.randint(-128, 128, (K, C, R, S), dtype=torch.int8, generator=g)
+    run_and_check(ci8, _fill(xs, xv, 1), xs, _fill(ws, wv, 2), ws, os_, pre, post, st, dl,
+                  label=f"k-major filter {tile} case {case_i}")
+
+
 # ---------------------------------------------------------------------------
 # The 1x1 streaming kernel: ragged pixel counts (not a multiple of 32 or of a
 # wave's four tiles), ragged output channels and channels, stride and padding
