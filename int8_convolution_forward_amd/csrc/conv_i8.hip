@@ -1005,6 +1005,12 @@ conv_i8_status_t launch_repacks(const RepackJob *jobs, int njobs, hipStream_t st
                       : launch_repacks_n<kRepackMaxJobs>(jobs, njobs, stream);
 }
 
+#ifdef CONV_I8_PHASE_CLOCK
+// Instrumented builds only: where the 3x3 ring kernel writes its
+// per-workgroup phase stamps (set by conv_i8_set_phase_clock).
+long long *g_phase_clk = nullptr;
+#endif
+
 conv_i8_status_t run(const Problem &pb, const Plan &pl, const void *x_ptr, const void *w_ptr,
                      void *y_ptr, void *ws, hipStream_t stream, const conv_i8_requant_t *rq = nullptr)
 {
@@ -1043,6 +1049,9 @@ conv_i8_status_t run(const Problem &pb, const Plan &pl, const void *x_ptr, const
     a.fR = (int)pl.wsR;
     a.fS = (int)pl.wsS;
     a.kmaj = pl.kmaj ? 1 : 0;
+#ifdef CONV_I8_PHASE_CLOCK
+    a.phase_clk = g_phase_clk;
+#endif
     if (pb.mode == CONV_I8_MODE_CONVOLUTION) {
         // true convolution: tap (r, s) reads filter tap (R-1-r, S-1-s), i.e.
         // the taps from the far corner with negated strides (the offsets stay
@@ -2251,6 +2260,17 @@ conv_i8_status_t conv_i8_mfma_ceiling(int workgroups, int iters, uint32_t seed, 
                        (unsigned)seed, (int *)out);
     return hipGetLastError() == hipSuccess ? CONV_I8_OK : CONV_I8_ERR_HIP;
 }
+
+#ifdef CONV_I8_PHASE_CLOCK
+// Instrumented builds only (CONV_I8_PHASE_CLOCK; not part of the product
+// library or its header): a device buffer of 16 int64 per workgroup that
+// every later 3x3 ring kernel launch fills with its phase stamps, or null.
+conv_i8_status_t conv_i8_set_phase_clock(void *buf)
+{
+    g_phase_clk = (long long *)buf;
+    return CONV_I8_OK;
+}
+#endif
 
 conv_i8_status_t conv_i8_tile_names(char *buf, size_t len)
 {

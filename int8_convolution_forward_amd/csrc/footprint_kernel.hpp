@@ -494,6 +494,7 @@ constexpr int tail_len(int FM, int x) { return FM >= 4 && x == 0 ? 2 : 1; }
 template <int TM, int TN, int FPIX, int WGM, int WGN, bool PIX_J, bool TAIL, bool KMAJ = false>
 __global__ __launch_bounds__(64 * WGM * WGN) void conv_fp3x3_ring9_kernel(IgemmArgs a)
 {
+    CONV_I8_PHASE_DECL;   // phase stamps of instrumented builds (nothing otherwise)
     using namespace fp3x3;
     using namespace fp9;
     constexpr int NW = WGM * WGN;
@@ -531,6 +532,7 @@ __global__ __launch_bounds__(64 * WGM * WGN) void conv_fp3x3_ring9_kernel(IgemmA
     asm volatile("" ::"s"(a.Q), "s"(a.PQ), "s"(a.M), "s"(a.strH), "s"(a.strW), "s"(a.dilH), "s"(a.dilW),
                  "s"(a.padH), "s"(a.padW), "s"(a.d_pq.m), "s"(a.d_pq.l), "s"(a.d_q.m), "s"(a.d_q.l),
                  "s"(a.d_tn.m), "s"(a.d_tn.l), "s"(a.inv_pr), "s"(a.inv_hp));
+    CONV_I8_PHASE(ph1);   // arguments loaded
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -588,6 +590,7 @@ __global__ __launch_bounds__(64 * WGM * WGN) void conv_fp3x3_ring9_kernel(IgemmA
         load16_to_lds(img_rsrc, fbuf_lds + (cb & 1) * FBUF + g * GB, foff[g] + coff);
     };
 
+    CONV_I8_PHASE(ph2);   // prologue loads start
     // ---- prologue: the filter of (0, 0) goes out first (its offsets are
     // ready); then the footprint of block 0, each group as soon as its
     // offsets are known, so that the address arithmetic overlaps the loads;
@@ -697,6 +700,7 @@ __global__ __launch_bounds__(64 * WGM * WGN) void conv_fp3x3_ring9_kernel(IgemmA
 #pragma unroll
     for (int g = chunk_lo<NG>(0); g < chunk_lo<NG>(1); ++g)
         dma_piece(1, g);
+    CONV_I8_PHASE(ph3);   // footprint of block 0 issued
     if constexpr (!PIX_J) {
         if (!a.pix_linear)
             fill_out_rows<TM, 64 * NW>(a, m0, out_row);
@@ -746,6 +750,7 @@ __global__ __launch_bounds__(64 * WGM * WGN) void conv_fp3x3_ring9_kernel(IgemmA
 #pragma unroll
     for (int i = 0; i < NRD; ++i)
         read_one(0, 0, 0, i);
+    CONV_I8_PHASE(ph4);   // main loop starts
 
     // ---- main loop ----------------------------------------------------------
     // Stage (cb, t) runs MFMAs on fragments read during the previous stage,
@@ -817,6 +822,7 @@ __global__ __launch_bounds__(64 * WGM * WGN) void conv_fp3x3_ring9_kernel(IgemmA
     }
     if (cb < nend)
         run_block(cb, I1{}, Steady{});
+    CONV_I8_PHASE(ph5);   // main loop done
 
     if (!tail) {
         wait_vm_lgkm0<0>();
@@ -845,6 +851,7 @@ __global__ __launch_bounds__(64 * WGM * WGN) void conv_fp3x3_ring9_kernel(IgemmA
         }
         wait_vm_lgkm0<0>();
         __builtin_amdgcn_s_barrier();
+        CONV_I8_PHASE(ph6);   // tail starts
         constexpr int NRB = tail_blocks(FM);
         constexpr int RBM = tail_len(FM, 0);   // fragments of the largest row block
         constexpr int NSTEP = kTaps * KS;
@@ -1019,6 +1026,7 @@ __global__ __launch_bounds__(64 * WGM * WGN) void conv_fp3x3_ring9_kernel(IgemmA
         else
             run_mode(std::false_type{});
     }
+    CONV_I8_PHASE_FLUSH(a);
 }
 
 

@@ -99,7 +99,39 @@ struct IgemmArgs {
     // (a reduction kernel adds the copies); part == 0: atomics into out
     int part;
     long long part_stride;
+#ifdef CONV_I8_PHASE_CLOCK
+    long long *phase_clk;  // per-workgroup phase stamps (instrumented builds only)
+#endif
 };
+
+// Per-workgroup phase stamps of the 3x3 ring kernel, compiled in only with
+// CONV_I8_PHASE_CLOCK (int8_convolution_forward_amd/phase_clock.py builds and
+// runs such a library): stamp i (shader clock, s_memtime; 0 entry, 1
+// arguments loaded, 2 prologue loads start, 3 footprint of block 0 issued,
+// 4 main loop starts, 5 main loop done, 6 tail starts, 11 end) goes to
+// phase_clk[16 * workgroup + i], the constant 100 MHz clock at the start and
+// the end to slots 14 and 15, all written by thread 0 at the end.  The
+// stamps are plain locals of the kernel body (an object holding them ended
+// up in scratch memory); without the macro every hook expands to nothing.
+#ifdef CONV_I8_PHASE_CLOCK
+#define CONV_I8_PHASE_DECL                                                                              \
+    long long ph0 = __builtin_amdgcn_s_memtime(), ph_rt0 = __builtin_amdgcn_s_memrealtime(), ph1 = 0, \
+              ph2 = 0, ph3 = 0, ph4 = 0, ph5 = 0, ph6 = 0
+#define CONV_I8_PHASE(v) v = __builtin_amdgcn_s_memtime()
+#define CONV_I8_PHASE_FLUSH(a)                                                                          \
+    do {                                                                                                \
+        const long long ph11 = __builtin_amdgcn_s_memtime();                                            \
+        if ((a).phase_clk && threadIdx.x == 0) {                                                        \
+            long long *o = (a).phase_clk + 16 * blockIdx.x;                                             \
+            o[0] = ph0; o[1] = ph1; o[2] = ph2; o[3] = ph3; o[4] = ph4; o[5] = ph5; o[6] = ph6;         \
+            o[11] = ph11; o[14] = ph_rt0; o[15] = __builtin_amdgcn_s_memrealtime();                     \
+        }                                                                                               \
+    } while (0)
+#else
+#define CONV_I8_PHASE_DECL
+#define CONV_I8_PHASE(v)
+#define CONV_I8_PHASE_FLUSH(a)
+#endif
 
 // Requantising INT8 epilogue of one exact sum: the sum as a float, one fused
 // multiply-add with the channel's scale and bias, ReLU if asked, round half to
