@@ -83,6 +83,32 @@ def mfma_ceiling(ci8, stream, workgroup_counts, iters=2048, launches=10):
     return res
 
 
+def launch_floor(ci8, workgroups, launches=200):
+    """Device µs per launch of a kernel that does almost nothing (the
+    calibration kernel with zero operands and one iteration: eight MFMAs and
+    a 128-value sum per wave) on `workgroups` workgroups, `launches` of them
+    recorded in one HIP graph so that the host's launch rate does not enter:
+    the floor under every launch (dispatch, kernel end, the end-of-kernel
+    write-back), median of five replays."""
+    import torch
+
+    out = torch.empty(workgroups * 256, dtype=torch.int32, device="cuda")
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        ci8.conv_i8_mfma_ceiling(workgroups, 1, 0, out, side)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        cap = torch.cuda.current_stream()
+        for _ in range(launches):
+            ci8.conv_i8_mfma_ceiling(workgroups, 1, 0, out, cap)
+    g.replay()
+    torch.cuda.synchronize()
+    return median(timed_batches(g.replay, torch.cuda.current_stream(), launches)) * 1e3
+
+
 def host_description(orc):
     """nproc, the CPU model and the oracle's thread count."""
     model = None
@@ -474,6 +500,9 @@ def main():
         roof["mfma_ceiling"] = {"unit": "TOP/s", "operands": "random int8 in registers",
                                 "tops_by_busy_cus": ceil}
         roof["frac_of_ceiling"] = roof["achieved"] / ceil[str(wgs)]
+    floor_wgs = max(1, min(int(kf.get("tiles", "256")), 1 << 20))
+    roof["launch_floor_us"] = {"workgroups": floor_wgs, "us": launch_floor(ci8, floor_wgs),
+                               "launch": "hip graph of back-to-back near-empty kernels"}
     roof["traffic"] = traffic_from_profiles(c.name + ("_requant" if rq_on else ""), alg_bytes)
     if kf.get("tile") in RING9_TILES:
         roof["kernel"] = "conv_fp3x3_ring9_kernel"
