@@ -223,10 +223,27 @@ conv_i8_status_t analyze(const conv_i8_desc_t *image, const conv_i8_desc_t *filt
 // ---------------------------------------------------------------------------
 using Launcher = void (*)(bool flat, bool pix_j, dim3 grid, hipStream_t stream, const IgemmArgs &a);
 
+// im2col tiles whose filter stages can be read k-major (blocked order only,
+// and not the split epilogue): 64-channel stages of 64, 128 or 256 columns
+template <int TN, int BK, int EPI>
+constexpr bool kmajor_tile() { return BK == 64 && (TN == 64 || TN == 128 || TN == 256) && EPI != kEpiSplit; }
+
 template <int TM, int TN, int BK, int NS, int WGM, int WGN, int EPI>
 void launch_cfg_epi(bool flat, bool pix_j, dim3 grid, hipStream_t stream, const IgemmArgs &a)
 {
     const dim3 block(64 * WGM * WGN);
+    if constexpr (kmajor_tile<TN, BK, EPI>()) {
+        // the planner asks for k-major reads only on such tiles, blocked order
+        if (a.kmaj && !flat) {
+            if (pix_j)
+                hipLaunchKernelGGL((conv_igemm_kernel<TM, TN, BK, NS, WGM, WGN, false, true, EPI, true>), grid, block,
+                                   0, stream, a);
+            else
+                hipLaunchKernelGGL((conv_igemm_kernel<TM, TN, BK, NS, WGM, WGN, false, false, EPI, true>), grid, block,
+                                   0, stream, a);
+            return;
+        }
+    }
     if (flat) {
         if (pix_j)
             hipLaunchKernelGGL((conv_igemm_kernel<TM, TN, BK, NS, WGM, WGN, true, true, EPI>), grid, block, 0, stream, a);
@@ -514,7 +531,17 @@ bool kmajor_ok(const Problem &pb, const void *ptr)
     return ptr == nullptr || aligned16(ptr);
 }
 
-bool tile_reads_kmajor(const TileCfg &c) { return c.kind == kFootprint && c.ns == 9 && c.name[0] == 't'; }
+// Tiles that read a k-major filter: the 3x3 tail tiles, and im2col tiles of
+// 64-channel stages over 64, 128 or 256 columns in blocked order (the
+// instantiations launch_cfg_epi and launch_fp9 provide); not with a split
+// inner dimension.
+bool tile_reads_kmajor(const TileCfg &c, const Problem &pb)
+{
+    if (c.kind == kFootprint)
+        return c.ns == 9 && c.name[0] == 't';
+    return c.kind == kIm2col && c.bk == 64 && (c.tn == 64 || c.tn == 128 || c.tn == 256) && pb.C % c.bk == 0 &&
+           !pb.split_ok;
+}
 
 const char *env_tile() { return getenv("CONV_I8_TILE"); }
 
@@ -809,7 +836,7 @@ conv_i8_status_t make_plan(const Problem &pb, const void *x_ptr, const void *w_p
         pl->batch_chunk = std::max<int64_t>(pb.N, 1);
         return CONV_I8_OK;
     }
-    if (pl->repack_w && tile_reads_kmajor(c) && kmajor_ok(pb, w_ptr)) {
+    if (pl->repack_w && tile_reads_kmajor(c, pb) && kmajor_ok(pb, w_ptr)) {
         // the filter is read in place (no repack, its workspace region
         // dropped: it was the last one)
         int64_t sp;
@@ -1667,10 +1694,20 @@ conv_i8_status_t dgrad_pack_plan(const DgradProblem &dp, const void *dy_ptr, con
     conv_i8_status_t st = dgrad_phases(
         dp, dy_ptr, w_ptr, nullptr, mode,
         [&](const conv_i8_desc_t *img, const void *x, const conv_i8_desc_t *flt, const void *w,
-            const conv_i8_desc_t *, void *, const int64_t *, const int64_t *, const int64_t *,
-            const int64_t *, int32_t) {
+            const conv_i8_desc_t *out, void *, const int64_t *pre_, const int64_t *post_,
+            const int64_t *stride_, const int64_t *dil_, int32_t m) {
             if (flt->dims[1] == 0)
                 return CONV_I8_OK;         // a phase no tap reaches: zero channels, no filter
+            {
+                // a phase whose kernel reads its filter view in place, k-major:
+                // nothing to pack (the others, if any, repack their own view)
+                Problem ppb;
+                Plan ppl;
+                if (prepare(img, x, flt, w, out, pre_, post_, stride_, dil_, &ppb, &ppl, CONV_I8_DT_INT32, m) ==
+                        CONV_I8_OK &&
+                    ppl.kmaj)
+                    ok = false;
+            }
             T4 ti;
             conv_i8_status_t s1 = read_desc(img, CONV_I8_DT_INT8, &ti);
             if (s1 != CONV_I8_OK)

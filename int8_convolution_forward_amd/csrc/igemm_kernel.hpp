@@ -44,7 +44,11 @@
 
 namespace convi8 {
 
-template <int TM, int TN, int BK, int NS, int WGM, int WGN, bool FLAT, bool PIX_J, int EPI>
+// KMAJ: the filter is read in place k-major (output channels contiguous, fK
+// the stride of one input channel; blocked order only): a filter stage holds
+// BK input-channel rows of TN output channels and its fragments are formed by
+// LDS transposing reads, as in the 3x3 ring kernel.
+template <int TM, int TN, int BK, int NS, int WGM, int WGN, bool FLAT, bool PIX_J, int EPI, bool KMAJ = false>
 __global__ __launch_bounds__(64 * WGM * WGN) void conv_igemm_kernel(IgemmArgs a)
 {
     constexpr int NW = WGM * WGN;           // waves per workgroup (WGM x WGN grid)
@@ -63,6 +67,8 @@ __global__ __launch_bounds__(64 * WGM * WGN) void conv_igemm_kernel(IgemmArgs a)
     static_assert(TM % (NW * RPI) == 0 && TN % (NW * RPI) == 0, "tile rows must fill wave loads");
     static_assert(NW == 4 || NW == 8, "4 or 8 waves");
     static_assert(NS >= 2 && (NS - 2) * LPS < 64, "pipeline depth");
+    static_assert(!KMAJ || (!FLAT && (TN == 64 || TN == 128 || TN == 256)), "k-major filter stages");
+    constexpr int KRB = 1024 / TN;          // k-major: input-channel rows per 1 KB wave load
 
     __shared__ __attribute__((aligned(1024))) int8_t smem[NS * STAGE];
     __shared__ int out_row[PIX_J ? 1 : TM];
@@ -99,11 +105,21 @@ __global__ __launch_bounds__(64 * WGM * WGN) void conv_igemm_kernel(IgemmArgs a)
             a_off[i] = 0;
         }
     }
+    // k-major filter rows: 16-byte chunk position q of input-channel row kr
+    // holds global chunk q ^ kmaj_swz(kr), so that the eight rows of one
+    // transposing read sit in eight different bank groups
+    auto kmaj_swz = [](int kr) { return TN == 64 ? (kr >> 1) & 3 : kr & 7; };
     int b_off[BL];
 #pragma unroll
     for (int i = 0; i < BL; ++i) {
-        const int k = n0 + row0 + i * NW * RPI;
-        b_off[i] = k < a.K ? k * a.fK + (FLAT ? 0 : j * 16) : kOutOfRange;
+        if constexpr (KMAJ) {
+            const int kr = (i * NW + wave) * KRB + lane / (TN / 16);
+            const int col = n0 + (((lane % (TN / 16)) ^ kmaj_swz(kr)) << 4);
+            b_off[i] = col < a.K ? kr * a.fK + col : kOutOfRange;
+        } else {
+            const int k = n0 + row0 + i * NW * RPI;
+            b_off[i] = k < a.K ? k * a.fK + (FLAT ? 0 : j * 16) : kOutOfRange;
+        }
     }
     if constexpr (!PIX_J) {
         if (!a.pix_linear)
@@ -151,7 +167,7 @@ __global__ __launch_bounds__(64 * WGM * WGN) void conv_igemm_kernel(IgemmArgs a)
         rdh = live ? r * a.dilH : -0x20000000;  // dead stage: every row fails the bounds test
         sdw = s * a.dilW;
         itoff = rdh * a.sH + sdw * a.sW + cpos;
-        ftoff = live ? a.flt0 + r * a.fR + s * a.fS + cpos : kOutOfRange;
+        ftoff = live ? a.flt0 + r * a.fR + s * a.fS + (KMAJ ? cpos * a.fK : cpos) : kOutOfRange;
         lbase = smem_lds + slot * STAGE + wave * 1024;
     };
     auto dma_one = [&](int i) {  // i < LPS, compile-time after unrolling
@@ -201,6 +217,20 @@ __global__ __launch_bounds__(64 * WGM * WGN) void conv_igemm_kernel(IgemmArgs a)
     v4i frag[2][KS][FM + FN];
     auto read_one = [&](int buf, int slot, int i) {  // i < NRD
         const int ks = i / (FM + FN), f = i % (FM + FN);
+        if (KMAJ && f >= FM) {
+            // two transposing reads (rows kr .. kr+7, kr+8 .. kr+15): lane
+            // i of each 16-lane group gets byte i % 8 of the rows lanes
+            // 2b + i / 8 address, so lane j addresses row kr + j / 2 at
+            // output channel col + 8 (j & 1)
+            const int jj = lane & 15;
+            const int col = wn + (f - FM) * 32 + ((lane >> 4) & 1) * 16 + (jj & 1) * 8;
+            const int kr = ks * 32 + (lane >> 5) * 16 + (jj >> 1);
+            const int8_t *p = smem + slot * STAGE + A_BYTES + kr * TN + (((col >> 4) ^ kmaj_swz(kr)) << 4) + (col & 8);
+            const v2i lo = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_v2i *)p);
+            const v2i hi = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_v2i *)(p + 8 * TN));
+            frag[buf][ks][f] = v4i{lo.x, lo.y, hi.x, hi.y};
+            return;
+        }
         const int ch = ks * 2 + (lane >> 5);
         const int row = (f < FM ? wm + f * 32 : wn + (f - FM) * 32) + (lane & 31);
         const int8_t *base = smem + slot * STAGE + (f < FM ? 0 : A_BYTES);

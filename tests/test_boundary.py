@@ -260,15 +260,16 @@ def _plan_raw(x, w, y, wptr, pre=(1, 1), post=(1, 1), st=(1, 1), dl=(1, 1)):
 def test_kmajor_filter_plans(monkeypatch):
     """A filter whose output channels are contiguous (an R, S, C, K filter, or
     the data gradient's view of a KRSC filter) is read in place by the 3x3
-    tail tiles (no repack, no filter workspace); a misaligned pointer, K not a
-    multiple of 16, C not a multiple of 64 or another tile repack it."""
+    tail tiles and by the im2col tiles of 64-channel stages over 64, 128 or
+    256 columns (no repack, no filter workspace); a misaligned pointer, K not
+    a multiple of 16, C not a multiple of 64 or another tile repack it."""
     monkeypatch.delenv("CONV_I8_TILE", raising=False)
     D = ci8.desc
     N, C, H, W, K = 8, 128, 14, 14, 96
     x = D((N, C, H, W), wl.channels_last_strides((N, C, H, W)), 1)
     y = D((N, K, H, W), wl.channels_last_strides((N, K, H, W)), 2)
     hwio = lambda k, c: D((k, c, 3, 3), (1, k, 3 * c * k, c * k), 1)       # [R][S][C][K] storage
-    for tile in ("t256x128", "t128x128"):
+    for tile in ("t256x128", "t128x128", "64x64x64", "128x128x64", "w256x128x64"):
         monkeypatch.setenv("CONV_I8_TILE", tile)
         f = _plan_raw(x, hwio(K, C), y, FAKE)
         assert (f["tile"], f["filter_read"], f["repack_filter"], f["workspace"]) == (tile, "kmajor", "0", "0"), f
@@ -278,10 +279,10 @@ def test_kmajor_filter_plans(monkeypatch):
         assert _plan_raw(x, hwio(88, C), yk, FAKE)["filter_read"] == "packed"
         x96 = D((N, 96, H, W), wl.channels_last_strides((N, 96, H, W)), 1)
         assert _plan_raw(x96, hwio(K, 96), y, FAKE)["filter_read"] == "packed"
-    monkeypatch.setenv("CONV_I8_TILE", "r256x128")
-    assert _plan_raw(x, hwio(K, C), y, FAKE)["filter_read"] == "packed"
-    monkeypatch.setenv("CONV_I8_TILE", "128x128x64")
-    assert _plan_raw(x, hwio(K, C), y, FAKE)["filter_read"] == "packed"
+    for tile in ("r256x128", "128x128x128", "w128x192x128"):
+        monkeypatch.setenv("CONV_I8_TILE", tile)
+        f = _plan_raw(x, hwio(K, C), y, FAKE)
+        assert (f["tile"], f["filter_read"]) == (tile, "packed"), f
     # a channels-innermost filter stays read in place as before
     monkeypatch.setenv("CONV_I8_TILE", "t256x128")
     f = _plan_raw(x, D((K, C, 3, 3), wl.channels_last_strides((K, C, 3, 3)), 1), y, FAKE)

@@ -97,14 +97,13 @@ def test_random_dgrad_problems(ci8):
         done += 1
 
 
-@pytest.mark.parametrize("dy_layout,packed", [("nhwc", True), ("nchw", False)])
+@pytest.mark.parametrize("dy_layout", ["nhwc", "nchw"])
 @pytest.mark.parametrize("mode", [0, 1])
-def test_dgrad_phase_filters_packed_once(ci8, monkeypatch, capfd, dy_layout, packed, mode):
-    """A stride-2 layer (the downsample workload: 4 phases).  With a
-    channels-last loss every phase's filter view is packed by one repack
-    launch before the phases, so each phase plan reads its filter in place;
-    with an NCHW loss each phase repacks its part of the loss and its filter
-    in one launch of its own.  Both bit-exact."""
+def test_dgrad_phase_filters_read_kmajor(ci8, monkeypatch, capfd, dy_layout, mode):
+    """A stride-2 layer (the downsample workload: 4 phases, 64 input channels
+    per phase): every phase reads its view of the KRSC filter in place,
+    k-major, so nothing is packed; a channels-last loss is read in place, an
+    NCHW one repacked by each phase.  Bit-exact."""
     c = wl.case("downsample_s2_n8_c64_56")
     d = wl.make_inputs(c, c.seed_base + 8)
     dims = c.out.dims
@@ -113,8 +112,35 @@ def test_dgrad_phase_filters_packed_once(ci8, monkeypatch, capfd, dy_layout, pac
     dxspec = wl.TensorSpec(c.image.dims, wl.channels_last_strides(c.image.dims))
     monkeypatch.setenv("CONV_I8_LOG", "1")
     run_dgrad_check(ci8, _rand_storage(dyspec, 31 + mode), dyspec, d["w_storage"], c.filter, dxspec,
-                    c.pre, c.post, c.stride, c.dilation, mode=mode, label=f"packed {dy_layout}")
+                    c.pre, c.post, c.stride, c.dilation, mode=mode, label=f"k-major {dy_layout}")
+    logged = capfd.readouterr().err
+    plans = [ci8.plan_fields(l) for l in logged.splitlines() if "repack_filter=" in l]
+    assert len(plans) == 4, logged
+    assert all(p["repack_filter"] == "0" and p["filter_read"] == "kmajor" for p in plans), logged
+    assert all(p["repack_image"] == ("0" if dy_layout == "nhwc" else "1") for p in plans), logged
+
+
+@pytest.mark.parametrize("dy_layout,packed", [("nhwc", True), ("nchw", False)])
+@pytest.mark.parametrize("mode", [0, 1])
+def test_dgrad_phase_filters_packed_once(ci8, monkeypatch, capfd, dy_layout, packed, mode):
+    """A stride-2 layer with 48 output channels (4 phases whose 48 input
+    channels are no whole 64-channel stage, so no phase reads its filter view
+    k-major).  With a channels-last loss every phase's filter view is packed
+    by one repack launch before the phases, so each phase plan reads its
+    filter in place; with an NCHW loss each phase repacks its part of the
+    loss and its filter in one launch of its own.  Both bit-exact."""
+    N, C, H, W, K = 4, 64, 20, 20, 48
+    pre, post, st, dl = (1, 1), (1, 1), (2, 2), (1, 1)
+    wspec = wl.TensorSpec((K, C, 3, 3), wl.channels_last_strides((K, C, 3, 3)))
+    dims = oracle.out_dims((N, C, H, W), (K, C, 3, 3), pre, post, st, dl)
+    strides = wl.channels_last_strides(dims) if dy_layout == "nhwc" else wl.contiguous_strides(dims)
+    dyspec = wl.TensorSpec(dims, strides)
+    dxspec = wl.TensorSpec((N, C, H, W), wl.channels_last_strides((N, C, H, W)))
+    monkeypatch.setenv("CONV_I8_LOG", "1")
+    run_dgrad_check(ci8, _rand_storage(dyspec, 31 + mode), dyspec, _rand_storage(wspec, 41 + mode), wspec, dxspec,
+                    pre, post, st, dl, mode=mode, label=f"packed {dy_layout}")
     logged = capfd.readouterr().err
     plans = [ci8.plan_fields(l) for l in logged.splitlines() if "repack_filter=" in l]
     assert len(plans) == 4, logged
     assert all(p["repack_filter"] == ("0" if packed else "1") for p in plans), logged
+    assert not any(p["filter_read"] == "kmajor" for p in plans), logged

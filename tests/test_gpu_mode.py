@@ -128,13 +128,13 @@ def test_tile_shapes_convolution_mode(ci8, monkeypatch, tile, R, S, C, out_layou
                    label=f"tile {tile} {R}x{S} C={C} {out_layout}")
 
 
-@pytest.mark.parametrize("tile", ["t256x128", "t128x128"])
+@pytest.mark.parametrize("tile", ["t256x128", "t128x128", "64x64x64", "128x128x64", "w256x128x64"])
 @pytest.mark.parametrize("mode", [0, 1])
 @pytest.mark.parametrize("out_layout", ["nhwc", "nchw"])
 def test_kmajor_filter_modes_and_requant(ci8, monkeypatch, tile, mode, out_layout):
-    """Filters stored R, S, C, K, read k-major by the 3x3 tail tiles: both tap
-    orders, INT32 output and the requantising tail, a ragged second column
-    tile (K = 144)."""
+    """Filters stored R, S, C, K, read k-major by the 3x3 tail tiles and the
+    im2col tiles: both tap orders, INT32 output and the requantising
+    epilogues, a ragged second column tile (K = 144)."""
     monkeypatch.setenv("CONV_I8_TILE", tile)
     N, C, H, W, K = 3, 128, 9, 12, 144
     pre, post, st, dl = (1, 1), (1, 1), (1, 1), (1, 1)

@@ -403,6 +403,40 @@ def test_footprint_kernel_kmajor_filter(ci8, monkeypatch, tile, case_i, out_layo
                   label=f"k-major filter {tile} case {case_i}")
 
 
+# The im2col tiles of 64-channel stages over 64, 128 or 256 columns read such
+# filters in place too (blocked order), with any filter size, stride and
+# dilation: ragged column tiles, both output layouts.
+KMAJOR_IM2COL_TILES = ["64x64x64", "128x64x64", "64x128x64", "128x128x64", "256x128x64", "128x256x64",
+                       "w256x128x64", "w128x128x64"]
+KMAJOR_IM2COL_CASES = [
+    # N, C, H, W, K, R, S, stride, dil, pre, post
+    (2, 64, 9, 11, 80, 1, 1, (1, 1), (1, 1), (0, 0), (0, 0)),
+    (3, 128, 10, 7, 144, 3, 3, (2, 2), (1, 1), (1, 1), (1, 1)),
+    (2, 64, 12, 13, 48, 3, 5, (2, 1), (2, 2), (2, 1), (1, 3)),
+    (1, 192, 6, 6, 272, 2, 3, (1, 1), (1, 1), (0, 1), (1, 0)),
+]
+
+
+@pytest.mark.parametrize("tile", KMAJOR_IM2COL_TILES)
+@pytest.mark.parametrize("case_i", range(len(KMAJOR_IM2COL_CASES)))
+@pytest.mark.parametrize("out_layout", ["nhwc", "nchw"])
+def test_im2col_kmajor_filter(ci8, monkeypatch, tile, case_i, out_layout):
+    N, C, H, W, K, R, S, st, dl, pre, post = KMAJOR_IM2COL_CASES[case_i]
+    monkeypatch.setenv("CONV_I8_TILE", tile)
+    od = oracle.out_dims((N, C, H, W), (K, C, R, S), pre, post, st, dl)
+    xs = wl.TensorSpec((N, C, H, W), wl.channels_last_strides((N, C, H, W)))
+    ws = wl.TensorSpec((K, C, R, S), _rsck_strides(K, C, R, S))
+    os_ = wl.TensorSpec(od, wl.channels_last_strides(od) if out_layout == "nhwc" else wl.contiguous_strides(od))
+    plan = ci8.plan_fields(ci8.conv_fprop_i8_plan(ci8.desc(xs.dims, xs.strides, 1), ci8.desc(ws.dims, ws.strides, 1),
+                                                  ci8.desc(os_.dims, os_.strides, 2), pre, post, st, dl))
+    assert (plan["tile"], plan["filter_read"], plan["order"]) == (tile, "kmajor", "blocked"), plan
+    g = torch.Generator().manual_seed(70 + case_i)
+    xv = torch.randint(-128, 128, (N, C, H, W), dtype=torch.int8, generator=g)
+    wv = torch.randint(-128, 128, (K, C, R, S), dtype=torch.int8, generator=g)
+    run_and_check(ci8, _fill(xs, xv, 1), xs, _fill(ws, wv, 2), ws, os_, pre, post, st, dl,
+                  label=f"k-major filter {tile} case {case_i}")
+
+
 # ---------------------------------------------------------------------------
 # The 1x1 streaming kernel: ragged pixel counts (not a multiple of 32 or of a
 # wave's four tiles), ragged output channels and channels, stride and padding
