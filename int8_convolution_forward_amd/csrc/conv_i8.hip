@@ -223,10 +223,10 @@ conv_i8_status_t analyze(const conv_i8_desc_t *image, const conv_i8_desc_t *filt
 // ---------------------------------------------------------------------------
 using Launcher = void (*)(bool flat, bool pix_j, dim3 grid, hipStream_t stream, const IgemmArgs &a);
 
-// im2col tiles whose filter stages can be read k-major (blocked order only,
-// and not the split epilogue): 64-channel stages of 64, 128 or 256 columns
+// im2col tiles whose filter stages can be read k-major (blocked order only):
+// 64-channel stages of 64, 128 or 256 columns
 template <int TN, int BK, int EPI>
-constexpr bool kmajor_tile() { return BK == 64 && (TN == 64 || TN == 128 || TN == 256) && EPI != kEpiSplit; }
+constexpr bool kmajor_tile() { return BK == 64 && (TN == 64 || TN == 128 || TN == 256); }
 
 template <int TM, int TN, int BK, int NS, int WGM, int WGN, int EPI>
 void launch_cfg_epi(bool flat, bool pix_j, dim3 grid, hipStream_t stream, const IgemmArgs &a)
@@ -533,14 +533,13 @@ bool kmajor_ok(const Problem &pb, const void *ptr)
 
 // Tiles that read a k-major filter: the 3x3 tail tiles, and im2col tiles of
 // 64-channel stages over 64, 128 or 256 columns in blocked order (the
-// instantiations launch_cfg_epi and launch_fp9 provide); not with a split
-// inner dimension.
+// instantiations launch_cfg_epi and launch_fp9 provide), split inner
+// dimension included (the weight gradient's transposed loss).
 bool tile_reads_kmajor(const TileCfg &c, const Problem &pb)
 {
     if (c.kind == kFootprint)
         return c.ns == 9 && c.name[0] == 't';
-    return c.kind == kIm2col && c.bk == 64 && (c.tn == 64 || c.tn == 128 || c.tn == 256) && pb.C % c.bk == 0 &&
-           !pb.split_ok;
+    return c.kind == kIm2col && c.bk == 64 && (c.tn == 64 || c.tn == 128 || c.tn == 256) && pb.C % c.bk == 0;
 }
 
 const char *env_tile() { return getenv("CONV_I8_TILE"); }

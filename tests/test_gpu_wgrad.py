@@ -98,6 +98,26 @@ def test_random_wgrad_problems(ci8):
         done += 1
 
 
+@pytest.mark.parametrize("tile,mode", [("w256x128x64", 0), ("128x128x64", 1), ("256x128x64", 0)])
+def test_wgrad_kmajor_loss(ci8, monkeypatch, tile, mode):
+    """The large-channel layer's weight gradient on tiles that read the
+    transposed loss (channels-last, 64 images: [K, N, P, Q] with K
+    contiguous) in place, k-major, with the reduction split over workgroups
+    into partial copies; both modes."""
+    c = wl.case("large_channel_n64_c512_14")
+    monkeypatch.setenv("CONV_I8_TILE", tile)
+    d = wl.make_inputs(c, c.seed_base + 9)
+    dyspec = wl.TensorSpec(c.out.dims, c.out.strides)
+    dwspec = wl.TensorSpec(c.filter.dims, c.filter.strides)
+    f = ci8.plan_fields(ci8.conv_wgrad_i8_plan(ci8.desc(c.image.dims, c.image.strides, ci8.DT_INT8),
+                                               ci8.desc(dyspec.dims, dyspec.strides, ci8.DT_INT8),
+                                               ci8.desc(dwspec.dims, dwspec.strides, ci8.DT_INT32),
+                                               c.pre, c.post, c.stride, c.dilation, mode=mode))
+    assert (f["tile"], f["filter_read"], f["split_sum"]) == (tile, "kmajor", "partial"), f
+    run_wgrad_check(ci8, d["x_storage"], c.image, _rand_storage(dyspec, 17 + mode), dyspec, dwspec,
+                    c.pre, c.post, c.stride, c.dilation, mode=mode, label=f"k-major loss {tile}")
+
+
 @pytest.mark.parametrize("N", [3, 6, 20, 32])
 def test_wgrad_small_batch_transposes(ci8, N):
     """Channels-last operands with a small batch: the transposed views have
