@@ -222,6 +222,8 @@ conv_i8_status_t analyze(const conv_i8_desc_t *image, const conv_i8_desc_t *filt
 // Tile configurations instantiated for the implicit-GEMM kernels.
 // ---------------------------------------------------------------------------
 using Launcher = void (*)(bool flat, bool pix_j, dim3 grid, hipStream_t stream, const IgemmArgs &a);
+// several phases of one shape class in one launch (blocked order, k-major filters)
+using PhasesLauncher = void (*)(bool pix_j, dim3 grid, hipStream_t stream, const IgemmPhases &m);
 
 // im2col tiles whose filter stages can be read k-major (blocked order only):
 // 64-channel stages of 64, 128 or 256 columns
@@ -270,6 +272,29 @@ void launch_cfg(bool flat, bool pix_j, dim3 grid, hipStream_t stream, const Igem
         launch_cfg_epi<TM, TN, BK, NS, WGM, WGN, kEpiStream>(flat, pix_j, grid, stream, a);
     else
         launch_cfg_epi<TM, TN, BK, NS, WGM, WGN, kEpiDefault>(flat, pix_j, grid, stream, a);
+}
+
+// the phases of a strided data gradient in one launch: k-major filters, blocked
+// order, the streaming or the default store policy (the same for every phase)
+template <int TM, int TN, int BK, int NS, int WGM = 2, int WGN = 2>
+void launch_phases_cfg(bool pix_j, dim3 grid, hipStream_t stream, const IgemmPhases &m)
+{
+    const dim3 block(64 * WGM * WGN);
+    if (m.ph[0].out_nt) {
+        if (pix_j)
+            hipLaunchKernelGGL((conv_igemm_phases_kernel<TM, TN, BK, NS, WGM, WGN, false, true, kEpiStream, true>),
+                               grid, block, 0, stream, m);
+        else
+            hipLaunchKernelGGL((conv_igemm_phases_kernel<TM, TN, BK, NS, WGM, WGN, false, false, kEpiStream, true>),
+                               grid, block, 0, stream, m);
+    } else {
+        if (pix_j)
+            hipLaunchKernelGGL((conv_igemm_phases_kernel<TM, TN, BK, NS, WGM, WGN, false, true, kEpiDefault, true>),
+                               grid, block, 0, stream, m);
+        else
+            hipLaunchKernelGGL((conv_igemm_phases_kernel<TM, TN, BK, NS, WGM, WGN, false, false, kEpiDefault, true>),
+                               grid, block, 0, stream, m);
+    }
 }
 
 template <int TM, int TN, int NS, int FPIX, int WGM = 2, int WGN = 2, int KSPL = 1>
@@ -327,13 +352,17 @@ struct TileCfg {
     int fpix;          // footprint capacity (pixels)
     double eff;        // relative MFMA efficiency of this tile shape (cost model)
     Launcher launch;   // the kernel instantiation with exactly these parameters
+    PhasesLauncher launch_phases;   // several phases in one launch, or nullptr
 };
 
 const TileCfg kTiles[] = {
-    {"64x64x64", 64, 64, 64, 4, 4, kIm2col, 0, 0.40, launch_cfg<64, 64, 64, 4>},
-    {"128x64x64", 128, 64, 64, 4, 4, kIm2col, 0, 0.48, launch_cfg<128, 64, 64, 4>},
-    {"64x128x64", 64, 128, 64, 4, 4, kIm2col, 0, 0.48, launch_cfg<64, 128, 64, 4>},
-    {"128x128x64", 128, 128, 64, 4, 4, kIm2col, 0, 0.59, launch_cfg<128, 128, 64, 4>},
+    {"64x64x64", 64, 64, 64, 4, 4, kIm2col, 0, 0.40, launch_cfg<64, 64, 64, 4>, launch_phases_cfg<64, 64, 64, 4>},
+    {"128x64x64", 128, 64, 64, 4, 4, kIm2col, 0, 0.48, launch_cfg<128, 64, 64, 4>,
+     launch_phases_cfg<128, 64, 64, 4>},
+    {"64x128x64", 64, 128, 64, 4, 4, kIm2col, 0, 0.48, launch_cfg<64, 128, 64, 4>,
+     launch_phases_cfg<64, 128, 64, 4>},
+    {"128x128x64", 128, 128, 64, 4, 4, kIm2col, 0, 0.59, launch_cfg<128, 128, 64, 4>,
+     launch_phases_cfg<128, 128, 64, 4>},
     {"128x128x128", 128, 128, 128, 3, 4, kIm2col, 0, 0.55, launch_cfg<128, 128, 128, 3>},
     {"256x128x64", 256, 128, 64, 4, 4, kIm2col, 0, 0.52, launch_cfg<256, 128, 64, 4>},
     {"128x256x64", 128, 256, 64, 4, 4, kIm2col, 0, 0.50, launch_cfg<128, 256, 64, 4>},
@@ -1037,29 +1066,12 @@ conv_i8_status_t launch_repacks(const RepackJob *jobs, int njobs, hipStream_t st
 long long *g_phase_clk = nullptr;
 #endif
 
-conv_i8_status_t run(const Problem &pb, const Plan &pl, const void *x_ptr, const void *w_ptr,
-                     void *y_ptr, void *ws, hipStream_t stream, const conv_i8_requant_t *rq = nullptr)
+// The arguments of an implicit-GEMM launch (3x3, im2col or 1x1 kernel) that
+// do not depend on the batch chunk; w is the filter as the kernel reads it
+// (its packed copy when the plan repacks it).
+IgemmArgs make_args(const Problem &pb, const Plan &pl, const TileCfg &c, const int8_t *w, void *y_ptr,
+                    const conv_i8_requant_t *rq)
 {
-    if (kTiles[pl.cfg].kind == kDirect)
-        return launch_direct(pb, x_ptr, w_ptr, y_ptr, stream, rq);
-    const int64_t esize = rq ? 1 : 4;        // bytes per output element
-    const int8_t *x = (const int8_t *)x_ptr;
-    const int8_t *w = (const int8_t *)w_ptr;
-    int8_t *wsb = (int8_t *)ws;
-    conv_i8_status_t st;
-    RepackJob jobs[2];
-    int njobs = 0;
-    if (pl.repack_x && pb.C > 0) {
-        jobs[njobs++] = repack_job(pb.x, x, wsb + pl.ws_x_off, pl.Cp);
-        x = wsb + pl.ws_x_off;
-    }
-    if (pl.repack_w && pb.C > 0) {
-        jobs[njobs++] = repack_job(pb.w, w, wsb + pl.ws_w_off, pl.Cp);
-        w = wsb + pl.ws_w_off;
-    }
-    if (njobs > 0 && (st = launch_repacks(jobs, njobs, stream)) != CONV_I8_OK)
-        return st;
-    const TileCfg &c = kTiles[pl.cfg];
     IgemmArgs a{};
     a.flt = w;
     a.flt_range = (int)pl.w_span;
@@ -1138,26 +1150,65 @@ conv_i8_status_t run(const Problem &pb, const Plan &pl, const void *x_ptr, const
         a.q8_pack = pl.pix_linear && !pl.pix_j && pb.y.s[1] == 1 && pl.pix_stride % 4 == 0 &&
                     pb.K % 4 == 0 && ((uintptr_t)y_ptr & 3u) == 0 ? 1 : 0;
     }
+    return a;
+}
+
+// Batch chunk [n0, n0 + nb) of a launch: the image and output windows and
+// the tile count (0: nothing to launch).
+int64_t set_chunk(IgemmArgs &a, const Problem &pb, const Plan &pl, const TileCfg &c, const int8_t *x,
+                  void *y_ptr, int64_t n0, int64_t esize)
+{
+    const int64_t nb = std::min(pl.batch_chunk, pb.N - n0);
+    a.img = x + n0 * pl.xsN;
+    a.img_range = (int)((nb - 1) * pl.xsN + pl.x_img_span);
+    a.out = (int32_t *)((int8_t *)y_ptr + n0 * pb.y.s[0] * esize);
+    a.out_range = (int)(((nb - 1) * pb.y.s[0] + pl.y_img_span) * esize);
+    a.N = (int)nb;
+    a.sN = (int)pl.xsN;
+    a.M = (int)(nb * pb.P * pb.Q);
+    int64_t tiles = ((a.M + c.tm - 1) / c.tm) * (int64_t)a.tiles_n;
+    if (c.kind == kPointwise) {
+        // workgroups of four waves, each wave up to kPointwiseTilesPerWave
+        // 32-pixel tiles; at least one workgroup per CU while there is work
+        const int64_t t32 = (a.M + 31) / 32;
+        tiles = std::max((t32 + 4 * kPointwiseTilesPerWave - 1) / (4 * kPointwiseTilesPerWave),
+                         std::min<int64_t>(kCUs, (t32 + 3) / 4));
+    }
+    if (tiles == 0)
+        return 0;
+    a.tiles = (int)tiles;
+    return tiles;
+}
+
+conv_i8_status_t run(const Problem &pb, const Plan &pl, const void *x_ptr, const void *w_ptr,
+                     void *y_ptr, void *ws, hipStream_t stream, const conv_i8_requant_t *rq = nullptr)
+{
+    if (kTiles[pl.cfg].kind == kDirect)
+        return launch_direct(pb, x_ptr, w_ptr, y_ptr, stream, rq);
+    const int64_t esize = rq ? 1 : 4;        // bytes per output element
+    const int8_t *x = (const int8_t *)x_ptr;
+    const int8_t *w = (const int8_t *)w_ptr;
+    int8_t *wsb = (int8_t *)ws;
+    conv_i8_status_t st;
+    RepackJob jobs[2];
+    int njobs = 0;
+    if (pl.repack_x && pb.C > 0) {
+        jobs[njobs++] = repack_job(pb.x, x, wsb + pl.ws_x_off, pl.Cp);
+        x = wsb + pl.ws_x_off;
+    }
+    if (pl.repack_w && pb.C > 0) {
+        jobs[njobs++] = repack_job(pb.w, w, wsb + pl.ws_w_off, pl.Cp);
+        w = wsb + pl.ws_w_off;
+    }
+    if (njobs > 0 && (st = launch_repacks(jobs, njobs, stream)) != CONV_I8_OK)
+        return st;
+    const TileCfg &c = kTiles[pl.cfg];
+    IgemmArgs a = make_args(pb, pl, c, w, y_ptr, rq);
     for (int64_t n0 = 0; n0 < pb.N; n0 += pl.batch_chunk) {
         const int64_t nb = std::min(pl.batch_chunk, pb.N - n0);
-        a.img = x + n0 * pl.xsN;
-        a.img_range = (int)((nb - 1) * pl.xsN + pl.x_img_span);
-        a.out = (int32_t *)((int8_t *)y_ptr + n0 * pb.y.s[0] * esize);
-        a.out_range = (int)(((nb - 1) * pb.y.s[0] + pl.y_img_span) * esize);
-        a.N = (int)nb;
-        a.sN = (int)pl.xsN;
-        a.M = (int)(nb * pb.P * pb.Q);
-        int64_t tiles = ((a.M + c.tm - 1) / c.tm) * (int64_t)a.tiles_n;
-        if (c.kind == kPointwise) {
-            // workgroups of four waves, each wave up to kPointwiseTilesPerWave
-            // 32-pixel tiles; at least one workgroup per CU while there is work
-            const int64_t t32 = (a.M + 31) / 32;
-            tiles = std::max((t32 + 4 * kPointwiseTilesPerWave - 1) / (4 * kPointwiseTilesPerWave),
-                             std::min<int64_t>(kCUs, (t32 + 3) / 4));
-        }
+        const int64_t tiles = set_chunk(a, pb, pl, c, x, y_ptr, n0, esize);
         if (tiles == 0)
             continue;
-        a.tiles = (int)tiles;
         unsigned ksplit = 1;
         int32_t *const out_chunk = a.out;
         const int64_t chunk_span = (nb - 1) * pb.y.s[0] + pl.y_img_span;
@@ -1790,6 +1841,84 @@ conv_i8_status_t dgrad_workspace(const DgradProblem &dp, const void *dy_ptr, con
     return st;
 }
 
+// The phases of a strided data gradient in one launch, when every phase reads
+// its loss and its filter view in place (channels-last loss, k-major view)
+// on one im2col tile with one store policy, in one batch chunk: workgroups
+// [first[p], first[p+1]) run phase p.  The phases write disjoint elements of
+// dX, so running them together gives the bytes of running them in order.
+// *done is false (and nothing is launched) when the phases do not qualify.
+conv_i8_status_t dgrad_one_launch(const DgradProblem &dp, const void *loss_ptr, const void *filter_ptr,
+                                  void *dx_ptr, int32_t mode, hipStream_t stream, bool *done)
+{
+    *done = false;
+    struct Phase {
+        Problem pb;
+        Plan pl;
+        const void *x, *w;
+        void *y;
+    };
+    Phase ph[kMaxPhases];
+    int n = 0;
+    bool ok = true;
+    conv_i8_status_t st = dgrad_phases(
+        dp, loss_ptr, filter_ptr, dx_ptr, mode,
+        [&](const conv_i8_desc_t *img, const void *x, const conv_i8_desc_t *flt, const void *w,
+            const conv_i8_desc_t *out, void *y, const int64_t *pre_, const int64_t *post_, const int64_t *stride_,
+            const int64_t *dil_, int32_t m) {
+            if (!ok)
+                return CONV_I8_OK;
+            if (n >= kMaxPhases || flt->dims[1] == 0) {
+                ok = false;        // too many phases, or one that no tap reaches
+                return CONV_I8_OK;
+            }
+            Phase &p = ph[n++];
+            conv_i8_status_t r = prepare(img, x, flt, w, out, pre_, post_, stride_, dil_, &p.pb, &p.pl,
+                                         CONV_I8_DT_INT32, m);
+            if (r != CONV_I8_OK)
+                return r;
+            p.x = x;
+            p.w = w;
+            p.y = y;
+            const TileCfg &c = kTiles[p.pl.cfg];
+            if (!c.launch_phases || p.pl.repack_x || p.pl.repack_w || !p.pl.kmaj || !p.pl.blocked ||
+                p.pl.ksplit > 1 || p.pl.batch_chunk < p.pb.N || p.pb.C == 0 || p.pb.y.elems() == 0)
+                ok = false;
+            if (n > 1 && (p.pl.cfg != ph[0].pl.cfg || p.pl.pix_j != ph[0].pl.pix_j))
+                ok = false;
+            return CONV_I8_OK;
+        });
+    if (st != CONV_I8_OK || !ok || n < 2)
+        return st;
+    const TileCfg &c = kTiles[ph[0].pl.cfg];
+    IgemmPhases m{};
+    int64_t total = 0;
+    for (int i = 0; i < n; ++i) {
+        IgemmArgs a = make_args(ph[i].pb, ph[i].pl, c, (const int8_t *)ph[i].w, ph[i].y, nullptr);
+        const int64_t tiles = set_chunk(a, ph[i].pb, ph[i].pl, c, (const int8_t *)ph[i].x, ph[i].y, 0, 4);
+        if (tiles == 0 || (i > 0 && a.out_nt != m.ph[0].out_nt))
+            return CONV_I8_OK;   // one store policy for every phase
+        m.ph[i] = a;
+        m.first[i] = (int)total;
+        total += tiles;
+        if (total > kI32Max)
+            return CONV_I8_OK;
+    }
+    for (int i = n; i <= kMaxPhases; ++i)
+        m.first[i] = (int)total;
+    m.nph = n;
+    if (log_enabled()) {
+        for (int i = 0; i < n; ++i)
+            fprintf(stderr, "conv_i8%s: %s\n", mode == CONV_I8_MODE_CONVOLUTION ? " (convolution)" : "",
+                    describe(ph[i].pb, ph[i].pl).c_str());
+        fprintf(stderr, "conv_i8: %d data-gradient phases in one launch of %lld workgroups\n", n, (long long)total);
+    }
+    c.launch_phases(ph[0].pl.pix_j, dim3((unsigned)total), stream, m);
+    if (hipGetLastError() != hipSuccess)
+        return CONV_I8_ERR_HIP;
+    *done = true;
+    return CONV_I8_OK;
+}
+
 conv_i8_status_t dgrad_entry(const conv_i8_desc_t *loss, const void *loss_ptr,
                              const conv_i8_desc_t *filter, const void *filter_ptr,
                              const conv_i8_desc_t *dx, void *dx_ptr, const int64_t *pre,
@@ -1822,6 +1951,15 @@ conv_i8_status_t dgrad_entry(const conv_i8_desc_t *loss, const void *loss_ptr,
             return CONV_I8_ERR_NULL;
         if (need > 0 && ((uintptr_t)workspace & 255u) != 0)
             return CONV_I8_ERR_WORKSPACE;
+    }
+    if (!pk.on) {
+        bool done = false;
+        st = dgrad_one_launch(dp, loss_ptr, filter_ptr, dx_ptr, mode, s, &done);
+        if (st != CONV_I8_OK || done) {
+            if (alloc && ws && hipFreeAsync(ws, s) != hipSuccess && st == CONV_I8_OK)
+                st = CONV_I8_ERR_HIP;
+            return st;
+        }
     }
     if (pk.on) {
         // every phase's filter view packed in one launch

@@ -48,8 +48,10 @@ namespace convi8 {
 // the stride of one input channel; blocked order only): a filter stage holds
 // BK input-channel rows of TN output channels and its fragments are formed by
 // LDS transposing reads, as in the 3x3 ring kernel.
-template <int TM, int TN, int BK, int NS, int WGM, int WGN, bool FLAT, bool PIX_J, int EPI, bool KMAJ = false>
-__global__ __launch_bounds__(64 * WGM * WGN) void conv_igemm_kernel(IgemmArgs a)
+// One workgroup's tile: workgroup bx of the launch's tiles, split by of the
+// inner dimension (the kernels below run it with their block index).
+template <int TM, int TN, int BK, int NS, int WGM, int WGN, bool FLAT, bool PIX_J, int EPI, bool KMAJ>
+__device__ __forceinline__ void igemm_tile(const IgemmArgs &a, int bx, int by)
 {
     constexpr int NW = WGM * WGN;           // waves per workgroup (WGM x WGN grid)
     constexpr int CPS = BK / 16;            // 16-byte chunks per row per stage
@@ -76,7 +78,7 @@ __global__ __launch_bounds__(64 * WGM * WGN) void conv_igemm_kernel(IgemmArgs a)
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int tile = xcd_tile(blockIdx.x, a.tiles);
+    const int tile = xcd_tile(bx, a.tiles);
     const int m0 = (tile / a.tiles_n) * TM;
     const int n0 = (tile % a.tiles_n) * TN;
 
@@ -131,7 +133,7 @@ __global__ __launch_bounds__(64 * WGM * WGN) void conv_igemm_kernel(IgemmArgs a)
     // with selects; flat: each thread's chunk index g = stage*CPS + j is split
     // into (r, s, c16) afresh for every stage.
     // split z of the inner dimension: stages [stage0, stage_end)
-    const int stage0 = (int)blockIdx.y * a.kchunk;
+    const int stage0 = by * a.kchunk;
     const int stage_end = min(a.nstages, stage0 + a.kchunk);
     int r = 0, s = 0, cpos = 0;
     int issued = stage0;
@@ -302,6 +304,34 @@ __global__ __launch_bounds__(64 * WGM * WGN) void conv_igemm_kernel(IgemmArgs a)
 
     // ---- epilogue ---------------------------------------------------------
     store_tile_any<FM, FN, PIX_J, EPI>(a, acc, m0, n0, wm, wn, lane, out_row);
+}
+
+template <int TM, int TN, int BK, int NS, int WGM, int WGN, bool FLAT, bool PIX_J, int EPI, bool KMAJ = false>
+__global__ __launch_bounds__(64 * WGM * WGN) void conv_igemm_kernel(IgemmArgs a)
+{
+    igemm_tile<TM, TN, BK, NS, WGM, WGN, FLAT, PIX_J, EPI, KMAJ>(a, blockIdx.x, blockIdx.y);
+}
+
+// Several convolutions of one shape class in one launch (the stride phases
+// of a data gradient): workgroups [first[p], first[p+1]) run phase p with its
+// own arguments; every phase uses the same tile, order, layout and epilogue.
+constexpr int kMaxPhases = 4;
+struct IgemmPhases {
+    IgemmArgs ph[kMaxPhases];
+    int first[kMaxPhases + 1];
+    int nph;
+};
+static_assert(sizeof(IgemmPhases) <= 4096, "the phases' arguments must fit one kernel argument block");
+
+template <int TM, int TN, int BK, int NS, int WGM, int WGN, bool FLAT, bool PIX_J, int EPI, bool KMAJ>
+__global__ __launch_bounds__(64 * WGM * WGN) void conv_igemm_phases_kernel(IgemmPhases m)
+{
+    const int b = blockIdx.x;
+    int p = 0;
+#pragma unroll
+    for (int i = 1; i < kMaxPhases; ++i)
+        p += i < m.nph && b >= m.first[i] ? 1 : 0;
+    igemm_tile<TM, TN, BK, NS, WGM, WGN, FLAT, PIX_J, EPI, KMAJ>(m.ph[p], b - m.first[p], 0);
 }
 
 // Sum of the partial outputs of a split inner dimension: out[i] = the sum

@@ -102,8 +102,9 @@ def test_random_dgrad_problems(ci8):
 def test_dgrad_phase_filters_read_kmajor(ci8, monkeypatch, capfd, dy_layout, mode):
     """A stride-2 layer (the downsample workload: 4 phases, 64 input channels
     per phase): every phase reads its view of the KRSC filter in place,
-    k-major, so nothing is packed; a channels-last loss is read in place, an
-    NCHW one repacked by each phase.  Bit-exact."""
+    k-major, so nothing is packed; a channels-last loss is read in place and
+    the four phases run in one launch, an NCHW one is repacked by each phase
+    (one launch per phase).  Bit-exact."""
     c = wl.case("downsample_s2_n8_c64_56")
     d = wl.make_inputs(c, c.seed_base + 8)
     dims = c.out.dims
@@ -118,6 +119,7 @@ def test_dgrad_phase_filters_read_kmajor(ci8, monkeypatch, capfd, dy_layout, mod
     assert len(plans) == 4, logged
     assert all(p["repack_filter"] == "0" and p["filter_read"] == "kmajor" for p in plans), logged
     assert all(p["repack_image"] == ("0" if dy_layout == "nhwc" else "1") for p in plans), logged
+    assert ("4 data-gradient phases in one launch" in logged) == (dy_layout == "nhwc"), logged
 
 
 @pytest.mark.parametrize("dy_layout,packed", [("nhwc", True), ("nchw", False)])
