@@ -97,6 +97,40 @@ def test_random_dgrad_problems(ci8):
         done += 1
 
 
+def test_random_dgrad_kmajor_problems(ci8, capfd, monkeypatch):
+    """Random layers whose filter views the kernels read k-major (KRSC or
+    R, S, C, K filters, K a multiple of 64, C a multiple of 16) with a
+    channels-last loss: strides 1-3 (one launch for up to four phases),
+    dilation, padding past the taps' reach, non-square filters, both modes;
+    the k-major reads and the one-launch path must both occur."""
+    rng = np.random.default_rng(97)
+    monkeypatch.setenv("CONV_I8_LOG", "1")
+    done = 0
+    while done < 30:
+        N, K, C = int(rng.integers(1, 4)), 64 * int(rng.integers(1, 3)), 16 * int(rng.integers(1, 7))
+        H, W = (int(v) for v in rng.integers(3, 18, 2))
+        R, S = (int(v) for v in rng.integers(1, 5, 2))
+        pre = tuple(int(v) for v in rng.integers(0, 4, 2))
+        post = tuple(int(v) for v in rng.integers(0, 4, 2))
+        st = tuple(int(v) for v in rng.integers(1, 4, 2))
+        dl = tuple(int(v) for v in rng.integers(1, 3, 2))
+        try:
+            od = oracle.out_dims((N, C, H, W), (K, C, R, S), pre, post, st, dl)
+        except oracle.OracleError:
+            continue
+        dyspec = wl.TensorSpec(od, wl.channels_last_strides(od))
+        wstr = wl.channels_last_strides((K, C, R, S)) if done % 2 else (1, K, S * C * K, C * K)
+        wspec = wl.TensorSpec((K, C, R, S), wstr)
+        dxspec = wl.TensorSpec((N, C, H, W), wl.channels_last_strides((N, C, H, W)))
+        run_dgrad_check(ci8, _rand_storage(dyspec, 300 + done), dyspec, _rand_storage(wspec, 400 + done),
+                        wspec, dxspec, pre, post, st, dl, mode=(done // 2) % 2, label=f"random k-major {done}",
+                        entry="plain" if done % 7 == 0 else "ws")
+        done += 1
+    logged = capfd.readouterr().err
+    assert "filter_read=kmajor" in logged
+    assert "data-gradient phases in one launch" in logged
+
+
 @pytest.mark.parametrize("dy_layout", ["nhwc", "nchw"])
 @pytest.mark.parametrize("mode", [0, 1])
 def test_dgrad_phase_filters_read_kmajor(ci8, monkeypatch, capfd, dy_layout, mode):
