@@ -437,6 +437,51 @@ def test_im2col_kmajor_filter(ci8, monkeypatch, tile, case_i, out_layout):
                   label=f"k-major filter {tile} case {case_i}")
 
 
+def test_random_kmajor_filter_problems(ci8, monkeypatch):
+    """Random layers with R, S, C, K filters, on the planner's own choice or
+    on a tile drawn from those that read such filters k-major (a forced tile
+    that does not apply falls back to the plan): C a multiple of 64, K of 16,
+    strides, dilation, padding, both output layouts; at least a third of them
+    k-major, on several tiles."""
+    rng = np.random.default_rng(61)
+    choices = [None, "t256x128", "t128x128", "64x128x64", "128x64x64", "128x128x64", "256x128x64",
+               "128x256x64", "w256x128x64", "w128x128x64"]
+    done = kmaj = 0
+    seen = set()
+    while done < 24:
+        tile = choices[int(rng.integers(0, len(choices)))]
+        if tile is None:
+            monkeypatch.delenv("CONV_I8_TILE", raising=False)
+        else:
+            monkeypatch.setenv("CONV_I8_TILE", tile)
+        N, C, K = int(rng.integers(1, 4)), 64 * int(rng.integers(1, 4)), 16 * int(rng.integers(1, 17))
+        H, W = (int(v) for v in rng.integers(3, 20, 2))
+        R, S = (3, 3) if done % 3 == 0 else tuple(int(v) for v in rng.integers(1, 5, 2))
+        pre = tuple(int(v) for v in rng.integers(0, 3, 2))
+        post = tuple(int(v) for v in rng.integers(0, 3, 2))
+        st = tuple(int(v) for v in rng.integers(1, 3, 2))
+        dl = tuple(int(v) for v in rng.integers(1, 3, 2))
+        try:
+            od = oracle.out_dims((N, C, H, W), (K, C, R, S), pre, post, st, dl)
+        except oracle.OracleError:
+            continue
+        xs = wl.TensorSpec((N, C, H, W), wl.channels_last_strides((N, C, H, W)))
+        ws = wl.TensorSpec((K, C, R, S), _rsck_strides(K, C, R, S))
+        os_ = wl.TensorSpec(od, wl.channels_last_strides(od) if done % 2 else wl.contiguous_strides(od))
+        plan = ci8.plan_fields(ci8.conv_fprop_i8_plan(ci8.desc(xs.dims, xs.strides, 1),
+                                                      ci8.desc(ws.dims, ws.strides, 1),
+                                                      ci8.desc(os_.dims, os_.strides, 2), pre, post, st, dl))
+        kmaj += plan["filter_read"] == "kmajor"
+        seen.add(plan["tile"])
+        g = torch.Generator().manual_seed(900 + done)
+        xv = torch.randint(-128, 128, (N, C, H, W), dtype=torch.int8, generator=g)
+        wv = torch.randint(-128, 128, (K, C, R, S), dtype=torch.int8, generator=g)
+        run_and_check(ci8, _fill(xs, xv, 1), xs, _fill(ws, wv, 2), ws, os_, pre, post, st, dl,
+                      label=f"random R,S,C,K filter {done} ({plan['tile']}, {plan['filter_read']})")
+        done += 1
+    assert kmaj >= 8 and len(seen) >= 4, (kmaj, seen)
+
+
 # ---------------------------------------------------------------------------
 # The 1x1 streaming kernel: ragged pixel counts (not a multiple of 32 or of a
 # wave's four tiles), ragged output channels and channels, stride and padding
