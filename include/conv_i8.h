@@ -406,13 +406,17 @@ conv_i8_status_t conv_fprop_i8_ex_ws(const conv_i8_desc_t *image, const void *im
  * forward convolutions, one per residue class of (h, w), each a stride-1
  * true convolution of dY with the filter transposed to [C, K, ...] and
  * subsampled to the taps that reach that class; they run one after another
- * on `stream` and share the workspace.  The workspace holds the packed
- * operands of the phases; with several phases, K a multiple of 16 and a
- * channel-innermost dY, every phase's packed filter view gets a region of its
- * own, written by one repack launch before the phases.  The size depends on
- * whether the operands can be read in place, so pass the pointers of the
- * call to the size query.  Errors and stream behaviour as conv_fprop_i8_ws;
- * never allocates, never synchronises.
+ * on `stream` and share the workspace.  A filter view whose K is contiguous
+ * (a KRSC filter) is read in place when K is a multiple of 64 and C of 16;
+ * when every phase reads its view that way and a channel-innermost dY in
+ * place, all the phases (up to four) run as one launch and no workspace is
+ * needed.  Otherwise the workspace holds the packed operands of the phases;
+ * with several phases, K a multiple of 16 and a channel-innermost dY, every
+ * phase's packed filter view gets a region of its own, written by one repack
+ * launch before the phases.  The size depends on whether the operands can be
+ * read in place, so pass the pointers of the call to the size query.  Errors
+ * and stream behaviour as conv_fprop_i8_ws; never allocates, never
+ * synchronises.
  */
 conv_i8_status_t conv_dgrad_i8_workspace_size(const conv_i8_desc_t *loss, const void *loss_ptr,
                                               const conv_i8_desc_t *filter,

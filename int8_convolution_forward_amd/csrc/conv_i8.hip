@@ -1715,11 +1715,11 @@ conv_i8_status_t dgrad_phases(const DgradProblem &dp, const void *dy_ptr, const 
 // The filter views of a strided layer's phases, packed once for all phases.
 // With several phases each phase's convolution would repack its own
 // (transposed, subsampled) filter view in a launch of its own; when every
-// view needs a repack, the packed copies are directly readable (K a multiple
-// of 16) and the phases read the loss in place (else each phase repacks its
-// part of the loss, and that launch carries its filter too), one repack
-// launch writes all the views into regions at the start of the workspace and
-// each phase reads its region in place.
+// view needs a repack (none is read k-major), the packed copies are directly
+// readable (K a multiple of 16) and the phases read the loss in place (else
+// each phase repacks its part of the loss, and that launch carries its filter
+// too), one repack launch writes all the views into regions at the start of
+// the workspace and each phase reads its region in place.
 struct DgradPack {
     bool on = false;
     int n = 0;                             // phases with taps, in dgrad_phases order
