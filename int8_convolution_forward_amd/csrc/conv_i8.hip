@@ -1810,9 +1810,60 @@ conv_i8_desc_t dgrad_packed_desc(const DgradPack &pk, int i)
     return make_desc(CONV_I8_DT_INT8, d, st);
 }
 
-conv_i8_status_t dgrad_workspace(const DgradProblem &dp, const void *dy_ptr, const void *w_ptr,
-                                 int32_t mode, size_t *bytes, DgradPack *pack = nullptr)
+// The loss of a strided layer packed once for all phases.  With several
+// phases each phase reads dY in full; a dY the kernels cannot read in place
+// (not channel-innermost, or misaligned) would be repacked by every phase.
+// When K is a multiple of 16 it is instead packed once, channel-innermost
+// ([N][P][Q][K], 256-byte aligned at the start of the workspace), and the
+// phases are planned and run on that copy (so the filter pack and the
+// one-launch path of a channels-last loss apply to them too).
+struct DgradLossPack {
+    bool on = false;
+    size_t bytes = 0;                      // the region, rounded to 256 bytes
+};
+
+DgradLossPack dgrad_loss_pack(const DgradProblem &dp, const void *dy_ptr, int32_t mode, DgradProblem *dp2)
 {
+    DgradLossPack lp;
+    *dp2 = dp;
+    int64_t b;
+    if (dp.str[0] * dp.str[1] < 2 || dp.K % 16 != 0 || dp.K == 0 || direct_ok(dp.dy, dy_ptr) ||
+        !mul_ok(dp.N * dp.P, dp.Q * dp.K, &b) || b == 0)
+        return lp;
+    int64_t tiles = 0;
+    repack_job(dp.dy, nullptr, nullptr, dp.K, &tiles);
+    if (tiles > kI32Max || dp.P * dp.Q > kI32Max)
+        return lp;
+    // only when two or more phases have taps (and would each repack dY)
+    int with_taps = 0;
+    dgrad_phases(dp, nullptr, nullptr, nullptr, mode,
+                 [&](const conv_i8_desc_t *, const void *, const conv_i8_desc_t *flt, const void *,
+                     const conv_i8_desc_t *, void *, const int64_t *, const int64_t *, const int64_t *,
+                     const int64_t *, int32_t) {
+                     with_taps += flt->dims[1] > 0 ? 1 : 0;
+                     return CONV_I8_OK;
+                 });
+    if (with_taps < 2)
+        return lp;
+    lp.on = true;
+    lp.bytes = align_up((size_t)b, 256);
+    const int64_t ps[4] = {dp.P * dp.Q * dp.K, 1, dp.Q * dp.K, dp.K};
+    for (int i = 0; i < 4; ++i)
+        dp2->dy.s[i] = ps[i];
+    return lp;
+}
+
+conv_i8_status_t dgrad_workspace(const DgradProblem &dp0, const void *dy_ptr0, const void *w_ptr,
+                                 int32_t mode, size_t *bytes, DgradPack *pack = nullptr,
+                                 DgradLossPack *loss_pack = nullptr)
+{
+    DgradProblem dp;
+    const DgradLossPack lp = dgrad_loss_pack(dp0, dy_ptr0, mode, &dp);
+    if (loss_pack)
+        *loss_pack = lp;
+    // planned on the packed copy when there is one (its region is 256-byte
+    // aligned: no pointer needed for the alignment checks)
+    const void *dy_ptr = lp.on ? nullptr : dy_ptr0;
     DgradPack own;
     DgradPack &pk = pack ? *pack : own;
     conv_i8_status_t st = dgrad_pack_plan(dp, dy_ptr, w_ptr, mode, &pk);
@@ -1837,7 +1888,7 @@ conv_i8_status_t dgrad_workspace(const DgradProblem &dp, const void *dy_ptr, con
             most = std::max(most, n);
             return s;
         });
-    *bytes = pk.bytes + most;
+    *bytes = lp.bytes + pk.bytes + most;
     return st;
 }
 
@@ -1936,7 +1987,8 @@ conv_i8_status_t dgrad_entry(const conv_i8_desc_t *loss, const void *loss_ptr,
         return CONV_I8_ERR_NULL;
     size_t need = 0;
     DgradPack pk;
-    if ((st = dgrad_workspace(dp, loss_ptr, filter_ptr, mode, &need, &pk)) != CONV_I8_OK)
+    DgradLossPack lp;
+    if ((st = dgrad_workspace(dp, loss_ptr, filter_ptr, mode, &need, &pk, &lp)) != CONV_I8_OK)
         return st;
     hipStream_t s = (hipStream_t)stream;
     void *ws = workspace;
@@ -1952,40 +2004,63 @@ conv_i8_status_t dgrad_entry(const conv_i8_desc_t *loss, const void *loss_ptr,
         if (need > 0 && ((uintptr_t)workspace & 255u) != 0)
             return CONV_I8_ERR_WORKSPACE;
     }
-    if (!pk.on) {
+    // workspace: [packed loss][packed filter views][the phases' own]
+    int8_t *const wsb = (int8_t *)ws;
+    int8_t *const ws_pk = wsb + lp.bytes;
+    DgradProblem dpr = dp;                  // the problem the phases run on
+    const void *dy_run = loss_ptr;
+    if (lp.on) {
+        dgrad_loss_pack(dp, loss_ptr, mode, &dpr);
+        dy_run = wsb;
+        if (log_enabled())
+            fprintf(stderr, "conv_i8: data-gradient loss packed once for %lld phases\n",
+                    (long long)(dp.str[0] * dp.str[1]));
+    }
+    {
+        // the loss and every phase's filter view packed in as few launches
+        // as the job slots allow
+        RepackJob jobs[kRepackMaxJobs];
+        int nj = 0;
+        if (lp.on)
+            jobs[nj++] = repack_job(dp.dy, (const int8_t *)loss_ptr, wsb, dp.K);
+        for (int i = 0; pk.on && i < pk.n && st == CONV_I8_OK; ++i) {
+            if (nj == kRepackMaxJobs) {
+                st = launch_repacks(jobs, nj, s);
+                nj = 0;
+            }
+            jobs[nj++] = repack_job(pk.view[i], (const int8_t *)pk.src[i], ws_pk + pk.off[i], pk.Kp);
+        }
+        if (nj > 0 && st == CONV_I8_OK)
+            st = launch_repacks(jobs, nj, s);
+    }
+    if (st == CONV_I8_OK && !pk.on) {
         bool done = false;
-        st = dgrad_one_launch(dp, loss_ptr, filter_ptr, dx_ptr, mode, s, &done);
+        st = dgrad_one_launch(dpr, dy_run, filter_ptr, dx_ptr, mode, s, &done);
         if (st != CONV_I8_OK || done) {
             if (alloc && ws && hipFreeAsync(ws, s) != hipSuccess && st == CONV_I8_OK)
                 st = CONV_I8_ERR_HIP;
             return st;
         }
     }
-    if (pk.on) {
-        // every phase's filter view packed in one launch
-        RepackJob jobs[kRepackMaxJobs];
-        for (int i = 0; i < pk.n; ++i)
-            jobs[i] = repack_job(pk.view[i], (const int8_t *)pk.src[i], (int8_t *)ws + pk.off[i], pk.Kp);
-        st = launch_repacks(jobs, pk.n, s);
-    }
     // the phases run one after another on the stream and share the workspace
-    // past the packed filters
+    // past the packed loss and filters
     int i = 0;
+    const size_t phase_ws = need - lp.bytes - pk.bytes;
     if (st == CONV_I8_OK)
-        st = dgrad_phases(dp, loss_ptr, filter_ptr, dx_ptr, mode,
+        st = dgrad_phases(dpr, dy_run, filter_ptr, dx_ptr, mode,
                           [&](const conv_i8_desc_t *img, const void *x, const conv_i8_desc_t *flt,
                               const void *w, const conv_i8_desc_t *out, void *y, const int64_t *pre_,
                               const int64_t *post_, const int64_t *stride_, const int64_t *dil_,
                               int32_t m) {
                               conv_i8_desc_t packed;
                               if (pk.on && flt->dims[1] > 0) {
-                                  w = (const int8_t *)ws + pk.off[i];
+                                  w = ws_pk + pk.off[i];
                                   packed = dgrad_packed_desc(pk, i++);
                                   flt = &packed;
                               }
                               return entry_run(img, x, flt, w, out, y, pre_, post_, stride_, dil_,
                                                CONV_I8_DT_INT32, m, nullptr, false,
-                                               (int8_t *)ws + pk.bytes, need - pk.bytes, stream);
+                                               phase_ws ? ws_pk + pk.bytes : nullptr, phase_ws, stream);
                           });
     if (alloc && ws && hipFreeAsync(ws, s) != hipSuccess && st == CONV_I8_OK)
         st = CONV_I8_ERR_HIP;

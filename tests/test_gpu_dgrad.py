@@ -136,9 +136,9 @@ def test_random_dgrad_kmajor_problems(ci8, capfd, monkeypatch):
 def test_dgrad_phase_filters_read_kmajor(ci8, monkeypatch, capfd, dy_layout, mode):
     """A stride-2 layer (the downsample workload: 4 phases, 64 input channels
     per phase): every phase reads its view of the KRSC filter in place,
-    k-major, so nothing is packed; a channels-last loss is read in place and
-    the four phases run in one launch, an NCHW one is repacked by each phase
-    (one launch per phase).  Bit-exact."""
+    k-major, so no filter is packed; a channels-last loss is read in place, an
+    NCHW one packed once for all phases; either way the four phases run in
+    one launch.  Bit-exact."""
     c = wl.case("downsample_s2_n8_c64_56")
     d = wl.make_inputs(c, c.seed_base + 8)
     dims = c.out.dims
@@ -152,19 +152,19 @@ def test_dgrad_phase_filters_read_kmajor(ci8, monkeypatch, capfd, dy_layout, mod
     plans = [ci8.plan_fields(l) for l in logged.splitlines() if "repack_filter=" in l]
     assert len(plans) == 4, logged
     assert all(p["repack_filter"] == "0" and p["filter_read"] == "kmajor" for p in plans), logged
-    assert all(p["repack_image"] == ("0" if dy_layout == "nhwc" else "1") for p in plans), logged
-    assert ("4 data-gradient phases in one launch" in logged) == (dy_layout == "nhwc"), logged
+    assert all(p["repack_image"] == "0" for p in plans), logged
+    assert ("loss packed once for 4 phases" in logged) == (dy_layout == "nchw"), logged
+    assert "4 data-gradient phases in one launch" in logged, logged
 
 
-@pytest.mark.parametrize("dy_layout,packed", [("nhwc", True), ("nchw", False)])
+@pytest.mark.parametrize("dy_layout,loss_in_place", [("nhwc", True), ("nchw", False)])
 @pytest.mark.parametrize("mode", [0, 1])
-def test_dgrad_phase_filters_packed_once(ci8, monkeypatch, capfd, dy_layout, packed, mode):
+def test_dgrad_phase_filters_packed_once(ci8, monkeypatch, capfd, dy_layout, loss_in_place, mode):
     """A stride-2 layer with 48 output channels (4 phases whose 48 input
     channels are no whole 64-channel stage, so no phase reads its filter view
-    k-major).  With a channels-last loss every phase's filter view is packed
-    by one repack launch before the phases, so each phase plan reads its
-    filter in place; with an NCHW loss each phase repacks its part of the
-    loss and its filter in one launch of its own.  Both bit-exact."""
+    k-major): every phase's filter view is packed by one repack launch before
+    the phases (which also packs an NCHW loss once for all of them), so each
+    phase plan reads its loss and its filter in place.  Bit-exact."""
     N, C, H, W, K = 4, 64, 20, 20, 48
     pre, post, st, dl = (1, 1), (1, 1), (2, 2), (1, 1)
     wspec = wl.TensorSpec((K, C, 3, 3), wl.channels_last_strides((K, C, 3, 3)))
@@ -178,5 +178,6 @@ def test_dgrad_phase_filters_packed_once(ci8, monkeypatch, capfd, dy_layout, pac
     logged = capfd.readouterr().err
     plans = [ci8.plan_fields(l) for l in logged.splitlines() if "repack_filter=" in l]
     assert len(plans) == 4, logged
-    assert all(p["repack_filter"] == ("0" if packed else "1") for p in plans), logged
+    assert all(p["repack_filter"] == "0" and p["repack_image"] == "0" for p in plans), logged
     assert not any(p["filter_read"] == "kmajor" for p in plans), logged
+    assert ("loss packed once" in logged) == (not loss_in_place), logged
