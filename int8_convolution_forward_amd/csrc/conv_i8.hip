@@ -26,6 +26,7 @@
 #include "repack_kernel.hpp"
 #include "mfma_ceiling_kernel.hpp"
 #include "direct_kernel.hpp"
+#include "wgrad1x1_kernel.hpp"
 
 #ifdef CONV_I8_HOST_ONLY
 // Host-only build of the validation and planning code (built with the host
@@ -2189,6 +2190,129 @@ conv_i8_status_t wgrad_call(const WgradProblem &wp, const void *x_ptr, const voi
               mode == CONV_I8_MODE_CONVOLUTION);
 }
 
+// A 1x1 weight gradient of stride 1 without padding on channels-last
+// operands: dW[k, c] = sum over pixels of dY * X, both operands read in place
+// by wgrad1x1_kernel (one launch), its pixels split over workgroups whose
+// partial copies of dW split_reduce_kernel adds.  The forward call of the
+// transposed operands would repack both, each a full pass over HBM.
+constexpr int kWg1TM = 128, kWg1TN = 128, kWg1NS = 4;
+constexpr int kWg1Target = kCUs, kWg1MinSteps = 8;
+
+struct Wgrad1x1Plan {
+    int64_t rows, dy_pitch, x_pitch;
+    int tiles, tiles_n, nsteps, ksplit, kchunk;
+    size_t ws_bytes;
+};
+
+// Bytes between consecutive pixels when every pixel (n, p, q) of a
+// channels-last tensor lies at (n*P*Q + p*Q + q) * pitch, or 0.
+int64_t pixel_pitch(const T4 &t)
+{
+    if (t.s[1] != 1)
+        return 0;
+    const int64_t P = t.d[2], Q = t.d[3];
+    const int64_t pitch = Q > 1 ? t.s[3] : P > 1 ? t.s[2] : t.d[0] > 1 ? t.s[0] : 16 * ((t.d[1] + 15) / 16);
+    if (pitch <= 0 || pitch % 16 != 0)
+        return 0;
+    if ((P > 1 && t.s[2] != Q * pitch) || (t.d[0] > 1 && t.s[0] != P * Q * pitch))
+        return 0;
+    return pitch;
+}
+
+bool wgrad1x1_plan(const WgradProblem &wp, const void *x_ptr, const void *dy_ptr, Wgrad1x1Plan *q)
+{
+    if (env_tile())
+        return false;  // a forced tile is for the forward call of the transposed operands
+    if (wp.R != 1 || wp.S != 1 || wp.str[0] != 1 || wp.str[1] != 1)
+        return false;
+    for (int i = 0; i < 2; ++i)
+        if (wp.pre[i] != 0 || wp.post[i] != 0)
+            return false;
+    if (wp.K % 16 != 0 || wp.C % 16 != 0 || ((uintptr_t)x_ptr & 15u) != 0 || ((uintptr_t)dy_ptr & 15u) != 0)
+        return false;
+    const int64_t rows = wp.N * wp.P * wp.Q;
+    q->dy_pitch = pixel_pitch(wp.dy);
+    q->x_pitch = pixel_pitch(wp.x);
+    if (rows < 1 || q->dy_pitch == 0 || q->x_pitch == 0)
+        return false;
+    int64_t e1, e2;
+    if (!mul_ok(rows - 1, q->dy_pitch, &e1) || e1 + wp.K > kI32Max || !mul_ok(rows - 1, q->x_pitch, &e2) ||
+        e2 + wp.C > kI32Max)
+        return false;
+    // dW dense (the partial copies and their sum walk its span)
+    int64_t span;
+    if (!span_of(wp.dw, &span) || span != wp.K * wp.C || 4 * span > kI32Max)
+        return false;
+    q->rows = rows;
+    q->tiles_n = (int)((wp.C + kWg1TN - 1) / kWg1TN);
+    q->tiles = (int)((wp.K + kWg1TM - 1) / kWg1TM) * q->tiles_n;
+    q->nsteps = (int)((rows + 63) / 64);
+    // about one workgroup per CU, each at least kWg1MinSteps steps of 64 pixels
+    const int want = std::max(1, std::min(kWg1Target / std::max(q->tiles, 1), q->nsteps / kWg1MinSteps));
+    q->kchunk = (q->nsteps + want - 1) / want;
+    q->ksplit = (q->nsteps + q->kchunk - 1) / q->kchunk;
+    q->ws_bytes = q->ksplit > 1 ? (size_t)q->ksplit * (size_t)span * 4 : 0;
+    return true;
+}
+
+std::string describe_wgrad1x1(const Wgrad1x1Plan &q)
+{
+    char b[256];
+    snprintf(b, sizeof b,
+             "kernel=wgrad1x1 tile=%dx%d operands=in_place pixels=%lld steps=%d tiles=%d ksplit=%d "
+             "split_sum=%s workspace=%zu",
+             kWg1TM, kWg1TN, (long long)q.rows, q.nsteps, q.tiles, q.ksplit, q.ksplit > 1 ? "partial" : "none",
+             q.ws_bytes);
+    return b;
+}
+
+conv_i8_status_t wgrad1x1_run(const WgradProblem &wp, const Wgrad1x1Plan &q, const void *x_ptr,
+                              const void *dy_ptr, void *dw_ptr, void *ws, hipStream_t stream)
+{
+    Wgrad1x1Args a{};
+    a.dy = (const int8_t *)dy_ptr;
+    a.x = (const int8_t *)x_ptr;
+    a.rows = (int)q.rows;
+    a.K = (int)wp.K;
+    a.C = (int)wp.C;
+    a.dy_pitch = (int)q.dy_pitch;
+    a.x_pitch = (int)q.x_pitch;
+    a.dy_range = (int)((q.rows - 1) * q.dy_pitch + wp.K);
+    a.x_range = (int)((q.rows - 1) * q.x_pitch + wp.C);
+    a.oK = (int)wp.dw.s[0];
+    a.oC = (int)wp.dw.s[1];
+    const int64_t span = wp.K * wp.C;
+    a.out_range = (int)(4 * span);
+    a.tiles_n = q.tiles_n;
+    a.nsteps = q.nsteps;
+    a.kchunk = q.kchunk;
+    a.part_stride = span;
+    a.out = q.ksplit > 1 ? (int32_t *)ws : (int32_t *)dw_ptr;
+    hipLaunchKernelGGL((wgrad1x1_kernel<kWg1TM, kWg1TN, kWg1NS>), dim3((unsigned)q.tiles, (unsigned)q.ksplit),
+                       dim3(256), 0, stream, a);
+    if (hipGetLastError() != hipSuccess)
+        return CONV_I8_ERR_HIP;
+    if (q.ksplit > 1) {
+        const int32_t *part = a.out;
+        int32_t *out = (int32_t *)dw_ptr;
+        const bool v4 = span % 4 == 0 && ((uintptr_t)out & 15u) == 0 && ((uintptr_t)part & 15u) == 0;
+        const int64_t items = v4 ? span / 4 : span;
+        const dim3 grid((unsigned)std::min<int64_t>(std::max<int64_t>((items + 255) / 256, 1), 4 * kCUs));
+        if (v4 && q.ksplit >= 16)
+            hipLaunchKernelGGL(split_reduce_wide_kernel<16>, dim3((unsigned)((items + 15) / 16)), dim3(256), 0, stream,
+                               part, (long long)span, q.ksplit, out, (long long)span);
+        else if (v4)
+            hipLaunchKernelGGL(split_reduce_kernel<true>, grid, dim3(256), 0, stream, part, (long long)span,
+                               q.ksplit, out, (long long)span);
+        else
+            hipLaunchKernelGGL(split_reduce_kernel<false>, grid, dim3(256), 0, stream, part, (long long)span,
+                               q.ksplit, out, (long long)span);
+        if (hipGetLastError() != hipSuccess)
+            return CONV_I8_ERR_HIP;
+    }
+    return CONV_I8_OK;
+}
+
 conv_i8_status_t wgrad_entry(const conv_i8_desc_t *image, const void *image_ptr,
                              const conv_i8_desc_t *loss, const void *loss_ptr,
                              const conv_i8_desc_t *dw, void *dw_ptr, const int64_t *pre,
@@ -2204,6 +2328,35 @@ conv_i8_status_t wgrad_entry(const conv_i8_desc_t *image, const void *image_ptr,
         if (ws_size)
             *ws_size = 0;
         return CONV_I8_OK;
+    }
+    Wgrad1x1Plan q1;
+    if (wgrad1x1_plan(wp, image_ptr, loss_ptr, &q1)) {
+        if (size_only) {
+            *ws_size = q1.ws_bytes;
+            return CONV_I8_OK;
+        }
+        if (!image_ptr || !loss_ptr || !dw_ptr)
+            return CONV_I8_ERR_NULL;
+        hipStream_t s = (hipStream_t)stream;
+        void *ws = workspace;
+        if (alloc) {
+            ws = nullptr;
+            if (q1.ws_bytes > 0 && hipMallocAsync(&ws, q1.ws_bytes, s) != hipSuccess)
+                return CONV_I8_ERR_HIP;
+        } else {
+            if (workspace_bytes < q1.ws_bytes)
+                return CONV_I8_ERR_WORKSPACE;
+            if (q1.ws_bytes > 0 && !workspace)
+                return CONV_I8_ERR_NULL;
+            if (q1.ws_bytes > 0 && ((uintptr_t)workspace & 255u) != 0)
+                return CONV_I8_ERR_WORKSPACE;
+        }
+        if (log_enabled())
+            fprintf(stderr, "conv_i8 (weight gradient): %s\n", describe_wgrad1x1(q1).c_str());
+        st = wgrad1x1_run(wp, q1, image_ptr, loss_ptr, dw_ptr, ws, s);
+        if (alloc && ws && hipFreeAsync(ws, s) != hipSuccess && st == CONV_I8_OK)
+            st = CONV_I8_ERR_HIP;
+        return st;
     }
     const char *tuned = tuned_wgrad_tile(wp);
     if (size_only)
@@ -2443,6 +2596,11 @@ conv_i8_status_t conv_wgrad_i8_plan(const conv_i8_desc_t *image, const void *ima
         return st;
     if (wp.dw.elems() == 0) {
         snprintf(buf, len, "empty");
+        return CONV_I8_OK;
+    }
+    Wgrad1x1Plan q1;
+    if (wgrad1x1_plan(wp, image_ptr, loss_ptr, &q1)) {
+        snprintf(buf, len, "%s", describe_wgrad1x1(q1).c_str());
         return CONV_I8_OK;
     }
     const char *tuned = tuned_wgrad_tile(wp);

@@ -364,4 +364,40 @@ __global__ __launch_bounds__(256) void split_reduce_kernel(const int32_t *part, 
     }
 }
 
+// The same sum for many copies of a small output (16-byte vectors): each
+// workgroup takes 256/G vectors, its G groups of threads add copies g, g+G,
+// g+2G, ... of them (four loads in flight per thread), and the G group sums
+// of each vector are added through LDS.  Enough loads are then in flight for
+// an output of a few thousand vectors to be summed at HBM speed.
+template <int G>
+__global__ __launch_bounds__(256) void split_reduce_wide_kernel(const int32_t *part, long long stride, int nsplit,
+                                                                int32_t *out, long long n)
+{
+    typedef int i32x4 __attribute__((ext_vector_type(4)));
+    constexpr int V = 256 / G;   // vectors per workgroup
+    __shared__ i32x4 red[G][V];
+    const int it = threadIdx.x % V, g = threadIdx.x / V;
+    const long long i = (long long)blockIdx.x * V + it;
+    const long long n4 = n / 4, s4 = stride / 4;
+    i32x4 s = {0, 0, 0, 0};
+    if (i < n4) {
+        const i32x4 *p = (const i32x4 *)part + i;
+        int z = g;
+        for (; z + 3 * G < nsplit; z += 4 * G) {
+            const i32x4 a = p[z * s4], b = p[(z + G) * s4], c = p[(z + 2 * G) * s4], d = p[(z + 3 * G) * s4];
+            s += (a + b) + (c + d);
+        }
+        for (; z < nsplit; z += G)
+            s += p[z * s4];
+    }
+    red[g][it] = s;
+    __syncthreads();
+    if (g == 0 && i < n4) {
+#pragma unroll
+        for (int k = 1; k < G; ++k)
+            s += red[k][it];
+        ((i32x4 *)out)[i] = s;
+    }
+}
+
 }  // namespace convi8

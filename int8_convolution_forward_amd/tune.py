@@ -107,6 +107,12 @@ def sweep(name, op="fprop", calls_per_batch=200, warmup=300, rotate_mb=600.0, lo
     saved = os.environ.pop("CONV_I8_TILE", None)
     results = []
     lanes = None
+    if op == "wgrad" and ci8.plan_fields(plan(sets[0])).get("kernel") == "wgrad1x1":
+        # a 1x1 gradient read in place by its own kernel: no tile to choose
+        print(f"tune: {op} {name}: the in-place 1x1 kernel, not swept", file=log, flush=True)
+        if saved is not None:
+            os.environ["CONV_I8_TILE"] = saved
+        return [], None
     try:
         for tile in ci8.conv_i8_tile_names():
             os.environ["CONV_I8_TILE"] = tile
@@ -169,9 +175,12 @@ def read_table(path=INC):
 
 def write_table(rows, device_name, path=INC):
     """rows: [(op, workload, key, [(tile, us), ...])]; entries of the table
-    already at `path` for other (op, workload) pairs are kept."""
+    already at `path` for other (op, workload) pairs are kept, and a pair
+    swept with no tile to choose (key None) loses its entry."""
     table = read_table(path)
     for op, name, key, res in rows:
+        if key is None:
+            table.pop((op, name), None)
         if not res:
             continue
         others = ", ".join(f"{t} {us:.2f}" for t, us in res[1:])

@@ -154,3 +154,43 @@ def test_wgrad_split_paths(ci8, monkeypatch, capfd, layout, split_sum):
     logged = capfd.readouterr().err
     plans = [ci8.plan_fields(l) for l in logged.splitlines() if "ksplit=" in l]
     assert plans and all(p["split_sum"] == split_sum and int(p["ksplit"]) > 1 for p in plans), logged
+
+
+# (N, C, K, H, W, x pitch or None (dense channels-last), dW layout, mode, ksplit > 1 expected)
+WGRAD_1X1_CASES = [
+    (2, 48, 80, 9, 11, None, "kcrs", 0, False),
+    (2, 48, 80, 9, 11, None, "krsc", 1, False),
+    (1, 272, 144, 20, 20, None, "kcrs", 0, False),     # ragged tiles along both K and C
+    (4, 64, 32, 32, 32, None, "krsc", 0, True),        # 4096 pixels over several splits
+    (3, 48, 96, 17, 23, 64, "kcrs", 1, True),          # image pixels 64 bytes apart (a channel slice)
+    (1, 16, 16, 1, 1, None, "kcrs", 0, False),         # one pixel
+]
+
+
+@pytest.mark.parametrize("case", WGRAD_1X1_CASES)
+def test_wgrad_1x1_in_place(ci8, case):
+    """A 1x1 weight gradient of stride 1 without padding on channels-last
+    operands: both read in place by the dedicated kernel (no repack), ragged
+    tiles, one or several splits, a pixel pitch wider than the channels, both
+    dW layouts and both modes."""
+    N, C, K, H, W, pitch, dwl, mode, split = case
+    xdims = (N, C, H, W)
+    if pitch is None:
+        xspec = wl.TensorSpec(xdims, wl.channels_last_strides(xdims))
+    else:
+        xspec = wl.TensorSpec(xdims, (H * W * pitch, 1, W * pitch, pitch))
+    dydims = (N, K, H, W)
+    dyspec = wl.TensorSpec(dydims, wl.channels_last_strides(dydims))
+    dwdims = (K, C, 1, 1)
+    dwspec = wl.TensorSpec(dwdims, wl.contiguous_strides(dwdims) if dwl == "kcrs" else wl.channels_last_strides(dwdims))
+    zero, one = (0, 0), (1, 1)
+    f = ci8.plan_fields(ci8.conv_wgrad_i8_plan(ci8.desc(xdims, xspec.strides, ci8.DT_INT8),
+                                               ci8.desc(dydims, dyspec.strides, ci8.DT_INT8),
+                                               ci8.desc(dwdims, dwspec.strides, ci8.DT_INT32),
+                                               zero, zero, one, one, mode=mode))
+    assert f["kernel"] == "wgrad1x1" and (int(f["ksplit"]) > 1) == split, f
+    seed = N * 1000 + C + K
+    run_wgrad_check(ci8, _rand_storage(xspec, seed), xspec, _rand_storage(dyspec, seed + 1), dyspec, dwspec,
+                    zero, zero, one, one, mode=mode, label=f"1x1 in place {case}")
+    run_wgrad_check(ci8, _rand_storage(xspec, seed + 2), xspec, _rand_storage(dyspec, seed + 3), dyspec, dwspec,
+                    zero, zero, one, one, mode=mode, label=f"1x1 in place {case}, plain entry", entry="plain")
