@@ -279,10 +279,16 @@ def bench_grad(args, c):
     else:
         roof = {"bound": "hbm", "achieved": alg_bytes / (ms * 1e-3) / 1e9, "peak": HBM_PEAK_GBS,
                 "unit": "GB/s"}
+    plan = ci8.conv_wgrad_i8_plan(sets[0][3], sets[0][4], sets[0][5], c.pre, c.post, c.stride, c.dilation,
+                                  mode=mode) if wg else None
+    if wg and ci8.plan_fields(plan).get("kernel") == "wgrad1x1":
+        what = "whole wgrad call (the 1x1 kernel reading both operands in place + the sum of its partial copies)"
+    elif wg:
+        what = "whole wgrad call (repacks of both transposed operands + one forward kernel)"
+    else:
+        what = "whole dgrad call (filter repack + one forward kernel per stride phase)"
     roof.update({"frac": roof["achieved"] / roof["peak"], "traffic": None,
-                 "kernel": ("whole wgrad call (repacks of both transposed operands + one forward "
-                            "kernel)") if wg else
-                           "whole dgrad call (filter repack + one forward kernel per stride phase)",
+                 "kernel": what,
                  "kernel_avg_us": ms * 1e3, "kernel_only_launch": False,
                  "timed_batches_ms_per_step": batches,
                  "algorithmic_bytes": alg_bytes, "algorithmic_ops": ops})
@@ -322,7 +328,8 @@ def bench_grad(args, c):
                    ("dw_strides" if wg else "dx_strides"): list(dx_strides),
                    "pre_padding": list(c.pre), "post_padding": list(c.post),
                    "stride": list(c.stride), "dilation": list(c.dilation),
-                   "accumulate": "int32", "output": "int32", "buffer_sets": nsets},
+                   "accumulate": "int32", "output": "int32", "buffer_sets": nsets,
+                   **({"plan": plan} if plan else {})},
         "frac_of_int8_peak": tops / INT8_PEAK_TOPS,
         "roofline": roof,
         "cpu_baseline": cpu,
