@@ -281,8 +281,8 @@ def bench_grad(args, c):
                 "unit": "GB/s"}
     plan = ci8.conv_wgrad_i8_plan(sets[0][3], sets[0][4], sets[0][5], c.pre, c.post, c.stride, c.dilation,
                                   mode=mode) if wg else None
-    if wg and ci8.plan_fields(plan).get("kernel") == "wgrad1x1":
-        what = "whole wgrad call (the 1x1 kernel reading both operands in place + the sum of its partial copies)"
+    if wg and ci8.plan_fields(plan).get("kernel") == "wgrad_in_place":
+        what = "whole wgrad call (the in-place kernel reading both operands + the sum of its partial copies)"
     elif wg:
         what = "whole wgrad call (repacks of both transposed operands + one forward kernel)"
     else:

@@ -468,12 +468,13 @@ conv_i8_status_t conv_dgrad_i8(const conv_i8_desc_t *loss, const void *loss_ptr,
  * forward convolution: the image transposed to [C, N, H, W] convolved with the
  * loss transposed to [K, N, P, Q] at stride = dilation and dilation = stride,
  * written to dW transposed to [C, K, R, S] (reversed along R and S for true
- * convolution).  A 1x1 filter at stride 1 without padding, on channels-last
- * image and loss (channel stride 1, every pixel at the same multiple of 16
- * bytes from the previous one, 16-byte aligned pointers), C and K multiples
- * of 16 and a dense dw, takes one kernel instead that reads both operands in
- * place (dW = the product of the two over the N*P*Q pixels; both modes are
- * the same there).  Errors and stream behaviour as conv_fprop_i8_ws; never
+ * convolution).  Channels-last image and loss (channel stride 1, image
+ * strides and the loss's pixel pitch multiples of 16 bytes, 16-byte aligned
+ * pointers), C and K multiples of 16 and a dense dw of at most 128 tiles of
+ * 128x128 per filter tap take one kernel instead that reads both operands in
+ * place: for each tap, the product of the loss and the image pixels the tap
+ * reads, over the N*P*Q output pixels.  Errors and stream behaviour as
+ * conv_fprop_i8_ws; never
  * allocates, never synchronises.  The workspace holds the packed transposed
  * operands and, when the long N*P*Q reduction is split over workgroups and dw
  * is dense, one int32 partial copy of dw per split (added into dw by a
@@ -517,8 +518,8 @@ conv_i8_status_t conv_wgrad_i8(const conv_i8_desc_t *image, const void *image_pt
  * "Convolutions" page, section "Convolution Wgrad"; the plan list of the
  * cuDNN frontend tutorial page, autotuning paragraph): the description of
  * the one forward call conv_wgrad_i8_ws makes (tile, split of the N*P*Q
- * reduction, workspace), "kernel=wgrad1x1 ..." for a gradient the in-place
- * 1x1 kernel serves, or "empty" for a dw with no elements.  Arguments
+ * reduction, workspace), "kernel=wgrad_in_place ..." for a gradient the
+ * in-place kernel serves, or "empty" for a dw with no elements.  Arguments
  * and errors as conv_wgrad_i8_workspace_size; writes at most `len` bytes
  * including the terminating NUL.  Host-only.
  */

@@ -14,7 +14,7 @@ LIB = os.path.join(LIB_DIR, "libconv_i8.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 SOURCES = [os.path.join(CSRC, "conv_i8.hip")]
-HEADERS = [os.path.join(CSRC, f) for f in ("kernel_common.hpp", "igemm_kernel.hpp", "footprint_kernel.hpp", "pointwise_kernel.hpp", "mfma_ceiling_kernel.hpp", "direct_kernel.hpp", "wgrad1x1_kernel.hpp", "tuned_tiles.inc",
+HEADERS = [os.path.join(CSRC, f) for f in ("kernel_common.hpp", "igemm_kernel.hpp", "footprint_kernel.hpp", "pointwise_kernel.hpp", "mfma_ceiling_kernel.hpp", "direct_kernel.hpp", "wgrad_kernel.hpp", "tuned_tiles.inc",
                                                "repack_kernel.hpp")] + [
     os.path.join(INCLUDE, "conv_i8.h")]
 

@@ -26,7 +26,7 @@
 #include "repack_kernel.hpp"
 #include "mfma_ceiling_kernel.hpp"
 #include "direct_kernel.hpp"
-#include "wgrad1x1_kernel.hpp"
+#include "wgrad_kernel.hpp"
 
 #ifdef CONV_I8_HOST_ONLY
 // Host-only build of the validation and planning code (built with the host
@@ -2190,16 +2190,20 @@ conv_i8_status_t wgrad_call(const WgradProblem &wp, const void *x_ptr, const voi
               mode == CONV_I8_MODE_CONVOLUTION);
 }
 
-// A 1x1 weight gradient of stride 1 without padding on channels-last
-// operands: dW[k, c] = sum over pixels of dY * X, both operands read in place
-// by wgrad1x1_kernel (one launch), its pixels split over workgroups whose
-// partial copies of dW split_reduce_kernel adds.  The forward call of the
-// transposed operands would repack both, each a full pass over HBM.
-constexpr int kWg1TM = 128, kWg1TN = 128, kWg1NS = 4;
-constexpr int kWg1Target = kCUs, kWg1MinSteps = 8;
+// A weight gradient on channels-last image and loss read in place: for each
+// filter tap dW[., ., r, s] = sum over the output pixels of dY times the image
+// pixel the tap reads, both operands read by wgrad_inplace_kernel as they lie
+// in memory (one launch), its pixels split over workgroups whose partial
+// copies of dW split_reduce_kernel adds.  The forward call of the transposed
+// operands repacks both, each a full pass over HBM.  A 1x1 filter at stride 1
+// without padding whose image pixels are equally spaced needs no index
+// arithmetic (the image row of output pixel j is pixel j).
+constexpr int kWgIpTM = 128, kWgIpTN = 128, kWgIpNS = 4;
+constexpr int kWgIpTarget = kCUs, kWgIpMinSteps = 8;
 
-struct Wgrad1x1Plan {
-    int64_t rows, dy_pitch, x_pitch;
+struct WgradInPlacePlan {
+    int64_t rows, dy_pitch, x_pitch, x_span;
+    bool taps;
     int tiles, tiles_n, nsteps, ksplit, kchunk;
     size_t ws_bytes;
 };
@@ -2219,57 +2223,72 @@ int64_t pixel_pitch(const T4 &t)
     return pitch;
 }
 
-bool wgrad1x1_plan(const WgradProblem &wp, const void *x_ptr, const void *dy_ptr, Wgrad1x1Plan *q)
+bool wgrad_inplace_plan(const WgradProblem &wp, const void *x_ptr, const void *dy_ptr, WgradInPlacePlan *q)
 {
     if (env_tile())
         return false;  // a forced tile is for the forward call of the transposed operands
-    if (wp.R != 1 || wp.S != 1 || wp.str[0] != 1 || wp.str[1] != 1)
-        return false;
-    for (int i = 0; i < 2; ++i)
-        if (wp.pre[i] != 0 || wp.post[i] != 0)
-            return false;
     if (wp.K % 16 != 0 || wp.C % 16 != 0 || ((uintptr_t)x_ptr & 15u) != 0 || ((uintptr_t)dy_ptr & 15u) != 0)
         return false;
     const int64_t rows = wp.N * wp.P * wp.Q;
     q->dy_pitch = pixel_pitch(wp.dy);
-    q->x_pitch = pixel_pitch(wp.x);
-    if (rows < 1 || q->dy_pitch == 0 || q->x_pitch == 0)
+    if (rows < 1 || rows > (1 << 22) - 256 || q->dy_pitch == 0)
         return false;
-    int64_t e1, e2;
-    if (!mul_ok(rows - 1, q->dy_pitch, &e1) || e1 + wp.K > kI32Max || !mul_ok(rows - 1, q->x_pitch, &e2) ||
-        e2 + wp.C > kI32Max)
+    int64_t e;
+    if (!mul_ok(rows - 1, q->dy_pitch, &e) || e + wp.K > kI32Max)
         return false;
     // dW dense (the partial copies and their sum walk its span)
     int64_t span;
-    if (!span_of(wp.dw, &span) || span != wp.K * wp.C || 4 * span > kI32Max)
+    if (!span_of(wp.dw, &span) || span != wp.K * wp.C * wp.R * wp.S || 4 * span > kI32Max)
         return false;
+    const bool unit = wp.R == 1 && wp.S == 1 && wp.str[0] == 1 && wp.str[1] == 1 && wp.pre[0] == 0 &&
+                      wp.pre[1] == 0 && wp.post[0] == 0 && wp.post[1] == 0;
+    q->x_pitch = unit ? pixel_pitch(wp.x) : 0;
+    q->taps = q->x_pitch == 0;
+    if (q->taps) {
+        // image pixels through their strides: 16-byte chunks, 32-bit offsets
+        if (wp.x.s[1] != 1 || wp.x.s[0] % 16 != 0 || wp.x.s[2] % 16 != 0 || wp.x.s[3] % 16 != 0)
+            return false;
+        if (!span_of(wp.x, &q->x_span) || q->x_span > kI32Max || wp.P * wp.Q > (1 << 22) - 256)
+            return false;
+    } else {
+        if (!mul_ok(rows - 1, q->x_pitch, &e) || e + wp.C > kI32Max)
+            return false;
+        q->x_span = e + wp.C;
+    }
     q->rows = rows;
-    q->tiles_n = (int)((wp.C + kWg1TN - 1) / kWg1TN);
-    q->tiles = (int)((wp.K + kWg1TM - 1) / kWg1TM) * q->tiles_n;
+    q->tiles_n = (int)((wp.C + kWgIpTN - 1) / kWgIpTN);
+    q->tiles = (int)((wp.K + kWgIpTM - 1) / kWgIpTM) * q->tiles_n;
     q->nsteps = (int)((rows + 63) / 64);
-    // about one workgroup per CU, each at least kWg1MinSteps steps of 64 pixels
-    const int want = std::max(1, std::min(kWg1Target / std::max(q->tiles, 1), q->nsteps / kWg1MinSteps));
+    // A dW of more tiles than half the CUs fills the chip without a split:
+    // there the forward call's larger tiles and deeper schedule win (the
+    // large-channel layer: 63 against 97 us), here the streaming of both
+    // operands does.
+    const int64_t units = (int64_t)q->tiles * wp.R * wp.S;
+    if (units > kWgIpTarget / 2)
+        return false;
+    // about one workgroup per CU, each at least kWgIpMinSteps steps of 64 pixels
+    const int want = (int)std::max<int64_t>(1, std::min<int64_t>(kWgIpTarget / units, q->nsteps / kWgIpMinSteps));
     q->kchunk = (q->nsteps + want - 1) / want;
     q->ksplit = (q->nsteps + q->kchunk - 1) / q->kchunk;
     q->ws_bytes = q->ksplit > 1 ? (size_t)q->ksplit * (size_t)span * 4 : 0;
     return true;
 }
 
-std::string describe_wgrad1x1(const Wgrad1x1Plan &q)
+std::string describe_wgrad_inplace(const WgradProblem &wp, const WgradInPlacePlan &q)
 {
     char b[256];
     snprintf(b, sizeof b,
-             "kernel=wgrad1x1 tile=%dx%d operands=in_place pixels=%lld steps=%d tiles=%d ksplit=%d "
-             "split_sum=%s workspace=%zu",
-             kWg1TM, kWg1TN, (long long)q.rows, q.nsteps, q.tiles, q.ksplit, q.ksplit > 1 ? "partial" : "none",
-             q.ws_bytes);
+             "kernel=wgrad_in_place tile=%dx%d operands=in_place image_rows=%s pixels=%lld steps=%d tiles=%lld "
+             "ksplit=%d split_sum=%s workspace=%zu",
+             kWgIpTM, kWgIpTN, q.taps ? "per_tap" : "linear", (long long)q.rows, q.nsteps,
+             (long long)q.tiles * wp.R * wp.S, q.ksplit, q.ksplit > 1 ? "partial" : "none", q.ws_bytes);
     return b;
 }
 
-conv_i8_status_t wgrad1x1_run(const WgradProblem &wp, const Wgrad1x1Plan &q, const void *x_ptr,
-                              const void *dy_ptr, void *dw_ptr, void *ws, hipStream_t stream)
+conv_i8_status_t wgrad_inplace_run(const WgradProblem &wp, const WgradInPlacePlan &q, const void *x_ptr,
+                                   const void *dy_ptr, void *dw_ptr, void *ws, int32_t mode, hipStream_t stream)
 {
-    Wgrad1x1Args a{};
+    WgradInPlaceArgs a{};
     a.dy = (const int8_t *)dy_ptr;
     a.x = (const int8_t *)x_ptr;
     a.rows = (int)q.rows;
@@ -2278,18 +2297,42 @@ conv_i8_status_t wgrad1x1_run(const WgradProblem &wp, const Wgrad1x1Plan &q, con
     a.dy_pitch = (int)q.dy_pitch;
     a.x_pitch = (int)q.x_pitch;
     a.dy_range = (int)((q.rows - 1) * q.dy_pitch + wp.K);
-    a.x_range = (int)((q.rows - 1) * q.x_pitch + wp.C);
+    a.x_range = (int)q.x_span;
     a.oK = (int)wp.dw.s[0];
     a.oC = (int)wp.dw.s[1];
-    const int64_t span = wp.K * wp.C;
+    const int64_t span = wp.K * wp.C * wp.R * wp.S;
     a.out_range = (int)(4 * span);
     a.tiles_n = q.tiles_n;
     a.nsteps = q.nsteps;
     a.kchunk = q.kchunk;
     a.part_stride = span;
     a.out = q.ksplit > 1 ? (int32_t *)ws : (int32_t *)dw_ptr;
-    hipLaunchKernelGGL((wgrad1x1_kernel<kWg1TM, kWg1TN, kWg1NS>), dim3((unsigned)q.tiles, (unsigned)q.ksplit),
-                       dim3(256), 0, stream, a);
+    a.tiles = q.tiles;
+    a.R = (int)wp.R;
+    a.S = (int)wp.S;
+    a.PQ = (int)(wp.P * wp.Q);
+    a.Q = (int)wp.Q;
+    a.inv_pq = 1.0f / (float)a.PQ;
+    a.inv_q = 1.0f / (float)a.Q;
+    a.H = (int)wp.H;
+    a.W = (int)wp.W;
+    a.sN = (int)wp.x.s[0];
+    a.sH = (int)wp.x.s[2];
+    a.sW = (int)wp.x.s[3];
+    a.st_h = (int)wp.str[0];
+    a.st_w = (int)wp.str[1];
+    a.dil_h = (int)wp.dil[0];
+    a.dil_w = (int)wp.dil[1];
+    a.pre_h = (int)wp.pre[0];
+    a.pre_w = (int)wp.pre[1];
+    a.oR = (int)wp.dw.s[2];
+    a.oS = (int)wp.dw.s[3];
+    a.flip = mode == CONV_I8_MODE_CONVOLUTION;
+    const dim3 grid((unsigned)(q.taps ? (int64_t)q.tiles * wp.R * wp.S : q.tiles), (unsigned)q.ksplit);
+    if (q.taps)
+        hipLaunchKernelGGL((wgrad_inplace_kernel<kWgIpTM, kWgIpTN, kWgIpNS, true>), grid, dim3(256), 0, stream, a);
+    else
+        hipLaunchKernelGGL((wgrad_inplace_kernel<kWgIpTM, kWgIpTN, kWgIpNS, false>), grid, dim3(256), 0, stream, a);
     if (hipGetLastError() != hipSuccess)
         return CONV_I8_ERR_HIP;
     if (q.ksplit > 1) {
@@ -2297,15 +2340,15 @@ conv_i8_status_t wgrad1x1_run(const WgradProblem &wp, const Wgrad1x1Plan &q, con
         int32_t *out = (int32_t *)dw_ptr;
         const bool v4 = span % 4 == 0 && ((uintptr_t)out & 15u) == 0 && ((uintptr_t)part & 15u) == 0;
         const int64_t items = v4 ? span / 4 : span;
-        const dim3 grid((unsigned)std::min<int64_t>(std::max<int64_t>((items + 255) / 256, 1), 4 * kCUs));
+        const dim3 rgrid((unsigned)std::min<int64_t>(std::max<int64_t>((items + 255) / 256, 1), 4 * kCUs));
         if (v4 && q.ksplit >= 16)
-            hipLaunchKernelGGL(split_reduce_wide_kernel<16>, dim3((unsigned)((items + 15) / 16)), dim3(256), 0, stream,
-                               part, (long long)span, q.ksplit, out, (long long)span);
+            hipLaunchKernelGGL(split_reduce_wide_kernel<16>, dim3((unsigned)((items + 15) / 16)), dim3(256), 0,
+                               stream, part, (long long)span, q.ksplit, out, (long long)span);
         else if (v4)
-            hipLaunchKernelGGL(split_reduce_kernel<true>, grid, dim3(256), 0, stream, part, (long long)span,
+            hipLaunchKernelGGL(split_reduce_kernel<true>, rgrid, dim3(256), 0, stream, part, (long long)span,
                                q.ksplit, out, (long long)span);
         else
-            hipLaunchKernelGGL(split_reduce_kernel<false>, grid, dim3(256), 0, stream, part, (long long)span,
+            hipLaunchKernelGGL(split_reduce_kernel<false>, rgrid, dim3(256), 0, stream, part, (long long)span,
                                q.ksplit, out, (long long)span);
         if (hipGetLastError() != hipSuccess)
             return CONV_I8_ERR_HIP;
@@ -2329,8 +2372,8 @@ conv_i8_status_t wgrad_entry(const conv_i8_desc_t *image, const void *image_ptr,
             *ws_size = 0;
         return CONV_I8_OK;
     }
-    Wgrad1x1Plan q1;
-    if (wgrad1x1_plan(wp, image_ptr, loss_ptr, &q1)) {
+    WgradInPlacePlan q1;
+    if (wgrad_inplace_plan(wp, image_ptr, loss_ptr, &q1)) {
         if (size_only) {
             *ws_size = q1.ws_bytes;
             return CONV_I8_OK;
@@ -2352,8 +2395,8 @@ conv_i8_status_t wgrad_entry(const conv_i8_desc_t *image, const void *image_ptr,
                 return CONV_I8_ERR_WORKSPACE;
         }
         if (log_enabled())
-            fprintf(stderr, "conv_i8 (weight gradient): %s\n", describe_wgrad1x1(q1).c_str());
-        st = wgrad1x1_run(wp, q1, image_ptr, loss_ptr, dw_ptr, ws, s);
+            fprintf(stderr, "conv_i8 (weight gradient): %s\n", describe_wgrad_inplace(wp, q1).c_str());
+        st = wgrad_inplace_run(wp, q1, image_ptr, loss_ptr, dw_ptr, ws, mode, s);
         if (alloc && ws && hipFreeAsync(ws, s) != hipSuccess && st == CONV_I8_OK)
             st = CONV_I8_ERR_HIP;
         return st;
@@ -2598,9 +2641,9 @@ conv_i8_status_t conv_wgrad_i8_plan(const conv_i8_desc_t *image, const void *ima
         snprintf(buf, len, "empty");
         return CONV_I8_OK;
     }
-    Wgrad1x1Plan q1;
-    if (wgrad1x1_plan(wp, image_ptr, loss_ptr, &q1)) {
-        snprintf(buf, len, "%s", describe_wgrad1x1(q1).c_str());
+    WgradInPlacePlan q1;
+    if (wgrad_inplace_plan(wp, image_ptr, loss_ptr, &q1)) {
+        snprintf(buf, len, "%s", describe_wgrad_inplace(wp, q1).c_str());
         return CONV_I8_OK;
     }
     const char *tuned = tuned_wgrad_tile(wp);

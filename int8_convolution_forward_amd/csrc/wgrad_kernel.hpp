@@ -1,28 +1,31 @@
-// Weight gradient of a 1x1 convolution of stride 1 without padding, read in
-// place from channels-last operands on gfx950 (CDNA4).
+// Weight gradient read in place from channels-last operands on gfx950
+// (CDNA4).
 //
-// With a 1x1 filter every output pixel j = (n, p, q) reads the input pixel at
-// the same place, so dW[k, c] = sum_j dY[j, k] * X[j, c]: a matrix product
-// whose reduction runs over the pixels.  Channels-last loss and image store
-// each pixel's channels contiguously, i.e. both operands come reduction-major
-// ("k-major": a row per pixel, the GEMM's M or N dimension along the row).
-// The kernel stages 64 pixels of both per step in LDS exactly as they lie in
-// memory and builds the MFMA fragments with transposing LDS reads
-// (ds_read_b64_tr_b8), so neither operand is repacked and each byte of the
-// loss and the image is read from HBM about once per tile column or row.
+// dW[k, c, r, s] = sum over output pixels j = (n, p, q) of dY[j, k] *
+// X[n, p*st_h - pre_h + r*dil_h, q*st_w - pre_w + s*dil_w, c] (X is 0 outside
+// the image): for each filter tap a matrix product whose reduction runs over
+// the pixels.  Channels-last loss and image store each pixel's channels
+// contiguously, i.e. both operands come reduction-major ("k-major": a row per
+// pixel, the GEMM's M or N dimension along the row).  The kernel stages 64
+// pixels of both per step in LDS exactly as they lie in memory (the image row
+// of pixel j is the pixel tap (r, s) of output pixel j reads, or zeros in the
+// padding) and builds the MFMA fragments with transposing LDS reads
+// (ds_read_b64_tr_b8), so neither operand is repacked.  For a 1x1 filter at
+// stride 1 without padding (TAPS false) the image row of pixel j is pixel j
+// itself and no index arithmetic is needed.
 //
-// Tile TM x TN of dW (TM loss channels k, TN image channels c), four waves
-// 2 x 2; the pixels split over gridDim.y (split z runs steps [z*kchunk,
-// (z+1)*kchunk)) and each split stores its partial sums into its own copy
-// of dW, which a reduction kernel adds (integer adds: the sum does not depend
-// on their order).
+// Tile TM x TN of one tap of dW (TM loss channels k, TN image channels c),
+// four waves 2 x 2; workgroup x = tap * tiles + tile; the pixels split over
+// gridDim.y (split z runs steps [z*kchunk, (z+1)*kchunk)) and each split
+// stores its partial sums into its own copy of dW, which a reduction kernel
+// adds (integer adds: the sum does not depend on their order).
 #pragma once
 
 #include "kernel_common.hpp"
 
 namespace convi8 {
 
-struct Wgrad1x1Args {
+struct WgradInPlaceArgs {
     const int8_t *dy;     // loss: pixel j's K channels at dy + j*dy_pitch
     const int8_t *x;      // image: pixel j's C channels at x + j*x_pitch
     int32_t *out;         // dW, or partial copy 0: (k, c) at out[k*oK + c*oC]
@@ -36,10 +39,22 @@ struct Wgrad1x1Args {
     int nsteps;              // ceil(rows / 64)
     int kchunk;              // steps per split
     long long part_stride;   // elements from one partial copy to the next
+    // taps (TAPS): pixel j = (n, p, q) of the output, tap (r, s) reads image
+    // pixel (n, p*st_h + r*dil_h - pre_h, q*st_w + s*dil_w - pre_w)
+    int tiles;               // tiles of one tap
+    int S;                   // filter width (tap = r*S + s)
+    int R;
+    int PQ, Q;
+    float inv_pq, inv_q;     // 1/PQ, 1/Q rounded to float (fdiv)
+    int H, W;
+    int sN, sH, sW;          // image strides in bytes (channel stride 1)
+    int st_h, st_w, dil_h, dil_w, pre_h, pre_w;
+    int oR, oS;              // element strides of dW along r and s
+    int flip;                // true convolution: tap (r, s) goes to (R-1-r, S-1-s)
 };
 
-template <int TM, int TN, int NS>
-__global__ __launch_bounds__(256) void wgrad1x1_kernel(Wgrad1x1Args a)
+template <int TM, int TN, int NS, bool TAPS>
+__global__ __launch_bounds__(256) void wgrad_inplace_kernel(WgradInPlaceArgs a)
 {
     constexpr int NW = 4;                    // waves, 2 x 2
     constexpr int BK = 64;                   // pixels per step
@@ -58,8 +73,12 @@ __global__ __launch_bounds__(256) void wgrad1x1_kernel(Wgrad1x1Args a)
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int m0 = (int)(blockIdx.x / (unsigned)a.tiles_n) * TM;
-    const int n0 = (int)(blockIdx.x % (unsigned)a.tiles_n) * TN;
+    const int tile = TAPS ? (int)(blockIdx.x % (unsigned)a.tiles) : (int)blockIdx.x;
+    const int tap = TAPS ? (int)(blockIdx.x / (unsigned)a.tiles) : 0;
+    const int m0 = (tile / a.tiles_n) * TM;
+    const int n0 = (tile % a.tiles_n) * TN;
+    const int tr = TAPS ? tap / a.S : 0, ts = TAPS ? tap - tr * a.S : 0;
+    const int dh = tr * a.dil_h - a.pre_h, dw = ts * a.dil_w - a.pre_w;
     const int s0 = (int)blockIdx.y * a.kchunk;
     const int ns = max(min(a.kchunk, a.nsteps - s0), 0);
     const v4i dy_rsrc = make_rsrc(a.dy, a.dy_range);
@@ -83,7 +102,7 @@ __global__ __launch_bounds__(256) void wgrad1x1_kernel(Wgrad1x1Args a)
         const int kr = (i * NW + wave) * 8 + (lane >> 3);
         const int col = n0 + (((lane & 7) ^ (kr & 7)) << 4);
         b_row[i] = kr;
-        b_off[i] = col < a.C ? kr * a.x_pitch + col : -1;
+        b_off[i] = col < a.C ? (TAPS ? col : kr * a.x_pitch + col) : -1;
     }
     // step s (local) into ring slot s % NS; pixels past the last and steps
     // past the split read zeros (out-of-range offsets)
@@ -98,9 +117,21 @@ __global__ __launch_bounds__(256) void wgrad1x1_kernel(Wgrad1x1Args a)
         }
 #pragma unroll
         for (int i = 0; i < BL; ++i) {
-            const bool ok = live && b_off[i] >= 0 && j0 + b_row[i] < a.rows;
-            load16_to_lds(x_rsrc, slot + A_BYTES + i * GB + wave * 1024,
-                          ok ? b_off[i] + j0 * a.x_pitch : kOutOfRange);
+            const int j = j0 + b_row[i];
+            bool ok = live && b_off[i] >= 0 && j < a.rows;
+            int off;
+            if constexpr (TAPS) {
+                // the image pixel tap (r, s) of output pixel j reads
+                const int n = fdiv(j, a.PQ, a.inv_pq);
+                const int rem = j - n * a.PQ;
+                const int p = fdiv(rem, a.Q, a.inv_q);
+                const int h = p * a.st_h + dh, w = (rem - p * a.Q) * a.st_w + dw;
+                ok = ok && (unsigned)h < (unsigned)a.H && (unsigned)w < (unsigned)a.W;
+                off = n * a.sN + h * a.sH + w * a.sW + b_off[i];
+            } else {
+                off = b_off[i] + j0 * a.x_pitch;
+            }
+            load16_to_lds(x_rsrc, slot + A_BYTES + i * GB + wave * 1024, ok ? off : kOutOfRange);
         }
     };
 
@@ -177,6 +208,7 @@ __global__ __launch_bounds__(256) void wgrad1x1_kernel(Wgrad1x1Args a)
     // v%4 (loss channel k), column l%32 (image channel c)
     const __amdgpu_buffer_rsrc_t out_rsrc = __builtin_amdgcn_make_buffer_rsrc(
         (void *)(a.out + (long long)blockIdx.y * a.part_stride), (short)0, a.out_range, kRsrcWord3);
+    const int tap_off = TAPS ? (a.flip ? a.R - 1 - tr : tr) * a.oR + (a.flip ? a.S - 1 - ts : ts) * a.oS : 0;
 #pragma unroll
     for (int x = 0; x < FM; ++x)
 #pragma unroll
@@ -185,7 +217,7 @@ __global__ __launch_bounds__(256) void wgrad1x1_kernel(Wgrad1x1Args a)
 #pragma unroll
             for (int v = 0; v < 16; ++v) {
                 const int k = m0 + wm + x * 32 + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
-                const int off = (k < a.K && c < a.C) ? (k * a.oK + c * a.oC) * 4 : kOutOfRange;
+                const int off = (k < a.K && c < a.C) ? (k * a.oK + c * a.oC + tap_off) * 4 : kOutOfRange;
                 __builtin_amdgcn_raw_buffer_store_b32(acc[x][y][v], out_rsrc, off, 0, kOutStoreDefault);
             }
         }

@@ -107,9 +107,9 @@ def sweep(name, op="fprop", calls_per_batch=200, warmup=300, rotate_mb=600.0, lo
     saved = os.environ.pop("CONV_I8_TILE", None)
     results = []
     lanes = None
-    if op == "wgrad" and ci8.plan_fields(plan(sets[0])).get("kernel") == "wgrad1x1":
-        # a 1x1 gradient read in place by its own kernel: no tile to choose
-        print(f"tune: {op} {name}: the in-place 1x1 kernel, not swept", file=log, flush=True)
+    if op == "wgrad" and ci8.plan_fields(plan(sets[0])).get("kernel") == "wgrad_in_place":
+        # a gradient read in place by its own kernel: no tile to choose
+        print(f"tune: {op} {name}: the in-place weight-gradient kernel, not swept", file=log, flush=True)
         if saved is not None:
             os.environ["CONV_I8_TILE"] = saved
         return [], None

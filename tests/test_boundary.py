@@ -561,11 +561,50 @@ def test_wgrad_argument_errors():
     # a tiny problem: the direct kernel reads the transposed operands in place
     assert ci8.conv_wgrad_i8_workspace_size(x, dy, dw, pre, post, st, dl) == 0
     dy, w, dx, pre, post, st, dl = _dgrad_args(K=32, C=64)
-    x = D(dx.dims, dx.strides, ci8.DT_INT8)
+    N, C, H, W = dx.dims
+    x = D(dx.dims, (C * H * W, H * W, W, 1), ci8.DT_INT8)   # NCHW: not read in place
     dw = D(w.dims, w.strides, ci8.DT_INT32)
     n = ci8.conv_wgrad_i8_workspace_size(x, dy, dw, pre, post, st, dl)
     assert n > 0                                 # both transposed operands are repacked
     assert call(x, dy, dw, ws_bytes=n - 1, ws=FAKE) == 10
+    # channels-last, many pixels: read in place, the pixels split into partial copies of dW
+    dy, w, dx, pre, post, st, dl = _dgrad_args(N=8, K=32, C=64, H=40, W=40)
+    x = D(dx.dims, dx.strides, ci8.DT_INT8)
+    dw = D(w.dims, w.strides, ci8.DT_INT32)
+    f = ci8.plan_fields(ci8.conv_wgrad_i8_plan(x, dy, dw, pre, post, st, dl))
+    n = ci8.conv_wgrad_i8_workspace_size(x, dy, dw, pre, post, st, dl)
+    assert f["kernel"] == "wgrad_in_place" and int(f["ksplit"]) > 1, f
+    assert n == int(f["workspace"]) == int(f["ksplit"]) * 32 * 64 * 9 * 4
+    assert call(x, dy, dw, ws_bytes=n - 1, ws=FAKE) == 10
+
+
+def test_wgrad_in_place_plans(monkeypatch):
+    """Which weight gradients the in-place kernel takes: channels-last image
+    and loss with C and K multiples of 16 and a dense dW whose tiles (128x128
+    per filter tap) number at most half the CUs; anything else, or a forced
+    tile, goes to the forward call of the transposed operands."""
+    monkeypatch.delenv("CONV_I8_TILE", raising=False)
+    D = ci8.desc
+
+    def plan(N=4, K=64, C=64, H=20, W=20, R=3, S=3, x_nchw=False, dw_gaps=False, st=(1, 1), pad=(1, 1)):
+        dy, w, dx, pre, post, st_, dl = _dgrad_args(N=N, K=K, C=C, H=H, W=W, R=R, S=S, pre=pad, post=pad, st=st)
+        xs = (C * H * W, H * W, W, 1) if x_nchw else dx.strides
+        ws_ = (R * S * 2 * C, 1, S * 2 * C, 2 * C) if dw_gaps else w.strides
+        return ci8.plan_fields(ci8.conv_wgrad_i8_plan(D(dx.dims, xs, ci8.DT_INT8), dy,
+                                                      D(w.dims, ws_, ci8.DT_INT32), pre, post, st_, dl))
+    f = plan()
+    assert (f["kernel"], f["image_rows"]) == ("wgrad_in_place", "per_tap"), f
+    f = plan(R=1, S=1, pad=(0, 0))
+    assert (f["kernel"], f["image_rows"]) == ("wgrad_in_place", "linear"), f
+    f = plan(R=1, S=1, pad=(0, 0), st=(2, 2))
+    assert (f["kernel"], f["image_rows"]) == ("wgrad_in_place", "per_tap"), f
+    assert plan(x_nchw=True)["kernel"] != "wgrad_in_place"
+    assert plan(C=40)["kernel"] != "wgrad_in_place"
+    assert plan(dw_gaps=True)["kernel"] != "wgrad_in_place"
+    assert plan(K=512, C=512, H=14, W=14)["kernel"] != "wgrad_in_place"    # 144 tile-taps
+    assert plan(K=384, C=384, H=14, W=14)["kernel"] == "wgrad_in_place"    # 81
+    monkeypatch.setenv("CONV_I8_TILE", "128x128x64")
+    assert plan()["tile"] == "128x128x64"
 
 
 class _NoCalls:

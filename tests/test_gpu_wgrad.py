@@ -188,9 +188,44 @@ def test_wgrad_1x1_in_place(ci8, case):
                                                ci8.desc(dydims, dyspec.strides, ci8.DT_INT8),
                                                ci8.desc(dwdims, dwspec.strides, ci8.DT_INT32),
                                                zero, zero, one, one, mode=mode))
-    assert f["kernel"] == "wgrad1x1" and (int(f["ksplit"]) > 1) == split, f
+    assert f["kernel"] == "wgrad_in_place" and (int(f["ksplit"]) > 1) == split, f
     seed = N * 1000 + C + K
     run_wgrad_check(ci8, _rand_storage(xspec, seed), xspec, _rand_storage(dyspec, seed + 1), dyspec, dwspec,
                     zero, zero, one, one, mode=mode, label=f"1x1 in place {case}")
     run_wgrad_check(ci8, _rand_storage(xspec, seed + 2), xspec, _rand_storage(dyspec, seed + 3), dyspec, dwspec,
                     zero, zero, one, one, mode=mode, label=f"1x1 in place {case}, plain entry", entry="plain")
+
+
+def test_random_wgrad_in_place_taps(ci8):
+    """Random channels-last weight gradients (C and K multiples of 16) that
+    the in-place kernel serves tap by tap: strides, dilations, padding on
+    either side (taps that read only padding included), non-square filters,
+    both dW layouts, both modes, one or several splits."""
+    rng = np.random.default_rng(97)
+    done = 0
+    while done < 24:
+        N = int(rng.integers(1, 5))
+        C, K = 16 * int(rng.integers(1, 12)), 16 * int(rng.integers(1, 12))
+        R, S = int(rng.integers(1, 6)), int(rng.integers(1, 6))
+        H, W = int(rng.integers(1, 30)), int(rng.integers(1, 30))
+        st = (int(rng.integers(1, 4)), int(rng.integers(1, 4)))
+        dl = (int(rng.integers(1, 3)), int(rng.integers(1, 3)))
+        pre = (int(rng.integers(0, 4)), int(rng.integers(0, 4)))
+        post = (int(rng.integers(0, 4)), int(rng.integers(0, 4)))
+        od = oracle.out_dims((N, C, H, W), (K, C, R, S), pre, post, st, dl)
+        if min(od) < 1:
+            continue
+        xspec = wl.TensorSpec((N, C, H, W), wl.channels_last_strides((N, C, H, W)))
+        dyspec = wl.TensorSpec(od, wl.channels_last_strides(od))
+        dwd = (K, C, R, S)
+        dwspec = wl.TensorSpec(dwd, wl.contiguous_strides(dwd) if done % 2 else wl.channels_last_strides(dwd))
+        mode = int(rng.integers(0, 2))
+        f = ci8.plan_fields(ci8.conv_wgrad_i8_plan(ci8.desc(xspec.dims, xspec.strides, ci8.DT_INT8),
+                                                   ci8.desc(od, dyspec.strides, ci8.DT_INT8),
+                                                   ci8.desc(dwd, dwspec.strides, ci8.DT_INT32),
+                                                   pre, post, st, dl, mode=mode))
+        assert f["kernel"] == "wgrad_in_place", f
+        run_wgrad_check(ci8, _rand_storage(xspec, 900 + done), xspec, _rand_storage(dyspec, 950 + done), dyspec,
+                        dwspec, pre, post, st, dl, mode=mode, label=f"in place taps #{done} {f['image_rows']} "
+                        f"ksplit {f['ksplit']}")
+        done += 1
