@@ -2259,15 +2259,14 @@ bool wgrad_inplace_plan(const WgradProblem &wp, const void *x_ptr, const void *d
     q->tiles_n = (int)((wp.C + kWgIpTN - 1) / kWgIpTN);
     q->tiles = (int)((wp.K + kWgIpTM - 1) / kWgIpTM) * q->tiles_n;
     q->nsteps = (int)((rows + 63) / 64);
-    // A dW of more tiles than half the CUs fills the chip without a split:
-    // there the forward call's larger tiles and deeper schedule win (the
-    // large-channel layer: 63 against 97 us), here the streaming of both
-    // operands does.
+    // About one workgroup per CU, each at least kWgIpMinSteps steps of 64
+    // pixels; a dW of more tile-taps than half the CUs aims at two per CU (the
+    // kernel's 64 KB of LDS lets two share a CU, and the second hides the
+    // first's waits: the large-channel layer, 144 tile-taps, takes 53 us in
+    // three splits against 98 us in one)
     const int64_t units = (int64_t)q->tiles * wp.R * wp.S;
-    if (units > kWgIpTarget / 2)
-        return false;
-    // about one workgroup per CU, each at least kWgIpMinSteps steps of 64 pixels
-    const int want = (int)std::max<int64_t>(1, std::min<int64_t>(kWgIpTarget / units, q->nsteps / kWgIpMinSteps));
+    const int64_t target = units * 2 > kWgIpTarget ? 2 * kWgIpTarget : kWgIpTarget;
+    const int want = (int)std::max<int64_t>(1, std::min<int64_t>(target / units, q->nsteps / kWgIpMinSteps));
     q->kchunk = (q->nsteps + want - 1) / want;
     q->ksplit = (q->nsteps + q->kchunk - 1) / q->kchunk;
     q->ws_bytes = q->ksplit > 1 ? (size_t)q->ksplit * (size_t)span * 4 : 0;

@@ -580,9 +580,10 @@ def test_wgrad_argument_errors():
 
 def test_wgrad_in_place_plans(monkeypatch):
     """Which weight gradients the in-place kernel takes: channels-last image
-    and loss with C and K multiples of 16 and a dense dW whose tiles (128x128
-    per filter tap) number at most half the CUs; anything else, or a forced
-    tile, goes to the forward call of the transposed operands."""
+    and loss with C and K multiples of 16 and a dense dW; anything else, or a
+    forced tile, goes to the forward call of the transposed operands.  A dW
+    of more tile-taps (128x128 per filter tap) than half the CUs is split for
+    two workgroups per CU."""
     monkeypatch.delenv("CONV_I8_TILE", raising=False)
     D = ci8.desc
 
@@ -601,8 +602,10 @@ def test_wgrad_in_place_plans(monkeypatch):
     assert plan(x_nchw=True)["kernel"] != "wgrad_in_place"
     assert plan(C=40)["kernel"] != "wgrad_in_place"
     assert plan(dw_gaps=True)["kernel"] != "wgrad_in_place"
-    assert plan(K=512, C=512, H=14, W=14)["kernel"] != "wgrad_in_place"    # 144 tile-taps
-    assert plan(K=384, C=384, H=14, W=14)["kernel"] == "wgrad_in_place"    # 81
+    f = plan(N=64, K=512, C=512, H=14, W=14)       # the large-channel layer: 144 tile-taps
+    assert (f["kernel"], f["tiles"], f["ksplit"]) == ("wgrad_in_place", "144", "3"), f
+    f = plan(N=64, K=256, C=256, H=14, W=14)       # 36 tile-taps: one workgroup per CU
+    assert (f["kernel"], f["tiles"], f["ksplit"]) == ("wgrad_in_place", "36", "7"), f
     monkeypatch.setenv("CONV_I8_TILE", "128x128x64")
     assert plan()["tile"] == "128x128x64"
 
