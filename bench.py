@@ -167,10 +167,17 @@ def parse():
                     help="int32: the plain entry; requant: INT8 output with per-channel "
                          "scale and bias and ReLU")
     ap.add_argument("--rotate-mb", type=float, default=600.0)
+    ap.add_argument("--seed", type=int, default=None,
+                    help="seed of the synthetic inputs (default: the workload's own)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="target CPU time of the oracle baseline sample")
     return ap.parse_args()
+
+
+def input_seed(args, c) -> int:
+    """Seed of the timed inputs: --seed, else the workload's own."""
+    return c.seed_base if args.seed is None else args.seed
 
 
 def kernel_source_digest() -> str:
@@ -209,7 +216,7 @@ def bench_grad(args, c):
 
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
-    d = wl.make_inputs(c, c.seed_base)
+    d = wl.make_inputs(c, input_seed(args, c))
     N, K, P, Q = c.out.dims
     _, C, R, S = c.filter.dims
     H, W = c.image.dims[2], c.image.dims[3]
@@ -320,7 +327,7 @@ def bench_grad(args, c):
         "warmup": args.warmup, "ms_per_step": ms, "timed_batches_ms_per_step": batches,
         "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": "int8", "data": "synthetic",
-        "config": {"workload": c.name, "op": args.op, "mode": args.mode,
+        "config": {"workload": c.name, "seed": input_seed(args, c), "op": args.op, "mode": args.mode,
                    "loss": list(c.out.dims), "loss_strides": list(c.out.strides),
                    ("image" if wg else "filter"): list(in_spec.dims),
                    ("image_strides" if wg else "filter_strides"): list(in_spec.strides),
@@ -357,7 +364,7 @@ def main():
     esize = 1 if rq_on else 4
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
-    d = wl.make_inputs(c, c.seed_base)
+    d = wl.make_inputs(c, input_seed(args, c))
     N, K, P, Q = c.out.dims
     _, C, R, S = c.filter.dims
     ops = c.ops
@@ -570,7 +577,7 @@ def main():
         "vs_baseline": None,
         "dtype": "int8",
         "data": "synthetic",
-        "config": {"workload": c.name, "image": list(c.image.dims), "image_strides": list(c.image.strides),
+        "config": {"workload": c.name, "seed": input_seed(args, c), "image": list(c.image.dims), "image_strides": list(c.image.strides),
                    "filter": list(c.filter.dims), "filter_strides": list(c.filter.strides),
                    "out": list(c.out.dims), "out_strides": list(c.out.strides),
                    "pre_padding": list(c.pre), "post_padding": list(c.post),
