@@ -222,7 +222,7 @@ def bench_grad(args, c):
     H, W = c.image.dims[2], c.image.dims[3]
     ops = c.ops
     mode = 1 if args.mode == "convolution" else 0
-    g = torch.Generator().manual_seed(c.seed_base + 91)
+    g = torch.Generator().manual_seed(input_seed(args, c) + 91)
     dy0 = torch.randint(-128, 128, (c.out.storage_size,), dtype=torch.int8, generator=g).to(dev)
     wg = args.op == "wgrad"
     if wg:
@@ -385,7 +385,7 @@ def main():
         sets.append((xs, ws_, ys, x, w, y))
     # requantisation parameters: per-channel scales that keep typical sums of
     # random operands around +-64, biases, ReLU (all on the device)
-    g = torch.Generator().manual_seed(c.seed_base + 77)
+    g = torch.Generator().manual_seed(input_seed(args, c) + 77)
     typical = (C * R * S) ** 0.5 * 128 * 128 / 3
     q_scale = ((torch.rand(K, generator=g) + 0.5) * 64 / typical).to(dev)
     q_bias = ((torch.rand(K, generator=g) - 0.5) * 40).to(dev)
